@@ -26,6 +26,7 @@ from .fp8 import (  # noqa: F401
 )
 from .model import (  # noqa: F401
     bf16_to_f32,
+    round_bf16,
     rmsnorm,
     silu,
     rope_cos_sin,

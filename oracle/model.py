@@ -32,7 +32,11 @@ Readings where the pages leave a step open (each also listed in the design doc):
     steps consume); logits and argmax codes are still the model's own.
 
 Precision: `dt` (np.float32 by default, np.float64 for cross-checks). Weights
-are the canonical bf16 values (or, for fp8, s * dec(q)), held in `dt`.
+are the canonical bf16 values (or, for fp8, s * dec(q)), held in `dt`. The KV
+caches hold activations, whose dtype the s2-pro-fp8 model card ("What is
+this?") gives as bfloat16: cached keys (after RoPE) and values are rounded to
+bf16 (nearest even) when written, unless kv="fp32". Queries, scores, softmax,
+the residual stream and every matrix product stay in `dt`.
 """
 from __future__ import annotations
 
@@ -44,6 +48,20 @@ from .fp8 import e4m3_decode, quantize_rows
 def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
     """bf16 bit patterns (uint16) -> fp32 values (exact widening)."""
     return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def round_bf16(x: np.ndarray) -> np.ndarray:
+    """Nearest bf16 value (ties to even) of each entry, returned in x's dtype.
+
+    fp64 inputs are first rounded to fp32 (the precision the KV values are
+    produced in); NaN stays NaN.
+    """
+    f = np.asarray(x, dtype=np.float32)
+    u = f.view(np.uint32).astype(np.uint64)
+    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+    out = r.astype(np.uint32).view(np.float32)
+    out = np.where(np.isnan(f), f, out)
+    return out.astype(np.asarray(x).dtype, copy=False)
 
 
 def rmsnorm(x: np.ndarray, g: np.ndarray, eps: float) -> np.ndarray:
@@ -140,12 +158,16 @@ class OracleModel:
     used as s * dec(q); tables and norm gains stay bf16.
     """
 
-    def __init__(self, dims, tensors: dict, wtype: str = "bf16", dt=np.float32, drop_source: bool = False):
+    def __init__(self, dims, tensors: dict, wtype: str = "bf16", dt=np.float32, drop_source: bool = False,
+                 kv: str = "bf16"):
         if wtype not in ("bf16", "fp8"):
             raise ValueError(wtype)
+        if kv not in ("bf16", "fp32"):
+            raise ValueError(kv)
         self.dims = dims
         self.wtype = wtype
         self.dt = dt
+        self.kv_bf16 = kv == "bf16"
         self.fp8 = {}
 
         def get(name):
@@ -188,8 +210,8 @@ class OracleModel:
         cos, sin = rope_cos_sin(pos, hd, d.rope_base, self.dt)
         q = apply_rope(q, cos[:, None, :], sin[:, None, :])
         k = apply_rope(k, cos[:, None, :], sin[:, None, :])
-        cache_k[p0:p0 + n] = k
-        cache_v[p0:p0 + n] = v
+        cache_k[p0:p0 + n] = round_bf16(k) if self.kv_bf16 else k
+        cache_v[p0:p0 + n] = round_bf16(v) if self.kv_bf16 else v
         o = gqa_attention(q, cache_k[:p0 + n], cache_v[:p0 + n], pos)
         x = x + layer.wo(o.reshape(n, qw))
         h2 = rmsnorm(x, layer.ffn_norm, d.rms_eps)
@@ -326,6 +348,8 @@ def _full(model, layers, x, d, final):
         v = qkv[:, d.q_width + d.kv_width:].reshape(n, d.n_heads_kv, hd)
         q = apply_rope(q, cos[:, None, :], sin[:, None, :])
         k = apply_rope(k, cos[:, None, :], sin[:, None, :])
+        if model.kv_bf16:
+            k, v = round_bf16(k), round_bf16(v)
         k_rep = np.repeat(k, g, axis=1)                               # [n, n_q, hd]
         v_rep = np.repeat(v, g, axis=1)
         s = np.einsum("ihd,jhd->hij", q, k_rep) * scale               # [n_q, n, n]

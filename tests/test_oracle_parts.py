@@ -164,3 +164,26 @@ def test_greedy_argmax_first_index_and_nan():
     assert greedy_argmax(np.array([1.0, 3.0, 3.0, 2.0])) == 1
     assert greedy_argmax(np.array([np.nan, -5.0, -7.0])) == 1
     assert greedy_argmax(np.array([-np.inf, -np.inf])) == 0
+
+
+def test_round_bf16_nearest_even():
+    from oracle import round_bf16
+    one = np.float32(1.0)
+    ulp = np.float32(2.0 ** -7)                       # bf16 spacing at 1
+    x = np.array([1.0, 1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, 1 + 2.0 ** -9, -1 - 2.0 ** -8, 3e38, 1e-40],
+                 dtype=np.float32)
+    r = round_bf16(x)
+    assert r[0] == one
+    assert r[1] == one                                # tie -> even (1.0)
+    assert r[2] == one + 2 * ulp                      # tie -> even (1 + 2^-6)
+    assert r[3] == one                                # below half
+    assert r[4] == -one                               # tie -> even
+    assert np.isfinite(r[5]) or r[5] == np.inf
+    assert r[6] >= 0
+    # every value is representable: low 16 bits clear
+    assert np.all(r.view(np.uint32) & 0xFFFF == 0)
+    # agrees with torch's bf16 cast (a library routine) on random values
+    import torch
+    v = np.random.default_rng(0).standard_normal(100000).astype(np.float32) * 10
+    ref = torch.from_numpy(v).to(torch.bfloat16).to(torch.float32).numpy()
+    assert np.array_equal(round_bf16(v), ref)
