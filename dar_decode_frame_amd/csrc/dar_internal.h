@@ -1,0 +1,134 @@
+// Internal interface between the runtime (dar_runtime.hip) and the gfx950
+// kernels (dar_kernels.hip). Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dar {
+
+constexpr int kWave = 64;
+constexpr int kBlock = 256;
+constexpr int kWaves = kBlock / kWave;
+constexpr int kMaxM = 2;           // input rows per GEMV launch (fast pass 1 runs two)
+constexpr int kAttnChunkDefault = 64;
+
+enum WType : int { W_BF16 = 0, W_FP8 = 1 };
+
+// y[m][r] (+)= scale[r] * sum_j W[r][j] * xin[m][j], xin = x or RMSNorm(x) * gain
+struct GemvArgs {
+  const void* W;
+  const float* scale;       // per-row scales (fp8) or nullptr
+  int rows, K, M;
+  const float* x;
+  int x_stride;
+  const uint16_t* gain;     // RMSNorm gain (bf16) or nullptr for no norm
+  float eps;
+  float* y;
+  int y_stride;
+  int accumulate;           // 1: y += result (residual stream), 0: y = result
+};
+
+// Fused RMSNorm + QKV GEMV + RoPE + KV append.
+struct QkvArgs {
+  const void* W;
+  const float* scale;
+  int K, M;
+  const float* x;
+  int x_stride;
+  const uint16_t* gain;
+  float eps;
+  int n_heads_q, n_heads_kv, head_dim;
+  const int* pos;           // device: position of input row 0 (row m is at pos + m)
+  const float2* rope;       // [positions][head_dim/2] (cos, sin)
+  float* q_out;
+  int q_stride;
+  uint16_t* kc;             // bf16 [n_kv][cache_len][head_dim]
+  uint16_t* vc;
+  int cache_len;
+};
+
+// Fused RMSNorm + W1/W3 GEMV + SiLU(a) * b.
+struct SwigluArgs {
+  const void* W1;
+  const float* s1;
+  const void* W3;
+  const float* s3;
+  int F, K, M;
+  const float* x;
+  int x_stride;
+  const uint16_t* gain;
+  float eps;
+  float* h;
+  int h_stride;
+};
+
+// Fused RMSNorm + head GEMV + argmax + frame bookkeeping (last workgroup).
+struct HeadArgs {
+  const void* W;
+  const float* scale;
+  int rows, K;
+  const float* x;           // one input row
+  const uint16_t* gain;
+  float eps;
+  float* logits;            // [rows]
+  unsigned long long* slot; // packed (value, index) maximum, reset by the last workgroup
+  unsigned* counter;        // arrival counter, reset by the last workgroup
+  int* anomalies;           // +1 per non-finite logit
+  int code_index;           // k in the frame
+  int frame_codes;          // 1 + n_res
+  int* pred;                // [frame_codes] argmax codes
+  int* committed;           // [frame_codes] codes the next steps consume
+  const int* forced;        // [frame_codes]
+  const int* force_flag;
+  int* ring;                // [max_len][frame_codes]
+  const int* pos;           // slow position of this frame
+  int* pos_inc;             // non-null: ++*pos_inc at the end (last head of the frame)
+  float* h_out;             // non-null: write the normalised input row here
+  const uint16_t* next_table; // non-null: next_x = next_table[code] (bf16 -> fp32)
+  int next_rows;
+  float* next_x;
+  const uint16_t* slow_table; // non-null: slow_x = slow_table[code] (next frame's slow input)
+  int slow_rows;
+  float* slow_x;
+};
+
+struct AttnArgs {
+  const float* q;
+  int q_stride;
+  const uint16_t* K;        // bf16 [n_kv][cache_len][head_dim]
+  const uint16_t* V;
+  int cache_len;
+  const int* pos;           // device: position of query row 0
+  int n_heads_q, n_heads_kv, head_dim;
+  int chunk;                // positions per split (multiple of 16)
+  int nsplit_max;           // grid.x
+  int M;
+  float* part;              // [M][n_kv][nsplit_max][group][head_dim + 2]
+  unsigned* counters;       // [M][n_kv], zero between launches
+  float* out;
+  int out_stride;
+};
+
+hipError_t launch_gemv(int wtype, const GemvArgs& a, hipStream_t s);
+hipError_t launch_qkv(int wtype, const QkvArgs& a, hipStream_t s);
+hipError_t launch_swiglu(int wtype, const SwigluArgs& a, hipStream_t s);
+hipError_t launch_head(int wtype, const HeadArgs& a, hipStream_t s);
+hipError_t launch_attn(const AttnArgs& a, hipStream_t s);
+
+// x = table[clamp(*tok)] as fp32, *pos_out = pos_value (prefill step input)
+hipError_t launch_embed(const uint16_t* table, int rows, int K, const int* tok, float* x,
+                        int* pos_out, int pos_value, int* anomalies, hipStream_t s);
+// forced (nullable) -> dst, *flag = forced != nullptr
+hipError_t launch_set_forced(const int* forced, int n, int* dst, int* flag, hipStream_t s);
+// dst[i] = value for i < n
+hipError_t launch_fill_i32(int* dst, int n, int value, hipStream_t s);
+hipError_t launch_fill_u32(unsigned* dst, size_t n, hipStream_t s);
+hipError_t launch_quantize_fp8(const uint16_t* w, int rows, int cols, uint8_t* q, float* scale,
+                               hipStream_t s);
+hipError_t launch_fp8_decode(const uint8_t* codes, int n, float* out, hipStream_t s);
+hipError_t launch_copy_i32(const int* src, int* dst, int n, hipStream_t s);
+
+size_t attn_partial_floats(int M, int n_kv, int nsplit_max, int group, int head_dim);
+
+}  // namespace dar

@@ -1,0 +1,943 @@
+// gfx950 kernels of the batch-1 Dual-AR decode frame.
+//
+// At batch 1 every projection is a matrix-vector product whose cost is the
+// weight stream from HBM (tuna-fish README, "Inference estimation": decode
+// time is parameters plus static KV over bandwidth). The kernels below are
+// built around that: 16-byte-per-lane coalesced weight loads issued in batches
+// before any arithmetic, fp32 accumulation, one 64-lane wave per row group
+// reduced with DPP, and the small per-token work (RMSNorm, RoPE, KV append,
+// residual add, SiLU*mul, argmax, the next step's embedding gather) folded into
+// the prologue or epilogue of the GEMV that needs it, so that a decoder layer is
+// five launches: QKV, attention, O-projection, W1/W3, W2.
+//
+// Weights: bf16 (two per 32-bit word) or float8_e4m3fn with one fp32 scale per
+// output row (s2-pro-fp8 model card, "Quantization Details"); the scale is
+// applied once to the finished dot product. Activations on the residual path
+// stay fp32; the slow and fast KV caches are bf16.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "dar_internal.h"
+
+namespace dar {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// ---------------------------------------------------------------- helpers --
+
+__device__ __forceinline__ float bf_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+__device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float(((uint32_t)h) << 16); }
+
+// fp32 -> bf16, round to nearest even; NaN stays NaN
+__device__ __forceinline__ uint16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// Sum within each 16-lane row, result in every lane of the row.
+template <int LANES>
+__device__ __forceinline__ float row_sum(float v) {
+  static_assert(LANES == 4 || LANES == 8 || LANES == 16, "row_sum lanes");
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));  // quad_perm 1,0,3,2
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true));  // quad_perm 2,3,0,1
+  if (LANES >= 8)
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, true));  // row_half_mirror
+  if (LANES >= 16)
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, true));  // row_mirror
+  return v;
+}
+
+__device__ __forceinline__ float readlane_f(float v, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
+// Full 64-lane sum, wave-uniform result.
+__device__ __forceinline__ float wave_sum(float v) {
+  v = row_sum<16>(v);
+  return (readlane_f(v, 0) + readlane_f(v, 16)) + (readlane_f(v, 32) + readlane_f(v, 48));
+}
+
+// Workgroup barrier that orders LDS only (outstanding global loads keep flying).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+__device__ __forceinline__ u32x4 ld16_nt(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+
+// ------------------------------------------------------- weight dot product --
+
+struct BF16 { static constexpr int kBytes = 2; };
+struct FP8 { static constexpr int kBytes = 1; };
+
+template <typename WT>
+struct Dot;
+
+template <>
+struct Dot<BF16> {
+  static constexpr int E = 8;  // elements per 16-byte load
+  __device__ static __forceinline__ float run(u32x4 w, const float* x) {
+    const float4 a = *reinterpret_cast<const float4*>(x);
+    const float4 b = *reinterpret_cast<const float4*>(x + 4);
+    float s0 = bf_lo(w.x) * a.x;
+    float s1 = bf_hi(w.x) * a.y;
+    s0 = fmaf(bf_lo(w.y), a.z, s0);
+    s1 = fmaf(bf_hi(w.y), a.w, s1);
+    s0 = fmaf(bf_lo(w.z), b.x, s0);
+    s1 = fmaf(bf_hi(w.z), b.y, s1);
+    s0 = fmaf(bf_lo(w.w), b.z, s0);
+    s1 = fmaf(bf_hi(w.w), b.w, s1);
+    return s0 + s1;
+  }
+};
+
+// e4m3fn -> fp32 through the gfx950 packed converter (OCP E4M3).
+__device__ __forceinline__ f32x2 fp8x2_lo(uint32_t u) { return __builtin_amdgcn_cvt_pk_f32_fp8((int)u, false); }
+__device__ __forceinline__ f32x2 fp8x2_hi(uint32_t u) { return __builtin_amdgcn_cvt_pk_f32_fp8((int)u, true); }
+
+template <>
+struct Dot<FP8> {
+  static constexpr int E = 16;
+  __device__ static __forceinline__ float word(uint32_t u, const float4 x, float s) {
+    const f32x2 lo = fp8x2_lo(u);
+    const f32x2 hi = fp8x2_hi(u);
+    s = fmaf(lo.x, x.x, s);
+    s = fmaf(lo.y, x.y, s);
+    s = fmaf(hi.x, x.z, s);
+    s = fmaf(hi.y, x.w, s);
+    return s;
+  }
+  __device__ static __forceinline__ float run(u32x4 w, const float* x) {
+    const float4* x4 = reinterpret_cast<const float4*>(x);
+    float s0 = word(w.x, x4[0], 0.f);
+    float s1 = word(w.y, x4[1], 0.f);
+    s0 = word(w.z, x4[2], s0);
+    s1 = word(w.w, x4[3], s1);
+    return s0 + s1;
+  }
+};
+
+// Streams RPW weight rows (K elements each, starting at base[i]) against M
+// input vectors staged in LDS (xs[m*K + j]). Lane l covers 16 bytes of every
+// 1024-byte chunk of a row. Chunks are fetched in batches of U per row, one
+// batch ahead of the arithmetic; the first batch is issued by start(), which
+// kernels call before their prologue so the HBM stream overlaps it. Lanes past
+// the row end load a clamped (valid) address and skip the arithmetic.
+template <typename WT, int M, int RPW>
+struct RowStream {
+  static constexpr int E = Dot<WT>::E;
+  static constexpr int CW = kWave * E;
+  static constexpr int U = (RPW >= 4) ? 2 : (8 / RPW);
+  const char* base[RPW];
+  int K, nchunks, lane;
+  u32x4 buf[U][RPW];
+
+  __device__ __forceinline__ void fetch(int c0, u32x4 (&w)[U][RPW]) const {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int col = min((c0 + u) * CW + lane * E, K - E);
+#pragma unroll
+      for (int i = 0; i < RPW; ++i) w[u][i] = ld16_nt(base[i] + (size_t)col * WT::kBytes);
+    }
+  }
+
+  __device__ __forceinline__ void start(const char* const (&rows)[RPW], int K_, int lane_) {
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) base[i] = rows[i];
+    K = K_;
+    lane = lane_;
+    nchunks = (K + CW - 1) / CW;
+    fetch(0, buf);
+  }
+
+  __device__ __forceinline__ void run(const float* xs, float (&acc)[RPW][M]) {
+#pragma unroll
+    for (int i = 0; i < RPW; ++i)
+#pragma unroll
+      for (int m = 0; m < M; ++m) acc[i][m] = 0.f;
+    for (int c0 = 0; c0 < nchunks; c0 += U) {
+      u32x4 nxt[U][RPW];
+      const bool more = c0 + U < nchunks;
+      if (more) fetch(c0 + U, nxt);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int col = (c0 + u) * CW + lane * E;
+        if ((c0 + u < nchunks) && (col < K)) {
+#pragma unroll
+          for (int m = 0; m < M; ++m) {
+#pragma unroll
+            for (int i = 0; i < RPW; ++i) acc[i][m] += Dot<WT>::run(buf[u][i], xs + m * K + col);
+          }
+        }
+      }
+      if (more) {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+          for (int i = 0; i < RPW; ++i) buf[u][i] = nxt[u][i];
+      }
+    }
+  }
+};
+
+// Stages M fp32 input rows into LDS, applying RMSNorm when a gain is given:
+// xs = x / sqrt(mean(x^2) + eps) * gain.
+// issue() loads this thread's share (up to NV float4 per row, at clamped
+// indices so the loads go out back to back) into registers; kernels call it
+// before starting their weight stream, so that waiting for these loads (memory
+// counters retire in issue order) never waits for weights. finish() reduces,
+// normalises and writes LDS. Rows longer than NV*1024 loop over the rest after
+// the first block.
+template <int M>
+struct Stager {
+  static constexpr int NV = 4;
+  static constexpr int SPAN = kBlock * 4 * NV;
+  float4 v[M][NV];
+  uint2 g2[NV];
+  const float* x;
+  const uint16_t* gain;
+  int x_stride, K;
+
+  __device__ __forceinline__ void load(int kb) {
+    const int tid = threadIdx.x;
+    const uint16_t* gsrc = gain ? gain : reinterpret_cast<const uint16_t*>(x);
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int kc = min(kb + (j * kBlock + tid) * 4, K - 4);
+#pragma unroll
+      for (int m = 0; m < M; ++m) v[m][j] = *reinterpret_cast<const float4*>(x + (size_t)m * x_stride + kc);
+      g2[j] = *reinterpret_cast<const uint2*>(gsrc + kc);
+    }
+  }
+
+  __device__ __forceinline__ void issue(const float* x_, int x_stride_, int K_, const uint16_t* gain_) {
+    x = x_;
+    x_stride = x_stride_;
+    K = K_;
+    gain = gain_;
+    load(0);
+  }
+
+  // sum of squares of the block at kb (already in registers); optionally store raw
+  __device__ __forceinline__ void absorb(float* xs, int kb, bool store_raw, float (&ss)[M]) {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int k = kb + (j * kBlock + tid) * 4;
+      if (k < K) {
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+          ss[m] += (v[m][j].x * v[m][j].x + v[m][j].y * v[m][j].y) + (v[m][j].z * v[m][j].z + v[m][j].w * v[m][j].w);
+          if (store_raw) *reinterpret_cast<float4*>(xs + m * K + k) = v[m][j];
+        }
+      }
+    }
+  }
+
+  __device__ __forceinline__ void finish(float* xs, float eps) {
+    __shared__ float red[M][kWaves];
+    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    const bool one_pass = K <= SPAN;
+    float ss[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) ss[m] = 0.f;
+    absorb(xs, 0, gain == nullptr || !one_pass, ss);
+    if (!one_pass) {
+      for (int kb = SPAN; kb < K; kb += SPAN) {
+        load(kb);
+        absorb(xs, kb, true, ss);
+      }
+    }
+    if (gain == nullptr) {
+      lds_barrier();
+      return;
+    }
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      const float t = wave_sum(ss[m]);
+      if (lane == 0) red[m][wave] = t;
+    }
+    lds_barrier();
+    float inv[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      float t = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) t += red[m][w];
+      inv[m] = 1.0f / sqrtf(t / (float)K + eps);
+    }
+    if (one_pass) {
+#pragma unroll
+      for (int j = 0; j < NV; ++j) {
+        const int k = (j * kBlock + tid) * 4;
+        if (k < K) {
+          const float g[4] = {bf_lo(g2[j].x), bf_hi(g2[j].x), bf_lo(g2[j].y), bf_hi(g2[j].y)};
+#pragma unroll
+          for (int m = 0; m < M; ++m) {
+            float4 r;
+            r.x = (v[m][j].x * inv[m]) * g[0];
+            r.y = (v[m][j].y * inv[m]) * g[1];
+            r.z = (v[m][j].z * inv[m]) * g[2];
+            r.w = (v[m][j].w * inv[m]) * g[3];
+            *reinterpret_cast<float4*>(xs + m * K + k) = r;
+          }
+        }
+      }
+    } else {
+      for (int k = tid * 4; k < K; k += kBlock * 4) {
+        const uint2 gg = *reinterpret_cast<const uint2*>(gain + k);
+        const float g[4] = {bf_lo(gg.x), bf_hi(gg.x), bf_lo(gg.y), bf_hi(gg.y)};
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+          float4* p = reinterpret_cast<float4*>(xs + m * K + k);
+          float4 r = *p;
+          r.x = (r.x * inv[m]) * g[0];
+          r.y = (r.y * inv[m]) * g[1];
+          r.z = (r.z * inv[m]) * g[2];
+          r.w = (r.w * inv[m]) * g[3];
+          *p = r;
+        }
+      }
+    }
+    lds_barrier();
+  }
+};
+
+template <typename WT>
+__device__ __forceinline__ const char* row_ptr(const void* W, int r, int K) {
+  return reinterpret_cast<const char*>(W) + (size_t)r * K * WT::kBytes;
+}
+
+// ------------------------------------------------------------------ GEMV --
+
+template <typename WT, int M, int RPW>
+__global__ __launch_bounds__(kBlock) void k_gemv(GemvArgs a) {
+  extern __shared__ __align__(16) float xs[];
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int r0 = (blockIdx.x * kWaves + wave) * RPW;
+  const bool active = r0 < a.rows;
+  Stager<M> st;
+  st.issue(a.x, a.x_stride, a.K, a.gain);
+  // every wave streams (inactive ones a clamped row): no branch around the
+  // prefetch, so the staging wait above stays exact
+  RowStream<WT, M, RPW> rs;
+  {
+    const char* base[RPW];
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) base[i] = row_ptr<WT>(a.W, min(r0 + i, a.rows - 1), a.K);
+    rs.start(base, a.K, lane);
+  }
+  st.finish(xs, a.eps);
+  if (!active) return;
+  float acc[RPW][M];
+  rs.run(xs, acc);
+#pragma unroll
+  for (int i = 0; i < RPW; ++i) {
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      float s = wave_sum(acc[i][m]);
+      const int r = r0 + i;
+      if (lane == 0 && r < a.rows) {
+        if (a.scale) s *= a.scale[r];
+        float* y = a.y + (size_t)m * a.y_stride + r;
+        *y = a.accumulate ? (*y + s) : s;
+      }
+    }
+  }
+}
+
+// --------------------------------------------------- RMSNorm+QKV+RoPE+KV --
+
+// Wave w handles rotation pairs (head, i) and (head, i + hd/2) so RoPE is
+// applied where both halves are known. Pair p: head = p / (hd/2), i = p % (hd/2).
+template <typename WT, int M>
+__global__ __launch_bounds__(kBlock) void k_qkv(QkvArgs a) {
+  extern __shared__ __align__(16) float xs[];
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int half = a.head_dim / 2;
+  const int n_heads = a.n_heads_q + 2 * a.n_heads_kv;
+  const int p = blockIdx.x * kWaves + wave;
+  const bool active = p < n_heads * half;
+  const int pc = min(p, n_heads * half - 1);
+  const int head = pc / half, i = pc % half;
+  const int r1 = head * a.head_dim + i, r2 = r1 + half;
+  Stager<M> st;
+  st.issue(a.x, a.x_stride, a.K, a.gain);
+  RowStream<WT, M, 2> rs;
+  {
+    const char* base[2] = {row_ptr<WT>(a.W, r1, a.K), row_ptr<WT>(a.W, r2, a.K)};
+    rs.start(base, a.K, lane);
+  }
+  st.finish(xs, a.eps);
+  if (!active) return;
+  float acc[2][M];
+  rs.run(xs, acc);
+  float y1[M], y2[M];
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    y1[m] = wave_sum(acc[0][m]);
+    y2[m] = wave_sum(acc[1][m]);
+  }
+  if (lane != 0) return;
+  const float sc1 = a.scale ? a.scale[r1] : 1.f, sc2 = a.scale ? a.scale[r2] : 1.f;
+  const int pos0 = *a.pos;
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    const float u = y1[m] * sc1, v = y2[m] * sc2;
+    const int pos = pos0 + m;
+    if (head < a.n_heads_q + a.n_heads_kv) {
+      const float2 cs = a.rope[(size_t)pos * half + i];
+      const float o1 = u * cs.x - v * cs.y;
+      const float o2 = u * cs.y + v * cs.x;
+      if (head < a.n_heads_q) {
+        a.q_out[(size_t)m * a.q_stride + r1] = o1;
+        a.q_out[(size_t)m * a.q_stride + r2] = o2;
+      } else {
+        uint16_t* kp = a.kc + ((size_t)(head - a.n_heads_q) * a.cache_len + pos) * a.head_dim;
+        kp[i] = f2bf(o1);
+        kp[i + half] = f2bf(o2);
+      }
+    } else {
+      uint16_t* vp = a.vc + ((size_t)(head - a.n_heads_q - a.n_heads_kv) * a.cache_len + pos) * a.head_dim;
+      vp[i] = f2bf(u);
+      vp[i + half] = f2bf(v);
+    }
+  }
+}
+
+// ------------------------------------------------ RMSNorm + W1/W3 + SwiGLU --
+
+template <typename WT, int M>
+__global__ __launch_bounds__(kBlock) void k_swiglu(SwigluArgs a) {
+  extern __shared__ __align__(16) float xs[];
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int r = blockIdx.x * kWaves + wave;
+  const bool active = r < a.F;
+  Stager<M> st;
+  st.issue(a.x, a.x_stride, a.K, a.gain);
+  RowStream<WT, M, 2> rs;
+  {
+    const int rc = min(r, a.F - 1);
+    const char* base[2] = {row_ptr<WT>(a.W1, rc, a.K), row_ptr<WT>(a.W3, rc, a.K)};
+    rs.start(base, a.K, lane);
+  }
+  st.finish(xs, a.eps);
+  if (!active) return;
+  float acc[2][M];
+  rs.run(xs, acc);
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    float g = wave_sum(acc[0][m]);
+    float u = wave_sum(acc[1][m]);
+    if (lane == 0) {
+      if (a.s1) g *= a.s1[r];
+      if (a.s3) u *= a.s3[r];
+      const float silu = g / (1.0f + expf(-g));
+      a.h[(size_t)m * a.h_stride + r] = silu * u;
+    }
+  }
+}
+
+// ----------------------------------------- RMSNorm + head + argmax + commit --
+
+// Order-preserving key: larger float -> larger key; NaN -> smallest key.
+__device__ __forceinline__ unsigned long long argmax_key(float v, int idx) {
+  uint32_t u = __float_as_uint(v);
+  uint32_t k;
+  if (v != v) {
+    k = 0u;
+  } else {
+    k = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  }
+  return ((unsigned long long)k << 32) | (unsigned long long)(0xffffffffu - (uint32_t)idx);
+}
+
+template <typename WT>
+__global__ __launch_bounds__(kBlock) void k_head(HeadArgs a) {
+  extern __shared__ __align__(16) float xs[];
+  __shared__ unsigned long long wbest[kWaves];
+  __shared__ int last;
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  constexpr int RPW = 2;
+  const int r0 = (blockIdx.x * kWaves + wave) * RPW;
+  Stager<1> st;
+  st.issue(a.x, a.K, a.K, a.gain);
+  RowStream<WT, 1, RPW> rs;
+  {
+    const char* base[RPW];
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) base[i] = row_ptr<WT>(a.W, min(r0 + i, a.rows - 1), a.K);
+    rs.start(base, a.K, lane);
+  }
+  st.finish(xs, a.eps);
+  unsigned long long best = 0ull;
+  if (r0 < a.rows) {
+    float acc[RPW][1];
+    rs.run(xs, acc);
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+      float s = wave_sum(acc[i][0]);
+      const int r = r0 + i;
+      if (r < a.rows) {
+        if (a.scale) s *= a.scale[r];
+        if (lane == 0) {
+          a.logits[r] = s;
+          if (!isfinite(s)) atomicAdd(a.anomalies, 1);
+        }
+        const unsigned long long k = argmax_key(s, r);
+        best = k > best ? k : best;
+      }
+    }
+  }
+  if (lane == 0) wbest[wave] = best;
+  __syncthreads();
+  if (tid == 0) {
+    unsigned long long b = wbest[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) b = wbest[w] > b ? wbest[w] : b;
+    atomicMax(a.slot, b);
+    __threadfence();
+    const unsigned prev = atomicAdd(a.counter, 1u);
+    last = (prev == gridDim.x - 1);
+  }
+  __syncthreads();
+  if (!last) return;
+  __threadfence();
+  // Last workgroup: every logit and the maximum are in place.
+  __shared__ int code_sh;
+  if (tid == 0) {
+    const unsigned long long key = atomicAdd(a.slot, 0ull);
+    const int pred = (int)(0xffffffffu - (uint32_t)(key & 0xffffffffull));
+    const int code = (*a.force_flag) ? a.forced[a.code_index] : pred;
+    a.pred[a.code_index] = pred;
+    a.committed[a.code_index] = code;
+    a.ring[(size_t)(*a.pos) * a.frame_codes + a.code_index] = code;
+    code_sh = code;
+    *a.slot = 0ull;
+    *a.counter = 0u;
+  }
+  __syncthreads();
+  const int code = code_sh;
+  if (a.h_out) {
+    for (int k = tid; k < a.K; k += kBlock) a.h_out[k] = xs[k];
+  }
+  if (a.next_table) {
+    const int c = min(max(code, 0), a.next_rows - 1);
+    const uint16_t* row = a.next_table + (size_t)c * a.K;
+    for (int k = tid; k < a.K; k += kBlock) a.next_x[k] = bf2f(row[k]);
+  }
+  if (a.slow_table) {
+    const int c = min(max(code, 0), a.slow_rows - 1);
+    const uint16_t* row = a.slow_table + (size_t)c * a.K;
+    for (int k = tid; k < a.K; k += kBlock) a.slow_x[k] = bf2f(row[k]);
+  }
+  if (a.pos_inc && tid == 0) *a.pos_inc = *a.pos_inc + 1;
+}
+
+// ------------------------------------------------ split-K decode attention --
+
+// One workgroup = one KV head x one split of `chunk` positions for one query
+// row. hd/8 lanes cover one key row (16 bytes each); a wave covers 64/(hd/8)
+// positions per step and keeps an online softmax per lane group; groups and
+// waves are merged at the end, the split's (max, sum, acc) is written, and the
+// last split to finish for that head combines all splits into the output.
+template <int HD, int G>
+__global__ __launch_bounds__(kBlock) void k_attn(AttnArgs a) {
+  constexpr int LPP = HD / 8;
+  constexpr int PPW = kWave / LPP;
+  constexpr int U = 2;
+  const int s = blockIdx.x, kvh = blockIdx.y, m = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int T = *a.pos + m + 1;
+  const int nsplit = (T + a.chunk - 1) / a.chunk;
+  if (s >= nsplit) return;
+  const int j0 = s * a.chunk, j1 = min(T, j0 + a.chunk);
+  const int grp = lane / LPP, sub = lane % LPP;
+
+  const float qscale = 1.4426950408889634f / sqrtf((float)HD);  // log2(e)/sqrt(hd)
+  float qv[G][8];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const float* qp = a.q + (size_t)m * a.q_stride + (kvh * G + h) * HD + sub * 8;
+    const float4 q0 = *reinterpret_cast<const float4*>(qp);
+    const float4 q1 = *reinterpret_cast<const float4*>(qp + 4);
+    qv[h][0] = q0.x * qscale; qv[h][1] = q0.y * qscale; qv[h][2] = q0.z * qscale; qv[h][3] = q0.w * qscale;
+    qv[h][4] = q1.x * qscale; qv[h][5] = q1.y * qscale; qv[h][6] = q1.z * qscale; qv[h][7] = q1.w * qscale;
+  }
+  float mx[G], l[G], acc[G][8];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    mx[h] = -INFINITY;
+    l[h] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+  }
+  const uint16_t* Kb = a.K + (size_t)kvh * a.cache_len * HD + sub * 8;
+  const uint16_t* Vb = a.V + (size_t)kvh * a.cache_len * HD + sub * 8;
+  constexpr int STEP = kWaves * PPW;
+  for (int jb = j0 + wave * PPW; jb < j1; jb += STEP * U) {
+    u32x4 kk[U], vv[U];
+    bool ok[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int j = jb + u * STEP + grp;
+      ok[u] = j < j1;
+      kk[u] = ok[u] ? ld16(Kb + (size_t)j * HD) : u32x4{0u, 0u, 0u, 0u};
+      vv[u] = ok[u] ? ld16(Vb + (size_t)j * HD) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float kf[8] = {bf_lo(kk[u].x), bf_hi(kk[u].x), bf_lo(kk[u].y), bf_hi(kk[u].y),
+                           bf_lo(kk[u].z), bf_hi(kk[u].z), bf_lo(kk[u].w), bf_hi(kk[u].w)};
+      const float vf[8] = {bf_lo(vv[u].x), bf_hi(vv[u].x), bf_lo(vv[u].y), bf_hi(vv[u].y),
+                           bf_lo(vv[u].z), bf_hi(vv[u].z), bf_lo(vv[u].w), bf_hi(vv[u].w)};
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float sc = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sc = fmaf(qv[h][e], kf[e], sc);
+        sc = row_sum<LPP>(sc);
+        if (ok[u]) {
+          const float mn = fmaxf(mx[h], sc);
+          const float corr = exp2f(mx[h] - mn);
+          const float pr = exp2f(sc - mn);
+          l[h] = l[h] * corr + pr;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(pr, vf[e], acc[h][e] * corr);
+          mx[h] = mn;
+        }
+      }
+    }
+  }
+  // merge the PPW lane groups of this wave (xor over the group bits of the lane id)
+#pragma unroll
+  for (int off = LPP; off < kWave; off <<= 1) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float mo = __shfl_xor(mx[h], off);
+      const float lo = __shfl_xor(l[h], off);
+      const float mn = fmaxf(mx[h], mo);
+      const float ca = (mx[h] == -INFINITY) ? 0.f : exp2f(mx[h] - mn);
+      const float cb = (mo == -INFINITY) ? 0.f : exp2f(mo - mn);
+      l[h] = l[h] * ca + lo * cb;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float ao = __shfl_xor(acc[h][e], off);
+        acc[h][e] = acc[h][e] * ca + ao * cb;
+      }
+      mx[h] = mn;
+    }
+  }
+  // merge the waves through LDS
+  __shared__ float sm_acc[kWaves][G][HD];
+  __shared__ float sm_ml[kWaves][G][2];
+  if (grp == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sm_acc[wave][h][sub * 8 + e] = acc[h][e];
+      if (sub == 0) {
+        sm_ml[wave][h][0] = mx[h];
+        sm_ml[wave][h][1] = l[h];
+      }
+    }
+  }
+  __syncthreads();
+  const int stride_s = G * (HD + 2);
+  float* part = a.part + (((size_t)m * a.n_heads_kv + kvh) * a.nsplit_max) * stride_s;
+  for (int idx = tid; idx < G * HD; idx += kBlock) {
+    const int h = idx / HD, e = idx % HD;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_ml[w][h][0]);
+    float num = 0.f, den = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float mw = sm_ml[w][h][0];
+      const float c = (mw == -INFINITY) ? 0.f : exp2f(mw - M);
+      num += sm_acc[w][h][e] * c;
+      den += sm_ml[w][h][1] * c;
+    }
+    float* ps = part + (size_t)s * stride_s + h * (HD + 2);
+    ps[e] = num;
+    if (e == 0) {
+      ps[HD] = M;
+      ps[HD + 1] = den;
+    }
+  }
+  __shared__ int last;
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) {
+    const unsigned prev = atomicAdd(a.counters + m * a.n_heads_kv + kvh, 1u);
+    last = (prev == (unsigned)(nsplit - 1));
+  }
+  __syncthreads();
+  if (!last) return;
+  __threadfence();
+  for (int idx = tid; idx < G * HD; idx += kBlock) {
+    const int h = idx / HD, e = idx % HD;
+    float M = -INFINITY;
+    for (int t = 0; t < nsplit; ++t) M = fmaxf(M, part[(size_t)t * stride_s + h * (HD + 2) + HD]);
+    float num = 0.f, den = 0.f;
+    for (int t = 0; t < nsplit; ++t) {
+      const float* ps = part + (size_t)t * stride_s + h * (HD + 2);
+      const float c = exp2f(ps[HD] - M);
+      num += ps[e] * c;
+      den += ps[HD + 1] * c;
+    }
+    a.out[(size_t)m * a.out_stride + (kvh * G + h) * HD + e] = num / den;
+  }
+  if (tid == 0) a.counters[m * a.n_heads_kv + kvh] = 0u;
+}
+
+// ---------------------------------------------------------- small kernels --
+
+__global__ void k_embed(const uint16_t* table, int rows, int K, const int* tok, float* x, int* pos_out,
+                        int pos_value, int* anomalies) {
+  const int t = *tok;
+  const int c = min(max(t, 0), rows - 1);
+  if (threadIdx.x == 0 && blockIdx.x == 0) {
+    if (t != c) atomicAdd(anomalies, 1);
+    if (pos_out) *pos_out = pos_value;
+  }
+  const uint16_t* row = table + (size_t)c * K;
+  for (int k = blockIdx.x * blockDim.x + threadIdx.x; k < K; k += gridDim.x * blockDim.x) x[k] = bf2f(row[k]);
+}
+
+__global__ void k_set_forced(const int* forced, int n, int* dst, int* flag) {
+  const int i = threadIdx.x;
+  if (forced && i < n) dst[i] = forced[i];
+  if (i == 0) *flag = forced ? 1 : 0;
+}
+
+__global__ void k_fill_i32(int* dst, int n, int value) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) dst[i] = value;
+}
+
+__global__ void k_fill_u32(unsigned* dst, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+    dst[i] = 0u;
+}
+
+__global__ void k_copy_i32(const int* src, int* dst, int n) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) dst[i] = src[i];
+}
+
+// e4m3fn encode of a finite fp32 value: nearest, ties to even, saturate at 448.
+// Every step is exact in fp32 (scaling by powers of two), so the result is the
+// correctly rounded code.
+__device__ __forceinline__ uint8_t e4m3_encode(float x) {
+  const uint32_t sign = (__float_as_uint(x) >> 24) & 0x80u;
+  const float a = fabsf(x);
+  uint32_t code;
+  if (a >= 448.0f) {
+    code = 0x7Eu;
+  } else if (a < 0.015625f) {  // below 2^-6: subnormal step 2^-9
+    code = (uint32_t)rintf(a * 512.0f);  // 8 here is the smallest normal's code
+  } else {
+    int e = (int)((__float_as_uint(a) >> 23) & 0xffu) - 127;  // a normal fp32 here
+    const float mant = __uint_as_float(__float_as_uint(a) & 0x807fffffu | 0x3f800000u) - 1.0f;
+    uint32_t mq = (uint32_t)rintf(mant * 8.0f);
+    if (mq == 8u) {
+      mq = 0u;
+      e += 1;
+    }
+    code = ((uint32_t)(e + 7) << 3) | mq;
+    if (code > 0x7Eu) code = 0x7Eu;
+  }
+  return (uint8_t)(code | sign);
+}
+
+// One workgroup per row: scale = rowmax|w| / 448, codes = e4m3(w / scale).
+__global__ __launch_bounds__(kBlock) void k_quantize_fp8(const uint16_t* w, int rows, int cols, uint8_t* q,
+                                                        float* scale) {
+  __shared__ float red[kWaves];
+  const int r = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const uint16_t* row = w + (size_t)r * cols;
+  float mx = 0.f;
+  for (int k = tid; k < cols; k += kBlock) mx = fmaxf(mx, fabsf(bf2f(row[k])));
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+  if (lane == 0) red[wave] = mx;
+  __syncthreads();
+  float amax = red[0];
+#pragma unroll
+  for (int i = 1; i < kWaves; ++i) amax = fmaxf(amax, red[i]);
+  const float s = amax / 448.0f;
+  if (tid == 0) scale[r] = s;
+  uint8_t* qr = q + (size_t)r * cols;
+  for (int k = tid; k < cols; k += kBlock) {
+    qr[k] = (s > 0.f) ? e4m3_encode(bf2f(row[k]) / s) : (uint8_t)0;
+  }
+}
+
+__global__ void k_fp8_decode(const uint8_t* codes, int n, float* out) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) {
+    const uint32_t u = codes[i];
+    out[i] = fp8x2_lo(u).x;
+  }
+}
+
+// ---------------------------------------------------------------- launchers --
+
+static size_t lds_bytes(int M, int K) { return (size_t)M * K * sizeof(float); }
+
+template <typename KernelT>
+static hipError_t prep(KernelT kern, size_t lds) {
+  if (lds > 64 * 1024) {
+    return hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                               (int)lds);
+  }
+  return hipSuccess;
+}
+
+template <typename WT, int M>
+static hipError_t gemv_impl(const GemvArgs& a, hipStream_t s) {
+  constexpr int RPW = 2;
+  auto kern = k_gemv<WT, M, RPW>;
+  const size_t lds = lds_bytes(M, a.K);
+  hipError_t e = prep(kern, lds);
+  if (e != hipSuccess) return e;
+  const int grid = (a.rows + kWaves * RPW - 1) / (kWaves * RPW);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kBlock), lds, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemv(int wtype, const GemvArgs& a, hipStream_t s) {
+  if (wtype == W_FP8) return a.M == 1 ? gemv_impl<FP8, 1>(a, s) : gemv_impl<FP8, 2>(a, s);
+  return a.M == 1 ? gemv_impl<BF16, 1>(a, s) : gemv_impl<BF16, 2>(a, s);
+}
+
+template <typename WT, int M>
+static hipError_t qkv_impl(const QkvArgs& a, hipStream_t s) {
+  auto kern = k_qkv<WT, M>;
+  const size_t lds = lds_bytes(M, a.K);
+  hipError_t e = prep(kern, lds);
+  if (e != hipSuccess) return e;
+  const int pairs = (a.n_heads_q + 2 * a.n_heads_kv) * a.head_dim / 2;
+  const int grid = (pairs + kWaves - 1) / kWaves;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kBlock), lds, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_qkv(int wtype, const QkvArgs& a, hipStream_t s) {
+  if (wtype == W_FP8) return a.M == 1 ? qkv_impl<FP8, 1>(a, s) : qkv_impl<FP8, 2>(a, s);
+  return a.M == 1 ? qkv_impl<BF16, 1>(a, s) : qkv_impl<BF16, 2>(a, s);
+}
+
+template <typename WT, int M>
+static hipError_t swiglu_impl(const SwigluArgs& a, hipStream_t s) {
+  auto kern = k_swiglu<WT, M>;
+  const size_t lds = lds_bytes(M, a.K);
+  hipError_t e = prep(kern, lds);
+  if (e != hipSuccess) return e;
+  const int grid = (a.F + kWaves - 1) / kWaves;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kBlock), lds, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_swiglu(int wtype, const SwigluArgs& a, hipStream_t s) {
+  if (wtype == W_FP8) return a.M == 1 ? swiglu_impl<FP8, 1>(a, s) : swiglu_impl<FP8, 2>(a, s);
+  return a.M == 1 ? swiglu_impl<BF16, 1>(a, s) : swiglu_impl<BF16, 2>(a, s);
+}
+
+template <typename WT>
+static hipError_t head_impl(const HeadArgs& a, hipStream_t s) {
+  auto kern = k_head<WT>;
+  const size_t lds = lds_bytes(1, a.K);
+  hipError_t e = prep(kern, lds);
+  if (e != hipSuccess) return e;
+  const int grid = (a.rows + kWaves * 2 - 1) / (kWaves * 2);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kBlock), lds, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_head(int wtype, const HeadArgs& a, hipStream_t s) {
+  return wtype == W_FP8 ? head_impl<FP8>(a, s) : head_impl<BF16>(a, s);
+}
+
+template <int HD, int G>
+static hipError_t attn_impl(const AttnArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL((k_attn<HD, G>), dim3(a.nsplit_max, a.n_heads_kv, a.M), dim3(kBlock), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
+  const int g = a.n_heads_q / a.n_heads_kv;
+  if (a.head_dim == 128) {
+    switch (g) {
+      case 1: return attn_impl<128, 1>(a, s);
+      case 2: return attn_impl<128, 2>(a, s);
+      case 4: return attn_impl<128, 4>(a, s);
+      case 8: return attn_impl<128, 8>(a, s);
+    }
+  } else if (a.head_dim == 64) {
+    switch (g) {
+      case 1: return attn_impl<64, 1>(a, s);
+      case 2: return attn_impl<64, 2>(a, s);
+      case 4: return attn_impl<64, 4>(a, s);
+      case 8: return attn_impl<64, 8>(a, s);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+size_t attn_partial_floats(int M, int n_kv, int nsplit_max, int group, int head_dim) {
+  return (size_t)M * n_kv * nsplit_max * group * (head_dim + 2);
+}
+
+hipError_t launch_embed(const uint16_t* table, int rows, int K, const int* tok, float* x, int* pos_out,
+                        int pos_value, int* anomalies, hipStream_t s) {
+  const int grid = (K + kBlock - 1) / kBlock;
+  hipLaunchKernelGGL(k_embed, dim3(grid), dim3(kBlock), 0, s, table, rows, K, tok, x, pos_out, pos_value,
+                     anomalies);
+  return hipGetLastError();
+}
+
+hipError_t launch_set_forced(const int* forced, int n, int* dst, int* flag, hipStream_t s) {
+  hipLaunchKernelGGL(k_set_forced, dim3(1), dim3(64), 0, s, forced, n, dst, flag);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_i32(int* dst, int n, int value, hipStream_t s) {
+  const int grid = n > 0 ? (n + kBlock - 1) / kBlock : 1;
+  hipLaunchKernelGGL(k_fill_i32, dim3(grid < 1024 ? grid : 1024), dim3(kBlock), 0, s, dst, n, value);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_u32(unsigned* dst, size_t n, hipStream_t s) {
+  size_t grid = n > 0 ? (n + kBlock - 1) / kBlock : 1;
+  if (grid > 4096) grid = 4096;
+  hipLaunchKernelGGL(k_fill_u32, dim3((unsigned)grid), dim3(kBlock), 0, s, dst, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_i32(const int* src, int* dst, int n, hipStream_t s) {
+  const int grid = n > 0 ? (n + kBlock - 1) / kBlock : 1;
+  hipLaunchKernelGGL(k_copy_i32, dim3(grid < 1024 ? grid : 1024), dim3(kBlock), 0, s, src, dst, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_fp8(const uint16_t* w, int rows, int cols, uint8_t* q, float* scale, hipStream_t s) {
+  hipLaunchKernelGGL(k_quantize_fp8, dim3(rows), dim3(kBlock), 0, s, w, rows, cols, q, scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_fp8_decode(const uint8_t* codes, int n, float* out, hipStream_t s) {
+  hipLaunchKernelGGL(k_fp8_decode, dim3((n + kBlock - 1) / kBlock), dim3(kBlock), 0, s, codes, n, out);
+  return hipGetLastError();
+}
+
+}  // namespace dar

@@ -1,0 +1,175 @@
+"""A decode session over the C ABI, with torch providing device memory and the stream.
+
+DeviceWeights uploads canonical bf16 weights (uint16 bit arrays) and, for the
+fp8 mode, quantises every Linear matrix on the device with
+dar_quantize_fp8_rows. DarSession owns the workspace and the dar_ctx and wraps
+prefill / decode_frame with torch tensors. Everything here is marshalling:
+pointers, sizes and buffers; the arithmetic runs in libdar.so.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import numpy as np
+import torch
+
+from . import native as N
+
+LINEAR_SUFFIXES = ("wqkv", "wo", "w1", "w3", "w2")
+
+
+def _dev(t):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+class DeviceWeights:
+    """Device copies of the canonical tensors; fp8 mode adds codes and row scales."""
+
+    def __init__(self, dims, host_tensors: dict, wtype: str = "bf16", device="cuda", stream=None,
+                 keep_bf16_linears: bool = False):
+        self.dims = dims
+        self.wtype = wtype
+        self.t = {}
+        self.scale = {}
+        s = stream if stream is not None else torch.cuda.current_stream(device)
+        sp = ctypes.c_void_p(s.cuda_stream)
+        for name, bits in host_tensors.items():
+            arr = np.ascontiguousarray(bits).view(np.int16)
+            dev = torch.from_numpy(arr).to(device, non_blocking=False)
+            if wtype == "fp8" and self.is_linear(name):
+                rows, cols = dev.shape
+                q = torch.empty((rows, cols), dtype=torch.uint8, device=device)
+                sc = torch.empty((rows,), dtype=torch.float32, device=device)
+                with torch.cuda.stream(s):
+                    N.dar_quantize_fp8_rows(_dev(dev), rows, cols, _dev(q), _dev(sc), sp)
+                self.t[name] = q
+                self.scale[name] = sc
+                if keep_bf16_linears:
+                    self.t[name + ".bf16"] = dev
+                else:
+                    s.synchronize()
+                    del dev
+            else:
+                self.t[name] = dev
+        s.synchronize()
+
+    @staticmethod
+    def is_linear(name):
+        return name == "fast.head" or name.split(".")[-1] in LINEAR_SUFFIXES
+
+    def ptr(self, name):
+        return self.t[name].data_ptr()
+
+    def sptr(self, name):
+        return self.scale[name].data_ptr() if name in self.scale else None
+
+    def layer_struct(self, prefix):
+        L = N.dar_layer_weights()
+        L.attn_norm = self.ptr(f"{prefix}.attn_norm")
+        L.ffn_norm = self.ptr(f"{prefix}.ffn_norm")
+        for m in LINEAR_SUFFIXES:
+            setattr(L, m, self.ptr(f"{prefix}.{m}"))
+            setattr(L, f"{m}_scale", self.sptr(f"{prefix}.{m}"))
+        return L
+
+    def struct(self):
+        d = self.dims
+        W = N.dar_weights()
+        W.w0 = self.ptr("w0")
+        slow = (N.dar_layer_weights * d.n_layers_slow)(*[self.layer_struct(f"slow.{i}") for i in range(d.n_layers_slow)])
+        W.slow = slow
+        W.slow_final_norm = self.ptr("slow.final_norm")
+        keep = [slow]
+        if d.n_res > 0:
+            emb = (ctypes.c_void_p * d.n_res)(*[self.ptr(f"fast.emb.{k}") for k in range(d.n_res)])
+            fast = (N.dar_layer_weights * d.n_layers_fast)(*[self.layer_struct(f"fast.{i}") for i in range(d.n_layers_fast)])
+            W.fast_emb = emb
+            W.fast = fast
+            W.fast_final_norm = self.ptr("fast.final_norm")
+            W.fast_head = self.ptr("fast.head")
+            W.fast_head_scale = self.sptr("fast.head")
+            keep += [emb, fast]
+        return W, keep
+
+
+class DarSession:
+    """One dar_ctx: workspace, stream, prefill and frame decode with torch tensors."""
+
+    def __init__(self, dims, weights: DeviceWeights, max_len: int, device="cuda", stream=None, graph=True):
+        self.dims = dims
+        self.max_len = max_len
+        self.device = device
+        self.stream = stream if stream is not None else torch.cuda.Stream(device)
+        self.cfg = N.make_config(dims, max_len, weights.wtype)
+        nbytes = N.dar_workspace_bytes(self.cfg)
+        self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        self.weights = weights
+        wstruct, self._keep = weights.struct()
+        self.ctx = N.dar_create(self.cfg, wstruct, ctypes.c_void_p(self.workspace.data_ptr()), nbytes,
+                                ctypes.c_void_p(self.stream.cuda_stream))
+        N.dar_set_graph(self.ctx, graph)
+        self.fc = dims.n_res + 1
+        self.vmax = max(dims.vocab_c0, dims.vocab_res if dims.n_res > 0 else 0)
+        self.codes = torch.zeros(self.fc, dtype=torch.int32, device=device)
+        self.logits = torch.zeros(self.fc, self.vmax, dtype=torch.float32, device=device)
+        self.forced = torch.zeros(self.fc, dtype=torch.int32, device=device)
+
+    def close(self):
+        if self.ctx:
+            N.dar_destroy(self.ctx)
+            self.ctx = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def _forced_ptr(self, forced):
+        if forced is None:
+            return None
+        f = torch.as_tensor(np.asarray(forced, dtype=np.int32))
+        with torch.cuda.stream(self.stream):
+            self.forced.copy_(f.to(self.device, non_blocking=False))
+        return _dev(self.forced)
+
+    def prefill(self, tokens, forced=None, want=True):
+        toks = torch.as_tensor(np.asarray(tokens, dtype=np.int32)).to(self.device)
+        torch.cuda.current_stream(self.device).synchronize()
+        fp = self._forced_ptr(forced)
+        N.dar_prefill(self.ctx, 1, _dev(toks), [len(tokens)], fp, _dev(self.codes) if want else None,
+                      _dev(self.logits) if want else None)
+        self._toks = toks
+        return self._out(want)
+
+    def decode_frame(self, forced=None, want=True):
+        fp = self._forced_ptr(forced)
+        N.dar_decode_frame(self.ctx, fp, _dev(self.codes) if want else None, _dev(self.logits) if want else None)
+        return self._out(want)
+
+    def _out(self, want):
+        if not want:
+            return None
+        self.stream.synchronize()
+        return self.codes.cpu().numpy().copy(), self.logits.cpu().numpy().copy()
+
+    def ring(self, first, count):
+        dst = torch.zeros(count, self.fc, dtype=torch.int32, device=self.device)
+        N.dar_codes(self.ctx, first, count, _dev(dst))
+        self.stream.synchronize()
+        return dst.cpu().numpy()
+
+    def position(self):
+        return N.dar_position(self.ctx)[0]
+
+    def reset(self):
+        N.dar_reset(self.ctx)
+
+    def set_graph(self, enable):
+        N.dar_set_graph(self.ctx, enable)
+
+    def nonfinite(self):
+        return N.dar_nonfinite(self.ctx)
+
+    def profile_frame(self):
+        return N.dar_profile_frame(self.ctx)

@@ -1,0 +1,236 @@
+/*
+ * dar.h - C ABI of libdar.so: the batch-1 Dual-AR (RQ-Transformer) decode frame
+ * on AMD Instinct MI355X (gfx950).
+ *
+ * What a frame is (tuna-fish README, intro and "Inference estimation"; groxaxo
+ * fork README, architecture paragraph; s2-pro-fp8 model card, "Architecture"):
+ * one slow-AR token runs through the slow decoder layers against the slow KV
+ * cache, the codebook-0 head picks codebook 0 by argmax, then the fast AR runs
+ * along depth and emits the residual codebooks one after another, each through
+ * the fast layers and a shared head. A frame is 1 + n_res codes. Greedy argmax
+ * everywhere (first index among equal maxima).
+ *
+ * The layer is a pre-RMSNorm decoder block with rotary position embedding and
+ * grouped-query attention (pyshine fish-speech tour, "Why You Need This"),
+ * SwiGLU FFN, no biases. Weights are bf16, or per-row symmetric
+ * float8_e4m3fn with one fp32 scale per output row for every Linear matrix
+ * (s2-pro-fp8 model card, "What is this?" and "Quantization Details");
+ * tables and norm gains stay bf16 in both modes.
+ *
+ * Conventions for every entry point:
+ *  - Return value: DAR_OK (0) or a negative dar_status. No exceptions cross
+ *    the ABI. On DAR_E_HIP the HIP error text is kept in dar_last_error().
+ *  - "device" pointers are HIP device memory; "host" pointers are CPU memory.
+ *  - Work is stream-ordered on the stream given to dar_create; nothing blocks
+ *    the host unless stated. Device outputs are valid after the caller
+ *    synchronises that stream.
+ *  - Argument checks (null pointers, shapes, alignment, state, capacity)
+ *    happen on the host before any HIP call; a failed check changes nothing.
+ *  - One dar_ctx is used from one host thread at a time.
+ */
+#ifndef DAR_H_
+#define DAR_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DAR_ABI_VERSION 1
+
+typedef enum {
+  DAR_OK = 0,
+  DAR_E_INVAL = -1,       /* null pointer, bad shape or alignment, id out of range */
+  DAR_E_STATE = -2,       /* decode before prefill, use of a destroyed context     */
+  DAR_E_CAPACITY = -3,    /* position would reach max_len, batch > max_batch        */
+  DAR_E_HIP = -4,         /* a HIP runtime call failed (text in dar_last_error)     */
+  DAR_E_WORKSPACE = -5,   /* workspace smaller than dar_workspace_bytes()           */
+  DAR_E_UNSUPPORTED = -6  /* valid but not implemented shape or mode                */
+} dar_status;
+
+typedef enum {
+  DAR_WTYPE_BF16 = 0,           /* every matrix bf16 [rows][cols], row-major                  */
+  DAR_WTYPE_FP8_E4M3_ROW = 1    /* Linear matrices e4m3fn [rows][cols] + fp32 scale [rows]   */
+} dar_wtype;
+
+/* Model geometry and capacity. Checked by dar_workspace_bytes / dar_create.
+ * Requirements: head_dim in {64, 128}; n_heads_q a multiple of n_heads_kv;
+ * d_model, ffn_dim and n_heads_q*head_dim multiples of 256 and at most 16384;
+ * n_res in [0, 15]; n_res > 0 needs n_layers_fast >= 1 and vocab_res >= 1;
+ * max_batch == 1 (batched decode is not in this version: DAR_E_UNSUPPORTED). */
+typedef struct {
+  int32_t n_layers_slow;
+  int32_t n_layers_fast;  /* 0 with n_res == 0: slow-AR-only decode (frame = 1 code) */
+  int32_t d_model;
+  int32_t n_heads_q;
+  int32_t n_heads_kv;
+  int32_t head_dim;
+  int32_t ffn_dim;
+  int32_t vocab_c0;       /* codebook-0 entries: rows of the tied table w0           */
+  int32_t vocab_res;      /* entries of each residual codebook (fast head rows)      */
+  int32_t n_res;          /* residual codebooks per frame                            */
+  float rms_eps;
+  double rope_base;       /* RoPE angle p * rope_base^(-2i/head_dim), rotate-half    */
+  int32_t max_len;        /* slow KV capacity in positions                           */
+  int32_t max_batch;
+  int32_t wtype;          /* dar_wtype                                               */
+} dar_config;
+
+/* One decoder block. All device pointers, 16-byte aligned, caller-owned and
+ * unchanged while the context lives. Matrix rows are output features.
+ *   attn_norm, ffn_norm : bf16 [d_model]
+ *   wqkv : [(n_heads_q + 2*n_heads_kv)*head_dim][d_model]: q rows (head-major),
+ *          then k rows, then v rows
+ *   wo   : [d_model][n_heads_q*head_dim]
+ *   w1, w3 : [ffn_dim][d_model] (gate and up); w2 : [d_model][ffn_dim]
+ *   *_scale : fp32 [rows] per-row scales; required for DAR_WTYPE_FP8_E4M3_ROW,
+ *             ignored (may be NULL) for bf16. */
+typedef struct {
+  const void* attn_norm;
+  const void* wqkv;
+  const float* wqkv_scale;
+  const void* wo;
+  const float* wo_scale;
+  const void* ffn_norm;
+  const void* w1;
+  const float* w1_scale;
+  const void* w3;
+  const float* w3_scale;
+  const void* w2;
+  const float* w2_scale;
+} dar_layer_weights;
+
+/* The whole model. Top-level arrays (slow, fast, fast_emb) are host arrays of
+ * device pointers and are copied by dar_create; the device memory they name is
+ * referenced, not copied.
+ *   w0 : bf16 [vocab_c0][d_model]: slow input table tied to the codebook-0 head
+ *   slow_final_norm, fast_final_norm : bf16 [d_model]
+ *   fast_emb[k] : bf16 table for codebook k feeding fast step k+1;
+ *                 [vocab_c0][d] for k = 0, [vocab_res][d] for k >= 1
+ *   fast_head : [vocab_res][d_model] (+ fp32 scale [vocab_res] in fp8 mode)
+ * Fast members are ignored when n_res == 0. */
+typedef struct {
+  const void* w0;
+  const dar_layer_weights* slow;      /* host array [n_layers_slow] */
+  const void* slow_final_norm;
+  const void* const* fast_emb;        /* host array [n_res]         */
+  const dar_layer_weights* fast;      /* host array [n_layers_fast] */
+  const void* fast_final_norm;
+  const void* fast_head;
+  const float* fast_head_scale;
+} dar_weights;
+
+typedef struct dar_ctx dar_ctx;
+
+/* Bytes of device workspace the context needs for this config (host only). */
+int dar_workspace_bytes(const dar_config* cfg, size_t* bytes_out);
+
+/* Create a decode context. `workspace` is device memory of at least
+ * dar_workspace_bytes() bytes, 256-byte aligned, caller-owned, not touched by
+ * anyone else while the context lives; it holds the KV caches, activations,
+ * the committed-code ring and the RoPE table. `stream` is a hipStream_t (NULL =
+ * the null stream). Launches initialisation work on `stream` and waits for it. */
+int dar_create(const dar_config* cfg, const dar_weights* weights, void* workspace,
+               size_t workspace_bytes, void* stream, dar_ctx** ctx_out);
+
+/* Prefill a prompt and produce frame 0 (the tuna-fish README's
+ * "prefill ... decode" run). Positions restart at 0: any previous state is
+ * dropped. tokens: device int32 [lens_host[0]] ids in [0, vocab_c0); lens_host:
+ * host int32 [batch]; 1 <= lens_host[0] < max_len. forced: NULL or device int32
+ * [batch][1+n_res], the frame the following steps consume instead of the
+ * argmax codes (teacher forcing). codes_out: NULL or device int32
+ * [batch][1+n_res] argmax codes of frame 0. logits_out: NULL or device fp32
+ * [batch][1+n_res][max(vocab_c0, vocab_res)] (entries past a codebook's size
+ * are left untouched). Token ids are not range-checked on the host (they are
+ * in device memory); an out-of-range id is clamped to the table. */
+int dar_prefill(dar_ctx* ctx, int32_t batch, const int32_t* tokens, const int32_t* lens_host,
+                const int32_t* forced, int32_t* codes_out, float* logits_out);
+
+/* Decode one frame at the next position: the slow AR consumes the previous
+ * frame's committed codebook-0 id, then the fast AR emits codebooks 1..n_res.
+ * forced / codes_out / logits_out as in dar_prefill. Runs as one replay of a
+ * captured HIP graph (unless disabled with dar_set_graph). Errors: DAR_E_STATE
+ * before prefill, DAR_E_CAPACITY when the position has reached max_len. */
+int dar_decode_frame(dar_ctx* ctx, const int32_t* forced, int32_t* codes_out, float* logits_out);
+
+/* Release the context (graph, events, host state). Waits for the context's
+ * stream. Workspace and weights stay with the caller. NULL is a no-op. */
+int dar_destroy(dar_ctx* ctx);
+
+/* ---- helpers ---------------------------------------------------------- */
+
+/* Drop the decode state (position 0, needs a new prefill); keeps the graph. */
+int dar_reset(dar_ctx* ctx);
+
+/* Next slow position of each sequence, host int32 [max_batch] (host mirror,
+ * no synchronisation). */
+int dar_position(const dar_ctx* ctx, int32_t* pos_out);
+
+/* Use the captured frame graph (1, default) or eager launches (0). */
+int dar_set_graph(dar_ctx* ctx, int32_t enable);
+
+/* Committed frames [first, first+count) of the ring (index = slow position the
+ * frame's codebook 0 was predicted from), copied to device int32
+ * [count][max_batch][1+n_res], stream-ordered. */
+int dar_codes(dar_ctx* ctx, int32_t first, int32_t count, int32_t* dst);
+
+/* Non-finite logit counter since create/reset (synchronises the stream). */
+int dar_nonfinite(dar_ctx* ctx, int32_t* count_out);
+
+/* Algorithmic bytes of one decode frame that attends over T slow positions:
+ * every weight and norm the frame reads (the fast AR once per residual
+ * codebook), fp8 row scales, the codebook-0 head, T slow KV positions and the
+ * fast AR's per-frame KV reads (tuna-fish README, "Inference estimation"). */
+int dar_bytes_per_frame(const dar_config* cfg, int32_t T, double* bytes_out);
+
+/* Per-row symmetric e4m3fn quantisation on the device (s2-pro-fp8 model card,
+ * "Quantization Details"): scale[r] = max_j |w[r][j]| / 448 in fp32,
+ * q[r][j] = e4m3fn(w[r][j] / scale[r]) rounded to nearest even and saturated
+ * at 448; a zero row gives scale 0 and codes 0. w: device bf16 [rows][cols];
+ * q: device uint8 [rows][cols]; scale: device fp32 [rows]. cols % 16 == 0. */
+int dar_quantize_fp8_rows(const void* w, int32_t rows, int32_t cols, void* q, float* scale,
+                          void* stream);
+
+const char* dar_status_string(int status);
+const char* dar_last_error(const dar_ctx* ctx);   /* ctx may be NULL: last create error */
+
+/* ---- diagnostics: single operations of the frame, for tests and timing --- */
+
+/* y[m][r] = sum_j W[r][j] * x[m][j] (times scale[r] in fp8 mode) for m < M,
+ * r < rows: the frame's weight-streaming GEMV kernel with no prologue or
+ * epilogue. W device [rows][cols] bf16 or e4m3fn (wtype), scale fp32 [rows]
+ * or NULL for bf16, x device fp32 [M][cols], y device fp32 [M][rows].
+ * M in {1, 2}; cols % 256 == 0 and cols <= 16384. */
+int dar_op_gemv(int32_t wtype, const void* W, const float* scale, int32_t rows, int32_t cols,
+                const float* x, int32_t M, float* y, void* stream);
+
+/* Decode attention of one layer (the frame's split-K kernel): for query row m
+ * at position pos+m, head h, out[m][h] = softmax(q[m][h] . K[kv][0..pos+m] /
+ * sqrt(head_dim)) V[kv][0..pos+m] with kv = h / (n_heads_q/n_heads_kv).
+ * q device fp32 [M][n_heads_q*head_dim]; K, V device bf16
+ * [n_heads_kv][max_len][head_dim]; out device fp32 [M][n_heads_q*head_dim];
+ * 0 <= pos, pos + M <= max_len; M in {1, 2}; chunk = positions per split
+ * (multiple of 16, 0 = default). Uses its own scratch (allocated per call). */
+int dar_op_attention(const float* q, const void* K, const void* V, int32_t n_heads_q,
+                     int32_t n_heads_kv, int32_t head_dim, int32_t max_len, int32_t pos,
+                     int32_t M, int32_t chunk, float* out, void* stream);
+
+/* Decode e4m3fn codes with the same conversion the fp8 GEMV uses:
+ * out[i] = value of codes[i] (fp32). codes device uint8 [n], out device fp32 [n]. */
+int dar_op_fp8_decode(const void* codes, int32_t n, float* out, void* stream);
+
+/* Run one frame eagerly with a HIP event pair around every launch and report
+ * per-launch milliseconds, kind and layer (host arrays of capacity cap; *n_out
+ * is the number of launches). Kinds: 0 qkv, 1 attention, 2 wo, 3 w13, 4 w2,
+ * 5 codebook head, 6 other. The frame advances the state like
+ * dar_decode_frame(ctx, NULL, NULL, NULL). Synchronises the stream. */
+int dar_profile_frame(dar_ctx* ctx, int32_t cap, float* ms_out, int32_t* kind_out,
+                      int32_t* layer_out, int32_t* n_out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DAR_H_ */

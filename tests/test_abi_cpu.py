@@ -1,0 +1,109 @@
+"""The C ABI without a GPU: the library loads, exports every declared entry
+point, and rejects bad arguments on the host before touching HIP.
+
+dar_bytes_per_frame must agree with the host bytes model, which is itself
+pinned to the pages' numbers (tests/test_bytes_model.py)."""
+import ctypes
+
+import pytest
+
+from dar_decode_frame_amd import bytes_model as bm
+from synth import DIMS
+
+
+@pytest.fixture(scope="module")
+def N():
+    from dar_decode_frame_amd import native
+    return native
+
+
+def test_every_declared_symbol_is_exported(N):
+    names = N.header_functions()
+    assert len(names) >= 18
+    for name in names:
+        assert hasattr(N.lib, name), name
+        assert name in N._SIGS, f"binding misses {name}"
+
+
+@pytest.mark.parametrize("dname,max_len", [("tiny", 32), ("s2pro_slow", 1024), ("s2pro_dual", 1024)])
+def test_workspace_bytes_cover_kv(N, dname, max_len):
+    d = DIMS[dname]
+    n = N.dar_workspace_bytes(N.make_config(d, max_len))
+    kv = 2 * d.n_layers_slow * d.n_heads_kv * max_len * d.head_dim * 2
+    assert n >= kv and n < kv + 64 * 2 ** 20
+
+
+@pytest.mark.parametrize("dname,wtype", [("tiny", "bf16"), ("tiny", "fp8"), ("s2pro_slow", "bf16"),
+                                         ("s2pro_dual", "bf16"), ("s2pro_dual", "fp8")])
+@pytest.mark.parametrize("T", [0, 1, 129, 1024])
+def test_bytes_per_frame_matches_host_model(N, dname, wtype, T):
+    d = DIMS[dname]
+    got = N.dar_bytes_per_frame(N.make_config(d, 1024, wtype), T)
+    assert got == float(bm.frame_bytes(d, wtype, T))
+
+
+def _cfg(N, **kw):
+    c = N.make_config(DIMS["tiny"], 32)
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("head_dim", 96, -6), ("n_heads_kv", 3, -1), ("d_model", 200, -6), ("max_batch", 4, -6),
+    ("max_len", 1, -1), ("rms_eps", 0.0, -1), ("rope_base", 1.0, -1), ("wtype", 7, -1),
+    ("n_res", 16, -6), ("n_layers_slow", 0, -1), ("vocab_c0", 0, -1),
+])
+def test_config_validation(N, field, value, status):
+    c = _cfg(N, **{field: value})
+    out = ctypes.c_size_t(0)
+    assert N.lib.dar_workspace_bytes(ctypes.byref(c), ctypes.byref(out)) == status
+    assert N.dar_last_error(None)
+
+
+def test_create_rejects_before_hip(N):
+    c = _cfg(N)
+    w = N.dar_weights()
+    ctx = ctypes.c_void_p(0)
+    need = N.dar_workspace_bytes(c)
+    # NULL weights pointers
+    assert N.lib.dar_create(ctypes.byref(c), ctypes.byref(w), ctypes.c_void_p(1 << 20), need, None,
+                            ctypes.byref(ctx)) == N.DAR_E_INVAL
+    # misaligned workspace
+    assert N.lib.dar_create(ctypes.byref(c), ctypes.byref(w), ctypes.c_void_p((1 << 20) + 8), need, None,
+                            ctypes.byref(ctx)) == N.DAR_E_INVAL
+    # workspace too small
+    assert N.lib.dar_create(ctypes.byref(c), ctypes.byref(w), ctypes.c_void_p(1 << 20), need - 1, None,
+                            ctypes.byref(ctx)) == N.DAR_E_WORKSPACE
+    assert ctx.value is None
+    # misaligned weight pointers are caught too
+    layers = (N.dar_layer_weights * 2)()
+    for L in layers:
+        for f, _ in N.dar_layer_weights._fields_:
+            setattr(L, f, 4096 + 2)
+    w.w0 = 4096
+    w.slow = layers
+    w.slow_final_norm = 4096
+    assert N.lib.dar_create(ctypes.byref(c), ctypes.byref(w), ctypes.c_void_p(1 << 20), need, None,
+                            ctypes.byref(ctx)) == N.DAR_E_INVAL
+
+
+def test_null_context_and_ops_reject(N):
+    assert N.lib.dar_prefill(None, 1, None, None, None, None, None) == N.DAR_E_INVAL
+    assert N.lib.dar_decode_frame(None, None, None, None) == N.DAR_E_INVAL
+    assert N.lib.dar_reset(None) == N.DAR_E_INVAL
+    assert N.lib.dar_destroy(None) == N.DAR_OK
+    assert N.lib.dar_op_gemv(0, None, None, 4, 256, None, 1, None, None) == N.DAR_E_INVAL
+    assert N.lib.dar_op_gemv(0, ctypes.c_void_p(4096), None, 4, 300, ctypes.c_void_p(4096), 1,
+                             ctypes.c_void_p(4096), None) == N.DAR_E_INVAL
+    assert N.lib.dar_op_gemv(1, ctypes.c_void_p(4096), None, 4, 256, ctypes.c_void_p(4096), 1,
+                             ctypes.c_void_p(4096), None) == N.DAR_E_INVAL
+    assert N.lib.dar_op_attention(None, None, None, 4, 2, 64, 16, 0, 1, 0, None, None) == N.DAR_E_INVAL
+    assert N.lib.dar_quantize_fp8_rows(ctypes.c_void_p(4096), 4, 24, ctypes.c_void_p(4096),
+                                       ctypes.c_void_p(4096), None) == N.DAR_E_INVAL
+
+
+def test_status_strings(N):
+    for s in range(-6, 1):
+        assert N.dar_status_string(s) not in ("", "unknown status")
+    assert N.dar_status_string(-99) == "unknown status"
