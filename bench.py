@@ -1,0 +1,236 @@
+#!/usr/bin/env python3
+"""Benchmark: batch-1 Dual-AR decode frames/s and achieved bandwidth on one MI355X.
+
+Workload (default s2pro_dual_bf16): 36 slow layers + 4 fast layers x 9
+residual codebooks, d 2560, 32/8 heads of 128, SwiGLU 9728, 4096-entry
+codebooks, random-init N(0, 0.02) bf16 weights, prefill 128 random ids, then
+decode frames at positions 128.. (the tuna-fish README's "prefill 128, decode
+896" run to a 1024 context). A step is one decode frame (one replay of the
+captured frame graph). Inputs are resident in HBM before timing starts.
+
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "Dual-AR decode frames/s @batch1 + achieved HBM GB/s (% of ~8 TB/s peak)"
+HBM_PEAK = 8.0e12
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=896)
+    ap.add_argument("--warmup", type=int, default=16)
+    ap.add_argument("--workload", default="s2pro_dual_bf16")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile-frames", type=int, default=3)
+    ap.add_argument("--eager", action="store_true", help="eager launches instead of the frame graph")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    from dar_decode_frame_amd import bytes_model as bm
+    from dar_decode_frame_amd import native as N
+    from dar_decode_frame_amd.session import DarSession, DeviceWeights
+
+    wl = synth.WORKLOADS[args.workload]
+    dims = wl.dims
+    if wl.batch != 1:
+        raise SystemExit("batched workloads are not part of this version")
+    max_steps = wl.max_len - wl.prefill_len
+    if args.steps > max_steps or args.steps < 1:
+        raise SystemExit(f"--steps must be in [1, {max_steps}] for {wl.name}")
+    dev = torch.device("cuda:0")
+
+    t0 = time.time()
+    host = synth.gen_weights(dims, wl.weight_seed)
+    log(f"generated {len(host)} tensors in {time.time() - t0:.1f}s")
+    t0 = time.time()
+    weights = DeviceWeights(dims, host, wl.wtype, dev)
+    log(f"uploaded{' and quantised' if wl.wtype == 'fp8' else ''} in {time.time() - t0:.1f}s")
+    prompt = synth.gen_prompt(wl.prefill_len, dims.vocab_c0, wl.prompt_seed)
+    sess = DarSession(dims, weights, wl.max_len, dev, graph=not args.eager)
+    stream = sess.stream
+
+    # warmup: prefill, W frames (captures the graph), then start over
+    t0 = time.time()
+    sess.prefill(prompt, want=False)
+    stream.synchronize()
+    for _ in range(args.warmup):
+        sess.decode_frame(want=False)
+    stream.synchronize()
+    log(f"warmup ({args.warmup} frames) done in {time.time() - t0:.1f}s")
+    sess.reset()
+    ev_p0 = torch.cuda.Event(enable_timing=True)
+    ev_p1 = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        ev_p0.record(stream)
+    sess.prefill(prompt, want=False)
+    with torch.cuda.stream(stream):
+        ev_p1.record(stream)
+    stream.synchronize()
+    prefill_ms = ev_p0.elapsed_time(ev_p1)
+
+    # timed region: K frames back to back, HIP events on the session stream
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        sess.decode_frame(want=False)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1)
+    fps = args.steps * 1000.0 / ms
+    t_first = wl.prefill_len + 1
+    alg_bytes = bm.run_bytes(dims, wl.wtype, t_first, args.steps)
+    gbs = alg_bytes / (ms / 1000.0)
+    log(f"timed {args.steps} frames: {ms:.1f} ms, {fps:.1f} frames/s, {gbs / 1e9:.0f} GB/s")
+    n_bad = sess.nonfinite()
+    codes = sess.ring(wl.prefill_len - 1, args.steps + 1)
+
+    # dominant kernel: per-launch HIP-event timing of eager frames on the same stream
+    roof = None
+    kernel_table = {}
+    if args.profile_frames > 0:
+        sess.reset()
+        sess.prefill(prompt, want=False)
+        recs = []
+        for _ in range(args.profile_frames):
+            recs += sess.profile_frame()
+        for ms_k, kind, layer in recs:
+            name = N.KIND_NAMES[kind]
+            kernel_table.setdefault(name, []).append((ms_k, layer))
+        totals = {k: sum(m for m, _ in v) for k, v in kernel_table.items()}
+        dom = max(totals, key=totals.get)
+        per = per_launch_bytes(dims, wl.wtype, dom)
+        # average over the single-row launches (fast pass 1 runs two rows)
+        one_row = [m for m, layer in kernel_table[dom] if not (1000 <= layer < 2000)]
+        avg_ms = sum(one_row) / len(one_row)
+        achieved = per / (avg_ms / 1000.0)
+        roof = {"kernel": dom, "bound": "hbm", "achieved": round(achieved / 1e9, 1), "peak": HBM_PEAK / 1e9,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK, 4), "traffic": None,
+                "bytes_per_launch": per, "avg_launch_us": round(avg_ms * 1000, 2),
+                "launches_timed": len(one_row)}
+        share = {k: round(v / sum(totals.values()), 4) for k, v in totals.items()}
+        roof["frame_time_share"] = share
+        log(f"dominant kernel {dom}: {avg_ms * 1000:.1f} us/launch, {achieved / 1e9:.0f} GB/s; shares {share}")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(dims, wl, host, prompt)
+
+    out = {
+        "metric": METRIC,
+        "value": round(fps, 2),
+        "unit": "frames/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.wtype == "bf16" else "fp8_e4m3",
+        "data": "synthetic (seeded random-init weights and prompt ids)",
+        "config": {"workload": wl.name, "batch": 1, "prefill": wl.prefill_len, "first_decode_position": wl.prefill_len,
+                   "decode_frames": args.steps, "max_len": wl.max_len, "layers_slow": dims.n_layers_slow,
+                   "layers_fast": dims.n_layers_fast, "residual_codebooks": dims.n_res,
+                   "graph": not args.eager},
+        "achieved_gb_s": round(gbs / 1e9, 1),
+        "hbm_frac": round(gbs / HBM_PEAK, 4),
+        "alg_bytes_per_frame_avg": int(alg_bytes // args.steps),
+        "prefill_ms": round(prefill_ms, 2),
+        "nonfinite_logits": n_bad,
+        "codes_checksum": int(np.asarray(codes, dtype=np.int64).sum()),
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    sess.close()
+    print(json.dumps(out), flush=True)
+
+
+def per_launch_bytes(dims, wtype, kind):
+    """Algorithmic bytes one single-row launch of `kind` reads (weights, row scales, norm gain)."""
+    d, F, hd = dims.d_model, dims.ffn_dim, dims.head_dim
+    eb = 2 if wtype == "bf16" else 1
+    sc = 0 if wtype == "bf16" else 4
+
+    def mat(rows, cols, scaled=True):
+        return rows * cols * eb + (rows * sc if scaled else 0)
+
+    if kind == "w13":
+        return mat(2 * F, d) + 2 * d
+    if kind == "w2":
+        return mat(d, F)
+    if kind == "wo":
+        return mat(d, dims.q_width)
+    if kind == "qkv":
+        return mat(dims.qkv_rows, d) + 2 * d
+    if kind == "head":
+        return dims.vocab_c0 * d * 2 + 2 * d
+    raise ValueError(kind)
+
+
+def cpu_baseline(dims, wl, host, prompt):
+    """The oracle on this host's cores: prefill 128 then two decode frames; decode timed."""
+    import numpy as np
+    from oracle import OracleDecoder, OracleModel
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 0) for i in threadpool_info()), default=os.cpu_count())
+    except Exception:
+        threads = os.cpu_count()
+    t0 = time.time()
+    model = OracleModel(dims, host, wtype=wl.wtype)
+    t_build = time.time() - t0
+    dec = OracleDecoder(model, wl.max_len)
+    t0 = time.time()
+    dec.prefill(prompt)
+    t_prefill = time.time() - t0
+    frames = 2
+    t0 = time.time()
+    for _ in range(frames):
+        dec.decode_frame()
+    t_dec = time.time() - t0
+    log(f"oracle: build {t_build:.1f}s, prefill {t_prefill:.1f}s, {frames} frames {t_dec:.1f}s on {threads} threads")
+    del model, dec
+    return {"value": round(frames / t_dec, 4), "unit": "frames/s", "cores": threads, "kind": "oracle",
+            "sample": f"{wl.name}: oracle (NumPy fp32) prefill {wl.prefill_len} as one causal block, then "
+                      f"{frames} decode frames timed ({t_dec:.1f} s); weight conversion {t_build:.1f} s and "
+                      f"prefill {t_prefill:.1f} s not timed",
+            "cpu_model": _cpu_model()}
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+if __name__ == "__main__":
+    main()
