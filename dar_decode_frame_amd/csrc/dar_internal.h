@@ -63,7 +63,7 @@ struct SwigluArgs {
   int h_stride;
 };
 
-// Fused RMSNorm + head GEMV + argmax + frame bookkeeping (last workgroup).
+// Fused RMSNorm + head GEMV + per-workgroup argmax.
 struct HeadArgs {
   const void* W;
   const float* scale;
@@ -72,9 +72,15 @@ struct HeadArgs {
   const uint16_t* gain;
   float eps;
   float* logits;            // [rows]
-  unsigned long long* slot; // packed (value, index) maximum, reset by the last workgroup
-  unsigned* counter;        // arrival counter, reset by the last workgroup
+  unsigned long long* slots;// [head_grid(rows)] packed (value, index) maximum per workgroup
   int* anomalies;           // +1 per non-finite logit
+  float* h_out;             // non-null: workgroup 0 writes the normalised input row here
+};
+
+// Reduce a head's slots to its code and do the frame bookkeeping.
+struct CommitArgs {
+  const unsigned long long* slots;
+  int nslots;
   int code_index;           // k in the frame
   int frame_codes;          // 1 + n_res
   int* pred;                // [frame_codes] argmax codes
@@ -83,8 +89,8 @@ struct HeadArgs {
   const int* force_flag;
   int* ring;                // [max_len][frame_codes]
   const int* pos;           // slow position of this frame
-  int* pos_inc;             // non-null: ++*pos_inc at the end (last head of the frame)
-  float* h_out;             // non-null: write the normalised input row here
+  int* pos_inc;             // non-null: ++*pos_inc at the end (last code of the frame)
+  int K;                    // row width of the tables below
   const uint16_t* next_table; // non-null: next_x = next_table[code] (bf16 -> fp32)
   int next_rows;
   float* next_x;
@@ -105,7 +111,6 @@ struct AttnArgs {
   int nsplit_max;           // grid.x
   int M;
   float* part;              // [M][n_kv][nsplit_max][group][head_dim + 2]
-  unsigned* counters;       // [M][n_kv], zero between launches
   float* out;
   int out_stride;
 };
@@ -114,6 +119,8 @@ hipError_t launch_gemv(int wtype, const GemvArgs& a, hipStream_t s);
 hipError_t launch_qkv(int wtype, const QkvArgs& a, hipStream_t s);
 hipError_t launch_swiglu(int wtype, const SwigluArgs& a, hipStream_t s);
 hipError_t launch_head(int wtype, const HeadArgs& a, hipStream_t s);
+hipError_t launch_commit(const CommitArgs& a, hipStream_t s);
+int head_grid(int rows);
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s);
 
 // x = table[clamp(*tok)] as fp32, *pos_out = pos_value (prefill step input)

@@ -465,7 +465,6 @@ template <typename WT>
 __global__ __launch_bounds__(kBlock) void k_head(HeadArgs a) {
   extern __shared__ __align__(16) float xs[];
   __shared__ unsigned long long wbest[kWaves];
-  __shared__ int last;
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   constexpr int RPW = 2;
   const int r0 = (blockIdx.x * kWaves + wave) * RPW;
@@ -479,6 +478,9 @@ __global__ __launch_bounds__(kBlock) void k_head(HeadArgs a) {
     rs.start(base, a.K, lane);
   }
   st.finish(xs, a.eps);
+  if (a.h_out && blockIdx.x == 0) {
+    for (int k = tid; k < a.K; k += kBlock) a.h_out[k] = xs[k];
+  }
   unsigned long long best = 0ull;
   if (r0 < a.rows) {
     float acc[RPW][1];
@@ -504,32 +506,39 @@ __global__ __launch_bounds__(kBlock) void k_head(HeadArgs a) {
     unsigned long long b = wbest[0];
 #pragma unroll
     for (int w = 1; w < kWaves; ++w) b = wbest[w] > b ? wbest[w] : b;
-    atomicMax(a.slot, b);
-    __threadfence();
-    const unsigned prev = atomicAdd(a.counter, 1u);
-    last = (prev == gridDim.x - 1);
+    a.slots[blockIdx.x] = b;  // reduced by k_commit after this kernel
   }
-  __syncthreads();
-  if (!last) return;
-  __threadfence();
-  // Last workgroup: every logit and the maximum are in place.
+}
+
+// One workgroup after each head: reduce the per-workgroup maxima to the code,
+// record it (argmax and committed/forced), gather the next step's inputs and,
+// after the frame's last head, advance the position.
+__global__ __launch_bounds__(kBlock) void k_commit(CommitArgs a) {
+  __shared__ unsigned long long red[kWaves];
   __shared__ int code_sh;
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  unsigned long long b = 0ull;
+  for (int i = tid; i < a.nslots; i += kBlock) b = a.slots[i] > b ? a.slots[i] : b;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const unsigned long long o = __shfl_xor(b, off);
+    b = o > b ? o : b;
+  }
+  if (lane == 0) red[wave] = b;
+  __syncthreads();
   if (tid == 0) {
-    const unsigned long long key = atomicAdd(a.slot, 0ull);
-    const int pred = (int)(0xffffffffu - (uint32_t)(key & 0xffffffffull));
+    unsigned long long m = red[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) m = red[w] > m ? red[w] : m;
+    const int pred = (int)(0xffffffffu - (uint32_t)(m & 0xffffffffull));
     const int code = (*a.force_flag) ? a.forced[a.code_index] : pred;
     a.pred[a.code_index] = pred;
     a.committed[a.code_index] = code;
     a.ring[(size_t)(*a.pos) * a.frame_codes + a.code_index] = code;
     code_sh = code;
-    *a.slot = 0ull;
-    *a.counter = 0u;
   }
   __syncthreads();
   const int code = code_sh;
-  if (a.h_out) {
-    for (int k = tid; k < a.K; k += kBlock) a.h_out[k] = xs[k];
-  }
   if (a.next_table) {
     const int c = min(max(code, 0), a.next_rows - 1);
     const uint16_t* row = a.next_table + (size_t)c * a.K;
@@ -540,6 +549,7 @@ __global__ __launch_bounds__(kBlock) void k_head(HeadArgs a) {
     const uint16_t* row = a.slow_table + (size_t)c * a.K;
     for (int k = tid; k < a.K; k += kBlock) a.slow_x[k] = bf2f(row[k]);
   }
+  __syncthreads();
   if (a.pos_inc && tid == 0) *a.pos_inc = *a.pos_inc + 1;
 }
 
@@ -548,8 +558,9 @@ __global__ __launch_bounds__(kBlock) void k_head(HeadArgs a) {
 // One workgroup = one KV head x one split of `chunk` positions for one query
 // row. hd/8 lanes cover one key row (16 bytes each); a wave covers 64/(hd/8)
 // positions per step and keeps an online softmax per lane group; groups and
-// waves are merged at the end, the split's (max, sum, acc) is written, and the
-// last split to finish for that head combines all splits into the output.
+// waves are merged at the end. With one split the workgroup writes the output;
+// otherwise it writes the split's (max, sum, acc) and k_attn_combine merges the
+// splits in a second launch (no cross-workgroup signalling inside a kernel).
 template <int HD, int G>
 __global__ __launch_bounds__(kBlock) void k_attn(AttnArgs a) {
   constexpr int LPP = HD / 8;
@@ -652,6 +663,25 @@ __global__ __launch_bounds__(kBlock) void k_attn(AttnArgs a) {
     }
   }
   __syncthreads();
+  if (a.nsplit_max == 1) {
+    // a single split covers every position: normalise and write the output
+    for (int idx = tid; idx < G * HD; idx += kBlock) {
+      const int h = idx / HD, e = idx % HD;
+      float M = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_ml[w][h][0]);
+      float num = 0.f, den = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float mw = sm_ml[w][h][0];
+        const float c = (mw == -INFINITY) ? 0.f : exp2f(mw - M);
+        num += sm_acc[w][h][e] * c;
+        den += sm_ml[w][h][1] * c;
+      }
+      a.out[(size_t)m * a.out_stride + (kvh * G + h) * HD + e] = num / den;
+    }
+    return;
+  }
   const int stride_s = G * (HD + 2);
   float* part = a.part + (((size_t)m * a.n_heads_kv + kvh) * a.nsplit_max) * stride_s;
   for (int idx = tid; idx < G * HD; idx += kBlock) {
@@ -674,16 +704,17 @@ __global__ __launch_bounds__(kBlock) void k_attn(AttnArgs a) {
       ps[HD + 1] = den;
     }
   }
-  __shared__ int last;
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    const unsigned prev = atomicAdd(a.counters + m * a.n_heads_kv + kvh, 1u);
-    last = (prev == (unsigned)(nsplit - 1));
-  }
-  __syncthreads();
-  if (!last) return;
-  __threadfence();
+}
+
+// Combine the splits of one KV head (blockIdx.x) for query row blockIdx.y:
+// out = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s.
+template <int HD, int G>
+__global__ __launch_bounds__(kBlock) void k_attn_combine(AttnArgs a) {
+  const int kvh = blockIdx.x, m = blockIdx.y, tid = threadIdx.x;
+  const int T = *a.pos + m + 1;
+  const int nsplit = (T + a.chunk - 1) / a.chunk;
+  const int stride_s = G * (HD + 2);
+  const float* part = a.part + (((size_t)m * a.n_heads_kv + kvh) * a.nsplit_max) * stride_s;
   for (int idx = tid; idx < G * HD; idx += kBlock) {
     const int h = idx / HD, e = idx % HD;
     float M = -INFINITY;
@@ -697,7 +728,6 @@ __global__ __launch_bounds__(kBlock) void k_attn(AttnArgs a) {
     }
     a.out[(size_t)m * a.out_stride + (kvh * G + h) * HD + e] = num / den;
   }
-  if (tid == 0) a.counters[m * a.n_heads_kv + kvh] = 0u;
 }
 
 // ---------------------------------------------------------- small kernels --
@@ -792,6 +822,8 @@ __global__ void k_fp8_decode(const uint8_t* codes, int n, float* out) {
 
 // ---------------------------------------------------------------- launchers --
 
+int head_grid(int rows);
+
 static size_t lds_bytes(int M, int K) { return (size_t)M * K * sizeof(float); }
 
 template <typename KernelT>
@@ -859,8 +891,7 @@ static hipError_t head_impl(const HeadArgs& a, hipStream_t s) {
   const size_t lds = lds_bytes(1, a.K);
   hipError_t e = prep(kern, lds);
   if (e != hipSuccess) return e;
-  const int grid = (a.rows + kWaves * 2 - 1) / (kWaves * 2);
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(kBlock), lds, s, a);
+  hipLaunchKernelGGL(kern, dim3(head_grid(a.rows)), dim3(kBlock), lds, s, a);
   return hipGetLastError();
 }
 
@@ -868,9 +899,19 @@ hipError_t launch_head(int wtype, const HeadArgs& a, hipStream_t s) {
   return wtype == W_FP8 ? head_impl<FP8>(a, s) : head_impl<BF16>(a, s);
 }
 
+int head_grid(int rows) { return (rows + kWaves * 2 - 1) / (kWaves * 2); }
+
+hipError_t launch_commit(const CommitArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(k_commit, dim3(1), dim3(kBlock), 0, s, a);
+  return hipGetLastError();
+}
+
 template <int HD, int G>
 static hipError_t attn_impl(const AttnArgs& a, hipStream_t s) {
   hipLaunchKernelGGL((k_attn<HD, G>), dim3(a.nsplit_max, a.n_heads_kv, a.M), dim3(kBlock), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.nsplit_max == 1) return e;
+  hipLaunchKernelGGL((k_attn_combine<HD, G>), dim3(a.n_heads_kv, a.M), dim3(kBlock), 0, s, a);
   return hipGetLastError();
 }
 

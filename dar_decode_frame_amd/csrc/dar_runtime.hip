@@ -39,9 +39,9 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
-  size_t x_s, x_f, q, o, h, part, logits, slots, head_ctr, attn_ctr, pred, committed, forced, flags, pos,
+  size_t x_s, x_f, q, o, h, part, logits, slots, pred, committed, forced, flags, pos,
       seqpos, ring, rope, ks, vs, kf, vf, total;
-  int nsplit_max, chunk, rope_len, seq_len, vmax, fast_len;
+  int nsplit_max, chunk, rope_len, seq_len, vmax, fast_len, nslots;
 };
 
 int frame_codes(const dar_config* c) { return 1 + c->n_res; }
@@ -71,9 +71,8 @@ Layout make_layout(const dar_config* c) {
   L.h = take(sizeof(float) * 2 * F);
   L.part = take(sizeof(float) * attn_partial_floats(2, c->n_heads_kv, L.nsplit_max, g, c->head_dim));
   L.logits = take(sizeof(float) * (size_t)fc * L.vmax);
-  L.slots = take(sizeof(unsigned long long) * fc);
-  L.head_ctr = take(sizeof(unsigned) * fc);
-  L.attn_ctr = take(sizeof(unsigned) * 2 * c->n_heads_kv);
+  L.nslots = std::max(head_grid(c->vocab_c0), has_fast(c) ? head_grid(c->vocab_res) : 0);
+  L.slots = take(sizeof(unsigned long long) * fc * L.nslots);
   L.pred = take(sizeof(int) * fc);
   L.committed = take(sizeof(int) * fc);
   L.forced = take(sizeof(int) * fc);
@@ -183,7 +182,6 @@ struct dar_ctx {
   char* ws = nullptr;
   float *x_s, *x_f, *q, *o, *h, *part, *logits;
   unsigned long long* slots;
-  unsigned *head_ctr, *attn_ctr;
   int *pred, *committed, *forced, *flags, *pos, *seqpos, *ring;
   float2* rope;
   uint16_t *ks, *vs, *kf, *vf;
@@ -279,7 +277,6 @@ hipError_t enqueue_layer(dar_ctx* c, hipStream_t s, const dar_layer_weights& w, 
   aa.nsplit_max = (cache_len + c->L.chunk - 1) / c->L.chunk;
   aa.M = M;
   aa.part = c->part;
-  aa.counters = c->attn_ctr;
   aa.out = c->o;
   aa.out_stride = qw;
   e = tracked(c, s, K_ATTN, layer_tag, [&] { return launch_attn(aa, s); });
@@ -345,23 +342,30 @@ hipError_t enqueue_slow_layers(dar_ctx* c, hipStream_t s) {
   return hipSuccess;
 }
 
-HeadArgs head_common(dar_ctx* c, int k) {
+HeadArgs head_args(dar_ctx* c, int k) {
   HeadArgs h{};
   h.K = c->cfg.d_model;
   h.eps = c->cfg.rms_eps;
   h.logits = c->logits + (size_t)k * c->L.vmax;
-  h.slot = c->slots + k;
-  h.counter = c->head_ctr + k;
+  h.slots = c->slots + (size_t)k * c->L.nslots;
   h.anomalies = c->flags + 1;
-  h.code_index = k;
-  h.frame_codes = frame_codes(&c->cfg);
-  h.pred = c->pred;
-  h.committed = c->committed;
-  h.forced = c->forced;
-  h.force_flag = c->flags + 0;
-  h.ring = c->ring;
-  h.pos = c->pos;
   return h;
+}
+
+CommitArgs commit_args(dar_ctx* c, int k, int rows) {
+  CommitArgs a{};
+  a.slots = c->slots + (size_t)k * c->L.nslots;
+  a.nslots = head_grid(rows);
+  a.code_index = k;
+  a.frame_codes = frame_codes(&c->cfg);
+  a.pred = c->pred;
+  a.committed = c->committed;
+  a.forced = c->forced;
+  a.force_flag = c->flags + 0;
+  a.ring = c->ring;
+  a.pos = c->pos;
+  a.K = c->cfg.d_model;
+  return a;
 }
 
 // Codebook-0 head and the fast AR: the tail of every frame.
@@ -372,21 +376,24 @@ hipError_t enqueue_tail(dar_ctx* c, hipStream_t s) {
   const int wt = c->fp8 ? W_FP8 : W_BF16;
   hipError_t e;
 
-  HeadArgs h0 = head_common(c, 0);
+  HeadArgs h0 = head_args(c, 0);
   h0.W = c->w0;
   h0.scale = nullptr;
   h0.rows = g.vocab_c0;
   h0.x = c->x_s;
   h0.gain = c->slow_fn;
-  h0.pos_inc = fast ? nullptr : c->pos;
-  h0.h_out = fast ? c->x_f : nullptr;
-  h0.next_table = fast ? c->fast_emb[0] : nullptr;
-  h0.next_rows = g.vocab_c0;
-  h0.next_x = c->x_f + d;
-  h0.slow_table = c->w0;
-  h0.slow_rows = g.vocab_c0;
-  h0.slow_x = c->x_s;
+  h0.h_out = fast ? c->x_f : nullptr;  // h_t: fast input at fast position 0
   e = tracked(c, s, K_HEAD, 0, [&] { return launch_head(W_BF16, h0, s); });
+  if (e != hipSuccess) return e;
+  CommitArgs c0 = commit_args(c, 0, g.vocab_c0);
+  c0.pos_inc = fast ? nullptr : c->pos;
+  c0.next_table = fast ? c->fast_emb[0] : nullptr;
+  c0.next_rows = g.vocab_c0;
+  c0.next_x = c->x_f + d;
+  c0.slow_table = c->w0;
+  c0.slow_rows = g.vocab_c0;
+  c0.slow_x = c->x_s;
+  e = tracked(c, s, K_OTHER, 0, [&] { return launch_commit(c0, s); });
   if (e != hipSuccess || !fast) return e;
 
   const size_t per_layer = (size_t)g.n_heads_kv * c->L.fast_len * g.head_dim;
@@ -398,17 +405,20 @@ hipError_t enqueue_tail(dar_ctx* c, hipStream_t s) {
                         c->vf + l * per_layer, c->L.fast_len);
       if (e != hipSuccess) return e;
     }
-    HeadArgs hk = head_common(c, k);
+    HeadArgs hk = head_args(c, k);
     hk.W = c->fast_head;
     hk.scale = c->fp8 ? c->fast_head_scale : nullptr;
     hk.rows = g.vocab_res;
     hk.x = c->x_f + (size_t)(M - 1) * d;
     hk.gain = c->fast_fn;
-    hk.pos_inc = (k == g.n_res) ? c->pos : nullptr;
-    hk.next_table = (k < g.n_res) ? c->fast_emb[k] : nullptr;
-    hk.next_rows = g.vocab_res;
-    hk.next_x = c->x_f;
     e = tracked(c, s, K_HEAD, k, [&] { return launch_head(wt, hk, s); });
+    if (e != hipSuccess) return e;
+    CommitArgs ck = commit_args(c, k, g.vocab_res);
+    ck.pos_inc = (k == g.n_res) ? c->pos : nullptr;
+    ck.next_table = (k < g.n_res) ? c->fast_emb[k] : nullptr;
+    ck.next_rows = g.vocab_res;
+    ck.next_x = c->x_f;
+    e = tracked(c, s, K_OTHER, k, [&] { return launch_commit(ck, s); });
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
@@ -564,8 +574,6 @@ int dar_create(const dar_config* cfg, const dar_weights* w, void* workspace, siz
   c->part = reinterpret_cast<float*>(b + L.part);
   c->logits = reinterpret_cast<float*>(b + L.logits);
   c->slots = reinterpret_cast<unsigned long long*>(b + L.slots);
-  c->head_ctr = reinterpret_cast<unsigned*>(b + L.head_ctr);
-  c->attn_ctr = reinterpret_cast<unsigned*>(b + L.attn_ctr);
   c->pred = reinterpret_cast<int*>(b + L.pred);
   c->committed = reinterpret_cast<int*>(b + L.committed);
   c->forced = reinterpret_cast<int*>(b + L.forced);
@@ -816,12 +824,10 @@ int dar_op_attention(const float* q, const void* K, const void* V, int32_t n_hea
   const int nsplit_max = (max_len + chunk - 1) / chunk;
   const size_t pf = attn_partial_floats(M, n_heads_kv, nsplit_max, g, head_dim);
   char* scratch = nullptr;
-  const size_t off_ctr = align_up(pf * sizeof(float));
-  const size_t off_pos = align_up(off_ctr + sizeof(unsigned) * M * n_heads_kv);
+  const size_t off_pos = align_up(pf * sizeof(float));
   const size_t bytes = off_pos + 256;
   hipError_t e = hipMalloc(&scratch, bytes);
   if (e != hipSuccess) return hip_fail(nullptr, e, "attention scratch");
-  unsigned* ctr = reinterpret_cast<unsigned*>(scratch + off_ctr);
   int* dpos = reinterpret_cast<int*>(scratch + off_pos);
   AttnArgs a{};
   a.q = q;
@@ -837,11 +843,9 @@ int dar_op_attention(const float* q, const void* K, const void* V, int32_t n_hea
   a.nsplit_max = nsplit_max;
   a.M = M;
   a.part = reinterpret_cast<float*>(scratch);
-  a.counters = ctr;
   a.out = out;
   a.out_stride = n_heads_q * head_dim;
-  if ((e = launch_fill_u32(ctr, (size_t)M * n_heads_kv, s)) == hipSuccess &&
-      (e = launch_fill_i32(dpos, 1, pos, s)) == hipSuccess && (e = launch_attn(a, s)) == hipSuccess) {
+  if ((e = launch_fill_i32(dpos, 1, pos, s)) == hipSuccess && (e = launch_attn(a, s)) == hipSuccess) {
     e = hipStreamSynchronize(s);
   }
   (void)hipFree(scratch);
@@ -868,7 +872,7 @@ int dar_profile_frame(dar_ctx* c, int32_t cap, float* ms_out, int32_t* kind_out,
     return DAR_E_CAPACITY;
   }
   const dar_config& g = c->cfg;
-  const int launches = 5 * g.n_layers_slow + 1 + (g.n_res > 0 ? g.n_res * (5 * g.n_layers_fast + 1) : 0);
+  const int launches = 5 * g.n_layers_slow + 2 + (g.n_res > 0 ? g.n_res * (5 * g.n_layers_fast + 2) : 0);
   if (cap < launches) {
     c->err = "profile capacity below the frame's launch count";
     return DAR_E_INVAL;
