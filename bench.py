@@ -208,16 +208,19 @@ def cpu_baseline(dims, wl, host, prompt):
     t0 = time.time()
     dec.prefill(prompt)
     t_prefill = time.time() - t0
-    frames = 2
+    # decode frames until about 12 s of CPU work (at least 2), within the capacity
+    budget_s, frames = 12.0, 0
     t0 = time.time()
-    for _ in range(frames):
+    while frames < 2 or (time.time() - t0 < budget_s and dec.pos < wl.max_len):
         dec.decode_frame()
+        frames += 1
     t_dec = time.time() - t0
     log(f"oracle: build {t_build:.1f}s, prefill {t_prefill:.1f}s, {frames} frames {t_dec:.1f}s on {threads} threads")
     del model, dec
     return {"value": round(frames / t_dec, 4), "unit": "frames/s", "cores": threads, "kind": "oracle",
             "sample": f"{wl.name}: oracle (NumPy fp32) prefill {wl.prefill_len} as one causal block, then "
-                      f"{frames} decode frames timed ({t_dec:.1f} s); weight conversion {t_build:.1f} s and "
+                      f"{frames} decode frames at positions {wl.prefill_len}..{wl.prefill_len + frames - 1} timed "
+                      f"({t_dec:.1f} s, budget about 12 s); weight conversion {t_build:.1f} s and "
                       f"prefill {t_prefill:.1f} s not timed",
             "cpu_model": _cpu_model()}
 
