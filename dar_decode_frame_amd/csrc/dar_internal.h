@@ -75,6 +75,7 @@ struct HeadArgs {
   unsigned long long* slots;// [head_grid(rows)] packed (value, index) maximum per workgroup
   int* anomalies;           // +1 per non-finite logit
   float* h_out;             // non-null: workgroup 0 writes the normalised input row here
+  int* pos_inc;             // non-null: workgroup 0 does ++*pos_inc (no other reader in the kernel)
 };
 
 // Reduce a head's slots to its code and do the frame bookkeeping.
@@ -97,6 +98,9 @@ struct CommitArgs {
   const uint16_t* slow_table; // non-null: slow_x = slow_table[code] (next frame's slow input)
   int slow_rows;
   float* slow_x;
+  const float* copy_src[2];   // optional plain copies done by the same workgroup
+  float* copy_dst[2];
+  int copy_n[2];
 };
 
 struct AttnArgs {

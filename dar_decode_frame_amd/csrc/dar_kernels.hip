@@ -507,6 +507,7 @@ __global__ __launch_bounds__(kBlock) void k_head(HeadArgs a) {
 #pragma unroll
     for (int w = 1; w < kWaves; ++w) b = wbest[w] > b ? wbest[w] : b;
     a.slots[blockIdx.x] = b;  // reduced by k_commit after this kernel
+    if (a.pos_inc && blockIdx.x == 0) *a.pos_inc = *a.pos_inc + 1;
   }
 }
 
@@ -548,6 +549,12 @@ __global__ __launch_bounds__(kBlock) void k_commit(CommitArgs a) {
     const int c = min(max(code, 0), a.slow_rows - 1);
     const uint16_t* row = a.slow_table + (size_t)c * a.K;
     for (int k = tid; k < a.K; k += kBlock) a.slow_x[k] = bf2f(row[k]);
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    if (a.copy_src[j]) {
+      for (int k = tid; k < a.copy_n[j]; k += kBlock) a.copy_dst[j][k] = a.copy_src[j][k];
+    }
   }
   __syncthreads();
   if (a.pos_inc && tid == 0) *a.pos_inc = *a.pos_inc + 1;

@@ -1,19 +1,24 @@
 // C-ABI runtime of libdar.so: context, workspace carve-up, RoPE table, the
-// frame's launch sequence, HIP-graph capture and replay, prefill, helpers.
+// frame's launch sequences, HIP-graph capture and replay, prefill, helpers.
 //
 // Frame (tuna-fish README, intro: "slowAR decode + fastAR loop"; "Inference
 // estimation": slow AR once, fast AR nine times with a 10-long fast KV):
-//   slow layers 0..Ls-1 : QKV(+norm,RoPE,KV append) -> attention -> Wo(+res)
+//   slow layers 0..Ls-1 : QKV(+norm, RoPE, KV append) -> attention -> Wo(+res)
 //                         -> W1/W3(+norm, SiLU*mul) -> W2(+res)
-//   codebook-0 head     : norm -> W0 -> argmax; its last workgroup commits c0,
-//                         writes the fast inputs [h_t, E0[c0]] and the next
-//                         frame's slow input W0[c0]
+//   codebook-0 head     : norm -> W0 -> per-workgroup argmax
+//   commit c0           : argmax (or the forced code) -> ring, fast inputs
+//                         [h_t, E0[c0]], next frame's slow input W0[c0]
 //   fast pass 1         : the fast layers over fast positions 0 and 1 together
 //   fast passes 2..R    : the fast layers over position k; after each pass the
-//                         shared head's last workgroup commits c_k and gathers
-//                         E_k[c_k] as the next pass's input
-// Every position and code the graph needs lives in device memory, so one
-// captured graph replays every frame.
+//                         shared head and a commit that gathers E_k[c_k]
+//
+// The slow step of frame i+1 needs only codebook 0 of frame i, not frame i's
+// fast AR, so each call runs two chains concurrently on two streams, each one
+// replaying its own captured graph: the fast chain finishes frame i while the
+// slow chain computes the slow step and codebook-0 head of frame i+1. Their
+// weights are nearly equal in size (slow 7.29 GB, fast 9 x 0.83 GB at full
+// shape), so each chain's launch gaps are filled by the other's weight stream.
+// Every position and code the chains need lives in device memory.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -39,9 +44,10 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
-  size_t x_s, x_f, q, o, h, part, logits, slots, pred, committed, forced, flags, pos,
-      seqpos, ring, rope, ks, vs, kf, vf, total;
-  int nsplit_max, chunk, rope_len, seq_len, vmax, fast_len, nslots;
+  size_t x[2], q[2], o[2], h[2], part[2];  // chain scratch: [0] slow (one row), [1] fast (two rows)
+  size_t ht, logits0, flogits, slots0, slotsf, pred, committed, forced, flags, pos, seqpos, ring, rope;
+  size_t ks, vs, kf, vf, total;
+  int nsplit_slow, chunk, rope_len, seq_len, vmax, fast_len, nslots;
 };
 
 int frame_codes(const dar_config* c) { return 1 + c->n_res; }
@@ -53,26 +59,32 @@ Layout make_layout(const dar_config* c) {
   const int g = c->n_heads_q / c->n_heads_kv;
   const int fc = frame_codes(c);
   L.chunk = kAttnChunkDefault;
-  L.nsplit_max = (c->max_len + L.chunk - 1) / L.chunk;
+  L.nsplit_slow = (c->max_len + L.chunk - 1) / L.chunk;
   L.fast_len = has_fast(c) ? c->n_res + 1 : 1;
   L.rope_len = std::max(c->max_len, L.fast_len);
   L.seq_len = std::max(c->max_len, L.fast_len + 1);
   L.vmax = std::max(c->vocab_c0, has_fast(c) ? c->vocab_res : 0);
+  L.nslots = std::max(head_grid(c->vocab_c0), has_fast(c) ? head_grid(c->vocab_res) : 0);
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t at = off;
     off = align_up(off + bytes);
     return at;
   };
-  L.x_s = take(sizeof(float) * d);
-  L.x_f = take(sizeof(float) * 2 * d);
-  L.q = take(sizeof(float) * 2 * qw);
-  L.o = take(sizeof(float) * 2 * qw);
-  L.h = take(sizeof(float) * 2 * F);
-  L.part = take(sizeof(float) * attn_partial_floats(2, c->n_heads_kv, L.nsplit_max, g, c->head_dim));
-  L.logits = take(sizeof(float) * (size_t)fc * L.vmax);
-  L.nslots = std::max(head_grid(c->vocab_c0), has_fast(c) ? head_grid(c->vocab_res) : 0);
-  L.slots = take(sizeof(unsigned long long) * fc * L.nslots);
+  for (int ch = 0; ch < 2; ++ch) {
+    const int M = ch == 0 ? 1 : 2;
+    const int nsplit = ch == 0 ? L.nsplit_slow : 1;
+    L.x[ch] = take(sizeof(float) * M * d);
+    L.q[ch] = take(sizeof(float) * M * qw);
+    L.o[ch] = take(sizeof(float) * M * qw);
+    L.h[ch] = take(sizeof(float) * M * F);
+    L.part[ch] = take(sizeof(float) * attn_partial_floats(M, c->n_heads_kv, nsplit, g, c->head_dim));
+  }
+  L.ht = take(sizeof(float) * d);
+  L.logits0 = take(sizeof(float) * c->vocab_c0);
+  L.flogits = take(sizeof(float) * (size_t)fc * L.vmax);
+  L.slots0 = take(sizeof(unsigned long long) * L.nslots);
+  L.slotsf = take(sizeof(unsigned long long) * L.nslots);
   L.pred = take(sizeof(int) * fc);
   L.committed = take(sizeof(int) * fc);
   L.forced = take(sizeof(int) * fc);
@@ -161,6 +173,15 @@ struct LaunchRec {
   int kind, layer;
 };
 
+// One dependent chain of launches with its own stream, scratch and graph.
+struct Chain {
+  float *x = nullptr, *q = nullptr, *o = nullptr, *h = nullptr, *part = nullptr;
+  int M = 1;
+  hipStream_t s = nullptr;
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t exec = nullptr;
+};
+
 struct dar_ctx {
   dar_config cfg{};
   Layout L{};
@@ -173,25 +194,23 @@ struct dar_ctx {
   const void* fast_head = nullptr;
   const float* fast_head_scale = nullptr;
 
-  hipStream_t stream = nullptr;
-  hipStream_t cap = nullptr;
-  hipGraph_t graph = nullptr;
-  hipGraphExec_t exec = nullptr;
+  hipStream_t stream = nullptr;  // the caller's stream
+  Chain cs, cf;                  // slow chain (frame i+1) and fast chain (frame i)
+  hipEvent_t ev_start = nullptr, ev_c0 = nullptr, ev_f_done = nullptr, ev_s_done = nullptr;
   bool use_graph = true;
 
   char* ws = nullptr;
-  float *x_s, *x_f, *q, *o, *h, *part, *logits;
-  unsigned long long* slots;
-  int *pred, *committed, *forced, *flags, *pos, *seqpos, *ring;
+  float *ht, *logits0, *flogits;
+  unsigned long long *slots0, *slotsf;
+  int *pred, *committed, *forced, *flags, *pos_s, *pos_f, *seqpos, *ring;
   float2* rope;
   uint16_t *ks, *vs, *kf, *vf;
 
-  int pos_host = 0;
+  int pos_host = 0;       // slow position of the next frame to decode
   bool prefilled = false;
   bool force_dev = false;
   std::string err;
 
-  // profiling
   std::vector<hipEvent_t> events;
   std::vector<LaunchRec> recs;
   bool profiling = false;
@@ -208,9 +227,9 @@ int hip_fail(dar_ctx* c, hipError_t e, const char* what) {
   return DAR_E_HIP;
 }
 
-#define DAR_HIP(ctx, call, what)             \
-  do {                                       \
-    hipError_t e_ = (call);                  \
+#define DAR_HIP(ctx, call, what)                           \
+  do {                                                     \
+    hipError_t e_ = (call);                                \
     if (e_ != hipSuccess) return hip_fail(ctx, e_, what); \
   } while (0)
 
@@ -233,9 +252,9 @@ hipError_t tracked(dar_ctx* c, hipStream_t s, int kind, int layer, F&& launch) {
 
 enum Kind { K_QKV = 0, K_ATTN = 1, K_WO = 2, K_W13 = 3, K_W2 = 4, K_HEAD = 5, K_OTHER = 6 };
 
-// One decoder layer over M input rows at device position *pos (row m at +m).
-hipError_t enqueue_layer(dar_ctx* c, hipStream_t s, const dar_layer_weights& w, int layer_tag, float* x, int M,
-                         const int* pos, uint16_t* kc, uint16_t* vc, int cache_len) {
+// One decoder layer of a chain over M input rows at device position *pos (row m at +m).
+hipError_t enqueue_layer(dar_ctx* c, const Chain& ch, hipStream_t s, const dar_layer_weights& w, int layer_tag,
+                         int M, const int* pos, uint16_t* kc, uint16_t* vc, int cache_len, int nsplit_max) {
   const dar_config& g = c->cfg;
   const int d = g.d_model, qw = g.n_heads_q * g.head_dim;
   const int wt = c->fp8 ? W_FP8 : W_BF16;
@@ -246,7 +265,7 @@ hipError_t enqueue_layer(dar_ctx* c, hipStream_t s, const dar_layer_weights& w, 
   qa.scale = c->fp8 ? w.wqkv_scale : nullptr;
   qa.K = d;
   qa.M = M;
-  qa.x = x;
+  qa.x = ch.x;
   qa.x_stride = d;
   qa.gain = static_cast<const uint16_t*>(w.attn_norm);
   qa.eps = g.rms_eps;
@@ -255,7 +274,7 @@ hipError_t enqueue_layer(dar_ctx* c, hipStream_t s, const dar_layer_weights& w, 
   qa.head_dim = g.head_dim;
   qa.pos = pos;
   qa.rope = c->rope;
-  qa.q_out = c->q;
+  qa.q_out = ch.q;
   qa.q_stride = qw;
   qa.kc = kc;
   qa.vc = vc;
@@ -264,7 +283,7 @@ hipError_t enqueue_layer(dar_ctx* c, hipStream_t s, const dar_layer_weights& w, 
   if (e != hipSuccess) return e;
 
   AttnArgs aa{};
-  aa.q = c->q;
+  aa.q = ch.q;
   aa.q_stride = qw;
   aa.K = kc;
   aa.V = vc;
@@ -274,10 +293,10 @@ hipError_t enqueue_layer(dar_ctx* c, hipStream_t s, const dar_layer_weights& w, 
   aa.n_heads_kv = g.n_heads_kv;
   aa.head_dim = g.head_dim;
   aa.chunk = c->L.chunk;
-  aa.nsplit_max = (cache_len + c->L.chunk - 1) / c->L.chunk;
+  aa.nsplit_max = nsplit_max;
   aa.M = M;
-  aa.part = c->part;
-  aa.out = c->o;
+  aa.part = ch.part;
+  aa.out = ch.o;
   aa.out_stride = qw;
   e = tracked(c, s, K_ATTN, layer_tag, [&] { return launch_attn(aa, s); });
   if (e != hipSuccess) return e;
@@ -288,11 +307,9 @@ hipError_t enqueue_layer(dar_ctx* c, hipStream_t s, const dar_layer_weights& w, 
   wo.rows = d;
   wo.K = qw;
   wo.M = M;
-  wo.x = c->o;
+  wo.x = ch.o;
   wo.x_stride = qw;
-  wo.gain = nullptr;
-  wo.eps = 0.f;
-  wo.y = x;
+  wo.y = ch.x;
   wo.y_stride = d;
   wo.accumulate = 1;
   e = tracked(c, s, K_WO, layer_tag, [&] { return launch_gemv(wt, wo, s); });
@@ -306,11 +323,11 @@ hipError_t enqueue_layer(dar_ctx* c, hipStream_t s, const dar_layer_weights& w, 
   sa.F = g.ffn_dim;
   sa.K = d;
   sa.M = M;
-  sa.x = x;
+  sa.x = ch.x;
   sa.x_stride = d;
   sa.gain = static_cast<const uint16_t*>(w.ffn_norm);
   sa.eps = g.rms_eps;
-  sa.h = c->h;
+  sa.h = ch.h;
   sa.h_stride = g.ffn_dim;
   e = tracked(c, s, K_W13, layer_tag, [&] { return launch_swiglu(wt, sa, s); });
   if (e != hipSuccess) return e;
@@ -321,40 +338,44 @@ hipError_t enqueue_layer(dar_ctx* c, hipStream_t s, const dar_layer_weights& w, 
   w2.rows = d;
   w2.K = g.ffn_dim;
   w2.M = M;
-  w2.x = c->h;
+  w2.x = ch.h;
   w2.x_stride = g.ffn_dim;
-  w2.gain = nullptr;
-  w2.eps = 0.f;
-  w2.y = x;
+  w2.y = ch.x;
   w2.y_stride = d;
   w2.accumulate = 1;
   return tracked(c, s, K_W2, layer_tag, [&] { return launch_gemv(wt, w2, s); });
 }
 
-hipError_t enqueue_slow_layers(dar_ctx* c, hipStream_t s) {
+// Slow chain: the slow layers at *pos_s over the slow residual; with_head adds the
+// codebook-0 head (logits, per-workgroup maxima, h_t) and advances pos_s.
+hipError_t enqueue_slow(dar_ctx* c, hipStream_t s, bool with_head) {
   const dar_config& g = c->cfg;
   const size_t per_layer = (size_t)g.n_heads_kv * g.max_len * g.head_dim;
   for (int l = 0; l < g.n_layers_slow; ++l) {
-    hipError_t e = enqueue_layer(c, s, c->slow[l], l, c->x_s, 1, c->pos, c->ks + l * per_layer,
-                                 c->vs + l * per_layer, g.max_len);
+    hipError_t e = enqueue_layer(c, c->cs, s, c->slow[l], l, 1, c->pos_s, c->ks + l * per_layer,
+                                 c->vs + l * per_layer, g.max_len, c->L.nsplit_slow);
     if (e != hipSuccess) return e;
   }
-  return hipSuccess;
+  if (!with_head) return hipSuccess;
+  HeadArgs h0{};
+  h0.W = c->w0;
+  h0.scale = nullptr;
+  h0.rows = g.vocab_c0;
+  h0.K = g.d_model;
+  h0.x = c->cs.x;
+  h0.gain = c->slow_fn;
+  h0.eps = g.rms_eps;
+  h0.logits = c->logits0;
+  h0.slots = c->slots0;
+  h0.anomalies = c->flags + 1;
+  h0.h_out = c->ht;
+  h0.pos_inc = c->pos_s;
+  return tracked(c, s, K_HEAD, 0, [&] { return launch_head(W_BF16, h0, s); });
 }
 
-HeadArgs head_args(dar_ctx* c, int k) {
-  HeadArgs h{};
-  h.K = c->cfg.d_model;
-  h.eps = c->cfg.rms_eps;
-  h.logits = c->logits + (size_t)k * c->L.vmax;
-  h.slots = c->slots + (size_t)k * c->L.nslots;
-  h.anomalies = c->flags + 1;
-  return h;
-}
-
-CommitArgs commit_args(dar_ctx* c, int k, int rows) {
+CommitArgs commit_common(dar_ctx* c, int k, const unsigned long long* slots, int rows) {
   CommitArgs a{};
-  a.slots = c->slots + (size_t)k * c->L.nslots;
+  a.slots = slots;
   a.nslots = head_grid(rows);
   a.code_index = k;
   a.frame_codes = frame_codes(&c->cfg);
@@ -363,114 +384,162 @@ CommitArgs commit_args(dar_ctx* c, int k, int rows) {
   a.forced = c->forced;
   a.force_flag = c->flags + 0;
   a.ring = c->ring;
-  a.pos = c->pos;
+  a.pos = c->pos_f;
   a.K = c->cfg.d_model;
   return a;
 }
 
-// Codebook-0 head and the fast AR: the tail of every frame.
-hipError_t enqueue_tail(dar_ctx* c, hipStream_t s) {
+// Start of the fast chain: commit codebook 0 of the frame (argmax of the slow
+// head, or the forced code), move its logits and h_t into the frame's buffers,
+// write the fast inputs [h_t, E0[c0]] and the next slow input W0[c0].
+hipError_t enqueue_commit0(dar_ctx* c, hipStream_t s) {
   const dar_config& g = c->cfg;
   const int d = g.d_model;
   const bool fast = has_fast(&g);
+  CommitArgs a = commit_common(c, 0, c->slots0, g.vocab_c0);
+  a.pos_inc = fast ? nullptr : c->pos_f;
+  a.next_table = fast ? c->fast_emb[0] : nullptr;
+  a.next_rows = g.vocab_c0;
+  a.next_x = c->cf.x + d;
+  a.slow_table = c->w0;
+  a.slow_rows = g.vocab_c0;
+  a.slow_x = c->cs.x;
+  a.copy_src[0] = c->logits0;
+  a.copy_dst[0] = c->flogits;
+  a.copy_n[0] = g.vocab_c0;
+  if (fast) {
+    a.copy_src[1] = c->ht;
+    a.copy_dst[1] = c->cf.x;
+    a.copy_n[1] = d;
+  }
+  return tracked(c, s, K_OTHER, 0, [&] { return launch_commit(a, s); });
+}
+
+// The fast AR of one frame: pass 1 over fast positions 0 and 1, passes 2..R
+// over position k, each followed by the shared head and its commit.
+hipError_t enqueue_fast(dar_ctx* c, hipStream_t s) {
+  const dar_config& g = c->cfg;
+  const int d = g.d_model;
   const int wt = c->fp8 ? W_FP8 : W_BF16;
-  hipError_t e;
-
-  HeadArgs h0 = head_args(c, 0);
-  h0.W = c->w0;
-  h0.scale = nullptr;
-  h0.rows = g.vocab_c0;
-  h0.x = c->x_s;
-  h0.gain = c->slow_fn;
-  h0.h_out = fast ? c->x_f : nullptr;  // h_t: fast input at fast position 0
-  e = tracked(c, s, K_HEAD, 0, [&] { return launch_head(W_BF16, h0, s); });
-  if (e != hipSuccess) return e;
-  CommitArgs c0 = commit_args(c, 0, g.vocab_c0);
-  c0.pos_inc = fast ? nullptr : c->pos;
-  c0.next_table = fast ? c->fast_emb[0] : nullptr;
-  c0.next_rows = g.vocab_c0;
-  c0.next_x = c->x_f + d;
-  c0.slow_table = c->w0;
-  c0.slow_rows = g.vocab_c0;
-  c0.slow_x = c->x_s;
-  e = tracked(c, s, K_OTHER, 0, [&] { return launch_commit(c0, s); });
-  if (e != hipSuccess || !fast) return e;
-
   const size_t per_layer = (size_t)g.n_heads_kv * c->L.fast_len * g.head_dim;
   for (int k = 1; k <= g.n_res; ++k) {
     const int M = (k == 1) ? 2 : 1;
     const int* fpos = c->seqpos + (k == 1 ? 0 : k);
     for (int l = 0; l < g.n_layers_fast; ++l) {
-      e = enqueue_layer(c, s, c->fast[l], 1000 * k + l, c->x_f, M, fpos, c->kf + l * per_layer,
-                        c->vf + l * per_layer, c->L.fast_len);
+      hipError_t e = enqueue_layer(c, c->cf, s, c->fast[l], 1000 * k + l, M, fpos, c->kf + l * per_layer,
+                                   c->vf + l * per_layer, c->L.fast_len, 1);
       if (e != hipSuccess) return e;
     }
-    HeadArgs hk = head_args(c, k);
+    HeadArgs hk{};
     hk.W = c->fast_head;
     hk.scale = c->fp8 ? c->fast_head_scale : nullptr;
     hk.rows = g.vocab_res;
-    hk.x = c->x_f + (size_t)(M - 1) * d;
+    hk.K = d;
+    hk.x = c->cf.x + (size_t)(M - 1) * d;
     hk.gain = c->fast_fn;
-    e = tracked(c, s, K_HEAD, k, [&] { return launch_head(wt, hk, s); });
+    hk.eps = g.rms_eps;
+    hk.logits = c->flogits + (size_t)k * c->L.vmax;
+    hk.slots = c->slotsf;
+    hk.anomalies = c->flags + 1;
+    hipError_t e = tracked(c, s, K_HEAD, k, [&] { return launch_head(wt, hk, s); });
     if (e != hipSuccess) return e;
-    CommitArgs ck = commit_args(c, k, g.vocab_res);
-    ck.pos_inc = (k == g.n_res) ? c->pos : nullptr;
+    CommitArgs ck = commit_common(c, k, c->slotsf, g.vocab_res);
+    ck.pos_inc = (k == g.n_res) ? c->pos_f : nullptr;
     ck.next_table = (k < g.n_res) ? c->fast_emb[k] : nullptr;
     ck.next_rows = g.vocab_res;
-    ck.next_x = c->x_f;
+    ck.next_x = c->cf.x;
     e = tracked(c, s, K_OTHER, k, [&] { return launch_commit(ck, s); });
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
 }
 
-hipError_t enqueue_frame(dar_ctx* c, hipStream_t s) {
-  hipError_t e = enqueue_slow_layers(c, s);
-  if (e != hipSuccess) return e;
-  return enqueue_tail(c, s);
+int capture(dar_ctx* c, Chain& ch, hipError_t (*body)(dar_ctx*, hipStream_t), const char* what) {
+  if (ch.exec) return DAR_OK;
+  DAR_HIP(c, hipStreamBeginCapture(ch.s, hipStreamCaptureModeThreadLocal), "begin capture");
+  hipError_t e = body(c, ch.s);
+  hipGraph_t g = nullptr;
+  hipError_t e2 = hipStreamEndCapture(ch.s, &g);
+  if (e != hipSuccess) {
+    if (g) (void)hipGraphDestroy(g);
+    return hip_fail(c, e, what);
+  }
+  if (e2 != hipSuccess) return hip_fail(c, e2, "end capture");
+  ch.graph = g;
+  DAR_HIP(c, hipGraphInstantiate(&ch.exec, ch.graph, nullptr, nullptr, 0), "instantiate graph");
+  return DAR_OK;
 }
 
-int copy_outputs(dar_ctx* c, int32_t* codes_out, float* logits_out) {
+hipError_t body_fast(dar_ctx* c, hipStream_t s) { return enqueue_fast(c, s); }
+hipError_t body_slow(dar_ctx* c, hipStream_t s) { return enqueue_slow(c, s, true); }
+
+int copy_outputs(dar_ctx* c, hipStream_t s, int32_t* codes_out, float* logits_out) {
   const dar_config& g = c->cfg;
-  if (codes_out) DAR_HIP(c, launch_copy_i32(c->pred, codes_out, frame_codes(&g), c->stream), "copy codes");
+  if (codes_out) DAR_HIP(c, launch_copy_i32(c->pred, codes_out, frame_codes(&g), s), "copy codes");
   if (logits_out) {
     const size_t fc = frame_codes(&g);
     for (size_t k = 0; k < fc; ++k) {
       const int V = (k == 0) ? g.vocab_c0 : g.vocab_res;
       DAR_HIP(c,
-              hipMemcpyAsync(logits_out + k * c->L.vmax, c->logits + k * c->L.vmax, sizeof(float) * V,
-                             hipMemcpyDeviceToDevice, c->stream),
+              hipMemcpyAsync(logits_out + k * c->L.vmax, c->flogits + k * c->L.vmax, sizeof(float) * V,
+                             hipMemcpyDeviceToDevice, s),
               "copy logits");
     }
   }
   return DAR_OK;
 }
 
-int set_force(dar_ctx* c, const int32_t* forced) {
+int set_force(dar_ctx* c, hipStream_t s, const int32_t* forced) {
   const int fc = frame_codes(&c->cfg);
   if (forced) {
-    DAR_HIP(c, launch_set_forced(forced, fc, c->forced, c->flags + 0, c->stream), "set forced");
+    DAR_HIP(c, launch_set_forced(forced, fc, c->forced, c->flags + 0, s), "set forced");
     c->force_dev = true;
   } else if (c->force_dev) {
-    DAR_HIP(c, launch_set_forced(nullptr, fc, c->forced, c->flags + 0, c->stream), "clear forced");
+    DAR_HIP(c, launch_set_forced(nullptr, fc, c->forced, c->flags + 0, s), "clear forced");
     c->force_dev = false;
   }
   return DAR_OK;
 }
 
-int ensure_graph(dar_ctx* c) {
-  if (c->exec) return DAR_OK;
-  DAR_HIP(c, hipStreamBeginCapture(c->cap, hipStreamCaptureModeThreadLocal), "begin capture");
-  hipError_t e = enqueue_frame(c, c->cap);
-  hipGraph_t g = nullptr;
-  hipError_t e2 = hipStreamEndCapture(c->cap, &g);
-  if (e != hipSuccess) {
-    if (g) (void)hipGraphDestroy(g);
-    return hip_fail(c, e, "capture frame");
+// One pipeline step: the fast chain finishes frame i (commit c0, fast AR,
+// outputs) while the slow chain computes the slow step and codebook-0 head of
+// frame i+1. The slow chain starts once c0 of frame i is committed (its input).
+int pipeline_step(dar_ctx* c, const int32_t* forced, int32_t* codes_out, float* logits_out, bool run_slow) {
+  const bool fast = has_fast(&c->cfg);
+  if (c->use_graph) {
+    int st = fast ? capture(c, c->cf, body_fast, "capture fast chain") : DAR_OK;
+    if (st == DAR_OK && run_slow) st = capture(c, c->cs, body_slow, "capture slow chain");
+    if (st != DAR_OK) return st;
   }
-  if (e2 != hipSuccess) return hip_fail(c, e2, "end capture");
-  c->graph = g;
-  DAR_HIP(c, hipGraphInstantiate(&c->exec, c->graph, nullptr, nullptr, 0), "instantiate graph");
+  hipStream_t sf = c->cf.s, ss = c->cs.s;
+  DAR_HIP(c, hipEventRecord(c->ev_start, c->stream), "record start");
+  DAR_HIP(c, hipStreamWaitEvent(sf, c->ev_start, 0), "wait start");
+  DAR_HIP(c, hipStreamWaitEvent(sf, c->ev_s_done, 0), "wait slow chain");
+  int st = set_force(c, sf, forced);
+  if (st != DAR_OK) return st;
+  DAR_HIP(c, enqueue_commit0(c, sf), "commit codebook 0");
+  DAR_HIP(c, hipEventRecord(c->ev_c0, sf), "record c0");
+  if (run_slow) {
+    DAR_HIP(c, hipStreamWaitEvent(ss, c->ev_c0, 0), "slow waits c0");
+    if (c->use_graph) {
+      DAR_HIP(c, hipGraphLaunch(c->cs.exec, ss), "slow graph launch");
+    } else {
+      DAR_HIP(c, enqueue_slow(c, ss, true), "slow chain");
+    }
+    DAR_HIP(c, hipEventRecord(c->ev_s_done, ss), "record slow done");
+  }
+  if (fast) {
+    if (c->use_graph) {
+      DAR_HIP(c, hipGraphLaunch(c->cf.exec, sf), "fast graph launch");
+    } else {
+      DAR_HIP(c, enqueue_fast(c, sf), "fast chain");
+    }
+  }
+  st = copy_outputs(c, sf, codes_out, logits_out);
+  if (st != DAR_OK) return st;
+  DAR_HIP(c, hipEventRecord(c->ev_f_done, sf), "record fast done");
+  DAR_HIP(c, hipStreamWaitEvent(c->stream, c->ev_f_done, 0), "join fast");
+  DAR_HIP(c, hipStreamWaitEvent(c->stream, c->ev_s_done, 0), "join slow");
   return DAR_OK;
 }
 
@@ -566,19 +635,26 @@ int dar_create(const dar_config* cfg, const dar_weights* w, void* workspace, siz
   c->stream = static_cast<hipStream_t>(stream);
   c->ws = static_cast<char*>(workspace);
   char* b = c->ws;
-  c->x_s = reinterpret_cast<float*>(b + L.x_s);
-  c->x_f = reinterpret_cast<float*>(b + L.x_f);
-  c->q = reinterpret_cast<float*>(b + L.q);
-  c->o = reinterpret_cast<float*>(b + L.o);
-  c->h = reinterpret_cast<float*>(b + L.h);
-  c->part = reinterpret_cast<float*>(b + L.part);
-  c->logits = reinterpret_cast<float*>(b + L.logits);
-  c->slots = reinterpret_cast<unsigned long long*>(b + L.slots);
+  Chain* chains[2] = {&c->cs, &c->cf};
+  for (int i = 0; i < 2; ++i) {
+    chains[i]->x = reinterpret_cast<float*>(b + L.x[i]);
+    chains[i]->q = reinterpret_cast<float*>(b + L.q[i]);
+    chains[i]->o = reinterpret_cast<float*>(b + L.o[i]);
+    chains[i]->h = reinterpret_cast<float*>(b + L.h[i]);
+    chains[i]->part = reinterpret_cast<float*>(b + L.part[i]);
+    chains[i]->M = i == 0 ? 1 : 2;
+  }
+  c->ht = reinterpret_cast<float*>(b + L.ht);
+  c->logits0 = reinterpret_cast<float*>(b + L.logits0);
+  c->flogits = reinterpret_cast<float*>(b + L.flogits);
+  c->slots0 = reinterpret_cast<unsigned long long*>(b + L.slots0);
+  c->slotsf = reinterpret_cast<unsigned long long*>(b + L.slotsf);
   c->pred = reinterpret_cast<int*>(b + L.pred);
   c->committed = reinterpret_cast<int*>(b + L.committed);
   c->forced = reinterpret_cast<int*>(b + L.forced);
   c->flags = reinterpret_cast<int*>(b + L.flags);
-  c->pos = reinterpret_cast<int*>(b + L.pos);
+  c->pos_s = reinterpret_cast<int*>(b + L.pos);
+  c->pos_f = c->pos_s + 1;
   c->seqpos = reinterpret_cast<int*>(b + L.seqpos);
   c->ring = reinterpret_cast<int*>(b + L.ring);
   c->rope = reinterpret_cast<float2*>(b + L.rope);
@@ -589,12 +665,18 @@ int dar_create(const dar_config* cfg, const dar_weights* w, void* workspace, siz
 
   auto fail = [&](hipError_t e, const char* what) {
     g_create_error = std::string(what) + ": " + hipGetErrorString(e);
-    if (c->cap) (void)hipStreamDestroy(c->cap);
+    for (Chain* ch : chains)
+      if (ch->s) (void)hipStreamDestroy(ch->s);
+    for (hipEvent_t ev : {c->ev_start, c->ev_c0, c->ev_f_done, c->ev_s_done})
+      if (ev) (void)hipEventDestroy(ev);
     delete c;
     return DAR_E_HIP;
   };
-  hipError_t e = hipStreamCreateWithFlags(&c->cap, hipStreamNonBlocking);
-  if (e != hipSuccess) return fail(e, "create capture stream");
+  hipError_t e;
+  for (Chain* ch : chains)
+    if ((e = hipStreamCreateWithFlags(&ch->s, hipStreamNonBlocking)) != hipSuccess) return fail(e, "create stream");
+  for (hipEvent_t* ev : {&c->ev_start, &c->ev_c0, &c->ev_f_done, &c->ev_s_done})
+    if ((e = hipEventCreateWithFlags(ev, hipEventDisableTiming)) != hipSuccess) return fail(e, "create event");
 
   // RoPE table: angle p * base^(-2i/hd) in double, cos/sin stored as fp32.
   const int half = cfg->head_dim / 2;
@@ -607,9 +689,9 @@ int dar_create(const dar_config* cfg, const dar_weights* w, void* workspace, siz
   }
   std::vector<int> seq(L.seq_len);
   for (int i = 0; i < L.seq_len; ++i) seq[i] = i;
-  // zero everything from the activations to the ring (counters, slots, flags included)
-  const size_t zero_words = (L.rope - L.x_s) / 4;
-  if ((e = launch_fill_u32(reinterpret_cast<unsigned*>(b + L.x_s), zero_words, c->stream)) != hipSuccess)
+  // zero everything from the activations to the ring (slots, flags, positions included)
+  const size_t zero_words = L.rope / 4;
+  if ((e = launch_fill_u32(reinterpret_cast<unsigned*>(b), zero_words, c->stream)) != hipSuccess)
     return fail(e, "zero workspace");
   if ((e = hipMemcpyAsync(c->rope, rope.data(), rope.size() * sizeof(float2), hipMemcpyHostToDevice, c->stream)) !=
       hipSuccess)
@@ -618,6 +700,7 @@ int dar_create(const dar_config* cfg, const dar_weights* w, void* workspace, siz
       hipSuccess)
     return fail(e, "upload positions");
   if ((e = hipStreamSynchronize(c->stream)) != hipSuccess) return fail(e, "synchronize create");
+  if ((e = hipEventRecord(c->ev_s_done, c->cs.s)) != hipSuccess) return fail(e, "record event");
   *ctx_out = c;
   return DAR_OK;
 }
@@ -644,15 +727,20 @@ int dar_prefill(dar_ctx* c, int32_t batch, const int32_t* tokens, const int32_t*
   }
   c->prefilled = false;
   const int d = c->cfg.d_model;
-  int st = set_force(c, forced);
-  if (st != DAR_OK) return st;
+  hipStream_t ss = c->cs.s;
+  // the slow chain runs the prompt token by token after anything already queued
+  DAR_HIP(c, hipEventRecord(c->ev_start, c->stream), "record start");
+  DAR_HIP(c, hipStreamWaitEvent(ss, c->ev_start, 0), "wait start");
+  DAR_HIP(c, hipStreamWaitEvent(ss, c->ev_f_done, 0), "wait fast chain");
   for (int p = 0; p < n; ++p) {
-    DAR_HIP(c, launch_embed(c->w0, c->cfg.vocab_c0, d, tokens + p, c->x_s, c->pos, p, c->flags + 1, c->stream),
+    DAR_HIP(c, launch_embed(c->w0, c->cfg.vocab_c0, d, tokens + p, c->cs.x, c->pos_s, p, c->flags + 1, ss),
             "prefill embed");
-    DAR_HIP(c, enqueue_slow_layers(c, c->stream), "prefill layers");
+    DAR_HIP(c, enqueue_slow(c, ss, p == n - 1), "prefill layers");
   }
-  DAR_HIP(c, enqueue_tail(c, c->stream), "prefill frame 0");
-  st = copy_outputs(c, codes_out, logits_out);
+  // frame 0 sits at position n-1; the slow head above moved pos_s to n
+  DAR_HIP(c, launch_fill_i32(c->pos_f, 1, n - 1, ss), "set frame position");
+  DAR_HIP(c, hipEventRecord(c->ev_s_done, ss), "record slow done");
+  const int st = pipeline_step(c, forced, codes_out, logits_out, n < c->cfg.max_len);
   if (st != DAR_OK) return st;
   c->pos_host = n;
   c->prefilled = true;
@@ -669,16 +757,7 @@ int dar_decode_frame(dar_ctx* c, const int32_t* forced, int32_t* codes_out, floa
     c->err = "position reached max_len";
     return DAR_E_CAPACITY;
   }
-  int st = set_force(c, forced);
-  if (st != DAR_OK) return st;
-  if (c->use_graph) {
-    st = ensure_graph(c);
-    if (st != DAR_OK) return st;
-    DAR_HIP(c, hipGraphLaunch(c->exec, c->stream), "graph launch");
-  } else {
-    DAR_HIP(c, enqueue_frame(c, c->stream), "eager frame");
-  }
-  st = copy_outputs(c, codes_out, logits_out);
+  const int st = pipeline_step(c, forced, codes_out, logits_out, c->pos_host + 1 < c->cfg.max_len);
   if (st != DAR_OK) return st;
   c->pos_host += 1;
   return DAR_OK;
@@ -687,17 +766,21 @@ int dar_decode_frame(dar_ctx* c, const int32_t* forced, int32_t* codes_out, floa
 int dar_destroy(dar_ctx* c) {
   if (!c) return DAR_OK;
   (void)hipStreamSynchronize(c->stream);
-  if (c->exec) (void)hipGraphExecDestroy(c->exec);
-  if (c->graph) (void)hipGraphDestroy(c->graph);
+  for (Chain* ch : {&c->cs, &c->cf}) {
+    if (ch->s) (void)hipStreamSynchronize(ch->s);
+    if (ch->exec) (void)hipGraphExecDestroy(ch->exec);
+    if (ch->graph) (void)hipGraphDestroy(ch->graph);
+    if (ch->s) (void)hipStreamDestroy(ch->s);
+  }
   for (hipEvent_t ev : c->events) (void)hipEventDestroy(ev);
-  if (c->cap) (void)hipStreamDestroy(c->cap);
+  for (hipEvent_t ev : {c->ev_start, c->ev_c0, c->ev_f_done, c->ev_s_done})
+    if (ev) (void)hipEventDestroy(ev);
   delete c;
   return DAR_OK;
 }
 
 int dar_reset(dar_ctx* c) {
   if (!c) return DAR_E_INVAL;
-  DAR_HIP(c, launch_fill_i32(c->pos, 1, 0, c->stream), "reset position");
   DAR_HIP(c, launch_fill_i32(c->flags + 1, 1, 0, c->stream), "reset counters");
   c->pos_host = 0;
   c->prefilled = false;
@@ -872,24 +955,35 @@ int dar_profile_frame(dar_ctx* c, int32_t cap, float* ms_out, int32_t* kind_out,
     return DAR_E_CAPACITY;
   }
   const dar_config& g = c->cfg;
-  const int launches = 5 * g.n_layers_slow + 2 + (g.n_res > 0 ? g.n_res * (5 * g.n_layers_fast + 2) : 0);
+  const bool run_slow = c->pos_host + 1 < g.max_len;
+  const int launches = 1 + (g.n_res > 0 ? g.n_res * (5 * g.n_layers_fast + 2) : 0) +
+                       (run_slow ? 5 * g.n_layers_slow + 1 : 0);
   if (cap < launches) {
     c->err = "profile capacity below the frame's launch count";
     return DAR_E_INVAL;
   }
-  int st = set_force(c, nullptr);
-  if (st != DAR_OK) return st;
   while ((int)c->events.size() < 2 * cap) {
     hipEvent_t ev;
     DAR_HIP(c, hipEventCreate(&ev), "create event");
     c->events.push_back(ev);
   }
+  // one stream, fast chain of this frame then slow chain of the next, every launch bracketed
+  hipStream_t s = c->cf.s;
+  DAR_HIP(c, hipEventRecord(c->ev_start, c->stream), "record start");
+  DAR_HIP(c, hipStreamWaitEvent(s, c->ev_start, 0), "wait start");
+  DAR_HIP(c, hipStreamWaitEvent(s, c->ev_s_done, 0), "wait slow chain");
+  int st = set_force(c, s, nullptr);
+  if (st != DAR_OK) return st;
   c->recs.clear();
   c->profiling = true;
-  hipError_t e = enqueue_frame(c, c->stream);
+  hipError_t e = enqueue_commit0(c, s);
+  if (e == hipSuccess && has_fast(&g)) e = enqueue_fast(c, s);
+  if (e == hipSuccess && run_slow) e = enqueue_slow(c, s, true);
   c->profiling = false;
   if (e != hipSuccess) return hip_fail(c, e, "profiled frame");
-  DAR_HIP(c, hipStreamSynchronize(c->stream), "synchronize profile");
+  DAR_HIP(c, hipEventRecord(c->ev_f_done, s), "record fast done");
+  DAR_HIP(c, hipEventRecord(c->ev_s_done, s), "record slow done");
+  DAR_HIP(c, hipStreamSynchronize(s), "synchronize profile");
   const int n = (int)c->recs.size();
   for (int i = 0; i < n && i < cap; ++i) {
     float ms = 0.f;
