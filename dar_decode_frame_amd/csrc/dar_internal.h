@@ -119,13 +119,38 @@ struct AttnArgs {
   int out_stride;
 };
 
-hipError_t launch_gemv(int wtype, const GemvArgs& a, hipStream_t s);
-hipError_t launch_qkv(int wtype, const QkvArgs& a, hipStream_t s);
-hipError_t launch_swiglu(int wtype, const SwigluArgs& a, hipStream_t s);
-hipError_t launch_head(int wtype, const HeadArgs& a, hipStream_t s);
-hipError_t launch_commit(const CommitArgs& a, hipStream_t s);
+enum TaskKind : int {
+  T_NONE = 0,
+  T_QKV,        // QkvArgs
+  T_ATTN,       // AttnArgs: split-K attention (direct output when nsplit_max == 1)
+  T_COMBINE,    // AttnArgs: merge the splits
+  T_GEMV,       // GemvArgs
+  T_SWIGLU,     // SwigluArgs
+  T_HEAD,       // HeadArgs, weights of the launch's weight type
+  T_HEAD_BF16,  // HeadArgs, bf16 weights (the tied codebook-0 head in every mode)
+  T_COMMIT      // CommitArgs, one block
+};
+
+// One stage of a chain: its kind, input rows and arguments.
+struct Task {
+  int kind, M;
+  union {
+    GemvArgs gemv;
+    QkvArgs qkv;
+    SwigluArgs swiglu;
+    AttnArgs attn;
+    HeadArgs head;
+    CommitArgs commit;
+  };
+};
+
+
 int head_grid(int rows);
-hipError_t launch_attn(const AttnArgs& a, hipStream_t s);
+// Launch the kernel specialised for this task (kind, rows M, input width).
+hipError_t launch_task(int wtype, const Task& t, hipStream_t s);
+// Allow the LDS-staged kernels their dynamic LDS; call once before any launch
+// (and outside graph capture).
+hipError_t prepare_kernels();
 
 // x = table[clamp(*tok)] as fp32, *pos_out = pos_value (prefill step input)
 hipError_t launch_embed(const uint16_t* table, int rows, int K, const int* tok, float* x,

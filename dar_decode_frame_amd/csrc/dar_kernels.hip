@@ -8,7 +8,10 @@
 // reduced with DPP, and the small per-token work (RMSNorm, RoPE, KV append,
 // residual add, SiLU*mul, argmax, the next step's embedding gather) folded into
 // the prologue or epilogue of the GEMV that needs it, so that a decoder layer is
-// five launches: QKV, attention, O-projection, W1/W3, W2.
+// five stages: QKV, attention, O-projection, W1/W3, W2. Inputs of up to eight
+// 1 KB chunks per row are held in registers by every wave (no LDS, no barrier,
+// every weight load of a wave issued at once); wider inputs and two-row passes
+// are staged in LDS.
 //
 // Weights: bf16 (two per 32-bit word) or float8_e4m3fn with one fp32 scale per
 // output row (s2-pro-fp8 model card, "Quantization Details"); the scale is
@@ -192,11 +195,11 @@ struct RowStream {
 // Stages M fp32 input rows into LDS, applying RMSNorm when a gain is given:
 // xs = x / sqrt(mean(x^2) + eps) * gain.
 // issue() loads this thread's share (up to NV float4 per row, at clamped
-// indices so the loads go out back to back) into registers; kernels call it
+// indices so the loads go out back to back) into registers; bodies call it
 // before starting their weight stream, so that waiting for these loads (memory
 // counters retire in issue order) never waits for weights. finish() reduces,
 // normalises and writes LDS. Rows longer than NV*1024 loop over the rest after
-// the first block.
+// the first block. `red` is M*kWaves floats of LDS scratch.
 template <int M>
 struct Stager {
   static constexpr int NV = 4;
@@ -243,8 +246,7 @@ struct Stager {
     }
   }
 
-  __device__ __forceinline__ void finish(float* xs, float eps) {
-    __shared__ float red[M][kWaves];
+  __device__ __forceinline__ void finish(float* xs, float* red, float eps) {
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
     const bool one_pass = K <= SPAN;
     float ss[M];
@@ -264,7 +266,7 @@ struct Stager {
 #pragma unroll
     for (int m = 0; m < M; ++m) {
       const float t = wave_sum(ss[m]);
-      if (lane == 0) red[m][wave] = t;
+      if (lane == 0) red[m * kWaves + wave] = t;
     }
     lds_barrier();
     float inv[M];
@@ -272,7 +274,7 @@ struct Stager {
     for (int m = 0; m < M; ++m) {
       float t = 0.f;
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) t += red[m][w];
+      for (int w = 0; w < kWaves; ++w) t += red[m * kWaves + w];
       inv[m] = 1.0f / sqrtf(t / (float)K + eps);
     }
     if (one_pass) {
@@ -317,13 +319,20 @@ __device__ __forceinline__ const char* row_ptr(const void* W, int r, int K) {
   return reinterpret_cast<const char*>(W) + (size_t)r * K * WT::kBytes;
 }
 
+// LDS of the GEMV-shaped bodies: the staged input rows, then small scratch.
+__device__ __forceinline__ float* lds_scratch(char* lds, int M, int K) {
+  return reinterpret_cast<float*>(lds + (((size_t)M * K * 4 + 15) & ~(size_t)15));
+}
+
 // ------------------------------------------------------------------ GEMV --
 
+// y[m][r] (+)= scale[r] * W[r] . x[m]; wave w of block `bid` owns rows
+// (bid*kWaves + w)*RPW .. +RPW.
 template <typename WT, int M, int RPW>
-__global__ __launch_bounds__(kBlock) void k_gemv(GemvArgs a) {
-  extern __shared__ __align__(16) float xs[];
+__device__ __forceinline__ void gemv_body(const GemvArgs& a, int bid, char* lds) {
+  float* xs = reinterpret_cast<float*>(lds);
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-  const int r0 = (blockIdx.x * kWaves + wave) * RPW;
+  const int r0 = (bid * kWaves + wave) * RPW;
   const bool active = r0 < a.rows;
   Stager<M> st;
   st.issue(a.x, a.x_stride, a.K, a.gain);
@@ -336,7 +345,7 @@ __global__ __launch_bounds__(kBlock) void k_gemv(GemvArgs a) {
     for (int i = 0; i < RPW; ++i) base[i] = row_ptr<WT>(a.W, min(r0 + i, a.rows - 1), a.K);
     rs.start(base, a.K, lane);
   }
-  st.finish(xs, a.eps);
+  st.finish(xs, lds_scratch(lds, M, a.K), a.eps);
   if (!active) return;
   float acc[RPW][M];
   rs.run(xs, acc);
@@ -360,12 +369,12 @@ __global__ __launch_bounds__(kBlock) void k_gemv(GemvArgs a) {
 // Wave w handles rotation pairs (head, i) and (head, i + hd/2) so RoPE is
 // applied where both halves are known. Pair p: head = p / (hd/2), i = p % (hd/2).
 template <typename WT, int M>
-__global__ __launch_bounds__(kBlock) void k_qkv(QkvArgs a) {
-  extern __shared__ __align__(16) float xs[];
+__device__ __forceinline__ void qkv_body(const QkvArgs& a, int bid, char* lds) {
+  float* xs = reinterpret_cast<float*>(lds);
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
   const int half = a.head_dim / 2;
   const int n_heads = a.n_heads_q + 2 * a.n_heads_kv;
-  const int p = blockIdx.x * kWaves + wave;
+  const int p = bid * kWaves + wave;
   const bool active = p < n_heads * half;
   const int pc = min(p, n_heads * half - 1);
   const int head = pc / half, i = pc % half;
@@ -377,7 +386,7 @@ __global__ __launch_bounds__(kBlock) void k_qkv(QkvArgs a) {
     const char* base[2] = {row_ptr<WT>(a.W, r1, a.K), row_ptr<WT>(a.W, r2, a.K)};
     rs.start(base, a.K, lane);
   }
-  st.finish(xs, a.eps);
+  st.finish(xs, lds_scratch(lds, M, a.K), a.eps);
   if (!active) return;
   float acc[2][M];
   rs.run(xs, acc);
@@ -417,10 +426,10 @@ __global__ __launch_bounds__(kBlock) void k_qkv(QkvArgs a) {
 // ------------------------------------------------ RMSNorm + W1/W3 + SwiGLU --
 
 template <typename WT, int M>
-__global__ __launch_bounds__(kBlock) void k_swiglu(SwigluArgs a) {
-  extern __shared__ __align__(16) float xs[];
+__device__ __forceinline__ void swiglu_body(const SwigluArgs& a, int bid, char* lds) {
+  float* xs = reinterpret_cast<float*>(lds);
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-  const int r = blockIdx.x * kWaves + wave;
+  const int r = bid * kWaves + wave;
   const bool active = r < a.F;
   Stager<M> st;
   st.issue(a.x, a.x_stride, a.K, a.gain);
@@ -430,7 +439,7 @@ __global__ __launch_bounds__(kBlock) void k_swiglu(SwigluArgs a) {
     const char* base[2] = {row_ptr<WT>(a.W1, rc, a.K), row_ptr<WT>(a.W3, rc, a.K)};
     rs.start(base, a.K, lane);
   }
-  st.finish(xs, a.eps);
+  st.finish(xs, lds_scratch(lds, M, a.K), a.eps);
   if (!active) return;
   float acc[2][M];
   rs.run(xs, acc);
@@ -447,7 +456,7 @@ __global__ __launch_bounds__(kBlock) void k_swiglu(SwigluArgs a) {
   }
 }
 
-// ----------------------------------------- RMSNorm + head + argmax + commit --
+// ----------------------------------------- RMSNorm + head + per-block argmax --
 
 // Order-preserving key: larger float -> larger key; NaN -> smallest key.
 __device__ __forceinline__ unsigned long long argmax_key(float v, int idx) {
@@ -462,12 +471,13 @@ __device__ __forceinline__ unsigned long long argmax_key(float v, int idx) {
 }
 
 template <typename WT>
-__global__ __launch_bounds__(kBlock) void k_head(HeadArgs a) {
-  extern __shared__ __align__(16) float xs[];
-  __shared__ unsigned long long wbest[kWaves];
+__device__ __forceinline__ void head_body(const HeadArgs& a, int bid, char* lds) {
+  float* xs = reinterpret_cast<float*>(lds);
+  float* red = lds_scratch(lds, 1, a.K);
+  unsigned long long* wbest = reinterpret_cast<unsigned long long*>(red + 2 * kWaves);
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   constexpr int RPW = 2;
-  const int r0 = (blockIdx.x * kWaves + wave) * RPW;
+  const int r0 = (bid * kWaves + wave) * RPW;
   Stager<1> st;
   st.issue(a.x, a.K, a.K, a.gain);
   RowStream<WT, 1, RPW> rs;
@@ -477,8 +487,8 @@ __global__ __launch_bounds__(kBlock) void k_head(HeadArgs a) {
     for (int i = 0; i < RPW; ++i) base[i] = row_ptr<WT>(a.W, min(r0 + i, a.rows - 1), a.K);
     rs.start(base, a.K, lane);
   }
-  st.finish(xs, a.eps);
-  if (a.h_out && blockIdx.x == 0) {
+  st.finish(xs, red, a.eps);
+  if (a.h_out && bid == 0) {
     for (int k = tid; k < a.K; k += kBlock) a.h_out[k] = xs[k];
   }
   unsigned long long best = 0ull;
@@ -506,17 +516,17 @@ __global__ __launch_bounds__(kBlock) void k_head(HeadArgs a) {
     unsigned long long b = wbest[0];
 #pragma unroll
     for (int w = 1; w < kWaves; ++w) b = wbest[w] > b ? wbest[w] : b;
-    a.slots[blockIdx.x] = b;  // reduced by k_commit after this kernel
-    if (a.pos_inc && blockIdx.x == 0) *a.pos_inc = *a.pos_inc + 1;
+    a.slots[bid] = b;  // reduced by the commit that follows
+    if (a.pos_inc && bid == 0) *a.pos_inc = *a.pos_inc + 1;
   }
 }
 
-// One workgroup after each head: reduce the per-workgroup maxima to the code,
+// One workgroup after each head: reduce the per-block maxima to the code,
 // record it (argmax and committed/forced), gather the next step's inputs and,
 // after the frame's last head, advance the position.
-__global__ __launch_bounds__(kBlock) void k_commit(CommitArgs a) {
-  __shared__ unsigned long long red[kWaves];
-  __shared__ int code_sh;
+__device__ __forceinline__ void commit_body(const CommitArgs& a, char* lds) {
+  unsigned long long* red = reinterpret_cast<unsigned long long*>(lds);
+  int* code_sh = reinterpret_cast<int*>(lds + kWaves * sizeof(unsigned long long));
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   unsigned long long b = 0ull;
   for (int i = tid; i < a.nslots; i += kBlock) b = a.slots[i] > b ? a.slots[i] : b;
@@ -536,10 +546,10 @@ __global__ __launch_bounds__(kBlock) void k_commit(CommitArgs a) {
     a.pred[a.code_index] = pred;
     a.committed[a.code_index] = code;
     a.ring[(size_t)(*a.pos) * a.frame_codes + a.code_index] = code;
-    code_sh = code;
+    *code_sh = code;
   }
   __syncthreads();
-  const int code = code_sh;
+  const int code = *code_sh;
   if (a.next_table) {
     const int c = min(max(code, 0), a.next_rows - 1);
     const uint16_t* row = a.next_table + (size_t)c * a.K;
@@ -562,24 +572,29 @@ __global__ __launch_bounds__(kBlock) void k_commit(CommitArgs a) {
 
 // ------------------------------------------------ split-K decode attention --
 
-// One workgroup = one KV head x one split of `chunk` positions for one query
-// row. hd/8 lanes cover one key row (16 bytes each); a wave covers 64/(hd/8)
-// positions per step and keeps an online softmax per lane group; groups and
-// waves are merged at the end. With one split the workgroup writes the output;
-// otherwise it writes the split's (max, sum, acc) and k_attn_combine merges the
-// splits in a second launch (no cross-workgroup signalling inside a kernel).
+// One block = one KV head x one split of `chunk` positions for one query row
+// (bid = (m * n_kv + kvh) * nsplit_max + s). hd/8 lanes cover one key row (16
+// bytes each); a wave covers 64/(hd/8) positions per step and keeps an online
+// softmax per lane group; groups and waves are merged at the end. With one
+// split the block writes the output; otherwise it writes the split's (max,
+// sum, acc) and combine_body merges the splits in the following launch (no
+// cross-workgroup signalling inside a launch).
 template <int HD, int G>
-__global__ __launch_bounds__(kBlock) void k_attn(AttnArgs a) {
+__device__ __forceinline__ void attn_body(const AttnArgs& a, int bid, char* lds) {
   constexpr int LPP = HD / 8;
   constexpr int PPW = kWave / LPP;
-  constexpr int U = 2;
-  const int s = blockIdx.x, kvh = blockIdx.y, m = blockIdx.z;
+  constexpr int U = 4;
+  const int s = bid % a.nsplit_max;
+  const int kvh = (bid / a.nsplit_max) % a.n_heads_kv;
+  const int m = bid / (a.nsplit_max * a.n_heads_kv);
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const int T = *a.pos + m + 1;
   const int nsplit = (T + a.chunk - 1) / a.chunk;
   if (s >= nsplit) return;
   const int j0 = s * a.chunk, j1 = min(T, j0 + a.chunk);
   const int grp = lane / LPP, sub = lane % LPP;
+  float* sm_acc = reinterpret_cast<float*>(lds);            // [kWaves][G][HD]
+  float* sm_ml = sm_acc + kWaves * G * HD;                   // [kWaves][G][2]
 
   const float qscale = 1.4426950408889634f / sqrtf((float)HD);  // log2(e)/sqrt(hd)
   float qv[G][8];
@@ -656,68 +671,53 @@ __global__ __launch_bounds__(kBlock) void k_attn(AttnArgs a) {
     }
   }
   // merge the waves through LDS
-  __shared__ float sm_acc[kWaves][G][HD];
-  __shared__ float sm_ml[kWaves][G][2];
   if (grp == 0) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) sm_acc[wave][h][sub * 8 + e] = acc[h][e];
+      for (int e = 0; e < 8; ++e) sm_acc[(wave * G + h) * HD + sub * 8 + e] = acc[h][e];
       if (sub == 0) {
-        sm_ml[wave][h][0] = mx[h];
-        sm_ml[wave][h][1] = l[h];
+        sm_ml[(wave * G + h) * 2 + 0] = mx[h];
+        sm_ml[(wave * G + h) * 2 + 1] = l[h];
       }
     }
   }
   __syncthreads();
-  if (a.nsplit_max == 1) {
-    // a single split covers every position: normalise and write the output
-    for (int idx = tid; idx < G * HD; idx += kBlock) {
-      const int h = idx / HD, e = idx % HD;
-      float M = -INFINITY;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_ml[w][h][0]);
-      float num = 0.f, den = 0.f;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        const float mw = sm_ml[w][h][0];
-        const float c = (mw == -INFINITY) ? 0.f : exp2f(mw - M);
-        num += sm_acc[w][h][e] * c;
-        den += sm_ml[w][h][1] * c;
-      }
-      a.out[(size_t)m * a.out_stride + (kvh * G + h) * HD + e] = num / den;
-    }
-    return;
-  }
+  const bool direct = a.nsplit_max == 1;
   const int stride_s = G * (HD + 2);
   float* part = a.part + (((size_t)m * a.n_heads_kv + kvh) * a.nsplit_max) * stride_s;
   for (int idx = tid; idx < G * HD; idx += kBlock) {
     const int h = idx / HD, e = idx % HD;
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_ml[w][h][0]);
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_ml[(w * G + h) * 2]);
     float num = 0.f, den = 0.f;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
-      const float mw = sm_ml[w][h][0];
+      const float mw = sm_ml[(w * G + h) * 2];
       const float c = (mw == -INFINITY) ? 0.f : exp2f(mw - M);
-      num += sm_acc[w][h][e] * c;
-      den += sm_ml[w][h][1] * c;
+      num += sm_acc[(w * G + h) * HD + e] * c;
+      den += sm_ml[(w * G + h) * 2 + 1] * c;
     }
-    float* ps = part + (size_t)s * stride_s + h * (HD + 2);
-    ps[e] = num;
-    if (e == 0) {
-      ps[HD] = M;
-      ps[HD + 1] = den;
+    if (direct) {
+      // a single split covers every position: normalise and write the output
+      a.out[(size_t)m * a.out_stride + (kvh * G + h) * HD + e] = num / den;
+    } else {
+      float* ps = part + (size_t)s * stride_s + h * (HD + 2);
+      ps[e] = num;
+      if (e == 0) {
+        ps[HD] = M;
+        ps[HD + 1] = den;
+      }
     }
   }
 }
 
-// Combine the splits of one KV head (blockIdx.x) for query row blockIdx.y:
+// Combine the splits of one KV head for one query row (bid = m * n_kv + kvh):
 // out = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s.
 template <int HD, int G>
-__global__ __launch_bounds__(kBlock) void k_attn_combine(AttnArgs a) {
-  const int kvh = blockIdx.x, m = blockIdx.y, tid = threadIdx.x;
+__device__ __forceinline__ void combine_body(const AttnArgs& a, int bid) {
+  const int kvh = bid % a.n_heads_kv, m = bid / a.n_heads_kv, tid = threadIdx.x;
   const int T = *a.pos + m + 1;
   const int nsplit = (T + a.chunk - 1) / a.chunk;
   const int stride_s = G * (HD + 2);
@@ -735,6 +735,380 @@ __global__ __launch_bounds__(kBlock) void k_attn_combine(AttnArgs a) {
     }
     a.out[(size_t)m * a.out_stride + (kvh * G + h) * HD + e] = num / den;
   }
+}
+
+// -------------------------------------------- register-input weight streaming --
+
+// Wave-independent GEMV machinery for inputs of at most NCH chunks (NCH*64*E
+// columns, E = 8 bf16 or 16 fp8 per 16-byte load). Each lane keeps its own
+// slice of the input row in registers (the same columns for every weight row
+// it touches), so no LDS staging and no workgroup barrier are needed: a wave
+// issues its input loads, then every weight load of all its rows at once (one
+// memory round trip), normalises its slice with one wave reduction, and
+// consumes the weights as they arrive. Lanes past the row end load a clamped
+// address and hold a zero input, so they add nothing.
+template <typename WT, int NCH, int RPW>
+struct RegStream {
+  static constexpr int E = Dot<WT>::E;
+  static constexpr int CW = kWave * E;
+  static constexpr int NX = E / 4;   // float4 of input per chunk
+  static constexpr int NG = E / 8;   // 16-byte loads of bf16 gain per chunk
+  float4 x[NCH][NX];
+  u32x4 g[NCH][NG];
+  u32x4 w[RPW][NCH];
+  int lane, K;
+
+  __device__ __forceinline__ void load_x(const float* xp, const uint16_t* gain, int K_, int lane_) {
+    lane = lane_;
+    K = K_;
+    const uint16_t* gsrc = gain ? gain : reinterpret_cast<const uint16_t*>(xp);
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int col = min(c * CW + lane * E, K - E);
+#pragma unroll
+      for (int j = 0; j < NX; ++j) x[c][j] = *reinterpret_cast<const float4*>(xp + col + 4 * j);
+#pragma unroll
+      for (int j = 0; j < NG; ++j) g[c][j] = *reinterpret_cast<const u32x4*>(gsrc + col + 8 * j);
+    }
+  }
+
+  __device__ __forceinline__ void load_w(const char* const (&base)[RPW]) {
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int col = min(c * CW + lane * E, K - E);
+#pragma unroll
+      for (int i = 0; i < RPW; ++i) w[i][c] = ld16_nt(base[i] + (size_t)col * WT::kBytes);
+    }
+  }
+
+  // zero the slices past the row end; with a gain, x <- x / sqrt(mean(x^2) + eps) * gain
+  __device__ __forceinline__ void prepare(bool has_gain, float eps) {
+    float ss = 0.f;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const bool valid = c * CW + lane * E < K;
+#pragma unroll
+      for (int j = 0; j < NX; ++j) {
+        if (!valid) x[c][j] = make_float4(0.f, 0.f, 0.f, 0.f);
+        ss += (x[c][j].x * x[c][j].x + x[c][j].y * x[c][j].y) + (x[c][j].z * x[c][j].z + x[c][j].w * x[c][j].w);
+      }
+    }
+    if (!has_gain) return;
+    ss = wave_sum(ss);
+    const float inv = 1.0f / sqrtf(ss / (float)K + eps);
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+#pragma unroll
+      for (int j = 0; j < NG; ++j) {
+        const u32x4 gg = g[c][j];
+        float4& a = x[c][2 * j];
+        float4& b = x[c][2 * j + 1];
+        a.x = (a.x * inv) * bf_lo(gg.x);
+        a.y = (a.y * inv) * bf_hi(gg.x);
+        a.z = (a.z * inv) * bf_lo(gg.y);
+        a.w = (a.w * inv) * bf_hi(gg.y);
+        b.x = (b.x * inv) * bf_lo(gg.z);
+        b.y = (b.y * inv) * bf_hi(gg.z);
+        b.z = (b.z * inv) * bf_lo(gg.w);
+        b.w = (b.w * inv) * bf_hi(gg.w);
+      }
+    }
+  }
+
+  __device__ __forceinline__ float dot_row(int i) const {
+    float acc = 0.f;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) acc += Dot<WT>::run(w[i][c], reinterpret_cast<const float*>(&x[c][0]));
+    return acc;
+  }
+
+  // write this lane's (normalised) slice of the input to dst (valid columns only)
+  __device__ __forceinline__ void store_x(float* dst) const {
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int col = c * CW + lane * E;
+      if (col < K) {
+#pragma unroll
+        for (int j = 0; j < NX; ++j) *reinterpret_cast<float4*>(dst + col + 4 * j) = x[c][j];
+      }
+    }
+  }
+};
+
+// y[r] (+)= scale[r] * W[r] . x, one row per wave
+template <typename WT, int NCH>
+__global__ __launch_bounds__(kBlock) void k_gemv_reg(GemvArgs a) {
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int r = blockIdx.x * kWaves + wave;
+  RegStream<WT, NCH, 1> rs;
+  rs.load_x(a.x, a.gain, a.K, lane);
+  const char* base[1] = {row_ptr<WT>(a.W, min(r, a.rows - 1), a.K)};
+  rs.load_w(base);
+  rs.prepare(a.gain != nullptr, a.eps);
+  if (r >= a.rows) return;
+  float s = wave_sum(rs.dot_row(0));
+  if (lane == 0) {
+    if (a.scale) s *= a.scale[r];
+    float* y = a.y + r;
+    *y = a.accumulate ? (*y + s) : s;
+  }
+}
+
+// fused RMSNorm + QKV + RoPE + KV append; wave = rotation pair (head, i), (head, i + hd/2)
+template <typename WT, int NCH>
+__global__ __launch_bounds__(kBlock) void k_qkv_reg(QkvArgs a) {
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int half = a.head_dim / 2;
+  const int n_heads = a.n_heads_q + 2 * a.n_heads_kv;
+  const int p = blockIdx.x * kWaves + wave;
+  const bool active = p < n_heads * half;
+  const int pc = min(p, n_heads * half - 1);
+  const int head = pc / half, i = pc % half;
+  const int r1 = head * a.head_dim + i, r2 = r1 + half;
+  RegStream<WT, NCH, 2> rs;
+  rs.load_x(a.x, a.gain, a.K, lane);
+  const char* base[2] = {row_ptr<WT>(a.W, r1, a.K), row_ptr<WT>(a.W, r2, a.K)};
+  rs.load_w(base);
+  rs.prepare(true, a.eps);
+  if (!active) return;
+  const float y1 = wave_sum(rs.dot_row(0));
+  const float y2 = wave_sum(rs.dot_row(1));
+  if (lane != 0) return;
+  const float u = y1 * (a.scale ? a.scale[r1] : 1.f), v = y2 * (a.scale ? a.scale[r2] : 1.f);
+  const int pos = *a.pos;
+  if (head < a.n_heads_q + a.n_heads_kv) {
+    const float2 cs = a.rope[(size_t)pos * half + i];
+    const float o1 = u * cs.x - v * cs.y;
+    const float o2 = u * cs.y + v * cs.x;
+    if (head < a.n_heads_q) {
+      a.q_out[r1] = o1;
+      a.q_out[r2] = o2;
+    } else {
+      uint16_t* kp = a.kc + ((size_t)(head - a.n_heads_q) * a.cache_len + pos) * a.head_dim;
+      kp[i] = f2bf(o1);
+      kp[i + half] = f2bf(o2);
+    }
+  } else {
+    uint16_t* vp = a.vc + ((size_t)(head - a.n_heads_q - a.n_heads_kv) * a.cache_len + pos) * a.head_dim;
+    vp[i] = f2bf(u);
+    vp[i + half] = f2bf(v);
+  }
+}
+
+// fused RMSNorm + W1/W3 + SiLU(a)*b; wave = output r (rows W1[r], W3[r])
+template <typename WT, int NCH>
+__global__ __launch_bounds__(kBlock) void k_swiglu_reg(SwigluArgs a) {
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int r = blockIdx.x * kWaves + wave;
+  const int rc = min(r, a.F - 1);
+  RegStream<WT, NCH, 2> rs;
+  rs.load_x(a.x, a.gain, a.K, lane);
+  const char* base[2] = {row_ptr<WT>(a.W1, rc, a.K), row_ptr<WT>(a.W3, rc, a.K)};
+  rs.load_w(base);
+  rs.prepare(true, a.eps);
+  if (r >= a.F) return;
+  float g = wave_sum(rs.dot_row(0));
+  float u = wave_sum(rs.dot_row(1));
+  if (lane == 0) {
+    if (a.s1) g *= a.s1[r];
+    if (a.s3) u *= a.s3[r];
+    const float silu = g / (1.0f + expf(-g));
+    a.h[r] = silu * u;
+  }
+}
+
+// fused RMSNorm + head GEMV + per-block argmax (two rows per wave)
+template <typename WT, int NCH>
+__global__ __launch_bounds__(kBlock) void k_head_reg(HeadArgs a) {
+  __shared__ unsigned long long wbest[kWaves];
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int r0 = (blockIdx.x * kWaves + wave) * 2;
+  RegStream<WT, NCH, 2> rs;
+  rs.load_x(a.x, a.gain, a.K, lane);
+  const char* base[2] = {row_ptr<WT>(a.W, min(r0, a.rows - 1), a.K), row_ptr<WT>(a.W, min(r0 + 1, a.rows - 1), a.K)};
+  rs.load_w(base);
+  rs.prepare(true, a.eps);
+  if (a.h_out && blockIdx.x == 0 && wave == 0) rs.store_x(a.h_out);
+  unsigned long long best = 0ull;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = r0 + i;
+    float s = wave_sum(rs.dot_row(i));
+    if (r < a.rows) {
+      if (a.scale) s *= a.scale[r];
+      if (lane == 0) {
+        a.logits[r] = s;
+        if (!isfinite(s)) atomicAdd(a.anomalies, 1);
+      }
+      const unsigned long long k = argmax_key(s, r);
+      best = k > best ? k : best;
+    }
+  }
+  if (lane == 0) wbest[wave] = best;
+  __syncthreads();
+  if (tid == 0) {
+    unsigned long long b = wbest[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) b = wbest[w] > b ? wbest[w] : b;
+    a.slots[blockIdx.x] = b;  // reduced by the commit that follows
+    if (a.pos_inc && blockIdx.x == 0) *a.pos_inc = *a.pos_inc + 1;
+  }
+}
+
+// ------------------------------------------- one-workgroup-per-head attention --
+
+// Decode attention without splits: block = (query row m, KV head kvh), NW
+// waves; wave w takes passes w, w+NW, ... of PPW positions each, U passes of
+// K/V loads in flight; per-lane online softmax, merged across lane groups with
+// shuffles and across waves through LDS; the block writes the g heads' output.
+template <int HD, int G, int NW, int U>
+__global__ __launch_bounds__(NW * kWave) void k_attn_wide(AttnArgs a) {
+  extern __shared__ __align__(16) char lds[];
+  constexpr int LPP = HD / 8;
+  constexpr int PPW = kWave / LPP;
+  constexpr int STEP = NW * PPW;
+  constexpr int NT = NW * kWave;
+  const int kvh = blockIdx.x % a.n_heads_kv, m = blockIdx.x / a.n_heads_kv;
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int T = *a.pos + m + 1;
+  const int grp = lane / LPP, sub = lane % LPP;
+  float* sm_acc = reinterpret_cast<float*>(lds);  // [NW][G][HD]
+  float* sm_ml = sm_acc + NW * G * HD;            // [NW][G][2]
+
+  const float qscale = 1.4426950408889634f / sqrtf((float)HD);  // log2(e)/sqrt(hd)
+  float qv[G][8];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const float* qp = a.q + (size_t)m * a.q_stride + (kvh * G + h) * HD + sub * 8;
+    const float4 q0 = *reinterpret_cast<const float4*>(qp);
+    const float4 q1 = *reinterpret_cast<const float4*>(qp + 4);
+    qv[h][0] = q0.x * qscale; qv[h][1] = q0.y * qscale; qv[h][2] = q0.z * qscale; qv[h][3] = q0.w * qscale;
+    qv[h][4] = q1.x * qscale; qv[h][5] = q1.y * qscale; qv[h][6] = q1.z * qscale; qv[h][7] = q1.w * qscale;
+  }
+  float mx[G], l[G], acc[G][8];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    mx[h] = -INFINITY;
+    l[h] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+  }
+  const uint16_t* Kb = a.K + (size_t)kvh * a.cache_len * HD + sub * 8;
+  const uint16_t* Vb = a.V + (size_t)kvh * a.cache_len * HD + sub * 8;
+  for (int jb = wave * PPW; jb < T; jb += STEP * U) {
+    u32x4 kk[U], vv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int j = min(jb + u * STEP + grp, T - 1);  // clamped: always a valid row
+      kk[u] = ld16(Kb + (size_t)j * HD);
+      vv[u] = ld16(Vb + (size_t)j * HD);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bool ok = jb + u * STEP + grp < T;
+      const float kf[8] = {bf_lo(kk[u].x), bf_hi(kk[u].x), bf_lo(kk[u].y), bf_hi(kk[u].y),
+                           bf_lo(kk[u].z), bf_hi(kk[u].z), bf_lo(kk[u].w), bf_hi(kk[u].w)};
+      const float vf[8] = {bf_lo(vv[u].x), bf_hi(vv[u].x), bf_lo(vv[u].y), bf_hi(vv[u].y),
+                           bf_lo(vv[u].z), bf_hi(vv[u].z), bf_lo(vv[u].w), bf_hi(vv[u].w)};
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float sc = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sc = fmaf(qv[h][e], kf[e], sc);
+        sc = row_sum<LPP>(sc);
+        if (ok) {
+          const float mn = fmaxf(mx[h], sc);
+          const float corr = exp2f(mx[h] - mn);
+          const float pr = exp2f(sc - mn);
+          l[h] = l[h] * corr + pr;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(pr, vf[e], acc[h][e] * corr);
+          mx[h] = mn;
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int off = LPP; off < kWave; off <<= 1) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float mo = __shfl_xor(mx[h], off);
+      const float lo = __shfl_xor(l[h], off);
+      const float mn = fmaxf(mx[h], mo);
+      const float ca = (mx[h] == -INFINITY) ? 0.f : exp2f(mx[h] - mn);
+      const float cb = (mo == -INFINITY) ? 0.f : exp2f(mo - mn);
+      l[h] = l[h] * ca + lo * cb;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float ao = __shfl_xor(acc[h][e], off);
+        acc[h][e] = acc[h][e] * ca + ao * cb;
+      }
+      mx[h] = mn;
+    }
+  }
+  if (grp == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sm_acc[(wave * G + h) * HD + sub * 8 + e] = acc[h][e];
+      if (sub == 0) {
+        sm_ml[(wave * G + h) * 2 + 0] = mx[h];
+        sm_ml[(wave * G + h) * 2 + 1] = l[h];
+      }
+    }
+  }
+  __syncthreads();
+  for (int idx = tid; idx < G * HD; idx += NT) {
+    const int h = idx / HD, e = idx % HD;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_ml[(w * G + h) * 2]);
+    float num = 0.f, den = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float mw = sm_ml[(w * G + h) * 2];
+      const float c = (mw == -INFINITY) ? 0.f : exp2f(mw - M);
+      num += sm_acc[(w * G + h) * HD + e] * c;
+      den += sm_ml[(w * G + h) * 2 + 1] * c;
+    }
+    a.out[(size_t)m * a.out_stride + (kvh * G + h) * HD + e] = num / den;
+  }
+}
+
+// ------------------------------------------------- block-index kernels (LDS) --
+
+template <typename WT, int M, int RPW>
+__global__ __launch_bounds__(kBlock) void k_gemv(GemvArgs a) {
+  extern __shared__ __align__(16) char lds[];
+  gemv_body<WT, M, RPW>(a, blockIdx.x, lds);
+}
+template <typename WT, int M>
+__global__ __launch_bounds__(kBlock) void k_qkv(QkvArgs a) {
+  extern __shared__ __align__(16) char lds[];
+  qkv_body<WT, M>(a, blockIdx.x, lds);
+}
+template <typename WT, int M>
+__global__ __launch_bounds__(kBlock) void k_swiglu(SwigluArgs a) {
+  extern __shared__ __align__(16) char lds[];
+  swiglu_body<WT, M>(a, blockIdx.x, lds);
+}
+template <typename WT>
+__global__ __launch_bounds__(kBlock) void k_head(HeadArgs a) {
+  extern __shared__ __align__(16) char lds[];
+  head_body<WT>(a, blockIdx.x, lds);
+}
+__global__ __launch_bounds__(kBlock) void k_commit(CommitArgs a) {
+  extern __shared__ __align__(16) char lds[];
+  commit_body(a, lds);
+}
+template <int HD, int G>
+__global__ __launch_bounds__(kBlock) void k_attn_split(AttnArgs a) {
+  extern __shared__ __align__(16) char lds[];
+  attn_body<HD, G>(a, blockIdx.x, lds);
+}
+template <int HD, int G>
+__global__ __launch_bounds__(kBlock) void k_attn_combine(AttnArgs a) {
+  combine_body<HD, G>(a, blockIdx.x);
 }
 
 // ---------------------------------------------------------- small kernels --
@@ -829,117 +1203,169 @@ __global__ void k_fp8_decode(const uint8_t* codes, int n, float* out) {
 
 // ---------------------------------------------------------------- launchers --
 
-int head_grid(int rows);
+int head_grid(int rows) { return (rows + kWaves * 2 - 1) / (kWaves * 2); }
 
-static size_t lds_bytes(int M, int K) { return (size_t)M * K * sizeof(float); }
+static size_t gemv_lds(int M, int K) { return (((size_t)M * K * 4 + 15) & ~(size_t)15) + 64; }
 
-template <typename KernelT>
-static hipError_t prep(KernelT kern, size_t lds) {
-  if (lds > 64 * 1024) {
-    return hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
-                               (int)lds);
+template <typename WT>
+static int nch_of(int K) {
+  constexpr int CW = kWave * Dot<WT>::E;
+  return (K + CW - 1) / CW;
+}
+
+template <typename KernelT, typename ArgT>
+static hipError_t go(KernelT kern, int grid, int block, size_t lds, hipStream_t s, const ArgT& a) {
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(block), lds, s, a);
+  return hipGetLastError();
+}
+
+#define DAR_NCH_SWITCH(NCH, CALL) \
+  switch (NCH) {                  \
+    case 1: CALL(1);              \
+    case 2: CALL(2);              \
+    case 3: CALL(3);              \
+    case 4: CALL(4);              \
+    case 5: CALL(5);              \
+    case 8: CALL(8);              \
+    default: break;               \
   }
-  return hipSuccess;
-}
 
-template <typename WT, int M>
-static hipError_t gemv_impl(const GemvArgs& a, hipStream_t s) {
-  constexpr int RPW = 2;
-  auto kern = k_gemv<WT, M, RPW>;
-  const size_t lds = lds_bytes(M, a.K);
-  hipError_t e = prep(kern, lds);
-  if (e != hipSuccess) return e;
-  const int grid = (a.rows + kWaves * RPW - 1) / (kWaves * RPW);
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(kBlock), lds, s, a);
-  return hipGetLastError();
-}
-
-hipError_t launch_gemv(int wtype, const GemvArgs& a, hipStream_t s) {
-  if (wtype == W_FP8) return a.M == 1 ? gemv_impl<FP8, 1>(a, s) : gemv_impl<FP8, 2>(a, s);
-  return a.M == 1 ? gemv_impl<BF16, 1>(a, s) : gemv_impl<BF16, 2>(a, s);
-}
-
-template <typename WT, int M>
-static hipError_t qkv_impl(const QkvArgs& a, hipStream_t s) {
-  auto kern = k_qkv<WT, M>;
-  const size_t lds = lds_bytes(M, a.K);
-  hipError_t e = prep(kern, lds);
-  if (e != hipSuccess) return e;
-  const int pairs = (a.n_heads_q + 2 * a.n_heads_kv) * a.head_dim / 2;
-  const int grid = (pairs + kWaves - 1) / kWaves;
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(kBlock), lds, s, a);
-  return hipGetLastError();
-}
-
-hipError_t launch_qkv(int wtype, const QkvArgs& a, hipStream_t s) {
-  if (wtype == W_FP8) return a.M == 1 ? qkv_impl<FP8, 1>(a, s) : qkv_impl<FP8, 2>(a, s);
-  return a.M == 1 ? qkv_impl<BF16, 1>(a, s) : qkv_impl<BF16, 2>(a, s);
-}
-
-template <typename WT, int M>
-static hipError_t swiglu_impl(const SwigluArgs& a, hipStream_t s) {
-  auto kern = k_swiglu<WT, M>;
-  const size_t lds = lds_bytes(M, a.K);
-  hipError_t e = prep(kern, lds);
-  if (e != hipSuccess) return e;
-  const int grid = (a.F + kWaves - 1) / kWaves;
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(kBlock), lds, s, a);
-  return hipGetLastError();
-}
-
-hipError_t launch_swiglu(int wtype, const SwigluArgs& a, hipStream_t s) {
-  if (wtype == W_FP8) return a.M == 1 ? swiglu_impl<FP8, 1>(a, s) : swiglu_impl<FP8, 2>(a, s);
-  return a.M == 1 ? swiglu_impl<BF16, 1>(a, s) : swiglu_impl<BF16, 2>(a, s);
+template <typename WT>
+static hipError_t gemv_launch(const GemvArgs& a, int M, hipStream_t s) {
+  if (M == 1) {
+    const int grid = (a.rows + kWaves - 1) / kWaves;
+#define CALL(N) return go(k_gemv_reg<WT, N>, grid, kBlock, 0, s, a)
+    DAR_NCH_SWITCH(nch_of<WT>(a.K), CALL)
+#undef CALL
+  }
+  const int grid = (a.rows + kWaves * 2 - 1) / (kWaves * 2);
+  if (M == 2) return go(k_gemv<WT, 2, 2>, grid, kBlock, gemv_lds(2, a.K), s, a);
+  return go(k_gemv<WT, 1, 2>, grid, kBlock, gemv_lds(1, a.K), s, a);
 }
 
 template <typename WT>
-static hipError_t head_impl(const HeadArgs& a, hipStream_t s) {
-  auto kern = k_head<WT>;
-  const size_t lds = lds_bytes(1, a.K);
-  hipError_t e = prep(kern, lds);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3(head_grid(a.rows)), dim3(kBlock), lds, s, a);
-  return hipGetLastError();
+static hipError_t qkv_launch(const QkvArgs& a, int M, hipStream_t s) {
+  const int pairs = (a.n_heads_q + 2 * a.n_heads_kv) * a.head_dim / 2;
+  const int grid = (pairs + kWaves - 1) / kWaves;
+  if (M == 1) {
+#define CALL(N) return go(k_qkv_reg<WT, N>, grid, kBlock, 0, s, a)
+    DAR_NCH_SWITCH(nch_of<WT>(a.K), CALL)
+#undef CALL
+  }
+  if (M == 2) return go(k_qkv<WT, 2>, grid, kBlock, gemv_lds(2, a.K), s, a);
+  return go(k_qkv<WT, 1>, grid, kBlock, gemv_lds(1, a.K), s, a);
 }
 
-hipError_t launch_head(int wtype, const HeadArgs& a, hipStream_t s) {
-  return wtype == W_FP8 ? head_impl<FP8>(a, s) : head_impl<BF16>(a, s);
+template <typename WT>
+static hipError_t swiglu_launch(const SwigluArgs& a, int M, hipStream_t s) {
+  const int grid = (a.F + kWaves - 1) / kWaves;
+  if (M == 1) {
+#define CALL(N) return go(k_swiglu_reg<WT, N>, grid, kBlock, 0, s, a)
+    DAR_NCH_SWITCH(nch_of<WT>(a.K), CALL)
+#undef CALL
+  }
+  if (M == 2) return go(k_swiglu<WT, 2>, grid, kBlock, gemv_lds(2, a.K), s, a);
+  return go(k_swiglu<WT, 1>, grid, kBlock, gemv_lds(1, a.K), s, a);
 }
 
-int head_grid(int rows) { return (rows + kWaves * 2 - 1) / (kWaves * 2); }
-
-hipError_t launch_commit(const CommitArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(k_commit, dim3(1), dim3(kBlock), 0, s, a);
-  return hipGetLastError();
+template <typename WT>
+static hipError_t head_launch(const HeadArgs& a, hipStream_t s) {
+  const int grid = head_grid(a.rows);
+#define CALL(N) return go(k_head_reg<WT, N>, grid, kBlock, 0, s, a)
+  DAR_NCH_SWITCH(nch_of<WT>(a.K), CALL)
+#undef CALL
+  return go(k_head<WT>, grid, kBlock, gemv_lds(1, a.K), s, a);
 }
 
 template <int HD, int G>
-static hipError_t attn_impl(const AttnArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((k_attn<HD, G>), dim3(a.nsplit_max, a.n_heads_kv, a.M), dim3(kBlock), 0, s, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.nsplit_max == 1) return e;
-  hipLaunchKernelGGL((k_attn_combine<HD, G>), dim3(a.n_heads_kv, a.M), dim3(kBlock), 0, s, a);
-  return hipGetLastError();
+static hipError_t attn_launch(const AttnArgs& a, int kind, hipStream_t s) {
+  if (kind == T_COMBINE) return go(k_attn_combine<HD, G>, a.n_heads_kv * a.M, kBlock, 0, s, a);
+  if (a.nsplit_max > 1)
+    return go(k_attn_split<HD, G>, a.nsplit_max * a.n_heads_kv * a.M, kBlock, (size_t)kWaves * G * (HD + 2) * 4, s, a);
+  // one block per (query row, KV head): for short contexts (the fast AR's <= R+1 positions)
+  return go(k_attn_wide<HD, G, 4, 2>, a.n_heads_kv * a.M, 4 * kWave, (size_t)4 * G * (HD + 2) * 4, s, a);
 }
 
-hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
+static hipError_t attn_dispatch(const AttnArgs& a, int kind, hipStream_t s) {
   const int g = a.n_heads_q / a.n_heads_kv;
   if (a.head_dim == 128) {
     switch (g) {
-      case 1: return attn_impl<128, 1>(a, s);
-      case 2: return attn_impl<128, 2>(a, s);
-      case 4: return attn_impl<128, 4>(a, s);
-      case 8: return attn_impl<128, 8>(a, s);
+      case 1: return attn_launch<128, 1>(a, kind, s);
+      case 2: return attn_launch<128, 2>(a, kind, s);
+      case 4: return attn_launch<128, 4>(a, kind, s);
+      case 8: return attn_launch<128, 8>(a, kind, s);
     }
   } else if (a.head_dim == 64) {
     switch (g) {
-      case 1: return attn_impl<64, 1>(a, s);
-      case 2: return attn_impl<64, 2>(a, s);
-      case 4: return attn_impl<64, 4>(a, s);
-      case 8: return attn_impl<64, 8>(a, s);
+      case 1: return attn_launch<64, 1>(a, kind, s);
+      case 2: return attn_launch<64, 2>(a, kind, s);
+      case 4: return attn_launch<64, 4>(a, kind, s);
+      case 8: return attn_launch<64, 8>(a, kind, s);
     }
   }
   return hipErrorInvalidValue;
+}
+
+template <typename WT>
+static hipError_t task_launch(const Task& t, hipStream_t s) {
+  switch (t.kind) {
+    case T_QKV: return qkv_launch<WT>(t.qkv, t.M, s);
+    case T_ATTN:
+    case T_COMBINE: return attn_dispatch(t.attn, t.kind, s);
+    case T_GEMV: return gemv_launch<WT>(t.gemv, t.M, s);
+    case T_SWIGLU: return swiglu_launch<WT>(t.swiglu, t.M, s);
+    case T_HEAD: return head_launch<WT>(t.head, s);
+    case T_HEAD_BF16: return head_launch<BF16>(t.head, s);
+    case T_COMMIT: return go(k_commit, 1, kBlock, 64, s, t.commit);
+    default: return hipSuccess;
+  }
+}
+
+hipError_t launch_task(int wtype, const Task& t, hipStream_t s) {
+  return wtype == W_FP8 ? task_launch<FP8>(t, s) : task_launch<BF16>(t, s);
+}
+
+template <typename KernelT>
+static hipError_t allow_lds(KernelT kern) {
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                             160 * 1024);
+}
+
+template <typename WT>
+static hipError_t prepare_wt() {
+  hipError_t e;
+  if ((e = allow_lds(k_gemv<WT, 1, 2>)) != hipSuccess) return e;
+  if ((e = allow_lds(k_gemv<WT, 2, 2>)) != hipSuccess) return e;
+  if ((e = allow_lds(k_qkv<WT, 1>)) != hipSuccess) return e;
+  if ((e = allow_lds(k_qkv<WT, 2>)) != hipSuccess) return e;
+  if ((e = allow_lds(k_swiglu<WT, 1>)) != hipSuccess) return e;
+  if ((e = allow_lds(k_swiglu<WT, 2>)) != hipSuccess) return e;
+  return allow_lds(k_head<WT>);
+}
+
+template <int HD, int G>
+static hipError_t prepare_attn() {
+  hipError_t e;
+  if ((e = allow_lds(k_attn_wide<HD, G, 4, 2>)) != hipSuccess) return e;
+  return allow_lds(k_attn_split<HD, G>);
+}
+
+hipError_t prepare_kernels() {
+  static bool done = false;
+  if (done) return hipSuccess;
+  hipError_t e;
+  if ((e = prepare_wt<BF16>()) != hipSuccess) return e;
+  if ((e = prepare_wt<FP8>()) != hipSuccess) return e;
+  if ((e = prepare_attn<128, 1>()) != hipSuccess) return e;
+  if ((e = prepare_attn<128, 2>()) != hipSuccess) return e;
+  if ((e = prepare_attn<128, 4>()) != hipSuccess) return e;
+  if ((e = prepare_attn<128, 8>()) != hipSuccess) return e;
+  if ((e = prepare_attn<64, 1>()) != hipSuccess) return e;
+  if ((e = prepare_attn<64, 2>()) != hipSuccess) return e;
+  if ((e = prepare_attn<64, 4>()) != hipSuccess) return e;
+  if ((e = prepare_attn<64, 8>()) != hipSuccess) return e;
+  done = true;
+  return hipSuccess;
 }
 
 size_t attn_partial_floats(int M, int n_kv, int nsplit_max, int group, int head_dim) {

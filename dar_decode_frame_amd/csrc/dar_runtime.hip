@@ -1,11 +1,12 @@
 // C-ABI runtime of libdar.so: context, workspace carve-up, RoPE table, the
-// frame's launch sequences, HIP-graph capture and replay, prefill, helpers.
+// frame's launch plans, HIP-graph capture and replay, prefill, helpers.
 //
 // Frame (tuna-fish README, intro: "slowAR decode + fastAR loop"; "Inference
 // estimation": slow AR once, fast AR nine times with a 10-long fast KV):
-//   slow layers 0..Ls-1 : QKV(+norm, RoPE, KV append) -> attention -> Wo(+res)
-//                         -> W1/W3(+norm, SiLU*mul) -> W2(+res)
-//   codebook-0 head     : norm -> W0 -> per-workgroup argmax
+//   slow layers 0..Ls-1 : QKV(+norm, RoPE, KV append) -> attention (-> split
+//                         combine) -> Wo(+res) -> W1/W3(+norm, SiLU*mul)
+//                         -> W2(+res)
+//   codebook-0 head     : norm -> W0 -> per-block argmax
 //   commit c0           : argmax (or the forced code) -> ring, fast inputs
 //                         [h_t, E0[c0]], next frame's slow input W0[c0]
 //   fast pass 1         : the fast layers over fast positions 0 and 1 together
@@ -13,12 +14,14 @@
 //                         shared head and a commit that gathers E_k[c_k]
 //
 // The slow step of frame i+1 needs only codebook 0 of frame i, not frame i's
-// fast AR, so each call runs two chains concurrently on two streams, each one
-// replaying its own captured graph: the fast chain finishes frame i while the
-// slow chain computes the slow step and codebook-0 head of frame i+1. Their
-// weights are nearly equal in size (slow 7.29 GB, fast 9 x 0.83 GB at full
-// shape), so each chain's launch gaps are filled by the other's weight stream.
-// Every position and code the chains need lives in device memory.
+// fast AR. A call therefore runs two independent chains of launches on two
+// streams: the fast chain finishing frame i (after the commit of its codebook
+// 0) and the slow chain computing the slow step and codebook-0 head of frame
+// i+1; the slow chain starts once codebook 0 is committed. Their weights are
+// nearly equal in size (slow 7.29 GB, fast 9 x 0.83 GB at full shape), so the
+// fixed cost of each launch on one stream is covered by the other stream's
+// weight traffic. Each chain is a plan of launches built once at create and
+// replayed as its own captured graph.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -43,6 +46,12 @@ constexpr size_t kAlign = 256;
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
+int frame_codes(const dar_config* c) { return 1 + c->n_res; }
+bool has_fast(const dar_config* c) { return c->n_res > 0; }
+
+// the slow chain splits its attention over 64-position chunks once the cache is longer than one chunk
+int nsplit_slow_of(const dar_config* c) { return (c->max_len + kAttnChunkDefault - 1) / kAttnChunkDefault; }
+
 struct Layout {
   size_t x[2], q[2], o[2], h[2], part[2];  // chain scratch: [0] slow (one row), [1] fast (two rows)
   size_t ht, logits0, flogits, slots0, slotsf, pred, committed, forced, flags, pos, seqpos, ring, rope;
@@ -50,16 +59,13 @@ struct Layout {
   int nsplit_slow, chunk, rope_len, seq_len, vmax, fast_len, nslots;
 };
 
-int frame_codes(const dar_config* c) { return 1 + c->n_res; }
-bool has_fast(const dar_config* c) { return c->n_res > 0; }
-
 Layout make_layout(const dar_config* c) {
   Layout L{};
   const int d = c->d_model, qw = c->n_heads_q * c->head_dim, F = c->ffn_dim;
   const int g = c->n_heads_q / c->n_heads_kv;
   const int fc = frame_codes(c);
   L.chunk = kAttnChunkDefault;
-  L.nsplit_slow = (c->max_len + L.chunk - 1) / L.chunk;
+  L.nsplit_slow = nsplit_slow_of(c);
   L.fast_len = has_fast(c) ? c->n_res + 1 : 1;
   L.rope_len = std::max(c->max_len, L.fast_len);
   L.seq_len = std::max(c->max_len, L.fast_len + 1);
@@ -169,17 +175,26 @@ int check_layer(const dar_layer_weights& w, bool fp8, std::string& why, const ch
 
 }  // namespace
 
-struct LaunchRec {
-  int kind, layer;
+enum Kind { K_QKV = 0, K_ATTN = 1, K_WO = 2, K_W13 = 3, K_W2 = 4, K_HEAD = 5, K_OTHER = 6 };
+
+struct TaskRec {
+  Task t;
+  int kind, layer;  // for the profiler
 };
 
-// One dependent chain of launches with its own stream, scratch and graph.
-struct Chain {
-  float *x = nullptr, *q = nullptr, *o = nullptr, *h = nullptr, *part = nullptr;
-  int M = 1;
-  hipStream_t s = nullptr;
+// A sequence of launches, one task each.
+struct Plan {
+  std::vector<Task> tasks;
+  std::vector<int> kind, layer;
   hipGraph_t graph = nullptr;
   hipGraphExec_t exec = nullptr;
+  size_t launches() const { return tasks.size(); }
+};
+
+// Scratch and stream of one chain of launches.
+struct Chain {
+  float *x = nullptr, *q = nullptr, *o = nullptr, *h = nullptr, *part = nullptr;
+  hipStream_t s = nullptr;
 };
 
 struct dar_ctx {
@@ -196,6 +211,7 @@ struct dar_ctx {
 
   hipStream_t stream = nullptr;  // the caller's stream
   Chain cs, cf;                  // slow chain (frame i+1) and fast chain (frame i)
+  Plan p_c0, p_fast, p_slow, p_prefill;  // commit of c0, fast AR, slow step + c0 head, slow step alone
   hipEvent_t ev_start = nullptr, ev_c0 = nullptr, ev_f_done = nullptr, ev_s_done = nullptr;
   bool use_graph = true;
 
@@ -212,8 +228,6 @@ struct dar_ctx {
   std::string err;
 
   std::vector<hipEvent_t> events;
-  std::vector<LaunchRec> recs;
-  bool profiling = false;
 };
 
 namespace {
@@ -233,34 +247,31 @@ int hip_fail(dar_ctx* c, hipError_t e, const char* what) {
     if (e_ != hipSuccess) return hip_fail(ctx, e_, what); \
   } while (0)
 
-// Every launch goes through here so the profiler can bracket it with events.
-template <typename F>
-hipError_t tracked(dar_ctx* c, hipStream_t s, int kind, int layer, F&& launch) {
-  if (c->profiling) {
-    const size_t i = c->recs.size();
-    if (2 * i + 2 > c->events.size()) return hipErrorOutOfMemory;
-    hipError_t e = hipEventRecord(c->events[2 * i], s);
-    if (e != hipSuccess) return e;
-    e = launch();
-    if (e != hipSuccess) return e;
-    e = hipEventRecord(c->events[2 * i + 1], s);
-    c->recs.push_back({kind, layer});
-    return e;
-  }
-  return launch();
+Task none_task() {
+  Task t;
+  std::memset(&t, 0, sizeof t);
+  t.kind = T_NONE;
+  return t;
 }
 
-enum Kind { K_QKV = 0, K_ATTN = 1, K_WO = 2, K_W13 = 3, K_W2 = 4, K_HEAD = 5, K_OTHER = 6 };
+TaskRec rec(const Task& t, int kind, int layer) {
+  TaskRec r;
+  r.t = t;
+  r.kind = kind;
+  r.layer = layer;
+  return r;
+}
 
-// One decoder layer of a chain over M input rows at device position *pos (row m at +m).
-hipError_t enqueue_layer(dar_ctx* c, const Chain& ch, hipStream_t s, const dar_layer_weights& w, int layer_tag,
-                         int M, const int* pos, uint16_t* kc, uint16_t* vc, int cache_len, int nsplit_max) {
+// The five or six stages of one decoder layer over M rows at device position *pos.
+void add_layer(dar_ctx* c, std::vector<TaskRec>& out, const Chain& ch, const dar_layer_weights& w, int tag, int M,
+               const int* pos, uint16_t* kc, uint16_t* vc, int cache_len, int nsplit_max) {
   const dar_config& g = c->cfg;
   const int d = g.d_model, qw = g.n_heads_q * g.head_dim;
-  const int wt = c->fp8 ? W_FP8 : W_BF16;
-  hipError_t e;
+  Task t = none_task();
 
-  QkvArgs qa{};
+  t.kind = T_QKV;
+  t.M = M;
+  QkvArgs& qa = t.qkv;
   qa.W = w.wqkv;
   qa.scale = c->fp8 ? w.wqkv_scale : nullptr;
   qa.K = d;
@@ -279,10 +290,12 @@ hipError_t enqueue_layer(dar_ctx* c, const Chain& ch, hipStream_t s, const dar_l
   qa.kc = kc;
   qa.vc = vc;
   qa.cache_len = cache_len;
-  e = tracked(c, s, K_QKV, layer_tag, [&] { return launch_qkv(wt, qa, s); });
-  if (e != hipSuccess) return e;
+  out.push_back(rec(t, K_QKV, tag));
 
-  AttnArgs aa{};
+  t = none_task();
+  t.kind = T_ATTN;
+  t.M = M;
+  AttnArgs& aa = t.attn;
   aa.q = ch.q;
   aa.q_stride = qw;
   aa.K = kc;
@@ -298,10 +311,16 @@ hipError_t enqueue_layer(dar_ctx* c, const Chain& ch, hipStream_t s, const dar_l
   aa.part = ch.part;
   aa.out = ch.o;
   aa.out_stride = qw;
-  e = tracked(c, s, K_ATTN, layer_tag, [&] { return launch_attn(aa, s); });
-  if (e != hipSuccess) return e;
+  out.push_back(rec(t, K_ATTN, tag));
+  if (nsplit_max > 1) {
+    t.kind = T_COMBINE;
+    out.push_back(rec(t, K_ATTN, tag));
+  }
 
-  GemvArgs wo{};
+  t = none_task();
+  t.kind = T_GEMV;
+  t.M = M;
+  GemvArgs& wo = t.gemv;
   wo.W = w.wo;
   wo.scale = c->fp8 ? w.wo_scale : nullptr;
   wo.rows = d;
@@ -312,10 +331,12 @@ hipError_t enqueue_layer(dar_ctx* c, const Chain& ch, hipStream_t s, const dar_l
   wo.y = ch.x;
   wo.y_stride = d;
   wo.accumulate = 1;
-  e = tracked(c, s, K_WO, layer_tag, [&] { return launch_gemv(wt, wo, s); });
-  if (e != hipSuccess) return e;
+  out.push_back(rec(t, K_WO, tag));
 
-  SwigluArgs sa{};
+  t = none_task();
+  t.kind = T_SWIGLU;
+  t.M = M;
+  SwigluArgs& sa = t.swiglu;
   sa.W1 = w.w1;
   sa.s1 = c->fp8 ? w.w1_scale : nullptr;
   sa.W3 = w.w3;
@@ -329,10 +350,12 @@ hipError_t enqueue_layer(dar_ctx* c, const Chain& ch, hipStream_t s, const dar_l
   sa.eps = g.rms_eps;
   sa.h = ch.h;
   sa.h_stride = g.ffn_dim;
-  e = tracked(c, s, K_W13, layer_tag, [&] { return launch_swiglu(wt, sa, s); });
-  if (e != hipSuccess) return e;
+  out.push_back(rec(t, K_W13, tag));
 
-  GemvArgs w2{};
+  t = none_task();
+  t.kind = T_GEMV;
+  t.M = M;
+  GemvArgs& w2 = t.gemv;
   w2.W = w.w2;
   w2.scale = c->fp8 ? w.w2_scale : nullptr;
   w2.rows = d;
@@ -343,38 +366,45 @@ hipError_t enqueue_layer(dar_ctx* c, const Chain& ch, hipStream_t s, const dar_l
   w2.y = ch.x;
   w2.y_stride = d;
   w2.accumulate = 1;
-  return tracked(c, s, K_W2, layer_tag, [&] { return launch_gemv(wt, w2, s); });
+  out.push_back(rec(t, K_W2, tag));
 }
 
-// Slow chain: the slow layers at *pos_s over the slow residual; with_head adds the
-// codebook-0 head (logits, per-workgroup maxima, h_t) and advances pos_s.
-hipError_t enqueue_slow(dar_ctx* c, hipStream_t s, bool with_head) {
+// Slow chain: the slow layers at *pos_s over the slow residual; with_head adds
+// the codebook-0 head (logits, per-block maxima, h_t), which also advances pos_s.
+std::vector<TaskRec> slow_chain(dar_ctx* c, bool with_head) {
   const dar_config& g = c->cfg;
+  std::vector<TaskRec> out;
   const size_t per_layer = (size_t)g.n_heads_kv * g.max_len * g.head_dim;
-  for (int l = 0; l < g.n_layers_slow; ++l) {
-    hipError_t e = enqueue_layer(c, c->cs, s, c->slow[l], l, 1, c->pos_s, c->ks + l * per_layer,
-                                 c->vs + l * per_layer, g.max_len, c->L.nsplit_slow);
-    if (e != hipSuccess) return e;
+  for (int l = 0; l < g.n_layers_slow; ++l)
+    add_layer(c, out, c->cs, c->slow[l], l, 1, c->pos_s, c->ks + l * per_layer, c->vs + l * per_layer, g.max_len,
+              c->L.nsplit_slow);
+  if (with_head) {
+    Task t = none_task();
+    t.kind = T_HEAD_BF16;
+    t.M = 1;
+    HeadArgs& h0 = t.head;
+    h0.W = c->w0;
+    h0.scale = nullptr;
+    h0.rows = g.vocab_c0;
+    h0.K = g.d_model;
+    h0.x = c->cs.x;
+    h0.gain = c->slow_fn;
+    h0.eps = g.rms_eps;
+    h0.logits = c->logits0;
+    h0.slots = c->slots0;
+    h0.anomalies = c->flags + 1;
+    h0.h_out = c->ht;
+    h0.pos_inc = c->pos_s;
+    out.push_back(rec(t, K_HEAD, 0));
   }
-  if (!with_head) return hipSuccess;
-  HeadArgs h0{};
-  h0.W = c->w0;
-  h0.scale = nullptr;
-  h0.rows = g.vocab_c0;
-  h0.K = g.d_model;
-  h0.x = c->cs.x;
-  h0.gain = c->slow_fn;
-  h0.eps = g.rms_eps;
-  h0.logits = c->logits0;
-  h0.slots = c->slots0;
-  h0.anomalies = c->flags + 1;
-  h0.h_out = c->ht;
-  h0.pos_inc = c->pos_s;
-  return tracked(c, s, K_HEAD, 0, [&] { return launch_head(W_BF16, h0, s); });
+  return out;
 }
 
-CommitArgs commit_common(dar_ctx* c, int k, const unsigned long long* slots, int rows) {
-  CommitArgs a{};
+Task commit_task(dar_ctx* c, int k, const unsigned long long* slots, int rows) {
+  Task t = none_task();
+  t.kind = T_COMMIT;
+  t.M = 1;
+  CommitArgs& a = t.commit;
   a.slots = slots;
   a.nslots = head_grid(rows);
   a.code_index = k;
@@ -386,17 +416,21 @@ CommitArgs commit_common(dar_ctx* c, int k, const unsigned long long* slots, int
   a.ring = c->ring;
   a.pos = c->pos_f;
   a.K = c->cfg.d_model;
-  return a;
+  return t;
 }
 
-// Start of the fast chain: commit codebook 0 of the frame (argmax of the slow
-// head, or the forced code), move its logits and h_t into the frame's buffers,
-// write the fast inputs [h_t, E0[c0]] and the next slow input W0[c0].
-hipError_t enqueue_commit0(dar_ctx* c, hipStream_t s) {
+// Fast chain: commit codebook 0 of the frame (argmax of the slow head, or the
+// forced code), move its logits and h_t into the frame's buffers, write the
+// fast inputs [h_t, E0[c0]] and the next slow input W0[c0]; then the fast AR:
+// pass 1 over fast positions 0 and 1, passes 2..R over position k, each
+// followed by the shared head and its commit.
+std::vector<TaskRec> commit0_chain(dar_ctx* c) {
   const dar_config& g = c->cfg;
   const int d = g.d_model;
   const bool fast = has_fast(&g);
-  CommitArgs a = commit_common(c, 0, c->slots0, g.vocab_c0);
+  std::vector<TaskRec> out;
+  Task t0 = commit_task(c, 0, c->slots0, g.vocab_c0);
+  CommitArgs& a = t0.commit;
   a.pos_inc = fast ? nullptr : c->pos_f;
   a.next_table = fast ? c->fast_emb[0] : nullptr;
   a.next_rows = g.vocab_c0;
@@ -412,25 +446,26 @@ hipError_t enqueue_commit0(dar_ctx* c, hipStream_t s) {
     a.copy_dst[1] = c->cf.x;
     a.copy_n[1] = d;
   }
-  return tracked(c, s, K_OTHER, 0, [&] { return launch_commit(a, s); });
+  out.push_back(rec(t0, K_OTHER, 0));
+  return out;
 }
 
-// The fast AR of one frame: pass 1 over fast positions 0 and 1, passes 2..R
-// over position k, each followed by the shared head and its commit.
-hipError_t enqueue_fast(dar_ctx* c, hipStream_t s) {
+std::vector<TaskRec> fast_chain(dar_ctx* c) {
   const dar_config& g = c->cfg;
   const int d = g.d_model;
-  const int wt = c->fp8 ? W_FP8 : W_BF16;
+  std::vector<TaskRec> out;
+  if (!has_fast(&g)) return out;
   const size_t per_layer = (size_t)g.n_heads_kv * c->L.fast_len * g.head_dim;
   for (int k = 1; k <= g.n_res; ++k) {
     const int M = (k == 1) ? 2 : 1;
     const int* fpos = c->seqpos + (k == 1 ? 0 : k);
-    for (int l = 0; l < g.n_layers_fast; ++l) {
-      hipError_t e = enqueue_layer(c, c->cf, s, c->fast[l], 1000 * k + l, M, fpos, c->kf + l * per_layer,
-                                   c->vf + l * per_layer, c->L.fast_len, 1);
-      if (e != hipSuccess) return e;
-    }
-    HeadArgs hk{};
+    for (int l = 0; l < g.n_layers_fast; ++l)
+      add_layer(c, out, c->cf, c->fast[l], 1000 * k + l, M, fpos, c->kf + l * per_layer, c->vf + l * per_layer,
+                c->L.fast_len, 1);
+    Task t = none_task();
+    t.kind = T_HEAD;
+    t.M = 1;
+    HeadArgs& hk = t.head;
     hk.W = c->fast_head;
     hk.scale = c->fp8 ? c->fast_head_scale : nullptr;
     hk.rows = g.vocab_res;
@@ -441,37 +476,65 @@ hipError_t enqueue_fast(dar_ctx* c, hipStream_t s) {
     hk.logits = c->flogits + (size_t)k * c->L.vmax;
     hk.slots = c->slotsf;
     hk.anomalies = c->flags + 1;
-    hipError_t e = tracked(c, s, K_HEAD, k, [&] { return launch_head(wt, hk, s); });
+    out.push_back(rec(t, K_HEAD, k));
+    Task ck = commit_task(c, k, c->slotsf, g.vocab_res);
+    ck.commit.pos_inc = (k == g.n_res) ? c->pos_f : nullptr;
+    ck.commit.next_table = (k < g.n_res) ? c->fast_emb[k] : nullptr;
+    ck.commit.next_rows = g.vocab_res;
+    ck.commit.next_x = c->cf.x;
+    out.push_back(rec(ck, K_OTHER, k));
+  }
+  return out;
+}
+
+void plan_single(Plan& p, const std::vector<TaskRec>& chain) {
+  for (const TaskRec& r : chain) {
+    p.tasks.push_back(r.t);
+    p.kind.push_back(r.kind);
+    p.layer.push_back(r.layer);
+  }
+}
+
+hipError_t enqueue_plan(dar_ctx* c, const Plan& p, hipStream_t s, size_t ev_base = SIZE_MAX) {
+  const int wt = c->fp8 ? W_FP8 : W_BF16;
+  for (size_t i = 0; i < p.launches(); ++i) {
+    if (ev_base != SIZE_MAX) {
+      hipError_t e = hipEventRecord(c->events[2 * (ev_base + i)], s);
+      if (e != hipSuccess) return e;
+    }
+    hipError_t e = launch_task(wt, p.tasks[i], s);
     if (e != hipSuccess) return e;
-    CommitArgs ck = commit_common(c, k, c->slotsf, g.vocab_res);
-    ck.pos_inc = (k == g.n_res) ? c->pos_f : nullptr;
-    ck.next_table = (k < g.n_res) ? c->fast_emb[k] : nullptr;
-    ck.next_rows = g.vocab_res;
-    ck.next_x = c->cf.x;
-    e = tracked(c, s, K_OTHER, k, [&] { return launch_commit(ck, s); });
-    if (e != hipSuccess) return e;
+    if (ev_base != SIZE_MAX) {
+      e = hipEventRecord(c->events[2 * (ev_base + i) + 1], s);
+      if (e != hipSuccess) return e;
+    }
   }
   return hipSuccess;
 }
 
-int capture(dar_ctx* c, Chain& ch, hipError_t (*body)(dar_ctx*, hipStream_t), const char* what) {
-  if (ch.exec) return DAR_OK;
-  DAR_HIP(c, hipStreamBeginCapture(ch.s, hipStreamCaptureModeThreadLocal), "begin capture");
-  hipError_t e = body(c, ch.s);
-  hipGraph_t g = nullptr;
-  hipError_t e2 = hipStreamEndCapture(ch.s, &g);
-  if (e != hipSuccess) {
-    if (g) (void)hipGraphDestroy(g);
-    return hip_fail(c, e, what);
+// replay the plan's graph on s (captured on s the first time), or launch eagerly
+int run_plan(dar_ctx* c, Plan& p, hipStream_t s, const char* what) {
+  if (p.launches() == 0) return DAR_OK;
+  if (!c->use_graph) {
+    DAR_HIP(c, enqueue_plan(c, p, s), what);
+    return DAR_OK;
   }
-  if (e2 != hipSuccess) return hip_fail(c, e2, "end capture");
-  ch.graph = g;
-  DAR_HIP(c, hipGraphInstantiate(&ch.exec, ch.graph, nullptr, nullptr, 0), "instantiate graph");
+  if (!p.exec) {
+    DAR_HIP(c, hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal), "begin capture");
+    hipError_t e = enqueue_plan(c, p, s);
+    hipGraph_t g = nullptr;
+    hipError_t e2 = hipStreamEndCapture(s, &g);
+    if (e != hipSuccess) {
+      if (g) (void)hipGraphDestroy(g);
+      return hip_fail(c, e, what);
+    }
+    if (e2 != hipSuccess) return hip_fail(c, e2, "end capture");
+    p.graph = g;
+    DAR_HIP(c, hipGraphInstantiate(&p.exec, p.graph, nullptr, nullptr, 0), "instantiate graph");
+  }
+  DAR_HIP(c, hipGraphLaunch(p.exec, s), what);
   return DAR_OK;
 }
-
-hipError_t body_fast(dar_ctx* c, hipStream_t s) { return enqueue_fast(c, s); }
-hipError_t body_slow(dar_ctx* c, hipStream_t s) { return enqueue_slow(c, s, true); }
 
 int copy_outputs(dar_ctx* c, hipStream_t s, int32_t* codes_out, float* logits_out) {
   const dar_config& g = c->cfg;
@@ -503,44 +566,38 @@ int set_force(dar_ctx* c, hipStream_t s, const int32_t* forced) {
 
 // One pipeline step: the fast chain finishes frame i (commit c0, fast AR,
 // outputs) while the slow chain computes the slow step and codebook-0 head of
-// frame i+1. The slow chain starts once c0 of frame i is committed (its input).
+// frame i+1 (when that position exists), starting once c0 is committed.
 int pipeline_step(dar_ctx* c, const int32_t* forced, int32_t* codes_out, float* logits_out, bool run_slow) {
-  const bool fast = has_fast(&c->cfg);
-  if (c->use_graph) {
-    int st = fast ? capture(c, c->cf, body_fast, "capture fast chain") : DAR_OK;
-    if (st == DAR_OK && run_slow) st = capture(c, c->cs, body_slow, "capture slow chain");
-    if (st != DAR_OK) return st;
-  }
   hipStream_t sf = c->cf.s, ss = c->cs.s;
   DAR_HIP(c, hipEventRecord(c->ev_start, c->stream), "record start");
   DAR_HIP(c, hipStreamWaitEvent(sf, c->ev_start, 0), "wait start");
   DAR_HIP(c, hipStreamWaitEvent(sf, c->ev_s_done, 0), "wait slow chain");
   int st = set_force(c, sf, forced);
   if (st != DAR_OK) return st;
-  DAR_HIP(c, enqueue_commit0(c, sf), "commit codebook 0");
+  st = run_plan(c, c->p_c0, sf, "commit codebook 0");
+  if (st != DAR_OK) return st;
   DAR_HIP(c, hipEventRecord(c->ev_c0, sf), "record c0");
   if (run_slow) {
     DAR_HIP(c, hipStreamWaitEvent(ss, c->ev_c0, 0), "slow waits c0");
-    if (c->use_graph) {
-      DAR_HIP(c, hipGraphLaunch(c->cs.exec, ss), "slow graph launch");
-    } else {
-      DAR_HIP(c, enqueue_slow(c, ss, true), "slow chain");
-    }
+    st = run_plan(c, c->p_slow, ss, "slow chain");
+    if (st != DAR_OK) return st;
     DAR_HIP(c, hipEventRecord(c->ev_s_done, ss), "record slow done");
   }
-  if (fast) {
-    if (c->use_graph) {
-      DAR_HIP(c, hipGraphLaunch(c->cf.exec, sf), "fast graph launch");
-    } else {
-      DAR_HIP(c, enqueue_fast(c, sf), "fast chain");
-    }
-  }
+  st = run_plan(c, c->p_fast, sf, "fast chain");
+  if (st != DAR_OK) return st;
   st = copy_outputs(c, sf, codes_out, logits_out);
   if (st != DAR_OK) return st;
   DAR_HIP(c, hipEventRecord(c->ev_f_done, sf), "record fast done");
   DAR_HIP(c, hipStreamWaitEvent(c->stream, c->ev_f_done, 0), "join fast");
   DAR_HIP(c, hipStreamWaitEvent(c->stream, c->ev_s_done, 0), "join slow");
   return DAR_OK;
+}
+
+void free_plan(Plan& p) {
+  if (p.exec) (void)hipGraphExecDestroy(p.exec);
+  if (p.graph) (void)hipGraphDestroy(p.graph);
+  p.exec = nullptr;
+  p.graph = nullptr;
 }
 
 }  // namespace
@@ -642,7 +699,6 @@ int dar_create(const dar_config* cfg, const dar_weights* w, void* workspace, siz
     chains[i]->o = reinterpret_cast<float*>(b + L.o[i]);
     chains[i]->h = reinterpret_cast<float*>(b + L.h[i]);
     chains[i]->part = reinterpret_cast<float*>(b + L.part[i]);
-    chains[i]->M = i == 0 ? 1 : 2;
   }
   c->ht = reinterpret_cast<float*>(b + L.ht);
   c->logits0 = reinterpret_cast<float*>(b + L.logits0);
@@ -663,6 +719,13 @@ int dar_create(const dar_config* cfg, const dar_weights* w, void* workspace, siz
   c->kf = reinterpret_cast<uint16_t*>(b + L.kf);
   c->vf = reinterpret_cast<uint16_t*>(b + L.vf);
 
+  // launch plans: commit of codebook 0, the fast AR, the slow step with its
+  // codebook-0 head, and the slow step alone (prompt positions before the last)
+  plan_single(c->p_c0, commit0_chain(c));
+  plan_single(c->p_fast, fast_chain(c));
+  plan_single(c->p_slow, slow_chain(c, true));
+  plan_single(c->p_prefill, slow_chain(c, false));
+
   auto fail = [&](hipError_t e, const char* what) {
     g_create_error = std::string(what) + ": " + hipGetErrorString(e);
     for (Chain* ch : chains)
@@ -673,6 +736,7 @@ int dar_create(const dar_config* cfg, const dar_weights* w, void* workspace, siz
     return DAR_E_HIP;
   };
   hipError_t e;
+  if ((e = prepare_kernels()) != hipSuccess) return fail(e, "prepare kernels");
   for (Chain* ch : chains)
     if ((e = hipStreamCreateWithFlags(&ch->s, hipStreamNonBlocking)) != hipSuccess) return fail(e, "create stream");
   for (hipEvent_t* ev : {&c->ev_start, &c->ev_c0, &c->ev_f_done, &c->ev_s_done})
@@ -701,6 +765,7 @@ int dar_create(const dar_config* cfg, const dar_weights* w, void* workspace, siz
     return fail(e, "upload positions");
   if ((e = hipStreamSynchronize(c->stream)) != hipSuccess) return fail(e, "synchronize create");
   if ((e = hipEventRecord(c->ev_s_done, c->cs.s)) != hipSuccess) return fail(e, "record event");
+  if ((e = hipEventRecord(c->ev_f_done, c->cf.s)) != hipSuccess) return fail(e, "record event");
   *ctx_out = c;
   return DAR_OK;
 }
@@ -727,19 +792,21 @@ int dar_prefill(dar_ctx* c, int32_t batch, const int32_t* tokens, const int32_t*
   }
   c->prefilled = false;
   const int d = c->cfg.d_model;
-  hipStream_t ss = c->cs.s;
-  // the slow chain runs the prompt token by token after anything already queued
+  hipStream_t s = c->cs.s;
+  // the slow stream runs the prompt token by token after anything already
+  // queued; the last step adds the codebook-0 head, which moves pos_s to n
   DAR_HIP(c, hipEventRecord(c->ev_start, c->stream), "record start");
-  DAR_HIP(c, hipStreamWaitEvent(ss, c->ev_start, 0), "wait start");
-  DAR_HIP(c, hipStreamWaitEvent(ss, c->ev_f_done, 0), "wait fast chain");
+  DAR_HIP(c, hipStreamWaitEvent(s, c->ev_start, 0), "wait start");
+  DAR_HIP(c, hipStreamWaitEvent(s, c->ev_f_done, 0), "wait fast chain");
   for (int p = 0; p < n; ++p) {
-    DAR_HIP(c, launch_embed(c->w0, c->cfg.vocab_c0, d, tokens + p, c->cs.x, c->pos_s, p, c->flags + 1, ss),
+    DAR_HIP(c, launch_embed(c->w0, c->cfg.vocab_c0, d, tokens + p, c->cs.x, c->pos_s, p, c->flags + 1, s),
             "prefill embed");
-    DAR_HIP(c, enqueue_slow(c, ss, p == n - 1), "prefill layers");
+    const int st = run_plan(c, p == n - 1 ? c->p_slow : c->p_prefill, s, "prefill layers");
+    if (st != DAR_OK) return st;
   }
-  // frame 0 sits at position n-1; the slow head above moved pos_s to n
-  DAR_HIP(c, launch_fill_i32(c->pos_f, 1, n - 1, ss), "set frame position");
-  DAR_HIP(c, hipEventRecord(c->ev_s_done, ss), "record slow done");
+  // frame 0 sits at position n-1
+  DAR_HIP(c, launch_fill_i32(c->pos_f, 1, n - 1, s), "set frame position");
+  DAR_HIP(c, hipEventRecord(c->ev_s_done, s), "record slow done");
   const int st = pipeline_step(c, forced, codes_out, logits_out, n < c->cfg.max_len);
   if (st != DAR_OK) return st;
   c->pos_host = n;
@@ -766,15 +833,14 @@ int dar_decode_frame(dar_ctx* c, const int32_t* forced, int32_t* codes_out, floa
 int dar_destroy(dar_ctx* c) {
   if (!c) return DAR_OK;
   (void)hipStreamSynchronize(c->stream);
-  for (Chain* ch : {&c->cs, &c->cf}) {
+  for (Chain* ch : {&c->cs, &c->cf})
     if (ch->s) (void)hipStreamSynchronize(ch->s);
-    if (ch->exec) (void)hipGraphExecDestroy(ch->exec);
-    if (ch->graph) (void)hipGraphDestroy(ch->graph);
-    if (ch->s) (void)hipStreamDestroy(ch->s);
-  }
+  for (Plan* p : {&c->p_c0, &c->p_fast, &c->p_slow, &c->p_prefill}) free_plan(*p);
   for (hipEvent_t ev : c->events) (void)hipEventDestroy(ev);
   for (hipEvent_t ev : {c->ev_start, c->ev_c0, c->ev_f_done, c->ev_s_done})
     if (ev) (void)hipEventDestroy(ev);
+  for (Chain* ch : {&c->cs, &c->cf})
+    if (ch->s) (void)hipStreamDestroy(ch->s);
   delete c;
   return DAR_OK;
 }
@@ -870,6 +936,15 @@ const char* dar_status_string(int status) {
 
 const char* dar_last_error(const dar_ctx* c) { return c ? c->err.c_str() : g_create_error.c_str(); }
 
+// Run one task alone (diagnostic entry points); waits for it.
+static int run_single_task(const Task& t, int wtype, hipStream_t s, const char* what) {
+  hipError_t e = prepare_kernels();
+  if (e == hipSuccess) e = launch_task(wtype, t, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(nullptr, e, what);
+  return DAR_OK;
+}
+
 int dar_op_gemv(int32_t wtype, const void* W, const float* scale, int32_t rows, int32_t cols, const float* x,
                 int32_t M, float* y, void* stream) {
   if (!W || !x || !y || rows < 1 || cols < 256 || cols % 256 || cols > 16384 || (M != 1 && M != 2))
@@ -877,7 +952,10 @@ int dar_op_gemv(int32_t wtype, const void* W, const float* scale, int32_t rows, 
   if (wtype != DAR_WTYPE_BF16 && wtype != DAR_WTYPE_FP8_E4M3_ROW) return DAR_E_INVAL;
   if (wtype == DAR_WTYPE_FP8_E4M3_ROW && !scale) return DAR_E_INVAL;
   if (!aligned16(W) || !aligned16(x)) return DAR_E_INVAL;
-  GemvArgs a{};
+  Task t = none_task();
+  t.kind = T_GEMV;
+  t.M = M;
+  GemvArgs& a = t.gemv;
   a.W = W;
   a.scale = wtype == DAR_WTYPE_FP8_E4M3_ROW ? scale : nullptr;
   a.rows = rows;
@@ -889,9 +967,8 @@ int dar_op_gemv(int32_t wtype, const void* W, const float* scale, int32_t rows, 
   a.y = y;
   a.y_stride = rows;
   a.accumulate = 0;
-  hipError_t e = launch_gemv(wtype == DAR_WTYPE_FP8_E4M3_ROW ? W_FP8 : W_BF16, a, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(nullptr, e, "gemv");
-  return DAR_OK;
+  return run_single_task(t, wtype == DAR_WTYPE_FP8_E4M3_ROW ? W_FP8 : W_BF16, static_cast<hipStream_t>(stream),
+                         "gemv");
 }
 
 int dar_op_attention(const float* q, const void* K, const void* V, int32_t n_heads_q, int32_t n_heads_kv,
@@ -901,18 +978,20 @@ int dar_op_attention(const float* q, const void* K, const void* V, int32_t n_hea
   const int g = n_heads_q / n_heads_kv;
   if ((head_dim != 64 && head_dim != 128) || (g != 1 && g != 2 && g != 4 && g != 8)) return DAR_E_UNSUPPORTED;
   if ((M != 1 && M != 2) || pos < 0 || pos + M > max_len) return DAR_E_INVAL;
-  if (chunk == 0) chunk = kAttnChunkDefault;
-  if (chunk < 16 || chunk % 16) return DAR_E_INVAL;
+  if (chunk != 0 && (chunk < 16 || chunk % 16)) return DAR_E_INVAL;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const int nsplit_max = (max_len + chunk - 1) / chunk;
+  // chunk 0: one block per (query row, KV head), no split
+  const int nsplit_max = chunk == 0 ? 1 : (max_len + chunk - 1) / chunk;
   const size_t pf = attn_partial_floats(M, n_heads_kv, nsplit_max, g, head_dim);
   char* scratch = nullptr;
   const size_t off_pos = align_up(pf * sizeof(float));
-  const size_t bytes = off_pos + 256;
-  hipError_t e = hipMalloc(&scratch, bytes);
+  hipError_t e = hipMalloc(&scratch, off_pos + 256);
   if (e != hipSuccess) return hip_fail(nullptr, e, "attention scratch");
   int* dpos = reinterpret_cast<int*>(scratch + off_pos);
-  AttnArgs a{};
+  Task t = none_task();
+  t.kind = T_ATTN;
+  t.M = M;
+  AttnArgs& a = t.attn;
   a.q = q;
   a.q_stride = n_heads_q * head_dim;
   a.K = static_cast<const uint16_t*>(K);
@@ -922,18 +1001,22 @@ int dar_op_attention(const float* q, const void* K, const void* V, int32_t n_hea
   a.n_heads_q = n_heads_q;
   a.n_heads_kv = n_heads_kv;
   a.head_dim = head_dim;
-  a.chunk = chunk;
+  a.chunk = chunk == 0 ? max_len : chunk;
   a.nsplit_max = nsplit_max;
   a.M = M;
   a.part = reinterpret_cast<float*>(scratch);
   a.out = out;
   a.out_stride = n_heads_q * head_dim;
-  if ((e = launch_fill_i32(dpos, 1, pos, s)) == hipSuccess && (e = launch_attn(a, s)) == hipSuccess) {
-    e = hipStreamSynchronize(s);
+  int st = DAR_OK;
+  if ((e = launch_fill_i32(dpos, 1, pos, s)) != hipSuccess) st = hip_fail(nullptr, e, "attention");
+  if (st == DAR_OK) st = run_single_task(t, W_BF16, s, "attention");
+  if (st == DAR_OK && nsplit_max > 1) {
+    t.kind = T_COMBINE;
+    st = run_single_task(t, W_BF16, s, "attention combine");
   }
+  (void)hipStreamSynchronize(s);
   (void)hipFree(scratch);
-  if (e != hipSuccess) return hip_fail(nullptr, e, "attention");
-  return DAR_OK;
+  return st;
 }
 
 int dar_op_fp8_decode(const void* codes, int32_t n, float* out, void* stream) {
@@ -954,45 +1037,48 @@ int dar_profile_frame(dar_ctx* c, int32_t cap, float* ms_out, int32_t* kind_out,
     c->err = "position reached max_len";
     return DAR_E_CAPACITY;
   }
-  const dar_config& g = c->cfg;
-  const bool run_slow = c->pos_host + 1 < g.max_len;
-  const int launches = 1 + (g.n_res > 0 ? g.n_res * (5 * g.n_layers_fast + 2) : 0) +
-                       (run_slow ? 5 * g.n_layers_slow + 1 : 0);
-  if (cap < launches) {
+  const bool run_slow = c->pos_host + 1 < c->cfg.max_len;
+  const Plan* plans[3] = {&c->p_c0, &c->p_fast, run_slow ? &c->p_slow : nullptr};
+  size_t launches = 0;
+  for (const Plan* p : plans)
+    if (p) launches += p->launches();
+  if ((size_t)cap < launches) {
     c->err = "profile capacity below the frame's launch count";
     return DAR_E_INVAL;
   }
-  while ((int)c->events.size() < 2 * cap) {
+  while (c->events.size() < 2 * launches) {
     hipEvent_t ev;
     DAR_HIP(c, hipEventCreate(&ev), "create event");
     c->events.push_back(ev);
   }
-  // one stream, fast chain of this frame then slow chain of the next, every launch bracketed
+  // the same frame as dar_decode_frame, every launch on one stream and bracketed by events
   hipStream_t s = c->cf.s;
   DAR_HIP(c, hipEventRecord(c->ev_start, c->stream), "record start");
   DAR_HIP(c, hipStreamWaitEvent(s, c->ev_start, 0), "wait start");
   DAR_HIP(c, hipStreamWaitEvent(s, c->ev_s_done, 0), "wait slow chain");
   int st = set_force(c, s, nullptr);
   if (st != DAR_OK) return st;
-  c->recs.clear();
-  c->profiling = true;
-  hipError_t e = enqueue_commit0(c, s);
-  if (e == hipSuccess && has_fast(&g)) e = enqueue_fast(c, s);
-  if (e == hipSuccess && run_slow) e = enqueue_slow(c, s, true);
-  c->profiling = false;
-  if (e != hipSuccess) return hip_fail(c, e, "profiled frame");
+  size_t base = 0;
+  for (const Plan* p : plans) {
+    if (!p) continue;
+    DAR_HIP(c, enqueue_plan(c, *p, s, base), "profiled frame");
+    base += p->launches();
+  }
   DAR_HIP(c, hipEventRecord(c->ev_f_done, s), "record fast done");
   DAR_HIP(c, hipEventRecord(c->ev_s_done, s), "record slow done");
   DAR_HIP(c, hipStreamSynchronize(s), "synchronize profile");
-  const int n = (int)c->recs.size();
-  for (int i = 0; i < n && i < cap; ++i) {
-    float ms = 0.f;
-    DAR_HIP(c, hipEventElapsedTime(&ms, c->events[2 * i], c->events[2 * i + 1]), "event time");
-    ms_out[i] = ms;
-    kind_out[i] = c->recs[i].kind;
-    layer_out[i] = c->recs[i].layer;
+  size_t i = 0;
+  for (const Plan* p : plans) {
+    if (!p) continue;
+    for (size_t j = 0; j < p->launches(); ++j, ++i) {
+      float ms = 0.f;
+      DAR_HIP(c, hipEventElapsedTime(&ms, c->events[2 * i], c->events[2 * i + 1]), "event time");
+      ms_out[i] = ms;
+      kind_out[i] = p->kind[j];
+      layer_out[i] = p->layer[j];
+    }
   }
-  *n_out = n;
+  *n_out = (int32_t)i;
   c->pos_host += 1;
   return DAR_OK;
 }
