@@ -118,22 +118,26 @@ def main():
         recs = []
         for _ in range(args.profile_frames):
             recs += sess.profile_frame()
-        for ms_k, kind, layer in recs:
-            name = N.KIND_NAMES[kind]
-            kernel_table.setdefault(name, []).append((ms_k, layer))
+        # a launch runs one task or two independent tasks side by side; group
+        # launches by the kinds they run
+        for ms_k, tasks in recs:
+            name = "+".join(N.KIND_NAMES[k] for k, _ in tasks)
+            kernel_table.setdefault(name, []).append((ms_k, tasks))
         totals = {k: sum(m for m, _ in v) for k, v in kernel_table.items()}
         dom = max(totals, key=totals.get)
-        per = per_launch_bytes(dims, wl.wtype, dom)
-        # average over the single-row launches (fast pass 1 runs two rows)
-        one_row = [m for m, layer in kernel_table[dom] if not (1000 <= layer < 2000)]
-        avg_ms = sum(one_row) / len(one_row)
+        # average over launches of single-row tasks (fast pass 1 runs two rows)
+        one_row = [(m, tasks) for m, tasks in kernel_table[dom]
+                   if not any(1000 <= layer < 2000 for _, layer in tasks)]
+        per = sum(per_launch_bytes(dims, wl.wtype, N.KIND_NAMES[k]) for k, _ in one_row[0][1])
+        avg_ms = sum(m for m, _ in one_row) / len(one_row)
         achieved = per / (avg_ms / 1000.0)
         roof = {"kernel": dom, "bound": "hbm", "achieved": round(achieved / 1e9, 1), "peak": HBM_PEAK / 1e9,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK, 4), "traffic": None,
                 "bytes_per_launch": per, "avg_launch_us": round(avg_ms * 1000, 2),
                 "launches_timed": len(one_row)}
-        share = {k: round(v / sum(totals.values()), 4) for k, v in totals.items()}
+        share = {k: round(v / sum(totals.values()), 4) for k, v in sorted(totals.items(), key=lambda kv: -kv[1])}
         roof["frame_time_share"] = share
+        roof["launches_per_frame"] = len(recs) // args.profile_frames
         log(f"dominant kernel {dom}: {avg_ms * 1000:.1f} us/launch, {achieved / 1e9:.0f} GB/s; shares {share}")
 
     cpu = None

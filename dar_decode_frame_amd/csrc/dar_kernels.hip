@@ -21,6 +21,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "dar_internal.h"
 
 namespace dar {
@@ -528,6 +530,8 @@ __device__ __forceinline__ void commit_body(const CommitArgs& a, char* lds) {
   unsigned long long* red = reinterpret_cast<unsigned long long*>(lds);
   int* code_sh = reinterpret_cast<int*>(lds + kWaves * sizeof(unsigned long long));
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  // independent loads first: they overlap the slot reduction
+  const int force = *a.force_flag, forced = a.forced[a.code_index], pos = *a.pos;
   unsigned long long b = 0ull;
   for (int i = tid; i < a.nslots; i += kBlock) b = a.slots[i] > b ? a.slots[i] : b;
 #pragma unroll
@@ -542,10 +546,10 @@ __device__ __forceinline__ void commit_body(const CommitArgs& a, char* lds) {
 #pragma unroll
     for (int w = 1; w < kWaves; ++w) m = red[w] > m ? red[w] : m;
     const int pred = (int)(0xffffffffu - (uint32_t)(m & 0xffffffffull));
-    const int code = (*a.force_flag) ? a.forced[a.code_index] : pred;
+    const int code = force ? forced : pred;
     a.pred[a.code_index] = pred;
     a.committed[a.code_index] = code;
-    a.ring[(size_t)(*a.pos) * a.frame_codes + a.code_index] = code;
+    a.ring[(size_t)pos * a.frame_codes + a.code_index] = code;
     *code_sh = code;
   }
   __syncthreads();
@@ -713,27 +717,55 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, int bid, char* lds)
   }
 }
 
-// Combine the splits of one KV head for one query row (bid = m * n_kv + kvh):
-// out = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s.
+// Combine the splits of one query head (bid = (m * n_kv + kvh) * G + h):
+// out = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s. Latency first: the
+// split maxima are loaded in one pass and reduced across wave 0, then every
+// thread issues all its accumulator loads before summing them.
 template <int HD, int G>
-__device__ __forceinline__ void combine_body(const AttnArgs& a, int bid) {
-  const int kvh = bid % a.n_heads_kv, m = bid / a.n_heads_kv, tid = threadIdx.x;
+__device__ __forceinline__ void combine_body(const AttnArgs& a, int bid, char* lds) {
+  constexpr int R = kBlock / HD;  // threads per output element
+  constexpr int U = 8;            // loads in flight per thread
+  const int h = bid % G, kvh = (bid / G) % a.n_heads_kv, m = bid / (G * a.n_heads_kv);
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const int T = *a.pos + m + 1;
   const int nsplit = (T + a.chunk - 1) / a.chunk;
   const int stride_s = G * (HD + 2);
-  const float* part = a.part + (((size_t)m * a.n_heads_kv + kvh) * a.nsplit_max) * stride_s;
-  for (int idx = tid; idx < G * HD; idx += kBlock) {
-    const int h = idx / HD, e = idx % HD;
-    float M = -INFINITY;
-    for (int t = 0; t < nsplit; ++t) M = fmaxf(M, part[(size_t)t * stride_s + h * (HD + 2) + HD]);
-    float num = 0.f, den = 0.f;
-    for (int t = 0; t < nsplit; ++t) {
-      const float* ps = part + (size_t)t * stride_s + h * (HD + 2);
-      const float c = exp2f(ps[HD] - M);
-      num += ps[e] * c;
-      den += ps[HD + 1] * c;
+  const float* part = a.part + (((size_t)m * a.n_heads_kv + kvh) * a.nsplit_max) * stride_s + h * (HD + 2);
+  float* wsh = reinterpret_cast<float*>(lds);  // [nsplit_max] split weights, then the denominator
+  float* red = wsh + a.nsplit_max + 1;         // [R][HD]
+  if (wave == 0) {
+    float mx = -INFINITY;
+    for (int t = lane; t < nsplit; t += kWave) mx = fmaxf(mx, part[(size_t)t * stride_s + HD]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+    float den = 0.f;
+    for (int t = lane; t < nsplit; t += kWave) {
+      const float* ps = part + (size_t)t * stride_s;
+      const float c = exp2f(ps[HD] - mx);
+      wsh[t] = c;
+      den += c * ps[HD + 1];
     }
-    a.out[(size_t)m * a.out_stride + (kvh * G + h) * HD + e] = num / den;
+    den = wave_sum(den);
+    if (lane == 0) wsh[a.nsplit_max] = den;
+  }
+  __syncthreads();
+  const int e = tid % HD, r = tid / HD;
+  float num = 0.f;
+  for (int t0 = r; t0 < nsplit; t0 += R * U) {
+    float v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = part[(size_t)min(t0 + u * R, nsplit - 1) * stride_s + e];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (t0 + u * R < nsplit) num = fmaf(wsh[t0 + u * R], v[u], num);
+  }
+  red[r * HD + e] = num;
+  __syncthreads();
+  if (r == 0) {
+    float sum = red[e];
+#pragma unroll
+    for (int q = 1; q < R; ++q) sum += red[q * HD + e];
+    a.out[(size_t)m * a.out_stride + (kvh * G + h) * HD + e] = sum / wsh[a.nsplit_max];
   }
 }
 
@@ -837,9 +869,9 @@ struct RegStream {
 
 // y[r] (+)= scale[r] * W[r] . x, one row per wave
 template <typename WT, int NCH>
-__global__ __launch_bounds__(kBlock) void k_gemv_reg(GemvArgs a) {
+__device__ __forceinline__ void gemv_reg_body(const GemvArgs& a, int bid) {
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-  const int r = blockIdx.x * kWaves + wave;
+  const int r = bid * kWaves + wave;
   RegStream<WT, NCH, 1> rs;
   rs.load_x(a.x, a.gain, a.K, lane);
   const char* base[1] = {row_ptr<WT>(a.W, min(r, a.rows - 1), a.K)};
@@ -856,11 +888,11 @@ __global__ __launch_bounds__(kBlock) void k_gemv_reg(GemvArgs a) {
 
 // fused RMSNorm + QKV + RoPE + KV append; wave = rotation pair (head, i), (head, i + hd/2)
 template <typename WT, int NCH>
-__global__ __launch_bounds__(kBlock) void k_qkv_reg(QkvArgs a) {
+__device__ __forceinline__ void qkv_reg_body(const QkvArgs& a, int bid) {
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
   const int half = a.head_dim / 2;
   const int n_heads = a.n_heads_q + 2 * a.n_heads_kv;
-  const int p = blockIdx.x * kWaves + wave;
+  const int p = bid * kWaves + wave;
   const bool active = p < n_heads * half;
   const int pc = min(p, n_heads * half - 1);
   const int head = pc / half, i = pc % half;
@@ -897,9 +929,9 @@ __global__ __launch_bounds__(kBlock) void k_qkv_reg(QkvArgs a) {
 
 // fused RMSNorm + W1/W3 + SiLU(a)*b; wave = output r (rows W1[r], W3[r])
 template <typename WT, int NCH>
-__global__ __launch_bounds__(kBlock) void k_swiglu_reg(SwigluArgs a) {
+__device__ __forceinline__ void swiglu_reg_body(const SwigluArgs& a, int bid) {
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-  const int r = blockIdx.x * kWaves + wave;
+  const int r = bid * kWaves + wave;
   const int rc = min(r, a.F - 1);
   RegStream<WT, NCH, 2> rs;
   rs.load_x(a.x, a.gain, a.K, lane);
@@ -919,16 +951,16 @@ __global__ __launch_bounds__(kBlock) void k_swiglu_reg(SwigluArgs a) {
 
 // fused RMSNorm + head GEMV + per-block argmax (two rows per wave)
 template <typename WT, int NCH>
-__global__ __launch_bounds__(kBlock) void k_head_reg(HeadArgs a) {
-  __shared__ unsigned long long wbest[kWaves];
+__device__ __forceinline__ void head_reg_body(const HeadArgs& a, int bid, char* lds) {
+  unsigned long long* wbest = reinterpret_cast<unsigned long long*>(lds);
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-  const int r0 = (blockIdx.x * kWaves + wave) * 2;
+  const int r0 = (bid * kWaves + wave) * 2;
   RegStream<WT, NCH, 2> rs;
   rs.load_x(a.x, a.gain, a.K, lane);
   const char* base[2] = {row_ptr<WT>(a.W, min(r0, a.rows - 1), a.K), row_ptr<WT>(a.W, min(r0 + 1, a.rows - 1), a.K)};
   rs.load_w(base);
   rs.prepare(true, a.eps);
-  if (a.h_out && blockIdx.x == 0 && wave == 0) rs.store_x(a.h_out);
+  if (a.h_out && bid == 0 && wave == 0) rs.store_x(a.h_out);
   unsigned long long best = 0ull;
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
@@ -950,8 +982,8 @@ __global__ __launch_bounds__(kBlock) void k_head_reg(HeadArgs a) {
     unsigned long long b = wbest[0];
 #pragma unroll
     for (int w = 1; w < kWaves; ++w) b = wbest[w] > b ? wbest[w] : b;
-    a.slots[blockIdx.x] = b;  // reduced by the commit that follows
-    if (a.pos_inc && blockIdx.x == 0) *a.pos_inc = *a.pos_inc + 1;
+    a.slots[bid] = b;  // reduced by the commit that follows
+    if (a.pos_inc && bid == 0) *a.pos_inc = *a.pos_inc + 1;
   }
 }
 
@@ -962,13 +994,12 @@ __global__ __launch_bounds__(kBlock) void k_head_reg(HeadArgs a) {
 // K/V loads in flight; per-lane online softmax, merged across lane groups with
 // shuffles and across waves through LDS; the block writes the g heads' output.
 template <int HD, int G, int NW, int U>
-__global__ __launch_bounds__(NW * kWave) void k_attn_wide(AttnArgs a) {
-  extern __shared__ __align__(16) char lds[];
+__device__ __forceinline__ void attn_wide_body(const AttnArgs& a, int bid, char* lds) {
   constexpr int LPP = HD / 8;
   constexpr int PPW = kWave / LPP;
   constexpr int STEP = NW * PPW;
   constexpr int NT = NW * kWave;
-  const int kvh = blockIdx.x % a.n_heads_kv, m = blockIdx.x / a.n_heads_kv;
+  const int kvh = bid % a.n_heads_kv, m = bid / a.n_heads_kv;
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const int T = *a.pos + m + 1;
   const int grp = lane / LPP, sub = lane % LPP;
@@ -1075,40 +1106,114 @@ __global__ __launch_bounds__(NW * kWave) void k_attn_wide(AttnArgs a) {
   }
 }
 
-// ------------------------------------------------- block-index kernels (LDS) --
+// --------------------------------------------------------- stage bodies --
+//
+// Every stage is a body run by one 256-lane workgroup given its block index
+// within the stage. A launch runs one stage, or two independent stages side by
+// side (the slow step of one frame and the fast AR of the previous frame share
+// no data): blocks [0, na) run the first, the rest the second, so the fixed
+// cost of a launch is paid once for both weight streams.
 
-template <typename WT, int M, int RPW>
-__global__ __launch_bounds__(kBlock) void k_gemv(GemvArgs a) {
-  extern __shared__ __align__(16) char lds[];
-  gemv_body<WT, M, RPW>(a, blockIdx.x, lds);
-}
-template <typename WT, int M>
-__global__ __launch_bounds__(kBlock) void k_qkv(QkvArgs a) {
-  extern __shared__ __align__(16) char lds[];
-  qkv_body<WT, M>(a, blockIdx.x, lds);
-}
-template <typename WT, int M>
-__global__ __launch_bounds__(kBlock) void k_swiglu(SwigluArgs a) {
-  extern __shared__ __align__(16) char lds[];
-  swiglu_body<WT, M>(a, blockIdx.x, lds);
-}
-template <typename WT>
-__global__ __launch_bounds__(kBlock) void k_head(HeadArgs a) {
-  extern __shared__ __align__(16) char lds[];
-  head_body<WT>(a, blockIdx.x, lds);
-}
-__global__ __launch_bounds__(kBlock) void k_commit(CommitArgs a) {
-  extern __shared__ __align__(16) char lds[];
-  commit_body(a, lds);
-}
+enum Family { F_GEMV_R, F_GEMV_L, F_QKV_R, F_QKV_L, F_SWI_R, F_SWI_L, F_HEAD_R, F_HEAD_L, F_COMMIT, F_ATT_S,
+              F_ATT_C, F_ATT_W };
+
+template <typename WT_, int NCH>
+struct GemvR {
+  using Args = GemvArgs;
+  using WT = WT_;
+  static constexpr int kFamily = F_GEMV_R, kN = NCH;
+  __device__ static void run(const Args& a, int bid, char*) { gemv_reg_body<WT, NCH>(a, bid); }
+};
+template <typename WT_, int M>
+struct GemvL {
+  using Args = GemvArgs;
+  using WT = WT_;
+  static constexpr int kFamily = F_GEMV_L, kN = M;
+  __device__ static void run(const Args& a, int bid, char* lds) { gemv_body<WT, M, 2>(a, bid, lds); }
+};
+template <typename WT_, int NCH>
+struct QkvR {
+  using Args = QkvArgs;
+  using WT = WT_;
+  static constexpr int kFamily = F_QKV_R, kN = NCH;
+  __device__ static void run(const Args& a, int bid, char*) { qkv_reg_body<WT, NCH>(a, bid); }
+};
+template <typename WT_, int M>
+struct QkvL {
+  using Args = QkvArgs;
+  using WT = WT_;
+  static constexpr int kFamily = F_QKV_L, kN = M;
+  __device__ static void run(const Args& a, int bid, char* lds) { qkv_body<WT, M>(a, bid, lds); }
+};
+template <typename WT_, int NCH>
+struct SwiR {
+  using Args = SwigluArgs;
+  using WT = WT_;
+  static constexpr int kFamily = F_SWI_R, kN = NCH;
+  __device__ static void run(const Args& a, int bid, char*) { swiglu_reg_body<WT, NCH>(a, bid); }
+};
+template <typename WT_, int M>
+struct SwiL {
+  using Args = SwigluArgs;
+  using WT = WT_;
+  static constexpr int kFamily = F_SWI_L, kN = M;
+  __device__ static void run(const Args& a, int bid, char* lds) { swiglu_body<WT, M>(a, bid, lds); }
+};
+template <typename WT_, int NCH>
+struct HeadR {
+  using Args = HeadArgs;
+  using WT = WT_;
+  static constexpr int kFamily = F_HEAD_R, kN = NCH;
+  __device__ static void run(const Args& a, int bid, char* lds) { head_reg_body<WT, NCH>(a, bid, lds); }
+};
+template <typename WT_>
+struct HeadL {
+  using Args = HeadArgs;
+  using WT = WT_;
+  static constexpr int kFamily = F_HEAD_L, kN = 1;
+  __device__ static void run(const Args& a, int bid, char* lds) { head_body<WT>(a, bid, lds); }
+};
+struct Commit {
+  using Args = CommitArgs;
+  using WT = BF16;
+  static constexpr int kFamily = F_COMMIT, kN = 0;
+  __device__ static void run(const Args& a, int, char* lds) { commit_body(a, lds); }
+};
 template <int HD, int G>
-__global__ __launch_bounds__(kBlock) void k_attn_split(AttnArgs a) {
-  extern __shared__ __align__(16) char lds[];
-  attn_body<HD, G>(a, blockIdx.x, lds);
-}
+struct AttS {
+  using Args = AttnArgs;
+  using WT = BF16;
+  static constexpr int kFamily = F_ATT_S, kN = HD * 16 + G;
+  __device__ static void run(const Args& a, int bid, char* lds) { attn_body<HD, G>(a, bid, lds); }
+};
 template <int HD, int G>
-__global__ __launch_bounds__(kBlock) void k_attn_combine(AttnArgs a) {
-  combine_body<HD, G>(a, blockIdx.x);
+struct AttC {
+  using Args = AttnArgs;
+  using WT = BF16;
+  static constexpr int kFamily = F_ATT_C, kN = HD * 16 + G;
+  __device__ static void run(const Args& a, int bid, char* lds) { combine_body<HD, G>(a, bid, lds); }
+};
+template <int HD, int G>
+struct AttW {
+  using Args = AttnArgs;
+  using WT = BF16;
+  static constexpr int kFamily = F_ATT_W, kN = HD * 16 + G;
+  __device__ static void run(const Args& a, int bid, char* lds) { attn_wide_body<HD, G, 4, 2>(a, bid, lds); }
+};
+
+template <class A>
+__global__ __launch_bounds__(kBlock) void k_one(typename A::Args a) {
+  extern __shared__ __align__(16) char lds[];
+  A::run(a, blockIdx.x, lds);
+}
+
+template <class A, class B>
+__global__ __launch_bounds__(kBlock) void k_two(typename A::Args a, typename B::Args b, int na) {
+  extern __shared__ __align__(16) char lds[];
+  if ((int)blockIdx.x < na)
+    A::run(a, blockIdx.x, lds);
+  else
+    B::run(b, (int)blockIdx.x - na, lds);
 }
 
 // ---------------------------------------------------------- small kernels --
@@ -1213,160 +1318,224 @@ static int nch_of(int K) {
   return (K + CW - 1) / CW;
 }
 
-template <typename KernelT, typename ArgT>
-static hipError_t go(KernelT kern, int grid, int block, size_t lds, hipStream_t s, const ArgT& a) {
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(block), lds, s, a);
+// grid and dynamic LDS of one task
+struct Geo {
+  int grid;
+  size_t lds;
+};
+
+// Calls f(Body{}, args, geo) with the body that runs task t (weights of type
+// WT, the codebook-0 head always bf16); false when t has no body.
+#define DAR_NCH_CASES(CALL)    \
+  case 1: CALL(1); return true; \
+  case 2: CALL(2); return true; \
+  case 3: CALL(3); return true; \
+  case 4: CALL(4); return true; \
+  case 5: CALL(5); return true; \
+  case 8: CALL(8); return true; \
+  default: break;
+
+template <typename WT, typename HWT, typename F>
+static bool head_body_for(const HeadArgs& a, F&& f) {
+  const Geo g{head_grid(a.rows), 64};
+#define CALL(N) f(HeadR<HWT, N>{}, a, g)
+  switch (nch_of<HWT>(a.K)) { DAR_NCH_CASES(CALL) }
+#undef CALL
+  f(HeadL<HWT>{}, a, Geo{g.grid, gemv_lds(1, a.K)});
+  return true;
+}
+
+template <int HD, int G, typename F>
+static bool attn_body_for(const Task& t, F&& f) {
+  const AttnArgs& a = t.attn;
+  if (t.kind == T_COMBINE) {
+    f(AttC<HD, G>{}, a, Geo{a.n_heads_kv * G * a.M, ((size_t)a.nsplit_max + 1 + kBlock) * 4});
+  } else if (a.nsplit_max > 1) {
+    f(AttS<HD, G>{}, a, Geo{a.nsplit_max * a.n_heads_kv * a.M, (size_t)kWaves * G * (HD + 2) * 4});
+  } else {
+    // one block per (query row, KV head): the fast AR's <= R+1 positions
+    f(AttW<HD, G>{}, a, Geo{a.n_heads_kv * a.M, (size_t)4 * G * (HD + 2) * 4});
+  }
+  return true;
+}
+
+template <typename WT, typename F>
+static bool with_body(const Task& t, F&& f) {
+  switch (t.kind) {
+    case T_GEMV: {
+      const GemvArgs& a = t.gemv;
+      if (t.M == 1) {
+        const Geo g{(a.rows + kWaves - 1) / kWaves, 0};
+#define CALL(N) f(GemvR<WT, N>{}, a, g)
+        switch (nch_of<WT>(a.K)) { DAR_NCH_CASES(CALL) }
+#undef CALL
+      }
+      const Geo g{(a.rows + kWaves * 2 - 1) / (kWaves * 2), gemv_lds(t.M, a.K)};
+      if (t.M == 2)
+        f(GemvL<WT, 2>{}, a, g);
+      else
+        f(GemvL<WT, 1>{}, a, g);
+      return true;
+    }
+    case T_QKV: {
+      const QkvArgs& a = t.qkv;
+      const int pairs = (a.n_heads_q + 2 * a.n_heads_kv) * a.head_dim / 2;
+      const int grid = (pairs + kWaves - 1) / kWaves;
+      if (t.M == 1) {
+#define CALL(N) f(QkvR<WT, N>{}, a, Geo{grid, 0})
+        switch (nch_of<WT>(a.K)) { DAR_NCH_CASES(CALL) }
+#undef CALL
+      }
+      if (t.M == 2)
+        f(QkvL<WT, 2>{}, a, Geo{grid, gemv_lds(2, a.K)});
+      else
+        f(QkvL<WT, 1>{}, a, Geo{grid, gemv_lds(1, a.K)});
+      return true;
+    }
+    case T_SWIGLU: {
+      const SwigluArgs& a = t.swiglu;
+      const int grid = (a.F + kWaves - 1) / kWaves;
+      if (t.M == 1) {
+#define CALL(N) f(SwiR<WT, N>{}, a, Geo{grid, 0})
+        switch (nch_of<WT>(a.K)) { DAR_NCH_CASES(CALL) }
+#undef CALL
+      }
+      if (t.M == 2)
+        f(SwiL<WT, 2>{}, a, Geo{grid, gemv_lds(2, a.K)});
+      else
+        f(SwiL<WT, 1>{}, a, Geo{grid, gemv_lds(1, a.K)});
+      return true;
+    }
+    case T_HEAD: return head_body_for<WT, WT>(t.head, f);
+    case T_HEAD_BF16: return head_body_for<WT, BF16>(t.head, f);
+    case T_COMMIT: f(Commit{}, t.commit, Geo{1, 64}); return true;
+    case T_ATTN:
+    case T_COMBINE: {
+      const int g = t.attn.n_heads_q / t.attn.n_heads_kv;
+      if (t.attn.head_dim == 128) {
+        switch (g) {
+          case 1: return attn_body_for<128, 1>(t, f);
+          case 2: return attn_body_for<128, 2>(t, f);
+          case 4: return attn_body_for<128, 4>(t, f);
+          case 8: return attn_body_for<128, 8>(t, f);
+        }
+      } else if (t.attn.head_dim == 64) {
+        switch (g) {
+          case 1: return attn_body_for<64, 1>(t, f);
+          case 2: return attn_body_for<64, 2>(t, f);
+          case 4: return attn_body_for<64, 4>(t, f);
+          case 8: return attn_body_for<64, 8>(t, f);
+        }
+      }
+      return false;
+    }
+    default: return false;
+  }
+}
+#undef DAR_NCH_CASES
+
+// Stage pairs that share a launch: the same operation on the two chains (same
+// input width, so the same register layout), with the fast AR's two-row first
+// pass beside a one-row slow stage, and split attention beside the fast AR's
+// one-block-per-head attention.
+template <class A, class B>
+struct PairOk {
+  static constexpr bool kSameWt = std::is_same<typename A::WT, typename B::WT>::value;
+  static constexpr int fa = A::kFamily, fb = B::kFamily;
+  static constexpr bool value =
+      (fa == F_GEMV_R && fb == F_GEMV_R && A::kN == B::kN && kSameWt) ||
+      (fa == F_GEMV_R && fb == F_GEMV_L && B::kN == 2 && kSameWt) ||
+      (fa == F_GEMV_L && fb == F_GEMV_L && A::kN == 1 && kSameWt) ||
+      (fa == F_QKV_R && fb == F_QKV_R && A::kN == B::kN && kSameWt) ||
+      (fa == F_QKV_R && fb == F_QKV_L && B::kN == 2 && kSameWt) ||
+      (fa == F_QKV_L && fb == F_QKV_L && A::kN == 1 && kSameWt) ||
+      (fa == F_SWI_R && fb == F_SWI_R && A::kN == B::kN && kSameWt) ||
+      (fa == F_SWI_R && fb == F_SWI_L && B::kN == 2 && kSameWt) ||
+      (fa == F_SWI_L && fb == F_SWI_L && A::kN == 1 && kSameWt) ||
+      (fa == F_HEAD_R && fb == F_HEAD_R && (kSameWt ? A::kN == B::kN : B::kN == (A::kN + 1) / 2)) ||
+      (fa == F_ATT_S && fb == F_ATT_W && A::kN == B::kN);
+};
+
+// kernels whose dynamic LDS may exceed the default 64 KB get the 160 KB limit once
+template <typename KernelT>
+static hipError_t allow_lds(KernelT kern, size_t lds, bool& done) {
+  if (lds <= 65536 || done) return hipSuccess;
+  const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+  if (e == hipSuccess) done = true;
+  return e;
+}
+
+// prep: only raise the LDS limit (before graph capture), no launch
+template <class A>
+static hipError_t go1(const typename A::Args& a, const Geo& g, hipStream_t s, bool prep) {
+  static bool big = false;
+  hipError_t e = allow_lds(k_one<A>, g.lds, big);
+  if (e != hipSuccess || prep) return e;
+  hipLaunchKernelGGL(k_one<A>, dim3(g.grid), dim3(kBlock), g.lds, s, a);
   return hipGetLastError();
 }
 
-#define DAR_NCH_SWITCH(NCH, CALL) \
-  switch (NCH) {                  \
-    case 1: CALL(1);              \
-    case 2: CALL(2);              \
-    case 3: CALL(3);              \
-    case 4: CALL(4);              \
-    case 5: CALL(5);              \
-    case 8: CALL(8);              \
-    default: break;               \
-  }
-
-template <typename WT>
-static hipError_t gemv_launch(const GemvArgs& a, int M, hipStream_t s) {
-  if (M == 1) {
-    const int grid = (a.rows + kWaves - 1) / kWaves;
-#define CALL(N) return go(k_gemv_reg<WT, N>, grid, kBlock, 0, s, a)
-    DAR_NCH_SWITCH(nch_of<WT>(a.K), CALL)
-#undef CALL
-  }
-  const int grid = (a.rows + kWaves * 2 - 1) / (kWaves * 2);
-  if (M == 2) return go(k_gemv<WT, 2, 2>, grid, kBlock, gemv_lds(2, a.K), s, a);
-  return go(k_gemv<WT, 1, 2>, grid, kBlock, gemv_lds(1, a.K), s, a);
+template <class A, class B>
+static hipError_t go2(const typename A::Args& a, const Geo& ga, const typename B::Args& b, const Geo& gb,
+                      hipStream_t s, bool prep) {
+  static bool big = false;
+  const size_t lds = ga.lds > gb.lds ? ga.lds : gb.lds;
+  hipError_t e = allow_lds(k_two<A, B>, lds, big);
+  if (e != hipSuccess || prep) return e;
+  hipLaunchKernelGGL((k_two<A, B>), dim3(ga.grid + gb.grid), dim3(kBlock), lds, s, a, b, ga.grid);
+  return hipGetLastError();
 }
 
 template <typename WT>
-static hipError_t qkv_launch(const QkvArgs& a, int M, hipStream_t s) {
-  const int pairs = (a.n_heads_q + 2 * a.n_heads_kv) * a.head_dim / 2;
-  const int grid = (pairs + kWaves - 1) / kWaves;
-  if (M == 1) {
-#define CALL(N) return go(k_qkv_reg<WT, N>, grid, kBlock, 0, s, a)
-    DAR_NCH_SWITCH(nch_of<WT>(a.K), CALL)
-#undef CALL
-  }
-  if (M == 2) return go(k_qkv<WT, 2>, grid, kBlock, gemv_lds(2, a.K), s, a);
-  return go(k_qkv<WT, 1>, grid, kBlock, gemv_lds(1, a.K), s, a);
+static hipError_t single_launch(const Task& t, hipStream_t s, bool prep) {
+  if (t.kind == T_NONE) return hipSuccess;
+  hipError_t err = hipErrorInvalidValue;
+  with_body<WT>(t, [&](auto body, const auto& args, const Geo& g) { err = go1<decltype(body)>(args, g, s, prep); });
+  return err;
 }
 
+// dry: only report whether the pair has a kernel; prep: see go1
 template <typename WT>
-static hipError_t swiglu_launch(const SwigluArgs& a, int M, hipStream_t s) {
-  const int grid = (a.F + kWaves - 1) / kWaves;
-  if (M == 1) {
-#define CALL(N) return go(k_swiglu_reg<WT, N>, grid, kBlock, 0, s, a)
-    DAR_NCH_SWITCH(nch_of<WT>(a.K), CALL)
-#undef CALL
-  }
-  if (M == 2) return go(k_swiglu<WT, 2>, grid, kBlock, gemv_lds(2, a.K), s, a);
-  return go(k_swiglu<WT, 1>, grid, kBlock, gemv_lds(1, a.K), s, a);
+static bool pair_launch(const Task& ta, const Task& tb, hipStream_t s, bool dry, bool prep, hipError_t& err) {
+  bool ok = false;
+  with_body<WT>(ta, [&](auto ba, const auto& aa, const Geo& ga) {
+    using A = decltype(ba);
+    with_body<WT>(tb, [&](auto bb, const auto& ab, const Geo& gb) {
+      using B = decltype(bb);
+      if constexpr (PairOk<A, B>::value) {
+        ok = true;
+        if (!dry) err = go2<A, B>(aa, ga, ab, gb, s, prep);
+      }
+    });
+  });
+  return ok;
 }
 
-template <typename WT>
-static hipError_t head_launch(const HeadArgs& a, hipStream_t s) {
-  const int grid = head_grid(a.rows);
-#define CALL(N) return go(k_head_reg<WT, N>, grid, kBlock, 0, s, a)
-  DAR_NCH_SWITCH(nch_of<WT>(a.K), CALL)
-#undef CALL
-  return go(k_head<WT>, grid, kBlock, gemv_lds(1, a.K), s, a);
+static hipError_t single(int wtype, const Task& t, hipStream_t s, bool prep) {
+  return wtype == W_FP8 ? single_launch<FP8>(t, s, prep) : single_launch<BF16>(t, s, prep);
 }
 
-template <int HD, int G>
-static hipError_t attn_launch(const AttnArgs& a, int kind, hipStream_t s) {
-  if (kind == T_COMBINE) return go(k_attn_combine<HD, G>, a.n_heads_kv * a.M, kBlock, 0, s, a);
-  if (a.nsplit_max > 1)
-    return go(k_attn_split<HD, G>, a.nsplit_max * a.n_heads_kv * a.M, kBlock, (size_t)kWaves * G * (HD + 2) * 4, s, a);
-  // one block per (query row, KV head): for short contexts (the fast AR's <= R+1 positions)
-  return go(k_attn_wide<HD, G, 4, 2>, a.n_heads_kv * a.M, 4 * kWave, (size_t)4 * G * (HD + 2) * 4, s, a);
+static hipError_t pair(int wtype, const Task& a, const Task& b, hipStream_t s, bool prep) {
+  if (b.kind == T_NONE) return single(wtype, a, s, prep);
+  if (a.kind == T_NONE) return single(wtype, b, s, prep);
+  hipError_t e = hipSuccess;
+  const bool ok = wtype == W_FP8 ? pair_launch<FP8>(a, b, s, false, prep, e)
+                                 : pair_launch<BF16>(a, b, s, false, prep, e);
+  return ok ? e : hipErrorInvalidValue;
 }
 
-static hipError_t attn_dispatch(const AttnArgs& a, int kind, hipStream_t s) {
-  const int g = a.n_heads_q / a.n_heads_kv;
-  if (a.head_dim == 128) {
-    switch (g) {
-      case 1: return attn_launch<128, 1>(a, kind, s);
-      case 2: return attn_launch<128, 2>(a, kind, s);
-      case 4: return attn_launch<128, 4>(a, kind, s);
-      case 8: return attn_launch<128, 8>(a, kind, s);
-    }
-  } else if (a.head_dim == 64) {
-    switch (g) {
-      case 1: return attn_launch<64, 1>(a, kind, s);
-      case 2: return attn_launch<64, 2>(a, kind, s);
-      case 4: return attn_launch<64, 4>(a, kind, s);
-      case 8: return attn_launch<64, 8>(a, kind, s);
-    }
-  }
-  return hipErrorInvalidValue;
+hipError_t launch_task(int wtype, const Task& t, hipStream_t s) { return single(wtype, t, s, false); }
+
+bool pair_supported(int wtype, const Task& a, const Task& b) {
+  hipError_t e = hipSuccess;
+  return wtype == W_FP8 ? pair_launch<FP8>(a, b, nullptr, true, false, e)
+                        : pair_launch<BF16>(a, b, nullptr, true, false, e);
 }
 
-template <typename WT>
-static hipError_t task_launch(const Task& t, hipStream_t s) {
-  switch (t.kind) {
-    case T_QKV: return qkv_launch<WT>(t.qkv, t.M, s);
-    case T_ATTN:
-    case T_COMBINE: return attn_dispatch(t.attn, t.kind, s);
-    case T_GEMV: return gemv_launch<WT>(t.gemv, t.M, s);
-    case T_SWIGLU: return swiglu_launch<WT>(t.swiglu, t.M, s);
-    case T_HEAD: return head_launch<WT>(t.head, s);
-    case T_HEAD_BF16: return head_launch<BF16>(t.head, s);
-    case T_COMMIT: return go(k_commit, 1, kBlock, 64, s, t.commit);
-    default: return hipSuccess;
-  }
-}
+hipError_t launch_pair(int wtype, const Task& a, const Task& b, hipStream_t s) { return pair(wtype, a, b, s, false); }
 
-hipError_t launch_task(int wtype, const Task& t, hipStream_t s) {
-  return wtype == W_FP8 ? task_launch<FP8>(t, s) : task_launch<BF16>(t, s);
-}
-
-template <typename KernelT>
-static hipError_t allow_lds(KernelT kern) {
-  return hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
-                             160 * 1024);
-}
-
-template <typename WT>
-static hipError_t prepare_wt() {
-  hipError_t e;
-  if ((e = allow_lds(k_gemv<WT, 1, 2>)) != hipSuccess) return e;
-  if ((e = allow_lds(k_gemv<WT, 2, 2>)) != hipSuccess) return e;
-  if ((e = allow_lds(k_qkv<WT, 1>)) != hipSuccess) return e;
-  if ((e = allow_lds(k_qkv<WT, 2>)) != hipSuccess) return e;
-  if ((e = allow_lds(k_swiglu<WT, 1>)) != hipSuccess) return e;
-  if ((e = allow_lds(k_swiglu<WT, 2>)) != hipSuccess) return e;
-  return allow_lds(k_head<WT>);
-}
-
-template <int HD, int G>
-static hipError_t prepare_attn() {
-  hipError_t e;
-  if ((e = allow_lds(k_attn_wide<HD, G, 4, 2>)) != hipSuccess) return e;
-  return allow_lds(k_attn_split<HD, G>);
-}
-
-hipError_t prepare_kernels() {
-  static bool done = false;
-  if (done) return hipSuccess;
-  hipError_t e;
-  if ((e = prepare_wt<BF16>()) != hipSuccess) return e;
-  if ((e = prepare_wt<FP8>()) != hipSuccess) return e;
-  if ((e = prepare_attn<128, 1>()) != hipSuccess) return e;
-  if ((e = prepare_attn<128, 2>()) != hipSuccess) return e;
-  if ((e = prepare_attn<128, 4>()) != hipSuccess) return e;
-  if ((e = prepare_attn<128, 8>()) != hipSuccess) return e;
-  if ((e = prepare_attn<64, 1>()) != hipSuccess) return e;
-  if ((e = prepare_attn<64, 2>()) != hipSuccess) return e;
-  if ((e = prepare_attn<64, 4>()) != hipSuccess) return e;
-  if ((e = prepare_attn<64, 8>()) != hipSuccess) return e;
-  done = true;
-  return hipSuccess;
-}
+hipError_t prepare_pair(int wtype, const Task& a, const Task& b) { return pair(wtype, a, b, nullptr, true); }
 
 size_t attn_partial_floats(int M, int n_kv, int nsplit_max, int group, int head_dim) {
   return (size_t)M * n_kv * nsplit_max * group * (head_dim + 2);

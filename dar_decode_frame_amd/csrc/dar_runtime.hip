@@ -14,14 +14,15 @@
 //                         shared head and a commit that gathers E_k[c_k]
 //
 // The slow step of frame i+1 needs only codebook 0 of frame i, not frame i's
-// fast AR. A call therefore runs two independent chains of launches on two
-// streams: the fast chain finishing frame i (after the commit of its codebook
-// 0) and the slow chain computing the slow step and codebook-0 head of frame
-// i+1; the slow chain starts once codebook 0 is committed. Their weights are
-// nearly equal in size (slow 7.29 GB, fast 9 x 0.83 GB at full shape), so the
-// fixed cost of each launch on one stream is covered by the other stream's
-// weight traffic. Each chain is a plan of launches built once at create and
-// replayed as its own captured graph.
+// fast AR. After the commit of codebook 0, a call therefore has two
+// independent chains of stages: the fast chain finishing frame i and the slow
+// chain computing the slow step and codebook-0 head of frame i+1. Their
+// weights are nearly equal in size (slow 7.29 GB, fast 9 x 0.83 GB at full
+// shape) and their layers have the same shapes, so the two chains are merged
+// into one sequence of launches in which a launch runs a stage of each chain
+// side by side (disjoint blocks): the fixed cost of a launch is paid once for
+// two weight streams. The merged plan is built once at create and replayed as
+// one captured graph (or launched eagerly).
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -182,19 +183,18 @@ struct TaskRec {
   int kind, layer;  // for the profiler
 };
 
-// A sequence of launches, one task each.
+// A sequence of launches of one or two tasks each (b[i].kind == T_NONE: one).
 struct Plan {
-  std::vector<Task> tasks;
-  std::vector<int> kind, layer;
+  std::vector<Task> a, b;
+  std::vector<int> kind_a, kind_b, layer_a, layer_b;
   hipGraph_t graph = nullptr;
   hipGraphExec_t exec = nullptr;
-  size_t launches() const { return tasks.size(); }
+  size_t launches() const { return a.size(); }
 };
 
-// Scratch and stream of one chain of launches.
+// Scratch of one chain of stages.
 struct Chain {
   float *x = nullptr, *q = nullptr, *o = nullptr, *h = nullptr, *part = nullptr;
-  hipStream_t s = nullptr;
 };
 
 struct dar_ctx {
@@ -210,9 +210,11 @@ struct dar_ctx {
   const float* fast_head_scale = nullptr;
 
   hipStream_t stream = nullptr;  // the caller's stream
+  hipStream_t cap = nullptr;     // capture stream
   Chain cs, cf;                  // slow chain (frame i+1) and fast chain (frame i)
-  Plan p_c0, p_fast, p_slow, p_prefill;  // commit of c0, fast AR, slow step + c0 head, slow step alone
-  hipEvent_t ev_start = nullptr, ev_c0 = nullptr, ev_f_done = nullptr, ev_s_done = nullptr;
+  // commit of c0 then the merged slow and fast chains; commit of c0 then the
+  // fast chain alone (last position); slow step with c0 head; slow step alone
+  Plan p_step, p_last, p_slow, p_prefill;
   bool use_graph = true;
 
   char* ws = nullptr;
@@ -487,11 +489,46 @@ std::vector<TaskRec> fast_chain(dar_ctx* c) {
   return out;
 }
 
+void plan_push(Plan& p, const TaskRec* x, const TaskRec* y) {
+  p.a.push_back(x->t);
+  p.kind_a.push_back(x->kind);
+  p.layer_a.push_back(x->layer);
+  p.b.push_back(y ? y->t : none_task());
+  p.kind_b.push_back(y ? y->kind : -1);
+  p.layer_b.push_back(y ? y->layer : -1);
+}
+
 void plan_single(Plan& p, const std::vector<TaskRec>& chain) {
-  for (const TaskRec& r : chain) {
-    p.tasks.push_back(r.t);
-    p.kind.push_back(r.kind);
-    p.layer.push_back(r.layer);
+  for (const TaskRec& r : chain) plan_push(p, &r, nullptr);
+}
+
+// Merge two independent chains into the fewest launches: an order-preserving
+// matching of stages of s with stages of f that may share a launch, of
+// maximum size (longest common subsequence over the pairing relation).
+void plan_merge(Plan& p, const std::vector<TaskRec>& s, const std::vector<TaskRec>& f, int wtype) {
+  const size_t n = s.size(), m = f.size();
+  std::vector<int> best((n + 1) * (m + 1), 0);
+  std::vector<char> ok(n * m, 0);
+  for (size_t i = 0; i < n; ++i)
+    for (size_t j = 0; j < m; ++j) ok[i * m + j] = pair_supported(wtype, s[i].t, f[j].t) ? 1 : 0;
+  auto at = [&](size_t i, size_t j) -> int& { return best[i * (m + 1) + j]; };
+  for (size_t i = n + 1; i-- > 0;) {
+    for (size_t j = m + 1; j-- > 0;) {
+      if (i == n || j == m) continue;
+      int v = at(i + 1, j) > at(i, j + 1) ? at(i + 1, j) : at(i, j + 1);
+      if (ok[i * m + j] && 1 + at(i + 1, j + 1) > v) v = 1 + at(i + 1, j + 1);
+      at(i, j) = v;
+    }
+  }
+  size_t i = 0, j = 0;
+  while (i < n || j < m) {
+    if (i < n && j < m && ok[i * m + j] && at(i, j) == 1 + at(i + 1, j + 1)) {
+      plan_push(p, &s[i++], &f[j++]);
+    } else if (i < n && (j == m || at(i, j) == at(i + 1, j))) {
+      plan_push(p, &s[i++], nullptr);
+    } else {
+      plan_push(p, &f[j++], nullptr);
+    }
   }
 }
 
@@ -502,7 +539,7 @@ hipError_t enqueue_plan(dar_ctx* c, const Plan& p, hipStream_t s, size_t ev_base
       hipError_t e = hipEventRecord(c->events[2 * (ev_base + i)], s);
       if (e != hipSuccess) return e;
     }
-    hipError_t e = launch_task(wt, p.tasks[i], s);
+    hipError_t e = launch_pair(wt, p.a[i], p.b[i], s);
     if (e != hipSuccess) return e;
     if (ev_base != SIZE_MAX) {
       e = hipEventRecord(c->events[2 * (ev_base + i) + 1], s);
@@ -512,7 +549,7 @@ hipError_t enqueue_plan(dar_ctx* c, const Plan& p, hipStream_t s, size_t ev_base
   return hipSuccess;
 }
 
-// replay the plan's graph on s (captured on s the first time), or launch eagerly
+// replay the plan's graph on s (captured on the capture stream the first time), or launch eagerly
 int run_plan(dar_ctx* c, Plan& p, hipStream_t s, const char* what) {
   if (p.launches() == 0) return DAR_OK;
   if (!c->use_graph) {
@@ -520,10 +557,12 @@ int run_plan(dar_ctx* c, Plan& p, hipStream_t s, const char* what) {
     return DAR_OK;
   }
   if (!p.exec) {
-    DAR_HIP(c, hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal), "begin capture");
-    hipError_t e = enqueue_plan(c, p, s);
+    for (size_t i = 0; i < p.launches(); ++i)
+      DAR_HIP(c, prepare_pair(c->fp8 ? W_FP8 : W_BF16, p.a[i], p.b[i]), "prepare launch");
+    DAR_HIP(c, hipStreamBeginCapture(c->cap, hipStreamCaptureModeThreadLocal), "begin capture");
+    hipError_t e = enqueue_plan(c, p, c->cap);
     hipGraph_t g = nullptr;
-    hipError_t e2 = hipStreamEndCapture(s, &g);
+    hipError_t e2 = hipStreamEndCapture(c->cap, &g);
     if (e != hipSuccess) {
       if (g) (void)hipGraphDestroy(g);
       return hip_fail(c, e, what);
@@ -564,33 +603,15 @@ int set_force(dar_ctx* c, hipStream_t s, const int32_t* forced) {
   return DAR_OK;
 }
 
-// One pipeline step: the fast chain finishes frame i (commit c0, fast AR,
-// outputs) while the slow chain computes the slow step and codebook-0 head of
-// frame i+1 (when that position exists), starting once c0 is committed.
+// One pipeline step: commit codebook 0 of frame i, then the fast AR finishing
+// frame i merged with the slow step and codebook-0 head of frame i+1 (when
+// that position exists), then the outputs.
 int pipeline_step(dar_ctx* c, const int32_t* forced, int32_t* codes_out, float* logits_out, bool run_slow) {
-  hipStream_t sf = c->cf.s, ss = c->cs.s;
-  DAR_HIP(c, hipEventRecord(c->ev_start, c->stream), "record start");
-  DAR_HIP(c, hipStreamWaitEvent(sf, c->ev_start, 0), "wait start");
-  DAR_HIP(c, hipStreamWaitEvent(sf, c->ev_s_done, 0), "wait slow chain");
-  int st = set_force(c, sf, forced);
+  int st = set_force(c, c->stream, forced);
   if (st != DAR_OK) return st;
-  st = run_plan(c, c->p_c0, sf, "commit codebook 0");
+  st = run_plan(c, run_slow ? c->p_step : c->p_last, c->stream, "frame");
   if (st != DAR_OK) return st;
-  DAR_HIP(c, hipEventRecord(c->ev_c0, sf), "record c0");
-  if (run_slow) {
-    DAR_HIP(c, hipStreamWaitEvent(ss, c->ev_c0, 0), "slow waits c0");
-    st = run_plan(c, c->p_slow, ss, "slow chain");
-    if (st != DAR_OK) return st;
-    DAR_HIP(c, hipEventRecord(c->ev_s_done, ss), "record slow done");
-  }
-  st = run_plan(c, c->p_fast, sf, "fast chain");
-  if (st != DAR_OK) return st;
-  st = copy_outputs(c, sf, codes_out, logits_out);
-  if (st != DAR_OK) return st;
-  DAR_HIP(c, hipEventRecord(c->ev_f_done, sf), "record fast done");
-  DAR_HIP(c, hipStreamWaitEvent(c->stream, c->ev_f_done, 0), "join fast");
-  DAR_HIP(c, hipStreamWaitEvent(c->stream, c->ev_s_done, 0), "join slow");
-  return DAR_OK;
+  return copy_outputs(c, c->stream, codes_out, logits_out);
 }
 
 void free_plan(Plan& p) {
@@ -721,26 +742,24 @@ int dar_create(const dar_config* cfg, const dar_weights* w, void* workspace, siz
 
   // launch plans: commit of codebook 0, the fast AR, the slow step with its
   // codebook-0 head, and the slow step alone (prompt positions before the last)
-  plan_single(c->p_c0, commit0_chain(c));
-  plan_single(c->p_fast, fast_chain(c));
-  plan_single(c->p_slow, slow_chain(c, true));
-  plan_single(c->p_prefill, slow_chain(c, false));
+  {
+    const std::vector<TaskRec> c0 = commit0_chain(c), fast = fast_chain(c), slow = slow_chain(c, true);
+    plan_single(c->p_step, c0);
+    plan_merge(c->p_step, slow, fast, fp8 ? W_FP8 : W_BF16);
+    plan_single(c->p_last, c0);
+    plan_single(c->p_last, fast);
+    plan_single(c->p_slow, slow);
+    plan_single(c->p_prefill, slow_chain(c, false));
+  }
 
   auto fail = [&](hipError_t e, const char* what) {
     g_create_error = std::string(what) + ": " + hipGetErrorString(e);
-    for (Chain* ch : chains)
-      if (ch->s) (void)hipStreamDestroy(ch->s);
-    for (hipEvent_t ev : {c->ev_start, c->ev_c0, c->ev_f_done, c->ev_s_done})
-      if (ev) (void)hipEventDestroy(ev);
+    if (c->cap) (void)hipStreamDestroy(c->cap);
     delete c;
     return DAR_E_HIP;
   };
   hipError_t e;
-  if ((e = prepare_kernels()) != hipSuccess) return fail(e, "prepare kernels");
-  for (Chain* ch : chains)
-    if ((e = hipStreamCreateWithFlags(&ch->s, hipStreamNonBlocking)) != hipSuccess) return fail(e, "create stream");
-  for (hipEvent_t* ev : {&c->ev_start, &c->ev_c0, &c->ev_f_done, &c->ev_s_done})
-    if ((e = hipEventCreateWithFlags(ev, hipEventDisableTiming)) != hipSuccess) return fail(e, "create event");
+  if ((e = hipStreamCreateWithFlags(&c->cap, hipStreamNonBlocking)) != hipSuccess) return fail(e, "create stream");
 
   // RoPE table: angle p * base^(-2i/hd) in double, cos/sin stored as fp32.
   const int half = cfg->head_dim / 2;
@@ -764,8 +783,6 @@ int dar_create(const dar_config* cfg, const dar_weights* w, void* workspace, siz
       hipSuccess)
     return fail(e, "upload positions");
   if ((e = hipStreamSynchronize(c->stream)) != hipSuccess) return fail(e, "synchronize create");
-  if ((e = hipEventRecord(c->ev_s_done, c->cs.s)) != hipSuccess) return fail(e, "record event");
-  if ((e = hipEventRecord(c->ev_f_done, c->cf.s)) != hipSuccess) return fail(e, "record event");
   *ctx_out = c;
   return DAR_OK;
 }
@@ -792,12 +809,9 @@ int dar_prefill(dar_ctx* c, int32_t batch, const int32_t* tokens, const int32_t*
   }
   c->prefilled = false;
   const int d = c->cfg.d_model;
-  hipStream_t s = c->cs.s;
-  // the slow stream runs the prompt token by token after anything already
-  // queued; the last step adds the codebook-0 head, which moves pos_s to n
-  DAR_HIP(c, hipEventRecord(c->ev_start, c->stream), "record start");
-  DAR_HIP(c, hipStreamWaitEvent(s, c->ev_start, 0), "wait start");
-  DAR_HIP(c, hipStreamWaitEvent(s, c->ev_f_done, 0), "wait fast chain");
+  hipStream_t s = c->stream;
+  // the prompt runs token by token; the last step adds the codebook-0 head,
+  // which moves pos_s to n
   for (int p = 0; p < n; ++p) {
     DAR_HIP(c, launch_embed(c->w0, c->cfg.vocab_c0, d, tokens + p, c->cs.x, c->pos_s, p, c->flags + 1, s),
             "prefill embed");
@@ -806,7 +820,6 @@ int dar_prefill(dar_ctx* c, int32_t batch, const int32_t* tokens, const int32_t*
   }
   // frame 0 sits at position n-1
   DAR_HIP(c, launch_fill_i32(c->pos_f, 1, n - 1, s), "set frame position");
-  DAR_HIP(c, hipEventRecord(c->ev_s_done, s), "record slow done");
   const int st = pipeline_step(c, forced, codes_out, logits_out, n < c->cfg.max_len);
   if (st != DAR_OK) return st;
   c->pos_host = n;
@@ -833,14 +846,9 @@ int dar_decode_frame(dar_ctx* c, const int32_t* forced, int32_t* codes_out, floa
 int dar_destroy(dar_ctx* c) {
   if (!c) return DAR_OK;
   (void)hipStreamSynchronize(c->stream);
-  for (Chain* ch : {&c->cs, &c->cf})
-    if (ch->s) (void)hipStreamSynchronize(ch->s);
-  for (Plan* p : {&c->p_c0, &c->p_fast, &c->p_slow, &c->p_prefill}) free_plan(*p);
+  for (Plan* p : {&c->p_step, &c->p_last, &c->p_slow, &c->p_prefill}) free_plan(*p);
   for (hipEvent_t ev : c->events) (void)hipEventDestroy(ev);
-  for (hipEvent_t ev : {c->ev_start, c->ev_c0, c->ev_f_done, c->ev_s_done})
-    if (ev) (void)hipEventDestroy(ev);
-  for (Chain* ch : {&c->cs, &c->cf})
-    if (ch->s) (void)hipStreamDestroy(ch->s);
+  if (c->cap) (void)hipStreamDestroy(c->cap);
   delete c;
   return DAR_OK;
 }
@@ -938,8 +946,7 @@ const char* dar_last_error(const dar_ctx* c) { return c ? c->err.c_str() : g_cre
 
 // Run one task alone (diagnostic entry points); waits for it.
 static int run_single_task(const Task& t, int wtype, hipStream_t s, const char* what) {
-  hipError_t e = prepare_kernels();
-  if (e == hipSuccess) e = launch_task(wtype, t, s);
+  hipError_t e = launch_task(wtype, t, s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (e != hipSuccess) return hip_fail(nullptr, e, what);
   return DAR_OK;
@@ -1038,10 +1045,8 @@ int dar_profile_frame(dar_ctx* c, int32_t cap, float* ms_out, int32_t* kind_out,
     return DAR_E_CAPACITY;
   }
   const bool run_slow = c->pos_host + 1 < c->cfg.max_len;
-  const Plan* plans[3] = {&c->p_c0, &c->p_fast, run_slow ? &c->p_slow : nullptr};
-  size_t launches = 0;
-  for (const Plan* p : plans)
-    if (p) launches += p->launches();
+  const Plan& p = run_slow ? c->p_step : c->p_last;
+  const size_t launches = p.launches();
   if ((size_t)cap < launches) {
     c->err = "profile capacity below the frame's launch count";
     return DAR_E_INVAL;
@@ -1051,34 +1056,22 @@ int dar_profile_frame(dar_ctx* c, int32_t cap, float* ms_out, int32_t* kind_out,
     DAR_HIP(c, hipEventCreate(&ev), "create event");
     c->events.push_back(ev);
   }
-  // the same frame as dar_decode_frame, every launch on one stream and bracketed by events
-  hipStream_t s = c->cf.s;
-  DAR_HIP(c, hipEventRecord(c->ev_start, c->stream), "record start");
-  DAR_HIP(c, hipStreamWaitEvent(s, c->ev_start, 0), "wait start");
-  DAR_HIP(c, hipStreamWaitEvent(s, c->ev_s_done, 0), "wait slow chain");
+  // the same frame as dar_decode_frame, launched eagerly, every launch bracketed by events
+  hipStream_t s = c->stream;
   int st = set_force(c, s, nullptr);
   if (st != DAR_OK) return st;
-  size_t base = 0;
-  for (const Plan* p : plans) {
-    if (!p) continue;
-    DAR_HIP(c, enqueue_plan(c, *p, s, base), "profiled frame");
-    base += p->launches();
-  }
-  DAR_HIP(c, hipEventRecord(c->ev_f_done, s), "record fast done");
-  DAR_HIP(c, hipEventRecord(c->ev_s_done, s), "record slow done");
+  DAR_HIP(c, enqueue_plan(c, p, s, 0), "profiled frame");
   DAR_HIP(c, hipStreamSynchronize(s), "synchronize profile");
-  size_t i = 0;
-  for (const Plan* p : plans) {
-    if (!p) continue;
-    for (size_t j = 0; j < p->launches(); ++j, ++i) {
-      float ms = 0.f;
-      DAR_HIP(c, hipEventElapsedTime(&ms, c->events[2 * i], c->events[2 * i + 1]), "event time");
-      ms_out[i] = ms;
-      kind_out[i] = p->kind[j];
-      layer_out[i] = p->layer[j];
-    }
+  for (size_t i = 0; i < launches; ++i) {
+    float ms = 0.f;
+    DAR_HIP(c, hipEventElapsedTime(&ms, c->events[2 * i], c->events[2 * i + 1]), "event time");
+    ms_out[i] = ms;
+    kind_out[2 * i] = p.kind_a[i];
+    kind_out[2 * i + 1] = p.kind_b[i];
+    layer_out[2 * i] = p.layer_a[i];
+    layer_out[2 * i + 1] = p.layer_b[i];
   }
-  *n_out = (int32_t)i;
+  *n_out = (int32_t)launches;
   c->pos_host += 1;
   return DAR_OK;
 }

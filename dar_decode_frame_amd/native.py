@@ -237,9 +237,14 @@ def dar_op_fp8_decode(codes_ptr, n, out_ptr, stream_ptr):
 
 
 def dar_profile_frame(ctx, cap=4096):
+    """Per launch: (ms, ((kind, layer), ...)) with one or two tasks."""
     ms = (ctypes.c_float * cap)()
-    kind = (ctypes.c_int32 * cap)()
-    layer = (ctypes.c_int32 * cap)()
+    kind = (ctypes.c_int32 * (2 * cap))()
+    layer = (ctypes.c_int32 * (2 * cap))()
     n = ctypes.c_int32(0)
     _check(lib.dar_profile_frame(ctx, cap, ms, kind, layer, ctypes.byref(n)), "dar_profile_frame", ctx)
-    return [(float(ms[i]), int(kind[i]), int(layer[i])) for i in range(n.value)]
+    out = []
+    for i in range(n.value):
+        tasks = tuple((int(kind[2 * i + j]), int(layer[2 * i + j])) for j in range(2) if kind[2 * i + j] >= 0)
+        out.append((float(ms[i]), tasks))
+    return out

@@ -222,9 +222,13 @@ int dar_op_attention(const float* q, const void* K, const void* V, int32_t n_hea
 int dar_op_fp8_decode(const void* codes, int32_t n, float* out, void* stream);
 
 /* Run one frame eagerly with a HIP event pair around every launch and report
- * per-launch milliseconds, kind and layer (host arrays of capacity cap; *n_out
- * is the number of launches). Kinds: 0 qkv, 1 attention, 2 wo, 3 w13, 4 w2,
- * 5 codebook head, 6 other. The frame advances the state like
+ * per-launch milliseconds (ms_out, host array of capacity cap; *n_out is the
+ * number of launches). A launch runs one task or two independent tasks side
+ * by side: kind_out and layer_out (host arrays of capacity 2*cap) hold the
+ * kind and layer tag of the launch's first task at [2i] and of its second at
+ * [2i+1] (-1 when there is none). Kinds: 0 qkv, 1 attention, 2 wo, 3 w13,
+ * 4 w2, 5 codebook head, 6 other. Layer tags: slow layer l is l; fast layer l
+ * of pass k is 1000k + l. The frame advances the state like
  * dar_decode_frame(ctx, NULL, NULL, NULL). Synchronises the stream. */
 int dar_profile_frame(dar_ctx* ctx, int32_t cap, float* ms_out, int32_t* kind_out,
                       int32_t* layer_out, int32_t* n_out);
