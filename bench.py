@@ -5,8 +5,9 @@ Workload (default s2pro_dual_bf16): 36 slow layers + 4 fast layers x 9
 residual codebooks, d 2560, 32/8 heads of 128, SwiGLU 9728, 4096-entry
 codebooks, random-init N(0, 0.02) bf16 weights, prefill 128 random ids, then
 decode frames at positions 128.. (the tuna-fish README's "prefill 128, decode
-896" run to a 1024 context). A step is one decode frame (one replay of the
-captured frame graph). Inputs are resident in HBM before timing starts.
+896" run to a 1024 context). A step is one decode frame: the fast AR of frame
+i and the slow step of frame i+1 on two streams (eager launches; --graph
+replays captured graphs instead). Inputs are resident in HBM before timing starts.
 
 Prints one JSON line on stdout; progress goes to stderr.
 """
@@ -37,7 +38,7 @@ def main():
     ap.add_argument("--workload", default="s2pro_dual_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-frames", type=int, default=3)
-    ap.add_argument("--eager", action="store_true", help="eager launches instead of the frame graph")
+    ap.add_argument("--graph", action="store_true", help="replay captured graphs instead of eager launches")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -69,7 +70,7 @@ def main():
     weights = DeviceWeights(dims, host, wl.wtype, dev)
     log(f"uploaded{' and quantised' if wl.wtype == 'fp8' else ''} in {time.time() - t0:.1f}s")
     prompt = synth.gen_prompt(wl.prefill_len, dims.vocab_c0, wl.prompt_seed)
-    sess = DarSession(dims, weights, wl.max_len, dev, graph=not args.eager)
+    sess = DarSession(dims, weights, wl.max_len, dev, graph=args.graph)
     stream = sess.stream
 
     # warmup: prefill, W frames (captures the graph), then start over
@@ -118,18 +119,14 @@ def main():
         recs = []
         for _ in range(args.profile_frames):
             recs += sess.profile_frame()
-        # a launch runs one task or two independent tasks side by side; group
-        # launches by the kinds they run
-        for ms_k, tasks in recs:
-            name = "+".join(N.KIND_NAMES[k] for k, _ in tasks)
-            kernel_table.setdefault(name, []).append((ms_k, tasks))
+        for ms_k, kind, layer in recs:
+            kernel_table.setdefault(N.KIND_NAMES[kind], []).append((ms_k, layer))
         totals = {k: sum(m for m, _ in v) for k, v in kernel_table.items()}
         dom = max(totals, key=totals.get)
-        # average over launches of single-row tasks (fast pass 1 runs two rows)
-        one_row = [(m, tasks) for m, tasks in kernel_table[dom]
-                   if not any(1000 <= layer < 2000 for _, layer in tasks)]
-        per = sum(per_launch_bytes(dims, wl.wtype, N.KIND_NAMES[k]) for k, _ in one_row[0][1])
-        avg_ms = sum(m for m, _ in one_row) / len(one_row)
+        per = per_launch_bytes(dims, wl.wtype, dom)
+        # average over the single-row launches (fast pass 1 runs two rows)
+        one_row = [m for m, layer in kernel_table[dom] if not (1000 <= layer < 2000)]
+        avg_ms = sum(one_row) / len(one_row)
         achieved = per / (avg_ms / 1000.0)
         roof = {"kernel": dom, "bound": "hbm", "achieved": round(achieved / 1e9, 1), "peak": HBM_PEAK / 1e9,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK, 4), "traffic": None,
@@ -160,7 +157,7 @@ def main():
         "config": {"workload": wl.name, "batch": 1, "prefill": wl.prefill_len, "first_decode_position": wl.prefill_len,
                    "decode_frames": args.steps, "max_len": wl.max_len, "layers_slow": dims.n_layers_slow,
                    "layers_fast": dims.n_layers_fast, "residual_codebooks": dims.n_res,
-                   "graph": not args.eager},
+                   "graph": args.graph},
         "achieved_gb_s": round(gbs / 1e9, 1),
         "hbm_frac": round(gbs / HBM_PEAK, 4),
         "alg_bytes_per_frame_avg": int(alg_bytes // args.steps),

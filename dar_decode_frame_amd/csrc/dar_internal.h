@@ -148,14 +148,9 @@ struct Task {
 int head_grid(int rows);
 // Launch the kernel specialised for this task (kind, rows M, input width).
 hipError_t launch_task(int wtype, const Task& t, hipStream_t s);
-// Whether tasks a and b (independent of each other) can share one launch.
-bool pair_supported(int wtype, const Task& a, const Task& b);
-// One launch running a on its first blocks and b on the rest; a task of kind
-// T_NONE on either side launches the other alone.
-hipError_t launch_pair(int wtype, const Task& a, const Task& b, hipStream_t s);
-// What launch_pair needs set up on the host (kernel LDS limits) without
-// launching; call before capturing a launch into a graph.
-hipError_t prepare_pair(int wtype, const Task& a, const Task& b);
+// What launch_task needs set up on the host (kernel LDS limits) without
+// launching; call before capturing the launch into a graph.
+hipError_t prepare_task(int wtype, const Task& t);
 
 // x = table[clamp(*tok)] as fp32, *pos_out = pos_value (prefill step input)
 hipError_t launch_embed(const uint16_t* table, int rows, int K, const int* tok, float* x,

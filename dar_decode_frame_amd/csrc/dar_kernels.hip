@@ -21,8 +21,6 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include <type_traits>
-
 #include "dar_internal.h"
 
 namespace dar {
@@ -1109,95 +1107,65 @@ __device__ __forceinline__ void attn_wide_body(const AttnArgs& a, int bid, char*
 // --------------------------------------------------------- stage bodies --
 //
 // Every stage is a body run by one 256-lane workgroup given its block index
-// within the stage. A launch runs one stage, or two independent stages side by
-// side (the slow step of one frame and the fast AR of the previous frame share
-// no data): blocks [0, na) run the first, the rest the second, so the fixed
-// cost of a launch is paid once for both weight streams.
+// within the stage; k_one<Body> launches one stage.
 
-enum Family { F_GEMV_R, F_GEMV_L, F_QKV_R, F_QKV_L, F_SWI_R, F_SWI_L, F_HEAD_R, F_HEAD_L, F_COMMIT, F_ATT_S,
-              F_ATT_C, F_ATT_W };
-
-template <typename WT_, int NCH>
+template <typename WT, int NCH>
 struct GemvR {
   using Args = GemvArgs;
-  using WT = WT_;
-  static constexpr int kFamily = F_GEMV_R, kN = NCH;
   __device__ static void run(const Args& a, int bid, char*) { gemv_reg_body<WT, NCH>(a, bid); }
 };
-template <typename WT_, int M>
+template <typename WT, int M>
 struct GemvL {
   using Args = GemvArgs;
-  using WT = WT_;
-  static constexpr int kFamily = F_GEMV_L, kN = M;
   __device__ static void run(const Args& a, int bid, char* lds) { gemv_body<WT, M, 2>(a, bid, lds); }
 };
-template <typename WT_, int NCH>
+template <typename WT, int NCH>
 struct QkvR {
   using Args = QkvArgs;
-  using WT = WT_;
-  static constexpr int kFamily = F_QKV_R, kN = NCH;
   __device__ static void run(const Args& a, int bid, char*) { qkv_reg_body<WT, NCH>(a, bid); }
 };
-template <typename WT_, int M>
+template <typename WT, int M>
 struct QkvL {
   using Args = QkvArgs;
-  using WT = WT_;
-  static constexpr int kFamily = F_QKV_L, kN = M;
   __device__ static void run(const Args& a, int bid, char* lds) { qkv_body<WT, M>(a, bid, lds); }
 };
-template <typename WT_, int NCH>
+template <typename WT, int NCH>
 struct SwiR {
   using Args = SwigluArgs;
-  using WT = WT_;
-  static constexpr int kFamily = F_SWI_R, kN = NCH;
   __device__ static void run(const Args& a, int bid, char*) { swiglu_reg_body<WT, NCH>(a, bid); }
 };
-template <typename WT_, int M>
+template <typename WT, int M>
 struct SwiL {
   using Args = SwigluArgs;
-  using WT = WT_;
-  static constexpr int kFamily = F_SWI_L, kN = M;
   __device__ static void run(const Args& a, int bid, char* lds) { swiglu_body<WT, M>(a, bid, lds); }
 };
-template <typename WT_, int NCH>
+template <typename WT, int NCH>
 struct HeadR {
   using Args = HeadArgs;
-  using WT = WT_;
-  static constexpr int kFamily = F_HEAD_R, kN = NCH;
   __device__ static void run(const Args& a, int bid, char* lds) { head_reg_body<WT, NCH>(a, bid, lds); }
 };
-template <typename WT_>
+template <typename WT>
 struct HeadL {
   using Args = HeadArgs;
-  using WT = WT_;
-  static constexpr int kFamily = F_HEAD_L, kN = 1;
   __device__ static void run(const Args& a, int bid, char* lds) { head_body<WT>(a, bid, lds); }
 };
 struct Commit {
   using Args = CommitArgs;
-  using WT = BF16;
-  static constexpr int kFamily = F_COMMIT, kN = 0;
   __device__ static void run(const Args& a, int, char* lds) { commit_body(a, lds); }
 };
 template <int HD, int G>
 struct AttS {
   using Args = AttnArgs;
-  using WT = BF16;
-  static constexpr int kFamily = F_ATT_S, kN = HD * 16 + G;
   __device__ static void run(const Args& a, int bid, char* lds) { attn_body<HD, G>(a, bid, lds); }
 };
 template <int HD, int G>
 struct AttC {
   using Args = AttnArgs;
-  using WT = BF16;
-  static constexpr int kFamily = F_ATT_C, kN = HD * 16 + G;
   __device__ static void run(const Args& a, int bid, char* lds) { combine_body<HD, G>(a, bid, lds); }
 };
 template <int HD, int G>
 struct AttW {
   using Args = AttnArgs;
-  using WT = BF16;
-  static constexpr int kFamily = F_ATT_W, kN = HD * 16 + G;
   __device__ static void run(const Args& a, int bid, char* lds) { attn_wide_body<HD, G, 4, 2>(a, bid, lds); }
 };
 
@@ -1207,14 +1175,6 @@ __global__ __launch_bounds__(kBlock) void k_one(typename A::Args a) {
   A::run(a, blockIdx.x, lds);
 }
 
-template <class A, class B>
-__global__ __launch_bounds__(kBlock) void k_two(typename A::Args a, typename B::Args b, int na) {
-  extern __shared__ __align__(16) char lds[];
-  if ((int)blockIdx.x < na)
-    A::run(a, blockIdx.x, lds);
-  else
-    B::run(b, (int)blockIdx.x - na, lds);
-}
 
 // ---------------------------------------------------------- small kernels --
 
@@ -1434,28 +1394,6 @@ static bool with_body(const Task& t, F&& f) {
 }
 #undef DAR_NCH_CASES
 
-// Stage pairs that share a launch: the same operation on the two chains (same
-// input width, so the same register layout), with the fast AR's two-row first
-// pass beside a one-row slow stage, and split attention beside the fast AR's
-// one-block-per-head attention.
-template <class A, class B>
-struct PairOk {
-  static constexpr bool kSameWt = std::is_same<typename A::WT, typename B::WT>::value;
-  static constexpr int fa = A::kFamily, fb = B::kFamily;
-  static constexpr bool value =
-      (fa == F_GEMV_R && fb == F_GEMV_R && A::kN == B::kN && kSameWt) ||
-      (fa == F_GEMV_R && fb == F_GEMV_L && B::kN == 2 && kSameWt) ||
-      (fa == F_GEMV_L && fb == F_GEMV_L && A::kN == 1 && kSameWt) ||
-      (fa == F_QKV_R && fb == F_QKV_R && A::kN == B::kN && kSameWt) ||
-      (fa == F_QKV_R && fb == F_QKV_L && B::kN == 2 && kSameWt) ||
-      (fa == F_QKV_L && fb == F_QKV_L && A::kN == 1 && kSameWt) ||
-      (fa == F_SWI_R && fb == F_SWI_R && A::kN == B::kN && kSameWt) ||
-      (fa == F_SWI_R && fb == F_SWI_L && B::kN == 2 && kSameWt) ||
-      (fa == F_SWI_L && fb == F_SWI_L && A::kN == 1 && kSameWt) ||
-      (fa == F_HEAD_R && fb == F_HEAD_R && (kSameWt ? A::kN == B::kN : B::kN == (A::kN + 1) / 2)) ||
-      (fa == F_ATT_S && fb == F_ATT_W && A::kN == B::kN);
-};
-
 // kernels whose dynamic LDS may exceed the default 64 KB get the 160 KB limit once
 template <typename KernelT>
 static hipError_t allow_lds(KernelT kern, size_t lds, bool& done) {
@@ -1476,17 +1414,6 @@ static hipError_t go1(const typename A::Args& a, const Geo& g, hipStream_t s, bo
   return hipGetLastError();
 }
 
-template <class A, class B>
-static hipError_t go2(const typename A::Args& a, const Geo& ga, const typename B::Args& b, const Geo& gb,
-                      hipStream_t s, bool prep) {
-  static bool big = false;
-  const size_t lds = ga.lds > gb.lds ? ga.lds : gb.lds;
-  hipError_t e = allow_lds(k_two<A, B>, lds, big);
-  if (e != hipSuccess || prep) return e;
-  hipLaunchKernelGGL((k_two<A, B>), dim3(ga.grid + gb.grid), dim3(kBlock), lds, s, a, b, ga.grid);
-  return hipGetLastError();
-}
-
 template <typename WT>
 static hipError_t single_launch(const Task& t, hipStream_t s, bool prep) {
   if (t.kind == T_NONE) return hipSuccess;
@@ -1495,47 +1422,13 @@ static hipError_t single_launch(const Task& t, hipStream_t s, bool prep) {
   return err;
 }
 
-// dry: only report whether the pair has a kernel; prep: see go1
-template <typename WT>
-static bool pair_launch(const Task& ta, const Task& tb, hipStream_t s, bool dry, bool prep, hipError_t& err) {
-  bool ok = false;
-  with_body<WT>(ta, [&](auto ba, const auto& aa, const Geo& ga) {
-    using A = decltype(ba);
-    with_body<WT>(tb, [&](auto bb, const auto& ab, const Geo& gb) {
-      using B = decltype(bb);
-      if constexpr (PairOk<A, B>::value) {
-        ok = true;
-        if (!dry) err = go2<A, B>(aa, ga, ab, gb, s, prep);
-      }
-    });
-  });
-  return ok;
+hipError_t launch_task(int wtype, const Task& t, hipStream_t s) {
+  return wtype == W_FP8 ? single_launch<FP8>(t, s, false) : single_launch<BF16>(t, s, false);
 }
 
-static hipError_t single(int wtype, const Task& t, hipStream_t s, bool prep) {
-  return wtype == W_FP8 ? single_launch<FP8>(t, s, prep) : single_launch<BF16>(t, s, prep);
+hipError_t prepare_task(int wtype, const Task& t) {
+  return wtype == W_FP8 ? single_launch<FP8>(t, nullptr, true) : single_launch<BF16>(t, nullptr, true);
 }
-
-static hipError_t pair(int wtype, const Task& a, const Task& b, hipStream_t s, bool prep) {
-  if (b.kind == T_NONE) return single(wtype, a, s, prep);
-  if (a.kind == T_NONE) return single(wtype, b, s, prep);
-  hipError_t e = hipSuccess;
-  const bool ok = wtype == W_FP8 ? pair_launch<FP8>(a, b, s, false, prep, e)
-                                 : pair_launch<BF16>(a, b, s, false, prep, e);
-  return ok ? e : hipErrorInvalidValue;
-}
-
-hipError_t launch_task(int wtype, const Task& t, hipStream_t s) { return single(wtype, t, s, false); }
-
-bool pair_supported(int wtype, const Task& a, const Task& b) {
-  hipError_t e = hipSuccess;
-  return wtype == W_FP8 ? pair_launch<FP8>(a, b, nullptr, true, false, e)
-                        : pair_launch<BF16>(a, b, nullptr, true, false, e);
-}
-
-hipError_t launch_pair(int wtype, const Task& a, const Task& b, hipStream_t s) { return pair(wtype, a, b, s, false); }
-
-hipError_t prepare_pair(int wtype, const Task& a, const Task& b) { return pair(wtype, a, b, nullptr, true); }
 
 size_t attn_partial_floats(int M, int n_kv, int nsplit_max, int group, int head_dim) {
   return (size_t)M * n_kv * nsplit_max * group * (head_dim + 2);

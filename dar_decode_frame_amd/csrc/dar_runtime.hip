@@ -14,15 +14,16 @@
 //                         shared head and a commit that gathers E_k[c_k]
 //
 // The slow step of frame i+1 needs only codebook 0 of frame i, not frame i's
-// fast AR. After the commit of codebook 0, a call therefore has two
-// independent chains of stages: the fast chain finishing frame i and the slow
-// chain computing the slow step and codebook-0 head of frame i+1. Their
-// weights are nearly equal in size (slow 7.29 GB, fast 9 x 0.83 GB at full
-// shape) and their layers have the same shapes, so the two chains are merged
-// into one sequence of launches in which a launch runs a stage of each chain
-// side by side (disjoint blocks): the fixed cost of a launch is paid once for
-// two weight streams. The merged plan is built once at create and replayed as
-// one captured graph (or launched eagerly).
+// fast AR. A call therefore runs two independent chains of launches on two
+// streams: the fast chain finishing frame i (after the commit of its codebook
+// 0) and the slow chain computing the slow step and codebook-0 head of frame
+// i+1; the slow chain starts once codebook 0 is committed. Their weights are
+// nearly equal in size (slow 7.29 GB, fast 9 x 0.83 GB at full shape), and
+// the GPU runs kernels of the two streams side by side, so the ramp-up and
+// drain of each launch on one stream is covered by the other stream's weight
+// traffic. Each chain is a plan of launches built once at create, launched
+// eagerly (default: two eager streams overlap better than two replayed graphs
+// on ROCm 7.2) or replayed as its own captured graph.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -183,18 +184,19 @@ struct TaskRec {
   int kind, layer;  // for the profiler
 };
 
-// A sequence of launches of one or two tasks each (b[i].kind == T_NONE: one).
+// A sequence of launches, one task each.
 struct Plan {
-  std::vector<Task> a, b;
-  std::vector<int> kind_a, kind_b, layer_a, layer_b;
+  std::vector<Task> tasks;
+  std::vector<int> kind, layer;
   hipGraph_t graph = nullptr;
   hipGraphExec_t exec = nullptr;
-  size_t launches() const { return a.size(); }
+  size_t launches() const { return tasks.size(); }
 };
 
-// Scratch of one chain of stages.
+// Scratch and stream of one chain of launches.
 struct Chain {
   float *x = nullptr, *q = nullptr, *o = nullptr, *h = nullptr, *part = nullptr;
+  hipStream_t s = nullptr;
 };
 
 struct dar_ctx {
@@ -210,12 +212,10 @@ struct dar_ctx {
   const float* fast_head_scale = nullptr;
 
   hipStream_t stream = nullptr;  // the caller's stream
-  hipStream_t cap = nullptr;     // capture stream
   Chain cs, cf;                  // slow chain (frame i+1) and fast chain (frame i)
-  // commit of c0 then the merged slow and fast chains; commit of c0 then the
-  // fast chain alone (last position); slow step with c0 head; slow step alone
-  Plan p_step, p_last, p_slow, p_prefill;
-  bool use_graph = true;
+  Plan p_c0, p_fast, p_slow, p_prefill;  // commit of c0, fast AR, slow step + c0 head, slow step alone
+  hipEvent_t ev_start = nullptr, ev_c0 = nullptr, ev_f_done = nullptr, ev_s_done = nullptr;
+  bool use_graph = false;
 
   char* ws = nullptr;
   float *ht, *logits0, *flogits;
@@ -489,46 +489,11 @@ std::vector<TaskRec> fast_chain(dar_ctx* c) {
   return out;
 }
 
-void plan_push(Plan& p, const TaskRec* x, const TaskRec* y) {
-  p.a.push_back(x->t);
-  p.kind_a.push_back(x->kind);
-  p.layer_a.push_back(x->layer);
-  p.b.push_back(y ? y->t : none_task());
-  p.kind_b.push_back(y ? y->kind : -1);
-  p.layer_b.push_back(y ? y->layer : -1);
-}
-
 void plan_single(Plan& p, const std::vector<TaskRec>& chain) {
-  for (const TaskRec& r : chain) plan_push(p, &r, nullptr);
-}
-
-// Merge two independent chains into the fewest launches: an order-preserving
-// matching of stages of s with stages of f that may share a launch, of
-// maximum size (longest common subsequence over the pairing relation).
-void plan_merge(Plan& p, const std::vector<TaskRec>& s, const std::vector<TaskRec>& f, int wtype) {
-  const size_t n = s.size(), m = f.size();
-  std::vector<int> best((n + 1) * (m + 1), 0);
-  std::vector<char> ok(n * m, 0);
-  for (size_t i = 0; i < n; ++i)
-    for (size_t j = 0; j < m; ++j) ok[i * m + j] = pair_supported(wtype, s[i].t, f[j].t) ? 1 : 0;
-  auto at = [&](size_t i, size_t j) -> int& { return best[i * (m + 1) + j]; };
-  for (size_t i = n + 1; i-- > 0;) {
-    for (size_t j = m + 1; j-- > 0;) {
-      if (i == n || j == m) continue;
-      int v = at(i + 1, j) > at(i, j + 1) ? at(i + 1, j) : at(i, j + 1);
-      if (ok[i * m + j] && 1 + at(i + 1, j + 1) > v) v = 1 + at(i + 1, j + 1);
-      at(i, j) = v;
-    }
-  }
-  size_t i = 0, j = 0;
-  while (i < n || j < m) {
-    if (i < n && j < m && ok[i * m + j] && at(i, j) == 1 + at(i + 1, j + 1)) {
-      plan_push(p, &s[i++], &f[j++]);
-    } else if (i < n && (j == m || at(i, j) == at(i + 1, j))) {
-      plan_push(p, &s[i++], nullptr);
-    } else {
-      plan_push(p, &f[j++], nullptr);
-    }
+  for (const TaskRec& r : chain) {
+    p.tasks.push_back(r.t);
+    p.kind.push_back(r.kind);
+    p.layer.push_back(r.layer);
   }
 }
 
@@ -539,7 +504,7 @@ hipError_t enqueue_plan(dar_ctx* c, const Plan& p, hipStream_t s, size_t ev_base
       hipError_t e = hipEventRecord(c->events[2 * (ev_base + i)], s);
       if (e != hipSuccess) return e;
     }
-    hipError_t e = launch_pair(wt, p.a[i], p.b[i], s);
+    hipError_t e = launch_task(wt, p.tasks[i], s);
     if (e != hipSuccess) return e;
     if (ev_base != SIZE_MAX) {
       e = hipEventRecord(c->events[2 * (ev_base + i) + 1], s);
@@ -549,7 +514,7 @@ hipError_t enqueue_plan(dar_ctx* c, const Plan& p, hipStream_t s, size_t ev_base
   return hipSuccess;
 }
 
-// replay the plan's graph on s (captured on the capture stream the first time), or launch eagerly
+// replay the plan's graph on s (captured on s the first time), or launch eagerly
 int run_plan(dar_ctx* c, Plan& p, hipStream_t s, const char* what) {
   if (p.launches() == 0) return DAR_OK;
   if (!c->use_graph) {
@@ -558,11 +523,11 @@ int run_plan(dar_ctx* c, Plan& p, hipStream_t s, const char* what) {
   }
   if (!p.exec) {
     for (size_t i = 0; i < p.launches(); ++i)
-      DAR_HIP(c, prepare_pair(c->fp8 ? W_FP8 : W_BF16, p.a[i], p.b[i]), "prepare launch");
-    DAR_HIP(c, hipStreamBeginCapture(c->cap, hipStreamCaptureModeThreadLocal), "begin capture");
-    hipError_t e = enqueue_plan(c, p, c->cap);
+      DAR_HIP(c, prepare_task(c->fp8 ? W_FP8 : W_BF16, p.tasks[i]), "prepare launch");
+    DAR_HIP(c, hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal), "begin capture");
+    hipError_t e = enqueue_plan(c, p, s);
     hipGraph_t g = nullptr;
-    hipError_t e2 = hipStreamEndCapture(c->cap, &g);
+    hipError_t e2 = hipStreamEndCapture(s, &g);
     if (e != hipSuccess) {
       if (g) (void)hipGraphDestroy(g);
       return hip_fail(c, e, what);
@@ -603,15 +568,33 @@ int set_force(dar_ctx* c, hipStream_t s, const int32_t* forced) {
   return DAR_OK;
 }
 
-// One pipeline step: commit codebook 0 of frame i, then the fast AR finishing
-// frame i merged with the slow step and codebook-0 head of frame i+1 (when
-// that position exists), then the outputs.
+// One pipeline step: the fast chain finishes frame i (commit c0, fast AR,
+// outputs) while the slow chain computes the slow step and codebook-0 head of
+// frame i+1 (when that position exists), starting once c0 is committed.
 int pipeline_step(dar_ctx* c, const int32_t* forced, int32_t* codes_out, float* logits_out, bool run_slow) {
-  int st = set_force(c, c->stream, forced);
+  hipStream_t sf = c->cf.s, ss = c->cs.s;
+  DAR_HIP(c, hipEventRecord(c->ev_start, c->stream), "record start");
+  DAR_HIP(c, hipStreamWaitEvent(sf, c->ev_start, 0), "wait start");
+  DAR_HIP(c, hipStreamWaitEvent(sf, c->ev_s_done, 0), "wait slow chain");
+  int st = set_force(c, sf, forced);
   if (st != DAR_OK) return st;
-  st = run_plan(c, run_slow ? c->p_step : c->p_last, c->stream, "frame");
+  st = run_plan(c, c->p_c0, sf, "commit codebook 0");
   if (st != DAR_OK) return st;
-  return copy_outputs(c, c->stream, codes_out, logits_out);
+  DAR_HIP(c, hipEventRecord(c->ev_c0, sf), "record c0");
+  if (run_slow) {
+    DAR_HIP(c, hipStreamWaitEvent(ss, c->ev_c0, 0), "slow waits c0");
+    st = run_plan(c, c->p_slow, ss, "slow chain");
+    if (st != DAR_OK) return st;
+    DAR_HIP(c, hipEventRecord(c->ev_s_done, ss), "record slow done");
+  }
+  st = run_plan(c, c->p_fast, sf, "fast chain");
+  if (st != DAR_OK) return st;
+  st = copy_outputs(c, sf, codes_out, logits_out);
+  if (st != DAR_OK) return st;
+  DAR_HIP(c, hipEventRecord(c->ev_f_done, sf), "record fast done");
+  DAR_HIP(c, hipStreamWaitEvent(c->stream, c->ev_f_done, 0), "join fast");
+  DAR_HIP(c, hipStreamWaitEvent(c->stream, c->ev_s_done, 0), "join slow");
+  return DAR_OK;
 }
 
 void free_plan(Plan& p) {
@@ -742,24 +725,25 @@ int dar_create(const dar_config* cfg, const dar_weights* w, void* workspace, siz
 
   // launch plans: commit of codebook 0, the fast AR, the slow step with its
   // codebook-0 head, and the slow step alone (prompt positions before the last)
-  {
-    const std::vector<TaskRec> c0 = commit0_chain(c), fast = fast_chain(c), slow = slow_chain(c, true);
-    plan_single(c->p_step, c0);
-    plan_merge(c->p_step, slow, fast, fp8 ? W_FP8 : W_BF16);
-    plan_single(c->p_last, c0);
-    plan_single(c->p_last, fast);
-    plan_single(c->p_slow, slow);
-    plan_single(c->p_prefill, slow_chain(c, false));
-  }
+  plan_single(c->p_c0, commit0_chain(c));
+  plan_single(c->p_fast, fast_chain(c));
+  plan_single(c->p_slow, slow_chain(c, true));
+  plan_single(c->p_prefill, slow_chain(c, false));
 
   auto fail = [&](hipError_t e, const char* what) {
     g_create_error = std::string(what) + ": " + hipGetErrorString(e);
-    if (c->cap) (void)hipStreamDestroy(c->cap);
+    for (Chain* ch : chains)
+      if (ch->s) (void)hipStreamDestroy(ch->s);
+    for (hipEvent_t ev : {c->ev_start, c->ev_c0, c->ev_f_done, c->ev_s_done})
+      if (ev) (void)hipEventDestroy(ev);
     delete c;
     return DAR_E_HIP;
   };
   hipError_t e;
-  if ((e = hipStreamCreateWithFlags(&c->cap, hipStreamNonBlocking)) != hipSuccess) return fail(e, "create stream");
+  for (Chain* ch : chains)
+    if ((e = hipStreamCreateWithFlags(&ch->s, hipStreamNonBlocking)) != hipSuccess) return fail(e, "create stream");
+  for (hipEvent_t* ev : {&c->ev_start, &c->ev_c0, &c->ev_f_done, &c->ev_s_done})
+    if ((e = hipEventCreateWithFlags(ev, hipEventDisableTiming)) != hipSuccess) return fail(e, "create event");
 
   // RoPE table: angle p * base^(-2i/hd) in double, cos/sin stored as fp32.
   const int half = cfg->head_dim / 2;
@@ -783,6 +767,8 @@ int dar_create(const dar_config* cfg, const dar_weights* w, void* workspace, siz
       hipSuccess)
     return fail(e, "upload positions");
   if ((e = hipStreamSynchronize(c->stream)) != hipSuccess) return fail(e, "synchronize create");
+  if ((e = hipEventRecord(c->ev_s_done, c->cs.s)) != hipSuccess) return fail(e, "record event");
+  if ((e = hipEventRecord(c->ev_f_done, c->cf.s)) != hipSuccess) return fail(e, "record event");
   *ctx_out = c;
   return DAR_OK;
 }
@@ -809,9 +795,12 @@ int dar_prefill(dar_ctx* c, int32_t batch, const int32_t* tokens, const int32_t*
   }
   c->prefilled = false;
   const int d = c->cfg.d_model;
-  hipStream_t s = c->stream;
-  // the prompt runs token by token; the last step adds the codebook-0 head,
-  // which moves pos_s to n
+  hipStream_t s = c->cs.s;
+  // the slow stream runs the prompt token by token after anything already
+  // queued; the last step adds the codebook-0 head, which moves pos_s to n
+  DAR_HIP(c, hipEventRecord(c->ev_start, c->stream), "record start");
+  DAR_HIP(c, hipStreamWaitEvent(s, c->ev_start, 0), "wait start");
+  DAR_HIP(c, hipStreamWaitEvent(s, c->ev_f_done, 0), "wait fast chain");
   for (int p = 0; p < n; ++p) {
     DAR_HIP(c, launch_embed(c->w0, c->cfg.vocab_c0, d, tokens + p, c->cs.x, c->pos_s, p, c->flags + 1, s),
             "prefill embed");
@@ -820,6 +809,7 @@ int dar_prefill(dar_ctx* c, int32_t batch, const int32_t* tokens, const int32_t*
   }
   // frame 0 sits at position n-1
   DAR_HIP(c, launch_fill_i32(c->pos_f, 1, n - 1, s), "set frame position");
+  DAR_HIP(c, hipEventRecord(c->ev_s_done, s), "record slow done");
   const int st = pipeline_step(c, forced, codes_out, logits_out, n < c->cfg.max_len);
   if (st != DAR_OK) return st;
   c->pos_host = n;
@@ -846,9 +836,14 @@ int dar_decode_frame(dar_ctx* c, const int32_t* forced, int32_t* codes_out, floa
 int dar_destroy(dar_ctx* c) {
   if (!c) return DAR_OK;
   (void)hipStreamSynchronize(c->stream);
-  for (Plan* p : {&c->p_step, &c->p_last, &c->p_slow, &c->p_prefill}) free_plan(*p);
+  for (Chain* ch : {&c->cs, &c->cf})
+    if (ch->s) (void)hipStreamSynchronize(ch->s);
+  for (Plan* p : {&c->p_c0, &c->p_fast, &c->p_slow, &c->p_prefill}) free_plan(*p);
   for (hipEvent_t ev : c->events) (void)hipEventDestroy(ev);
-  if (c->cap) (void)hipStreamDestroy(c->cap);
+  for (hipEvent_t ev : {c->ev_start, c->ev_c0, c->ev_f_done, c->ev_s_done})
+    if (ev) (void)hipEventDestroy(ev);
+  for (Chain* ch : {&c->cs, &c->cf})
+    if (ch->s) (void)hipStreamDestroy(ch->s);
   delete c;
   return DAR_OK;
 }
@@ -1045,8 +1040,10 @@ int dar_profile_frame(dar_ctx* c, int32_t cap, float* ms_out, int32_t* kind_out,
     return DAR_E_CAPACITY;
   }
   const bool run_slow = c->pos_host + 1 < c->cfg.max_len;
-  const Plan& p = run_slow ? c->p_step : c->p_last;
-  const size_t launches = p.launches();
+  const Plan* plans[3] = {&c->p_c0, &c->p_fast, run_slow ? &c->p_slow : nullptr};
+  size_t launches = 0;
+  for (const Plan* p : plans)
+    if (p) launches += p->launches();
   if ((size_t)cap < launches) {
     c->err = "profile capacity below the frame's launch count";
     return DAR_E_INVAL;
@@ -1056,22 +1053,34 @@ int dar_profile_frame(dar_ctx* c, int32_t cap, float* ms_out, int32_t* kind_out,
     DAR_HIP(c, hipEventCreate(&ev), "create event");
     c->events.push_back(ev);
   }
-  // the same frame as dar_decode_frame, launched eagerly, every launch bracketed by events
-  hipStream_t s = c->stream;
+  // the same frame as dar_decode_frame, every launch on one stream and bracketed by events
+  hipStream_t s = c->cf.s;
+  DAR_HIP(c, hipEventRecord(c->ev_start, c->stream), "record start");
+  DAR_HIP(c, hipStreamWaitEvent(s, c->ev_start, 0), "wait start");
+  DAR_HIP(c, hipStreamWaitEvent(s, c->ev_s_done, 0), "wait slow chain");
   int st = set_force(c, s, nullptr);
   if (st != DAR_OK) return st;
-  DAR_HIP(c, enqueue_plan(c, p, s, 0), "profiled frame");
-  DAR_HIP(c, hipStreamSynchronize(s), "synchronize profile");
-  for (size_t i = 0; i < launches; ++i) {
-    float ms = 0.f;
-    DAR_HIP(c, hipEventElapsedTime(&ms, c->events[2 * i], c->events[2 * i + 1]), "event time");
-    ms_out[i] = ms;
-    kind_out[2 * i] = p.kind_a[i];
-    kind_out[2 * i + 1] = p.kind_b[i];
-    layer_out[2 * i] = p.layer_a[i];
-    layer_out[2 * i + 1] = p.layer_b[i];
+  size_t base = 0;
+  for (const Plan* p : plans) {
+    if (!p) continue;
+    DAR_HIP(c, enqueue_plan(c, *p, s, base), "profiled frame");
+    base += p->launches();
   }
-  *n_out = (int32_t)launches;
+  DAR_HIP(c, hipEventRecord(c->ev_f_done, s), "record fast done");
+  DAR_HIP(c, hipEventRecord(c->ev_s_done, s), "record slow done");
+  DAR_HIP(c, hipStreamSynchronize(s), "synchronize profile");
+  size_t i = 0;
+  for (const Plan* p : plans) {
+    if (!p) continue;
+    for (size_t j = 0; j < p->launches(); ++j, ++i) {
+      float ms = 0.f;
+      DAR_HIP(c, hipEventElapsedTime(&ms, c->events[2 * i], c->events[2 * i + 1]), "event time");
+      ms_out[i] = ms;
+      kind_out[i] = p->kind[j];
+      layer_out[i] = p->layer[j];
+    }
+  }
+  *n_out = (int32_t)i;
   c->pos_host += 1;
   return DAR_OK;
 }

@@ -110,6 +110,13 @@ _SIGS = {
 def _load():
     if not os.path.exists(LIB_PATH):
         raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m dar_decode_frame_amd.build`")
+    # The library and PyTorch must share one HIP runtime (device pointers and
+    # streams cross between them). Loading torch first makes the library bind
+    # to the runtime torch already holds instead of loading a second one.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(LIB_PATH)
     for name, (args, res) in _SIGS.items():
         fn = getattr(lib, name)
@@ -237,14 +244,10 @@ def dar_op_fp8_decode(codes_ptr, n, out_ptr, stream_ptr):
 
 
 def dar_profile_frame(ctx, cap=4096):
-    """Per launch: (ms, ((kind, layer), ...)) with one or two tasks."""
+    """Per launch: (ms, kind, layer tag)."""
     ms = (ctypes.c_float * cap)()
-    kind = (ctypes.c_int32 * (2 * cap))()
-    layer = (ctypes.c_int32 * (2 * cap))()
+    kind = (ctypes.c_int32 * cap)()
+    layer = (ctypes.c_int32 * cap)()
     n = ctypes.c_int32(0)
     _check(lib.dar_profile_frame(ctx, cap, ms, kind, layer, ctypes.byref(n)), "dar_profile_frame", ctx)
-    out = []
-    for i in range(n.value):
-        tasks = tuple((int(kind[2 * i + j]), int(layer[2 * i + j])) for j in range(2) if kind[2 * i + j] >= 0)
-        out.append((float(ms[i]), tasks))
-    return out
+    return [(float(ms[i]), int(kind[i]), int(layer[i])) for i in range(n.value)]

@@ -95,7 +95,7 @@ class DeviceWeights:
 class DarSession:
     """One dar_ctx: workspace, stream, prefill and frame decode with torch tensors."""
 
-    def __init__(self, dims, weights: DeviceWeights, max_len: int, device="cuda", stream=None, graph=True):
+    def __init__(self, dims, weights: DeviceWeights, max_len: int, device="cuda", stream=None, graph=False):
         self.dims = dims
         self.max_len = max_len
         self.device = device

@@ -150,9 +150,14 @@ int dar_prefill(dar_ctx* ctx, int32_t batch, const int32_t* tokens, const int32_
 
 /* Decode one frame at the next position: the slow AR consumes the previous
  * frame's committed codebook-0 id, then the fast AR emits codebooks 1..n_res.
- * forced / codes_out / logits_out as in dar_prefill. Runs as one replay of a
- * captured HIP graph (unless disabled with dar_set_graph). Errors: DAR_E_STATE
- * before prefill, DAR_E_CAPACITY when the position has reached max_len. */
+ * forced / codes_out / logits_out as in dar_prefill. Internally a call commits
+ * the frame's codebook 0 (whose slow step ran in the previous call or the
+ * prefill), then runs the frame's fast AR and, on a second internal stream at
+ * the same time, the slow step and codebook-0 head of the next position. The
+ * work is ordered after what is already queued on the ctx's stream, and that
+ * stream waits for both internal streams before anything queued later.
+ * Errors: DAR_E_STATE before prefill, DAR_E_CAPACITY when the position has
+ * reached max_len. */
 int dar_decode_frame(dar_ctx* ctx, const int32_t* forced, int32_t* codes_out, float* logits_out);
 
 /* Release the context (graph, events, host state). Waits for the context's
@@ -168,7 +173,8 @@ int dar_reset(dar_ctx* ctx);
  * no synchronisation). */
 int dar_position(const dar_ctx* ctx, int32_t* pos_out);
 
-/* Use the captured frame graph (1, default) or eager launches (0). */
+/* Launch each chain of a frame eagerly (0, default) or replay it as a graph
+ * captured on first use (1). Same results either way. */
 int dar_set_graph(dar_ctx* ctx, int32_t enable);
 
 /* Committed frames [first, first+count) of the ring (index = slow position the
@@ -221,15 +227,12 @@ int dar_op_attention(const float* q, const void* K, const void* V, int32_t n_hea
  * out[i] = value of codes[i] (fp32). codes device uint8 [n], out device fp32 [n]. */
 int dar_op_fp8_decode(const void* codes, int32_t n, float* out, void* stream);
 
-/* Run one frame eagerly with a HIP event pair around every launch and report
- * per-launch milliseconds (ms_out, host array of capacity cap; *n_out is the
- * number of launches). A launch runs one task or two independent tasks side
- * by side: kind_out and layer_out (host arrays of capacity 2*cap) hold the
- * kind and layer tag of the launch's first task at [2i] and of its second at
- * [2i+1] (-1 when there is none). Kinds: 0 qkv, 1 attention, 2 wo, 3 w13,
- * 4 w2, 5 codebook head, 6 other. Layer tags: slow layer l is l; fast layer l
- * of pass k is 1000k + l. The frame advances the state like
- * dar_decode_frame(ctx, NULL, NULL, NULL). Synchronises the stream. */
+/* Run one frame eagerly on one stream with a HIP event pair around every
+ * launch and report per-launch milliseconds, kind and layer tag (host arrays
+ * of capacity cap; *n_out is the number of launches). Kinds: 0 qkv,
+ * 1 attention, 2 wo, 3 w13, 4 w2, 5 codebook head, 6 other. Layer tags: slow
+ * layer l is l; fast layer l of pass k is 1000k + l. The frame advances the
+ * state like dar_decode_frame(ctx, NULL, NULL, NULL). Synchronises. */
 int dar_profile_frame(dar_ctx* ctx, int32_t cap, float* ms_out, int32_t* kind_out,
                       int32_t* layer_out, int32_t* n_out);
 
