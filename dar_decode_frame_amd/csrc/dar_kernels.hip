@@ -787,6 +787,10 @@ struct RegStream {
   u32x4 g[NCH][NG];
   u32x4 w[RPW][NCH];
   int lane, K;
+  int c0 = 0, cs = 1;  // this wave's chunk c is input chunk c0 + c * cs
+
+  // column of this lane's slice of chunk c
+  __device__ __forceinline__ int col_of(int c) const { return (c0 + c * cs) * CW + lane * E; }
 
   __device__ __forceinline__ void load_x(const float* xp, const uint16_t* gain, int K_, int lane_) {
     lane = lane_;
@@ -794,7 +798,7 @@ struct RegStream {
     const uint16_t* gsrc = gain ? gain : reinterpret_cast<const uint16_t*>(xp);
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
-      const int col = min(c * CW + lane * E, K - E);
+      const int col = min(col_of(c), K - E);
 #pragma unroll
       for (int j = 0; j < NX; ++j) x[c][j] = *reinterpret_cast<const float4*>(xp + col + 4 * j);
 #pragma unroll
@@ -805,7 +809,7 @@ struct RegStream {
   __device__ __forceinline__ void load_w(const char* const (&base)[RPW]) {
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
-      const int col = min(c * CW + lane * E, K - E);
+      const int col = min(col_of(c), K - E);
 #pragma unroll
       for (int i = 0; i < RPW; ++i) w[i][c] = ld16_nt(base[i] + (size_t)col * WT::kBytes);
     }
@@ -816,7 +820,7 @@ struct RegStream {
     float ss = 0.f;
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
-      const bool valid = c * CW + lane * E < K;
+      const bool valid = col_of(c) < K;
 #pragma unroll
       for (int j = 0; j < NX; ++j) {
         if (!valid) x[c][j] = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -856,7 +860,7 @@ struct RegStream {
   __device__ __forceinline__ void store_x(float* dst) const {
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
-      const int col = c * CW + lane * E;
+      const int col = col_of(c);
       if (col < K) {
 #pragma unroll
         for (int j = 0; j < NX; ++j) *reinterpret_cast<float4*>(dst + col + 4 * j) = x[c][j];
@@ -878,6 +882,41 @@ __device__ __forceinline__ void gemv_reg_body(const GemvArgs& a, int bid) {
   if (r >= a.rows) return;
   float s = wave_sum(rs.dot_row(0));
   if (lane == 0) {
+    if (a.scale) s *= a.scale[r];
+    float* y = a.y + r;
+    *y = a.accumulate ? (*y + s) : s;
+  }
+}
+
+// Inputs wider than the register path (the FFN down-projection): the block's
+// waves split the input's chunks (wave w takes chunks w, w + 4, ...) over R
+// rows, so each wave holds a quarter of the input in registers and issues all
+// its row loads at once; the partial sums meet in LDS. No input norm.
+template <typename WT, int NCW, int R>
+__device__ __forceinline__ void gemv_split_body(const GemvArgs& a, int bid, char* lds) {
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int r0 = bid * R;
+  RegStream<WT, NCW, R> rs;
+  rs.c0 = wave;
+  rs.cs = kWaves;
+  rs.load_x(a.x, nullptr, a.K, lane);
+  const char* base[R];
+#pragma unroll
+  for (int i = 0; i < R; ++i) base[i] = row_ptr<WT>(a.W, min(r0 + i, a.rows - 1), a.K);
+  rs.load_w(base);
+  rs.prepare(false, 0.f);
+  float* part = reinterpret_cast<float*>(lds);  // [kWaves][R]
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    const float p = wave_sum(rs.dot_row(i));
+    if (lane == 0) part[wave * R + i] = p;
+  }
+  __syncthreads();
+  if (wave == 0 && lane < R && r0 + lane < a.rows) {
+    const int r = r0 + lane;
+    float s = part[lane];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) s += part[w * R + lane];
     if (a.scale) s *= a.scale[r];
     float* y = a.y + r;
     *y = a.accumulate ? (*y + s) : s;
@@ -1114,6 +1153,11 @@ struct GemvR {
   using Args = GemvArgs;
   __device__ static void run(const Args& a, int bid, char*) { gemv_reg_body<WT, NCH>(a, bid); }
 };
+template <typename WT, int NCW, int R>
+struct GemvS {
+  using Args = GemvArgs;
+  __device__ static void run(const Args& a, int bid, char* lds) { gemv_split_body<WT, NCW, R>(a, bid, lds); }
+};
 template <typename WT, int M>
 struct GemvL {
   using Args = GemvArgs;
@@ -1329,6 +1373,17 @@ static bool with_body(const Task& t, F&& f) {
 #define CALL(N) f(GemvR<WT, N>{}, a, g)
         switch (nch_of<WT>(a.K)) { DAR_NCH_CASES(CALL) }
 #undef CALL
+        if (!a.gain) {
+          // wider inputs: four waves split the chunks, two rows per block
+          const Geo gs{(a.rows + 1) / 2, 64};
+#define CALL(N) f(GemvS<WT, N, 2>{}, a, gs)
+          switch ((nch_of<WT>(a.K) + kWaves - 1) / kWaves) {
+            DAR_NCH_CASES(CALL)
+            case 6:
+            case 7: f(GemvS<WT, 8, 2>{}, a, gs); return true;
+          }
+#undef CALL
+        }
       }
       const Geo g{(a.rows + kWaves * 2 - 1) / (kWaves * 2), gemv_lds(t.M, a.K)};
       if (t.M == 2)

@@ -68,7 +68,8 @@ def test_quantizer_bit_exact(env, rows, cols):
     assert np.array_equal(q.cpu().numpy(), codes)
 
 
-GEMV_SHAPES = [(512, 256), (300, 768), (6144, 2560), (2560, 4096), (9728, 2560), (2560, 9728), (4096, 2560)]
+GEMV_SHAPES = [(512, 256), (300, 768), (6144, 2560), (2560, 4096), (9728, 2560), (2560, 9728), (4096, 2560),
+               (33, 3072), (17, 13312)]  # last two: ragged rows over chunk counts split unevenly across waves
 
 
 @pytest.mark.parametrize("wtype", ["bf16", "fp8"])
