@@ -869,22 +869,126 @@ struct RegStream {
   }
 };
 
-// y[r] (+)= scale[r] * W[r] . x, one row per wave
+// Outputs per wave of the register kernels: an fp8 row is half the bytes of a
+// bf16 row, so fp8 waves take two outputs to keep the weight bytes per input
+// slice (read from L2 by every wave) the same.
+template <typename WT>
+struct PerWave {
+  static constexpr int v = 1;
+};
+template <>
+struct PerWave<FP8> {
+  static constexpr int v = 2;
+};
+
+// y[r] (+)= scale[r] * W[r] . x, P rows per wave
 template <typename WT, int NCH>
 __device__ __forceinline__ void gemv_reg_body(const GemvArgs& a, int bid) {
+  constexpr int P = PerWave<WT>::v;
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-  const int r = bid * kWaves + wave;
-  RegStream<WT, NCH, 1> rs;
+  const int r0 = (bid * kWaves + wave) * P;
+  RegStream<WT, NCH, P> rs;
   rs.load_x(a.x, a.gain, a.K, lane);
-  const char* base[1] = {row_ptr<WT>(a.W, min(r, a.rows - 1), a.K)};
+  const char* base[P];
+#pragma unroll
+  for (int i = 0; i < P; ++i) base[i] = row_ptr<WT>(a.W, min(r0 + i, a.rows - 1), a.K);
   rs.load_w(base);
   rs.prepare(a.gain != nullptr, a.eps);
-  if (r >= a.rows) return;
-  float s = wave_sum(rs.dot_row(0));
-  if (lane == 0) {
-    if (a.scale) s *= a.scale[r];
-    float* y = a.y + r;
-    *y = a.accumulate ? (*y + s) : s;
+#pragma unroll
+  for (int i = 0; i < P; ++i) {
+    const int r = r0 + i;
+    if (r >= a.rows) return;
+    float s = wave_sum(rs.dot_row(i));
+    if (lane == 0) {
+      if (a.scale) s *= a.scale[r];
+      float* y = a.y + r;
+      *y = a.accumulate ? (*y + s) : s;
+    }
+  }
+}
+
+// fused RMSNorm + QKV + RoPE + KV append; a wave takes P rotation pairs
+// (head, i), (head, i + hd/2)
+template <typename WT, int NCH>
+__device__ __forceinline__ void qkv_reg_body(const QkvArgs& a, int bid) {
+  constexpr int P = PerWave<WT>::v;
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int half = a.head_dim / 2;
+  const int n_heads = a.n_heads_q + 2 * a.n_heads_kv;
+  const int npairs = n_heads * half;
+  const int p0 = (bid * kWaves + wave) * P;
+  RegStream<WT, NCH, 2 * P> rs;
+  rs.load_x(a.x, a.gain, a.K, lane);
+  const char* base[2 * P];
+#pragma unroll
+  for (int j = 0; j < P; ++j) {
+    const int pc = min(p0 + j, npairs - 1);
+    const int r1 = (pc / half) * a.head_dim + pc % half;
+    base[2 * j] = row_ptr<WT>(a.W, r1, a.K);
+    base[2 * j + 1] = row_ptr<WT>(a.W, r1 + half, a.K);
+  }
+  rs.load_w(base);
+  rs.prepare(true, a.eps);
+  const int pos = *a.pos;
+#pragma unroll
+  for (int j = 0; j < P; ++j) {
+    const int p = p0 + j;
+    if (p >= npairs) return;
+    const int head = p / half, i = p % half;
+    const int r1 = head * a.head_dim + i, r2 = r1 + half;
+    const float y1 = wave_sum(rs.dot_row(2 * j));
+    const float y2 = wave_sum(rs.dot_row(2 * j + 1));
+    if (lane != 0) continue;
+    const float u = y1 * (a.scale ? a.scale[r1] : 1.f), v = y2 * (a.scale ? a.scale[r2] : 1.f);
+    if (head < a.n_heads_q + a.n_heads_kv) {
+      const float2 cs = a.rope[(size_t)pos * half + i];
+      const float o1 = u * cs.x - v * cs.y;
+      const float o2 = u * cs.y + v * cs.x;
+      if (head < a.n_heads_q) {
+        a.q_out[r1] = o1;
+        a.q_out[r2] = o2;
+      } else {
+        uint16_t* kp = a.kc + ((size_t)(head - a.n_heads_q) * a.cache_len + pos) * a.head_dim;
+        kp[i] = f2bf(o1);
+        kp[i + half] = f2bf(o2);
+      }
+    } else {
+      uint16_t* vp = a.vc + ((size_t)(head - a.n_heads_q - a.n_heads_kv) * a.cache_len + pos) * a.head_dim;
+      vp[i] = f2bf(u);
+      vp[i + half] = f2bf(v);
+    }
+  }
+}
+
+// fused RMSNorm + W1/W3 + SiLU(a)*b; a wave takes P outputs r (rows W1[r], W3[r])
+template <typename WT, int NCH>
+__device__ __forceinline__ void swiglu_reg_body(const SwigluArgs& a, int bid) {
+  constexpr int P = PerWave<WT>::v;
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int r0 = (bid * kWaves + wave) * P;
+  RegStream<WT, NCH, 2 * P> rs;
+  rs.load_x(a.x, a.gain, a.K, lane);
+  const char* base[2 * P];
+#pragma unroll
+  for (int j = 0; j < P; ++j) {
+    const int rc = min(r0 + j, a.F - 1);
+    base[2 * j] = row_ptr<WT>(a.W1, rc, a.K);
+    base[2 * j + 1] = row_ptr<WT>(a.W3, rc, a.K);
+  }
+  rs.load_w(base);
+  rs.prepare(true, a.eps);
+#pragma unroll
+  for (int j = 0; j < P; ++j) {
+    const int r = r0 + j;
+    if (r >= a.F) return;
+    float g = wave_sum(rs.dot_row(2 * j));
+    float u = wave_sum(rs.dot_row(2 * j + 1));
+    if (lane == 0) {
+      if (a.s1) g *= a.s1[r];
+      if (a.s3) u *= a.s3[r];
+      const float silu = g / (1.0f + expf(-g));
+      a.h[r] = silu * u;
+    }
   }
 }
 
@@ -920,69 +1024,6 @@ __device__ __forceinline__ void gemv_split_body(const GemvArgs& a, int bid, char
     if (a.scale) s *= a.scale[r];
     float* y = a.y + r;
     *y = a.accumulate ? (*y + s) : s;
-  }
-}
-
-// fused RMSNorm + QKV + RoPE + KV append; wave = rotation pair (head, i), (head, i + hd/2)
-template <typename WT, int NCH>
-__device__ __forceinline__ void qkv_reg_body(const QkvArgs& a, int bid) {
-  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-  const int half = a.head_dim / 2;
-  const int n_heads = a.n_heads_q + 2 * a.n_heads_kv;
-  const int p = bid * kWaves + wave;
-  const bool active = p < n_heads * half;
-  const int pc = min(p, n_heads * half - 1);
-  const int head = pc / half, i = pc % half;
-  const int r1 = head * a.head_dim + i, r2 = r1 + half;
-  RegStream<WT, NCH, 2> rs;
-  rs.load_x(a.x, a.gain, a.K, lane);
-  const char* base[2] = {row_ptr<WT>(a.W, r1, a.K), row_ptr<WT>(a.W, r2, a.K)};
-  rs.load_w(base);
-  rs.prepare(true, a.eps);
-  if (!active) return;
-  const float y1 = wave_sum(rs.dot_row(0));
-  const float y2 = wave_sum(rs.dot_row(1));
-  if (lane != 0) return;
-  const float u = y1 * (a.scale ? a.scale[r1] : 1.f), v = y2 * (a.scale ? a.scale[r2] : 1.f);
-  const int pos = *a.pos;
-  if (head < a.n_heads_q + a.n_heads_kv) {
-    const float2 cs = a.rope[(size_t)pos * half + i];
-    const float o1 = u * cs.x - v * cs.y;
-    const float o2 = u * cs.y + v * cs.x;
-    if (head < a.n_heads_q) {
-      a.q_out[r1] = o1;
-      a.q_out[r2] = o2;
-    } else {
-      uint16_t* kp = a.kc + ((size_t)(head - a.n_heads_q) * a.cache_len + pos) * a.head_dim;
-      kp[i] = f2bf(o1);
-      kp[i + half] = f2bf(o2);
-    }
-  } else {
-    uint16_t* vp = a.vc + ((size_t)(head - a.n_heads_q - a.n_heads_kv) * a.cache_len + pos) * a.head_dim;
-    vp[i] = f2bf(u);
-    vp[i + half] = f2bf(v);
-  }
-}
-
-// fused RMSNorm + W1/W3 + SiLU(a)*b; wave = output r (rows W1[r], W3[r])
-template <typename WT, int NCH>
-__device__ __forceinline__ void swiglu_reg_body(const SwigluArgs& a, int bid) {
-  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-  const int r = bid * kWaves + wave;
-  const int rc = min(r, a.F - 1);
-  RegStream<WT, NCH, 2> rs;
-  rs.load_x(a.x, a.gain, a.K, lane);
-  const char* base[2] = {row_ptr<WT>(a.W1, rc, a.K), row_ptr<WT>(a.W3, rc, a.K)};
-  rs.load_w(base);
-  rs.prepare(true, a.eps);
-  if (r >= a.F) return;
-  float g = wave_sum(rs.dot_row(0));
-  float u = wave_sum(rs.dot_row(1));
-  if (lane == 0) {
-    if (a.s1) g *= a.s1[r];
-    if (a.s3) u *= a.s3[r];
-    const float silu = g / (1.0f + expf(-g));
-    a.h[r] = silu * u;
   }
 }
 
@@ -1369,7 +1410,7 @@ static bool with_body(const Task& t, F&& f) {
     case T_GEMV: {
       const GemvArgs& a = t.gemv;
       if (t.M == 1) {
-        const Geo g{(a.rows + kWaves - 1) / kWaves, 0};
+        const Geo g{(a.rows + kWaves * PerWave<WT>::v - 1) / (kWaves * PerWave<WT>::v), 0};
 #define CALL(N) f(GemvR<WT, N>{}, a, g)
         switch (nch_of<WT>(a.K)) { DAR_NCH_CASES(CALL) }
 #undef CALL
@@ -1397,7 +1438,8 @@ static bool with_body(const Task& t, F&& f) {
       const int pairs = (a.n_heads_q + 2 * a.n_heads_kv) * a.head_dim / 2;
       const int grid = (pairs + kWaves - 1) / kWaves;
       if (t.M == 1) {
-#define CALL(N) f(QkvR<WT, N>{}, a, Geo{grid, 0})
+        const int rgrid = (pairs + kWaves * PerWave<WT>::v - 1) / (kWaves * PerWave<WT>::v);
+#define CALL(N) f(QkvR<WT, N>{}, a, Geo{rgrid, 0})
         switch (nch_of<WT>(a.K)) { DAR_NCH_CASES(CALL) }
 #undef CALL
       }
@@ -1411,7 +1453,8 @@ static bool with_body(const Task& t, F&& f) {
       const SwigluArgs& a = t.swiglu;
       const int grid = (a.F + kWaves - 1) / kWaves;
       if (t.M == 1) {
-#define CALL(N) f(SwiR<WT, N>{}, a, Geo{grid, 0})
+        const int rgrid = (a.F + kWaves * PerWave<WT>::v - 1) / (kWaves * PerWave<WT>::v);
+#define CALL(N) f(SwiR<WT, N>{}, a, Geo{rgrid, 0})
         switch (nch_of<WT>(a.K)) { DAR_NCH_CASES(CALL) }
 #undef CALL
       }
