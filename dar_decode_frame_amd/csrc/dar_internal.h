@@ -12,6 +12,7 @@ constexpr int kBlock = 256;
 constexpr int kWaves = kBlock / kWave;
 constexpr int kMaxM = 2;           // input rows per GEMV launch (fast pass 1 runs two)
 constexpr int kAttnChunkDefault = 64;
+constexpr int kPrefillRows = 128;  // prompt positions per prefill block (GEMM rows)
 
 enum WType : int { W_BF16 = 0, W_FP8 = 1 };
 
@@ -119,6 +120,22 @@ struct AttnArgs {
   int out_stride;
 };
 
+// y[m][n] (+)= scale[n] * sum_k x[m][k] W[n][k] for m < M, n < N (prefill
+// GEMM on MFMA). The input rows come as two bf16 arrays with x = hi + lo,
+// [gemm_mpad(M)][K] (rows M.. zero). K % 64 == 0, M <= kPrefillRows.
+struct GemmArgs {
+  const void* W;            // [N][K] bf16 or e4m3fn
+  const float* scale;       // [N] (fp8) or nullptr
+  int N, K, M;
+  const uint16_t* xh;
+  const uint16_t* xl;
+  float* y;
+  int y_stride;
+  int accumulate;
+  float* part;              // partial sums of the K splits, [splits][M][N]
+  int splits, cps;          // set by launch_gemm: K splits, 64-wide chunks per split
+};
+
 enum TaskKind : int {
   T_NONE = 0,
   T_QKV,        // QkvArgs
@@ -151,6 +168,26 @@ hipError_t launch_task(int wtype, const Task& t, hipStream_t s);
 // What launch_task needs set up on the host (kernel LDS limits) without
 // launching; call before capturing the launch into a graph.
 hipError_t prepare_task(int wtype, const Task& t);
+
+// ---- prefill (dar_prefill.hip)
+// rows of the GEMM input arrays for M rows
+int gemm_mpad(int M);
+// GEMM with K split across workgroups (deterministic second pass) so that the
+// launch covers the chip; part must hold part_cap floats.
+hipError_t launch_gemm(int wtype, GemmArgs a, size_t part_cap, hipStream_t s);
+// hi/lo bf16 rows of x (RMSNorm(x) * gain when gain is set), gemm_mpad(M) rows
+hipError_t launch_norm_split(const float* x, int x_stride, int M, int K, const uint16_t* gain, float eps,
+                             uint16_t* xh, uint16_t* xl, hipStream_t s);
+// x[m] = table[clamp(tok[m])] for m < M
+hipError_t launch_embed_rows(const uint16_t* table, int rows, int K, const int* tok, int M, float* x,
+                             int* anomalies, hipStream_t s);
+// RoPE at positions p0.. of M rows of QKV output; q out, k/v appended to the caches
+hipError_t launch_rope_rows(const float* qkv, int M, int p0, int n_heads_q, int n_heads_kv, int head_dim,
+                            const float2* rope, float* q_out, uint16_t* kc, uint16_t* vc, int cache_len,
+                            hipStream_t s);
+// SiLU(a) * b as hi/lo bf16 rows
+hipError_t launch_silu_split(const float* a, const float* b, int M, int F, uint16_t* hh, uint16_t* hl,
+                             hipStream_t s);
 
 // x = table[clamp(*tok)] as fp32, *pos_out = pos_value (prefill step input)
 hipError_t launch_embed(const uint16_t* table, int rows, int K, const int* tok, float* x,

@@ -1,0 +1,317 @@
+// gfx950 kernels of the prompt prefill: the slow AR's layers over a block of
+// up to kPrefillRows prompt positions at once, so every weight matrix is read
+// once per block instead of once per token.
+//
+// The projections become GEMMs y[m][n] = sum_k x[m][k] W[n][k] with m over the
+// block's positions, run on MFMA (v_mfma_f32_32x32x16_bf16). The weights are
+// bf16 or e4m3fn (widened exactly to bf16 in registers, the per-row scale
+// applied to the finished sum). The inputs are split into two bf16 parts
+// x = hi + lo (|x - hi - lo| <= 2^-16 |x|) and both parts are multiplied, so
+// the GEMM keeps the fp32 inputs of the decode path to within fp32 rounding
+// noise. Attention over the block (causal, the cache holding earlier blocks)
+// reuses the decode attention kernels with one query row per position.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "dar_internal.h"
+
+namespace dar {
+
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kKC = 64;        // k per chunk of the GEMM main loop
+constexpr int kPitch = kKC + 8;  // LDS row pitch of staged inputs (bf16), padded against bank conflicts
+constexpr int kTileN = 128;    // weight rows per workgroup (32 per wave)
+
+__device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float(((uint32_t)h) << 16); }
+
+// fp32 -> bf16, round to nearest even (finite inputs)
+__device__ __forceinline__ uint16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+struct BF16W {
+  static constexpr int kBytes = 2;
+  // eight consecutive weights of a row as the MFMA B operand
+  __device__ static __forceinline__ bf16x8 frag(const char* p) {
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
+  }
+};
+
+struct FP8W {
+  static constexpr int kBytes = 1;
+  // e4m3fn values are exact in bf16: widen through fp32 and keep the top half
+  __device__ static __forceinline__ uint32_t pack2(f32x2 v) {
+    return (__float_as_uint(v.x) >> 16) | (__float_as_uint(v.y) & 0xffff0000u);
+  }
+  __device__ static __forceinline__ bf16x8 frag(const char* p) {
+    const u32x2 w = *reinterpret_cast<const u32x2*>(p);
+    u32x4 r;
+    r.x = pack2(__builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, false));
+    r.y = pack2(__builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, true));
+    r.z = pack2(__builtin_amdgcn_cvt_pk_f32_fp8((int)w.y, false));
+    r.w = pack2(__builtin_amdgcn_cvt_pk_f32_fp8((int)w.y, true));
+    return __builtin_bit_cast(bf16x8, r);
+  }
+};
+
+// One workgroup: weight rows [128 bx, +128) (wave w: 32 rows) x input rows
+// [32 MT by, +32 MT) x the k chunks of split bz. Per 64-wide chunk the inputs
+// (hi and lo) are staged in LDS; each wave streams its weight fragments from
+// HBM straight into registers (lane l: row l % 32, 8 consecutive k at
+// 8 (l / 32) of each 16-wide step), issued before the staging barrier.
+template <typename WT, int MT>
+__global__ __launch_bounds__(kBlock) void k_gemm(GemmArgs a) {
+  __shared__ __align__(16) uint16_t xs[2][32 * MT][kPitch];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n0 = blockIdx.x * kTileN + wave * 32;
+  const int m0 = blockIdx.y * 32 * MT;
+  const int nchunks = a.K / kKC;
+  const int c_begin = blockIdx.z * a.cps;
+  const int c_end = min(nchunks, c_begin + a.cps);
+  const int kl = 8 * (lane >> 5);
+  const char* wrow =
+      reinterpret_cast<const char*>(a.W) + (size_t)min(n0 + (lane & 31), a.N - 1) * a.K * WT::kBytes;
+  f32x16 acc[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[mt][v] = 0.f;
+
+  for (int c = c_begin; c < c_end; ++c) {
+    const int k0 = c * kKC;
+    bf16x8 b[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) b[s] = WT::frag(wrow + (size_t)(k0 + 16 * s + kl) * WT::kBytes);
+    __syncthreads();  // the previous chunk's LDS reads are done
+    constexpr int kPieces = 2 * 32 * MT * (kKC / 8);  // 16-byte pieces of hi and lo
+#pragma unroll
+    for (int p = tid; p < kPieces; p += kBlock) {
+      const int part = p / (32 * MT * (kKC / 8));
+      const int rem = p % (32 * MT * (kKC / 8));
+      const int r = rem / (kKC / 8), q = rem % (kKC / 8);
+      const uint16_t* src = (part ? a.xl : a.xh) + (size_t)(m0 + r) * a.K + k0 + q * 8;
+      *reinterpret_cast<u32x4*>(&xs[part][r][q * 8]) = *reinterpret_cast<const u32x4*>(src);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const int r = mt * 32 + (lane & 31);
+        const bf16x8 ah = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&xs[0][r][16 * s + kl]));
+        const bf16x8 al = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&xs[1][r][16 * s + kl]));
+        acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, b[s], acc[mt], 0, 0, 0);
+        acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, b[s], acc[mt], 0, 0, 0);
+      }
+    }
+  }
+  // accumulator v of lane l holds row (v % 4) + 4 (l / 32) + 8 (v / 4), column l % 32
+  const int n = n0 + (lane & 31);
+  if (n >= a.N) return;
+  const float sc = (a.scale && a.splits == 1) ? a.scale[n] : 1.f;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int m = m0 + mt * 32 + (v % 4) + 4 * (lane >> 5) + 8 * (v / 4);
+      if (m >= a.M) continue;
+      if (a.splits == 1) {
+        float* y = a.y + (size_t)m * a.y_stride + n;
+        const float val = acc[mt][v] * sc;
+        *y = a.accumulate ? *y + val : val;
+      } else {
+        a.part[((size_t)blockIdx.z * a.M + m) * a.N + n] = acc[mt][v];
+      }
+    }
+  }
+}
+
+// y[m][n] (+)= scale[n] * sum over splits (fixed order) of the partial sums
+__global__ void k_gemm_reduce(GemmArgs a) {
+  const size_t total = (size_t)a.M * a.N;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (size_t)gridDim.x * blockDim.x) {
+    const int m = (int)(i / a.N), n = (int)(i % a.N);
+    float s = 0.f;
+    for (int z = 0; z < a.splits; ++z) s += a.part[(size_t)z * total + i];
+    if (a.scale) s *= a.scale[n];
+    float* y = a.y + (size_t)m * a.y_stride + n;
+    *y = a.accumulate ? *y + s : s;
+  }
+}
+
+// Block reduction of one value per thread; result in every thread.
+__device__ __forceinline__ float block_sum(float v, float* red) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float t = 0.f;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) t += red[w];
+  __syncthreads();
+  return t;
+}
+
+// Row m of the GEMM input: v = x[m] (RMSNorm(x[m]) * gain when gain is set),
+// written as hi = bf16(v), lo = bf16(v - hi); rows M..Mpad-1 are zero.
+__global__ __launch_bounds__(kBlock) void k_norm_split(const float* x, int x_stride, int M, int K,
+                                                        const uint16_t* gain, float eps, uint16_t* xh, uint16_t* xl) {
+  __shared__ float red[kWaves];
+  const int m = blockIdx.x, tid = threadIdx.x;
+  uint16_t* oh = xh + (size_t)m * K;
+  uint16_t* ol = xl + (size_t)m * K;
+  if (m >= M) {
+    for (int k = tid; k < K; k += kBlock) oh[k] = ol[k] = 0;
+    return;
+  }
+  const float* xr = x + (size_t)m * x_stride;
+  float inv = 1.f;
+  if (gain) {
+    float ss = 0.f;
+    for (int k = tid; k < K; k += kBlock) ss += xr[k] * xr[k];
+    ss = block_sum(ss, red);
+    inv = 1.0f / sqrtf(ss / (float)K + eps);
+  }
+  for (int k = tid; k < K; k += kBlock) {
+    const float v = gain ? (xr[k] * inv) * bf2f(gain[k]) : xr[k];
+    const uint16_t h = f2bf(v);
+    oh[k] = h;
+    ol[k] = f2bf(v - bf2f(h));
+  }
+}
+
+// x[m] = table[clamp(tok[m])] as fp32 for the block's prompt ids
+__global__ __launch_bounds__(kBlock) void k_embed_rows(const uint16_t* table, int rows, int K, const int* tok,
+                                                        float* x, int* anomalies) {
+  const int m = blockIdx.x;
+  const int t = tok[m];
+  const int c = min(max(t, 0), rows - 1);
+  if (threadIdx.x == 0 && t != c) atomicAdd(anomalies, 1);
+  const uint16_t* row = table + (size_t)c * K;
+  for (int k = threadIdx.x; k < K; k += kBlock) x[(size_t)m * K + k] = bf2f(row[k]);
+}
+
+// RoPE at positions p0 + m on q and k of the block's QKV output, q to q_out,
+// k and v appended to the bf16 caches (rotate-half pairs (i, i + hd/2)).
+__global__ __launch_bounds__(kBlock) void k_rope_rows(const float* qkv, int M, int p0, int n_heads_q, int n_heads_kv,
+                                                       int head_dim, const float2* rope, float* q_out,
+                                                       uint16_t* kc, uint16_t* vc, int cache_len) {
+  const int m = blockIdx.x;
+  const int half = head_dim / 2;
+  const int n_heads = n_heads_q + 2 * n_heads_kv;
+  const int pos = p0 + m;
+  const float* row = qkv + (size_t)m * n_heads * head_dim;
+  for (int j = threadIdx.x; j < n_heads * half; j += kBlock) {
+    const int head = j / half, i = j % half;
+    const int r1 = head * head_dim + i, r2 = r1 + half;
+    const float u = row[r1], v = row[r2];
+    if (head < n_heads_q + n_heads_kv) {
+      const float2 cs = rope[(size_t)pos * half + i];
+      const float o1 = u * cs.x - v * cs.y;
+      const float o2 = u * cs.y + v * cs.x;
+      if (head < n_heads_q) {
+        q_out[(size_t)m * n_heads_q * head_dim + r1] = o1;
+        q_out[(size_t)m * n_heads_q * head_dim + r2] = o2;
+      } else {
+        uint16_t* kp = kc + ((size_t)(head - n_heads_q) * cache_len + pos) * head_dim;
+        kp[i] = f2bf(o1);
+        kp[i + half] = f2bf(o2);
+      }
+    } else {
+      uint16_t* vp = vc + ((size_t)(head - n_heads_q - n_heads_kv) * cache_len + pos) * head_dim;
+      vp[i] = f2bf(u);
+      vp[i + half] = f2bf(v);
+    }
+  }
+}
+
+// h = SiLU(a) * b per element, split into bf16 hi/lo rows (rows M..Mpad-1 zero)
+__global__ __launch_bounds__(kBlock) void k_silu_split(const float* a, const float* b, int M, int F, uint16_t* hh,
+                                                        uint16_t* hl) {
+  const int m = blockIdx.x;
+  for (int k = threadIdx.x; k < F; k += kBlock) {
+    uint16_t h = 0, l = 0;
+    if (m < M) {
+      const float g = a[(size_t)m * F + k];
+      const float v = g / (1.0f + expf(-g)) * b[(size_t)m * F + k];
+      h = f2bf(v);
+      l = f2bf(v - bf2f(h));
+    }
+    hh[(size_t)m * F + k] = h;
+    hl[(size_t)m * F + k] = l;
+  }
+}
+
+template <typename WT>
+hipError_t gemm_dispatch(const GemmArgs& a, int mt, dim3 grid, hipStream_t s) {
+  switch (mt) {
+    case 1: hipLaunchKernelGGL((k_gemm<WT, 1>), grid, dim3(kBlock), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((k_gemm<WT, 2>), grid, dim3(kBlock), 0, s, a); break;
+    default: hipLaunchKernelGGL((k_gemm<WT, 4>), grid, dim3(kBlock), 0, s, a); break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int gemm_mpad(int M) { return M <= 32 ? 32 : (M <= 64 ? 64 : ((M + 127) / 128) * 128); }
+
+hipError_t launch_gemm(int wtype, GemmArgs a, size_t part_cap, hipStream_t s) {
+  if (a.M < 1 || a.M > kPrefillRows || a.K % kKC || a.N < 1) return hipErrorInvalidValue;
+  const int mt = a.M <= 32 ? 1 : (a.M <= 64 ? 2 : 4);
+  const int gx = (a.N + kTileN - 1) / kTileN, gy = (a.M + 32 * mt - 1) / (32 * mt);
+  const int nchunks = a.K / kKC;
+  // split K until the launch covers every CU once, within the partial-sum buffer
+  int splits = (256 + gx * gy - 1) / (gx * gy);
+  splits = splits < 1 ? 1 : (splits > 16 ? 16 : splits);
+  if (splits > nchunks) splits = nchunks;
+  while (splits > 1 && (size_t)splits * a.M * a.N > part_cap) --splits;
+  a.cps = (nchunks + splits - 1) / splits;
+  a.splits = (nchunks + a.cps - 1) / a.cps;
+  const dim3 grid(gx, gy, a.splits);
+  hipError_t e = wtype == W_FP8 ? gemm_dispatch<FP8W>(a, mt, grid, s) : gemm_dispatch<BF16W>(a, mt, grid, s);
+  if (e != hipSuccess || a.splits == 1) return e;
+  const size_t total = (size_t)a.M * a.N;
+  size_t blocks = (total + kBlock - 1) / kBlock;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(k_gemm_reduce, dim3((unsigned)blocks), dim3(kBlock), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_norm_split(const float* x, int x_stride, int M, int K, const uint16_t* gain, float eps,
+                             uint16_t* xh, uint16_t* xl, hipStream_t s) {
+  hipLaunchKernelGGL(k_norm_split, dim3(gemm_mpad(M)), dim3(kBlock), 0, s, x, x_stride, M, K, gain, eps, xh, xl);
+  return hipGetLastError();
+}
+
+hipError_t launch_embed_rows(const uint16_t* table, int rows, int K, const int* tok, int M, float* x,
+                             int* anomalies, hipStream_t s) {
+  hipLaunchKernelGGL(k_embed_rows, dim3(M), dim3(kBlock), 0, s, table, rows, K, tok, x, anomalies);
+  return hipGetLastError();
+}
+
+hipError_t launch_rope_rows(const float* qkv, int M, int p0, int n_heads_q, int n_heads_kv, int head_dim,
+                            const float2* rope, float* q_out, uint16_t* kc, uint16_t* vc, int cache_len,
+                            hipStream_t s) {
+  hipLaunchKernelGGL(k_rope_rows, dim3(M), dim3(kBlock), 0, s, qkv, M, p0, n_heads_q, n_heads_kv, head_dim, rope,
+                     q_out, kc, vc, cache_len);
+  return hipGetLastError();
+}
+
+hipError_t launch_silu_split(const float* a, const float* b, int M, int F, uint16_t* hh, uint16_t* hl,
+                             hipStream_t s) {
+  hipLaunchKernelGGL(k_silu_split, dim3(gemm_mpad(M)), dim3(kBlock), 0, s, a, b, M, F, hh, hl);
+  return hipGetLastError();
+}
+
+}  // namespace dar

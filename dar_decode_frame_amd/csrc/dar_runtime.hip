@@ -57,7 +57,11 @@ int nsplit_slow_of(const dar_config* c) { return (c->max_len + kAttnChunkDefault
 struct Layout {
   size_t x[2], q[2], o[2], h[2], part[2];  // chain scratch: [0] slow (one row), [1] fast (two rows)
   size_t ht, logits0, flogits, slots0, slotsf, pred, committed, forced, flags, pos, seqpos, ring, rope;
-  size_t ks, vs, kf, vf, total;
+  size_t ks, vs, kf, vf;
+  // prefill block scratch (kPrefillRows rows): residual, GEMM input halves,
+  // QKV output, q, attention output, W1/W3 outputs, GEMM and attention partials
+  size_t px, pxh, pxl, pqkv, pq, po, ph1, ph3, pgp, patt, ppos, total;
+  size_t pgp_floats;
   int nsplit_slow, chunk, rope_len, seq_len, vmax, fast_len, nslots;
 };
 
@@ -107,6 +111,27 @@ Layout make_layout(const dar_config* c) {
   const size_t kv_fast = has_fast(c) ? (size_t)c->n_layers_fast * c->n_heads_kv * L.fast_len * c->head_dim * 2 : 0;
   L.kf = take(kv_fast);
   L.vf = take(kv_fast);
+  const size_t R = kPrefillRows;
+  const int qkv_rows = (c->n_heads_q + 2 * c->n_heads_kv) * c->head_dim;
+  const int kmax = std::max(std::max(d, qw), F);
+  L.px = take(sizeof(float) * R * d);
+  L.pxh = take(2 * R * kmax);
+  L.pxl = take(2 * R * kmax);
+  L.pqkv = take(sizeof(float) * R * qkv_rows);
+  L.pq = take(sizeof(float) * R * qw);
+  L.po = take(sizeof(float) * R * qw);
+  L.ph1 = take(sizeof(float) * R * F);
+  L.ph3 = take(sizeof(float) * R * F);
+  // partial sums of the widest K split launch_gemm picks for the block's GEMMs
+  L.pgp_floats = 0;
+  for (int N : {d, qkv_rows, F}) {
+    const int gx = (N + 127) / 128;
+    const int splits = std::min(16, (256 + gx - 1) / gx);
+    L.pgp_floats = std::max(L.pgp_floats, (size_t)splits * R * N);
+  }
+  L.pgp = take(sizeof(float) * L.pgp_floats);
+  L.patt = take(sizeof(float) * attn_partial_floats((int)R, c->n_heads_kv, L.nsplit_slow, g, c->head_dim));
+  L.ppos = take(sizeof(int) * 4);
   L.total = off;
   return L;
 }
@@ -213,7 +238,7 @@ struct dar_ctx {
 
   hipStream_t stream = nullptr;  // the caller's stream
   Chain cs, cf;                  // slow chain (frame i+1) and fast chain (frame i)
-  Plan p_c0, p_fast, p_slow, p_prefill;  // commit of c0, fast AR, slow step + c0 head, slow step alone
+  Plan p_c0, p_fast, p_slow;  // commit of c0, fast AR, slow step + c0 head
   hipEvent_t ev_start = nullptr, ev_c0 = nullptr, ev_f_done = nullptr, ev_s_done = nullptr;
   bool use_graph = false;
 
@@ -597,6 +622,101 @@ int pipeline_step(dar_ctx* c, const int32_t* forced, int32_t* codes_out, float* 
   return DAR_OK;
 }
 
+// The slow AR over the prompt in blocks of up to kPrefillRows positions:
+// every projection is one GEMM over the block's rows (each weight matrix read
+// once per block), attention is causal over the cache (earlier blocks) and the
+// block itself. Then the codebook-0 head on the last position, which leaves
+// pos_s = n; frame 0 sits at position n - 1.
+int prefill_blocks(dar_ctx* c, const int32_t* tokens, int n, hipStream_t s) {
+  const dar_config& g = c->cfg;
+  const Layout& L = c->L;
+  const int d = g.d_model, qw = g.n_heads_q * g.head_dim, F = g.ffn_dim;
+  const int qkv_rows = (g.n_heads_q + 2 * g.n_heads_kv) * g.head_dim;
+  const int wt = c->fp8 ? W_FP8 : W_BF16;
+  char* b = c->ws;
+  float* px = reinterpret_cast<float*>(b + L.px);
+  uint16_t* xh = reinterpret_cast<uint16_t*>(b + L.pxh);
+  uint16_t* xl = reinterpret_cast<uint16_t*>(b + L.pxl);
+  float* pqkv = reinterpret_cast<float*>(b + L.pqkv);
+  float* pq = reinterpret_cast<float*>(b + L.pq);
+  float* po = reinterpret_cast<float*>(b + L.po);
+  float* ph1 = reinterpret_cast<float*>(b + L.ph1);
+  float* ph3 = reinterpret_cast<float*>(b + L.ph3);
+  float* pgp = reinterpret_cast<float*>(b + L.pgp);
+  int* ppos = reinterpret_cast<int*>(b + L.ppos);
+  const size_t per_layer = (size_t)g.n_heads_kv * g.max_len * g.head_dim;
+  auto gemm = [&](const void* W, const float* scale, int N, int K, int M, float* y, int acc) {
+    GemmArgs a{};
+    a.W = W;
+    a.scale = c->fp8 ? scale : nullptr;
+    a.N = N;
+    a.K = K;
+    a.M = M;
+    a.xh = xh;
+    a.xl = xl;
+    a.y = y;
+    a.y_stride = N;
+    a.accumulate = acc;
+    a.part = pgp;
+    return launch_gemm(wt, a, L.pgp_floats, s);
+  };
+  int M = 0;
+  for (int p0 = 0; p0 < n; p0 += kPrefillRows) {
+    M = std::min(kPrefillRows, n - p0);
+    DAR_HIP(c, launch_embed_rows(c->w0, g.vocab_c0, d, tokens + p0, M, px, c->flags + 1, s), "prefill embed");
+    DAR_HIP(c, launch_fill_i32(ppos, 1, p0, s), "prefill position");
+    for (int l = 0; l < g.n_layers_slow; ++l) {
+      const dar_layer_weights& w = c->slow[l];
+      uint16_t* kc = c->ks + l * per_layer;
+      uint16_t* vc = c->vs + l * per_layer;
+      DAR_HIP(c, launch_norm_split(px, d, M, d, static_cast<const uint16_t*>(w.attn_norm), g.rms_eps, xh, xl, s),
+              "prefill attn norm");
+      DAR_HIP(c, gemm(w.wqkv, w.wqkv_scale, qkv_rows, d, M, pqkv, 0), "prefill qkv");
+      DAR_HIP(c, launch_rope_rows(pqkv, M, p0, g.n_heads_q, g.n_heads_kv, g.head_dim, c->rope, pq, kc, vc, g.max_len, s),
+              "prefill rope");
+      Task t{};
+      t.kind = T_ATTN;
+      t.M = M;
+      AttnArgs& aa = t.attn;
+      aa.q = pq;
+      aa.q_stride = qw;
+      aa.K = kc;
+      aa.V = vc;
+      aa.cache_len = g.max_len;
+      aa.pos = ppos;
+      aa.n_heads_q = g.n_heads_q;
+      aa.n_heads_kv = g.n_heads_kv;
+      aa.head_dim = g.head_dim;
+      aa.chunk = L.chunk;
+      aa.nsplit_max = L.nsplit_slow;
+      aa.M = M;
+      aa.part = reinterpret_cast<float*>(b + L.patt);
+      aa.out = po;
+      aa.out_stride = qw;
+      DAR_HIP(c, launch_task(wt, t, s), "prefill attention");
+      if (L.nsplit_slow > 1) {
+        t.kind = T_COMBINE;
+        DAR_HIP(c, launch_task(wt, t, s), "prefill attention combine");
+      }
+      DAR_HIP(c, launch_norm_split(po, qw, M, qw, nullptr, 0.f, xh, xl, s), "prefill split o");
+      DAR_HIP(c, gemm(w.wo, w.wo_scale, d, qw, M, px, 1), "prefill wo");
+      DAR_HIP(c, launch_norm_split(px, d, M, d, static_cast<const uint16_t*>(w.ffn_norm), g.rms_eps, xh, xl, s),
+              "prefill ffn norm");
+      DAR_HIP(c, gemm(w.w1, w.w1_scale, F, d, M, ph1, 0), "prefill w1");
+      DAR_HIP(c, gemm(w.w3, w.w3_scale, F, d, M, ph3, 0), "prefill w3");
+      DAR_HIP(c, launch_silu_split(ph1, ph3, M, F, xh, xl, s), "prefill silu");
+      DAR_HIP(c, gemm(w.w2, w.w2_scale, d, F, M, px, 1), "prefill w2");
+    }
+  }
+  // codebook-0 head on position n - 1 (moves pos_s to n)
+  DAR_HIP(c, launch_fill_i32(c->pos_s, 1, n - 1, s), "prefill head position");
+  Task t = c->p_slow.tasks.back();
+  t.head.x = px + (size_t)(M - 1) * d;
+  DAR_HIP(c, launch_task(wt, t, s), "prefill head");
+  DAR_HIP(c, launch_fill_i32(c->pos_f, 1, n - 1, s), "set frame position");
+  return DAR_OK;
+}
+
 void free_plan(Plan& p) {
   if (p.exec) (void)hipGraphExecDestroy(p.exec);
   if (p.graph) (void)hipGraphDestroy(p.graph);
@@ -728,7 +848,6 @@ int dar_create(const dar_config* cfg, const dar_weights* w, void* workspace, siz
   plan_single(c->p_c0, commit0_chain(c));
   plan_single(c->p_fast, fast_chain(c));
   plan_single(c->p_slow, slow_chain(c, true));
-  plan_single(c->p_prefill, slow_chain(c, false));
 
   auto fail = [&](hipError_t e, const char* what) {
     g_create_error = std::string(what) + ": " + hipGetErrorString(e);
@@ -794,21 +913,13 @@ int dar_prefill(dar_ctx* c, int32_t batch, const int32_t* tokens, const int32_t*
     return n < 1 ? DAR_E_INVAL : DAR_E_CAPACITY;
   }
   c->prefilled = false;
-  const int d = c->cfg.d_model;
   hipStream_t s = c->cs.s;
-  // the slow stream runs the prompt token by token after anything already
-  // queued; the last step adds the codebook-0 head, which moves pos_s to n
+  // the slow stream runs the prompt after anything already queued
   DAR_HIP(c, hipEventRecord(c->ev_start, c->stream), "record start");
   DAR_HIP(c, hipStreamWaitEvent(s, c->ev_start, 0), "wait start");
   DAR_HIP(c, hipStreamWaitEvent(s, c->ev_f_done, 0), "wait fast chain");
-  for (int p = 0; p < n; ++p) {
-    DAR_HIP(c, launch_embed(c->w0, c->cfg.vocab_c0, d, tokens + p, c->cs.x, c->pos_s, p, c->flags + 1, s),
-            "prefill embed");
-    const int st = run_plan(c, p == n - 1 ? c->p_slow : c->p_prefill, s, "prefill layers");
-    if (st != DAR_OK) return st;
-  }
-  // frame 0 sits at position n-1
-  DAR_HIP(c, launch_fill_i32(c->pos_f, 1, n - 1, s), "set frame position");
+  const int st0 = prefill_blocks(c, tokens, n, s);
+  if (st0 != DAR_OK) return st0;
   DAR_HIP(c, hipEventRecord(c->ev_s_done, s), "record slow done");
   const int st = pipeline_step(c, forced, codes_out, logits_out, n < c->cfg.max_len);
   if (st != DAR_OK) return st;
@@ -838,7 +949,7 @@ int dar_destroy(dar_ctx* c) {
   (void)hipStreamSynchronize(c->stream);
   for (Chain* ch : {&c->cs, &c->cf})
     if (ch->s) (void)hipStreamSynchronize(ch->s);
-  for (Plan* p : {&c->p_c0, &c->p_fast, &c->p_slow, &c->p_prefill}) free_plan(*p);
+  for (Plan* p : {&c->p_c0, &c->p_fast, &c->p_slow}) free_plan(*p);
   for (hipEvent_t ev : c->events) (void)hipEventDestroy(ev);
   for (hipEvent_t ev : {c->ev_start, c->ev_c0, c->ev_f_done, c->ev_s_done})
     if (ev) (void)hipEventDestroy(ev);
@@ -971,6 +1082,42 @@ int dar_op_gemv(int32_t wtype, const void* W, const float* scale, int32_t rows, 
   a.accumulate = 0;
   return run_single_task(t, wtype == DAR_WTYPE_FP8_E4M3_ROW ? W_FP8 : W_BF16, static_cast<hipStream_t>(stream),
                          "gemv");
+}
+
+int dar_op_gemm(int32_t wtype, const void* W, const float* scale, int32_t N, int32_t K, const float* x,
+                int32_t M, float* y, void* stream) {
+  if (!W || !x || !y || N < 1 || K < 256 || K % 256 || K > 16384 || M < 1 || M > kPrefillRows) return DAR_E_INVAL;
+  if (wtype != DAR_WTYPE_BF16 && wtype != DAR_WTYPE_FP8_E4M3_ROW) return DAR_E_INVAL;
+  if (wtype == DAR_WTYPE_FP8_E4M3_ROW && !scale) return DAR_E_INVAL;
+  if (!aligned16(W) || !aligned16(x)) return DAR_E_INVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int mpad = gemm_mpad(M);
+  const size_t half_bytes = align_up((size_t)mpad * K * sizeof(uint16_t));
+  const size_t part_cap = (size_t)16 * M * N;
+  char* scratch = nullptr;
+  hipError_t e = hipMalloc(&scratch, 2 * half_bytes + part_cap * sizeof(float));
+  if (e != hipSuccess) return hip_fail(nullptr, e, "gemm scratch");
+  uint16_t* xh = reinterpret_cast<uint16_t*>(scratch);
+  uint16_t* xl = reinterpret_cast<uint16_t*>(scratch + half_bytes);
+  GemmArgs a{};
+  a.W = W;
+  a.scale = wtype == DAR_WTYPE_FP8_E4M3_ROW ? scale : nullptr;
+  a.N = N;
+  a.K = K;
+  a.M = M;
+  a.xh = xh;
+  a.xl = xl;
+  a.y = y;
+  a.y_stride = N;
+  a.accumulate = 0;
+  a.part = reinterpret_cast<float*>(scratch + 2 * half_bytes);
+  if ((e = launch_norm_split(x, K, M, K, nullptr, 0.f, xh, xl, s)) == hipSuccess &&
+      (e = launch_gemm(wtype == DAR_WTYPE_FP8_E4M3_ROW ? W_FP8 : W_BF16, a, part_cap, s)) == hipSuccess)
+    e = hipStreamSynchronize(s);
+  (void)hipStreamSynchronize(s);
+  (void)hipFree(scratch);
+  if (e != hipSuccess) return hip_fail(nullptr, e, "gemm");
+  return DAR_OK;
 }
 
 int dar_op_attention(const float* q, const void* K, const void* V, int32_t n_heads_q, int32_t n_heads_kv,

@@ -101,6 +101,7 @@ _SIGS = {
     "dar_status_string": ([ctypes.c_int], ctypes.c_char_p),
     "dar_last_error": ([_VP], ctypes.c_char_p),
     "dar_op_gemv": ([_I32, _VP, _VP, _I32, _I32, _VP, _I32, _VP, _VP], ctypes.c_int),
+    "dar_op_gemm": ([_I32, _VP, _VP, _I32, _I32, _VP, _I32, _VP, _VP], ctypes.c_int),
     "dar_op_attention": ([_VP, _VP, _VP, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _VP, _VP], ctypes.c_int),
     "dar_op_fp8_decode": ([_VP, _I32, _VP, _VP], ctypes.c_int),
     "dar_profile_frame": ([_VP, _I32, _VP, _VP, _VP, ctypes.POINTER(_I32)], ctypes.c_int),
@@ -237,6 +238,10 @@ def dar_op_attention(q_ptr, k_ptr, v_ptr, n_heads_q, n_heads_kv, head_dim, max_l
                      stream_ptr):
     return _check(lib.dar_op_attention(q_ptr, k_ptr, v_ptr, n_heads_q, n_heads_kv, head_dim, max_len, pos, M, chunk,
                                        out_ptr, stream_ptr), "dar_op_attention")
+
+
+def dar_op_gemm(wtype, w_ptr, scale_ptr, N, K, x_ptr, M, y_ptr, stream_ptr):
+    return _check(lib.dar_op_gemm(wtype, w_ptr, scale_ptr, N, K, x_ptr, M, y_ptr, stream_ptr), "dar_op_gemm")
 
 
 def dar_op_fp8_decode(codes_ptr, n, out_ptr, stream_ptr):

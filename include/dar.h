@@ -212,6 +212,15 @@ const char* dar_last_error(const dar_ctx* ctx);   /* ctx may be NULL: last creat
 int dar_op_gemv(int32_t wtype, const void* W, const float* scale, int32_t rows, int32_t cols,
                 const float* x, int32_t M, float* y, void* stream);
 
+/* y[m][n] = sum_k x[m][k] * W[n][k] (times scale[n] in fp8 mode) for m < M,
+ * n < N: the prefill's MFMA GEMM, which splits the fp32 inputs into two bf16
+ * parts (hi + lo) and multiplies both. W device [N][K] bf16 or e4m3fn (wtype),
+ * scale fp32 [N] or NULL for bf16, x device fp32 [M][K], y device fp32 [M][N].
+ * 1 <= M <= 128; K % 256 == 0 and K <= 16384; N >= 1. Uses its own scratch
+ * (allocated per call) and synchronises the stream. */
+int dar_op_gemm(int32_t wtype, const void* W, const float* scale, int32_t N, int32_t K, const float* x,
+                int32_t M, float* y, void* stream);
+
 /* Decode attention of one layer (the frame's split-K kernel): for query row m
  * at position pos+m, head h, out[m][h] = softmax(q[m][h] . K[kv][0..pos+m] /
  * sqrt(head_dim)) V[kv][0..pos+m] with kv = h / (n_heads_q/n_heads_kv).

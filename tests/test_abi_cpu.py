@@ -30,7 +30,9 @@ def test_workspace_bytes_cover_kv(N, dname, max_len):
     d = DIMS[dname]
     n = N.dar_workspace_bytes(N.make_config(d, max_len))
     kv = 2 * d.n_layers_slow * d.n_heads_kv * max_len * d.head_dim * 2
-    assert n >= kv and n < kv + 64 * 2 ** 20
+    # beyond the slow KV cache: decode activations and the prefill block's
+    # scratch (128 rows of every activation, GEMM and attention partial sums)
+    assert n >= kv and n < kv + 160 * 2 ** 20
 
 
 @pytest.mark.parametrize("dname,wtype", [("tiny", "bf16"), ("tiny", "fp8"), ("s2pro_slow", "bf16"),

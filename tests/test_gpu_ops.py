@@ -102,6 +102,41 @@ def test_gemv_against_fp64(env, wtype, M, rows, cols):
     assert np.all(np.abs(got - want) <= bound), float(np.max(np.abs(got - want) / bound))
 
 
+# prefill GEMM: full blocks, ragged rows (M not a multiple of 32), narrow and
+# wide outputs (K split across workgroups), the frame's shapes
+GEMM_SHAPES = [(6144, 2560, 128), (2560, 4096, 128), (9728, 2560, 100), (2560, 9728, 7), (300, 768, 33),
+               (17, 256, 1), (129, 512, 64)]
+
+
+@pytest.mark.parametrize("wtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("n_out,k_in,M", GEMM_SHAPES)
+def test_gemm_against_fp64(env, wtype, n_out, k_in, M):
+    torch, N, dev = env
+    bits = _bf16_matrix(n_out, k_in, n_out * 5 + k_in)
+    w32 = bf16_to_f32(bits)
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal((M, k_in)).astype(np.float32)
+    xt = torch.from_numpy(x).to(dev)
+    y = torch.full((M, n_out), float("nan"), dtype=torch.float32, device=dev)
+    if wtype == "bf16":
+        w_dev = torch.from_numpy(bits.view(np.int16)).to(dev)
+        N.dar_op_gemm(0, _p(w_dev), None, n_out, k_in, _p(xt), M, _p(y), _sp(torch))
+        w_ref = w32.astype(np.float64)
+        sc = np.ones(n_out)
+    else:
+        codes, scale = quantize_rows(w32)
+        w_dev = torch.from_numpy(codes).to(dev)
+        s_dev = torch.from_numpy(scale).to(dev)
+        N.dar_op_gemm(1, _p(w_dev), _p(s_dev), n_out, k_in, _p(xt), M, _p(y), _sp(torch))
+        w_ref = e4m3_decode(codes).astype(np.float64)
+        sc = scale.astype(np.float64)
+    got = y.cpu().numpy().astype(np.float64)
+    want = (x.astype(np.float64) @ w_ref.T) * sc
+    # inputs carried as bf16 hi + lo (relative error <= 2^-16), fp32 accumulation
+    bound = 1e-5 * (np.abs(x.astype(np.float64)) @ np.abs(w_ref).T) * sc + 1e-30
+    assert np.all(np.abs(got - want) <= bound), float(np.max(np.abs(got - want) / bound))
+
+
 @pytest.mark.parametrize("n_q,n_kv,hd", [(4, 2, 64), (32, 8, 128), (8, 8, 128), (16, 2, 64)])
 @pytest.mark.parametrize("pos", [0, 6, 63, 64, 200, 1022])
 @pytest.mark.parametrize("M", [1, 2])
