@@ -65,13 +65,18 @@ struct FP8W {
 };
 
 // One workgroup: weight rows [128 bx, +128) (wave w: 32 rows) x input rows
-// [32 MT by, +32 MT) x the k chunks of split bz. Per 64-wide chunk the inputs
-// (hi and lo) are staged in LDS; each wave streams its weight fragments from
-// HBM straight into registers (lane l: row l % 32, 8 consecutive k at
-// 8 (l / 32) of each 16-wide step), issued before the staging barrier.
+// [32 MT by, +32 MT) x the k chunks of split bz. Each wave streams its weight
+// fragments from HBM straight into registers (lane l: row l % 32, 8
+// consecutive k at 8 (l / 32) of each 16-wide step), two chunks ahead of the
+// MFMAs; the input chunk (hi and lo) is loaded one chunk ahead and staged in
+// one of two LDS buffers, so a chunk costs one barrier.
 template <typename WT, int MT>
 __global__ __launch_bounds__(kBlock) void k_gemm(GemmArgs a) {
-  __shared__ __align__(16) uint16_t xs[2][32 * MT][kPitch];
+  constexpr int kRowPieces = kKC / 8;                  // 16-byte pieces per staged row
+  constexpr int kPieces = 2 * 32 * MT * kRowPieces;    // hi and lo
+  constexpr int kPer = kPieces / kBlock;               // pieces per thread
+  static_assert(kPieces % kBlock == 0, "staging split");
+  __shared__ __align__(16) uint16_t xs[2][2][32 * MT][kPitch];  // [buffer][hi/lo][row][k]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n0 = blockIdx.x * kTileN + wave * 32;
   const int m0 = blockIdx.y * 32 * MT;
@@ -81,39 +86,64 @@ __global__ __launch_bounds__(kBlock) void k_gemm(GemmArgs a) {
   const int kl = 8 * (lane >> 5);
   const char* wrow =
       reinterpret_cast<const char*>(a.W) + (size_t)min(n0 + (lane & 31), a.N - 1) * a.K * WT::kBytes;
+  auto load_w = [&](bf16x8 (&b)[4], int c) {
+    const int cc = min(c, c_end - 1);  // past the end: a valid chunk, never used
+#pragma unroll
+    for (int s = 0; s < 4; ++s) b[s] = WT::frag(wrow + (size_t)(cc * kKC + 16 * s + kl) * WT::kBytes);
+  };
+  auto load_x = [&](u32x4 (&r)[kPer], int c) {
+    const int k0 = min(c, c_end - 1) * kKC;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int p = tid + j * kBlock;
+      const int part = p / (32 * MT * kRowPieces);
+      const int rem = p % (32 * MT * kRowPieces);
+      const int row = rem / kRowPieces, q = rem % kRowPieces;
+      r[j] = *reinterpret_cast<const u32x4*>((part ? a.xl : a.xh) + (size_t)(m0 + row) * a.K + k0 + q * 8);
+    }
+  };
+  auto store_x = [&](const u32x4 (&r)[kPer], int buf) {
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int p = tid + j * kBlock;
+      const int part = p / (32 * MT * kRowPieces);
+      const int rem = p % (32 * MT * kRowPieces);
+      const int row = rem / kRowPieces, q = rem % kRowPieces;
+      *reinterpret_cast<u32x4*>(&xs[buf][part][row][q * 8]) = r[j];
+    }
+  };
   f32x16 acc[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc[mt][v] = 0.f;
 
-  for (int c = c_begin; c < c_end; ++c) {
-    const int k0 = c * kKC;
-    bf16x8 b[4];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) b[s] = WT::frag(wrow + (size_t)(k0 + 16 * s + kl) * WT::kBytes);
-    __syncthreads();  // the previous chunk's LDS reads are done
-    constexpr int kPieces = 2 * 32 * MT * (kKC / 8);  // 16-byte pieces of hi and lo
-#pragma unroll
-    for (int p = tid; p < kPieces; p += kBlock) {
-      const int part = p / (32 * MT * (kKC / 8));
-      const int rem = p % (32 * MT * (kKC / 8));
-      const int r = rem / (kKC / 8), q = rem % (kKC / 8);
-      const uint16_t* src = (part ? a.xl : a.xh) + (size_t)(m0 + r) * a.K + k0 + q * 8;
-      *reinterpret_cast<u32x4*>(&xs[part][r][q * 8]) = *reinterpret_cast<const u32x4*>(src);
-    }
-    __syncthreads();
+  bf16x8 b0[4], b1[4];
+  u32x4 xr[kPer];
+  load_w(b0, c_begin);
+  load_w(b1, c_begin + 1);
+  load_x(xr, c_begin);
+  auto step = [&](bf16x8 (&b)[4], int c) {
+    const int buf = (c - c_begin) & 1;
+    store_x(xr, buf);
+    __syncthreads();  // chunk c staged; every thread is past chunk c - 2's reads of this buffer
+    load_x(xr, c + 1);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         const int r = mt * 32 + (lane & 31);
-        const bf16x8 ah = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&xs[0][r][16 * s + kl]));
-        const bf16x8 al = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&xs[1][r][16 * s + kl]));
+        const bf16x8 ah = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&xs[buf][0][r][16 * s + kl]));
+        const bf16x8 al = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&xs[buf][1][r][16 * s + kl]));
         acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, b[s], acc[mt], 0, 0, 0);
         acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, b[s], acc[mt], 0, 0, 0);
       }
     }
+    load_w(b, c + 2);  // this register set's next chunk
+  };
+  for (int c = c_begin; c < c_end; c += 2) {
+    step(b0, c);
+    if (c + 1 < c_end) step(b1, c + 1);
   }
   // accumulator v of lane l holds row (v % 4) + 4 (l / 32) + 8 (v / 4), column l % 32
   const int n = n0 + (lane & 31);

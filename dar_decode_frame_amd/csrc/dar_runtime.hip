@@ -688,13 +688,13 @@ int prefill_blocks(dar_ctx* c, const int32_t* tokens, int n, hipStream_t s) {
       aa.n_heads_kv = g.n_heads_kv;
       aa.head_dim = g.head_dim;
       aa.chunk = L.chunk;
-      aa.nsplit_max = L.nsplit_slow;
+      aa.nsplit_max = (p0 + M + L.chunk - 1) / L.chunk;  // splits of the block's longest row
       aa.M = M;
       aa.part = reinterpret_cast<float*>(b + L.patt);
       aa.out = po;
       aa.out_stride = qw;
       DAR_HIP(c, launch_task(wt, t, s), "prefill attention");
-      if (L.nsplit_slow > 1) {
+      if (aa.nsplit_max > 1) {
         t.kind = T_COMBINE;
         DAR_HIP(c, launch_task(wt, t, s), "prefill attention combine");
       }
