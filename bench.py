@@ -39,6 +39,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-frames", type=int, default=3)
     ap.add_argument("--graph", action="store_true", help="replay captured graphs instead of eager launches")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="first copy MIB MiB device to device once (a known-size reference for HBM byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -62,6 +64,16 @@ def main():
     if args.steps > max_steps or args.steps < 1:
         raise SystemExit(f"--steps must be in [1, {max_steps}] for {wl.name}")
     dev = torch.device("cuda:0")
+
+    if args.calibrate_copy > 0:
+        n = args.calibrate_copy * 2 ** 20 // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"calibration copy of {args.calibrate_copy} MiB done")
+        del src, dst
 
     t0 = time.time()
     host = synth.gen_weights(dims, wl.weight_seed)
@@ -110,32 +122,46 @@ def main():
     n_bad = sess.nonfinite()
     codes = sess.ring(wl.prefill_len - 1, args.steps + 1)
 
-    # dominant kernel: per-launch HIP-event timing of eager frames on the same stream
+    # dominant kernel: the kind with the largest share of serialised frames
+    # (both chains on one stream, every launch bracketed by HIP events on that
+    # stream: the kernels' own durations, as rocprofv3, which also serialises
+    # the streams, reports them). Its launches are then also timed live on
+    # their own streams over a second pass of the two-stream frames, where a
+    # launch shares HBM with the other chain's kernels.
     roof = None
-    kernel_table = {}
     if args.profile_frames > 0:
         sess.reset()
         sess.prefill(prompt, want=False)
         recs = []
         for _ in range(args.profile_frames):
             recs += sess.profile_frame()
+        totals = {}
         for ms_k, kind, layer in recs:
-            kernel_table.setdefault(N.KIND_NAMES[kind], []).append((ms_k, layer))
-        totals = {k: sum(m for m, _ in v) for k, v in kernel_table.items()}
+            totals[kind] = totals.get(kind, 0.0) + ms_k
         dom = max(totals, key=totals.get)
-        per = per_launch_bytes(dims, wl.wtype, dom)
-        # average over the single-row launches (fast pass 1 runs two rows)
-        one_row = [m for m, layer in kernel_table[dom] if not (1000 <= layer < 2000)]
+        share = {N.KIND_NAMES[k]: round(v / sum(totals.values()), 4)
+                 for k, v in sorted(totals.items(), key=lambda kv: -kv[1])}
+        # one-row launches only (the fast AR's first pass runs two rows)
+        one_row = [ms_k for ms_k, kind, layer in recs if kind == dom and not (1000 <= layer < 2000)]
         avg_ms = sum(one_row) / len(one_row)
+        sess.reset()
+        sess.prefill(prompt, want=False)
+        sess.time_kind(dom)
+        for _ in range(args.steps):
+            sess.decode_frame(want=False)
+        live_ms, live_n = sess.kind_time()
+        sess.time_kind(-1)
+        name = N.KIND_NAMES[dom]
+        per = per_launch_bytes(dims, wl.wtype, name)
         achieved = per / (avg_ms / 1000.0)
-        roof = {"kernel": dom, "bound": "hbm", "achieved": round(achieved / 1e9, 1), "peak": HBM_PEAK / 1e9,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK, 4), "traffic": None,
-                "bytes_per_launch": per, "avg_launch_us": round(avg_ms * 1000, 2),
-                "launches_timed": len(one_row)}
-        share = {k: round(v / sum(totals.values()), 4) for k, v in sorted(totals.items(), key=lambda kv: -kv[1])}
-        roof["frame_time_share"] = share
-        roof["launches_per_frame"] = len(recs) // args.profile_frames
-        log(f"dominant kernel {dom}: {avg_ms * 1000:.1f} us/launch, {achieved / 1e9:.0f} GB/s; shares {share}")
+        roof = {"kernel": name, "bound": "hbm", "achieved": round(achieved / 1e9, 1), "peak": HBM_PEAK / 1e9,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK, 4),
+                "traffic": measured_traffic(name, wl.name),
+                "bytes_per_launch": per, "avg_launch_us": round(avg_ms * 1000, 2), "launches_timed": len(one_row),
+                "overlapped_avg_launch_us": round(live_ms / live_n * 1000, 2), "overlapped_launches": live_n,
+                "launches_per_frame": len(recs) // args.profile_frames, "frame_time_share": share}
+        log(f"dominant kernel {name}: {avg_ms * 1000:.1f} us/launch serialised ({achieved / 1e9:.0f} GB/s), "
+            f"{live_ms / live_n * 1000:.1f} us beside the other chain; serialised-frame shares {share}")
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -169,6 +195,26 @@ def main():
     }
     sess.close()
     print(json.dumps(out), flush=True)
+
+
+def measured_traffic(kind, workload):
+    """HBM bytes per launch of `kind` from the committed counter summary
+    (profiles/hbm_traffic_<kind>_<workload>.md), or None when there is none or
+    the kernel source has changed since the counters were taken."""
+    import hashlib
+    import re
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{kind}_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_t = re.search(r"traffic_bytes_per_launch:\s*(\d+)", text)
+    m_h = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)
+    if not m_t or not m_h:
+        return None
+    src = os.path.join(ROOT, "dar_decode_frame_amd", "csrc", "dar_kernels.hip")
+    if hashlib.sha256(open(src, "rb").read()).hexdigest() != m_h.group(1):
+        return None
+    return int(m_t.group(1))
 
 
 def per_launch_bytes(dims, wtype, kind):

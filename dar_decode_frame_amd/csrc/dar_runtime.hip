@@ -255,6 +255,10 @@ struct dar_ctx {
   std::string err;
 
   std::vector<hipEvent_t> events;
+  // live timing of one kind of launch in eager decode frames (dar_time_kind)
+  int timed_kind = -1;
+  std::vector<hipEvent_t> tpool;  // event pairs, reused
+  size_t tused = 0;               // events recorded since the last read
 };
 
 namespace {
@@ -522,17 +526,38 @@ void plan_single(Plan& p, const std::vector<TaskRec>& chain) {
   }
 }
 
+// a launch dar_time_kind selected: one-row launches of that kind (the fast
+// AR's two-row first pass is left out)
+bool timed(const dar_ctx* c, const Plan& p, size_t i) {
+  return c->timed_kind >= 0 && p.kind[i] == c->timed_kind && !(p.layer[i] >= 1000 && p.layer[i] < 2000);
+}
+
 hipError_t enqueue_plan(dar_ctx* c, const Plan& p, hipStream_t s, size_t ev_base = SIZE_MAX) {
   const int wt = c->fp8 ? W_FP8 : W_BF16;
   for (size_t i = 0; i < p.launches(); ++i) {
+    hipEvent_t before = nullptr, after = nullptr;
     if (ev_base != SIZE_MAX) {
-      hipError_t e = hipEventRecord(c->events[2 * (ev_base + i)], s);
+      before = c->events[2 * (ev_base + i)];
+      after = c->events[2 * (ev_base + i) + 1];
+    } else if (timed(c, p, i)) {
+      while (c->tpool.size() < c->tused + 2) {
+        hipEvent_t ev;
+        hipError_t e = hipEventCreate(&ev);
+        if (e != hipSuccess) return e;
+        c->tpool.push_back(ev);
+      }
+      before = c->tpool[c->tused];
+      after = c->tpool[c->tused + 1];
+      c->tused += 2;
+    }
+    if (before) {
+      hipError_t e = hipEventRecord(before, s);
       if (e != hipSuccess) return e;
     }
     hipError_t e = launch_task(wt, p.tasks[i], s);
     if (e != hipSuccess) return e;
-    if (ev_base != SIZE_MAX) {
-      e = hipEventRecord(c->events[2 * (ev_base + i) + 1], s);
+    if (after) {
+      e = hipEventRecord(after, s);
       if (e != hipSuccess) return e;
     }
   }
@@ -951,6 +976,7 @@ int dar_destroy(dar_ctx* c) {
     if (ch->s) (void)hipStreamSynchronize(ch->s);
   for (Plan* p : {&c->p_c0, &c->p_fast, &c->p_slow}) free_plan(*p);
   for (hipEvent_t ev : c->events) (void)hipEventDestroy(ev);
+  for (hipEvent_t ev : c->tpool) (void)hipEventDestroy(ev);
   for (hipEvent_t ev : {c->ev_start, c->ev_c0, c->ev_f_done, c->ev_s_done})
     if (ev) (void)hipEventDestroy(ev);
   for (Chain* ch : {&c->cs, &c->cf})
@@ -1172,6 +1198,29 @@ int dar_op_fp8_decode(const void* codes, int32_t n, float* out, void* stream) {
   if (!codes || !out || n < 1) return DAR_E_INVAL;
   hipError_t e = launch_fp8_decode(static_cast<const uint8_t*>(codes), n, out, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(nullptr, e, "fp8 decode");
+  return DAR_OK;
+}
+
+int dar_time_kind(dar_ctx* c, int32_t kind) {
+  if (!c || kind < -1 || kind > K_OTHER) return DAR_E_INVAL;
+  c->timed_kind = kind;
+  c->tused = 0;
+  return DAR_OK;
+}
+
+int dar_kind_time(dar_ctx* c, double* ms_total, int32_t* launches) {
+  if (!c || !ms_total || !launches) return DAR_E_INVAL;
+  DAR_HIP(c, hipStreamSynchronize(c->stream), "synchronize");
+  for (Chain* ch : {&c->cs, &c->cf}) DAR_HIP(c, hipStreamSynchronize(ch->s), "synchronize");
+  double total = 0.0;
+  for (size_t i = 0; i + 1 < c->tused; i += 2) {
+    float ms = 0.f;
+    DAR_HIP(c, hipEventElapsedTime(&ms, c->tpool[i], c->tpool[i + 1]), "event time");
+    total += ms;
+  }
+  *ms_total = total;
+  *launches = (int32_t)(c->tused / 2);
+  c->tused = 0;
   return DAR_OK;
 }
 

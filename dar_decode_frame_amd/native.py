@@ -104,6 +104,8 @@ _SIGS = {
     "dar_op_gemm": ([_I32, _VP, _VP, _I32, _I32, _VP, _I32, _VP, _VP], ctypes.c_int),
     "dar_op_attention": ([_VP, _VP, _VP, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _VP, _VP], ctypes.c_int),
     "dar_op_fp8_decode": ([_VP, _I32, _VP, _VP], ctypes.c_int),
+    "dar_time_kind": ([_VP, _I32], ctypes.c_int),
+    "dar_kind_time": ([_VP, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_I32)], ctypes.c_int),
     "dar_profile_frame": ([_VP, _I32, _VP, _VP, _VP, ctypes.POINTER(_I32)], ctypes.c_int),
 }
 
@@ -246,6 +248,18 @@ def dar_op_gemm(wtype, w_ptr, scale_ptr, N, K, x_ptr, M, y_ptr, stream_ptr):
 
 def dar_op_fp8_decode(codes_ptr, n, out_ptr, stream_ptr):
     return _check(lib.dar_op_fp8_decode(codes_ptr, n, out_ptr, stream_ptr), "dar_op_fp8_decode")
+
+
+def dar_time_kind(ctx, kind):
+    return _check(lib.dar_time_kind(ctx, kind), "dar_time_kind", ctx)
+
+
+def dar_kind_time(ctx):
+    """(summed ms, launches) of the launches timed since dar_time_kind or the last read."""
+    ms = ctypes.c_double(0.0)
+    n = ctypes.c_int32(0)
+    _check(lib.dar_kind_time(ctx, ctypes.byref(ms), ctypes.byref(n)), "dar_kind_time", ctx)
+    return ms.value, n.value
 
 
 def dar_profile_frame(ctx, cap=4096):

@@ -171,5 +171,11 @@ class DarSession:
     def nonfinite(self):
         return N.dar_nonfinite(self.ctx)
 
+    def time_kind(self, kind):
+        N.dar_time_kind(self.ctx, kind)
+
+    def kind_time(self):
+        return N.dar_kind_time(self.ctx)
+
     def profile_frame(self):
         return N.dar_profile_frame(self.ctx)
