@@ -1,0 +1,109 @@
+"""Parity at the benchmark's full shapes (36 + 4 layers, d 2560, 32/8 heads of
+128, SwiGLU 9728, 4096-entry codebooks; slow AR alone, bf16 frame, fp8 frame)
+against CPU oracle references written by tests/golden/make_fullshape.py, in
+the launch configuration bench.py times (two streams, eager launches).
+
+Two runs per workload: prefill 128 + 9 frames teacher-forced with the
+oracle's greedy frames (positions 127..136), and the frame at position 1007
+after 880 frames forced with seeded random codes. Compared per (frame,
+codebook): the code exactly wherever the oracle's top-1 - top-2 margin
+exceeds 1e-2; the logits at the stored sample indices (seeded ones plus the
+top two) within the relative-L2 tolerance of the weight type; and the argmax
+agreement over every compared vector (>= 99 %; every code when fewer than
+100 vectors are compared).
+"""
+import importlib.util
+import json
+import os
+
+import numpy as np
+import pytest
+
+import synth
+from parity import TOL
+
+pytestmark = pytest.mark.gpu
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+WORKLOADS = ["s2pro_slow_bf16", "s2pro_dual_bf16", "s2pro_dual_fp8"]
+
+
+def _golden(name):
+    with open(os.path.join(HERE, "golden", f"fullshape_{name}.json")) as f:
+        return json.load(f)
+
+
+def _random_frames():
+    # the generator of the forced codes lives with the script that wrote the references
+    spec = importlib.util.spec_from_file_location("make_fullshape", os.path.join(HERE, "golden", "make_fullshape.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod.random_frames
+
+
+def _compare(ref_vecs, codes, logits, dims, out):
+    for k, v in enumerate(ref_vecs):
+        idx = np.asarray(v["idx"])
+        o = np.asarray(v["logits"], dtype=np.float64)
+        g = np.asarray(logits[k], dtype=np.float64)[idx]
+        out["rel"].append(float(np.linalg.norm(g - o) / np.linalg.norm(o)))
+        out["n"] += 1
+        out["agree"] += int(codes[k] == v["code"])
+        if v["margin"] > 1e-2 and codes[k] != v["code"]:
+            out["exact_fail"].append((int(codes[k]), v["code"], v["margin"]))
+
+
+@pytest.fixture(scope="module", params=WORKLOADS)
+def full(request):
+    import torch
+
+    from dar_decode_frame_amd.session import DarSession, DeviceWeights
+    name = request.param
+    wl = synth.WORKLOADS[name]
+    host = synth.gen_weights(wl.dims, wl.weight_seed)
+    dw = DeviceWeights(wl.dims, host, wl.wtype)
+    del host
+    sess = DarSession(wl.dims, dw, wl.max_len)
+    yield name, wl, sess
+    sess.close()
+    del dw
+    torch.cuda.empty_cache()
+
+
+def test_fullshape_parity(full):
+    name, wl, sess = full
+    dims = wl.dims
+    ref = _golden(name)
+    assert ref["prefill"] == wl.prefill_len and ref["max_len"] == wl.max_len
+    prompt = synth.gen_prompt(wl.prefill_len, dims.vocab_c0, wl.prompt_seed)
+    stats = {"rel": [], "n": 0, "agree": 0, "exact_fail": []}
+
+    # early frames, forced with the oracle's greedy frames
+    forced = [np.asarray(f, dtype=np.int32) for f in ref["early"]["forced"]]
+    sess.reset()
+    frames = [sess.prefill(prompt, forced=forced[0])]
+    for f in forced[1:]:
+        frames.append(sess.decode_frame(forced=f))
+    for (codes, logits), rv in zip(frames, ref["early"]["frames"]):
+        _compare(rv, codes, logits, dims, stats)
+
+    # late frame at position 1007 after frames forced with seeded random codes
+    late = ref["late"]
+    forced = [np.asarray(f, dtype=np.int32) for f in _random_frames()(dims, late["frames_forced"], late["force_seed"])]
+    sess.reset()
+    sess.prefill(prompt, forced=forced[0], want=False)
+    for f in forced[1:-1]:
+        sess.decode_frame(forced=f, want=False)
+    codes, logits = sess.decode_frame(forced=forced[-1])
+    assert sess.position() == late["position"] + 1
+    _compare(late["frame"], codes, logits, dims, stats)
+
+    agree = stats["agree"] / stats["n"]
+    print(f"\n{name}: max rel {max(stats['rel']):.3e}, median rel {np.median(stats['rel']):.3e}, "
+          f"agreement {agree:.4f} over {stats['n']} vectors, exact failures {stats['exact_fail']}")
+    assert max(stats["rel"]) <= TOL[wl.wtype], stats
+    assert not stats["exact_fail"], stats
+    # 99 % needs at least 100 vectors to mean anything; with fewer (the slow AR
+    # alone has one code per frame) every code must agree
+    assert agree >= (0.99 if stats["n"] >= 100 else 1.0), stats
+    assert sess.nonfinite() == 0
