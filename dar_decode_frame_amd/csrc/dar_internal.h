@@ -118,6 +118,9 @@ struct AttnArgs {
   float* part;              // [M][n_kv][nsplit_max][group][head_dim + 2]
   float* out;
   int out_stride;
+  const int* row_pos;       // non-null: position of query row m is row_pos[m] (else *pos + m)
+  const int* row_seq;       // non-null: row m reads the cache of sequence row_seq[m]
+  long long seq_stride;     // elements between two sequences' caches
 };
 
 // y[m][n] (+)= scale[n] * sum_k x[m][k] W[n][k] for m < M, n < N (prefill
@@ -136,6 +139,33 @@ struct GemmArgs {
   int splits, cps;          // set by launch_gemm: K splits, 64-wide chunks per split
 };
 
+// Batched commit of codebook `code_index` for B sequences: argmax of each
+// logits row, codes and ring entries, next inputs, position advance.
+struct RowsCommitArgs {
+  const float* logits;      // [B][ld]
+  int ld, V, B;
+  int code_index, frame_codes;
+  int* pred;                // [B][frame_codes]
+  int* committed;           // [B][frame_codes]
+  const int* forced;        // [B][frame_codes]
+  const int* force_flag;
+  int* ring;                // [max_len][B][frame_codes]
+  const int* pos;           // [B] slow position of each sequence's frame
+  int* pos_inc;             // non-null: ++pos_inc[b] at the end
+  int K;                    // row width of the tables and copies
+  const uint16_t* next_table;  // non-null: next_x[b * next_stride ...] = next_table[code]
+  int next_rows;
+  float* next_x;
+  int next_stride;
+  const uint16_t* slow_table;  // non-null: slow_x[b] = slow_table[code]
+  int slow_rows;
+  float* slow_x;
+  const float* copy_src[2];  // non-null: copy_dst[j][b * dst_stride[j] + i] = copy_src[j][b * src_stride[j] + i]
+  float* copy_dst[2];        // for i < copy_n[j]
+  int copy_src_stride[2], copy_dst_stride[2], copy_n[2];
+  int* anomalies;
+};
+
 enum TaskKind : int {
   T_NONE = 0,
   T_QKV,        // QkvArgs
@@ -145,10 +175,56 @@ enum TaskKind : int {
   T_SWIGLU,     // SwigluArgs
   T_HEAD,       // HeadArgs, weights of the launch's weight type
   T_HEAD_BF16,  // HeadArgs, bf16 weights (the tied codebook-0 head in every mode)
-  T_COMMIT      // CommitArgs, one block
+  T_COMMIT,     // CommitArgs, one block
+  // many-row stages (batched decode)
+  T_NORM_SPLIT,   // NormSplitArgs
+  T_GEMM,         // GemmTask
+  T_ROPE_ROWS,    // RopeRowsArgs
+  T_SILU_SPLIT,   // SiluSplitArgs
+  T_COMMIT_ROWS,  // RowsCommitArgs
+  T_INC_ROWS      // IncRowsArgs
 };
 
 // One stage of a chain: its kind, input rows and arguments.
+struct NormSplitArgs {
+  const float* x;
+  int x_stride, M, K;
+  const uint16_t* gain;  // nullptr: no norm
+  float eps;
+  uint16_t* xh;
+  uint16_t* xl;
+  float* out_f32;        // optional normalised rows
+};
+struct GemmTask {
+  GemmArgs g;
+  int wtype;             // the matrix's weight type (the tied codebook-0 head is bf16 in every mode)
+  size_t part_cap;       // floats of g.part
+};
+struct RopeRowsArgs {
+  const float* qkv;
+  int M;
+  const int* row_pos;
+  const int* row_seq;
+  long long seq_stride;
+  int n_heads_q, n_heads_kv, head_dim;
+  const float2* rope;
+  float* q_out;
+  uint16_t* kc;
+  uint16_t* vc;
+  int cache_len;
+};
+struct SiluSplitArgs {
+  const float* a;
+  const float* b;
+  int M, F;
+  uint16_t* hh;
+  uint16_t* hl;
+};
+struct IncRowsArgs {
+  int* v;
+  int n;
+};
+
 struct Task {
   int kind, M;
   union {
@@ -158,6 +234,12 @@ struct Task {
     AttnArgs attn;
     HeadArgs head;
     CommitArgs commit;
+    NormSplitArgs norm;
+    GemmTask gemm;
+    RopeRowsArgs rope;
+    SiluSplitArgs silu;
+    RowsCommitArgs rows;
+    IncRowsArgs inc;
   };
 };
 
@@ -175,16 +257,23 @@ int gemm_mpad(int M);
 // GEMM with K split across workgroups (deterministic second pass) so that the
 // launch covers the chip; part must hold part_cap floats.
 hipError_t launch_gemm(int wtype, GemmArgs a, size_t part_cap, hipStream_t s);
-// hi/lo bf16 rows of x (RMSNorm(x) * gain when gain is set), gemm_mpad(M) rows
+// hi/lo bf16 rows of x (RMSNorm(x) * gain when gain is set), gemm_mpad(M)
+// rows; out_f32 (optional): the normalised rows in fp32, [M][K]
 hipError_t launch_norm_split(const float* x, int x_stride, int M, int K, const uint16_t* gain, float eps,
-                             uint16_t* xh, uint16_t* xl, hipStream_t s);
+                             uint16_t* xh, uint16_t* xl, hipStream_t s, float* out_f32 = nullptr);
 // x[m] = table[clamp(tok[m])] for m < M
 hipError_t launch_embed_rows(const uint16_t* table, int rows, int K, const int* tok, int M, float* x,
                              int* anomalies, hipStream_t s);
-// RoPE at positions p0.. of M rows of QKV output; q out, k/v appended to the caches
+// RoPE at positions p0 + m (or row_pos[m]) of M rows of QKV output; q out,
+// k/v appended to the caches (sequence row_seq[m]'s cache when row_seq is set)
 hipError_t launch_rope_rows(const float* qkv, int M, int p0, int n_heads_q, int n_heads_kv, int head_dim,
                             const float2* rope, float* q_out, uint16_t* kc, uint16_t* vc, int cache_len,
-                            hipStream_t s);
+                            hipStream_t s, const int* row_pos = nullptr, const int* row_seq = nullptr,
+                            long long seq_stride = 0);
+// argmax + commit of one codebook for B sequences (k_commit_rows)
+hipError_t launch_commit_rows(const RowsCommitArgs& a, hipStream_t s);
+// v[i] += 1 for i < n
+hipError_t launch_inc_rows(int* v, int n, hipStream_t s);
 // SiLU(a) * b as hi/lo bf16 rows
 hipError_t launch_silu_split(const float* a, const float* b, int M, int F, uint16_t* hh, uint16_t* hl,
                              hipStream_t s);

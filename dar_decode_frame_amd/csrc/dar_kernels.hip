@@ -572,6 +572,16 @@ __device__ __forceinline__ void commit_body(const CommitArgs& a, char* lds) {
   if (a.pos_inc && tid == 0) *a.pos_inc = *a.pos_inc + 1;
 }
 
+// Positions attended by query row m (its own position + 1, causal) and the
+// offset of its sequence's cache: rows at *pos + m of one cache by default,
+// or per-row positions and sequences (batched decode, fast AR first pass).
+__device__ __forceinline__ int attn_len(const AttnArgs& a, int m) {
+  return (a.row_pos ? a.row_pos[m] : *a.pos + m) + 1;
+}
+__device__ __forceinline__ size_t attn_seq_offset(const AttnArgs& a, int m) {
+  return a.row_seq ? (size_t)a.row_seq[m] * a.seq_stride : 0;
+}
+
 // ------------------------------------------------ split-K decode attention --
 
 // One block = one KV head x one split of `chunk` positions for one query row
@@ -590,7 +600,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, int bid, char* lds)
   const int kvh = (bid / a.nsplit_max) % a.n_heads_kv;
   const int m = bid / (a.nsplit_max * a.n_heads_kv);
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-  const int T = *a.pos + m + 1;
+  const int T = attn_len(a, m);
   const int nsplit = (T + a.chunk - 1) / a.chunk;
   if (s >= nsplit) return;
   const int j0 = s * a.chunk, j1 = min(T, j0 + a.chunk);
@@ -616,8 +626,9 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, int bid, char* lds)
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
   }
-  const uint16_t* Kb = a.K + (size_t)kvh * a.cache_len * HD + sub * 8;
-  const uint16_t* Vb = a.V + (size_t)kvh * a.cache_len * HD + sub * 8;
+  const size_t kv0 = attn_seq_offset(a, m) + (size_t)kvh * a.cache_len * HD + sub * 8;
+  const uint16_t* Kb = a.K + kv0;
+  const uint16_t* Vb = a.V + kv0;
   constexpr int STEP = kWaves * PPW;
   for (int jb = j0 + wave * PPW; jb < j1; jb += STEP * U) {
     u32x4 kk[U], vv[U];
@@ -725,7 +736,7 @@ __device__ __forceinline__ void combine_body(const AttnArgs& a, int bid, char* l
   constexpr int U = 8;            // loads in flight per thread
   const int h = bid % G, kvh = (bid / G) % a.n_heads_kv, m = bid / (G * a.n_heads_kv);
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-  const int T = *a.pos + m + 1;
+  const int T = attn_len(a, m);
   const int nsplit = (T + a.chunk - 1) / a.chunk;
   const int stride_s = G * (HD + 2);
   const float* part = a.part + (((size_t)m * a.n_heads_kv + kvh) * a.nsplit_max) * stride_s + h * (HD + 2);
@@ -1079,7 +1090,7 @@ __device__ __forceinline__ void attn_wide_body(const AttnArgs& a, int bid, char*
   constexpr int NT = NW * kWave;
   const int kvh = bid % a.n_heads_kv, m = bid / a.n_heads_kv;
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-  const int T = *a.pos + m + 1;
+  const int T = attn_len(a, m);
   const int grp = lane / LPP, sub = lane % LPP;
   float* sm_acc = reinterpret_cast<float*>(lds);  // [NW][G][HD]
   float* sm_ml = sm_acc + NW * G * HD;            // [NW][G][2]
@@ -1102,8 +1113,9 @@ __device__ __forceinline__ void attn_wide_body(const AttnArgs& a, int bid, char*
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
   }
-  const uint16_t* Kb = a.K + (size_t)kvh * a.cache_len * HD + sub * 8;
-  const uint16_t* Vb = a.V + (size_t)kvh * a.cache_len * HD + sub * 8;
+  const size_t kv0 = attn_seq_offset(a, m) + (size_t)kvh * a.cache_len * HD + sub * 8;
+  const uint16_t* Kb = a.K + kv0;
+  const uint16_t* Vb = a.V + kv0;
   for (int jb = wave * PPW; jb < T; jb += STEP * U) {
     u32x4 kk[U], vv[U];
 #pragma unroll
@@ -1276,9 +1288,9 @@ __global__ void k_embed(const uint16_t* table, int rows, int K, const int* tok, 
 }
 
 __global__ void k_set_forced(const int* forced, int n, int* dst, int* flag) {
-  const int i = threadIdx.x;
-  if (forced && i < n) dst[i] = forced[i];
-  if (i == 0) *flag = forced ? 1 : 0;
+  if (forced)
+    for (int i = threadIdx.x; i < n; i += blockDim.x) dst[i] = forced[i];
+  if (threadIdx.x == 0) *flag = forced ? 1 : 0;
 }
 
 __global__ void k_fill_i32(int* dst, int n, int value) {
@@ -1520,11 +1532,36 @@ static hipError_t single_launch(const Task& t, hipStream_t s, bool prep) {
   return err;
 }
 
+// the many-row stages (dar_prefill.hip); false when t is not one of them
+static bool row_stage(const Task& t, hipStream_t s, hipError_t& e) {
+  switch (t.kind) {
+    case T_NORM_SPLIT: {
+      const NormSplitArgs& a = t.norm;
+      e = launch_norm_split(a.x, a.x_stride, a.M, a.K, a.gain, a.eps, a.xh, a.xl, s, a.out_f32);
+      return true;
+    }
+    case T_GEMM: e = launch_gemm(t.gemm.wtype, t.gemm.g, t.gemm.part_cap, s); return true;
+    case T_ROPE_ROWS: {
+      const RopeRowsArgs& a = t.rope;
+      e = launch_rope_rows(a.qkv, a.M, 0, a.n_heads_q, a.n_heads_kv, a.head_dim, a.rope, a.q_out, a.kc, a.vc,
+                           a.cache_len, s, a.row_pos, a.row_seq, a.seq_stride);
+      return true;
+    }
+    case T_SILU_SPLIT: e = launch_silu_split(t.silu.a, t.silu.b, t.silu.M, t.silu.F, t.silu.hh, t.silu.hl, s); return true;
+    case T_COMMIT_ROWS: e = launch_commit_rows(t.rows, s); return true;
+    case T_INC_ROWS: e = launch_inc_rows(t.inc.v, t.inc.n, s); return true;
+    default: return false;
+  }
+}
+
 hipError_t launch_task(int wtype, const Task& t, hipStream_t s) {
+  hipError_t e = hipSuccess;
+  if (row_stage(t, s, e)) return e;
   return wtype == W_FP8 ? single_launch<FP8>(t, s, false) : single_launch<BF16>(t, s, false);
 }
 
 hipError_t prepare_task(int wtype, const Task& t) {
+  if (t.kind >= T_NORM_SPLIT) return hipSuccess;  // the many-row kernels need no set-up
   return wtype == W_FP8 ? single_launch<FP8>(t, nullptr, true) : single_launch<BF16>(t, nullptr, true);
 }
 

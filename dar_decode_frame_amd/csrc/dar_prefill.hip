@@ -1,6 +1,7 @@
-// gfx950 kernels of the prompt prefill: the slow AR's layers over a block of
-// up to kPrefillRows prompt positions at once, so every weight matrix is read
-// once per block instead of once per token.
+// gfx950 kernels that run a layer over many rows at once: the prompt prefill
+// (a block of up to kPrefillRows prompt positions) and batched decode (one
+// row per sequence, two in the fast AR's first pass), so every weight matrix
+// is read once per launch instead of once per row.
 //
 // The projections become GEMMs y[m][n] = sum_k x[m][k] W[n][k] with m over the
 // block's positions, run on MFMA (v_mfma_f32_32x32x16_bf16). The weights are
@@ -193,9 +194,11 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
 }
 
 // Row m of the GEMM input: v = x[m] (RMSNorm(x[m]) * gain when gain is set),
-// written as hi = bf16(v), lo = bf16(v - hi); rows M..Mpad-1 are zero.
+// written as hi = bf16(v), lo = bf16(v - hi); rows M..Mpad-1 are zero. With
+// out_f32 set, v is also written there in fp32 (row stride K).
 __global__ __launch_bounds__(kBlock) void k_norm_split(const float* x, int x_stride, int M, int K,
-                                                        const uint16_t* gain, float eps, uint16_t* xh, uint16_t* xl) {
+                                                        const uint16_t* gain, float eps, uint16_t* xh, uint16_t* xl,
+                                                        float* out_f32) {
   __shared__ float red[kWaves];
   const int m = blockIdx.x, tid = threadIdx.x;
   uint16_t* oh = xh + (size_t)m * K;
@@ -217,6 +220,7 @@ __global__ __launch_bounds__(kBlock) void k_norm_split(const float* x, int x_str
     const uint16_t h = f2bf(v);
     oh[k] = h;
     ol[k] = f2bf(v - bf2f(h));
+    if (out_f32) out_f32[(size_t)m * K + k] = v;
   }
 }
 
@@ -231,15 +235,21 @@ __global__ __launch_bounds__(kBlock) void k_embed_rows(const uint16_t* table, in
   for (int k = threadIdx.x; k < K; k += kBlock) x[(size_t)m * K + k] = bf2f(row[k]);
 }
 
-// RoPE at positions p0 + m on q and k of the block's QKV output, q to q_out,
-// k and v appended to the bf16 caches (rotate-half pairs (i, i + hd/2)).
-__global__ __launch_bounds__(kBlock) void k_rope_rows(const float* qkv, int M, int p0, int n_heads_q, int n_heads_kv,
-                                                       int head_dim, const float2* rope, float* q_out,
+// RoPE at positions p0 + m (or row_pos[m]) on q and k of the rows' QKV output,
+// q to q_out, k and v appended to the bf16 caches (rotate-half pairs
+// (i, i + hd/2)); with row_seq, row m appends to sequence row_seq[m]'s cache.
+__global__ __launch_bounds__(kBlock) void k_rope_rows(const float* qkv, int M, int p0, const int* row_pos,
+                                                       const int* row_seq, long long seq_stride, int n_heads_q,
+                                                       int n_heads_kv, int head_dim, const float2* rope, float* q_out,
                                                        uint16_t* kc, uint16_t* vc, int cache_len) {
   const int m = blockIdx.x;
   const int half = head_dim / 2;
   const int n_heads = n_heads_q + 2 * n_heads_kv;
-  const int pos = p0 + m;
+  const int pos = row_pos ? row_pos[m] : p0 + m;
+  if (row_seq) {
+    kc += (size_t)row_seq[m] * seq_stride;
+    vc += (size_t)row_seq[m] * seq_stride;
+  }
   const float* row = qkv + (size_t)m * n_heads * head_dim;
   for (int j = threadIdx.x; j < n_heads * half; j += kBlock) {
     const int head = j / half, i = j % half;
@@ -282,6 +292,75 @@ __global__ __launch_bounds__(kBlock) void k_silu_split(const float* a, const flo
   }
 }
 
+// Batched codebook commit, one workgroup per sequence b: the first index of
+// the maximum of logits[b] (NaN counts as -inf and as an anomaly), recorded as
+// the argmax and (or the forced code) as the committed code, then the next
+// inputs gathered from the tables and the position advanced.
+__global__ __launch_bounds__(kBlock) void k_commit_rows(RowsCommitArgs a) {
+  __shared__ unsigned long long red[kWaves];
+  __shared__ int code_sh;
+  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const float* lg = a.logits + (size_t)b * a.ld;
+  unsigned long long best = 0ull;
+  int bad = 0;
+  for (int i = tid; i < a.V; i += kBlock) {
+    float v = lg[i];
+    if (!isfinite(v)) {
+      ++bad;
+      if (v != v) v = -INFINITY;
+    }
+    // order-preserving key of the value, ties to the lower index
+    uint32_t u = __float_as_uint(v);
+    u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    const unsigned long long k = ((unsigned long long)u << 32) | (unsigned long long)(0xffffffffu - (uint32_t)i);
+    best = k > best ? k : best;
+  }
+  if (bad) atomicAdd(a.anomalies, bad);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const unsigned long long o = __shfl_xor(best, off);
+    best = o > best ? o : best;
+  }
+  if (lane == 0) red[wave] = best;
+  __syncthreads();
+  if (tid == 0) {
+    unsigned long long m = red[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) m = red[w] > m ? red[w] : m;
+    const int pred = (int)(0xffffffffu - (uint32_t)(m & 0xffffffffull));
+    const int slot = b * a.frame_codes + a.code_index;
+    const int code = *a.force_flag ? a.forced[slot] : pred;
+    a.pred[slot] = pred;
+    a.committed[slot] = code;
+    a.ring[((size_t)a.pos[b] * a.B + b) * a.frame_codes + a.code_index] = code;
+    code_sh = code;
+  }
+  __syncthreads();
+  const int code = code_sh;
+  if (a.next_table) {
+    const uint16_t* row = a.next_table + (size_t)min(max(code, 0), a.next_rows - 1) * a.K;
+    for (int k = tid; k < a.K; k += kBlock) a.next_x[(size_t)b * a.next_stride + k] = bf2f(row[k]);
+  }
+  if (a.slow_table) {
+    const uint16_t* row = a.slow_table + (size_t)min(max(code, 0), a.slow_rows - 1) * a.K;
+    for (int k = tid; k < a.K; k += kBlock) a.slow_x[(size_t)b * a.K + k] = bf2f(row[k]);
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    if (a.copy_src[j]) {
+      for (int k = tid; k < a.copy_n[j]; k += kBlock)
+        a.copy_dst[j][(size_t)b * a.copy_dst_stride[j] + k] = a.copy_src[j][(size_t)b * a.copy_src_stride[j] + k];
+    }
+  }
+  __syncthreads();
+  if (a.pos_inc && tid == 0) a.pos_inc[b] = a.pos_inc[b] + 1;
+}
+
+__global__ void k_inc_rows(int* v, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) v[i] = v[i] + 1;
+}
+
 template <typename WT>
 hipError_t gemm_dispatch(const GemmArgs& a, int mt, dim3 grid, hipStream_t s) {
   switch (mt) {
@@ -319,8 +398,9 @@ hipError_t launch_gemm(int wtype, GemmArgs a, size_t part_cap, hipStream_t s) {
 }
 
 hipError_t launch_norm_split(const float* x, int x_stride, int M, int K, const uint16_t* gain, float eps,
-                             uint16_t* xh, uint16_t* xl, hipStream_t s) {
-  hipLaunchKernelGGL(k_norm_split, dim3(gemm_mpad(M)), dim3(kBlock), 0, s, x, x_stride, M, K, gain, eps, xh, xl);
+                             uint16_t* xh, uint16_t* xl, hipStream_t s, float* out_f32) {
+  hipLaunchKernelGGL(k_norm_split, dim3(gemm_mpad(M)), dim3(kBlock), 0, s, x, x_stride, M, K, gain, eps, xh, xl,
+                     out_f32);
   return hipGetLastError();
 }
 
@@ -332,9 +412,19 @@ hipError_t launch_embed_rows(const uint16_t* table, int rows, int K, const int* 
 
 hipError_t launch_rope_rows(const float* qkv, int M, int p0, int n_heads_q, int n_heads_kv, int head_dim,
                             const float2* rope, float* q_out, uint16_t* kc, uint16_t* vc, int cache_len,
-                            hipStream_t s) {
-  hipLaunchKernelGGL(k_rope_rows, dim3(M), dim3(kBlock), 0, s, qkv, M, p0, n_heads_q, n_heads_kv, head_dim, rope,
-                     q_out, kc, vc, cache_len);
+                            hipStream_t s, const int* row_pos, const int* row_seq, long long seq_stride) {
+  hipLaunchKernelGGL(k_rope_rows, dim3(M), dim3(kBlock), 0, s, qkv, M, p0, row_pos, row_seq, seq_stride, n_heads_q,
+                     n_heads_kv, head_dim, rope, q_out, kc, vc, cache_len);
+  return hipGetLastError();
+}
+
+hipError_t launch_inc_rows(int* v, int n, hipStream_t s) {
+  hipLaunchKernelGGL(k_inc_rows, dim3((n + kBlock - 1) / kBlock), dim3(kBlock), 0, s, v, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_commit_rows(const RowsCommitArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(k_commit_rows, dim3(a.B), dim3(kBlock), 0, s, a);
   return hipGetLastError();
 }
 

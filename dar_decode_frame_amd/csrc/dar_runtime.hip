@@ -62,6 +62,11 @@ struct Layout {
   // QKV output, q, attention output, W1/W3 outputs, GEMM and attention partials
   size_t px, pxh, pxl, pqkv, pq, po, ph1, ph3, pgp, patt, ppos, total;
   size_t pgp_floats;
+  // batched decode (max_batch > 1): per chain the QKV output, the W3 output,
+  // the GEMM input halves and the K-split partial sums; the rows' positions
+  // and sequences
+  size_t bqkv[2], bh3[2], bxh[2], bxl[2], bgp[2], rows;
+  size_t bgp_floats[2];
   int nsplit_slow, chunk, rope_len, seq_len, vmax, fast_len, nslots;
 };
 
@@ -83,8 +88,9 @@ Layout make_layout(const dar_config* c) {
     off = align_up(off + bytes);
     return at;
   };
+  const int B = c->max_batch;
   for (int ch = 0; ch < 2; ++ch) {
-    const int M = ch == 0 ? 1 : 2;
+    const int M = (ch == 0 ? 1 : 2) * B;
     const int nsplit = ch == 0 ? L.nsplit_slow : 1;
     L.x[ch] = take(sizeof(float) * M * d);
     L.q[ch] = take(sizeof(float) * M * qw);
@@ -92,23 +98,24 @@ Layout make_layout(const dar_config* c) {
     L.h[ch] = take(sizeof(float) * M * F);
     L.part[ch] = take(sizeof(float) * attn_partial_floats(M, c->n_heads_kv, nsplit, g, c->head_dim));
   }
-  L.ht = take(sizeof(float) * d);
-  L.logits0 = take(sizeof(float) * c->vocab_c0);
-  L.flogits = take(sizeof(float) * (size_t)fc * L.vmax);
+  L.ht = take(sizeof(float) * (size_t)B * d);
+  L.logits0 = take(sizeof(float) * (size_t)B * c->vocab_c0);
+  L.flogits = take(sizeof(float) * (size_t)B * fc * L.vmax);
   L.slots0 = take(sizeof(unsigned long long) * L.nslots);
   L.slotsf = take(sizeof(unsigned long long) * L.nslots);
-  L.pred = take(sizeof(int) * fc);
-  L.committed = take(sizeof(int) * fc);
-  L.forced = take(sizeof(int) * fc);
+  L.pred = take(sizeof(int) * B * fc);
+  L.committed = take(sizeof(int) * B * fc);
+  L.forced = take(sizeof(int) * B * fc);
   L.flags = take(sizeof(int) * 4);
-  L.pos = take(sizeof(int) * 4);
+  L.pos = take(sizeof(int) * (2 * B + 4));  // slow positions [B], frame positions [B]
   L.seqpos = take(sizeof(int) * L.seq_len);
-  L.ring = take(sizeof(int) * (size_t)c->max_len * fc);
+  L.ring = take(sizeof(int) * (size_t)c->max_len * B * fc);
   L.rope = take(sizeof(float) * 2 * (size_t)L.rope_len * (c->head_dim / 2));
-  const size_t kv_slow = (size_t)c->n_layers_slow * c->n_heads_kv * c->max_len * c->head_dim * 2;
+  const size_t kv_slow = (size_t)c->n_layers_slow * B * c->n_heads_kv * c->max_len * c->head_dim * 2;
   L.ks = take(kv_slow);
   L.vs = take(kv_slow);
-  const size_t kv_fast = has_fast(c) ? (size_t)c->n_layers_fast * c->n_heads_kv * L.fast_len * c->head_dim * 2 : 0;
+  const size_t kv_fast =
+      has_fast(c) ? (size_t)c->n_layers_fast * B * c->n_heads_kv * L.fast_len * c->head_dim * 2 : 0;
   L.kf = take(kv_fast);
   L.vf = take(kv_fast);
   const size_t R = kPrefillRows;
@@ -132,6 +139,24 @@ Layout make_layout(const dar_config* c) {
   L.pgp = take(sizeof(float) * L.pgp_floats);
   L.patt = take(sizeof(float) * attn_partial_floats((int)R, c->n_heads_kv, L.nsplit_slow, g, c->head_dim));
   L.ppos = take(sizeof(int) * 4);
+  if (B > 1) {
+    for (int ch = 0; ch < 2; ++ch) {
+      const int M = (ch == 0 ? 1 : 2) * B;
+      L.bqkv[ch] = take(sizeof(float) * (size_t)M * qkv_rows);
+      L.bh3[ch] = take(sizeof(float) * (size_t)M * F);
+      L.bxh[ch] = take(2 * (size_t)gemm_mpad(M) * kmax);
+      L.bxl[ch] = take(2 * (size_t)gemm_mpad(M) * kmax);
+      L.bgp_floats[ch] = 0;
+      for (int N : {d, qkv_rows, F, c->vocab_c0, has_fast(c) ? c->vocab_res : 1}) {
+        const int gx = (N + 127) / 128;
+        const int splits = std::min(16, (256 + gx - 1) / gx);
+        L.bgp_floats[ch] = std::max(L.bgp_floats[ch], (size_t)splits * M * N);
+      }
+      L.bgp[ch] = take(sizeof(float) * L.bgp_floats[ch]);
+    }
+    // sequence ids [B], first-pass positions and sequences [2B], pass positions [R+1][B]
+    L.rows = take(sizeof(int) * (size_t)(B + 4 * B + (c->n_res + 1) * B));
+  }
   L.total = off;
   return L;
 }
@@ -169,7 +194,7 @@ int validate_config(const dar_config* c, std::string& why) {
   if (c->d_model % 256 || c->ffn_dim % 256 || qw % 256) return unsup("d_model, ffn_dim, n_heads_q*head_dim must be multiples of 256");
   if (c->d_model > 16384 || c->ffn_dim > 16384 || qw > 16384) return unsup("widths above 16384");
   if (c->n_res > 15) return unsup("n_res above 15");
-  if (c->max_batch != 1) return unsup("max_batch must be 1 in this version");
+  if (c->max_batch > kPrefillRows / 2) return unsup("max_batch above 64");
   if (c->max_len > (1 << 24)) return unsup("max_len above 2^24");
   return DAR_OK;
 }
@@ -246,6 +271,12 @@ struct dar_ctx {
   float *ht, *logits0, *flogits;
   unsigned long long *slots0, *slotsf;
   int *pred, *committed, *forced, *flags, *pos_s, *pos_f, *seqpos, *ring;
+  int B = 1;                   // sequences decoded in lockstep
+  float *bqkv[2], *bh3[2], *bgp[2];
+  uint16_t *bxh[2], *bxl[2];
+  int *seq_ident, *p1_pos, *p1_seq, *pk_pos;
+  std::vector<int> pos_hb;     // host mirror of each sequence's next slow position
+  std::vector<int> pos_init;   // host staging of the positions set by a prefill
   float2* rope;
   uint16_t *ks, *vs, *kf, *vf;
 
@@ -518,6 +549,217 @@ std::vector<TaskRec> fast_chain(dar_ctx* c) {
   return out;
 }
 
+// ---- batched decode (max_batch > 1): every stage runs the chain's rows at
+// once (one per sequence; two per sequence in the fast AR's first pass), the
+// projections as MFMA GEMMs over the rows.
+
+Task t_norm(const float* x, int x_stride, int M, int K, const void* gain, float eps, uint16_t* xh, uint16_t* xl,
+            float* out_f32 = nullptr) {
+  Task t = none_task();
+  t.kind = T_NORM_SPLIT;
+  t.M = M;
+  t.norm = NormSplitArgs{x, x_stride, M, K, static_cast<const uint16_t*>(gain), eps, xh, xl, out_f32};
+  return t;
+}
+
+Task t_gemm(int wtype, const void* W, const float* scale, int N, int K, int M, const uint16_t* xh,
+            const uint16_t* xl, float* y, int y_stride, int acc, float* part, size_t cap) {
+  Task t = none_task();
+  t.kind = T_GEMM;
+  t.M = M;
+  GemmArgs& g = t.gemm.g;
+  g.W = W;
+  g.scale = wtype == W_FP8 ? scale : nullptr;
+  g.N = N;
+  g.K = K;
+  g.M = M;
+  g.xh = xh;
+  g.xl = xl;
+  g.y = y;
+  g.y_stride = y_stride;
+  g.accumulate = acc;
+  g.part = part;
+  t.gemm.wtype = wtype;
+  t.gemm.part_cap = cap;
+  return t;
+}
+
+// One decoder layer over the chain's M rows: row m is at position row_pos[m]
+// of sequence row_seq[m]'s caches (kc/vc: this layer's caches of sequence 0,
+// seq_stride elements apart).
+void add_layer_rows(dar_ctx* c, std::vector<TaskRec>& out, int ch, const dar_layer_weights& w, int tag, int M,
+                    const int* row_pos, const int* row_seq, uint16_t* kc, uint16_t* vc, int cache_len,
+                    long long seq_stride, int nsplit_max) {
+  const dar_config& g = c->cfg;
+  const int d = g.d_model, qw = g.n_heads_q * g.head_dim, F = g.ffn_dim;
+  const int qkv_rows = (g.n_heads_q + 2 * g.n_heads_kv) * g.head_dim;
+  const int wt = c->fp8 ? W_FP8 : W_BF16;
+  const Chain& cn = ch == 0 ? c->cs : c->cf;
+  uint16_t *xh = c->bxh[ch], *xl = c->bxl[ch];
+  float* gp = c->bgp[ch];
+  const size_t cap = c->L.bgp_floats[ch];
+  out.push_back(rec(t_norm(cn.x, d, M, d, w.attn_norm, g.rms_eps, xh, xl), K_OTHER, tag));
+  out.push_back(rec(t_gemm(wt, w.wqkv, w.wqkv_scale, qkv_rows, d, M, xh, xl, c->bqkv[ch], qkv_rows, 0, gp, cap),
+                    K_QKV, tag));
+  Task t = none_task();
+  t.kind = T_ROPE_ROWS;
+  t.M = M;
+  t.rope = RopeRowsArgs{c->bqkv[ch], M, row_pos, row_seq, seq_stride, g.n_heads_q, g.n_heads_kv, g.head_dim,
+                        c->rope, cn.q, kc, vc, cache_len};
+  out.push_back(rec(t, K_OTHER, tag));
+  t = none_task();
+  t.kind = T_ATTN;
+  t.M = M;
+  AttnArgs& aa = t.attn;
+  aa.q = cn.q;
+  aa.q_stride = qw;
+  aa.K = kc;
+  aa.V = vc;
+  aa.cache_len = cache_len;
+  aa.pos = row_pos;
+  aa.n_heads_q = g.n_heads_q;
+  aa.n_heads_kv = g.n_heads_kv;
+  aa.head_dim = g.head_dim;
+  aa.chunk = c->L.chunk;
+  aa.nsplit_max = nsplit_max;
+  aa.M = M;
+  aa.part = cn.part;
+  aa.out = cn.o;
+  aa.out_stride = qw;
+  aa.row_pos = row_pos;
+  aa.row_seq = row_seq;
+  aa.seq_stride = seq_stride;
+  out.push_back(rec(t, K_ATTN, tag));
+  if (nsplit_max > 1) {
+    t.kind = T_COMBINE;
+    out.push_back(rec(t, K_ATTN, tag));
+  }
+  out.push_back(rec(t_norm(cn.o, qw, M, qw, nullptr, 0.f, xh, xl), K_OTHER, tag));
+  out.push_back(rec(t_gemm(wt, w.wo, w.wo_scale, d, qw, M, xh, xl, cn.x, d, 1, gp, cap), K_WO, tag));
+  out.push_back(rec(t_norm(cn.x, d, M, d, w.ffn_norm, g.rms_eps, xh, xl), K_OTHER, tag));
+  out.push_back(rec(t_gemm(wt, w.w1, w.w1_scale, F, d, M, xh, xl, cn.h, F, 0, gp, cap), K_W13, tag));
+  out.push_back(rec(t_gemm(wt, w.w3, w.w3_scale, F, d, M, xh, xl, c->bh3[ch], F, 0, gp, cap), K_W13, tag));
+  t = none_task();
+  t.kind = T_SILU_SPLIT;
+  t.M = M;
+  t.silu = SiluSplitArgs{cn.h, c->bh3[ch], M, F, xh, xl};
+  out.push_back(rec(t, K_OTHER, tag));
+  out.push_back(rec(t_gemm(wt, w.w2, w.w2_scale, d, F, M, xh, xl, cn.x, d, 1, gp, cap), K_W2, tag));
+}
+
+// Batched slow chain: the slow layers for every sequence at its position, the
+// final norm (h_t kept in fp32) and the codebook-0 head GEMM, then the slow
+// positions advance.
+std::vector<TaskRec> slow_chain_rows(dar_ctx* c) {
+  const dar_config& g = c->cfg;
+  const int B = c->B, d = g.d_model;
+  std::vector<TaskRec> out;
+  const long long seq_stride = (long long)g.n_heads_kv * g.max_len * g.head_dim;
+  for (int l = 0; l < g.n_layers_slow; ++l)
+    add_layer_rows(c, out, 0, c->slow[l], l, B, c->pos_s, c->seq_ident, c->ks + (size_t)l * B * seq_stride,
+                   c->vs + (size_t)l * B * seq_stride, g.max_len, seq_stride, c->L.nsplit_slow);
+  out.push_back(rec(t_norm(c->cs.x, d, B, d, c->slow_fn, g.rms_eps, c->bxh[0], c->bxl[0], c->ht), K_OTHER, 0));
+  out.push_back(rec(t_gemm(W_BF16, c->w0, nullptr, g.vocab_c0, d, B, c->bxh[0], c->bxl[0], c->logits0, g.vocab_c0, 0,
+                           c->bgp[0], c->L.bgp_floats[0]),
+                    K_HEAD, 0));
+  Task t = none_task();
+  t.kind = T_INC_ROWS;
+  t.inc = IncRowsArgs{c->pos_s, B};
+  out.push_back(rec(t, K_OTHER, 0));
+  return out;
+}
+
+RowsCommitArgs rows_commit(dar_ctx* c, int k, const float* logits, int ld, int V) {
+  const dar_config& g = c->cfg;
+  RowsCommitArgs r{};
+  r.logits = logits;
+  r.ld = ld;
+  r.V = V;
+  r.B = c->B;
+  r.code_index = k;
+  r.frame_codes = frame_codes(&g);
+  r.pred = c->pred;
+  r.committed = c->committed;
+  r.forced = c->forced;
+  r.force_flag = c->flags + 0;
+  r.ring = c->ring;
+  r.pos = c->pos_f;
+  r.K = g.d_model;
+  r.anomalies = c->flags + 1;
+  return r;
+}
+
+// Batched commit of codebook 0: codes, the next slow inputs W0[c0], the fast
+// inputs [h_t, E0[c0]] (rows 2b, 2b + 1) and the frame's codebook-0 logits.
+std::vector<TaskRec> commit0_chain_rows(dar_ctx* c) {
+  const dar_config& g = c->cfg;
+  const int d = g.d_model, fc = frame_codes(&g);
+  const bool fast = has_fast(&g);
+  Task t = none_task();
+  t.kind = T_COMMIT_ROWS;
+  RowsCommitArgs& r = t.rows;
+  r = rows_commit(c, 0, c->logits0, g.vocab_c0, g.vocab_c0);
+  r.pos_inc = fast ? nullptr : c->pos_f;
+  r.next_table = fast ? c->fast_emb[0] : nullptr;
+  r.next_rows = g.vocab_c0;
+  r.next_x = c->cf.x + d;
+  r.next_stride = 2 * d;
+  r.slow_table = c->w0;
+  r.slow_rows = g.vocab_c0;
+  r.slow_x = c->cs.x;
+  if (fast) {
+    r.copy_src[0] = c->ht;
+    r.copy_dst[0] = c->cf.x;
+    r.copy_src_stride[0] = d;
+    r.copy_dst_stride[0] = 2 * d;
+    r.copy_n[0] = d;
+  }
+  r.copy_src[1] = c->logits0;
+  r.copy_dst[1] = c->flogits;
+  r.copy_src_stride[1] = g.vocab_c0;
+  r.copy_dst_stride[1] = fc * c->L.vmax;
+  r.copy_n[1] = g.vocab_c0;
+  return {rec(t, K_OTHER, 0)};
+}
+
+// Batched fast AR: pass 1 over 2B rows (positions 0 and 1 of every
+// sequence), passes 2..R over B rows, each followed by the head GEMM and the
+// commit of c_k for every sequence.
+std::vector<TaskRec> fast_chain_rows(dar_ctx* c) {
+  const dar_config& g = c->cfg;
+  const int B = c->B, d = g.d_model, fc = frame_codes(&g);
+  std::vector<TaskRec> out;
+  if (!has_fast(&g)) return out;
+  const long long seq_stride = (long long)g.n_heads_kv * c->L.fast_len * g.head_dim;
+  for (int k = 1; k <= g.n_res; ++k) {
+    const int M = k == 1 ? 2 * B : B;
+    const int* rp = k == 1 ? c->p1_pos : c->pk_pos + (size_t)k * B;
+    const int* rs = k == 1 ? c->p1_seq : c->seq_ident;
+    for (int l = 0; l < g.n_layers_fast; ++l)
+      add_layer_rows(c, out, 1, c->fast[l], 1000 * k + l, M, rp, rs, c->kf + (size_t)l * B * seq_stride,
+                     c->vf + (size_t)l * B * seq_stride, c->L.fast_len, seq_stride, 1);
+    // head on each sequence's last row
+    out.push_back(rec(t_norm(c->cf.x + (k == 1 ? d : 0), k == 1 ? 2 * d : d, B, d, c->fast_fn, g.rms_eps, c->bxh[1],
+                             c->bxl[1]),
+                      K_OTHER, k));
+    out.push_back(rec(t_gemm(c->fp8 ? W_FP8 : W_BF16, c->fast_head, c->fast_head_scale, g.vocab_res, d, B, c->bxh[1],
+                             c->bxl[1], c->flogits + (size_t)k * c->L.vmax, fc * c->L.vmax, 0, c->bgp[1],
+                             c->L.bgp_floats[1]),
+                      K_HEAD, k));
+    Task t = none_task();
+    t.kind = T_COMMIT_ROWS;
+    RowsCommitArgs& r = t.rows;
+    r = rows_commit(c, k, c->flogits + (size_t)k * c->L.vmax, fc * c->L.vmax, g.vocab_res);
+    r.pos_inc = k == g.n_res ? c->pos_f : nullptr;
+    r.next_table = k < g.n_res ? c->fast_emb[k] : nullptr;
+    r.next_rows = g.vocab_res;
+    r.next_x = c->cf.x;
+    r.next_stride = d;
+    out.push_back(rec(t, K_OTHER, k));
+  }
+  return out;
+}
+
 void plan_single(Plan& p, const std::vector<TaskRec>& chain) {
   for (const TaskRec& r : chain) {
     p.tasks.push_back(r.t);
@@ -592,13 +834,13 @@ int run_plan(dar_ctx* c, Plan& p, hipStream_t s, const char* what) {
 
 int copy_outputs(dar_ctx* c, hipStream_t s, int32_t* codes_out, float* logits_out) {
   const dar_config& g = c->cfg;
-  if (codes_out) DAR_HIP(c, launch_copy_i32(c->pred, codes_out, frame_codes(&g), s), "copy codes");
+  const size_t fc = frame_codes(&g);
+  if (codes_out) DAR_HIP(c, launch_copy_i32(c->pred, codes_out, (int)fc * c->B, s), "copy codes");
   if (logits_out) {
-    const size_t fc = frame_codes(&g);
-    for (size_t k = 0; k < fc; ++k) {
-      const int V = (k == 0) ? g.vocab_c0 : g.vocab_res;
+    for (size_t r = 0; r < fc * c->B; ++r) {
+      const int V = (r % fc == 0) ? g.vocab_c0 : g.vocab_res;
       DAR_HIP(c,
-              hipMemcpyAsync(logits_out + k * c->L.vmax, c->flogits + k * c->L.vmax, sizeof(float) * V,
+              hipMemcpyAsync(logits_out + r * c->L.vmax, c->flogits + r * c->L.vmax, sizeof(float) * V,
                              hipMemcpyDeviceToDevice, s),
               "copy logits");
     }
@@ -607,7 +849,7 @@ int copy_outputs(dar_ctx* c, hipStream_t s, int32_t* codes_out, float* logits_ou
 }
 
 int set_force(dar_ctx* c, hipStream_t s, const int32_t* forced) {
-  const int fc = frame_codes(&c->cfg);
+  const int fc = frame_codes(&c->cfg) * c->B;
   if (forced) {
     DAR_HIP(c, launch_set_forced(forced, fc, c->forced, c->flags + 0, s), "set forced");
     c->force_dev = true;
@@ -652,7 +894,7 @@ int pipeline_step(dar_ctx* c, const int32_t* forced, int32_t* codes_out, float* 
 // once per block), attention is causal over the cache (earlier blocks) and the
 // block itself. Then the codebook-0 head on the last position, which leaves
 // pos_s = n; frame 0 sits at position n - 1.
-int prefill_blocks(dar_ctx* c, const int32_t* tokens, int n, hipStream_t s) {
+int prefill_blocks(dar_ctx* c, const int32_t* tokens, int n, hipStream_t s, int seq) {
   const dar_config& g = c->cfg;
   const Layout& L = c->L;
   const int d = g.d_model, qw = g.n_heads_q * g.head_dim, F = g.ffn_dim;
@@ -692,8 +934,8 @@ int prefill_blocks(dar_ctx* c, const int32_t* tokens, int n, hipStream_t s) {
     DAR_HIP(c, launch_fill_i32(ppos, 1, p0, s), "prefill position");
     for (int l = 0; l < g.n_layers_slow; ++l) {
       const dar_layer_weights& w = c->slow[l];
-      uint16_t* kc = c->ks + l * per_layer;
-      uint16_t* vc = c->vs + l * per_layer;
+      uint16_t* kc = c->ks + ((size_t)l * c->B + seq) * per_layer;  // layer l of sequence seq
+      uint16_t* vc = c->vs + ((size_t)l * c->B + seq) * per_layer;
       DAR_HIP(c, launch_norm_split(px, d, M, d, static_cast<const uint16_t*>(w.attn_norm), g.rms_eps, xh, xl, s),
               "prefill attn norm");
       DAR_HIP(c, gemm(w.wqkv, w.wqkv_scale, qkv_rows, d, M, pqkv, 0), "prefill qkv");
@@ -733,12 +975,10 @@ int prefill_blocks(dar_ctx* c, const int32_t* tokens, int n, hipStream_t s) {
       DAR_HIP(c, gemm(w.w2, w.w2_scale, d, F, M, px, 1), "prefill w2");
     }
   }
-  // codebook-0 head on position n - 1 (moves pos_s to n)
-  DAR_HIP(c, launch_fill_i32(c->pos_s, 1, n - 1, s), "prefill head position");
-  Task t = c->p_slow.tasks.back();
-  t.head.x = px + (size_t)(M - 1) * d;
-  DAR_HIP(c, launch_task(wt, t, s), "prefill head");
-  DAR_HIP(c, launch_fill_i32(c->pos_f, 1, n - 1, s), "set frame position");
+  // the last position's residual becomes the sequence's slow row (the head's input)
+  DAR_HIP(c, hipMemcpyAsync(c->cs.x + (size_t)seq * d, px + (size_t)(M - 1) * d, sizeof(float) * d,
+                            hipMemcpyDeviceToDevice, s),
+          "prefill last row");
   return DAR_OK;
 }
 
@@ -858,8 +1098,23 @@ int dar_create(const dar_config* cfg, const dar_weights* w, void* workspace, siz
   c->committed = reinterpret_cast<int*>(b + L.committed);
   c->forced = reinterpret_cast<int*>(b + L.forced);
   c->flags = reinterpret_cast<int*>(b + L.flags);
+  c->B = cfg->max_batch;
+  c->pos_hb.assign(c->B, 0);
   c->pos_s = reinterpret_cast<int*>(b + L.pos);
-  c->pos_f = c->pos_s + 1;
+  c->pos_f = c->pos_s + c->B;
+  if (c->B > 1) {
+    for (int ch = 0; ch < 2; ++ch) {
+      c->bqkv[ch] = reinterpret_cast<float*>(b + L.bqkv[ch]);
+      c->bh3[ch] = reinterpret_cast<float*>(b + L.bh3[ch]);
+      c->bgp[ch] = reinterpret_cast<float*>(b + L.bgp[ch]);
+      c->bxh[ch] = reinterpret_cast<uint16_t*>(b + L.bxh[ch]);
+      c->bxl[ch] = reinterpret_cast<uint16_t*>(b + L.bxl[ch]);
+    }
+    c->seq_ident = reinterpret_cast<int*>(b + L.rows);
+    c->p1_pos = c->seq_ident + c->B;
+    c->p1_seq = c->p1_pos + 2 * c->B;
+    c->pk_pos = c->p1_seq + 2 * c->B;
+  }
   c->seqpos = reinterpret_cast<int*>(b + L.seqpos);
   c->ring = reinterpret_cast<int*>(b + L.ring);
   c->rope = reinterpret_cast<float2*>(b + L.rope);
@@ -870,9 +1125,15 @@ int dar_create(const dar_config* cfg, const dar_weights* w, void* workspace, siz
 
   // launch plans: commit of codebook 0, the fast AR, the slow step with its
   // codebook-0 head, and the slow step alone (prompt positions before the last)
-  plan_single(c->p_c0, commit0_chain(c));
-  plan_single(c->p_fast, fast_chain(c));
-  plan_single(c->p_slow, slow_chain(c, true));
+  if (c->B == 1) {
+    plan_single(c->p_c0, commit0_chain(c));
+    plan_single(c->p_fast, fast_chain(c));
+    plan_single(c->p_slow, slow_chain(c, true));
+  } else {
+    plan_single(c->p_c0, commit0_chain_rows(c));
+    plan_single(c->p_fast, fast_chain_rows(c));
+    plan_single(c->p_slow, slow_chain_rows(c));
+  }
 
   auto fail = [&](hipError_t e, const char* what) {
     g_create_error = std::string(what) + ": " + hipGetErrorString(e);
@@ -900,6 +1161,17 @@ int dar_create(const dar_config* cfg, const dar_weights* w, void* workspace, siz
   }
   std::vector<int> seq(L.seq_len);
   for (int i = 0; i < L.seq_len; ++i) seq[i] = i;
+  // batched rows: sequence ids, first fast pass (positions 0, 1 of each
+  // sequence), later passes (position k of each sequence)
+  std::vector<int> rows;
+  if (c->B > 1) {
+    const int B = c->B;
+    for (int i = 0; i < B; ++i) rows.push_back(i);
+    for (int i = 0; i < 2 * B; ++i) rows.push_back(i % 2);
+    for (int i = 0; i < 2 * B; ++i) rows.push_back(i / 2);
+    for (int k = 0; k <= cfg->n_res; ++k)
+      for (int i = 0; i < B; ++i) rows.push_back(k);
+  }
   // zero everything from the activations to the ring (slots, flags, positions included)
   const size_t zero_words = L.rope / 4;
   if ((e = launch_fill_u32(reinterpret_cast<unsigned*>(b), zero_words, c->stream)) != hipSuccess)
@@ -910,6 +1182,9 @@ int dar_create(const dar_config* cfg, const dar_weights* w, void* workspace, siz
   if ((e = hipMemcpyAsync(c->seqpos, seq.data(), seq.size() * sizeof(int), hipMemcpyHostToDevice, c->stream)) !=
       hipSuccess)
     return fail(e, "upload positions");
+  if (!rows.empty() && (e = hipMemcpyAsync(c->seq_ident, rows.data(), rows.size() * sizeof(int),
+                                           hipMemcpyHostToDevice, c->stream)) != hipSuccess)
+    return fail(e, "upload rows");
   if ((e = hipStreamSynchronize(c->stream)) != hipSuccess) return fail(e, "synchronize create");
   if ((e = hipEventRecord(c->ev_s_done, c->cs.s)) != hipSuccess) return fail(e, "record event");
   if ((e = hipEventRecord(c->ev_f_done, c->cf.s)) != hipSuccess) return fail(e, "record event");
@@ -932,23 +1207,49 @@ int dar_prefill(dar_ctx* c, int32_t batch, const int32_t* tokens, const int32_t*
     c->err = "batch above max_batch";
     return DAR_E_CAPACITY;
   }
-  const int n = lens_host[0];
-  if (n < 1 || n >= c->cfg.max_len) {
-    c->err = "prompt length must be in [1, max_len)";
-    return n < 1 ? DAR_E_INVAL : DAR_E_CAPACITY;
+  if (batch != c->B) {
+    c->err = c->B == 1 ? "batch must be 1" : "batch must equal max_batch (sequences decode in lockstep)";
+    return DAR_E_INVAL;
+  }
+  int nmax = 0;
+  for (int b = 0; b < batch; ++b) {
+    const int n = lens_host[b];
+    if (n < 1 || n >= c->cfg.max_len) {
+      c->err = "prompt length must be in [1, max_len)";
+      return n < 1 ? DAR_E_INVAL : DAR_E_CAPACITY;
+    }
+    nmax = std::max(nmax, n);
   }
   c->prefilled = false;
   hipStream_t s = c->cs.s;
-  // the slow stream runs the prompt after anything already queued
+  const int wt = c->fp8 ? W_FP8 : W_BF16;
+  // the slow stream runs the prompts after anything already queued
   DAR_HIP(c, hipEventRecord(c->ev_start, c->stream), "record start");
   DAR_HIP(c, hipStreamWaitEvent(s, c->ev_start, 0), "wait start");
   DAR_HIP(c, hipStreamWaitEvent(s, c->ev_f_done, 0), "wait fast chain");
-  const int st0 = prefill_blocks(c, tokens, n, s);
-  if (st0 != DAR_OK) return st0;
+  size_t off = 0;
+  for (int b = 0; b < batch; ++b) {
+    const int st0 = prefill_blocks(c, tokens + off, lens_host[b], s, b);
+    if (st0 != DAR_OK) return st0;
+    off += lens_host[b];
+  }
+  // codebook-0 head on each sequence's last position (moves pos_s to the
+  // prompt length); frame 0 sits at the last prompt position
+  c->pos_init.assign(2 * c->B, 0);
+  for (int b = 0; b < batch; ++b) c->pos_init[b] = c->pos_init[c->B + b] = lens_host[b] - 1;
+  DAR_HIP(c, hipMemcpyAsync(c->pos_s, c->pos_init.data(), sizeof(int) * 2 * c->B, hipMemcpyHostToDevice, s),
+          "prefill positions");
+  if (c->B == 1) {
+    DAR_HIP(c, launch_task(wt, c->p_slow.tasks.back(), s), "prefill head");
+  } else {
+    const size_t nt = c->p_slow.tasks.size();
+    for (size_t i = nt - 3; i < nt; ++i) DAR_HIP(c, launch_task(wt, c->p_slow.tasks[i], s), "prefill head");
+  }
   DAR_HIP(c, hipEventRecord(c->ev_s_done, s), "record slow done");
-  const int st = pipeline_step(c, forced, codes_out, logits_out, n < c->cfg.max_len);
+  const int st = pipeline_step(c, forced, codes_out, logits_out, nmax < c->cfg.max_len);
   if (st != DAR_OK) return st;
-  c->pos_host = n;
+  for (int b = 0; b < batch; ++b) c->pos_hb[b] = lens_host[b];
+  c->pos_host = nmax;
   c->prefilled = true;
   return DAR_OK;
 }
@@ -966,6 +1267,7 @@ int dar_decode_frame(dar_ctx* c, const int32_t* forced, int32_t* codes_out, floa
   const int st = pipeline_step(c, forced, codes_out, logits_out, c->pos_host + 1 < c->cfg.max_len);
   if (st != DAR_OK) return st;
   c->pos_host += 1;
+  for (int& p : c->pos_hb) p += 1;
   return DAR_OK;
 }
 
@@ -989,13 +1291,14 @@ int dar_reset(dar_ctx* c) {
   if (!c) return DAR_E_INVAL;
   DAR_HIP(c, launch_fill_i32(c->flags + 1, 1, 0, c->stream), "reset counters");
   c->pos_host = 0;
+  std::fill(c->pos_hb.begin(), c->pos_hb.end(), 0);
   c->prefilled = false;
   return DAR_OK;
 }
 
 int dar_position(const dar_ctx* c, int32_t* pos_out) {
   if (!c || !pos_out) return DAR_E_INVAL;
-  pos_out[0] = c->pos_host;
+  for (int b = 0; b < c->B; ++b) pos_out[b] = c->pos_hb[b];
   return DAR_OK;
 }
 
@@ -1012,7 +1315,7 @@ int dar_codes(dar_ctx* c, int32_t first, int32_t count, int32_t* dst) {
     return DAR_E_INVAL;
   }
   if (count == 0) return DAR_OK;
-  const int fc = frame_codes(&c->cfg);
+  const int fc = frame_codes(&c->cfg) * c->B;
   DAR_HIP(c, launch_copy_i32(c->ring + (size_t)first * fc, dst, count * fc, c->stream), "copy ring");
   return DAR_OK;
 }

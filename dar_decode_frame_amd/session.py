@@ -93,14 +93,20 @@ class DeviceWeights:
 
 
 class DarSession:
-    """One dar_ctx: workspace, stream, prefill and frame decode with torch tensors."""
+    """One dar_ctx: workspace, stream, prefill and frame decode with torch tensors.
 
-    def __init__(self, dims, weights: DeviceWeights, max_len: int, device="cuda", stream=None, graph=False):
+    batch > 1 decodes that many sequences in lockstep: prefill takes one
+    prompt per sequence, frames and forced codes are [batch][1 + n_res], logits
+    [batch][1 + n_res][vmax]. With batch 1 the leading axis is dropped."""
+
+    def __init__(self, dims, weights: DeviceWeights, max_len: int, device="cuda", stream=None, graph=False,
+                 batch=1):
         self.dims = dims
         self.max_len = max_len
         self.device = device
+        self.batch = batch
         self.stream = stream if stream is not None else torch.cuda.Stream(device)
-        self.cfg = N.make_config(dims, max_len, weights.wtype)
+        self.cfg = N.make_config(dims, max_len, weights.wtype, max_batch=batch)
         nbytes = N.dar_workspace_bytes(self.cfg)
         self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
         self.weights = weights
@@ -110,9 +116,9 @@ class DarSession:
         N.dar_set_graph(self.ctx, graph)
         self.fc = dims.n_res + 1
         self.vmax = max(dims.vocab_c0, dims.vocab_res if dims.n_res > 0 else 0)
-        self.codes = torch.zeros(self.fc, dtype=torch.int32, device=device)
-        self.logits = torch.zeros(self.fc, self.vmax, dtype=torch.float32, device=device)
-        self.forced = torch.zeros(self.fc, dtype=torch.int32, device=device)
+        self.codes = torch.zeros(batch, self.fc, dtype=torch.int32, device=device)
+        self.logits = torch.zeros(batch, self.fc, self.vmax, dtype=torch.float32, device=device)
+        self.forced = torch.zeros(batch, self.fc, dtype=torch.int32, device=device)
 
     def close(self):
         if self.ctx:
@@ -128,16 +134,18 @@ class DarSession:
     def _forced_ptr(self, forced):
         if forced is None:
             return None
-        f = torch.as_tensor(np.asarray(forced, dtype=np.int32))
+        f = torch.as_tensor(np.asarray(forced, dtype=np.int32).reshape(self.batch, self.fc))
         with torch.cuda.stream(self.stream):
             self.forced.copy_(f.to(self.device, non_blocking=False))
         return _dev(self.forced)
 
     def prefill(self, tokens, forced=None, want=True):
-        toks = torch.as_tensor(np.asarray(tokens, dtype=np.int32)).to(self.device)
+        prompts = [tokens] if self.batch == 1 else list(tokens)
+        lens = [len(p) for p in prompts]
+        toks = torch.as_tensor(np.concatenate([np.asarray(p, dtype=np.int32) for p in prompts])).to(self.device)
         torch.cuda.current_stream(self.device).synchronize()
         fp = self._forced_ptr(forced)
-        N.dar_prefill(self.ctx, 1, _dev(toks), [len(tokens)], fp, _dev(self.codes) if want else None,
+        N.dar_prefill(self.ctx, self.batch, _dev(toks), lens, fp, _dev(self.codes) if want else None,
                       _dev(self.logits) if want else None)
         self._toks = toks
         return self._out(want)
@@ -151,16 +159,19 @@ class DarSession:
         if not want:
             return None
         self.stream.synchronize()
-        return self.codes.cpu().numpy().copy(), self.logits.cpu().numpy().copy()
+        codes, logits = self.codes.cpu().numpy().copy(), self.logits.cpu().numpy().copy()
+        return (codes[0], logits[0]) if self.batch == 1 else (codes, logits)
 
     def ring(self, first, count):
-        dst = torch.zeros(count, self.fc, dtype=torch.int32, device=self.device)
+        dst = torch.zeros(count, self.batch, self.fc, dtype=torch.int32, device=self.device)
         N.dar_codes(self.ctx, first, count, _dev(dst))
         self.stream.synchronize()
-        return dst.cpu().numpy()
+        out = dst.cpu().numpy()
+        return out[:, 0] if self.batch == 1 else out
 
     def position(self):
-        return N.dar_position(self.ctx)[0]
+        pos = N.dar_position(self.ctx, self.batch)
+        return pos[0] if self.batch == 1 else list(pos)
 
     def reset(self):
         N.dar_reset(self.ctx)

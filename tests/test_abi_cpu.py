@@ -52,7 +52,7 @@ def _cfg(N, **kw):
 
 
 @pytest.mark.parametrize("field,value,status", [
-    ("head_dim", 96, -6), ("n_heads_kv", 3, -1), ("d_model", 200, -6), ("max_batch", 4, -6),
+    ("head_dim", 96, -6), ("n_heads_kv", 3, -1), ("d_model", 200, -6), ("max_batch", 65, -6), ("max_batch", 0, -1),
     ("max_len", 1, -1), ("rms_eps", 0.0, -1), ("rope_base", 1.0, -1), ("wtype", 7, -1),
     ("n_res", 16, -6), ("n_layers_slow", 0, -1), ("vocab_c0", 0, -1),
 ])

@@ -1,0 +1,124 @@
+"""Batched decode (several sequences in lockstep, ragged prompt lengths).
+
+Tiny Dual-AR (2 slow layers, 1 fast layer, d 256): each sequence of the batch
+is teacher-forced with its own oracle greedy frames and compared with its own
+oracle run (logits rel-L2, argmax agreement, exact codes above the margin),
+bf16 and fp8, at B = 4 and at the largest batch (64, whose first fast pass is
+a 128-row GEMM). At full shape (36 + 4 layers, d 2560): a batch of two equals
+two batch-1 contexts decoding the same prompts (same codes where the margin
+exceeds 1e-2, logits within the bf16 tolerance).
+"""
+import numpy as np
+import pytest
+
+import synth
+from oracle import OracleDecoder, OracleModel
+from parity import TOL, assert_parity, compare_frames
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def tiny_host():
+    d = synth.DIMS["tiny"]
+    return d, synth.gen_weights(d, 0)
+
+
+def _oracle_frames(model, prompt, frames, max_len):
+    dec = OracleDecoder(model, max_len)
+    out = [dec.prefill(prompt)]
+    for _ in range(frames):
+        out.append(dec.decode_frame())
+    return out
+
+
+@pytest.mark.parametrize("wtype,B,frames", [("bf16", 4, 20), ("fp8", 4, 20), ("bf16", 64, 2)])
+def test_tiny_batched_parity(tiny_host, wtype, B, frames):
+    from dar_decode_frame_amd.session import DarSession, DeviceWeights
+    dims, host = tiny_host
+    max_len = 48
+    rng = np.random.default_rng(7)
+    lens = [int(x) for x in rng.integers(4, 24, B)]
+    prompts = [synth.gen_prompt(n, dims.vocab_c0, 100 + b) for b, n in enumerate(lens)]
+    model = OracleModel(dims, host, wtype=wtype)
+    refs = [_oracle_frames(model, p, frames, max_len) for p in prompts]
+    sess = DarSession(dims, DeviceWeights(dims, host, wtype), max_len, batch=B)
+    forced = [np.stack([refs[b][i][0] for b in range(B)]) for i in range(frames + 1)]
+    got = [sess.prefill(prompts, forced=forced[0])]
+    for i in range(1, frames + 1):
+        got.append(sess.decode_frame(forced=forced[i]))
+    stats_all = {"max_rel": 0.0, "agree": 0.0, "n": 0, "exact_fail": [], "tol": TOL[wtype]}
+    for b in range(B):
+        gb = [(codes[b], logits[b]) for codes, logits in got]
+        st = compare_frames(gb, refs[b], dims, wtype)
+        stats_all["max_rel"] = max(stats_all["max_rel"], st["max_rel"])
+        stats_all["agree"] += st["agree"] * st["n"]
+        stats_all["n"] += st["n"]
+        stats_all["exact_fail"] += [(b,) + e for e in st["exact_fail"]]
+    stats_all["agree"] /= stats_all["n"]
+    print(f"\n{wtype} B={B}: {stats_all}")
+    assert_parity(stats_all)
+    assert sess.position() == [n + frames for n in lens]
+    ring = sess.ring(0, max_len)
+    for b in range(B):
+        for i in range(frames + 1):
+            assert np.array_equal(ring[lens[b] - 1 + i, b], forced[i][b])
+    assert sess.nonfinite() == 0
+    sess.close()
+
+
+def test_batched_capacity_and_errors(tiny_host):
+    from dar_decode_frame_amd import native as N
+    from dar_decode_frame_amd.session import DarSession, DeviceWeights
+    dims, host = tiny_host
+    sess = DarSession(dims, DeviceWeights(dims, host, "bf16"), 16, batch=3)
+    # the batch decodes in lockstep: a prefill must bring one prompt per sequence
+    with pytest.raises(N.DarError) as e:
+        N.dar_prefill(sess.ctx, 2, 0, [4, 5], None, None, None)
+    assert e.value.status == N.DAR_E_INVAL
+    prompts = [synth.gen_prompt(n, dims.vocab_c0, n) for n in (3, 9, 14)]
+    sess.prefill(prompts, want=False)   # frame 0 at positions 2, 8, 13
+    sess.decode_frame(want=False)       # 3, 9, 14
+    sess.decode_frame(want=False)       # 4, 10, 15: the longest sequence reaches max_len - 1
+    assert sess.position() == [5, 11, 16]
+    with pytest.raises(N.DarError) as e:
+        sess.decode_frame(want=False)
+    assert e.value.status == N.DAR_E_CAPACITY
+    sess.close()
+
+
+def test_fullshape_batch_equals_single():
+    import torch
+
+    from dar_decode_frame_amd.session import DarSession, DeviceWeights
+    wl = synth.WORKLOADS["s2pro_dual_bf16"]
+    dims = wl.dims
+    host = synth.gen_weights(dims, wl.weight_seed)
+    dw = DeviceWeights(dims, host, "bf16")
+    del host
+    prompts = [synth.gen_prompt(n, dims.vocab_c0, 50 + n) for n in (128, 160)]
+    frames, max_len = 4, 256
+    single = []
+    for p in prompts:
+        s1 = DarSession(dims, dw, max_len)
+        out = [s1.prefill(p)]
+        for _ in range(frames):
+            out.append(s1.decode_frame())
+        single.append(out)
+        s1.close()
+    # the batch is forced with the single runs' own codes, so that a near-tie
+    # resolved differently cannot change the later inputs
+    forced = [np.stack([single[b][i][0] for b in range(2)]) for i in range(frames + 1)]
+    sb = DarSession(dims, dw, max_len, batch=2)
+    got = [sb.prefill(prompts, forced=forced[0])]
+    for i in range(1, frames + 1):
+        got.append(sb.decode_frame(forced=forced[i]))
+    sb.close()
+    for b in range(2):
+        gb = [(codes[b], logits[b]) for codes, logits in got]
+        st = compare_frames(gb, single[b], dims, "bf16")
+        print(f"\nsequence {b}: {st}")
+        assert st["max_rel"] <= TOL["bf16"], st
+        assert not st["exact_fail"], st
+    del dw
+    torch.cuda.empty_cache()
