@@ -59,7 +59,7 @@ def main():
     wl = synth.WORKLOADS[args.workload]
     dims = wl.dims
     if wl.batch != 1:
-        raise SystemExit("batched workloads are not part of this version")
+        return bench_batched(args, wl)
     max_steps = wl.max_len - wl.prefill_len
     if args.steps > max_steps or args.steps < 1:
         raise SystemExit(f"--steps must be in [1, {max_steps}] for {wl.name}")
@@ -194,6 +194,106 @@ def main():
         "cpu_baseline": cpu,
     }
     sess.close()
+    print(json.dumps(out), flush=True)
+
+
+def bench_batched(args, wl):
+    """Batched decode (the workload's sequences in lockstep, ragged prompts):
+    aggregate frames/s over --steps lockstep steps, algorithmic bytes = the
+    weights once per step + every sequence's KV reads, and the dominant
+    launch kind of serialised steps against HBM and its MFMA rate."""
+    import numpy as np
+    import torch
+
+    import synth
+    from dar_decode_frame_amd import bytes_model as bm
+    from dar_decode_frame_amd import native as N
+    from dar_decode_frame_amd.session import DarSession, DeviceWeights
+
+    dims, B = wl.dims, wl.batch
+    dev = torch.device("cuda:0")
+    lens, prompts = synth.gen_ragged_prompts(B, wl.prefill_len, wl.prefill_len_max, dims.vocab_c0, wl.prompt_seed,
+                                            wl.length_seed)
+    max_steps = wl.max_len - int(lens.max())
+    steps = min(args.steps, max_steps)
+    t0 = time.time()
+    host = synth.gen_weights(dims, wl.weight_seed)
+    weights = DeviceWeights(dims, host, wl.wtype, dev)
+    del host
+    log(f"weights ready in {time.time() - t0:.1f}s; {B} prompts of {int(lens.min())}..{int(lens.max())} ids")
+    sess = DarSession(dims, weights, wl.max_len, dev, graph=args.graph, batch=B)
+    stream = sess.stream
+    sess.prefill(prompts, want=False)
+    for _ in range(args.warmup):
+        sess.decode_frame(want=False)
+    stream.synchronize()
+    sess.reset()
+    ev_p0, ev_p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev_p0.record(stream)
+    sess.prefill(prompts, want=False)
+    ev_p1.record(stream)
+    stream.synchronize()
+    prefill_ms = ev_p0.elapsed_time(ev_p1)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(steps):
+        sess.decode_frame(want=False)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1)
+    fps = B * steps * 1000.0 / ms
+    # step i of sequence b attends T = lens[b] + 1 + i slow positions
+    weights_b = bm.slow_weight_bytes(dims, wl.wtype) + dims.n_res * bm.fast_pass_bytes(dims, wl.wtype)
+    kv = sum(bm.kv_bytes_per_position(dims) * (steps * (int(n) + 1) + steps * (steps - 1) // 2)
+             + steps * bm.fast_kv_bytes(dims) for n in lens)
+    alg_bytes = steps * weights_b + kv
+    gbs = alg_bytes / (ms / 1000.0)
+    log(f"timed {steps} steps x {B} sequences: {ms:.1f} ms, {fps:.1f} frames/s, {gbs / 1e9:.0f} GB/s")
+
+    roof = None
+    if args.profile_frames > 0:
+        sess.reset()
+        sess.prefill(prompts, want=False)
+        recs = []
+        for _ in range(args.profile_frames):
+            recs += sess.profile_frame()
+        totals = {}
+        for ms_k, kind, layer in recs:
+            totals[kind] = totals.get(kind, 0.0) + ms_k
+        share = {N.KIND_NAMES[k]: round(v / sum(totals.values()), 4)
+                 for k, v in sorted(totals.items(), key=lambda kv: -kv[1])}
+        gemm_kinds = [k for k in sorted(totals, key=totals.get, reverse=True) if N.KIND_NAMES[k] in ("w13", "w2", "wo",
+                                                                                                   "qkv")]
+        dom = gemm_kinds[0]
+        one_row = [m for m, kind, layer in recs if kind == dom and not (1000 <= layer < 2000)]
+        avg_ms = sum(one_row) / len(one_row)
+        name = N.KIND_NAMES[dom]
+        # w13 launches are W1 and W3 separately here (one matrix each)
+        per = per_launch_bytes(dims, wl.wtype, name) // (2 if name == "w13" else 1)
+        flops = 2 * 2 * B * per / (2 if wl.wtype == "bf16" else 1)  # inputs as hi + lo bf16: two MFMA passes
+        achieved = per / (avg_ms / 1000.0)
+        roof = {"kernel": name, "bound": "hbm", "achieved": round(achieved / 1e9, 1), "peak": HBM_PEAK / 1e9,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK, 4), "traffic": None, "bytes_per_launch": per,
+                "avg_launch_us": round(avg_ms * 1000, 2), "launches_timed": len(one_row),
+                "mfma_tflops": round(flops / (avg_ms / 1000.0) / 1e12, 1), "mfma_frac_bf16_dense": round(
+                    flops / (avg_ms / 1000.0) / 2.5e15, 4),
+                "launches_per_frame": len(recs) // args.profile_frames, "frame_time_share": share}
+        log(f"dominant GEMM {name}: {avg_ms * 1000:.1f} us/launch, {achieved / 1e9:.0f} GB/s; shares {share}")
+    n_bad = sess.nonfinite()
+    sess.close()
+    out = {
+        "metric": METRIC, "value": round(fps, 2), "unit": "frames/s", "n_gpus": 1, "steps": steps,
+        "warmup": args.warmup, "ms_per_step": round(ms / steps, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16" if wl.wtype == "bf16" else "fp8_e4m3",
+        "data": "synthetic (seeded random-init weights, ragged random prompts)",
+        "config": {"workload": wl.name, "batch": B, "prompt_lengths": [int(n) for n in lens], "max_len": wl.max_len,
+                   "layers_slow": dims.n_layers_slow, "layers_fast": dims.n_layers_fast,
+                   "residual_codebooks": dims.n_res, "graph": args.graph},
+        "achieved_gb_s": round(gbs / 1e9, 1), "hbm_frac": round(gbs / HBM_PEAK, 4),
+        "alg_bytes_per_step_avg": int(alg_bytes // steps), "prefill_ms": round(prefill_ms, 2),
+        "nonfinite_logits": n_bad, "roofline": roof, "cpu_baseline": None,
+    }
     print(json.dumps(out), flush=True)
 
 
