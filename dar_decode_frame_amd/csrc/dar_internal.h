@@ -254,6 +254,9 @@ hipError_t prepare_task(int wtype, const Task& t);
 // ---- prefill (dar_prefill.hip)
 // rows of the GEMM input arrays for M rows
 int gemm_mpad(int M);
+// K splits launch_gemm uses for an M x N x K product of weight type wtype
+// (partial sums: splits * M * N floats)
+int gemm_splits(int wtype, int M, int N, int K);
 // GEMM with K split across workgroups (deterministic second pass) so that the
 // launch covers the chip; part must hold part_cap floats.
 hipError_t launch_gemm(int wtype, GemmArgs a, size_t part_cap, hipStream_t s);

@@ -27,9 +27,12 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
-constexpr int kKC = 64;        // k per chunk of the GEMM main loop
-constexpr int kPitch = kKC + 8;  // LDS row pitch of staged inputs (bf16), padded against bank conflicts
 constexpr int kTileN = 128;    // weight rows per workgroup (32 per wave)
+constexpr int kRowChunk = 128; // bytes of every weight row per GEMM chunk
+constexpr int kStages = 3;     // chunks in the LDS ring of the GEMM
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) void glb_void;
 
 __device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float(((uint32_t)h) << 16); }
 
@@ -40,114 +43,143 @@ __device__ __forceinline__ uint16_t f2bf(float f) {
   return (uint16_t)(u >> 16);
 }
 
-struct BF16W {
+// 16 bytes per lane moved from global memory straight into LDS (no register
+// staging): lane l's bytes land at lds + 16 l, lds being the same for the
+// whole wave.
+__device__ __forceinline__ void load_lds16(const void* src, void* lds) {
+  __builtin_amdgcn_global_load_lds((glb_void*)src, (lds_void*)lds, 16, 0, 0);
+}
+
+// Wait until at most N of this wave's vector-memory loads are outstanding
+// (they complete in issue order); the other counters are left alone.
+template <int N>
+__device__ __forceinline__ void wait_loads() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// A staged chunk holds 128 B of each of 128 weight rows; the 16-byte units of
+// row r sit XOR-swizzled, unit u at slot u ^ (r % 8), so the 32 lanes that
+// read one unit of 32 consecutive rows hit distinct bank groups.
+struct BF16T {
   static constexpr int kBytes = 2;
-  // eight consecutive weights of a row as the MFMA B operand
-  __device__ static __forceinline__ bf16x8 frag(const char* p) {
-    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
+  // eight consecutive weights of row r at k = 16 s + 8 half, as the MFMA B operand
+  __device__ static __forceinline__ bf16x8 frag(const char* st, int r, int s, int half) {
+    const int u = (2 * s + half) ^ (r & 7);
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(st + (r * 8 + u) * 16));
   }
 };
 
-struct FP8W {
+struct FP8T {
   static constexpr int kBytes = 1;
   // e4m3fn values are exact in bf16: widen through fp32 and keep the top half
   __device__ static __forceinline__ uint32_t pack2(f32x2 v) {
     return (__float_as_uint(v.x) >> 16) | (__float_as_uint(v.y) & 0xffff0000u);
   }
-  __device__ static __forceinline__ bf16x8 frag(const char* p) {
-    const u32x2 w = *reinterpret_cast<const u32x2*>(p);
-    u32x4 r;
-    r.x = pack2(__builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, false));
-    r.y = pack2(__builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, true));
-    r.z = pack2(__builtin_amdgcn_cvt_pk_f32_fp8((int)w.y, false));
-    r.w = pack2(__builtin_amdgcn_cvt_pk_f32_fp8((int)w.y, true));
-    return __builtin_bit_cast(bf16x8, r);
+  __device__ static __forceinline__ bf16x8 frag(const char* st, int r, int s, int half) {
+    const int u = s ^ (r & 7);
+    const u32x2 w = *reinterpret_cast<const u32x2*>(st + (r * 8 + u) * 16 + 8 * half);
+    u32x4 o;
+    o.x = pack2(__builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, false));
+    o.y = pack2(__builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, true));
+    o.z = pack2(__builtin_amdgcn_cvt_pk_f32_fp8((int)w.y, false));
+    o.w = pack2(__builtin_amdgcn_cvt_pk_f32_fp8((int)w.y, true));
+    return __builtin_bit_cast(bf16x8, o);
   }
 };
 
 // One workgroup: weight rows [128 bx, +128) (wave w: 32 rows) x input rows
-// [32 MT by, +32 MT) x the k chunks of split bz. Each wave streams its weight
-// fragments from HBM straight into registers (lane l: row l % 32, 8
-// consecutive k at 8 (l / 32) of each 16-wide step), two chunks ahead of the
-// MFMAs; the input chunk (hi and lo) is loaded one chunk ahead and staged in
-// one of two LDS buffers, so a chunk costs one barrier.
+// [32 MT by, +32 MT) x the chunks of split bz. A chunk is 128 B of each
+// weight row (64 bf16 or 128 e4m3 weights) and the matching hi and lo input
+// columns (same swizzle, per input row). Chunks stream through a ring of
+// kStages LDS buffers by direct loads, issued kStages - 1 chunks ahead; a
+// chunk costs one barrier, after which every wave runs its MFMAs from LDS.
 template <typename WT, int MT>
 __global__ __launch_bounds__(kBlock) void k_gemm(GemmArgs a) {
-  constexpr int kRowPieces = kKC / 8;                  // 16-byte pieces per staged row
-  constexpr int kPieces = 2 * 32 * MT * kRowPieces;    // hi and lo
-  constexpr int kPer = kPieces / kBlock;               // pieces per thread
-  static_assert(kPieces % kBlock == 0, "staging split");
-  __shared__ __align__(16) uint16_t xs[2][2][32 * MT][kPitch];  // [buffer][hi/lo][row][k]
+  constexpr int KC = kRowChunk / WT::kBytes;           // k per chunk
+  constexpr int ST = KC / 16;                          // MFMA k-steps per chunk
+  constexpr int XU = KC / 8;                           // 16-byte units of an input row per chunk
+  constexpr int WB = kTileN * kRowChunk;               // weight bytes per stage
+  constexpr int XB = 2 * 32 * MT * XU * 16;            // input bytes per stage (hi, lo)
+  constexpr int SB = WB + XB;
+  constexpr int XL = XB / (16 * 64 * kWaves);          // input loads per wave per stage
+  constexpr int LPS = 4 + XL;                          // loads per wave per stage
+  static_assert(XL * 16 * 64 * kWaves == XB, "input staging split");
+  __shared__ __align__(16) char sm[kStages * SB];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int n0 = blockIdx.x * kTileN + wave * 32;
+  const int nb = blockIdx.x * kTileN;
   const int m0 = blockIdx.y * 32 * MT;
-  const int nchunks = a.K / kKC;
   const int c_begin = blockIdx.z * a.cps;
-  const int c_end = min(nchunks, c_begin + a.cps);
-  const int kl = 8 * (lane >> 5);
-  const char* wrow =
-      reinterpret_cast<const char*>(a.W) + (size_t)min(n0 + (lane & 31), a.N - 1) * a.K * WT::kBytes;
-  auto load_w = [&](bf16x8 (&b)[4], int c) {
-    const int cc = min(c, c_end - 1);  // past the end: a valid chunk, never used
+  const int nc = min(a.K / KC, c_begin + a.cps) - c_begin;
+  // weight load i of this wave fills rows 32 wave + 8 i + lane / 8, slot lane % 8
+  const char* wsrc[4];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) b[s] = WT::frag(wrow + (size_t)(cc * kKC + 16 * s + kl) * WT::kBytes);
-  };
-  auto load_x = [&](u32x4 (&r)[kPer], int c) {
-    const int k0 = min(c, c_end - 1) * kKC;
+  for (int i = 0; i < 4; ++i) {
+    const int r = wave * 32 + 8 * i + (lane >> 3);
+    wsrc[i] = reinterpret_cast<const char*>(a.W) + (size_t)min(nb + r, a.N - 1) * a.K * WT::kBytes +
+              (size_t)c_begin * kRowChunk + 16 * ((lane & 7) ^ (lane >> 3));
+  }
+  // input load j of this wave fills 64 consecutive slots of the hi or lo part
+  const char* xsrc[XL];
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      const int p = tid + j * kBlock;
-      const int part = p / (32 * MT * kRowPieces);
-      const int rem = p % (32 * MT * kRowPieces);
-      const int row = rem / kRowPieces, q = rem % kRowPieces;
-      r[j] = *reinterpret_cast<const u32x4*>((part ? a.xl : a.xh) + (size_t)(m0 + row) * a.K + k0 + q * 8);
-    }
-  };
-  auto store_x = [&](const u32x4 (&r)[kPer], int buf) {
+  for (int j = 0; j < XL; ++j) {
+    const int q0 = (wave * XL + j) * 64;
+    const int part = q0 / (32 * MT * XU);
+    const int q = q0 % (32 * MT * XU) + lane;
+    const int row = q / XU, u = (q % XU) ^ (row & 7);
+    xsrc[j] = reinterpret_cast<const char*>(part ? a.xl : a.xh) +
+              ((size_t)(m0 + row) * a.K + (size_t)c_begin * KC) * 2 + 16 * u;
+  }
+  auto issue = [&](int t, int stage) {
+    char* base = sm + stage * SB;
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      const int p = tid + j * kBlock;
-      const int part = p / (32 * MT * kRowPieces);
-      const int rem = p % (32 * MT * kRowPieces);
-      const int row = rem / kRowPieces, q = rem % kRowPieces;
-      *reinterpret_cast<u32x4*>(&xs[buf][part][row][q * 8]) = r[j];
-    }
+    for (int i = 0; i < 4; ++i) load_lds16(wsrc[i] + (size_t)t * kRowChunk, base + wave * 4096 + i * 1024);
+#pragma unroll
+    for (int j = 0; j < XL; ++j) load_lds16(xsrc[j] + (size_t)t * KC * 2, base + WB + (wave * XL + j) * 1024);
   };
   f32x16 acc[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc[mt][v] = 0.f;
-
-  bf16x8 b0[4], b1[4];
-  u32x4 xr[kPer];
-  load_w(b0, c_begin);
-  load_w(b1, c_begin + 1);
-  load_x(xr, c_begin);
-  auto step = [&](bf16x8 (&b)[4], int c) {
-    const int buf = (c - c_begin) & 1;
-    store_x(xr, buf);
-    __syncthreads();  // chunk c staged; every thread is past chunk c - 2's reads of this buffer
-    load_x(xr, c + 1);
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
+  for (int j = 0; j < kStages - 1; ++j)
+    if (j < nc) issue(j, j);
+  const int half = lane >> 5;
+  for (int t0 = 0; t0 < nc; t0 += kStages) {
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const int r = mt * 32 + (lane & 31);
-        const bf16x8 ah = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&xs[buf][0][r][16 * s + kl]));
-        const bf16x8 al = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&xs[buf][1][r][16 * s + kl]));
-        acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, b[s], acc[mt], 0, 0, 0);
-        acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, b[s], acc[mt], 0, 0, 0);
+    for (int j = 0; j < kStages; ++j) {
+      const int t = t0 + j;
+      if (t < nc) {
+        // chunk t has landed for this wave once only the later chunks' loads are outstanding
+        static_assert(kStages == 3, "wait counts below assume three stages");
+        if (t + 1 < nc) wait_loads<LPS>();
+        else wait_loads<0>();
+        // every wave's chunk t has landed, and every wave is done with chunk t - 1's buffer
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        if (t + kStages - 1 < nc) issue(t + kStages - 1, (j + kStages - 1) % kStages);
+        const char* ws = sm + j * SB;
+        const char* xs = ws + WB;
+#pragma unroll
+        for (int s = 0; s < ST; ++s) {
+          const bf16x8 b = WT::frag(ws, wave * 32 + (lane & 31), s, half);
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) {
+            const int row = mt * 32 + (lane & 31);
+            const int u = (2 * s + half) ^ (row & 7);
+            const bf16x8 ah = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(xs + (row * XU + u) * 16));
+            const bf16x8 al =
+                __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(xs + ((32 * MT + row) * XU + u) * 16));
+            acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, b, acc[mt], 0, 0, 0);
+            acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, b, acc[mt], 0, 0, 0);
+          }
+        }
       }
     }
-    load_w(b, c + 2);  // this register set's next chunk
-  };
-  for (int c = c_begin; c < c_end; c += 2) {
-    step(b0, c);
-    if (c + 1 < c_end) step(b1, c + 1);
   }
   // accumulator v of lane l holds row (v % 4) + 4 (l / 32) + 8 (v / 4), column l % 32
-  const int n = n0 + (lane & 31);
+  const int n = nb + wave * 32 + (lane & 31);
   if (n >= a.N) return;
   const float sc = (a.scale && a.splits == 1) ? a.scale[n] : 1.f;
 #pragma unroll
@@ -361,12 +393,16 @@ __global__ void k_inc_rows(int* v, int n) {
   if (i < n) v[i] = v[i] + 1;
 }
 
-template <typename WT>
-hipError_t gemm_dispatch(const GemmArgs& a, int mt, dim3 grid, hipStream_t s) {
-  switch (mt) {
-    case 1: hipLaunchKernelGGL((k_gemm<WT, 1>), grid, dim3(kBlock), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((k_gemm<WT, 2>), grid, dim3(kBlock), 0, s, a); break;
-    default: hipLaunchKernelGGL((k_gemm<WT, 4>), grid, dim3(kBlock), 0, s, a); break;
+hipError_t gemm_dispatch(int wtype, const GemmArgs& a, int mt, dim3 grid, hipStream_t s) {
+  if (wtype == W_FP8) {
+    if (mt == 1) hipLaunchKernelGGL((k_gemm<FP8T, 1>), grid, dim3(kBlock), 0, s, a);
+    else hipLaunchKernelGGL((k_gemm<FP8T, 2>), grid, dim3(kBlock), 0, s, a);
+  } else {
+    switch (mt) {
+      case 1: hipLaunchKernelGGL((k_gemm<BF16T, 1>), grid, dim3(kBlock), 0, s, a); break;
+      case 2: hipLaunchKernelGGL((k_gemm<BF16T, 2>), grid, dim3(kBlock), 0, s, a); break;
+      default: hipLaunchKernelGGL((k_gemm<BF16T, 4>), grid, dim3(kBlock), 0, s, a); break;
+    }
   }
   return hipGetLastError();
 }
@@ -375,20 +411,38 @@ hipError_t gemm_dispatch(const GemmArgs& a, int mt, dim3 grid, hipStream_t s) {
 
 int gemm_mpad(int M) { return M <= 32 ? 32 : (M <= 64 ? 64 : ((M + 127) / 128) * 128); }
 
+// input rows per workgroup / 32: the e4m3 kernel stages twice the input
+// columns per chunk, so its LDS ring holds at most 64 input rows
+static int gemm_mt(int wtype, int M) {
+  const int mt = M <= 32 ? 1 : (M <= 64 ? 2 : 4);
+  return (wtype == W_FP8 && mt > 2) ? 2 : mt;
+}
+
+// K splits: as many as keep the launch within one workgroup per CU (a
+// workgroup's LDS ring and loads in flight are what stream the weights; a
+// second one on a CU adds no bandwidth), each split at least one chunk
+int gemm_splits(int wtype, int M, int N, int K) {
+  const int mt = gemm_mt(wtype, M);
+  const int tiles = ((N + kTileN - 1) / kTileN) * ((M + 32 * mt - 1) / (32 * mt));
+  const int nchunks = K / (kRowChunk / (wtype == W_FP8 ? 1 : 2));
+  int splits = 256 / tiles;
+  splits = splits < 1 ? 1 : (splits > nchunks ? nchunks : splits);
+  const int cps = (nchunks + splits - 1) / splits;
+  return (nchunks + cps - 1) / cps;
+}
+
 hipError_t launch_gemm(int wtype, GemmArgs a, size_t part_cap, hipStream_t s) {
-  if (a.M < 1 || a.M > kPrefillRows || a.K % kKC || a.N < 1) return hipErrorInvalidValue;
-  const int mt = a.M <= 32 ? 1 : (a.M <= 64 ? 2 : 4);
+  const int kc = kRowChunk / (wtype == W_FP8 ? 1 : 2);
+  if (a.M < 1 || a.M > kPrefillRows || a.K < kc || a.K % kc || a.N < 1) return hipErrorInvalidValue;
+  const int mt = gemm_mt(wtype, a.M);
   const int gx = (a.N + kTileN - 1) / kTileN, gy = (a.M + 32 * mt - 1) / (32 * mt);
-  const int nchunks = a.K / kKC;
-  // split K until the launch covers every CU once, within the partial-sum buffer
-  int splits = (256 + gx * gy - 1) / (gx * gy);
-  splits = splits < 1 ? 1 : (splits > 16 ? 16 : splits);
-  if (splits > nchunks) splits = nchunks;
+  const int nchunks = a.K / kc;
+  int splits = gemm_splits(wtype, a.M, a.N, a.K);
   while (splits > 1 && (size_t)splits * a.M * a.N > part_cap) --splits;
   a.cps = (nchunks + splits - 1) / splits;
   a.splits = (nchunks + a.cps - 1) / a.cps;
   const dim3 grid(gx, gy, a.splits);
-  hipError_t e = wtype == W_FP8 ? gemm_dispatch<FP8W>(a, mt, grid, s) : gemm_dispatch<BF16W>(a, mt, grid, s);
+  hipError_t e = gemm_dispatch(wtype, a, mt, grid, s);
   if (e != hipSuccess || a.splits == 1) return e;
   const size_t total = (size_t)a.M * a.N;
   size_t blocks = (total + kBlock - 1) / kBlock;

@@ -130,11 +130,11 @@ Layout make_layout(const dar_config* c) {
   L.ph1 = take(sizeof(float) * R * F);
   L.ph3 = take(sizeof(float) * R * F);
   // partial sums of the widest K split launch_gemm picks for the block's GEMMs
+  const int wt = c->wtype == DAR_WTYPE_FP8_E4M3_ROW ? W_FP8 : W_BF16;
   L.pgp_floats = 0;
-  for (int N : {d, qkv_rows, F}) {
-    const int gx = (N + 127) / 128;
-    const int splits = std::min(16, (256 + gx - 1) / gx);
-    L.pgp_floats = std::max(L.pgp_floats, (size_t)splits * R * N);
+  for (auto nk : {std::pair<int, int>{qkv_rows, d}, {d, qw}, {F, d}, {d, F}}) {
+    for (int M = 1; M <= (int)R; ++M)
+      L.pgp_floats = std::max(L.pgp_floats, (size_t)gemm_splits(wt, M, nk.first, nk.second) * M * nk.first);
   }
   L.pgp = take(sizeof(float) * L.pgp_floats);
   L.patt = take(sizeof(float) * attn_partial_floats((int)R, c->n_heads_kv, L.nsplit_slow, g, c->head_dim));
@@ -147,10 +147,11 @@ Layout make_layout(const dar_config* c) {
       L.bxh[ch] = take(2 * (size_t)gemm_mpad(M) * kmax);
       L.bxl[ch] = take(2 * (size_t)gemm_mpad(M) * kmax);
       L.bgp_floats[ch] = 0;
-      for (int N : {d, qkv_rows, F, c->vocab_c0, has_fast(c) ? c->vocab_res : 1}) {
-        const int gx = (N + 127) / 128;
-        const int splits = std::min(16, (256 + gx - 1) / gx);
-        L.bgp_floats[ch] = std::max(L.bgp_floats[ch], (size_t)splits * M * N);
+      for (auto nk : {std::pair<int, int>{qkv_rows, d}, {d, qw}, {F, d}, {d, F}, {c->vocab_c0, d},
+                      {has_fast(c) ? c->vocab_res : 1, d}}) {
+        for (int m : {M, B})
+          L.bgp_floats[ch] =
+              std::max(L.bgp_floats[ch], (size_t)gemm_splits(wt, m, nk.first, nk.second) * m * nk.first);
       }
       L.bgp[ch] = take(sizeof(float) * L.bgp_floats[ch]);
     }
@@ -1422,7 +1423,8 @@ int dar_op_gemm(int32_t wtype, const void* W, const float* scale, int32_t N, int
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int mpad = gemm_mpad(M);
   const size_t half_bytes = align_up((size_t)mpad * K * sizeof(uint16_t));
-  const size_t part_cap = (size_t)16 * M * N;
+  const int wt = wtype == DAR_WTYPE_FP8_E4M3_ROW ? W_FP8 : W_BF16;
+  const size_t part_cap = (size_t)gemm_splits(wt, M, N, K) * M * N;
   char* scratch = nullptr;
   hipError_t e = hipMalloc(&scratch, 2 * half_bytes + part_cap * sizeof(float));
   if (e != hipSuccess) return hip_fail(nullptr, e, "gemm scratch");
