@@ -125,7 +125,10 @@ struct AttnArgs {
 
 // y[m][n] (+)= scale[n] * sum_k x[m][k] W[n][k] for m < M, n < N (prefill
 // GEMM on MFMA). The input rows come as two bf16 arrays with x = hi + lo,
-// [gemm_mpad(M)][K] (rows M.. zero). K % 64 == 0, M <= kPrefillRows.
+// [gemm_mpad(M)][K] (rows past M are never used for an output row).
+// K % 64 == 0 (bf16) or % 128 (e4m3), M <= kPrefillRows. With defer set the
+// K-split sums stay in part (scaled, [splits][M][N], one split included) for
+// the next row kernel to add up; y and accumulate are then unused.
 struct GemmArgs {
   const void* W;            // [N][K] bf16 or e4m3fn
   const float* scale;       // [N] (fp8) or nullptr
@@ -136,7 +139,16 @@ struct GemmArgs {
   int y_stride;
   int accumulate;
   float* part;              // partial sums of the K splits, [splits][M][N]
-  int splits, cps;          // set by launch_gemm: K splits, 64-wide chunks per split
+  int defer;                // leave the sums in part (no second pass)
+  int splits, cps;          // set by launch_gemm: K splits, chunks per split
+};
+
+// Split-K sums a GEMM left behind: element (m, j) of the product is
+// sum over z < n of p[z * stride + m * N + j], N being the product's width.
+struct PartSum {
+  const float* p;
+  int n;                    // 0: nothing pending
+  long long stride;         // floats between splits (M * N)
 };
 
 // Batched commit of codebook `code_index` for B sequences: argmax of each
@@ -187,13 +199,14 @@ enum TaskKind : int {
 
 // One stage of a chain: its kind, input rows and arguments.
 struct NormSplitArgs {
-  const float* x;
+  float* x;
   int x_stride, M, K;
   const uint16_t* gain;  // nullptr: no norm
   float eps;
   uint16_t* xh;
   uint16_t* xl;
   float* out_f32;        // optional normalised rows
+  PartSum add;           // pending residual sums, added into x first
 };
 struct GemmTask {
   GemmArgs g;
@@ -202,6 +215,7 @@ struct GemmTask {
 };
 struct RopeRowsArgs {
   const float* qkv;
+  PartSum src;           // when set, the QKV rows are these sums (qkv unused)
   int M;
   const int* row_pos;
   const int* row_seq;
@@ -216,6 +230,7 @@ struct RopeRowsArgs {
 struct SiluSplitArgs {
   const float* a;
   const float* b;
+  PartSum pa, pb;        // when set, a and b are these sums
   int M, F;
   uint16_t* hh;
   uint16_t* hl;
@@ -254,16 +269,21 @@ hipError_t prepare_task(int wtype, const Task& t);
 // ---- prefill (dar_prefill.hip)
 // rows of the GEMM input arrays for M rows
 int gemm_mpad(int M);
-// K splits launch_gemm uses for an M x N x K product of weight type wtype
+// K splits gemm_launch_splits picks before the partial-sum limit
 // (partial sums: splits * M * N floats)
 int gemm_splits(int wtype, int M, int N, int K);
-// GEMM with K split across workgroups (deterministic second pass) so that the
-// launch covers the chip; part must hold part_cap floats.
+// K splits launch_gemm runs for this product with part_cap floats of partial sums
+int gemm_launch_splits(int wtype, int M, int N, int K, size_t part_cap);
+// GEMM with K split across workgroups (deterministic second pass, or the
+// sums left in part with defer) so that the launch covers the chip; part
+// must hold part_cap floats.
 hipError_t launch_gemm(int wtype, GemmArgs a, size_t part_cap, hipStream_t s);
 // hi/lo bf16 rows of x (RMSNorm(x) * gain when gain is set), gemm_mpad(M)
-// rows; out_f32 (optional): the normalised rows in fp32, [M][K]
-hipError_t launch_norm_split(const float* x, int x_stride, int M, int K, const uint16_t* gain, float eps,
-                             uint16_t* xh, uint16_t* xl, hipStream_t s, float* out_f32 = nullptr);
+// rows; out_f32 (optional): the normalised rows in fp32, [M][K]. With add
+// pending, x += the sums first (x row stride == K then).
+hipError_t launch_norm_split(float* x, int x_stride, int M, int K, const uint16_t* gain, float eps,
+                             uint16_t* xh, uint16_t* xl, hipStream_t s, float* out_f32 = nullptr,
+                             PartSum add = PartSum{nullptr, 0, 0});
 // x[m] = table[clamp(tok[m])] for m < M
 hipError_t launch_embed_rows(const uint16_t* table, int rows, int K, const int* tok, int M, float* x,
                              int* anomalies, hipStream_t s);
@@ -272,14 +292,14 @@ hipError_t launch_embed_rows(const uint16_t* table, int rows, int K, const int* 
 hipError_t launch_rope_rows(const float* qkv, int M, int p0, int n_heads_q, int n_heads_kv, int head_dim,
                             const float2* rope, float* q_out, uint16_t* kc, uint16_t* vc, int cache_len,
                             hipStream_t s, const int* row_pos = nullptr, const int* row_seq = nullptr,
-                            long long seq_stride = 0);
+                            long long seq_stride = 0, PartSum src = PartSum{nullptr, 0, 0});
 // argmax + commit of one codebook for B sequences (k_commit_rows)
 hipError_t launch_commit_rows(const RowsCommitArgs& a, hipStream_t s);
 // v[i] += 1 for i < n
 hipError_t launch_inc_rows(int* v, int n, hipStream_t s);
-// SiLU(a) * b as hi/lo bf16 rows
+// SiLU(a) * b as hi/lo bf16 rows (a, b: the sums pa, pb when those are set)
 hipError_t launch_silu_split(const float* a, const float* b, int M, int F, uint16_t* hh, uint16_t* hl,
-                             hipStream_t s);
+                             hipStream_t s, PartSum pa = PartSum{nullptr, 0, 0}, PartSum pb = PartSum{nullptr, 0, 0});
 
 // x = table[clamp(*tok)] as fp32, *pos_out = pos_value (prefill step input)
 hipError_t launch_embed(const uint16_t* table, int rows, int K, const int* tok, float* x,

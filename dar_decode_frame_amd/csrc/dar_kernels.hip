@@ -1537,17 +1537,19 @@ static bool row_stage(const Task& t, hipStream_t s, hipError_t& e) {
   switch (t.kind) {
     case T_NORM_SPLIT: {
       const NormSplitArgs& a = t.norm;
-      e = launch_norm_split(a.x, a.x_stride, a.M, a.K, a.gain, a.eps, a.xh, a.xl, s, a.out_f32);
+      e = launch_norm_split(a.x, a.x_stride, a.M, a.K, a.gain, a.eps, a.xh, a.xl, s, a.out_f32, a.add);
       return true;
     }
     case T_GEMM: e = launch_gemm(t.gemm.wtype, t.gemm.g, t.gemm.part_cap, s); return true;
     case T_ROPE_ROWS: {
       const RopeRowsArgs& a = t.rope;
       e = launch_rope_rows(a.qkv, a.M, 0, a.n_heads_q, a.n_heads_kv, a.head_dim, a.rope, a.q_out, a.kc, a.vc,
-                           a.cache_len, s, a.row_pos, a.row_seq, a.seq_stride);
+                           a.cache_len, s, a.row_pos, a.row_seq, a.seq_stride, a.src);
       return true;
     }
-    case T_SILU_SPLIT: e = launch_silu_split(t.silu.a, t.silu.b, t.silu.M, t.silu.F, t.silu.hh, t.silu.hl, s); return true;
+    case T_SILU_SPLIT:
+      e = launch_silu_split(t.silu.a, t.silu.b, t.silu.M, t.silu.F, t.silu.hh, t.silu.hl, s, t.silu.pa, t.silu.pb);
+      return true;
     case T_COMMIT_ROWS: e = launch_commit_rows(t.rows, s); return true;
     case T_INC_ROWS: e = launch_inc_rows(t.inc.v, t.inc.n, s); return true;
     default: return false;

@@ -181,14 +181,16 @@ __global__ __launch_bounds__(kBlock) void k_gemm(GemmArgs a) {
   // accumulator v of lane l holds row (v % 4) + 4 (l / 32) + 8 (v / 4), column l % 32
   const int n = nb + wave * 32 + (lane & 31);
   if (n >= a.N) return;
-  const float sc = (a.scale && a.splits == 1) ? a.scale[n] : 1.f;
+  const float sc = (a.scale && (a.splits == 1 || a.defer)) ? a.scale[n] : 1.f;
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int m = m0 + mt * 32 + (v % 4) + 4 * (lane >> 5) + 8 * (v / 4);
       if (m >= a.M) continue;
-      if (a.splits == 1) {
+      if (a.defer) {
+        a.part[((size_t)blockIdx.z * a.M + m) * a.N + n] = acc[mt][v] * sc;
+      } else if (a.splits == 1) {
         float* y = a.y + (size_t)m * a.y_stride + n;
         const float val = acc[mt][v] * sc;
         *y = a.accumulate ? *y + val : val;
@@ -225,12 +227,45 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
   return t;
 }
 
+__device__ __forceinline__ float4 ld4(const float* p) { return *reinterpret_cast<const float4*>(p); }
+__device__ __forceinline__ float4 add4(float4 a, float4 b) { return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w); }
+
+// Four consecutive elements of a pending split-K sum starting at element idx
+// (fixed order: four running sums over the splits, then combined), so that
+// the splits' loads are in flight together.
+__device__ __forceinline__ float4 part_sum4(const PartSum& ps, size_t idx) {
+  const float* p = ps.p + idx;
+  const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
+  float4 s0 = z4, s1 = z4, s2 = z4, s3 = z4;
+  int z = 0;
+  for (; z + 4 <= ps.n; z += 4) {
+    const float4 a = ld4(p + (size_t)z * ps.stride), b = ld4(p + (size_t)(z + 1) * ps.stride);
+    const float4 c = ld4(p + (size_t)(z + 2) * ps.stride), d = ld4(p + (size_t)(z + 3) * ps.stride);
+    s0 = add4(s0, a);
+    s1 = add4(s1, b);
+    s2 = add4(s2, c);
+    s3 = add4(s3, d);
+  }
+  for (; z < ps.n; ++z) s0 = add4(s0, ld4(p + (size_t)z * ps.stride));
+  return add4(add4(s0, s1), add4(s2, s3));
+}
+
+// hi/lo bf16 of four values, stored as 8 bytes each
+__device__ __forceinline__ void split_store4(float4 v, uint16_t* oh, uint16_t* ol) {
+  const uint16_t h0 = f2bf(v.x), h1 = f2bf(v.y), h2 = f2bf(v.z), h3 = f2bf(v.w);
+  const uint16_t l0 = f2bf(v.x - bf2f(h0)), l1 = f2bf(v.y - bf2f(h1));
+  const uint16_t l2 = f2bf(v.z - bf2f(h2)), l3 = f2bf(v.w - bf2f(h3));
+  *reinterpret_cast<u32x2*>(oh) = u32x2{(uint32_t)h0 | ((uint32_t)h1 << 16), (uint32_t)h2 | ((uint32_t)h3 << 16)};
+  *reinterpret_cast<u32x2*>(ol) = u32x2{(uint32_t)l0 | ((uint32_t)l1 << 16), (uint32_t)l2 | ((uint32_t)l3 << 16)};
+}
+
 // Row m of the GEMM input: v = x[m] (RMSNorm(x[m]) * gain when gain is set),
 // written as hi = bf16(v), lo = bf16(v - hi); rows M..Mpad-1 are zero. With
-// out_f32 set, v is also written there in fp32 (row stride K).
-__global__ __launch_bounds__(kBlock) void k_norm_split(const float* x, int x_stride, int M, int K,
-                                                        const uint16_t* gain, float eps, uint16_t* xh, uint16_t* xl,
-                                                        float* out_f32) {
+// residual sums pending, x[m] += their sum first (written back). With out_f32
+// set, v is also written there in fp32 (row stride K). Columns in fours.
+__global__ __launch_bounds__(kBlock) void k_norm_split(float* x, int x_stride, int M, int K, const uint16_t* gain,
+                                                        float eps, uint16_t* xh, uint16_t* xl, float* out_f32,
+                                                        PartSum add) {
   __shared__ float red[kWaves];
   const int m = blockIdx.x, tid = threadIdx.x;
   uint16_t* oh = xh + (size_t)m * K;
@@ -239,20 +274,35 @@ __global__ __launch_bounds__(kBlock) void k_norm_split(const float* x, int x_str
     for (int k = tid; k < K; k += kBlock) oh[k] = ol[k] = 0;
     return;
   }
-  const float* xr = x + (size_t)m * x_stride;
+  float* xr = x + (size_t)m * x_stride;
+  float ss = 0.f;
+  if (add.n > 0 || gain) {
+    for (int k = 4 * tid; k < K; k += 4 * kBlock) {
+      float4 v = ld4(xr + k);
+      if (add.n > 0) {
+        v = add4(v, part_sum4(add, (size_t)m * K + k));
+        *reinterpret_cast<float4*>(xr + k) = v;
+      }
+      ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+    }
+  }
   float inv = 1.f;
   if (gain) {
-    float ss = 0.f;
-    for (int k = tid; k < K; k += kBlock) ss += xr[k] * xr[k];
     ss = block_sum(ss, red);
     inv = 1.0f / sqrtf(ss / (float)K + eps);
   }
-  for (int k = tid; k < K; k += kBlock) {
-    const float v = gain ? (xr[k] * inv) * bf2f(gain[k]) : xr[k];
-    const uint16_t h = f2bf(v);
-    oh[k] = h;
-    ol[k] = f2bf(v - bf2f(h));
-    if (out_f32) out_f32[(size_t)m * K + k] = v;
+  // each thread rereads only the columns it wrote above
+  for (int k = 4 * tid; k < K; k += 4 * kBlock) {
+    float4 v = ld4(xr + k);
+    if (gain) {
+      const u32x2 g = *reinterpret_cast<const u32x2*>(gain + k);
+      v.x = (v.x * inv) * bf2f((uint16_t)(g.x & 0xffffu));
+      v.y = (v.y * inv) * bf2f((uint16_t)(g.x >> 16));
+      v.z = (v.z * inv) * bf2f((uint16_t)(g.y & 0xffffu));
+      v.w = (v.w * inv) * bf2f((uint16_t)(g.y >> 16));
+    }
+    split_store4(v, oh + k, ol + k);
+    if (out_f32) *reinterpret_cast<float4*>(out_f32 + (size_t)m * K + k) = v;
   }
 }
 
@@ -267,61 +317,73 @@ __global__ __launch_bounds__(kBlock) void k_embed_rows(const uint16_t* table, in
   for (int k = threadIdx.x; k < K; k += kBlock) x[(size_t)m * K + k] = bf2f(row[k]);
 }
 
-// RoPE at positions p0 + m (or row_pos[m]) on q and k of the rows' QKV output,
-// q to q_out, k and v appended to the bf16 caches (rotate-half pairs
-// (i, i + hd/2)); with row_seq, row m appends to sequence row_seq[m]'s cache.
-__global__ __launch_bounds__(kBlock) void k_rope_rows(const float* qkv, int M, int p0, const int* row_pos,
-                                                       const int* row_seq, long long seq_stride, int n_heads_q,
-                                                       int n_heads_kv, int head_dim, const float2* rope, float* q_out,
-                                                       uint16_t* kc, uint16_t* vc, int cache_len) {
-  const int m = blockIdx.x;
+// RoPE at positions p0 + m (or row_pos[m]) on q and k of the rows' QKV output
+// (or of the pending split-K sums src), q to q_out, k and v appended to the
+// bf16 caches (rotate-half pairs (i, i + hd/2)); with row_seq, row m appends
+// to sequence row_seq[m]'s cache. One wave per (row, head), lane i: pair i.
+__global__ __launch_bounds__(kWave) void k_rope_rows(const float* qkv, PartSum src, int M, int p0,
+                                                      const int* row_pos, const int* row_seq, long long seq_stride,
+                                                      int n_heads_q, int n_heads_kv, int head_dim, const float2* rope,
+                                                      float* q_out, uint16_t* kc, uint16_t* vc, int cache_len) {
+  const int m = blockIdx.x, head = blockIdx.y, i = threadIdx.x;
   const int half = head_dim / 2;
-  const int n_heads = n_heads_q + 2 * n_heads_kv;
+  if (i >= half) return;
+  const int width = (n_heads_q + 2 * n_heads_kv) * head_dim;
   const int pos = row_pos ? row_pos[m] : p0 + m;
   if (row_seq) {
     kc += (size_t)row_seq[m] * seq_stride;
     vc += (size_t)row_seq[m] * seq_stride;
   }
-  const float* row = qkv + (size_t)m * n_heads * head_dim;
-  for (int j = threadIdx.x; j < n_heads * half; j += kBlock) {
-    const int head = j / half, i = j % half;
-    const int r1 = head * head_dim + i, r2 = r1 + half;
-    const float u = row[r1], v = row[r2];
-    if (head < n_heads_q + n_heads_kv) {
-      const float2 cs = rope[(size_t)pos * half + i];
-      const float o1 = u * cs.x - v * cs.y;
-      const float o2 = u * cs.y + v * cs.x;
-      if (head < n_heads_q) {
-        q_out[(size_t)m * n_heads_q * head_dim + r1] = o1;
-        q_out[(size_t)m * n_heads_q * head_dim + r2] = o2;
-      } else {
-        uint16_t* kp = kc + ((size_t)(head - n_heads_q) * cache_len + pos) * head_dim;
-        kp[i] = f2bf(o1);
-        kp[i + half] = f2bf(o2);
-      }
-    } else {
-      uint16_t* vp = vc + ((size_t)(head - n_heads_q - n_heads_kv) * cache_len + pos) * head_dim;
-      vp[i] = f2bf(u);
-      vp[i + half] = f2bf(v);
+  const int r1 = head * head_dim + i, r2 = r1 + half;
+  float u, v;
+  if (src.n > 0) {
+    const float* p = src.p + (size_t)m * width;
+    u = p[r1];
+    v = p[r2];
+    for (int z = 1; z < src.n; ++z) {
+      u += p[(size_t)z * src.stride + r1];
+      v += p[(size_t)z * src.stride + r2];
     }
+  } else {
+    u = qkv[(size_t)m * width + r1];
+    v = qkv[(size_t)m * width + r2];
+  }
+  if (head < n_heads_q + n_heads_kv) {
+    const float2 cs = rope[(size_t)pos * half + i];
+    const float o1 = u * cs.x - v * cs.y;
+    const float o2 = u * cs.y + v * cs.x;
+    if (head < n_heads_q) {
+      q_out[(size_t)m * n_heads_q * head_dim + r1] = o1;
+      q_out[(size_t)m * n_heads_q * head_dim + r2] = o2;
+    } else {
+      uint16_t* kp = kc + ((size_t)(head - n_heads_q) * cache_len + pos) * head_dim;
+      kp[i] = f2bf(o1);
+      kp[i + half] = f2bf(o2);
+    }
+  } else {
+    uint16_t* vp = vc + ((size_t)(head - n_heads_q - n_heads_kv) * cache_len + pos) * head_dim;
+    vp[i] = f2bf(u);
+    vp[i + half] = f2bf(v);
   }
 }
 
-// h = SiLU(a) * b per element, split into bf16 hi/lo rows (rows M..Mpad-1 zero)
-__global__ __launch_bounds__(kBlock) void k_silu_split(const float* a, const float* b, int M, int F, uint16_t* hh,
-                                                        uint16_t* hl) {
-  const int m = blockIdx.x;
-  for (int k = threadIdx.x; k < F; k += kBlock) {
-    uint16_t h = 0, l = 0;
-    if (m < M) {
-      const float g = a[(size_t)m * F + k];
-      const float v = g / (1.0f + expf(-g)) * b[(size_t)m * F + k];
-      h = f2bf(v);
-      l = f2bf(v - bf2f(h));
-    }
-    hh[(size_t)m * F + k] = h;
-    hl[(size_t)m * F + k] = l;
+// h = SiLU(a) * b per element (a, b: the pending sums pa, pb when set), split
+// into bf16 hi/lo rows (rows M..Mpad-1 zero). Block (row, 1024 columns).
+__global__ __launch_bounds__(kBlock) void k_silu_split(const float* a, const float* b, PartSum pa, PartSum pb, int M,
+                                                        int F, uint16_t* hh, uint16_t* hl) {
+  const int m = blockIdx.x, k = 4 * (blockIdx.y * kBlock + threadIdx.x);
+  if (k >= F) return;
+  float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (m < M) {
+    const size_t idx = (size_t)m * F + k;
+    const float4 g = pa.n > 0 ? part_sum4(pa, idx) : ld4(a + idx);
+    const float4 u = pb.n > 0 ? part_sum4(pb, idx) : ld4(b + idx);
+    v.x = g.x / (1.0f + expf(-g.x)) * u.x;
+    v.y = g.y / (1.0f + expf(-g.y)) * u.y;
+    v.z = g.z / (1.0f + expf(-g.z)) * u.z;
+    v.w = g.w / (1.0f + expf(-g.w)) * u.w;
   }
+  split_store4(v, hh + (size_t)m * F + k, hl + (size_t)m * F + k);
 }
 
 // Batched codebook commit, one workgroup per sequence b: the first index of
@@ -431,19 +493,26 @@ int gemm_splits(int wtype, int M, int N, int K) {
   return (nchunks + cps - 1) / cps;
 }
 
+int gemm_launch_splits(int wtype, int M, int N, int K, size_t part_cap) {
+  const int nchunks = K / (kRowChunk / (wtype == W_FP8 ? 1 : 2));
+  int splits = gemm_splits(wtype, M, N, K);
+  while (splits > 1 && (size_t)splits * M * N > part_cap) --splits;
+  const int cps = (nchunks + splits - 1) / splits;
+  return (nchunks + cps - 1) / cps;
+}
+
 hipError_t launch_gemm(int wtype, GemmArgs a, size_t part_cap, hipStream_t s) {
   const int kc = kRowChunk / (wtype == W_FP8 ? 1 : 2);
   if (a.M < 1 || a.M > kPrefillRows || a.K < kc || a.K % kc || a.N < 1) return hipErrorInvalidValue;
+  if (a.defer && (size_t)a.M * a.N > part_cap) return hipErrorInvalidValue;
   const int mt = gemm_mt(wtype, a.M);
   const int gx = (a.N + kTileN - 1) / kTileN, gy = (a.M + 32 * mt - 1) / (32 * mt);
   const int nchunks = a.K / kc;
-  int splits = gemm_splits(wtype, a.M, a.N, a.K);
-  while (splits > 1 && (size_t)splits * a.M * a.N > part_cap) --splits;
-  a.cps = (nchunks + splits - 1) / splits;
-  a.splits = (nchunks + a.cps - 1) / a.cps;
+  a.splits = gemm_launch_splits(wtype, a.M, a.N, a.K, part_cap);
+  a.cps = (nchunks + a.splits - 1) / a.splits;
   const dim3 grid(gx, gy, a.splits);
   hipError_t e = gemm_dispatch(wtype, a, mt, grid, s);
-  if (e != hipSuccess || a.splits == 1) return e;
+  if (e != hipSuccess || a.splits == 1 || a.defer) return e;
   const size_t total = (size_t)a.M * a.N;
   size_t blocks = (total + kBlock - 1) / kBlock;
   if (blocks > 4096) blocks = 4096;
@@ -451,10 +520,11 @@ hipError_t launch_gemm(int wtype, GemmArgs a, size_t part_cap, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_norm_split(const float* x, int x_stride, int M, int K, const uint16_t* gain, float eps,
-                             uint16_t* xh, uint16_t* xl, hipStream_t s, float* out_f32) {
+hipError_t launch_norm_split(float* x, int x_stride, int M, int K, const uint16_t* gain, float eps, uint16_t* xh,
+                             uint16_t* xl, hipStream_t s, float* out_f32, PartSum add) {
+  if (K % 4 || x_stride % 4 || (add.n > 0 && x_stride != K)) return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_norm_split, dim3(gemm_mpad(M)), dim3(kBlock), 0, s, x, x_stride, M, K, gain, eps, xh, xl,
-                     out_f32);
+                     out_f32, add);
   return hipGetLastError();
 }
 
@@ -466,9 +536,11 @@ hipError_t launch_embed_rows(const uint16_t* table, int rows, int K, const int* 
 
 hipError_t launch_rope_rows(const float* qkv, int M, int p0, int n_heads_q, int n_heads_kv, int head_dim,
                             const float2* rope, float* q_out, uint16_t* kc, uint16_t* vc, int cache_len,
-                            hipStream_t s, const int* row_pos, const int* row_seq, long long seq_stride) {
-  hipLaunchKernelGGL(k_rope_rows, dim3(M), dim3(kBlock), 0, s, qkv, M, p0, row_pos, row_seq, seq_stride, n_heads_q,
-                     n_heads_kv, head_dim, rope, q_out, kc, vc, cache_len);
+                            hipStream_t s, const int* row_pos, const int* row_seq, long long seq_stride,
+                            PartSum src) {
+  if (head_dim / 2 > kWave) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_rope_rows, dim3(M, n_heads_q + 2 * n_heads_kv), dim3(kWave), 0, s, qkv, src, M, p0, row_pos,
+                     row_seq, seq_stride, n_heads_q, n_heads_kv, head_dim, rope, q_out, kc, vc, cache_len);
   return hipGetLastError();
 }
 
@@ -483,8 +555,10 @@ hipError_t launch_commit_rows(const RowsCommitArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_silu_split(const float* a, const float* b, int M, int F, uint16_t* hh, uint16_t* hl,
-                             hipStream_t s) {
-  hipLaunchKernelGGL(k_silu_split, dim3(gemm_mpad(M)), dim3(kBlock), 0, s, a, b, M, F, hh, hl);
+                             hipStream_t s, PartSum pa, PartSum pb) {
+  if (F % 4) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_silu_split, dim3(gemm_mpad(M), (F + 4 * kBlock - 1) / (4 * kBlock)), dim3(kBlock), 0, s, a, b,
+                     pa, pb, M, F, hh, hl);
   return hipGetLastError();
 }
 

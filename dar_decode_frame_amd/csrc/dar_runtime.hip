@@ -60,14 +60,15 @@ struct Layout {
   size_t ks, vs, kf, vf;
   // prefill block scratch (kPrefillRows rows): residual, GEMM input halves,
   // QKV output, q, attention output, W1/W3 outputs, GEMM and attention partials
-  size_t px, pxh, pxl, pqkv, pq, po, ph1, ph3, pgp, patt, ppos, total;
+  size_t px, pxh, pxl, pq, po, pgp, patt, ppos, total;
   size_t pgp_floats;
   // batched decode (max_batch > 1): per chain the QKV output, the W3 output,
   // the GEMM input halves and the K-split partial sums; the rows' positions
   // and sequences
-  size_t bqkv[2], bh3[2], bxh[2], bxl[2], bgp[2], rows;
+  size_t bxh[2], bxl[2], bgp[2], rows;
   size_t bgp_floats[2];
   int nsplit_slow, chunk, rope_len, seq_len, vmax, fast_len, nslots;
+  int chunk_rows, nsplit_rows;  // batched slow attention: positions per split, most splits
 };
 
 Layout make_layout(const dar_config* c) {
@@ -77,6 +78,10 @@ Layout make_layout(const dar_config* c) {
   const int fc = frame_codes(c);
   L.chunk = kAttnChunkDefault;
   L.nsplit_slow = nsplit_slow_of(c);
+  // batched decode: B x n_kv x splits workgroups for the slow attention, the
+  // splits of the longest sequence only (set per frame, eager launches)
+  L.chunk_rows = kAttnChunkDefault;
+  L.nsplit_rows = (c->max_len + L.chunk_rows - 1) / L.chunk_rows;
   L.fast_len = has_fast(c) ? c->n_res + 1 : 1;
   L.rope_len = std::max(c->max_len, L.fast_len);
   L.seq_len = std::max(c->max_len, L.fast_len + 1);
@@ -124,11 +129,8 @@ Layout make_layout(const dar_config* c) {
   L.px = take(sizeof(float) * R * d);
   L.pxh = take(2 * R * kmax);
   L.pxl = take(2 * R * kmax);
-  L.pqkv = take(sizeof(float) * R * qkv_rows);
   L.pq = take(sizeof(float) * R * qw);
   L.po = take(sizeof(float) * R * qw);
-  L.ph1 = take(sizeof(float) * R * F);
-  L.ph3 = take(sizeof(float) * R * F);
   // partial sums of the widest K split launch_gemm picks for the block's GEMMs
   const int wt = c->wtype == DAR_WTYPE_FP8_E4M3_ROW ? W_FP8 : W_BF16;
   L.pgp_floats = 0;
@@ -136,14 +138,12 @@ Layout make_layout(const dar_config* c) {
     for (int M = 1; M <= (int)R; ++M)
       L.pgp_floats = std::max(L.pgp_floats, (size_t)gemm_splits(wt, M, nk.first, nk.second) * M * nk.first);
   }
-  L.pgp = take(sizeof(float) * L.pgp_floats);
+  L.pgp = take(2 * sizeof(float) * L.pgp_floats);  // two regions: W1's and W3's sums live together
   L.patt = take(sizeof(float) * attn_partial_floats((int)R, c->n_heads_kv, L.nsplit_slow, g, c->head_dim));
   L.ppos = take(sizeof(int) * 4);
   if (B > 1) {
     for (int ch = 0; ch < 2; ++ch) {
       const int M = (ch == 0 ? 1 : 2) * B;
-      L.bqkv[ch] = take(sizeof(float) * (size_t)M * qkv_rows);
-      L.bh3[ch] = take(sizeof(float) * (size_t)M * F);
       L.bxh[ch] = take(2 * (size_t)gemm_mpad(M) * kmax);
       L.bxl[ch] = take(2 * (size_t)gemm_mpad(M) * kmax);
       L.bgp_floats[ch] = 0;
@@ -153,7 +153,7 @@ Layout make_layout(const dar_config* c) {
           L.bgp_floats[ch] =
               std::max(L.bgp_floats[ch], (size_t)gemm_splits(wt, m, nk.first, nk.second) * m * nk.first);
       }
-      L.bgp[ch] = take(sizeof(float) * L.bgp_floats[ch]);
+      L.bgp[ch] = take(2 * sizeof(float) * L.bgp_floats[ch]);
     }
     // sequence ids [B], first-pass positions and sequences [2B], pass positions [R+1][B]
     L.rows = take(sizeof(int) * (size_t)(B + 4 * B + (c->n_res + 1) * B));
@@ -273,7 +273,7 @@ struct dar_ctx {
   unsigned long long *slots0, *slotsf;
   int *pred, *committed, *forced, *flags, *pos_s, *pos_f, *seqpos, *ring;
   int B = 1;                   // sequences decoded in lockstep
-  float *bqkv[2], *bh3[2], *bgp[2];
+  float* bgp[2];
   uint16_t *bxh[2], *bxl[2];
   int *seq_ident, *p1_pos, *p1_seq, *pk_pos;
   std::vector<int> pos_hb;     // host mirror of each sequence's next slow position
@@ -282,6 +282,7 @@ struct dar_ctx {
   uint16_t *ks, *vs, *kf, *vf;
 
   int pos_host = 0;       // slow position of the next frame to decode
+  int attn_splits_live = 0;  // batched slow attention splits for the coming frame (0: all)
   bool prefilled = false;
   bool force_dev = false;
   std::string err;
@@ -554,17 +555,19 @@ std::vector<TaskRec> fast_chain(dar_ctx* c) {
 // once (one per sequence; two per sequence in the fast AR's first pass), the
 // projections as MFMA GEMMs over the rows.
 
-Task t_norm(const float* x, int x_stride, int M, int K, const void* gain, float eps, uint16_t* xh, uint16_t* xl,
-            float* out_f32 = nullptr) {
+constexpr PartSum kNoSums{nullptr, 0, 0};
+
+Task t_norm(float* x, int x_stride, int M, int K, const void* gain, float eps, uint16_t* xh, uint16_t* xl,
+            float* out_f32 = nullptr, PartSum add = kNoSums) {
   Task t = none_task();
   t.kind = T_NORM_SPLIT;
   t.M = M;
-  t.norm = NormSplitArgs{x, x_stride, M, K, static_cast<const uint16_t*>(gain), eps, xh, xl, out_f32};
+  t.norm = NormSplitArgs{x, x_stride, M, K, static_cast<const uint16_t*>(gain), eps, xh, xl, out_f32, add};
   return t;
 }
 
 Task t_gemm(int wtype, const void* W, const float* scale, int N, int K, int M, const uint16_t* xh,
-            const uint16_t* xl, float* y, int y_stride, int acc, float* part, size_t cap) {
+            const uint16_t* xl, float* y, int y_stride, int acc, float* part, size_t cap, int defer = 0) {
   Task t = none_task();
   t.kind = T_GEMM;
   t.M = M;
@@ -580,6 +583,7 @@ Task t_gemm(int wtype, const void* W, const float* scale, int N, int K, int M, c
   g.y_stride = y_stride;
   g.accumulate = acc;
   g.part = part;
+  g.defer = defer;
   t.gemm.wtype = wtype;
   t.gemm.part_cap = cap;
   return t;
@@ -590,7 +594,7 @@ Task t_gemm(int wtype, const void* W, const float* scale, int N, int K, int M, c
 // seq_stride elements apart).
 void add_layer_rows(dar_ctx* c, std::vector<TaskRec>& out, int ch, const dar_layer_weights& w, int tag, int M,
                     const int* row_pos, const int* row_seq, uint16_t* kc, uint16_t* vc, int cache_len,
-                    long long seq_stride, int nsplit_max) {
+                    long long seq_stride, int nsplit_max, int chunk, PartSum& pend, bool defer_w2) {
   const dar_config& g = c->cfg;
   const int d = g.d_model, qw = g.n_heads_q * g.head_dim, F = g.ffn_dim;
   const int qkv_rows = (g.n_heads_q + 2 * g.n_heads_kv) * g.head_dim;
@@ -599,14 +603,18 @@ void add_layer_rows(dar_ctx* c, std::vector<TaskRec>& out, int ch, const dar_lay
   uint16_t *xh = c->bxh[ch], *xl = c->bxl[ch];
   float* gp = c->bgp[ch];
   const size_t cap = c->L.bgp_floats[ch];
-  out.push_back(rec(t_norm(cn.x, d, M, d, w.attn_norm, g.rms_eps, xh, xl), K_OTHER, tag));
-  out.push_back(rec(t_gemm(wt, w.wqkv, w.wqkv_scale, qkv_rows, d, M, xh, xl, c->bqkv[ch], qkv_rows, 0, gp, cap),
-                    K_QKV, tag));
+  float* gp2 = gp + cap;  // second region: W3's sums beside W1's
+  // each projection leaves its K-split sums for the row kernel that reads it
+  auto sums = [&](float* part, int N, int K) {
+    return PartSum{part, gemm_launch_splits(wt, M, N, K, cap), (long long)M * N};
+  };
+  out.push_back(rec(t_norm(cn.x, d, M, d, w.attn_norm, g.rms_eps, xh, xl, nullptr, pend), K_OTHER, tag));
+  out.push_back(rec(t_gemm(wt, w.wqkv, w.wqkv_scale, qkv_rows, d, M, xh, xl, nullptr, 0, 0, gp, cap, 1), K_QKV, tag));
   Task t = none_task();
   t.kind = T_ROPE_ROWS;
   t.M = M;
-  t.rope = RopeRowsArgs{c->bqkv[ch], M, row_pos, row_seq, seq_stride, g.n_heads_q, g.n_heads_kv, g.head_dim,
-                        c->rope, cn.q, kc, vc, cache_len};
+  t.rope = RopeRowsArgs{nullptr, sums(gp, qkv_rows, d), M, row_pos, row_seq, seq_stride, g.n_heads_q, g.n_heads_kv,
+                        g.head_dim, c->rope, cn.q, kc, vc, cache_len};
   out.push_back(rec(t, K_OTHER, tag));
   t = none_task();
   t.kind = T_ATTN;
@@ -621,7 +629,7 @@ void add_layer_rows(dar_ctx* c, std::vector<TaskRec>& out, int ch, const dar_lay
   aa.n_heads_q = g.n_heads_q;
   aa.n_heads_kv = g.n_heads_kv;
   aa.head_dim = g.head_dim;
-  aa.chunk = c->L.chunk;
+  aa.chunk = chunk;
   aa.nsplit_max = nsplit_max;
   aa.M = M;
   aa.part = cn.part;
@@ -636,16 +644,22 @@ void add_layer_rows(dar_ctx* c, std::vector<TaskRec>& out, int ch, const dar_lay
     out.push_back(rec(t, K_ATTN, tag));
   }
   out.push_back(rec(t_norm(cn.o, qw, M, qw, nullptr, 0.f, xh, xl), K_OTHER, tag));
-  out.push_back(rec(t_gemm(wt, w.wo, w.wo_scale, d, qw, M, xh, xl, cn.x, d, 1, gp, cap), K_WO, tag));
-  out.push_back(rec(t_norm(cn.x, d, M, d, w.ffn_norm, g.rms_eps, xh, xl), K_OTHER, tag));
-  out.push_back(rec(t_gemm(wt, w.w1, w.w1_scale, F, d, M, xh, xl, cn.h, F, 0, gp, cap), K_W13, tag));
-  out.push_back(rec(t_gemm(wt, w.w3, w.w3_scale, F, d, M, xh, xl, c->bh3[ch], F, 0, gp, cap), K_W13, tag));
+  out.push_back(rec(t_gemm(wt, w.wo, w.wo_scale, d, qw, M, xh, xl, nullptr, 0, 0, gp, cap, 1), K_WO, tag));
+  out.push_back(rec(t_norm(cn.x, d, M, d, w.ffn_norm, g.rms_eps, xh, xl, nullptr, sums(gp, d, qw)), K_OTHER, tag));
+  out.push_back(rec(t_gemm(wt, w.w1, w.w1_scale, F, d, M, xh, xl, nullptr, 0, 0, gp, cap, 1), K_W13, tag));
+  out.push_back(rec(t_gemm(wt, w.w3, w.w3_scale, F, d, M, xh, xl, nullptr, 0, 0, gp2, cap, 1), K_W13, tag));
   t = none_task();
   t.kind = T_SILU_SPLIT;
   t.M = M;
-  t.silu = SiluSplitArgs{cn.h, c->bh3[ch], M, F, xh, xl};
+  t.silu = SiluSplitArgs{nullptr, nullptr, sums(gp, F, d), sums(gp2, F, d), M, F, xh, xl};
   out.push_back(rec(t, K_OTHER, tag));
-  out.push_back(rec(t_gemm(wt, w.w2, w.w2_scale, d, F, M, xh, xl, cn.x, d, 1, gp, cap), K_W2, tag));
+  if (defer_w2) {
+    out.push_back(rec(t_gemm(wt, w.w2, w.w2_scale, d, F, M, xh, xl, nullptr, 0, 0, gp, cap, 1), K_W2, tag));
+    pend = sums(gp, d, F);
+  } else {
+    out.push_back(rec(t_gemm(wt, w.w2, w.w2_scale, d, F, M, xh, xl, cn.x, d, 1, gp, cap), K_W2, tag));
+    pend = kNoSums;
+  }
 }
 
 // Batched slow chain: the slow layers for every sequence at its position, the
@@ -656,10 +670,13 @@ std::vector<TaskRec> slow_chain_rows(dar_ctx* c) {
   const int B = c->B, d = g.d_model;
   std::vector<TaskRec> out;
   const long long seq_stride = (long long)g.n_heads_kv * g.max_len * g.head_dim;
+  PartSum pend = kNoSums;  // the layer's residual sums, added by the next norm
   for (int l = 0; l < g.n_layers_slow; ++l)
     add_layer_rows(c, out, 0, c->slow[l], l, B, c->pos_s, c->seq_ident, c->ks + (size_t)l * B * seq_stride,
-                   c->vs + (size_t)l * B * seq_stride, g.max_len, seq_stride, c->L.nsplit_slow);
-  out.push_back(rec(t_norm(c->cs.x, d, B, d, c->slow_fn, g.rms_eps, c->bxh[0], c->bxl[0], c->ht), K_OTHER, 0));
+                   c->vs + (size_t)l * B * seq_stride, g.max_len, seq_stride, c->L.nsplit_rows, c->L.chunk_rows, pend,
+                   true);
+  out.push_back(
+      rec(t_norm(c->cs.x, d, B, d, c->slow_fn, g.rms_eps, c->bxh[0], c->bxl[0], c->ht, pend), K_OTHER, 0));
   out.push_back(rec(t_gemm(W_BF16, c->w0, nullptr, g.vocab_c0, d, B, c->bxh[0], c->bxl[0], c->logits0, g.vocab_c0, 0,
                            c->bgp[0], c->L.bgp_floats[0]),
                     K_HEAD, 0));
@@ -736,12 +753,15 @@ std::vector<TaskRec> fast_chain_rows(dar_ctx* c) {
     const int M = k == 1 ? 2 * B : B;
     const int* rp = k == 1 ? c->p1_pos : c->pk_pos + (size_t)k * B;
     const int* rs = k == 1 ? c->p1_seq : c->seq_ident;
+    // pass 1's head reads every second row, so its last residual is summed in place
+    PartSum pend = kNoSums;
     for (int l = 0; l < g.n_layers_fast; ++l)
       add_layer_rows(c, out, 1, c->fast[l], 1000 * k + l, M, rp, rs, c->kf + (size_t)l * B * seq_stride,
-                     c->vf + (size_t)l * B * seq_stride, c->L.fast_len, seq_stride, 1);
+                     c->vf + (size_t)l * B * seq_stride, c->L.fast_len, seq_stride, 1, c->L.chunk, pend,
+                     k > 1 || l + 1 < g.n_layers_fast);
     // head on each sequence's last row
     out.push_back(rec(t_norm(c->cf.x + (k == 1 ? d : 0), k == 1 ? 2 * d : d, B, d, c->fast_fn, g.rms_eps, c->bxh[1],
-                             c->bxl[1]),
+                             c->bxl[1], nullptr, pend),
                       K_OTHER, k));
     out.push_back(rec(t_gemm(c->fp8 ? W_FP8 : W_BF16, c->fast_head, c->fast_head_scale, g.vocab_res, d, B, c->bxh[1],
                              c->bxl[1], c->flogits + (size_t)k * c->L.vmax, fc * c->L.vmax, 0, c->bgp[1],
@@ -775,7 +795,9 @@ bool timed(const dar_ctx* c, const Plan& p, size_t i) {
   return c->timed_kind >= 0 && p.kind[i] == c->timed_kind && !(p.layer[i] >= 1000 && p.layer[i] < 2000);
 }
 
-hipError_t enqueue_plan(dar_ctx* c, const Plan& p, hipStream_t s, size_t ev_base = SIZE_MAX) {
+// live: eager launches may trim the batched slow attention to the splits the
+// coming frame's longest sequence has (a captured graph keeps them all)
+hipError_t enqueue_plan(dar_ctx* c, const Plan& p, hipStream_t s, size_t ev_base = SIZE_MAX, bool live = true) {
   const int wt = c->fp8 ? W_FP8 : W_BF16;
   for (size_t i = 0; i < p.launches(); ++i) {
     hipEvent_t before = nullptr, after = nullptr;
@@ -797,7 +819,19 @@ hipError_t enqueue_plan(dar_ctx* c, const Plan& p, hipStream_t s, size_t ev_base
       hipError_t e = hipEventRecord(before, s);
       if (e != hipSuccess) return e;
     }
-    hipError_t e = launch_task(wt, p.tasks[i], s);
+    const Task& t = p.tasks[i];
+    hipError_t e;
+    if (live && c->B > 1 && c->attn_splits_live > 0 && (t.kind == T_ATTN || t.kind == T_COMBINE) &&
+        t.attn.nsplit_max == c->L.nsplit_rows && c->attn_splits_live < c->L.nsplit_rows) {
+      // split s of row m covers positions [s chunk, (s + 1) chunk): rows with
+      // fewer positions leave their later splits empty either way
+      // (at least two: the plan's combine launch follows and merges split partials)
+      Task trimmed = t;
+      trimmed.attn.nsplit_max = std::max(2, c->attn_splits_live);
+      e = launch_task(wt, trimmed, s);
+    } else {
+      e = launch_task(wt, t, s);
+    }
     if (e != hipSuccess) return e;
     if (after) {
       e = hipEventRecord(after, s);
@@ -818,7 +852,7 @@ int run_plan(dar_ctx* c, Plan& p, hipStream_t s, const char* what) {
     for (size_t i = 0; i < p.launches(); ++i)
       DAR_HIP(c, prepare_task(c->fp8 ? W_FP8 : W_BF16, p.tasks[i]), "prepare launch");
     DAR_HIP(c, hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal), "begin capture");
-    hipError_t e = enqueue_plan(c, p, s);
+    hipError_t e = enqueue_plan(c, p, s, SIZE_MAX, false);
     hipGraph_t g = nullptr;
     hipError_t e2 = hipStreamEndCapture(s, &g);
     if (e != hipSuccess) {
@@ -905,15 +939,14 @@ int prefill_blocks(dar_ctx* c, const int32_t* tokens, int n, hipStream_t s, int 
   float* px = reinterpret_cast<float*>(b + L.px);
   uint16_t* xh = reinterpret_cast<uint16_t*>(b + L.pxh);
   uint16_t* xl = reinterpret_cast<uint16_t*>(b + L.pxl);
-  float* pqkv = reinterpret_cast<float*>(b + L.pqkv);
   float* pq = reinterpret_cast<float*>(b + L.pq);
   float* po = reinterpret_cast<float*>(b + L.po);
-  float* ph1 = reinterpret_cast<float*>(b + L.ph1);
-  float* ph3 = reinterpret_cast<float*>(b + L.ph3);
   float* pgp = reinterpret_cast<float*>(b + L.pgp);
   int* ppos = reinterpret_cast<int*>(b + L.ppos);
   const size_t per_layer = (size_t)g.n_heads_kv * g.max_len * g.head_dim;
-  auto gemm = [&](const void* W, const float* scale, int N, int K, int M, float* y, int acc) {
+  float* pgp2 = pgp + L.pgp_floats;  // second region: W3's sums beside W1's
+  auto gemm = [&](const void* W, const float* scale, int N, int K, int M, float* y, int acc, float* part,
+                  int defer) {
     GemmArgs a{};
     a.W = W;
     a.scale = c->fp8 ? scale : nullptr;
@@ -925,22 +958,32 @@ int prefill_blocks(dar_ctx* c, const int32_t* tokens, int n, hipStream_t s, int 
     a.y = y;
     a.y_stride = N;
     a.accumulate = acc;
-    a.part = pgp;
+    a.part = part;
+    a.defer = defer;
     return launch_gemm(wt, a, L.pgp_floats, s);
+  };
+  // K-split sums a deferred projection left in part, for the row kernel that reads it
+  auto sums = [&](float* part, int N, int K, int M) {
+    return PartSum{part, gemm_launch_splits(wt, M, N, K, L.pgp_floats), (long long)M * N};
   };
   int M = 0;
   for (int p0 = 0; p0 < n; p0 += kPrefillRows) {
     M = std::min(kPrefillRows, n - p0);
     DAR_HIP(c, launch_embed_rows(c->w0, g.vocab_c0, d, tokens + p0, M, px, c->flags + 1, s), "prefill embed");
     DAR_HIP(c, launch_fill_i32(ppos, 1, p0, s), "prefill position");
+    PartSum pend{nullptr, 0, 0};  // the previous layer's residual sums
     for (int l = 0; l < g.n_layers_slow; ++l) {
       const dar_layer_weights& w = c->slow[l];
       uint16_t* kc = c->ks + ((size_t)l * c->B + seq) * per_layer;  // layer l of sequence seq
       uint16_t* vc = c->vs + ((size_t)l * c->B + seq) * per_layer;
-      DAR_HIP(c, launch_norm_split(px, d, M, d, static_cast<const uint16_t*>(w.attn_norm), g.rms_eps, xh, xl, s),
+      DAR_HIP(c,
+              launch_norm_split(px, d, M, d, static_cast<const uint16_t*>(w.attn_norm), g.rms_eps, xh, xl, s, nullptr,
+                                pend),
               "prefill attn norm");
-      DAR_HIP(c, gemm(w.wqkv, w.wqkv_scale, qkv_rows, d, M, pqkv, 0), "prefill qkv");
-      DAR_HIP(c, launch_rope_rows(pqkv, M, p0, g.n_heads_q, g.n_heads_kv, g.head_dim, c->rope, pq, kc, vc, g.max_len, s),
+      DAR_HIP(c, gemm(w.wqkv, w.wqkv_scale, qkv_rows, d, M, nullptr, 0, pgp, 1), "prefill qkv");
+      DAR_HIP(c,
+              launch_rope_rows(nullptr, M, p0, g.n_heads_q, g.n_heads_kv, g.head_dim, c->rope, pq, kc, vc, g.max_len,
+                               s, nullptr, nullptr, 0, sums(pgp, qkv_rows, d, M)),
               "prefill rope");
       Task t{};
       t.kind = T_ATTN;
@@ -967,13 +1010,19 @@ int prefill_blocks(dar_ctx* c, const int32_t* tokens, int n, hipStream_t s, int 
         DAR_HIP(c, launch_task(wt, t, s), "prefill attention combine");
       }
       DAR_HIP(c, launch_norm_split(po, qw, M, qw, nullptr, 0.f, xh, xl, s), "prefill split o");
-      DAR_HIP(c, gemm(w.wo, w.wo_scale, d, qw, M, px, 1), "prefill wo");
-      DAR_HIP(c, launch_norm_split(px, d, M, d, static_cast<const uint16_t*>(w.ffn_norm), g.rms_eps, xh, xl, s),
+      DAR_HIP(c, gemm(w.wo, w.wo_scale, d, qw, M, nullptr, 0, pgp, 1), "prefill wo");
+      DAR_HIP(c,
+              launch_norm_split(px, d, M, d, static_cast<const uint16_t*>(w.ffn_norm), g.rms_eps, xh, xl, s, nullptr,
+                                sums(pgp, d, qw, M)),
               "prefill ffn norm");
-      DAR_HIP(c, gemm(w.w1, w.w1_scale, F, d, M, ph1, 0), "prefill w1");
-      DAR_HIP(c, gemm(w.w3, w.w3_scale, F, d, M, ph3, 0), "prefill w3");
-      DAR_HIP(c, launch_silu_split(ph1, ph3, M, F, xh, xl, s), "prefill silu");
-      DAR_HIP(c, gemm(w.w2, w.w2_scale, d, F, M, px, 1), "prefill w2");
+      DAR_HIP(c, gemm(w.w1, w.w1_scale, F, d, M, nullptr, 0, pgp, 1), "prefill w1");
+      DAR_HIP(c, gemm(w.w3, w.w3_scale, F, d, M, nullptr, 0, pgp2, 1), "prefill w3");
+      DAR_HIP(c, launch_silu_split(nullptr, nullptr, M, F, xh, xl, s, sums(pgp, F, d, M), sums(pgp2, F, d, M)),
+              "prefill silu");
+      // the block's last residual is summed in place (its last row leaves the block)
+      const bool last = l + 1 == g.n_layers_slow;
+      DAR_HIP(c, gemm(w.w2, w.w2_scale, d, F, M, last ? px : nullptr, 1, pgp, last ? 0 : 1), "prefill w2");
+      pend = last ? PartSum{nullptr, 0, 0} : sums(pgp, d, F, M);
     }
   }
   // the last position's residual becomes the sequence's slow row (the head's input)
@@ -1105,8 +1154,6 @@ int dar_create(const dar_config* cfg, const dar_weights* w, void* workspace, siz
   c->pos_f = c->pos_s + c->B;
   if (c->B > 1) {
     for (int ch = 0; ch < 2; ++ch) {
-      c->bqkv[ch] = reinterpret_cast<float*>(b + L.bqkv[ch]);
-      c->bh3[ch] = reinterpret_cast<float*>(b + L.bh3[ch]);
       c->bgp[ch] = reinterpret_cast<float*>(b + L.bgp[ch]);
       c->bxh[ch] = reinterpret_cast<uint16_t*>(b + L.bxh[ch]);
       c->bxl[ch] = reinterpret_cast<uint16_t*>(b + L.bxl[ch]);
@@ -1243,10 +1290,18 @@ int dar_prefill(dar_ctx* c, int32_t batch, const int32_t* tokens, const int32_t*
   if (c->B == 1) {
     DAR_HIP(c, launch_task(wt, c->p_slow.tasks.back(), s), "prefill head");
   } else {
+    // the slow chain's final norm, head and position step; the prompt rows
+    // are complete, so the norm adds no pending layer sums
     const size_t nt = c->p_slow.tasks.size();
-    for (size_t i = nt - 3; i < nt; ++i) DAR_HIP(c, launch_task(wt, c->p_slow.tasks[i], s), "prefill head");
+    for (size_t i = nt - 3; i < nt; ++i) {
+      Task t = c->p_slow.tasks[i];
+      if (t.kind == T_NORM_SPLIT) t.norm.add = PartSum{nullptr, 0, 0};
+      DAR_HIP(c, launch_task(wt, t, s), "prefill head");
+    }
   }
   DAR_HIP(c, hipEventRecord(c->ev_s_done, s), "record slow done");
+  // the slow chain runs the longest sequence at position nmax
+  c->attn_splits_live = (nmax + 1 + c->L.chunk_rows) / c->L.chunk_rows;
   const int st = pipeline_step(c, forced, codes_out, logits_out, nmax < c->cfg.max_len);
   if (st != DAR_OK) return st;
   for (int b = 0; b < batch; ++b) c->pos_hb[b] = lens_host[b];
@@ -1265,6 +1320,8 @@ int dar_decode_frame(dar_ctx* c, const int32_t* forced, int32_t* codes_out, floa
     c->err = "position reached max_len";
     return DAR_E_CAPACITY;
   }
+  // the slow chain runs the longest sequence at position pos_host + 1
+  c->attn_splits_live = (c->pos_host + 2 + c->L.chunk_rows) / c->L.chunk_rows;
   const int st = pipeline_step(c, forced, codes_out, logits_out, c->pos_host + 1 < c->cfg.max_len);
   if (st != DAR_OK) return st;
   c->pos_host += 1;
@@ -1442,7 +1499,8 @@ int dar_op_gemm(int32_t wtype, const void* W, const float* scale, int32_t N, int
   a.y_stride = N;
   a.accumulate = 0;
   a.part = reinterpret_cast<float*>(scratch + 2 * half_bytes);
-  if ((e = launch_norm_split(x, K, M, K, nullptr, 0.f, xh, xl, s)) == hipSuccess &&
+  // x is only read: no sums are pending
+  if ((e = launch_norm_split(const_cast<float*>(x), K, M, K, nullptr, 0.f, xh, xl, s)) == hipSuccess &&
       (e = launch_gemm(wtype == DAR_WTYPE_FP8_E4M3_ROW ? W_FP8 : W_BF16, a, part_cap, s)) == hipSuccess)
     e = hipStreamSynchronize(s);
   (void)hipStreamSynchronize(s);

@@ -3,8 +3,8 @@
 Tiny Dual-AR (2 slow layers, 1 fast layer, d 256): each sequence of the batch
 is teacher-forced with its own oracle greedy frames and compared with its own
 oracle run (logits rel-L2, argmax agreement, exact codes above the margin),
-bf16 and fp8, at B = 4 and at the largest batch (64, whose first fast pass is
-a 128-row GEMM). At full shape (36 + 4 layers, d 2560): a batch of two equals
+bf16 and fp8, at B = 4, at the largest batch (64, whose first fast pass is
+a 128-row GEMM) and with prompts long enough for several attention splits. At full shape (36 + 4 layers, d 2560): a batch of two equals
 two batch-1 contexts decoding the same prompts (same codes where the margin
 exceeds 1e-2, logits within the bf16 tolerance).
 """
@@ -32,13 +32,18 @@ def _oracle_frames(model, prompt, frames, max_len):
     return out
 
 
-@pytest.mark.parametrize("wtype,B,frames", [("bf16", 4, 20), ("fp8", 4, 20), ("bf16", 64, 2)])
-def test_tiny_batched_parity(tiny_host, wtype, B, frames):
+# the last case spans several 64-position attention splits, with the longest
+# sequence crossing a split boundary while the frames are decoded
+@pytest.mark.parametrize("wtype,B,frames,max_len,lmax",
+                         [("bf16", 4, 20, 48, 24), ("fp8", 4, 20, 48, 24), ("bf16", 64, 2, 48, 24),
+                          ("bf16", 3, 24, 200, 130)])
+def test_tiny_batched_parity(tiny_host, wtype, B, frames, max_len, lmax):
     from dar_decode_frame_amd.session import DarSession, DeviceWeights
     dims, host = tiny_host
-    max_len = 48
     rng = np.random.default_rng(7)
-    lens = [int(x) for x in rng.integers(4, 24, B)]
+    lens = [int(x) for x in rng.integers(4, lmax, B)]
+    if lmax > 64:
+        lens[0] = lmax - 10  # frames take it across position 128
     prompts = [synth.gen_prompt(n, dims.vocab_c0, 100 + b) for b, n in enumerate(lens)]
     model = OracleModel(dims, host, wtype=wtype)
     refs = [_oracle_frames(model, p, frames, max_len) for p in prompts]
