@@ -215,6 +215,7 @@ __global__ void k_gemm_reduce(GemmArgs a) {
 }
 
 // Block reduction of one value per thread; result in every thread.
+template <int NW = kWaves>
 __device__ __forceinline__ float block_sum(float v, float* red) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
@@ -222,32 +223,38 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
   __syncthreads();
   float t = 0.f;
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) t += red[w];
+  for (int w = 0; w < NW; ++w) t += red[w];
   __syncthreads();
   return t;
 }
+
+constexpr int kNormBlock = 1024;  // threads per row of k_norm_split (a float4 each at d = 4096)
 
 __device__ __forceinline__ float4 ld4(const float* p) { return *reinterpret_cast<const float4*>(p); }
 __device__ __forceinline__ float4 add4(float4 a, float4 b) { return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w); }
 
 // Four consecutive elements of a pending split-K sum starting at element idx
-// (fixed order: four running sums over the splits, then combined), so that
-// the splits' loads are in flight together.
+// (fixed order: splits in groups of eight, each group summed pairwise), so
+// that up to eight splits' loads are in flight together.
 __device__ __forceinline__ float4 part_sum4(const PartSum& ps, size_t idx) {
   const float* p = ps.p + idx;
-  const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
-  float4 s0 = z4, s1 = z4, s2 = z4, s3 = z4;
+  float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
   int z = 0;
-  for (; z + 4 <= ps.n; z += 4) {
-    const float4 a = ld4(p + (size_t)z * ps.stride), b = ld4(p + (size_t)(z + 1) * ps.stride);
-    const float4 c = ld4(p + (size_t)(z + 2) * ps.stride), d = ld4(p + (size_t)(z + 3) * ps.stride);
-    s0 = add4(s0, a);
-    s1 = add4(s1, b);
-    s2 = add4(s2, c);
-    s3 = add4(s3, d);
+  for (; z + 8 <= ps.n; z += 8) {
+    float4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = ld4(p + (size_t)(z + u) * ps.stride);
+    s = add4(s, add4(add4(add4(v[0], v[1]), add4(v[2], v[3])), add4(add4(v[4], v[5]), add4(v[6], v[7]))));
   }
-  for (; z < ps.n; ++z) s0 = add4(s0, ld4(p + (size_t)z * ps.stride));
-  return add4(add4(s0, s1), add4(s2, s3));
+  if (z + 4 <= ps.n) {
+    float4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = ld4(p + (size_t)(z + u) * ps.stride);
+    s = add4(s, add4(add4(v[0], v[1]), add4(v[2], v[3])));
+    z += 4;
+  }
+  for (; z < ps.n; ++z) s = add4(s, ld4(p + (size_t)z * ps.stride));
+  return s;
 }
 
 // hi/lo bf16 of four values, stored as 8 bytes each
@@ -263,21 +270,22 @@ __device__ __forceinline__ void split_store4(float4 v, uint16_t* oh, uint16_t* o
 // written as hi = bf16(v), lo = bf16(v - hi); rows M..Mpad-1 are zero. With
 // residual sums pending, x[m] += their sum first (written back). With out_f32
 // set, v is also written there in fp32 (row stride K). Columns in fours.
-__global__ __launch_bounds__(kBlock) void k_norm_split(float* x, int x_stride, int M, int K, const uint16_t* gain,
-                                                        float eps, uint16_t* xh, uint16_t* xl, float* out_f32,
-                                                        PartSum add) {
-  __shared__ float red[kWaves];
+__global__ __launch_bounds__(kNormBlock) void k_norm_split(float* x, int x_stride, int M, int K,
+                                                            const uint16_t* gain, float eps, uint16_t* xh,
+                                                            uint16_t* xl, float* out_f32, PartSum add) {
+  constexpr int NW = kNormBlock / kWave;
+  __shared__ float red[NW];
   const int m = blockIdx.x, tid = threadIdx.x;
   uint16_t* oh = xh + (size_t)m * K;
   uint16_t* ol = xl + (size_t)m * K;
   if (m >= M) {
-    for (int k = tid; k < K; k += kBlock) oh[k] = ol[k] = 0;
+    for (int k = tid; k < K; k += kNormBlock) oh[k] = ol[k] = 0;
     return;
   }
   float* xr = x + (size_t)m * x_stride;
   float ss = 0.f;
   if (add.n > 0 || gain) {
-    for (int k = 4 * tid; k < K; k += 4 * kBlock) {
+    for (int k = 4 * tid; k < K; k += 4 * kNormBlock) {
       float4 v = ld4(xr + k);
       if (add.n > 0) {
         v = add4(v, part_sum4(add, (size_t)m * K + k));
@@ -288,11 +296,11 @@ __global__ __launch_bounds__(kBlock) void k_norm_split(float* x, int x_stride, i
   }
   float inv = 1.f;
   if (gain) {
-    ss = block_sum(ss, red);
+    ss = block_sum<NW>(ss, red);
     inv = 1.0f / sqrtf(ss / (float)K + eps);
   }
   // each thread rereads only the columns it wrote above
-  for (int k = 4 * tid; k < K; k += 4 * kBlock) {
+  for (int k = 4 * tid; k < K; k += 4 * kNormBlock) {
     float4 v = ld4(xr + k);
     if (gain) {
       const u32x2 g = *reinterpret_cast<const u32x2*>(gain + k);
@@ -523,7 +531,7 @@ hipError_t launch_gemm(int wtype, GemmArgs a, size_t part_cap, hipStream_t s) {
 hipError_t launch_norm_split(float* x, int x_stride, int M, int K, const uint16_t* gain, float eps, uint16_t* xh,
                              uint16_t* xl, hipStream_t s, float* out_f32, PartSum add) {
   if (K % 4 || x_stride % 4 || (add.n > 0 && x_stride != K)) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_norm_split, dim3(gemm_mpad(M)), dim3(kBlock), 0, s, x, x_stride, M, K, gain, eps, xh, xl,
+  hipLaunchKernelGGL(k_norm_split, dim3(gemm_mpad(M)), dim3(kNormBlock), 0, s, x, x_stride, M, K, gain, eps, xh, xl,
                      out_f32, add);
   return hipGetLastError();
 }
