@@ -59,7 +59,11 @@ typedef enum {
  * Requirements: head_dim in {64, 128}; n_heads_q a multiple of n_heads_kv;
  * d_model, ffn_dim and n_heads_q*head_dim multiples of 256 and at most 16384;
  * n_res in [0, 15]; n_res > 0 needs n_layers_fast >= 1 and vocab_res >= 1;
- * max_batch == 1 (batched decode is not in this version: DAR_E_UNSUPPORTED). */
+ * max_batch in [1, 64] (above 64: DAR_E_UNSUPPORTED). With max_batch > 1 the
+ * context decodes that many sequences in lockstep, each with its own prompt
+ * length and KV cache; every projection then reads its weights once for all
+ * of them (the fish-speech fork README's serving notes: the Dual-AR model
+ * takes the batching of ordinary LLM serving). */
 typedef struct {
   int32_t n_layers_slow;
   int32_t n_layers_fast;  /* 0 with n_res == 0: slow-AR-only decode (frame = 1 code) */
@@ -137,8 +141,11 @@ int dar_create(const dar_config* cfg, const dar_weights* weights, void* workspac
 
 /* Prefill a prompt and produce frame 0 (the tuna-fish README's
  * "prefill ... decode" run). Positions restart at 0: any previous state is
- * dropped. tokens: device int32 [lens_host[0]] ids in [0, vocab_c0); lens_host:
- * host int32 [batch]; 1 <= lens_host[0] < max_len. forced: NULL or device int32
+ * dropped. batch must equal max_batch (DAR_E_CAPACITY above it, DAR_E_INVAL
+ * below). tokens: device int32, the batch's prompts one after another
+ * (sum of lens_host ids in [0, vocab_c0)); lens_host: host int32 [batch],
+ * 1 <= lens_host[b] < max_len (0: DAR_E_INVAL, >= max_len: DAR_E_CAPACITY).
+ * Sequence b's frame 0 sits at position lens_host[b] - 1. forced: NULL or device int32
  * [batch][1+n_res], the frame the following steps consume instead of the
  * argmax codes (teacher forcing). codes_out: NULL or device int32
  * [batch][1+n_res] argmax codes of frame 0. logits_out: NULL or device fp32
@@ -156,8 +163,9 @@ int dar_prefill(dar_ctx* ctx, int32_t batch, const int32_t* tokens, const int32_
  * the same time, the slow step and codebook-0 head of the next position. The
  * work is ordered after what is already queued on the ctx's stream, and that
  * stream waits for both internal streams before anything queued later.
- * Errors: DAR_E_STATE before prefill, DAR_E_CAPACITY when the position has
- * reached max_len. */
+ * With a batch every sequence advances one position per call.
+ * Errors: DAR_E_STATE before prefill, DAR_E_CAPACITY when the longest
+ * sequence's position has reached max_len. */
 int dar_decode_frame(dar_ctx* ctx, const int32_t* forced, int32_t* codes_out, float* logits_out);
 
 /* Release the context (graph, events, host state). Waits for the context's
