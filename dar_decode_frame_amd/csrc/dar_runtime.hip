@@ -283,6 +283,7 @@ struct dar_ctx {
 
   int pos_host = 0;       // slow position of the next frame to decode
   int attn_splits_live = 0;  // batched slow attention splits for the coming frame (0: all)
+  int attn_chunk_live = 0;   // and the positions per split
   bool prefilled = false;
   bool force_dev = false;
   std::string err;
@@ -795,6 +796,23 @@ bool timed(const dar_ctx* c, const Plan& p, size_t i) {
   return c->timed_kind >= 0 && p.kind[i] == c->timed_kind && !(p.layer[i] >= 1000 && p.layer[i] < 2000);
 }
 
+// Batched slow attention of the coming frame, whose rows attend over at most
+// tmax positions: the splits that covers, with longer splits when the launch
+// has work enough (measured at 16 and 64 sequences: 64 positions per split
+// win at about 1k workgroups, 256 from there on).
+void set_live_attention(dar_ctx* c, int tmax) {
+  const int n_kv = c->cfg.n_heads_kv;
+  int chunk = c->L.chunk_rows;
+  for (int cand : {4 * c->L.chunk_rows, 2 * c->L.chunk_rows}) {
+    if ((long long)c->B * n_kv * ((tmax + cand - 1) / cand) >= 1024) {
+      chunk = cand;
+      break;
+    }
+  }
+  c->attn_chunk_live = chunk;
+  c->attn_splits_live = (tmax + chunk - 1) / chunk;
+}
+
 // live: eager launches may trim the batched slow attention to the splits the
 // coming frame's longest sequence has (a captured graph keeps them all)
 hipError_t enqueue_plan(dar_ctx* c, const Plan& p, hipStream_t s, size_t ev_base = SIZE_MAX, bool live = true) {
@@ -821,12 +839,15 @@ hipError_t enqueue_plan(dar_ctx* c, const Plan& p, hipStream_t s, size_t ev_base
     }
     const Task& t = p.tasks[i];
     hipError_t e;
-    if (live && c->B > 1 && c->attn_splits_live > 0 && (t.kind == T_ATTN || t.kind == T_COMBINE) &&
-        t.attn.nsplit_max == c->L.nsplit_rows && c->attn_splits_live < c->L.nsplit_rows) {
+    // (the batched slow attention: the plan's split attention followed by its
+    // combine, nsplit_rows > 1; the fast AR's attention has one split)
+    if (live && c->B > 1 && c->attn_splits_live > 0 && c->L.nsplit_rows > 1 &&
+        (t.kind == T_ATTN || t.kind == T_COMBINE) && t.attn.nsplit_max == c->L.nsplit_rows) {
       // split s of row m covers positions [s chunk, (s + 1) chunk): rows with
-      // fewer positions leave their later splits empty either way
-      // (at least two: the plan's combine launch follows and merges split partials)
+      // fewer positions leave their later splits empty either way; at least
+      // two splits, as the combine launch merges split partials
       Task trimmed = t;
+      trimmed.attn.chunk = c->attn_chunk_live;
       trimmed.attn.nsplit_max = std::max(2, c->attn_splits_live);
       e = launch_task(wt, trimmed, s);
     } else {
@@ -1301,7 +1322,7 @@ int dar_prefill(dar_ctx* c, int32_t batch, const int32_t* tokens, const int32_t*
   }
   DAR_HIP(c, hipEventRecord(c->ev_s_done, s), "record slow done");
   // the slow chain runs the longest sequence at position nmax
-  c->attn_splits_live = (nmax + 1 + c->L.chunk_rows) / c->L.chunk_rows;
+  set_live_attention(c, nmax + 1);
   const int st = pipeline_step(c, forced, codes_out, logits_out, nmax < c->cfg.max_len);
   if (st != DAR_OK) return st;
   for (int b = 0; b < batch; ++b) c->pos_hb[b] = lens_host[b];
@@ -1321,7 +1342,7 @@ int dar_decode_frame(dar_ctx* c, const int32_t* forced, int32_t* codes_out, floa
     return DAR_E_CAPACITY;
   }
   // the slow chain runs the longest sequence at position pos_host + 1
-  c->attn_splits_live = (c->pos_host + 2 + c->L.chunk_rows) / c->L.chunk_rows;
+  set_live_attention(c, c->pos_host + 2);
   const int st = pipeline_step(c, forced, codes_out, logits_out, c->pos_host + 1 < c->cfg.max_len);
   if (st != DAR_OK) return st;
   c->pos_host += 1;
@@ -1613,6 +1634,7 @@ int dar_profile_frame(dar_ctx* c, int32_t cap, float* ms_out, int32_t* kind_out,
     c->events.push_back(ev);
   }
   // the same frame as dar_decode_frame, every launch on one stream and bracketed by events
+  set_live_attention(c, c->pos_host + 2);
   hipStream_t s = c->cf.s;
   DAR_HIP(c, hipEventRecord(c->ev_start, c->stream), "record start");
   DAR_HIP(c, hipStreamWaitEvent(s, c->ev_start, 0), "wait start");
