@@ -33,7 +33,9 @@ def log(msg):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=896)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed frames (default: 896 at batch 1; a batched workload runs until its longest "
+                         "sequence reaches max_len)")
     ap.add_argument("--warmup", type=int, default=16)
     ap.add_argument("--workload", default="s2pro_dual_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -61,6 +63,8 @@ def main():
     if wl.batch != 1:
         return bench_batched(args, wl)
     max_steps = wl.max_len - wl.prefill_len
+    if args.steps is None:
+        args.steps = 896
     if args.steps > max_steps or args.steps < 1:
         raise SystemExit(f"--steps must be in [1, {max_steps}] for {wl.name}")
     dev = torch.device("cuda:0")
@@ -199,7 +203,8 @@ def main():
 
 def bench_batched(args, wl):
     """Batched decode (the workload's sequences in lockstep, ragged prompts):
-    aggregate frames/s over --steps lockstep steps, algorithmic bytes = the
+    aggregate frames/s over --steps lockstep steps (default: until the longest
+    sequence reaches max_len), algorithmic bytes = the
     weights once per step + every sequence's KV reads, and the dominant
     launch kind of serialised steps against HBM and its MFMA rate."""
     import numpy as np
@@ -215,7 +220,7 @@ def bench_batched(args, wl):
     lens, prompts = synth.gen_ragged_prompts(B, wl.prefill_len, wl.prefill_len_max, dims.vocab_c0, wl.prompt_seed,
                                             wl.length_seed)
     max_steps = wl.max_len - int(lens.max())
-    steps = min(args.steps, max_steps)
+    steps = max_steps if args.steps is None else min(args.steps, max_steps)
     t0 = time.time()
     host = synth.gen_weights(dims, wl.weight_seed)
     weights = DeviceWeights(dims, host, wl.wtype, dev)

@@ -15,6 +15,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "dar_internal.h"
 
 namespace dar {
@@ -87,6 +89,33 @@ struct FP8T {
     return __builtin_bit_cast(bf16x8, o);
   }
 };
+
+// The workgroup's finished sums: lane l holds weight row (output column) n =
+// its tile row, and accumulator v of tile mt holds input row
+// m0 + 32 mt + (v % 4) + 4 (l / 32) + 8 (v / 4). Split partials carry the row
+// scale when deferred (the reduce pass applies it otherwise).
+template <int MT>
+__device__ __forceinline__ void gemm_store(const GemmArgs& a, const f32x16 (&acc)[MT], int n, int m0, int lane) {
+  if (n >= a.N) return;
+  const float sc = (a.scale && (a.splits == 1 || a.defer)) ? a.scale[n] : 1.f;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int m = m0 + mt * 32 + (v % 4) + 4 * (lane >> 5) + 8 * (v / 4);
+      if (m >= a.M) continue;
+      if (a.defer) {
+        a.part[((size_t)blockIdx.z * a.M + m) * a.N + n] = acc[mt][v] * sc;
+      } else if (a.splits == 1) {
+        float* y = a.y + (size_t)m * a.y_stride + n;
+        const float val = acc[mt][v] * sc;
+        *y = a.accumulate ? *y + val : val;
+      } else {
+        a.part[((size_t)blockIdx.z * a.M + m) * a.N + n] = acc[mt][v];
+      }
+    }
+  }
+}
 
 // One workgroup: weight rows [128 bx, +128) (wave w: 32 rows) x input rows
 // [32 MT by, +32 MT) x the chunks of split bz. A chunk is 128 B of each
@@ -178,27 +207,107 @@ __global__ __launch_bounds__(kBlock) void k_gemm(GemmArgs a) {
       }
     }
   }
-  // accumulator v of lane l holds row (v % 4) + 4 (l / 32) + 8 (v / 4), column l % 32
-  const int n = nb + wave * 32 + (lane & 31);
-  if (n >= a.N) return;
-  const float sc = (a.scale && (a.splits == 1 || a.defer)) ? a.scale[n] : 1.f;
+  gemm_store<MT>(a, acc, nb + wave * 32 + (lane & 31), m0, lane);
+}
+
+// s_waitcnt vmcnt(4 n) for a count n in [0, 5] known only at run time
+__device__ __forceinline__ void wait_loads_x4(int n) {
+  switch (n) {
+    case 0: wait_loads<0>(); break;
+    case 1: wait_loads<4>(); break;
+    case 2: wait_loads<8>(); break;
+    case 3: wait_loads<12>(); break;
+    case 4: wait_loads<16>(); break;
+    default: wait_loads<20>(); break;
+  }
+}
+
+// Up to 32 input rows (MT = 1) with the split's input resident: the
+// workgroup first moves all of its split's input chunks into LDS (one
+// barrier), then every wave streams only its own 32 weight rows through its
+// own ring of kStages chunk slots, waiting on its own loads alone: no
+// workgroup barrier per chunk. The hi and lo products accumulate separately
+// so that consecutive MFMAs do not wait on each other. Same LDS layouts as
+// k_gemm. Needs a.cps <= kResidentChunks<WT>. (Staging only 16 input rows
+// for a six-slot ring was tried at 16 sequences: no faster.)
+template <typename WT>
+constexpr int kResidentChunks = WT::kBytes == 2 ? 14 : 7;  // an e4m3 chunk spans twice the input columns
+
+template <typename WT>
+__global__ __launch_bounds__(kBlock) void k_gemm_x(GemmArgs a) {
+  constexpr int KC = kRowChunk / WT::kBytes;
+  constexpr int ST = KC / 16;
+  constexpr int XU = KC / 8;
+  constexpr int XROWS = 32;                            // staged input rows
+  constexpr int XB = 2 * XROWS * XU * 16;              // input bytes per chunk (hi, lo)
+  constexpr int XL = XB / (16 * 64 * kWaves);          // input loads per wave per chunk
+  constexpr int WS = 32 * kRowChunk;                   // one wave's weight bytes per chunk
+  constexpr int S = kStages;                           // ring slots per wave
+  constexpr int XR = kResidentChunks<WT> * XB;
+  static_assert(XL * 16 * 64 * kWaves == XB, "input staging split");
+  static_assert(XR + kWaves * S * WS <= 160 * 1024, "LDS");
+  __shared__ __align__(16) char sm[XR + kWaves * S * WS];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nb = blockIdx.x * kTileN;
+  const int c_begin = blockIdx.z * a.cps;
+  const int nc = min(a.K / KC, c_begin + a.cps) - c_begin;
+  char* ring = sm + XR + wave * S * WS;
+  const char* wsrc[4];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
+  for (int i = 0; i < 4; ++i) {
+    const int r = wave * 32 + 8 * i + (lane >> 3);
+    wsrc[i] = reinterpret_cast<const char*>(a.W) + (size_t)min(nb + r, a.N - 1) * a.K * WT::kBytes +
+              (size_t)c_begin * kRowChunk + 16 * ((lane & 7) ^ (lane >> 3));
+  }
+  auto issue_w = [&](int t) {
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int m = m0 + mt * 32 + (v % 4) + 4 * (lane >> 5) + 8 * (v / 4);
-      if (m >= a.M) continue;
-      if (a.defer) {
-        a.part[((size_t)blockIdx.z * a.M + m) * a.N + n] = acc[mt][v] * sc;
-      } else if (a.splits == 1) {
-        float* y = a.y + (size_t)m * a.y_stride + n;
-        const float val = acc[mt][v] * sc;
-        *y = a.accumulate ? *y + val : val;
-      } else {
-        a.part[((size_t)blockIdx.z * a.M + m) * a.N + n] = acc[mt][v];
-      }
+    for (int i = 0; i < 4; ++i) load_lds16(wsrc[i] + (size_t)t * kRowChunk, ring + (t % S) * WS + i * 1024);
+  };
+  // the split's input, chunk t at sm + t XB
+  for (int t = 0; t < nc; ++t) {
+#pragma unroll
+    for (int j = 0; j < XL; ++j) {
+      const int q0 = (wave * XL + j) * 64;
+      const int part = q0 / (XROWS * XU);
+      const int q = q0 % (XROWS * XU) + lane;
+      const int row = q / XU, u = (q % XU) ^ (row & 7);
+      load_lds16(reinterpret_cast<const char*>(part ? a.xl : a.xh) +
+                     ((size_t)row * a.K + (size_t)(c_begin + t) * KC) * 2 + 16 * u,
+                 sm + t * XB + (wave * XL + j) * 1024);
     }
   }
+  for (int j = 0; j < S - 1 && j < nc; ++j) issue_w(j);
+  // the input has landed for this wave once only its weight loads are outstanding
+  wait_loads_x4(min(S - 1, nc));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  f32x16 acc[1], acc_lo;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) acc[0][v] = acc_lo[v] = 0.f;
+  const int half = lane >> 5;
+  const int xrow = lane & 31;
+  for (int t = 0; t < nc; ++t) {
+    // this wave's chunk t has landed once only its later chunks' loads are outstanding
+    wait_loads_x4(min(S - 2, nc - 1 - t));
+    asm volatile("" ::: "memory");
+    // the slot refilled here held chunk t - 1, whose reads this wave finished
+    if (t + S - 1 < nc) issue_w(t + S - 1);
+    const char* ws = ring + (t % S) * WS;
+    const char* xs = sm + t * XB;
+#pragma unroll
+    for (int s = 0; s < ST; ++s) {
+      const bf16x8 b = WT::frag(ws, lane & 31, s, half);
+      const int u = (2 * s + half) ^ (xrow & 7);
+      const bf16x8 ah = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(xs + (xrow * XU + u) * 16));
+      const bf16x8 al =
+          __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(xs + ((XROWS + xrow) * XU + u) * 16));
+      acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, b, acc[0], 0, 0, 0);
+      acc_lo = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, b, acc_lo, 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int v = 0; v < 16; ++v) acc[0][v] += acc_lo[v];
+  gemm_store<1>(a, acc, nb + wave * 32 + (lane & 31), 0, lane);
 }
 
 // y[m][n] (+)= scale[n] * sum over splits (fixed order) of the partial sums
@@ -465,11 +574,20 @@ __global__ void k_inc_rows(int* v, int n) {
 
 hipError_t gemm_dispatch(int wtype, const GemmArgs& a, int mt, dim3 grid, hipStream_t s) {
   if (wtype == W_FP8) {
-    if (mt == 1) hipLaunchKernelGGL((k_gemm<FP8T, 1>), grid, dim3(kBlock), 0, s, a);
-    else hipLaunchKernelGGL((k_gemm<FP8T, 2>), grid, dim3(kBlock), 0, s, a);
+    if (mt == 1 && a.cps <= kResidentChunks<FP8T>)
+      hipLaunchKernelGGL((k_gemm_x<FP8T>), grid, dim3(kBlock), 0, s, a);
+    else if (mt == 1)
+      hipLaunchKernelGGL((k_gemm<FP8T, 1>), grid, dim3(kBlock), 0, s, a);
+    else
+      hipLaunchKernelGGL((k_gemm<FP8T, 2>), grid, dim3(kBlock), 0, s, a);
   } else {
     switch (mt) {
-      case 1: hipLaunchKernelGGL((k_gemm<BF16T, 1>), grid, dim3(kBlock), 0, s, a); break;
+      case 1:
+        if (a.cps <= kResidentChunks<BF16T>)
+          hipLaunchKernelGGL((k_gemm_x<BF16T>), grid, dim3(kBlock), 0, s, a);
+        else
+          hipLaunchKernelGGL((k_gemm<BF16T, 1>), grid, dim3(kBlock), 0, s, a);
+        break;
       case 2: hipLaunchKernelGGL((k_gemm<BF16T, 2>), grid, dim3(kBlock), 0, s, a); break;
       default: hipLaunchKernelGGL((k_gemm<BF16T, 4>), grid, dim3(kBlock), 0, s, a); break;
     }
@@ -490,12 +608,17 @@ static int gemm_mt(int wtype, int M) {
 
 // K splits: as many as keep the launch within one workgroup per CU (a
 // workgroup's LDS ring and loads in flight are what stream the weights; a
-// second one on a CU adds no bandwidth), each split at least one chunk
+// second one on a CU adds no bandwidth), each split at least one chunk; up
+// to 32 rows, few enough chunks per split for the resident-input kernel
 int gemm_splits(int wtype, int M, int N, int K) {
   const int mt = gemm_mt(wtype, M);
   const int tiles = ((N + kTileN - 1) / kTileN) * ((M + 32 * mt - 1) / (32 * mt));
   const int nchunks = K / (kRowChunk / (wtype == W_FP8 ? 1 : 2));
   int splits = 256 / tiles;
+  if (mt == 1) {
+    const int resident = wtype == W_FP8 ? kResidentChunks<FP8T> : kResidentChunks<BF16T>;
+    splits = std::max(splits, (nchunks + resident - 1) / resident);
+  }
   splits = splits < 1 ? 1 : (splits > nchunks ? nchunks : splits);
   const int cps = (nchunks + splits - 1) / splits;
   return (nchunks + cps - 1) / cps;
