@@ -224,7 +224,8 @@ def bench_batched(args, wl):
     t0 = time.time()
     host = synth.gen_weights(dims, wl.weight_seed)
     weights = DeviceWeights(dims, host, wl.wtype, dev)
-    del host
+    if args.no_cpu_baseline:
+        del host
     log(f"weights ready in {time.time() - t0:.1f}s; {B} prompts of {int(lens.min())}..{int(lens.max())} ids")
     sess = DarSession(dims, weights, wl.max_len, dev, graph=args.graph, batch=B)
     stream = sess.stream
@@ -287,6 +288,12 @@ def bench_batched(args, wl):
         log(f"dominant GEMM {name}: {avg_ms * 1000:.1f} us/launch, {achieved / 1e9:.0f} GB/s; shares {share}")
     n_bad = sess.nonfinite()
     sess.close()
+    cpu = None
+    if not args.no_cpu_baseline:
+        del sess, weights
+        torch.cuda.empty_cache()
+        cpu = cpu_baseline_batched(dims, wl, host, lens, prompts)
+        del host
     out = {
         "metric": METRIC, "value": round(fps, 2), "unit": "frames/s", "n_gpus": 1, "steps": steps,
         "warmup": args.warmup, "ms_per_step": round(ms / steps, 4), "higher_is_better": True, "scaling": "weak",
@@ -297,7 +304,7 @@ def bench_batched(args, wl):
                    "residual_codebooks": dims.n_res, "graph": args.graph},
         "achieved_gb_s": round(gbs / 1e9, 1), "hbm_frac": round(gbs / HBM_PEAK, 4),
         "alg_bytes_per_step_avg": int(alg_bytes // steps), "prefill_ms": round(prefill_ms, 2),
-        "nonfinite_logits": n_bad, "roofline": roof, "cpu_baseline": None,
+        "nonfinite_logits": n_bad, "roofline": roof, "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
 
@@ -374,6 +381,45 @@ def cpu_baseline(dims, wl, host, prompt):
                       f"{frames} decode frames at positions {wl.prefill_len}..{wl.prefill_len + frames - 1} timed "
                       f"({t_dec:.1f} s, budget about 12 s); weight conversion {t_build:.1f} s and "
                       f"prefill {t_prefill:.1f} s not timed",
+            "cpu_model": _cpu_model()}
+
+
+def cpu_baseline_batched(dims, wl, host, lens, prompts):
+    """The oracle on this host's cores for a batched workload: the oracle
+    decodes one sequence at a time, so a sample of two of the batch's own
+    sequences (prefill, then frames alternating between them until about 12 s
+    of decode) gives its aggregate frames/s."""
+    from oracle import OracleDecoder, OracleModel
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 0) for i in threadpool_info()), default=os.cpu_count())
+    except Exception:
+        threads = os.cpu_count()
+    t0 = time.time()
+    model = OracleModel(dims, host, wtype=wl.wtype)
+    t_build = time.time() - t0
+    picks = [0, 1]
+    decs = []
+    t0 = time.time()
+    for b in picks:
+        d = OracleDecoder(model, wl.max_len)
+        d.prefill(prompts[b])
+        decs.append(d)
+    t_prefill = time.time() - t0
+    budget_s, frames = 12.0, 0
+    t0 = time.time()
+    while frames < 2 or time.time() - t0 < budget_s:
+        decs[frames % 2].decode_frame()
+        frames += 1
+    t_dec = time.time() - t0
+    log(f"oracle: build {t_build:.1f}s, prefill {t_prefill:.1f}s, {frames} frames {t_dec:.1f}s on {threads} threads")
+    del model, decs
+    return {"value": round(frames / t_dec, 4), "unit": "frames/s", "cores": threads, "kind": "oracle",
+            "sample": f"{wl.name}: oracle (NumPy fp32), sequences {picks} of the batch (prompts of "
+                      f"{[int(lens[b]) for b in picks]} ids) prefilled, then {frames} decode frames alternating "
+                      f"between them timed ({t_dec:.1f} s, budget about 12 s; the oracle decodes one sequence at a "
+                      f"time, so this is its aggregate rate); weight conversion {t_build:.1f} s and prefill "
+                      f"{t_prefill:.1f} s not timed",
             "cpu_model": _cpu_model()}
 
 
