@@ -43,6 +43,7 @@ from __future__ import annotations
 import numpy as np
 
 from .fp8 import e4m3_decode, quantize_rows
+from .int8 import quantize_int8_rows
 
 
 def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
@@ -125,7 +126,7 @@ def greedy_argmax(logits: np.ndarray) -> int:
 
 
 class Linear:
-    """y = W x for W [out][in]; fp8 form keeps (dec(q), s) and returns s * (dec(q) x)."""
+    """y = W x for W [out][in]; the quantised forms keep (dec(q), s) and return s * (dec(q) x)."""
 
     def __init__(self, w: np.ndarray, scale: np.ndarray | None = None):
         self.w = w
@@ -155,12 +156,13 @@ class OracleModel:
     tensors: {name: uint16 bf16 bits} in the canonical list's names.
     wtype "fp8": every Linear matrix (the ones named *.wqkv, *.wo, *.w1, *.w3,
     *.w2 and fast.head) is quantised per row with the oracle's quantiser and
-    used as s * dec(q); tables and norm gains stay bf16.
+    used as s * dec(q); tables and norm gains stay bf16. wtype "int8": the same
+    matrices quantised per row to int8 (oracle/int8.py), used as s * q.
     """
 
     def __init__(self, dims, tensors: dict, wtype: str = "bf16", dt=np.float32, drop_source: bool = False,
                  kv: str = "bf16"):
-        if wtype not in ("bf16", "fp8"):
+        if wtype not in ("bf16", "fp8", "int8"):
             raise ValueError(wtype)
         if kv not in ("bf16", "fp32"):
             raise ValueError(kv)
@@ -168,7 +170,7 @@ class OracleModel:
         self.wtype = wtype
         self.dt = dt
         self.kv_bf16 = kv == "bf16"
-        self.fp8 = {}
+        self.quant = {}  # name -> (codes, row scales) of every quantised matrix
 
         def get(name):
             return bf16_to_f32(tensors[name]).astype(dt, copy=False)
@@ -177,9 +179,13 @@ class OracleModel:
             w = bf16_to_f32(tensors[name])
             if wtype == "bf16":
                 out = Linear(w.astype(dt, copy=False))
+            elif wtype == "int8":
+                codes, scale = quantize_int8_rows(w)
+                self.quant[name] = (codes, scale)
+                out = Linear(codes.astype(dt), scale.astype(dt))
             else:
                 codes, scale = quantize_rows(w)
-                self.fp8[name] = (codes, scale)
+                self.quant[name] = (codes, scale)
                 out = Linear(e4m3_decode(codes).astype(dt, copy=False), scale.astype(dt))
             if drop_source:
                 tensors.pop(name, None)

@@ -156,7 +156,7 @@ def test_fp8_device_quantiser_matches_oracle(tiny_host):
     names = synth.linear_names(dims)
     assert len(m.fp8) == len(names)
     for name in names:
-        codes, scale = m.fp8[name]
+        codes, scale = m.quant[name]
         assert np.array_equal(dw.t[name].cpu().numpy(), codes), name
         assert np.array_equal(dw.scale[name].cpu().numpy(), scale), name
 

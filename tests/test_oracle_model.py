@@ -167,12 +167,12 @@ def test_fp8_model_uses_dequantised_linears():
     d = MICRO
     w = synth.gen_weights(d, 0)
     m8 = OracleModel(d, w, wtype="fp8", dt=np.float64)
-    codes, scale = m8.fp8["slow.1.w3"]
+    codes, scale = m8.quant["slow.1.w3"]
     from oracle import e4m3_decode
     x = np.random.default_rng(1).standard_normal(d.d_model)
     want = (e4m3_decode(codes).astype(np.float64) * scale[:, None].astype(np.float64)) @ x
     assert _rel(m8.slow[1].w3(x), want) < 1e-13
-    assert len(m8.fp8) == len(synth.linear_names(d))
+    assert len(m8.quant) == len(synth.linear_names(d))
     # tables and norms are untouched by quantisation
     assert np.array_equal(m8.w0, bf16_to_f32(w["w0"]).astype(np.float64))
 
