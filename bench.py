@@ -22,6 +22,7 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
+DTYPE_NAMES = {"bf16": "bf16", "fp8": "fp8_e4m3", "int8": "int8"}  # the weights' arithmetic type (activations fp32)
 METRIC = "Dual-AR decode frames/s @batch1 + achieved HBM GB/s (% of ~8 TB/s peak)"
 HBM_PEAK = 8.0e12
 
@@ -84,7 +85,7 @@ def main():
     log(f"generated {len(host)} tensors in {time.time() - t0:.1f}s")
     t0 = time.time()
     weights = DeviceWeights(dims, host, wl.wtype, dev)
-    log(f"uploaded{' and quantised' if wl.wtype == 'fp8' else ''} in {time.time() - t0:.1f}s")
+    log(f"uploaded{' and quantised' if wl.wtype != 'bf16' else ''} in {time.time() - t0:.1f}s")
     prompt = synth.gen_prompt(wl.prefill_len, dims.vocab_c0, wl.prompt_seed)
     sess = DarSession(dims, weights, wl.max_len, dev, graph=args.graph)
     stream = sess.stream
@@ -182,7 +183,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if wl.wtype == "bf16" else "fp8_e4m3",
+        "dtype": DTYPE_NAMES[wl.wtype],
         "data": "synthetic (seeded random-init weights and prompt ids)",
         "config": {"workload": wl.name, "batch": 1, "prefill": wl.prefill_len, "first_decode_position": wl.prefill_len,
                    "decode_frames": args.steps, "max_len": wl.max_len, "layers_slow": dims.n_layers_slow,
@@ -297,7 +298,7 @@ def bench_batched(args, wl):
     out = {
         "metric": METRIC, "value": round(fps, 2), "unit": "frames/s", "n_gpus": 1, "steps": steps,
         "warmup": args.warmup, "ms_per_step": round(ms / steps, 4), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16" if wl.wtype == "bf16" else "fp8_e4m3",
+        "vs_baseline": None, "dtype": DTYPE_NAMES[wl.wtype],
         "data": "synthetic (seeded random-init weights, ragged random prompts)",
         "config": {"workload": wl.name, "batch": B, "prompt_lengths": [int(n) for n in lens], "max_len": wl.max_len,
                    "layers_slow": dims.n_layers_slow, "layers_fast": dims.n_layers_fast,

@@ -66,7 +66,7 @@ def slow_weight_bytes(dims, wtype):
     L = dims.n_layers_slow
     if wtype == "bf16":
         w = 2 * L * mats
-    elif wtype == "fp8":
+    elif wtype in ("fp8", "int8"):  # one byte per weight + an fp32 scale per row
         w = L * mats + 4 * L * layer_rows(dims)
     else:
         raise ValueError(wtype)
@@ -81,7 +81,7 @@ def fast_pass_bytes(dims, wtype):
     head = dims.vocab_res * dims.d_model
     if wtype == "bf16":
         w = 2 * (L * mats + head)
-    elif wtype == "fp8":
+    elif wtype in ("fp8", "int8"):
         w = L * mats + head + 4 * (L * layer_rows(dims) + dims.vocab_res)
     else:
         raise ValueError(wtype)

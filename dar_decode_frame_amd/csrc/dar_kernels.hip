@@ -81,6 +81,7 @@ __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<
 
 struct BF16 { static constexpr int kBytes = 2; };
 struct FP8 { static constexpr int kBytes = 1; };
+struct INT8 { static constexpr int kBytes = 1; };
 
 template <typename WT>
 struct Dot;
@@ -117,6 +118,28 @@ struct Dot<FP8> {
     s = fmaf(lo.y, x.y, s);
     s = fmaf(hi.x, x.z, s);
     s = fmaf(hi.y, x.w, s);
+    return s;
+  }
+  __device__ static __forceinline__ float run(u32x4 w, const float* x) {
+    const float4* x4 = reinterpret_cast<const float4*>(x);
+    float s0 = word(w.x, x4[0], 0.f);
+    float s1 = word(w.y, x4[1], 0.f);
+    s0 = word(w.z, x4[2], s0);
+    s1 = word(w.w, x4[3], s1);
+    return s0 + s1;
+  }
+};
+
+// Signed int8 codes, four per word, sign-extended and converted exactly to fp32.
+template <>
+struct Dot<INT8> {
+  static constexpr int E = 16;
+  __device__ static __forceinline__ float word(uint32_t u, const float4 x, float s) {
+    const int v = (int)u;
+    s = fmaf((float)((v << 24) >> 24), x.x, s);
+    s = fmaf((float)((v << 16) >> 24), x.y, s);
+    s = fmaf((float)((v << 8) >> 24), x.z, s);
+    s = fmaf((float)(v >> 24), x.w, s);
     return s;
   }
   __device__ static __forceinline__ float run(u32x4 w, const float* x) {
@@ -891,6 +914,10 @@ template <>
 struct PerWave<FP8> {
   static constexpr int v = 2;
 };
+template <>
+struct PerWave<INT8> {
+  static constexpr int v = 2;
+};
 
 // y[r] (+)= scale[r] * W[r] . x, P rows per wave
 template <typename WT, int NCH>
@@ -1355,6 +1382,30 @@ __global__ __launch_bounds__(kBlock) void k_quantize_fp8(const uint16_t* w, int 
   }
 }
 
+// One workgroup per row: scale = rowmax|w| / 127, codes = rint(w / scale)
+// clamped to [-127, 127] (fp32 division, round half to even).
+__global__ __launch_bounds__(kBlock) void k_quantize_int8(const uint16_t* w, int rows, int cols, int8_t* q,
+                                                         float* scale) {
+  __shared__ float red[kWaves];
+  const int r = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const uint16_t* row = w + (size_t)r * cols;
+  float mx = 0.f;
+  for (int k = tid; k < cols; k += kBlock) mx = fmaxf(mx, fabsf(bf2f(row[k])));
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+  if (lane == 0) red[wave] = mx;
+  __syncthreads();
+  float amax = red[0];
+#pragma unroll
+  for (int i = 1; i < kWaves; ++i) amax = fmaxf(amax, red[i]);
+  const float s = amax / 127.0f;
+  if (tid == 0) scale[r] = s;
+  int8_t* qr = q + (size_t)r * cols;
+  for (int k = tid; k < cols; k += kBlock)
+    qr[k] = (s > 0.f) ? (int8_t)fminf(fmaxf(rintf(bf2f(row[k]) / s), -127.f), 127.f) : (int8_t)0;
+}
+
 __global__ void k_fp8_decode(const uint8_t* codes, int n, float* out) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) {
@@ -1559,12 +1610,16 @@ static bool row_stage(const Task& t, hipStream_t s, hipError_t& e) {
 hipError_t launch_task(int wtype, const Task& t, hipStream_t s) {
   hipError_t e = hipSuccess;
   if (row_stage(t, s, e)) return e;
-  return wtype == W_FP8 ? single_launch<FP8>(t, s, false) : single_launch<BF16>(t, s, false);
+  if (wtype == W_FP8) return single_launch<FP8>(t, s, false);
+  if (wtype == W_INT8) return single_launch<INT8>(t, s, false);
+  return single_launch<BF16>(t, s, false);
 }
 
 hipError_t prepare_task(int wtype, const Task& t) {
   if (t.kind >= T_NORM_SPLIT) return hipSuccess;  // the many-row kernels need no set-up
-  return wtype == W_FP8 ? single_launch<FP8>(t, nullptr, true) : single_launch<BF16>(t, nullptr, true);
+  if (wtype == W_FP8) return single_launch<FP8>(t, nullptr, true);
+  if (wtype == W_INT8) return single_launch<INT8>(t, nullptr, true);
+  return single_launch<BF16>(t, nullptr, true);
 }
 
 size_t attn_partial_floats(int M, int n_kv, int nsplit_max, int group, int head_dim) {
@@ -1605,6 +1660,11 @@ hipError_t launch_copy_i32(const int* src, int* dst, int n, hipStream_t s) {
 
 hipError_t launch_quantize_fp8(const uint16_t* w, int rows, int cols, uint8_t* q, float* scale, hipStream_t s) {
   hipLaunchKernelGGL(k_quantize_fp8, dim3(rows), dim3(kBlock), 0, s, w, rows, cols, q, scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_int8(const uint16_t* w, int rows, int cols, int8_t* q, float* scale, hipStream_t s) {
+  hipLaunchKernelGGL(k_quantize_int8, dim3(rows), dim3(kBlock), 0, s, w, rows, cols, q, scale);
   return hipGetLastError();
 }
 

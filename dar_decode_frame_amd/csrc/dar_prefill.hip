@@ -90,6 +90,25 @@ struct FP8T {
   }
 };
 
+struct INT8T {
+  static constexpr int kBytes = 1;
+  // int8 codes (|q| <= 127) are exact in bf16: sign-extend, convert, keep the top half
+  __device__ static __forceinline__ uint32_t pack2(int a, int b) {
+    return (__float_as_uint((float)a) >> 16) | (__float_as_uint((float)b) & 0xffff0000u);
+  }
+  __device__ static __forceinline__ bf16x8 frag(const char* st, int r, int s, int half) {
+    const int u = s ^ (r & 7);
+    const u32x2 w = *reinterpret_cast<const u32x2*>(st + (r * 8 + u) * 16 + 8 * half);
+    const int x = (int)w.x, y = (int)w.y;
+    u32x4 o;
+    o.x = pack2((x << 24) >> 24, (x << 16) >> 24);
+    o.y = pack2((x << 8) >> 24, x >> 24);
+    o.z = pack2((y << 24) >> 24, (y << 16) >> 24);
+    o.w = pack2((y << 8) >> 24, y >> 24);
+    return __builtin_bit_cast(bf16x8, o);
+  }
+};
+
 // The workgroup's finished sums: lane l holds weight row (output column) n =
 // its tile row, and accumulator v of tile mt holds input row
 // m0 + 32 mt + (v % 4) + 4 (l / 32) + 8 (v / 4). Split partials carry the row
@@ -231,7 +250,7 @@ __device__ __forceinline__ void wait_loads_x4(int n) {
 // k_gemm. Needs a.cps <= kResidentChunks<WT>. (Staging only 16 input rows
 // for a six-slot ring was tried at 16 sequences: no faster.)
 template <typename WT>
-constexpr int kResidentChunks = WT::kBytes == 2 ? 14 : 7;  // an e4m3 chunk spans twice the input columns
+constexpr int kResidentChunks = WT::kBytes == 2 ? 14 : 7;  // a one-byte chunk spans twice the input columns
 
 template <typename WT>
 __global__ __launch_bounds__(kBlock) void k_gemm_x(GemmArgs a) {
@@ -573,7 +592,14 @@ __global__ void k_inc_rows(int* v, int n) {
 }
 
 hipError_t gemm_dispatch(int wtype, const GemmArgs& a, int mt, dim3 grid, hipStream_t s) {
-  if (wtype == W_FP8) {
+  if (wtype == W_INT8) {
+    if (mt == 1 && a.cps <= kResidentChunks<INT8T>)
+      hipLaunchKernelGGL((k_gemm_x<INT8T>), grid, dim3(kBlock), 0, s, a);
+    else if (mt == 1)
+      hipLaunchKernelGGL((k_gemm<INT8T, 1>), grid, dim3(kBlock), 0, s, a);
+    else
+      hipLaunchKernelGGL((k_gemm<INT8T, 2>), grid, dim3(kBlock), 0, s, a);
+  } else if (wtype == W_FP8) {
     if (mt == 1 && a.cps <= kResidentChunks<FP8T>)
       hipLaunchKernelGGL((k_gemm_x<FP8T>), grid, dim3(kBlock), 0, s, a);
     else if (mt == 1)
@@ -599,11 +625,11 @@ hipError_t gemm_dispatch(int wtype, const GemmArgs& a, int mt, dim3 grid, hipStr
 
 int gemm_mpad(int M) { return M <= 32 ? 32 : (M <= 64 ? 64 : ((M + 127) / 128) * 128); }
 
-// input rows per workgroup / 32: the e4m3 kernel stages twice the input
-// columns per chunk, so its LDS ring holds at most 64 input rows
+// input rows per workgroup / 32: the one-byte kernels (e4m3, int8) stage
+// twice the input columns per chunk, so their LDS ring holds at most 64 input rows
 static int gemm_mt(int wtype, int M) {
   const int mt = M <= 32 ? 1 : (M <= 64 ? 2 : 4);
-  return (wtype == W_FP8 && mt > 2) ? 2 : mt;
+  return (wtype != W_BF16 && mt > 2) ? 2 : mt;
 }
 
 // K splits: as many as keep the launch within one workgroup per CU (a
@@ -613,10 +639,10 @@ static int gemm_mt(int wtype, int M) {
 int gemm_splits(int wtype, int M, int N, int K) {
   const int mt = gemm_mt(wtype, M);
   const int tiles = ((N + kTileN - 1) / kTileN) * ((M + 32 * mt - 1) / (32 * mt));
-  const int nchunks = K / (kRowChunk / (wtype == W_FP8 ? 1 : 2));
+  const int nchunks = K / (kRowChunk / (wtype == W_BF16 ? 2 : 1));
   int splits = 256 / tiles;
   if (mt == 1) {
-    const int resident = wtype == W_FP8 ? kResidentChunks<FP8T> : kResidentChunks<BF16T>;
+    const int resident = wtype == W_BF16 ? kResidentChunks<BF16T> : kResidentChunks<FP8T>;
     splits = std::max(splits, (nchunks + resident - 1) / resident);
   }
   splits = splits < 1 ? 1 : (splits > nchunks ? nchunks : splits);
@@ -625,7 +651,7 @@ int gemm_splits(int wtype, int M, int N, int K) {
 }
 
 int gemm_launch_splits(int wtype, int M, int N, int K, size_t part_cap) {
-  const int nchunks = K / (kRowChunk / (wtype == W_FP8 ? 1 : 2));
+  const int nchunks = K / (kRowChunk / (wtype == W_BF16 ? 2 : 1));
   int splits = gemm_splits(wtype, M, N, K);
   while (splits > 1 && (size_t)splits * M * N > part_cap) --splits;
   const int cps = (nchunks + splits - 1) / splits;
@@ -633,7 +659,7 @@ int gemm_launch_splits(int wtype, int M, int N, int K, size_t part_cap) {
 }
 
 hipError_t launch_gemm(int wtype, GemmArgs a, size_t part_cap, hipStream_t s) {
-  const int kc = kRowChunk / (wtype == W_FP8 ? 1 : 2);
+  const int kc = kRowChunk / (wtype == W_BF16 ? 2 : 1);
   if (a.M < 1 || a.M > kPrefillRows || a.K < kc || a.K % kc || a.N < 1) return hipErrorInvalidValue;
   if (a.defer && (size_t)a.M * a.N > part_cap) return hipErrorInvalidValue;
   const int mt = gemm_mt(wtype, a.M);

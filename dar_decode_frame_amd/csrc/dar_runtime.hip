@@ -71,6 +71,12 @@ struct Layout {
   int chunk_rows, nsplit_rows;  // batched slow attention: positions per split, most splits
 };
 
+// the kernels' weight type of a dar_wtype (callers have validated it)
+int wtype_of(int32_t wtype) {
+  return wtype == DAR_WTYPE_FP8_E4M3_ROW ? W_FP8 : (wtype == DAR_WTYPE_INT8_ROW ? W_INT8 : W_BF16);
+}
+bool has_row_scales(int32_t wtype) { return wtype == DAR_WTYPE_FP8_E4M3_ROW || wtype == DAR_WTYPE_INT8_ROW; }
+
 Layout make_layout(const dar_config* c) {
   Layout L{};
   const int d = c->d_model, qw = c->n_heads_q * c->head_dim, F = c->ffn_dim;
@@ -132,7 +138,7 @@ Layout make_layout(const dar_config* c) {
   L.pq = take(sizeof(float) * R * qw);
   L.po = take(sizeof(float) * R * qw);
   // partial sums of the widest K split launch_gemm picks for the block's GEMMs
-  const int wt = c->wtype == DAR_WTYPE_FP8_E4M3_ROW ? W_FP8 : W_BF16;
+  const int wt = wtype_of(c->wtype);
   L.pgp_floats = 0;
   for (auto nk : {std::pair<int, int>{qkv_rows, d}, {d, qw}, {F, d}, {d, F}}) {
     for (int M = 1; M <= (int)R; ++M)
@@ -183,7 +189,8 @@ int validate_config(const dar_config* c, std::string& why) {
   if (!(c->rope_base > 1.0) || !std::isfinite(c->rope_base)) return bad("rope_base must be > 1");
   if (c->max_len < 2) return bad("max_len must be >= 2");
   if (c->max_batch < 1) return bad("max_batch must be >= 1");
-  if (c->wtype != DAR_WTYPE_BF16 && c->wtype != DAR_WTYPE_FP8_E4M3_ROW) return bad("unknown wtype");
+  if (c->wtype != DAR_WTYPE_BF16 && c->wtype != DAR_WTYPE_FP8_E4M3_ROW && c->wtype != DAR_WTYPE_INT8_ROW)
+    return bad("unknown wtype");
   const int g = c->n_heads_q / c->n_heads_kv;
   auto unsup = [&](const char* msg) {
     why = msg;
@@ -202,7 +209,8 @@ int validate_config(const dar_config* c, std::string& why) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-int check_layer(const dar_layer_weights& w, bool fp8, std::string& why, const char* which, int idx) {
+
+int check_layer(const dar_layer_weights& w, bool scaled, std::string& why, const char* which, int idx) {
   const void* ptrs[] = {w.attn_norm, w.wqkv, w.wo, w.ffn_norm, w.w1, w.w3, w.w2};
   for (const void* p : ptrs) {
     if (!p || !aligned16(p)) {
@@ -212,12 +220,12 @@ int check_layer(const dar_layer_weights& w, bool fp8, std::string& why, const ch
       return DAR_E_INVAL;
     }
   }
-  if (fp8) {
+  if (scaled) {
     const float* s[] = {w.wqkv_scale, w.wo_scale, w.w1_scale, w.w3_scale, w.w2_scale};
     for (const float* p : s) {
       if (!p) {
         char buf[128];
-        snprintf(buf, sizeof buf, "%s layer %d: fp8 row scale pointer is NULL", which, idx);
+        snprintf(buf, sizeof buf, "%s layer %d: row scale pointer is NULL (fp8 / int8 weights)", which, idx);
         why = buf;
         return DAR_E_INVAL;
       }
@@ -253,7 +261,8 @@ struct Chain {
 struct dar_ctx {
   dar_config cfg{};
   Layout L{};
-  bool fp8 = false;
+  bool quant = false;      // one-byte weights with fp32 row scales (fp8 or int8)
+  int wq = W_BF16;         // the kernels' weight type of the Linear matrices
   std::vector<dar_layer_weights> slow, fast;
   std::vector<const uint16_t*> fast_emb;
   const uint16_t* w0 = nullptr;
@@ -338,7 +347,7 @@ void add_layer(dar_ctx* c, std::vector<TaskRec>& out, const Chain& ch, const dar
   t.M = M;
   QkvArgs& qa = t.qkv;
   qa.W = w.wqkv;
-  qa.scale = c->fp8 ? w.wqkv_scale : nullptr;
+  qa.scale = c->quant ? w.wqkv_scale : nullptr;
   qa.K = d;
   qa.M = M;
   qa.x = ch.x;
@@ -387,7 +396,7 @@ void add_layer(dar_ctx* c, std::vector<TaskRec>& out, const Chain& ch, const dar
   t.M = M;
   GemvArgs& wo = t.gemv;
   wo.W = w.wo;
-  wo.scale = c->fp8 ? w.wo_scale : nullptr;
+  wo.scale = c->quant ? w.wo_scale : nullptr;
   wo.rows = d;
   wo.K = qw;
   wo.M = M;
@@ -403,9 +412,9 @@ void add_layer(dar_ctx* c, std::vector<TaskRec>& out, const Chain& ch, const dar
   t.M = M;
   SwigluArgs& sa = t.swiglu;
   sa.W1 = w.w1;
-  sa.s1 = c->fp8 ? w.w1_scale : nullptr;
+  sa.s1 = c->quant ? w.w1_scale : nullptr;
   sa.W3 = w.w3;
-  sa.s3 = c->fp8 ? w.w3_scale : nullptr;
+  sa.s3 = c->quant ? w.w3_scale : nullptr;
   sa.F = g.ffn_dim;
   sa.K = d;
   sa.M = M;
@@ -422,7 +431,7 @@ void add_layer(dar_ctx* c, std::vector<TaskRec>& out, const Chain& ch, const dar
   t.M = M;
   GemvArgs& w2 = t.gemv;
   w2.W = w.w2;
-  w2.scale = c->fp8 ? w.w2_scale : nullptr;
+  w2.scale = c->quant ? w.w2_scale : nullptr;
   w2.rows = d;
   w2.K = g.ffn_dim;
   w2.M = M;
@@ -532,7 +541,7 @@ std::vector<TaskRec> fast_chain(dar_ctx* c) {
     t.M = 1;
     HeadArgs& hk = t.head;
     hk.W = c->fast_head;
-    hk.scale = c->fp8 ? c->fast_head_scale : nullptr;
+    hk.scale = c->quant ? c->fast_head_scale : nullptr;
     hk.rows = g.vocab_res;
     hk.K = d;
     hk.x = c->cf.x + (size_t)(M - 1) * d;
@@ -574,7 +583,7 @@ Task t_gemm(int wtype, const void* W, const float* scale, int N, int K, int M, c
   t.M = M;
   GemmArgs& g = t.gemm.g;
   g.W = W;
-  g.scale = wtype == W_FP8 ? scale : nullptr;
+  g.scale = wtype != W_BF16 ? scale : nullptr;  // one-byte weights carry row scales
   g.N = N;
   g.K = K;
   g.M = M;
@@ -599,7 +608,7 @@ void add_layer_rows(dar_ctx* c, std::vector<TaskRec>& out, int ch, const dar_lay
   const dar_config& g = c->cfg;
   const int d = g.d_model, qw = g.n_heads_q * g.head_dim, F = g.ffn_dim;
   const int qkv_rows = (g.n_heads_q + 2 * g.n_heads_kv) * g.head_dim;
-  const int wt = c->fp8 ? W_FP8 : W_BF16;
+  const int wt = c->wq;
   const Chain& cn = ch == 0 ? c->cs : c->cf;
   uint16_t *xh = c->bxh[ch], *xl = c->bxl[ch];
   float* gp = c->bgp[ch];
@@ -764,7 +773,7 @@ std::vector<TaskRec> fast_chain_rows(dar_ctx* c) {
     out.push_back(rec(t_norm(c->cf.x + (k == 1 ? d : 0), k == 1 ? 2 * d : d, B, d, c->fast_fn, g.rms_eps, c->bxh[1],
                              c->bxl[1], nullptr, pend),
                       K_OTHER, k));
-    out.push_back(rec(t_gemm(c->fp8 ? W_FP8 : W_BF16, c->fast_head, c->fast_head_scale, g.vocab_res, d, B, c->bxh[1],
+    out.push_back(rec(t_gemm(c->wq, c->fast_head, c->fast_head_scale, g.vocab_res, d, B, c->bxh[1],
                              c->bxl[1], c->flogits + (size_t)k * c->L.vmax, fc * c->L.vmax, 0, c->bgp[1],
                              c->L.bgp_floats[1]),
                       K_HEAD, k));
@@ -816,7 +825,7 @@ void set_live_attention(dar_ctx* c, int tmax) {
 // live: eager launches may trim the batched slow attention to the splits the
 // coming frame's longest sequence has (a captured graph keeps them all)
 hipError_t enqueue_plan(dar_ctx* c, const Plan& p, hipStream_t s, size_t ev_base = SIZE_MAX, bool live = true) {
-  const int wt = c->fp8 ? W_FP8 : W_BF16;
+  const int wt = c->wq;
   for (size_t i = 0; i < p.launches(); ++i) {
     hipEvent_t before = nullptr, after = nullptr;
     if (ev_base != SIZE_MAX) {
@@ -871,7 +880,7 @@ int run_plan(dar_ctx* c, Plan& p, hipStream_t s, const char* what) {
   }
   if (!p.exec) {
     for (size_t i = 0; i < p.launches(); ++i)
-      DAR_HIP(c, prepare_task(c->fp8 ? W_FP8 : W_BF16, p.tasks[i]), "prepare launch");
+      DAR_HIP(c, prepare_task(c->wq, p.tasks[i]), "prepare launch");
     DAR_HIP(c, hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal), "begin capture");
     hipError_t e = enqueue_plan(c, p, s, SIZE_MAX, false);
     hipGraph_t g = nullptr;
@@ -955,7 +964,7 @@ int prefill_blocks(dar_ctx* c, const int32_t* tokens, int n, hipStream_t s, int 
   const Layout& L = c->L;
   const int d = g.d_model, qw = g.n_heads_q * g.head_dim, F = g.ffn_dim;
   const int qkv_rows = (g.n_heads_q + 2 * g.n_heads_kv) * g.head_dim;
-  const int wt = c->fp8 ? W_FP8 : W_BF16;
+  const int wt = c->wq;
   char* b = c->ws;
   float* px = reinterpret_cast<float*>(b + L.px);
   uint16_t* xh = reinterpret_cast<uint16_t*>(b + L.pxh);
@@ -970,7 +979,7 @@ int prefill_blocks(dar_ctx* c, const int32_t* tokens, int n, hipStream_t s, int 
                   int defer) {
     GemmArgs a{};
     a.W = W;
-    a.scale = c->fp8 ? scale : nullptr;
+    a.scale = c->quant ? scale : nullptr;
     a.N = N;
     a.K = K;
     a.M = M;
@@ -1102,13 +1111,13 @@ int dar_create(const dar_config* cfg, const dar_weights* w, void* workspace, siz
     g_create_error = "workspace smaller than dar_workspace_bytes()";
     return DAR_E_WORKSPACE;
   }
-  const bool fp8 = cfg->wtype == DAR_WTYPE_FP8_E4M3_ROW;
+  const bool scaled = has_row_scales(cfg->wtype);
   if (!w->w0 || !aligned16(w->w0) || !w->slow || !w->slow_final_norm) {
     g_create_error = "w0, slow layers or slow_final_norm missing or misaligned";
     return DAR_E_INVAL;
   }
   for (int l = 0; l < cfg->n_layers_slow; ++l) {
-    st = check_layer(w->slow[l], fp8, why, "slow", l);
+    st = check_layer(w->slow[l], scaled, why, "slow", l);
     if (st != DAR_OK) {
       g_create_error = why;
       return st;
@@ -1116,7 +1125,7 @@ int dar_create(const dar_config* cfg, const dar_weights* w, void* workspace, siz
   }
   if (has_fast(cfg)) {
     if (!w->fast || !w->fast_emb || !w->fast_final_norm || !w->fast_head || !aligned16(w->fast_head) ||
-        (fp8 && !w->fast_head_scale)) {
+        (scaled && !w->fast_head_scale)) {
       g_create_error = "fast AR weights missing or misaligned";
       return DAR_E_INVAL;
     }
@@ -1127,7 +1136,7 @@ int dar_create(const dar_config* cfg, const dar_weights* w, void* workspace, siz
       }
     }
     for (int l = 0; l < cfg->n_layers_fast; ++l) {
-      st = check_layer(w->fast[l], fp8, why, "fast", l);
+      st = check_layer(w->fast[l], scaled, why, "fast", l);
       if (st != DAR_OK) {
         g_create_error = why;
         return st;
@@ -1138,7 +1147,8 @@ int dar_create(const dar_config* cfg, const dar_weights* w, void* workspace, siz
   dar_ctx* c = new dar_ctx();
   c->cfg = *cfg;
   c->L = L;
-  c->fp8 = fp8;
+  c->quant = scaled;
+  c->wq = wtype_of(cfg->wtype);
   c->slow.assign(w->slow, w->slow + cfg->n_layers_slow);
   if (has_fast(cfg)) {
     c->fast.assign(w->fast, w->fast + cfg->n_layers_fast);
@@ -1291,7 +1301,7 @@ int dar_prefill(dar_ctx* c, int32_t batch, const int32_t* tokens, const int32_t*
   }
   c->prefilled = false;
   hipStream_t s = c->cs.s;
-  const int wt = c->fp8 ? W_FP8 : W_BF16;
+  const int wt = c->wq;
   // the slow stream runs the prompts after anything already queued
   DAR_HIP(c, hipEventRecord(c->ev_start, c->stream), "record start");
   DAR_HIP(c, hipStreamWaitEvent(s, c->ev_start, 0), "wait start");
@@ -1417,7 +1427,7 @@ int dar_bytes_per_frame(const dar_config* cfg, int32_t T, double* bytes_out) {
   const double mats = qkv * d + d * qw + 3.0 * F * d;
   const double rows = qkv + d + 2.0 * F + d;
   const double norms = 2.0 * d;
-  const bool fp8 = cfg->wtype == DAR_WTYPE_FP8_E4M3_ROW;
+  const bool fp8 = has_row_scales(cfg->wtype);  // one byte per weight + fp32 row scales (fp8, int8)
   const double Ls = cfg->n_layers_slow, Lf = cfg->n_layers_fast;
   double slow = (fp8 ? Ls * mats + 4.0 * Ls * rows : 2.0 * Ls * mats) + 2.0 * (Ls * norms + d) +
                 2.0 * cfg->vocab_c0 * d;
@@ -1439,6 +1449,14 @@ int dar_quantize_fp8_rows(const void* w, int32_t rows, int32_t cols, void* q, fl
   if (!w || !q || !scale || rows < 1 || cols < 16 || cols % 16) return DAR_E_INVAL;
   hipError_t e = launch_quantize_fp8(static_cast<const uint16_t*>(w), rows, cols, static_cast<uint8_t*>(q), scale,
                                      static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(nullptr, e, "quantize");
+  return DAR_OK;
+}
+
+int dar_quantize_int8_rows(const void* w, int32_t rows, int32_t cols, void* q, float* scale, void* stream) {
+  if (!w || !q || !scale || rows < 1 || cols < 16 || cols % 16) return DAR_E_INVAL;
+  hipError_t e = launch_quantize_int8(static_cast<const uint16_t*>(w), rows, cols, static_cast<int8_t*>(q), scale,
+                                      static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(nullptr, e, "quantize");
   return DAR_OK;
 }
@@ -1470,15 +1488,15 @@ int dar_op_gemv(int32_t wtype, const void* W, const float* scale, int32_t rows, 
                 int32_t M, float* y, void* stream) {
   if (!W || !x || !y || rows < 1 || cols < 256 || cols % 256 || cols > 16384 || (M != 1 && M != 2))
     return DAR_E_INVAL;
-  if (wtype != DAR_WTYPE_BF16 && wtype != DAR_WTYPE_FP8_E4M3_ROW) return DAR_E_INVAL;
-  if (wtype == DAR_WTYPE_FP8_E4M3_ROW && !scale) return DAR_E_INVAL;
+  if (wtype != DAR_WTYPE_BF16 && !has_row_scales(wtype)) return DAR_E_INVAL;
+  if (has_row_scales(wtype) && !scale) return DAR_E_INVAL;
   if (!aligned16(W) || !aligned16(x)) return DAR_E_INVAL;
   Task t = none_task();
   t.kind = T_GEMV;
   t.M = M;
   GemvArgs& a = t.gemv;
   a.W = W;
-  a.scale = wtype == DAR_WTYPE_FP8_E4M3_ROW ? scale : nullptr;
+  a.scale = has_row_scales(wtype) ? scale : nullptr;
   a.rows = rows;
   a.K = cols;
   a.M = M;
@@ -1488,20 +1506,20 @@ int dar_op_gemv(int32_t wtype, const void* W, const float* scale, int32_t rows, 
   a.y = y;
   a.y_stride = rows;
   a.accumulate = 0;
-  return run_single_task(t, wtype == DAR_WTYPE_FP8_E4M3_ROW ? W_FP8 : W_BF16, static_cast<hipStream_t>(stream),
+  return run_single_task(t, wtype_of(wtype), static_cast<hipStream_t>(stream),
                          "gemv");
 }
 
 int dar_op_gemm(int32_t wtype, const void* W, const float* scale, int32_t N, int32_t K, const float* x,
                 int32_t M, float* y, void* stream) {
   if (!W || !x || !y || N < 1 || K < 256 || K % 256 || K > 16384 || M < 1 || M > kPrefillRows) return DAR_E_INVAL;
-  if (wtype != DAR_WTYPE_BF16 && wtype != DAR_WTYPE_FP8_E4M3_ROW) return DAR_E_INVAL;
-  if (wtype == DAR_WTYPE_FP8_E4M3_ROW && !scale) return DAR_E_INVAL;
+  if (wtype != DAR_WTYPE_BF16 && !has_row_scales(wtype)) return DAR_E_INVAL;
+  if (has_row_scales(wtype) && !scale) return DAR_E_INVAL;
   if (!aligned16(W) || !aligned16(x)) return DAR_E_INVAL;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int mpad = gemm_mpad(M);
   const size_t half_bytes = align_up((size_t)mpad * K * sizeof(uint16_t));
-  const int wt = wtype == DAR_WTYPE_FP8_E4M3_ROW ? W_FP8 : W_BF16;
+  const int wt = wtype_of(wtype);
   const size_t part_cap = (size_t)gemm_splits(wt, M, N, K) * M * N;
   char* scratch = nullptr;
   hipError_t e = hipMalloc(&scratch, 2 * half_bytes + part_cap * sizeof(float));
@@ -1510,7 +1528,7 @@ int dar_op_gemm(int32_t wtype, const void* W, const float* scale, int32_t N, int
   uint16_t* xl = reinterpret_cast<uint16_t*>(scratch + half_bytes);
   GemmArgs a{};
   a.W = W;
-  a.scale = wtype == DAR_WTYPE_FP8_E4M3_ROW ? scale : nullptr;
+  a.scale = has_row_scales(wtype) ? scale : nullptr;
   a.N = N;
   a.K = K;
   a.M = M;
@@ -1522,7 +1540,7 @@ int dar_op_gemm(int32_t wtype, const void* W, const float* scale, int32_t N, int
   a.part = reinterpret_cast<float*>(scratch + 2 * half_bytes);
   // x is only read: no sums are pending
   if ((e = launch_norm_split(const_cast<float*>(x), K, M, K, nullptr, 0.f, xh, xl, s)) == hipSuccess &&
-      (e = launch_gemm(wtype == DAR_WTYPE_FP8_E4M3_ROW ? W_FP8 : W_BF16, a, part_cap, s)) == hipSuccess)
+      (e = launch_gemm(wt, a, part_cap, s)) == hipSuccess)
     e = hipStreamSynchronize(s);
   (void)hipStreamSynchronize(s);
   (void)hipFree(scratch);

@@ -23,6 +23,8 @@ DAR_E_WORKSPACE = -5
 DAR_E_UNSUPPORTED = -6
 DAR_WTYPE_BF16 = 0
 DAR_WTYPE_FP8_E4M3_ROW = 1
+DAR_WTYPE_INT8_ROW = 2
+WTYPES = {"bf16": 0, "fp8": DAR_WTYPE_FP8_E4M3_ROW, "int8": DAR_WTYPE_INT8_ROW}
 KIND_NAMES = {0: "qkv", 1: "attention", 2: "wo", 3: "w13", 4: "w2", 5: "head", 6: "other"}
 
 
@@ -98,6 +100,7 @@ _SIGS = {
     "dar_nonfinite": ([_VP, ctypes.POINTER(_I32)], ctypes.c_int),
     "dar_bytes_per_frame": ([ctypes.POINTER(dar_config), _I32, ctypes.POINTER(ctypes.c_double)], ctypes.c_int),
     "dar_quantize_fp8_rows": ([_VP, _I32, _I32, _VP, _VP, _VP], ctypes.c_int),
+    "dar_quantize_int8_rows": ([_VP, _I32, _I32, _VP, _VP, _VP], ctypes.c_int),
     "dar_status_string": ([ctypes.c_int], ctypes.c_char_p),
     "dar_last_error": ([_VP], ctypes.c_char_p),
     "dar_op_gemv": ([_I32, _VP, _VP, _I32, _I32, _VP, _I32, _VP, _VP], ctypes.c_int),
@@ -157,7 +160,7 @@ def make_config(dims, max_len, wtype="bf16", max_batch=1):
         dims.n_layers_slow, dims.n_layers_fast if dims.n_res > 0 else 0, dims.d_model, dims.n_heads_q,
         dims.n_heads_kv, dims.head_dim, dims.ffn_dim, dims.vocab_c0, dims.vocab_res, dims.n_res,
         dims.rms_eps, dims.rope_base, max_len, max_batch,
-        DAR_WTYPE_FP8_E4M3_ROW if wtype == "fp8" else DAR_WTYPE_BF16,
+        WTYPES[wtype],
     )
 
 
@@ -222,6 +225,10 @@ def dar_bytes_per_frame(cfg, T):
 
 def dar_quantize_fp8_rows(w_ptr, rows, cols, q_ptr, scale_ptr, stream_ptr):
     return _check(lib.dar_quantize_fp8_rows(w_ptr, rows, cols, q_ptr, scale_ptr, stream_ptr), "dar_quantize_fp8_rows")
+
+
+def dar_quantize_int8_rows(w_ptr, rows, cols, q_ptr, scale_ptr, stream_ptr):
+    return _check(lib.dar_quantize_int8_rows(w_ptr, rows, cols, q_ptr, scale_ptr, stream_ptr), "dar_quantize_int8_rows")
 
 
 def dar_status_string(status):

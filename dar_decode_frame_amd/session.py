@@ -1,8 +1,8 @@
 """A decode session over the C ABI, with torch providing device memory and the stream.
 
 DeviceWeights uploads canonical bf16 weights (uint16 bit arrays) and, for the
-fp8 mode, quantises every Linear matrix on the device with
-dar_quantize_fp8_rows. DarSession owns the workspace and the dar_ctx and wraps
+fp8 and int8 modes, quantises every Linear matrix on the device with
+dar_quantize_fp8_rows / dar_quantize_int8_rows. DarSession owns the workspace and the dar_ctx and wraps
 prefill / decode_frame with torch tensors. Everything here is marshalling:
 pointers, sizes and buffers; the arithmetic runs in libdar.so.
 """
@@ -23,7 +23,7 @@ def _dev(t):
 
 
 class DeviceWeights:
-    """Device copies of the canonical tensors; fp8 mode adds codes and row scales."""
+    """Device copies of the canonical tensors; fp8 / int8 modes add codes and row scales."""
 
     def __init__(self, dims, host_tensors: dict, wtype: str = "bf16", device="cuda", stream=None,
                  keep_bf16_linears: bool = False):
@@ -36,12 +36,13 @@ class DeviceWeights:
         for name, bits in host_tensors.items():
             arr = np.ascontiguousarray(bits).view(np.int16)
             dev = torch.from_numpy(arr).to(device, non_blocking=False)
-            if wtype == "fp8" and self.is_linear(name):
+            if wtype in ("fp8", "int8") and self.is_linear(name):
                 rows, cols = dev.shape
-                q = torch.empty((rows, cols), dtype=torch.uint8, device=device)
+                q = torch.empty((rows, cols), dtype=torch.uint8 if wtype == "fp8" else torch.int8, device=device)
                 sc = torch.empty((rows,), dtype=torch.float32, device=device)
+                quantize = N.dar_quantize_fp8_rows if wtype == "fp8" else N.dar_quantize_int8_rows
                 with torch.cuda.stream(s):
-                    N.dar_quantize_fp8_rows(_dev(dev), rows, cols, _dev(q), _dev(sc), sp)
+                    quantize(_dev(dev), rows, cols, _dev(q), _dev(sc), sp)
                 self.t[name] = q
                 self.scale[name] = sc
                 if keep_bf16_linears:

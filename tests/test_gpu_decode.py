@@ -54,7 +54,7 @@ def _random_frames(dims, n, seed):
             for _ in range(n)]
 
 
-@pytest.mark.parametrize("wtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("wtype", ["bf16", "fp8", "int8"])
 @pytest.mark.parametrize("forcing", ["oracle", "random"])
 def test_tiny_teacher_forced_parity(tiny_host, wtype, forcing):
     # 60 frames instead of the workload's 16: the agreement rate is a
@@ -84,7 +84,7 @@ def test_tiny_teacher_forced_parity(tiny_host, wtype, forcing):
     sess.close()
 
 
-@pytest.mark.parametrize("wtype,n_prompt", [("bf16", 1), ("bf16", 128), ("bf16", 200), ("fp8", 200)])
+@pytest.mark.parametrize("wtype,n_prompt", [("bf16", 1), ("bf16", 128), ("bf16", 200), ("fp8", 200), ("int8", 200)])
 def test_tiny_prefill_blocks_parity(tiny_host, wtype, n_prompt):
     """Prompts of one position, exactly one prefill block, and two blocks (the
     second ragged), teacher-forced with the oracle's own frames."""
@@ -148,13 +148,14 @@ def test_reset_and_second_prefill_reproduce(tiny_host):
     sess.close()
 
 
-def test_fp8_device_quantiser_matches_oracle(tiny_host):
+@pytest.mark.parametrize("wtype", ["fp8", "int8"])
+def test_device_quantiser_matches_oracle(tiny_host, wtype):
     dims, host = tiny_host
     from dar_decode_frame_amd.session import DeviceWeights
-    dw = DeviceWeights(dims, host, "fp8")
-    m = OracleModel(dims, host, wtype="fp8")
+    dw = DeviceWeights(dims, host, wtype)
+    m = OracleModel(dims, host, wtype=wtype)
     names = synth.linear_names(dims)
-    assert len(m.fp8) == len(names)
+    assert len(m.quant) == len(names)
     for name in names:
         codes, scale = m.quant[name]
         assert np.array_equal(dw.t[name].cpu().numpy(), codes), name
