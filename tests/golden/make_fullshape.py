@@ -15,7 +15,7 @@ Per (frame, codebook) logit vector it stores the oracle's argmax, its top-1 -
 top-2 margin, and the logits at 64 seeded sample indices plus the top two,
 to 7 significant digits (the full vectors would be 160 K floats per run). Slow to run (the fp8
 oracle quantises 4 billion weights in NumPy: minutes); run from the
-repository root:  python3 tests/golden/make_fullshape.py
+repository root:  python3 tests/golden/make_fullshape.py [workload ...]
 """
 import json
 import os
@@ -30,7 +30,7 @@ sys.path.insert(0, ROOT)
 import synth  # noqa: E402
 from oracle import OracleDecoder, OracleModel  # noqa: E402
 
-WORKLOADS = ["s2pro_slow_bf16", "s2pro_dual_bf16", "s2pro_dual_fp8"]
+WORKLOADS = ["s2pro_slow_bf16", "s2pro_dual_bf16", "s2pro_dual_fp8", "s2pro_dual_int8"]
 EARLY_FRAMES = 9
 LATE_LAST_POS = 1007          # slow position of the late frame
 SAMPLES = 64
@@ -62,9 +62,9 @@ def record(frame, dims, seed):
     return vecs
 
 
-def main():
+def main(names):
     out_dir = os.path.dirname(os.path.abspath(__file__))
-    for name in WORKLOADS:
+    for name in names:
         wl = synth.WORKLOADS[name]
         dims = wl.dims
         t0 = time.time()
@@ -100,4 +100,5 @@ def main():
 
 
 if __name__ == "__main__":
-    main()
+    # optional: the workloads to (re)write, default all
+    main(sys.argv[1:] or WORKLOADS)
