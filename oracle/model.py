@@ -43,6 +43,7 @@ from __future__ import annotations
 import numpy as np
 
 from .fp8 import e4m3_decode, quantize_rows
+from .int4 import dequantize_int4, quantize_int4_groups
 from .int8 import quantize_int8_rows
 
 
@@ -158,11 +159,13 @@ class OracleModel:
     *.w2 and fast.head) is quantised per row with the oracle's quantiser and
     used as s * dec(q); tables and norm gains stay bf16. wtype "int8": the same
     matrices quantised per row to int8 (oracle/int8.py), used as s * q.
+    wtype "int4": the same matrices quantised to int4 in groups of 128 columns
+    (oracle/int4.py), used as the dequantised s_g * q.
     """
 
     def __init__(self, dims, tensors: dict, wtype: str = "bf16", dt=np.float32, drop_source: bool = False,
                  kv: str = "bf16"):
-        if wtype not in ("bf16", "fp8", "int8"):
+        if wtype not in ("bf16", "fp8", "int8", "int4"):
             raise ValueError(wtype)
         if kv not in ("bf16", "fp32"):
             raise ValueError(kv)
@@ -183,6 +186,10 @@ class OracleModel:
                 codes, scale = quantize_int8_rows(w)
                 self.quant[name] = (codes, scale)
                 out = Linear(codes.astype(dt), scale.astype(dt))
+            elif wtype == "int4":
+                codes, scale = quantize_int4_groups(w)
+                self.quant[name] = (codes, scale)
+                out = Linear(dequantize_int4(codes, scale).astype(dt, copy=False))
             else:
                 codes, scale = quantize_rows(w)
                 self.quant[name] = (codes, scale)
