@@ -22,7 +22,7 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-DTYPE_NAMES = {"bf16": "bf16", "fp8": "fp8_e4m3", "int8": "int8"}  # the weights' arithmetic type (activations fp32)
+DTYPE_NAMES = {"bf16": "bf16", "fp8": "fp8_e4m3", "int8": "int8", "int4": "int4"}  # the weights' arithmetic type (activations fp32)
 METRIC = "Dual-AR decode frames/s @batch1 + achieved HBM GB/s (% of ~8 TB/s peak)"
 HBM_PEAK = 8.0e12
 
@@ -331,13 +331,12 @@ def measured_traffic(kind, workload):
 
 
 def per_launch_bytes(dims, wtype, kind):
-    """Algorithmic bytes one single-row launch of `kind` reads (weights, row scales, norm gain)."""
-    d, F, hd = dims.d_model, dims.ffn_dim, dims.head_dim
-    eb = 2 if wtype == "bf16" else 1
-    sc = 0 if wtype == "bf16" else 4
+    """Algorithmic bytes one single-row launch of `kind` reads (weights, their scales, norm gain)."""
+    from dar_decode_frame_amd import bytes_model as bm
+    d, F = dims.d_model, dims.ffn_dim
 
-    def mat(rows, cols, scaled=True):
-        return rows * cols * eb + (rows * sc if scaled else 0)
+    def mat(rows, cols):
+        return bm.matrix_bytes(wtype, rows, rows * cols)
 
     if kind == "w13":
         return mat(2 * F, d) + 2 * d

@@ -8,9 +8,9 @@ speedtest"). This module gives:
   * `pages_decode_elements` - the pages' formula, in elements;
   * `frame_bytes` - the algorithmic bytes one frame of this implementation must
     read: every weight matrix and norm the frame touches (the fast AR nine
-    times), the codebook-0 head, fp8 row scales, the slow KV rows of the T
-    positions the step attends to, and the fast AR's per-frame KV as read by
-    its passes (pass k attends over k+1 fast positions). Embedding-row gathers
+    times), the codebook-0 head, the scales of quantised weights, the slow KV
+    rows of the T positions the step attends to, and the fast AR's per-frame
+    KV as read by its passes (pass k attends over k+1 fast positions). Embedding-row gathers
     (one row per step) are not counted.
 
 Pure host arithmetic; no GPU, no library.
@@ -61,15 +61,21 @@ def kv_bytes_per_position(dims, kv_elem_bytes=2):
     return dims.n_layers_slow * 2 * dims.kv_width * kv_elem_bytes
 
 
+def matrix_bytes(wtype, rows, entries):
+    """Bytes of Linear matrices with `rows` rows and `entries` weights in all."""
+    if wtype == "bf16":
+        return 2 * entries
+    if wtype in ("fp8", "int8"):  # one byte per weight + an fp32 scale per row
+        return entries + 4 * rows
+    if wtype == "int4":  # half a byte per weight + an fp32 scale per 128 weights of a row
+        return entries // 2 + 4 * (entries // 128)
+    raise ValueError(wtype)
+
+
 def slow_weight_bytes(dims, wtype):
     mats, norms = layer_params(dims)
     L = dims.n_layers_slow
-    if wtype == "bf16":
-        w = 2 * L * mats
-    elif wtype in ("fp8", "int8"):  # one byte per weight + an fp32 scale per row
-        w = L * mats + 4 * L * layer_rows(dims)
-    else:
-        raise ValueError(wtype)
+    w = matrix_bytes(wtype, L * layer_rows(dims), L * mats)
     return w + 2 * (L * norms + dims.d_model) + 2 * dims.vocab_c0 * dims.d_model
 
 
@@ -79,12 +85,7 @@ def fast_pass_bytes(dims, wtype):
     mats, norms = layer_params(dims)
     L = dims.n_layers_fast
     head = dims.vocab_res * dims.d_model
-    if wtype == "bf16":
-        w = 2 * (L * mats + head)
-    elif wtype in ("fp8", "int8"):
-        w = L * mats + head + 4 * (L * layer_rows(dims) + dims.vocab_res)
-    else:
-        raise ValueError(wtype)
+    w = matrix_bytes(wtype, L * layer_rows(dims) + dims.vocab_res, L * mats + head)
     return w + 2 * (L * norms + dims.d_model)
 
 

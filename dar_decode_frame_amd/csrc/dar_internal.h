@@ -14,7 +14,9 @@ constexpr int kMaxM = 2;           // input rows per GEMV launch (fast pass 1 ru
 constexpr int kAttnChunkDefault = 64;
 constexpr int kPrefillRows = 128;  // prompt positions per prefill block (GEMM rows)
 
-enum WType : int { W_BF16 = 0, W_FP8 = 1, W_INT8 = 2 };  // the last two: one byte per weight + fp32 row scales
+// W_FP8, W_INT8: one byte per weight + fp32 row scales; W_INT4: two weights per
+// byte + fp32 scales per (row, 128-column group)
+enum WType : int { W_BF16 = 0, W_FP8 = 1, W_INT8 = 2, W_INT4 = 3 };
 
 // y[m][r] (+)= scale[r] * sum_j W[r][j] * xin[m][j], xin = x or RMSNorm(x) * gain
 struct GemvArgs {
@@ -314,6 +316,9 @@ hipError_t launch_quantize_fp8(const uint16_t* w, int rows, int cols, uint8_t* q
 hipError_t launch_fp8_decode(const uint8_t* codes, int n, float* out, hipStream_t s);
 // per-row symmetric int8: scale = rowmax|w| / 127, q = rint(w / scale) in [-127, 127]
 hipError_t launch_quantize_int8(const uint16_t* w, int rows, int cols, int8_t* q, float* scale, hipStream_t s);
+// int4 in groups of 128 columns: scale [rows][cols/128] = max|w| / 7, codes
+// rint(w / scale) in [-7, 7], packed two per byte (even column low)
+hipError_t launch_quantize_int4(const uint16_t* w, int rows, int cols, uint8_t* q, float* scale, hipStream_t s);
 hipError_t launch_copy_i32(const int* src, int* dst, int n, hipStream_t s);
 
 size_t attn_partial_floats(int M, int n_kv, int nsplit_max, int group, int head_dim);

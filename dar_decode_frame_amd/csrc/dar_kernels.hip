@@ -79,9 +79,28 @@ __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<
 
 // ------------------------------------------------------- weight dot product --
 
-struct BF16 { static constexpr int kBytes = 2; };
-struct FP8 { static constexpr int kBytes = 1; };
-struct INT8 { static constexpr int kBytes = 1; };
+// Weight types: bits per weight; kGrouped: scales per (row, 128-column group)
+// applied to each 16-byte load's partial sum (else one scale per row, or none)
+struct BF16 { static constexpr int kBits = 16; static constexpr bool kGrouped = false; };
+struct FP8 { static constexpr int kBits = 8; static constexpr bool kGrouped = false; };
+struct INT8 { static constexpr int kBits = 8; static constexpr bool kGrouped = false; };
+struct INT4 { static constexpr int kBits = 4; static constexpr bool kGrouped = true; };
+constexpr int kGroup = 128;  // columns per int4 scale
+
+// byte offset of element n of a weight row
+template <typename WT>
+__device__ __forceinline__ size_t wbytes(size_t n) { return n * WT::kBits / 8; }
+
+// the per-row scale the epilogue applies (group-scaled types have none)
+template <typename WT>
+__device__ __forceinline__ float row_scale(const float* scale, int r) {
+  return (scale && !WT::kGrouped) ? scale[r] : 1.f;
+}
+// row r's group scales, [K / kGroup], for group-scaled types
+template <typename WT>
+__device__ __forceinline__ const float* group_scales(const float* scale, int r, int K) {
+  return WT::kGrouped ? scale + (size_t)r * (K / kGroup) : nullptr;
+}
 
 template <typename WT>
 struct Dot;
@@ -152,6 +171,25 @@ struct Dot<INT8> {
   }
 };
 
+// Two's complement int4 codes, eight per word (even column in the low nibble).
+template <>
+struct Dot<INT4> {
+  static constexpr int E = 32;
+  __device__ static __forceinline__ float word(uint32_t u, const float* x, float s) {
+    const int v = (int)u;
+#pragma unroll
+    for (int n = 0; n < 8; ++n) s = fmaf((float)((v << (28 - 4 * n)) >> 28), x[n], s);
+    return s;
+  }
+  __device__ static __forceinline__ float run(u32x4 w, const float* x) {
+    float s0 = word(w.x, x, 0.f);
+    float s1 = word(w.y, x + 8, 0.f);
+    s0 = word(w.z, x + 16, s0);
+    s1 = word(w.w, x + 24, s1);
+    return s0 + s1;
+  }
+};
+
 // Streams RPW weight rows (K elements each, starting at base[i]) against M
 // input vectors staged in LDS (xs[m*K + j]). Lane l covers 16 bytes of every
 // 1024-byte chunk of a row. Chunks are fetched in batches of U per row, one
@@ -164,25 +202,34 @@ struct RowStream {
   static constexpr int CW = kWave * E;
   static constexpr int U = (RPW >= 4) ? 2 : (8 / RPW);
   const char* base[RPW];
+  const float* sb[RPW];  // group scales of each row (group-scaled types)
   int K, nchunks, lane;
   u32x4 buf[U][RPW];
+  float gbuf[U][RPW];
 
-  __device__ __forceinline__ void fetch(int c0, u32x4 (&w)[U][RPW]) const {
+  __device__ __forceinline__ void fetch(int c0, u32x4 (&w)[U][RPW], float (&g)[U][RPW]) const {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int col = min((c0 + u) * CW + lane * E, K - E);
 #pragma unroll
-      for (int i = 0; i < RPW; ++i) w[u][i] = ld16_nt(base[i] + (size_t)col * WT::kBytes);
+      for (int i = 0; i < RPW; ++i) {
+        w[u][i] = ld16_nt(base[i] + wbytes<WT>(col));
+        if constexpr (WT::kGrouped) g[u][i] = sb[i][col / kGroup];
+      }
     }
   }
 
-  __device__ __forceinline__ void start(const char* const (&rows)[RPW], int K_, int lane_) {
+  __device__ __forceinline__ void start(const char* const (&rows)[RPW], int K_, int lane_,
+                                        const float* const* scales = nullptr) {
 #pragma unroll
-    for (int i = 0; i < RPW; ++i) base[i] = rows[i];
+    for (int i = 0; i < RPW; ++i) {
+      base[i] = rows[i];
+      sb[i] = scales ? scales[i] : nullptr;
+    }
     K = K_;
     lane = lane_;
     nchunks = (K + CW - 1) / CW;
-    fetch(0, buf);
+    fetch(0, buf, gbuf);
   }
 
   __device__ __forceinline__ void run(const float* xs, float (&acc)[RPW][M]) {
@@ -192,8 +239,9 @@ struct RowStream {
       for (int m = 0; m < M; ++m) acc[i][m] = 0.f;
     for (int c0 = 0; c0 < nchunks; c0 += U) {
       u32x4 nxt[U][RPW];
+      float gnxt[U][RPW];
       const bool more = c0 + U < nchunks;
-      if (more) fetch(c0 + U, nxt);
+      if (more) fetch(c0 + U, nxt, gnxt);
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int col = (c0 + u) * CW + lane * E;
@@ -201,7 +249,11 @@ struct RowStream {
 #pragma unroll
           for (int m = 0; m < M; ++m) {
 #pragma unroll
-            for (int i = 0; i < RPW; ++i) acc[i][m] += Dot<WT>::run(buf[u][i], xs + m * K + col);
+            for (int i = 0; i < RPW; ++i) {
+              const float d = Dot<WT>::run(buf[u][i], xs + m * K + col);
+              if constexpr (WT::kGrouped) acc[i][m] = fmaf(gbuf[u][i], d, acc[i][m]);
+              else acc[i][m] += d;
+            }
           }
         }
       }
@@ -209,7 +261,10 @@ struct RowStream {
 #pragma unroll
         for (int u = 0; u < U; ++u)
 #pragma unroll
-          for (int i = 0; i < RPW; ++i) buf[u][i] = nxt[u][i];
+          for (int i = 0; i < RPW; ++i) {
+            buf[u][i] = nxt[u][i];
+            gbuf[u][i] = gnxt[u][i];
+          }
       }
     }
   }
@@ -339,7 +394,7 @@ struct Stager {
 
 template <typename WT>
 __device__ __forceinline__ const char* row_ptr(const void* W, int r, int K) {
-  return reinterpret_cast<const char*>(W) + (size_t)r * K * WT::kBytes;
+  return reinterpret_cast<const char*>(W) + wbytes<WT>((size_t)r * K);
 }
 
 // LDS of the GEMV-shaped bodies: the staged input rows, then small scratch.
@@ -364,9 +419,13 @@ __device__ __forceinline__ void gemv_body(const GemvArgs& a, int bid, char* lds)
   RowStream<WT, M, RPW> rs;
   {
     const char* base[RPW];
+    const float* sc[RPW];
 #pragma unroll
-    for (int i = 0; i < RPW; ++i) base[i] = row_ptr<WT>(a.W, min(r0 + i, a.rows - 1), a.K);
-    rs.start(base, a.K, lane);
+    for (int i = 0; i < RPW; ++i) {
+      base[i] = row_ptr<WT>(a.W, min(r0 + i, a.rows - 1), a.K);
+      sc[i] = group_scales<WT>(a.scale, min(r0 + i, a.rows - 1), a.K);
+    }
+    rs.start(base, a.K, lane, sc);
   }
   st.finish(xs, lds_scratch(lds, M, a.K), a.eps);
   if (!active) return;
@@ -379,7 +438,7 @@ __device__ __forceinline__ void gemv_body(const GemvArgs& a, int bid, char* lds)
       float s = wave_sum(acc[i][m]);
       const int r = r0 + i;
       if (lane == 0 && r < a.rows) {
-        if (a.scale) s *= a.scale[r];
+        s *= row_scale<WT>(a.scale, r);
         float* y = a.y + (size_t)m * a.y_stride + r;
         *y = a.accumulate ? (*y + s) : s;
       }
@@ -407,7 +466,8 @@ __device__ __forceinline__ void qkv_body(const QkvArgs& a, int bid, char* lds) {
   RowStream<WT, M, 2> rs;
   {
     const char* base[2] = {row_ptr<WT>(a.W, r1, a.K), row_ptr<WT>(a.W, r2, a.K)};
-    rs.start(base, a.K, lane);
+    const float* sc[2] = {group_scales<WT>(a.scale, r1, a.K), group_scales<WT>(a.scale, r2, a.K)};
+    rs.start(base, a.K, lane, sc);
   }
   st.finish(xs, lds_scratch(lds, M, a.K), a.eps);
   if (!active) return;
@@ -420,7 +480,7 @@ __device__ __forceinline__ void qkv_body(const QkvArgs& a, int bid, char* lds) {
     y2[m] = wave_sum(acc[1][m]);
   }
   if (lane != 0) return;
-  const float sc1 = a.scale ? a.scale[r1] : 1.f, sc2 = a.scale ? a.scale[r2] : 1.f;
+  const float sc1 = row_scale<WT>(a.scale, r1), sc2 = row_scale<WT>(a.scale, r2);
   const int pos0 = *a.pos;
 #pragma unroll
   for (int m = 0; m < M; ++m) {
@@ -460,7 +520,8 @@ __device__ __forceinline__ void swiglu_body(const SwigluArgs& a, int bid, char* 
   {
     const int rc = min(r, a.F - 1);
     const char* base[2] = {row_ptr<WT>(a.W1, rc, a.K), row_ptr<WT>(a.W3, rc, a.K)};
-    rs.start(base, a.K, lane);
+    const float* sc[2] = {group_scales<WT>(a.s1, rc, a.K), group_scales<WT>(a.s3, rc, a.K)};
+    rs.start(base, a.K, lane, sc);
   }
   st.finish(xs, lds_scratch(lds, M, a.K), a.eps);
   if (!active) return;
@@ -471,8 +532,8 @@ __device__ __forceinline__ void swiglu_body(const SwigluArgs& a, int bid, char* 
     float g = wave_sum(acc[0][m]);
     float u = wave_sum(acc[1][m]);
     if (lane == 0) {
-      if (a.s1) g *= a.s1[r];
-      if (a.s3) u *= a.s3[r];
+      g *= row_scale<WT>(a.s1, r);
+      u *= row_scale<WT>(a.s3, r);
       const float silu = g / (1.0f + expf(-g));
       a.h[(size_t)m * a.h_stride + r] = silu * u;
     }
@@ -506,9 +567,13 @@ __device__ __forceinline__ void head_body(const HeadArgs& a, int bid, char* lds)
   RowStream<WT, 1, RPW> rs;
   {
     const char* base[RPW];
+    const float* sc[RPW];
 #pragma unroll
-    for (int i = 0; i < RPW; ++i) base[i] = row_ptr<WT>(a.W, min(r0 + i, a.rows - 1), a.K);
-    rs.start(base, a.K, lane);
+    for (int i = 0; i < RPW; ++i) {
+      base[i] = row_ptr<WT>(a.W, min(r0 + i, a.rows - 1), a.K);
+      sc[i] = group_scales<WT>(a.scale, min(r0 + i, a.rows - 1), a.K);
+    }
+    rs.start(base, a.K, lane, sc);
   }
   st.finish(xs, red, a.eps);
   if (a.h_out && bid == 0) {
@@ -523,7 +588,7 @@ __device__ __forceinline__ void head_body(const HeadArgs& a, int bid, char* lds)
       float s = wave_sum(acc[i][0]);
       const int r = r0 + i;
       if (r < a.rows) {
-        if (a.scale) s *= a.scale[r];
+        s *= row_scale<WT>(a.scale, r);
         if (lane == 0) {
           a.logits[r] = s;
           if (!isfinite(s)) atomicAdd(a.anomalies, 1);
@@ -820,6 +885,7 @@ struct RegStream {
   float4 x[NCH][NX];
   u32x4 g[NCH][NG];
   u32x4 w[RPW][NCH];
+  float gs[RPW][NCH];  // group scale of each row's chunk slice (group-scaled types)
   int lane, K;
   int c0 = 0, cs = 1;  // this wave's chunk c is input chunk c0 + c * cs
 
@@ -840,12 +906,15 @@ struct RegStream {
     }
   }
 
-  __device__ __forceinline__ void load_w(const char* const (&base)[RPW]) {
+  __device__ __forceinline__ void load_w(const char* const (&base)[RPW], const float* const* scales = nullptr) {
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
       const int col = min(col_of(c), K - E);
 #pragma unroll
-      for (int i = 0; i < RPW; ++i) w[i][c] = ld16_nt(base[i] + (size_t)col * WT::kBytes);
+      for (int i = 0; i < RPW; ++i) {
+        w[i][c] = ld16_nt(base[i] + wbytes<WT>(col));
+        if constexpr (WT::kGrouped) gs[i][c] = scales[i][col / kGroup];
+      }
     }
   }
 
@@ -886,7 +955,11 @@ struct RegStream {
   __device__ __forceinline__ float dot_row(int i) const {
     float acc = 0.f;
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) acc += Dot<WT>::run(w[i][c], reinterpret_cast<const float*>(&x[c][0]));
+    for (int c = 0; c < NCH; ++c) {
+      const float d = Dot<WT>::run(w[i][c], reinterpret_cast<const float*>(&x[c][0]));
+      if constexpr (WT::kGrouped) acc = fmaf(gs[i][c], d, acc);
+      else acc += d;
+    }
     return acc;
   }
 
@@ -918,6 +991,10 @@ template <>
 struct PerWave<INT8> {
   static constexpr int v = 2;
 };
+template <>
+struct PerWave<INT4> {
+  static constexpr int v = 4;  // a quarter of a bf16 row's bytes per row
+};
 
 // y[r] (+)= scale[r] * W[r] . x, P rows per wave
 template <typename WT, int NCH>
@@ -928,9 +1005,13 @@ __device__ __forceinline__ void gemv_reg_body(const GemvArgs& a, int bid) {
   RegStream<WT, NCH, P> rs;
   rs.load_x(a.x, a.gain, a.K, lane);
   const char* base[P];
+  const float* sc[P];
 #pragma unroll
-  for (int i = 0; i < P; ++i) base[i] = row_ptr<WT>(a.W, min(r0 + i, a.rows - 1), a.K);
-  rs.load_w(base);
+  for (int i = 0; i < P; ++i) {
+    base[i] = row_ptr<WT>(a.W, min(r0 + i, a.rows - 1), a.K);
+    sc[i] = group_scales<WT>(a.scale, min(r0 + i, a.rows - 1), a.K);
+  }
+  rs.load_w(base, sc);
   rs.prepare(a.gain != nullptr, a.eps);
 #pragma unroll
   for (int i = 0; i < P; ++i) {
@@ -938,7 +1019,7 @@ __device__ __forceinline__ void gemv_reg_body(const GemvArgs& a, int bid) {
     if (r >= a.rows) return;
     float s = wave_sum(rs.dot_row(i));
     if (lane == 0) {
-      if (a.scale) s *= a.scale[r];
+      s *= row_scale<WT>(a.scale, r);
       float* y = a.y + r;
       *y = a.accumulate ? (*y + s) : s;
     }
@@ -958,14 +1039,17 @@ __device__ __forceinline__ void qkv_reg_body(const QkvArgs& a, int bid) {
   RegStream<WT, NCH, 2 * P> rs;
   rs.load_x(a.x, a.gain, a.K, lane);
   const char* base[2 * P];
+  const float* sc[2 * P];
 #pragma unroll
   for (int j = 0; j < P; ++j) {
     const int pc = min(p0 + j, npairs - 1);
     const int r1 = (pc / half) * a.head_dim + pc % half;
     base[2 * j] = row_ptr<WT>(a.W, r1, a.K);
     base[2 * j + 1] = row_ptr<WT>(a.W, r1 + half, a.K);
+    sc[2 * j] = group_scales<WT>(a.scale, r1, a.K);
+    sc[2 * j + 1] = group_scales<WT>(a.scale, r1 + half, a.K);
   }
-  rs.load_w(base);
+  rs.load_w(base, sc);
   rs.prepare(true, a.eps);
   const int pos = *a.pos;
 #pragma unroll
@@ -977,7 +1061,7 @@ __device__ __forceinline__ void qkv_reg_body(const QkvArgs& a, int bid) {
     const float y1 = wave_sum(rs.dot_row(2 * j));
     const float y2 = wave_sum(rs.dot_row(2 * j + 1));
     if (lane != 0) continue;
-    const float u = y1 * (a.scale ? a.scale[r1] : 1.f), v = y2 * (a.scale ? a.scale[r2] : 1.f);
+    const float u = y1 * row_scale<WT>(a.scale, r1), v = y2 * row_scale<WT>(a.scale, r2);
     if (head < a.n_heads_q + a.n_heads_kv) {
       const float2 cs = a.rope[(size_t)pos * half + i];
       const float o1 = u * cs.x - v * cs.y;
@@ -1007,13 +1091,16 @@ __device__ __forceinline__ void swiglu_reg_body(const SwigluArgs& a, int bid) {
   RegStream<WT, NCH, 2 * P> rs;
   rs.load_x(a.x, a.gain, a.K, lane);
   const char* base[2 * P];
+  const float* sc[2 * P];
 #pragma unroll
   for (int j = 0; j < P; ++j) {
     const int rc = min(r0 + j, a.F - 1);
     base[2 * j] = row_ptr<WT>(a.W1, rc, a.K);
     base[2 * j + 1] = row_ptr<WT>(a.W3, rc, a.K);
+    sc[2 * j] = group_scales<WT>(a.s1, rc, a.K);
+    sc[2 * j + 1] = group_scales<WT>(a.s3, rc, a.K);
   }
-  rs.load_w(base);
+  rs.load_w(base, sc);
   rs.prepare(true, a.eps);
 #pragma unroll
   for (int j = 0; j < P; ++j) {
@@ -1022,8 +1109,8 @@ __device__ __forceinline__ void swiglu_reg_body(const SwigluArgs& a, int bid) {
     float g = wave_sum(rs.dot_row(2 * j));
     float u = wave_sum(rs.dot_row(2 * j + 1));
     if (lane == 0) {
-      if (a.s1) g *= a.s1[r];
-      if (a.s3) u *= a.s3[r];
+      g *= row_scale<WT>(a.s1, r);
+      u *= row_scale<WT>(a.s3, r);
       const float silu = g / (1.0f + expf(-g));
       a.h[r] = silu * u;
     }
@@ -1043,9 +1130,13 @@ __device__ __forceinline__ void gemv_split_body(const GemvArgs& a, int bid, char
   rs.cs = kWaves;
   rs.load_x(a.x, nullptr, a.K, lane);
   const char* base[R];
+  const float* sc[R];
 #pragma unroll
-  for (int i = 0; i < R; ++i) base[i] = row_ptr<WT>(a.W, min(r0 + i, a.rows - 1), a.K);
-  rs.load_w(base);
+  for (int i = 0; i < R; ++i) {
+    base[i] = row_ptr<WT>(a.W, min(r0 + i, a.rows - 1), a.K);
+    sc[i] = group_scales<WT>(a.scale, min(r0 + i, a.rows - 1), a.K);
+  }
+  rs.load_w(base, sc);
   rs.prepare(false, 0.f);
   float* part = reinterpret_cast<float*>(lds);  // [kWaves][R]
 #pragma unroll
@@ -1059,7 +1150,7 @@ __device__ __forceinline__ void gemv_split_body(const GemvArgs& a, int bid, char
     float s = part[lane];
 #pragma unroll
     for (int w = 1; w < kWaves; ++w) s += part[w * R + lane];
-    if (a.scale) s *= a.scale[r];
+    s *= row_scale<WT>(a.scale, r);
     float* y = a.y + r;
     *y = a.accumulate ? (*y + s) : s;
   }
@@ -1074,7 +1165,9 @@ __device__ __forceinline__ void head_reg_body(const HeadArgs& a, int bid, char* 
   RegStream<WT, NCH, 2> rs;
   rs.load_x(a.x, a.gain, a.K, lane);
   const char* base[2] = {row_ptr<WT>(a.W, min(r0, a.rows - 1), a.K), row_ptr<WT>(a.W, min(r0 + 1, a.rows - 1), a.K)};
-  rs.load_w(base);
+  const float* sc[2] = {group_scales<WT>(a.scale, min(r0, a.rows - 1), a.K),
+                        group_scales<WT>(a.scale, min(r0 + 1, a.rows - 1), a.K)};
+  rs.load_w(base, sc);
   rs.prepare(true, a.eps);
   if (a.h_out && bid == 0 && wave == 0) rs.store_x(a.h_out);
   unsigned long long best = 0ull;
@@ -1083,7 +1176,7 @@ __device__ __forceinline__ void head_reg_body(const HeadArgs& a, int bid, char* 
     const int r = r0 + i;
     float s = wave_sum(rs.dot_row(i));
     if (r < a.rows) {
-      if (a.scale) s *= a.scale[r];
+      s *= row_scale<WT>(a.scale, r);
       if (lane == 0) {
         a.logits[r] = s;
         if (!isfinite(s)) atomicAdd(a.anomalies, 1);
@@ -1406,6 +1499,32 @@ __global__ __launch_bounds__(kBlock) void k_quantize_int8(const uint16_t* w, int
     qr[k] = (s > 0.f) ? (int8_t)fminf(fmaxf(rintf(bf2f(row[k]) / s), -127.f), 127.f) : (int8_t)0;
 }
 
+// One workgroup per row; a wave per 128-column group at a time: scale =
+// max|w| / 7 over the group, codes = rint(w / scale) clamped to [-7, 7], two
+// per byte (the even column in the low nibble).
+__global__ __launch_bounds__(kBlock) void k_quantize_int4(const uint16_t* w, int rows, int cols, uint8_t* q,
+                                                         float* scale) {
+  const int r = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const uint16_t* row = w + (size_t)r * cols;
+  const int ngroups = cols / kGroup;
+  for (int gi = wave; gi < ngroups; gi += kWaves) {
+    const int c = gi * kGroup + 2 * lane;  // this lane's pair of columns
+    const float a = bf2f(row[c]), b = bf2f(row[c + 1]);
+    float mx = fmaxf(fabsf(a), fabsf(b));
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+    const float s = mx / 7.0f;
+    if (lane == 0) scale[(size_t)r * ngroups + gi] = s;
+    int qa = 0, qb = 0;
+    if (s > 0.f) {
+      qa = (int)fminf(fmaxf(rintf(a / s), -7.f), 7.f);
+      qb = (int)fminf(fmaxf(rintf(b / s), -7.f), 7.f);
+    }
+    q[((size_t)r * cols + c) / 2] = (uint8_t)((qa & 0xF) | ((qb & 0xF) << 4));
+  }
+}
+
 __global__ void k_fp8_decode(const uint8_t* codes, int n, float* out) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) {
@@ -1612,6 +1731,7 @@ hipError_t launch_task(int wtype, const Task& t, hipStream_t s) {
   if (row_stage(t, s, e)) return e;
   if (wtype == W_FP8) return single_launch<FP8>(t, s, false);
   if (wtype == W_INT8) return single_launch<INT8>(t, s, false);
+  if (wtype == W_INT4) return single_launch<INT4>(t, s, false);
   return single_launch<BF16>(t, s, false);
 }
 
@@ -1619,6 +1739,7 @@ hipError_t prepare_task(int wtype, const Task& t) {
   if (t.kind >= T_NORM_SPLIT) return hipSuccess;  // the many-row kernels need no set-up
   if (wtype == W_FP8) return single_launch<FP8>(t, nullptr, true);
   if (wtype == W_INT8) return single_launch<INT8>(t, nullptr, true);
+  if (wtype == W_INT4) return single_launch<INT4>(t, nullptr, true);
   return single_launch<BF16>(t, nullptr, true);
 }
 
@@ -1665,6 +1786,12 @@ hipError_t launch_quantize_fp8(const uint16_t* w, int rows, int cols, uint8_t* q
 
 hipError_t launch_quantize_int8(const uint16_t* w, int rows, int cols, int8_t* q, float* scale, hipStream_t s) {
   hipLaunchKernelGGL(k_quantize_int8, dim3(rows), dim3(kBlock), 0, s, w, rows, cols, q, scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_int4(const uint16_t* w, int rows, int cols, uint8_t* q, float* scale, hipStream_t s) {
+  if (cols % kGroup) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_quantize_int4, dim3(rows), dim3(kBlock), 0, s, w, rows, cols, q, scale);
   return hipGetLastError();
 }
 

@@ -64,7 +64,8 @@ __device__ __forceinline__ void wait_loads() {
 // row r sit XOR-swizzled, unit u at slot u ^ (r % 8), so the 32 lanes that
 // read one unit of 32 consecutive rows hit distinct bank groups.
 struct BF16T {
-  static constexpr int kBytes = 2;
+  static constexpr int kBits = 16;
+  static constexpr bool kGrouped = false;
   // eight consecutive weights of row r at k = 16 s + 8 half, as the MFMA B operand
   __device__ static __forceinline__ bf16x8 frag(const char* st, int r, int s, int half) {
     const int u = (2 * s + half) ^ (r & 7);
@@ -73,7 +74,8 @@ struct BF16T {
 };
 
 struct FP8T {
-  static constexpr int kBytes = 1;
+  static constexpr int kBits = 8;
+  static constexpr bool kGrouped = false;
   // e4m3fn values are exact in bf16: widen through fp32 and keep the top half
   __device__ static __forceinline__ uint32_t pack2(f32x2 v) {
     return (__float_as_uint(v.x) >> 16) | (__float_as_uint(v.y) & 0xffff0000u);
@@ -91,7 +93,8 @@ struct FP8T {
 };
 
 struct INT8T {
-  static constexpr int kBytes = 1;
+  static constexpr int kBits = 8;
+  static constexpr bool kGrouped = false;
   // int8 codes (|q| <= 127) are exact in bf16: sign-extend, convert, keep the top half
   __device__ static __forceinline__ uint32_t pack2(int a, int b) {
     return (__float_as_uint((float)a) >> 16) | (__float_as_uint((float)b) & 0xffff0000u);
@@ -105,6 +108,27 @@ struct INT8T {
     o.y = pack2((x << 8) >> 24, x >> 24);
     o.z = pack2((y << 24) >> 24, (y << 16) >> 24);
     o.w = pack2((y << 8) >> 24, y >> 24);
+    return __builtin_bit_cast(bf16x8, o);
+  }
+};
+
+// Two's complement int4 codes, two per byte (even column in the low nibble),
+// with an fp32 scale per (row, 128 columns): a 128-byte chunk of a row is two
+// scale groups of 128 codes. A k-step's eight codes are one 32-bit word.
+struct INT4T {
+  static constexpr int kBits = 4;
+  static constexpr bool kGrouped = true;
+  __device__ static __forceinline__ uint32_t pack2(int a, int b) {
+    return (__float_as_uint((float)a) >> 16) | (__float_as_uint((float)b) & 0xffff0000u);
+  }
+  __device__ static __forceinline__ bf16x8 frag(const char* st, int r, int s, int half) {
+    const int u = (s >> 1) ^ (r & 7);
+    const int w = *reinterpret_cast<const int*>(st + (r * 8 + u) * 16 + (s & 1) * 8 + 4 * half);
+    u32x4 o;
+    o.x = pack2((w << 28) >> 28, (w << 24) >> 28);
+    o.y = pack2((w << 20) >> 28, (w << 16) >> 28);
+    o.z = pack2((w << 12) >> 28, (w << 8) >> 28);
+    o.w = pack2((w << 4) >> 28, w >> 28);
     return __builtin_bit_cast(bf16x8, o);
   }
 };
@@ -136,23 +160,30 @@ __device__ __forceinline__ void gemm_store(const GemmArgs& a, const f32x16 (&acc
   }
 }
 
+// k per chunk (128 bytes of a weight row)
+template <typename WT>
+constexpr int kChunkK = kRowChunk * 8 / WT::kBits;
+
 // One workgroup: weight rows [128 bx, +128) (wave w: 32 rows) x input rows
 // [32 MT by, +32 MT) x the chunks of split bz. A chunk is 128 B of each
-// weight row (64 bf16 or 128 e4m3 weights) and the matching hi and lo input
-// columns (same swizzle, per input row). Chunks stream through a ring of
-// kStages LDS buffers by direct loads, issued kStages - 1 chunks ahead; a
-// chunk costs one barrier, after which every wave runs its MFMAs from LDS.
+// weight row (64 bf16, 128 e4m3 or int8, 256 int4 weights) and the matching
+// hi and lo input columns (same swizzle, per input row). Chunks stream
+// through a ring of kStages LDS buffers by direct loads, issued kStages - 1
+// chunks ahead; a chunk costs one barrier, after which every wave runs its
+// MFMAs from LDS. Group-scaled weights (int4) sum each 128-column group on its
+// own and add it times the group's scale, loaded with the chunk.
 template <typename WT, int MT>
 __global__ __launch_bounds__(kBlock) void k_gemm(GemmArgs a) {
-  constexpr int KC = kRowChunk / WT::kBytes;           // k per chunk
+  constexpr int KC = kChunkK<WT>;                      // k per chunk
   constexpr int ST = KC / 16;                          // MFMA k-steps per chunk
   constexpr int XU = KC / 8;                           // 16-byte units of an input row per chunk
   constexpr int WB = kTileN * kRowChunk;               // weight bytes per stage
   constexpr int XB = 2 * 32 * MT * XU * 16;            // input bytes per stage (hi, lo)
   constexpr int SB = WB + XB;
   constexpr int XL = XB / (16 * 64 * kWaves);          // input loads per wave per stage
-  constexpr int LPS = 4 + XL;                          // loads per wave per stage
+  constexpr int LPS = 4 + XL + (WT::kGrouped ? 1 : 0); // loads per wave per stage
   static_assert(XL * 16 * 64 * kWaves == XB, "input staging split");
+  static_assert(!WT::kGrouped || (MT == 1 && KC == 256), "group scales: two 128-column groups per chunk");
   __shared__ __align__(16) char sm[kStages * SB];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nb = blockIdx.x * kTileN;
@@ -164,9 +195,15 @@ __global__ __launch_bounds__(kBlock) void k_gemm(GemmArgs a) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int r = wave * 32 + 8 * i + (lane >> 3);
-    wsrc[i] = reinterpret_cast<const char*>(a.W) + (size_t)min(nb + r, a.N - 1) * a.K * WT::kBytes +
+    wsrc[i] = reinterpret_cast<const char*>(a.W) + (size_t)min(nb + r, a.N - 1) * a.K * WT::kBits / 8 +
               (size_t)c_begin * kRowChunk + 16 * ((lane & 7) ^ (lane >> 3));
   }
+  // group scales of this lane's weight row, two per chunk
+  const f32x2* gsrc = nullptr;
+  if constexpr (WT::kGrouped)
+    gsrc = reinterpret_cast<const f32x2*>(a.scale + (size_t)min(nb + wave * 32 + (lane & 31), a.N - 1) * (a.K / 128)) +
+           c_begin;
+  f32x2 gsc[kStages];
   // input load j of this wave fills 64 consecutive slots of the hi or lo part
   const char* xsrc[XL];
 #pragma unroll
@@ -184,6 +221,7 @@ __global__ __launch_bounds__(kBlock) void k_gemm(GemmArgs a) {
     for (int i = 0; i < 4; ++i) load_lds16(wsrc[i] + (size_t)t * kRowChunk, base + wave * 4096 + i * 1024);
 #pragma unroll
     for (int j = 0; j < XL; ++j) load_lds16(xsrc[j] + (size_t)t * KC * 2, base + WB + (wave * XL + j) * 1024);
+    if constexpr (WT::kGrouped) gsc[stage] = gsrc[t];
   };
   f32x16 acc[MT];
 #pragma unroll
@@ -209,24 +247,53 @@ __global__ __launch_bounds__(kBlock) void k_gemm(GemmArgs a) {
         if (t + kStages - 1 < nc) issue(t + kStages - 1, (j + kStages - 1) % kStages);
         const char* ws = sm + j * SB;
         const char* xs = ws + WB;
+        if constexpr (WT::kGrouped) {
+          const int row = lane & 31;
 #pragma unroll
-        for (int s = 0; s < ST; ++s) {
-          const bf16x8 b = WT::frag(ws, wave * 32 + (lane & 31), s, half);
+          for (int g = 0; g < 2; ++g) {
+            f32x16 gh, gl;
 #pragma unroll
-          for (int mt = 0; mt < MT; ++mt) {
-            const int row = mt * 32 + (lane & 31);
-            const int u = (2 * s + half) ^ (row & 7);
-            const bf16x8 ah = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(xs + (row * XU + u) * 16));
-            const bf16x8 al =
-                __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(xs + ((32 * MT + row) * XU + u) * 16));
-            acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, b, acc[mt], 0, 0, 0);
-            acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, b, acc[mt], 0, 0, 0);
+            for (int v = 0; v < 16; ++v) gh[v] = gl[v] = 0.f;
+#pragma unroll
+            for (int s = 8 * g; s < 8 * g + 8; ++s) {
+              const bf16x8 b = WT::frag(ws, wave * 32 + row, s, half);
+              const int u = (2 * s + half) ^ (row & 7);
+              const bf16x8 ah = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(xs + (row * XU + u) * 16));
+              const bf16x8 al =
+                  __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(xs + ((32 + row) * XU + u) * 16));
+              gh = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, b, gh, 0, 0, 0);
+              gl = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, b, gl, 0, 0, 0);
+            }
+            const float sc = g ? gsc[j].y : gsc[j].x;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[0][v] = fmaf(gh[v] + gl[v], sc, acc[0][v]);
+          }
+        } else {
+#pragma unroll
+          for (int s = 0; s < ST; ++s) {
+            const bf16x8 b = WT::frag(ws, wave * 32 + (lane & 31), s, half);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+              const int row = mt * 32 + (lane & 31);
+              const int u = (2 * s + half) ^ (row & 7);
+              const bf16x8 ah = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(xs + (row * XU + u) * 16));
+              const bf16x8 al =
+                  __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(xs + ((32 * MT + row) * XU + u) * 16));
+              acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, b, acc[mt], 0, 0, 0);
+              acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, b, acc[mt], 0, 0, 0);
+            }
           }
         }
       }
     }
   }
-  gemm_store<MT>(a, acc, nb + wave * 32 + (lane & 31), m0, lane);
+  if constexpr (WT::kGrouped) {
+    GemmArgs b = a;
+    b.scale = nullptr;  // already applied per group
+    gemm_store<MT>(b, acc, nb + wave * 32 + (lane & 31), m0, lane);
+  } else {
+    gemm_store<MT>(a, acc, nb + wave * 32 + (lane & 31), m0, lane);
+  }
 }
 
 // s_waitcnt vmcnt(4 n) for a count n in [0, 5] known only at run time
@@ -250,11 +317,12 @@ __device__ __forceinline__ void wait_loads_x4(int n) {
 // k_gemm. Needs a.cps <= kResidentChunks<WT>. (Staging only 16 input rows
 // for a six-slot ring was tried at 16 sequences: no faster.)
 template <typename WT>
-constexpr int kResidentChunks = WT::kBytes == 2 ? 14 : 7;  // a one-byte chunk spans twice the input columns
+constexpr int kResidentChunks = WT::kBits == 16 ? 14 : 7;  // a one-byte chunk spans twice the input columns
 
 template <typename WT>
 __global__ __launch_bounds__(kBlock) void k_gemm_x(GemmArgs a) {
-  constexpr int KC = kRowChunk / WT::kBytes;
+  static_assert(!WT::kGrouped, "row-scaled or unscaled weights only");
+  constexpr int KC = kChunkK<WT>;
   constexpr int ST = KC / 16;
   constexpr int XU = KC / 8;
   constexpr int XROWS = 32;                            // staged input rows
@@ -275,7 +343,7 @@ __global__ __launch_bounds__(kBlock) void k_gemm_x(GemmArgs a) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int r = wave * 32 + 8 * i + (lane >> 3);
-    wsrc[i] = reinterpret_cast<const char*>(a.W) + (size_t)min(nb + r, a.N - 1) * a.K * WT::kBytes +
+    wsrc[i] = reinterpret_cast<const char*>(a.W) + (size_t)min(nb + r, a.N - 1) * a.K * WT::kBits / 8 +
               (size_t)c_begin * kRowChunk + 16 * ((lane & 7) ^ (lane >> 3));
   }
   auto issue_w = [&](int t) {
@@ -592,7 +660,9 @@ __global__ void k_inc_rows(int* v, int n) {
 }
 
 hipError_t gemm_dispatch(int wtype, const GemmArgs& a, int mt, dim3 grid, hipStream_t s) {
-  if (wtype == W_INT8) {
+  if (wtype == W_INT4) {
+    hipLaunchKernelGGL((k_gemm<INT4T, 1>), grid, dim3(kBlock), 0, s, a);
+  } else if (wtype == W_INT8) {
     if (mt == 1 && a.cps <= kResidentChunks<INT8T>)
       hipLaunchKernelGGL((k_gemm_x<INT8T>), grid, dim3(kBlock), 0, s, a);
     else if (mt == 1)
@@ -626,10 +696,17 @@ hipError_t gemm_dispatch(int wtype, const GemmArgs& a, int mt, dim3 grid, hipStr
 int gemm_mpad(int M) { return M <= 32 ? 32 : (M <= 64 ? 64 : ((M + 127) / 128) * 128); }
 
 // input rows per workgroup / 32: the one-byte kernels (e4m3, int8) stage
-// twice the input columns per chunk, so their LDS ring holds at most 64 input rows
+// twice the input columns per chunk, so their LDS ring holds at most 64 input
+// rows; int4 stages four times as many, so 32
 static int gemm_mt(int wtype, int M) {
   const int mt = M <= 32 ? 1 : (M <= 64 ? 2 : 4);
+  if (wtype == W_INT4) return 1;
   return (wtype != W_BF16 && mt > 2) ? 2 : mt;
+}
+
+// k per chunk of a weight type
+static int gemm_kc(int wtype) {
+  return wtype == W_BF16 ? kChunkK<BF16T> : (wtype == W_INT4 ? kChunkK<INT4T> : kChunkK<FP8T>);
 }
 
 // K splits: as many as keep the launch within one workgroup per CU (a
@@ -639,9 +716,9 @@ static int gemm_mt(int wtype, int M) {
 int gemm_splits(int wtype, int M, int N, int K) {
   const int mt = gemm_mt(wtype, M);
   const int tiles = ((N + kTileN - 1) / kTileN) * ((M + 32 * mt - 1) / (32 * mt));
-  const int nchunks = K / (kRowChunk / (wtype == W_BF16 ? 2 : 1));
+  const int nchunks = K / gemm_kc(wtype);
   int splits = 256 / tiles;
-  if (mt == 1) {
+  if (mt == 1 && wtype != W_INT4) {
     const int resident = wtype == W_BF16 ? kResidentChunks<BF16T> : kResidentChunks<FP8T>;
     splits = std::max(splits, (nchunks + resident - 1) / resident);
   }
@@ -651,7 +728,7 @@ int gemm_splits(int wtype, int M, int N, int K) {
 }
 
 int gemm_launch_splits(int wtype, int M, int N, int K, size_t part_cap) {
-  const int nchunks = K / (kRowChunk / (wtype == W_BF16 ? 2 : 1));
+  const int nchunks = K / gemm_kc(wtype);
   int splits = gemm_splits(wtype, M, N, K);
   while (splits > 1 && (size_t)splits * M * N > part_cap) --splits;
   const int cps = (nchunks + splits - 1) / splits;
@@ -659,7 +736,8 @@ int gemm_launch_splits(int wtype, int M, int N, int K, size_t part_cap) {
 }
 
 hipError_t launch_gemm(int wtype, GemmArgs a, size_t part_cap, hipStream_t s) {
-  const int kc = kRowChunk / (wtype == W_BF16 ? 2 : 1);
+  const int kc = gemm_kc(wtype);
+  if (wtype == W_INT4 && !a.scale) return hipErrorInvalidValue;
   if (a.M < 1 || a.M > kPrefillRows || a.K < kc || a.K % kc || a.N < 1) return hipErrorInvalidValue;
   if (a.defer && (size_t)a.M * a.N > part_cap) return hipErrorInvalidValue;
   const int mt = gemm_mt(wtype, a.M);
@@ -670,6 +748,7 @@ hipError_t launch_gemm(int wtype, GemmArgs a, size_t part_cap, hipStream_t s) {
   const dim3 grid(gx, gy, a.splits);
   hipError_t e = gemm_dispatch(wtype, a, mt, grid, s);
   if (e != hipSuccess || a.splits == 1 || a.defer) return e;
+  if (wtype == W_INT4) a.scale = nullptr;  // the partials carry the group scales
   const size_t total = (size_t)a.M * a.N;
   size_t blocks = (total + kBlock - 1) / kBlock;
   if (blocks > 4096) blocks = 4096;

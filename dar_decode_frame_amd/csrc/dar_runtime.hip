@@ -73,9 +73,17 @@ struct Layout {
 
 // the kernels' weight type of a dar_wtype (callers have validated it)
 int wtype_of(int32_t wtype) {
-  return wtype == DAR_WTYPE_FP8_E4M3_ROW ? W_FP8 : (wtype == DAR_WTYPE_INT8_ROW ? W_INT8 : W_BF16);
+  switch (wtype) {
+    case DAR_WTYPE_FP8_E4M3_ROW: return W_FP8;
+    case DAR_WTYPE_INT8_ROW: return W_INT8;
+    case DAR_WTYPE_INT4_G128: return W_INT4;
+    default: return W_BF16;
+  }
 }
-bool has_row_scales(int32_t wtype) { return wtype == DAR_WTYPE_FP8_E4M3_ROW || wtype == DAR_WTYPE_INT8_ROW; }
+// quantised Linear matrices, which come with fp32 scales (per row, or per row and 128 columns)
+bool has_scales(int32_t wtype) {
+  return wtype == DAR_WTYPE_FP8_E4M3_ROW || wtype == DAR_WTYPE_INT8_ROW || wtype == DAR_WTYPE_INT4_G128;
+}
 
 Layout make_layout(const dar_config* c) {
   Layout L{};
@@ -189,8 +197,7 @@ int validate_config(const dar_config* c, std::string& why) {
   if (!(c->rope_base > 1.0) || !std::isfinite(c->rope_base)) return bad("rope_base must be > 1");
   if (c->max_len < 2) return bad("max_len must be >= 2");
   if (c->max_batch < 1) return bad("max_batch must be >= 1");
-  if (c->wtype != DAR_WTYPE_BF16 && c->wtype != DAR_WTYPE_FP8_E4M3_ROW && c->wtype != DAR_WTYPE_INT8_ROW)
-    return bad("unknown wtype");
+  if (c->wtype != DAR_WTYPE_BF16 && !has_scales(c->wtype)) return bad("unknown wtype");
   const int g = c->n_heads_q / c->n_heads_kv;
   auto unsup = [&](const char* msg) {
     why = msg;
@@ -225,7 +232,7 @@ int check_layer(const dar_layer_weights& w, bool scaled, std::string& why, const
     for (const float* p : s) {
       if (!p) {
         char buf[128];
-        snprintf(buf, sizeof buf, "%s layer %d: row scale pointer is NULL (fp8 / int8 weights)", which, idx);
+        snprintf(buf, sizeof buf, "%s layer %d: scale pointer is NULL (quantised weights)", which, idx);
         why = buf;
         return DAR_E_INVAL;
       }
@@ -261,7 +268,7 @@ struct Chain {
 struct dar_ctx {
   dar_config cfg{};
   Layout L{};
-  bool quant = false;      // one-byte weights with fp32 row scales (fp8 or int8)
+  bool quant = false;      // quantised weights with fp32 scales (fp8, int8: per row; int4: per 128 columns)
   int wq = W_BF16;         // the kernels' weight type of the Linear matrices
   std::vector<dar_layer_weights> slow, fast;
   std::vector<const uint16_t*> fast_emb;
@@ -1111,7 +1118,7 @@ int dar_create(const dar_config* cfg, const dar_weights* w, void* workspace, siz
     g_create_error = "workspace smaller than dar_workspace_bytes()";
     return DAR_E_WORKSPACE;
   }
-  const bool scaled = has_row_scales(cfg->wtype);
+  const bool scaled = has_scales(cfg->wtype);
   if (!w->w0 || !aligned16(w->w0) || !w->slow || !w->slow_final_norm) {
     g_create_error = "w0, slow layers or slow_final_norm missing or misaligned";
     return DAR_E_INVAL;
@@ -1427,15 +1434,23 @@ int dar_bytes_per_frame(const dar_config* cfg, int32_t T, double* bytes_out) {
   const double mats = qkv * d + d * qw + 3.0 * F * d;
   const double rows = qkv + d + 2.0 * F + d;
   const double norms = 2.0 * d;
-  const bool fp8 = has_row_scales(cfg->wtype);  // one byte per weight + fp32 row scales (fp8, int8)
+  // bytes of a Linear matrix of r rows and e entries: bf16; one byte per
+  // weight + an fp32 scale per row (fp8, int8); half a byte per weight + an
+  // fp32 scale per 128 entries (int4)
+  const int wt = wtype_of(cfg->wtype);
+  auto mat = [&](double r, double e) {
+    switch (wt) {
+      case W_BF16: return 2.0 * e;
+      case W_INT4: return 0.5 * e + 4.0 * e / 128.0;
+      default: return e + 4.0 * r;
+    }
+  };
   const double Ls = cfg->n_layers_slow, Lf = cfg->n_layers_fast;
-  double slow = (fp8 ? Ls * mats + 4.0 * Ls * rows : 2.0 * Ls * mats) + 2.0 * (Ls * norms + d) +
-                2.0 * cfg->vocab_c0 * d;
+  double slow = Ls * mat(rows, mats) + 2.0 * (Ls * norms + d) + 2.0 * cfg->vocab_c0 * d;
   double fast = 0.0, fast_kv = 0.0;
   if (cfg->n_res > 0) {
     const double head = (double)cfg->vocab_res * d;
-    fast = (fp8 ? Lf * mats + head + 4.0 * (Lf * rows + cfg->vocab_res) : 2.0 * (Lf * mats + head)) +
-           2.0 * (Lf * norms + d);
+    fast = Lf * mat(rows, mats) + mat(cfg->vocab_res, head) + 2.0 * (Lf * norms + d);
     double positions = 0;
     for (int k = 1; k <= cfg->n_res; ++k) positions += k + 1;
     fast_kv = positions * Lf * 2.0 * kvw * 2.0;
@@ -1456,6 +1471,14 @@ int dar_quantize_fp8_rows(const void* w, int32_t rows, int32_t cols, void* q, fl
 int dar_quantize_int8_rows(const void* w, int32_t rows, int32_t cols, void* q, float* scale, void* stream) {
   if (!w || !q || !scale || rows < 1 || cols < 16 || cols % 16) return DAR_E_INVAL;
   hipError_t e = launch_quantize_int8(static_cast<const uint16_t*>(w), rows, cols, static_cast<int8_t*>(q), scale,
+                                      static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(nullptr, e, "quantize");
+  return DAR_OK;
+}
+
+int dar_quantize_int4_groups(const void* w, int32_t rows, int32_t cols, void* q, float* scale, void* stream) {
+  if (!w || !q || !scale || rows < 1 || cols < 128 || cols % 128) return DAR_E_INVAL;
+  hipError_t e = launch_quantize_int4(static_cast<const uint16_t*>(w), rows, cols, static_cast<uint8_t*>(q), scale,
                                       static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(nullptr, e, "quantize");
   return DAR_OK;
@@ -1488,15 +1511,15 @@ int dar_op_gemv(int32_t wtype, const void* W, const float* scale, int32_t rows, 
                 int32_t M, float* y, void* stream) {
   if (!W || !x || !y || rows < 1 || cols < 256 || cols % 256 || cols > 16384 || (M != 1 && M != 2))
     return DAR_E_INVAL;
-  if (wtype != DAR_WTYPE_BF16 && !has_row_scales(wtype)) return DAR_E_INVAL;
-  if (has_row_scales(wtype) && !scale) return DAR_E_INVAL;
+  if (wtype != DAR_WTYPE_BF16 && !has_scales(wtype)) return DAR_E_INVAL;
+  if (has_scales(wtype) && !scale) return DAR_E_INVAL;
   if (!aligned16(W) || !aligned16(x)) return DAR_E_INVAL;
   Task t = none_task();
   t.kind = T_GEMV;
   t.M = M;
   GemvArgs& a = t.gemv;
   a.W = W;
-  a.scale = has_row_scales(wtype) ? scale : nullptr;
+  a.scale = has_scales(wtype) ? scale : nullptr;
   a.rows = rows;
   a.K = cols;
   a.M = M;
@@ -1513,8 +1536,8 @@ int dar_op_gemv(int32_t wtype, const void* W, const float* scale, int32_t rows, 
 int dar_op_gemm(int32_t wtype, const void* W, const float* scale, int32_t N, int32_t K, const float* x,
                 int32_t M, float* y, void* stream) {
   if (!W || !x || !y || N < 1 || K < 256 || K % 256 || K > 16384 || M < 1 || M > kPrefillRows) return DAR_E_INVAL;
-  if (wtype != DAR_WTYPE_BF16 && !has_row_scales(wtype)) return DAR_E_INVAL;
-  if (has_row_scales(wtype) && !scale) return DAR_E_INVAL;
+  if (wtype != DAR_WTYPE_BF16 && !has_scales(wtype)) return DAR_E_INVAL;
+  if (has_scales(wtype) && !scale) return DAR_E_INVAL;
   if (!aligned16(W) || !aligned16(x)) return DAR_E_INVAL;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int mpad = gemm_mpad(M);
@@ -1528,7 +1551,7 @@ int dar_op_gemm(int32_t wtype, const void* W, const float* scale, int32_t N, int
   uint16_t* xl = reinterpret_cast<uint16_t*>(scratch + half_bytes);
   GemmArgs a{};
   a.W = W;
-  a.scale = has_row_scales(wtype) ? scale : nullptr;
+  a.scale = has_scales(wtype) ? scale : nullptr;
   a.N = N;
   a.K = K;
   a.M = M;

@@ -24,7 +24,8 @@ DAR_E_UNSUPPORTED = -6
 DAR_WTYPE_BF16 = 0
 DAR_WTYPE_FP8_E4M3_ROW = 1
 DAR_WTYPE_INT8_ROW = 2
-WTYPES = {"bf16": 0, "fp8": DAR_WTYPE_FP8_E4M3_ROW, "int8": DAR_WTYPE_INT8_ROW}
+DAR_WTYPE_INT4_G128 = 3
+WTYPES = {"bf16": 0, "fp8": DAR_WTYPE_FP8_E4M3_ROW, "int8": DAR_WTYPE_INT8_ROW, "int4": DAR_WTYPE_INT4_G128}
 KIND_NAMES = {0: "qkv", 1: "attention", 2: "wo", 3: "w13", 4: "w2", 5: "head", 6: "other"}
 
 
@@ -101,6 +102,7 @@ _SIGS = {
     "dar_bytes_per_frame": ([ctypes.POINTER(dar_config), _I32, ctypes.POINTER(ctypes.c_double)], ctypes.c_int),
     "dar_quantize_fp8_rows": ([_VP, _I32, _I32, _VP, _VP, _VP], ctypes.c_int),
     "dar_quantize_int8_rows": ([_VP, _I32, _I32, _VP, _VP, _VP], ctypes.c_int),
+    "dar_quantize_int4_groups": ([_VP, _I32, _I32, _VP, _VP, _VP], ctypes.c_int),
     "dar_status_string": ([ctypes.c_int], ctypes.c_char_p),
     "dar_last_error": ([_VP], ctypes.c_char_p),
     "dar_op_gemv": ([_I32, _VP, _VP, _I32, _I32, _VP, _I32, _VP, _VP], ctypes.c_int),
@@ -229,6 +231,11 @@ def dar_quantize_fp8_rows(w_ptr, rows, cols, q_ptr, scale_ptr, stream_ptr):
 
 def dar_quantize_int8_rows(w_ptr, rows, cols, q_ptr, scale_ptr, stream_ptr):
     return _check(lib.dar_quantize_int8_rows(w_ptr, rows, cols, q_ptr, scale_ptr, stream_ptr), "dar_quantize_int8_rows")
+
+
+def dar_quantize_int4_groups(w_ptr, rows, cols, q_ptr, scale_ptr, stream_ptr):
+    return _check(lib.dar_quantize_int4_groups(w_ptr, rows, cols, q_ptr, scale_ptr, stream_ptr),
+                  "dar_quantize_int4_groups")
 
 
 def dar_status_string(status):

@@ -1,8 +1,9 @@
 """A decode session over the C ABI, with torch providing device memory and the stream.
 
 DeviceWeights uploads canonical bf16 weights (uint16 bit arrays) and, for the
-fp8 and int8 modes, quantises every Linear matrix on the device with
-dar_quantize_fp8_rows / dar_quantize_int8_rows. DarSession owns the workspace and the dar_ctx and wraps
+fp8, int8 and int4 modes, quantises every Linear matrix on the device with
+dar_quantize_fp8_rows / dar_quantize_int8_rows / dar_quantize_int4_groups.
+DarSession owns the workspace and the dar_ctx and wraps
 prefill / decode_frame with torch tensors. Everything here is marshalling:
 pointers, sizes and buffers; the arithmetic runs in libdar.so.
 """
@@ -23,7 +24,9 @@ def _dev(t):
 
 
 class DeviceWeights:
-    """Device copies of the canonical tensors; fp8 / int8 modes add codes and row scales."""
+    """Device copies of the canonical tensors; quantised modes replace each Linear
+    matrix by its codes (fp8, int8: [rows][cols]; int4: packed [rows][cols/2])
+    and add its scales (fp8, int8: [rows]; int4: [rows][cols/128])."""
 
     def __init__(self, dims, host_tensors: dict, wtype: str = "bf16", device="cuda", stream=None,
                  keep_bf16_linears: bool = False):
@@ -36,11 +39,16 @@ class DeviceWeights:
         for name, bits in host_tensors.items():
             arr = np.ascontiguousarray(bits).view(np.int16)
             dev = torch.from_numpy(arr).to(device, non_blocking=False)
-            if wtype in ("fp8", "int8") and self.is_linear(name):
+            if wtype in ("fp8", "int8", "int4") and self.is_linear(name):
                 rows, cols = dev.shape
-                q = torch.empty((rows, cols), dtype=torch.uint8 if wtype == "fp8" else torch.int8, device=device)
-                sc = torch.empty((rows,), dtype=torch.float32, device=device)
-                quantize = N.dar_quantize_fp8_rows if wtype == "fp8" else N.dar_quantize_int8_rows
+                if wtype == "int4":
+                    q = torch.empty((rows, cols // 2), dtype=torch.uint8, device=device)
+                    sc = torch.empty((rows, cols // 128), dtype=torch.float32, device=device)
+                    quantize = N.dar_quantize_int4_groups
+                else:
+                    q = torch.empty((rows, cols), dtype=torch.uint8 if wtype == "fp8" else torch.int8, device=device)
+                    sc = torch.empty((rows,), dtype=torch.float32, device=device)
+                    quantize = N.dar_quantize_fp8_rows if wtype == "fp8" else N.dar_quantize_int8_rows
                 with torch.cuda.stream(s):
                     quantize(_dev(dev), rows, cols, _dev(q), _dev(sc), sp)
                 self.t[name] = q

@@ -53,9 +53,14 @@ typedef enum {
 typedef enum {
   DAR_WTYPE_BF16 = 0,           /* every matrix bf16 [rows][cols], row-major                  */
   DAR_WTYPE_FP8_E4M3_ROW = 1,   /* Linear matrices e4m3fn [rows][cols] + fp32 scale [rows]   */
-  DAR_WTYPE_INT8_ROW = 2        /* Linear matrices int8 [rows][cols] + fp32 scale [rows]:
+  DAR_WTYPE_INT8_ROW = 2,       /* Linear matrices int8 [rows][cols] + fp32 scale [rows]:
                                    weight-only int8 (the tuna-fish README's int8wo mode),
                                    y_r = scale[r] * sum_j q[r][j] x[j]                       */
+  DAR_WTYPE_INT4_G128 = 3       /* Linear matrices int4, two per byte [rows][cols/2] (column
+                                   2i in the low nibble of byte i, two's complement), + fp32
+                                   scale [rows][cols/128]: weight-only int4 (the tuna-fish
+                                   README's int4wo mode), y_r = sum_g scale[r][g] *
+                                   sum_{j in group g} q[r][j] x[j]                           */
 } dar_wtype;
 
 /* Model geometry and capacity. Checked by dar_workspace_bytes / dar_create.
@@ -92,9 +97,9 @@ typedef struct {
  *          then k rows, then v rows
  *   wo   : [d_model][n_heads_q*head_dim]
  *   w1, w3 : [ffn_dim][d_model] (gate and up); w2 : [d_model][ffn_dim]
- *   *_scale : fp32 [rows] per-row scales; required for DAR_WTYPE_FP8_E4M3_ROW
- *             and DAR_WTYPE_INT8_ROW,
- *             ignored (may be NULL) for bf16. */
+ *   *_scale : fp32 [rows] per-row scales, required for DAR_WTYPE_FP8_E4M3_ROW
+ *             and DAR_WTYPE_INT8_ROW; fp32 [rows][cols/128] group scales,
+ *             required for DAR_WTYPE_INT4_G128; ignored (may be NULL) for bf16. */
 typedef struct {
   const void* attn_norm;
   const void* wqkv;
@@ -117,7 +122,7 @@ typedef struct {
  *   slow_final_norm, fast_final_norm : bf16 [d_model]
  *   fast_emb[k] : bf16 table for codebook k feeding fast step k+1;
  *                 [vocab_c0][d] for k = 0, [vocab_res][d] for k >= 1
- *   fast_head : [vocab_res][d_model] (+ fp32 scale [vocab_res] in fp8 / int8 mode)
+ *   fast_head : [vocab_res][d_model] (+ fp32 scales as for a layer matrix when quantised)
  * Fast members are ignored when n_res == 0. */
 typedef struct {
   const void* w0;
@@ -199,8 +204,9 @@ int dar_nonfinite(dar_ctx* ctx, int32_t* count_out);
 
 /* Algorithmic bytes of one decode frame that attends over T slow positions:
  * every weight and norm the frame reads (the fast AR once per residual
- * codebook), fp8 row scales, the codebook-0 head, T slow KV positions and the
- * fast AR's per-frame KV reads (tuna-fish README, "Inference estimation"). */
+ * codebook), the scales of quantised weights, the codebook-0 head, T slow KV
+ * positions and the fast AR's per-frame KV reads (tuna-fish README,
+ * "Inference estimation"). */
 int dar_bytes_per_frame(const dar_config* cfg, int32_t T, double* bytes_out);
 
 /* Per-row symmetric e4m3fn quantisation on the device (s2-pro-fp8 model card,
@@ -221,23 +227,36 @@ int dar_quantize_fp8_rows(const void* w, int32_t rows, int32_t cols, void* q, fl
 int dar_quantize_int8_rows(const void* w, int32_t rows, int32_t cols, void* q, float* scale,
                            void* stream);
 
+/* Group-wise symmetric int4 quantisation on the device, for
+ * DAR_WTYPE_INT4_G128. The pages name torchao's int4 weight-only mode but give
+ * no formula; the reading taken: groups of 128 consecutive columns of a row,
+ * scale[r][g] = max |w| over the group / 7 in fp32, q = round-half-to-even(w /
+ * scale) (fp32 division) clamped to [-7, 7]; an all-zero group gives scale 0
+ * and codes 0. Codes are packed two per byte, column 2i in the low nibble of
+ * byte i. w: device bf16 [rows][cols]; q: device uint8 [rows][cols/2]; scale:
+ * device fp32 [rows][cols/128]. cols % 128 == 0. Stream-ordered. */
+int dar_quantize_int4_groups(const void* w, int32_t rows, int32_t cols, void* q, float* scale,
+                             void* stream);
+
 const char* dar_status_string(int status);
 const char* dar_last_error(const dar_ctx* ctx);   /* ctx may be NULL: last create error */
 
 /* ---- diagnostics: single operations of the frame, for tests and timing --- */
 
-/* y[m][r] = sum_j W[r][j] * x[m][j] (times scale[r] with fp8 / int8 weights) for m < M,
- * r < rows: the frame's weight-streaming GEMV kernel with no prologue or
- * epilogue. W device [rows][cols] bf16, e4m3fn or int8 (wtype), scale fp32 [rows]
- * or NULL for bf16, x device fp32 [M][cols], y device fp32 [M][rows].
+/* y[m][r] = sum_j W[r][j] * x[m][j] (times scale[r] with fp8 / int8 weights,
+ * scale[r][j/128] inside the sum with int4) for m < M, r < rows: the frame's
+ * weight-streaming GEMV kernel with no prologue or epilogue. W device
+ * [rows][cols] bf16, e4m3fn or int8, or [rows][cols/2] packed int4 (wtype),
+ * scale fp32 [rows] ([rows][cols/128] for int4) or NULL for bf16, x device fp32 [M][cols], y device fp32 [M][rows].
  * M in {1, 2}; cols % 256 == 0 and cols <= 16384. */
 int dar_op_gemv(int32_t wtype, const void* W, const float* scale, int32_t rows, int32_t cols,
                 const float* x, int32_t M, float* y, void* stream);
 
-/* y[m][n] = sum_k x[m][k] * W[n][k] (times scale[n] with fp8 / int8 weights) for m < M,
- * n < N: the prefill's MFMA GEMM, which splits the fp32 inputs into two bf16
- * parts (hi + lo) and multiplies both. W device [N][K] bf16, e4m3fn or int8 (wtype),
- * scale fp32 [N] or NULL for bf16, x device fp32 [M][K], y device fp32 [M][N].
+/* y[m][n] = sum_k x[m][k] * W[n][k] (times scale[n] with fp8 / int8 weights,
+ * scale[n][k/128] inside the sum with int4) for m < M, n < N: the prefill's
+ * MFMA GEMM, which splits the fp32 inputs into two bf16 parts (hi + lo) and
+ * multiplies both. W device [N][K] bf16, e4m3fn or int8, or [N][K/2] packed
+ * int4 (wtype), scale fp32 [N] ([N][K/128] for int4) or NULL for bf16, x device fp32 [M][K], y device fp32 [M][N].
  * 1 <= M <= 128; K % 256 == 0 and K <= 16384; N >= 1. Uses its own scratch
  * (allocated per call) and synchronises the stream. */
 int dar_op_gemm(int32_t wtype, const void* W, const float* scale, int32_t N, int32_t K, const float* x,

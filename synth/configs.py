@@ -70,7 +70,7 @@ class Workload:
 
     name: str
     dims: DarDims
-    wtype: str              # "bf16", "fp8" or "int8"
+    wtype: str              # "bf16", "fp8", "int8" or "int4"
     batch: int
     prefill_len: int        # per sequence (batch 1) or the minimum (ragged)
     prefill_len_max: int    # == prefill_len unless ragged
@@ -98,6 +98,7 @@ WORKLOADS = {
     "tiny_bf16": Workload("tiny_bf16", TINY, "bf16", 1, 16, 16, 16, 32),
     "tiny_fp8": Workload("tiny_fp8", TINY, "fp8", 1, 16, 16, 16, 32),
     "tiny_int8": Workload("tiny_int8", TINY, "int8", 1, 16, 16, 16, 32),
+    "tiny_int4": Workload("tiny_int4", TINY, "int4", 1, 16, 16, 16, 32),
     # slow AR only, full shape: prefill 128 then 896 tokens to length 1024
     "s2pro_slow_bf16": Workload("s2pro_slow_bf16", S2_SLOW_ONLY, "bf16", 1, 128, 128, 896, 1024),
     # full Dual-AR frame, full shape, bf16 and per-row fp8
@@ -105,6 +106,8 @@ WORKLOADS = {
     "s2pro_dual_fp8": Workload("s2pro_dual_fp8", S2_DUAL, "fp8", 1, 128, 128, 896, 1024),
     # the same frame with per-row int8 weight-only matrices (the tuna-fish README's int8wo mode)
     "s2pro_dual_int8": Workload("s2pro_dual_int8", S2_DUAL, "int8", 1, 128, 128, 896, 1024),
+    # and with int4 weight-only matrices, a scale per 128 columns (its int4wo mode)
+    "s2pro_dual_int4": Workload("s2pro_dual_int4", S2_DUAL, "int4", 1, 128, 128, 896, 1024),
     # batched Dual-AR decode, ragged prompts 128..512, max length 4096
     "s2pro_dual_b16": Workload("s2pro_dual_b16", S2_DUAL, "bf16", 16, 128, 512, 3584, 4096),
     "s2pro_dual_b64": Workload("s2pro_dual_b64", S2_DUAL, "bf16", 64, 128, 512, 3584, 4096),

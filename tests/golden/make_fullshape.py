@@ -30,7 +30,7 @@ sys.path.insert(0, ROOT)
 import synth  # noqa: E402
 from oracle import OracleDecoder, OracleModel  # noqa: E402
 
-WORKLOADS = ["s2pro_slow_bf16", "s2pro_dual_bf16", "s2pro_dual_fp8", "s2pro_dual_int8"]
+WORKLOADS = ["s2pro_slow_bf16", "s2pro_dual_bf16", "s2pro_dual_fp8", "s2pro_dual_int8", "s2pro_dual_int4"]
 EARLY_FRAMES = 9
 LATE_LAST_POS = 1007          # slow position of the late frame
 SAMPLES = 64

@@ -2,9 +2,9 @@
 
 The bar for floating point: per (frame, codebook) logit vector the relative L2
 error ||l_gpu - l_oracle|| / ||l_oracle|| (max over vectors) stays within the
-tolerance of the weight type (2e-2 bf16, 5e-2 fp8, 2e-2 int8: the int8 codes
-are exact in fp32 and bf16 like bf16 weights, and both sides apply the same
-row scale, so the bf16 bar applies); argmax agreement over all
+tolerance of the weight type (2e-2 bf16, 5e-2 fp8, 2e-2 int8 and int4: the
+integer codes are exact in fp32 and bf16 like bf16 weights, and both sides
+apply the same row or group scales, so the bf16 bar applies); argmax agreement over all
 (frame, codebook) comparisons is at least 99 %; and where the oracle's top-1
 minus top-2 margin exceeds 1e-2 the codes are identical.
 """
@@ -12,7 +12,7 @@ from __future__ import annotations
 
 import numpy as np
 
-TOL = {"bf16": 2e-2, "fp8": 5e-2, "int8": 2e-2}
+TOL = {"bf16": 2e-2, "fp8": 5e-2, "int8": 2e-2, "int4": 2e-2}
 
 
 def margin(logits):

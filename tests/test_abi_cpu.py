@@ -35,8 +35,9 @@ def test_workspace_bytes_cover_kv(N, dname, max_len):
     assert n >= kv and n < kv + 160 * 2 ** 20
 
 
-@pytest.mark.parametrize("dname,wtype", [("tiny", "bf16"), ("tiny", "fp8"), ("tiny", "int8"), ("s2pro_slow", "bf16"),
-                                         ("s2pro_dual", "bf16"), ("s2pro_dual", "fp8"), ("s2pro_dual", "int8")])
+@pytest.mark.parametrize("dname,wtype", [("tiny", "bf16"), ("tiny", "fp8"), ("tiny", "int8"), ("tiny", "int4"),
+                                         ("s2pro_slow", "bf16"), ("s2pro_dual", "bf16"), ("s2pro_dual", "fp8"),
+                                         ("s2pro_dual", "int8"), ("s2pro_dual", "int4")])
 @pytest.mark.parametrize("T", [0, 1, 129, 1024])
 def test_bytes_per_frame_matches_host_model(N, dname, wtype, T):
     d = DIMS[dname]
@@ -98,16 +99,21 @@ def test_null_context_and_ops_reject(N):
     assert N.lib.dar_op_gemv(0, None, None, 4, 256, None, 1, None, None) == N.DAR_E_INVAL
     assert N.lib.dar_op_gemv(0, ctypes.c_void_p(4096), None, 4, 300, ctypes.c_void_p(4096), 1,
                              ctypes.c_void_p(4096), None) == N.DAR_E_INVAL
-    for wq in (1, 2):  # fp8 and int8 weights need their row scales
+    for wq in (1, 2, 3):  # fp8, int8 and int4 weights need their scales
         assert N.lib.dar_op_gemv(wq, ctypes.c_void_p(4096), None, 4, 256, ctypes.c_void_p(4096), 1,
                                  ctypes.c_void_p(4096), None) == N.DAR_E_INVAL
-    assert N.lib.dar_op_gemv(3, ctypes.c_void_p(4096), ctypes.c_void_p(4096), 4, 256, ctypes.c_void_p(4096), 1,
+        assert N.lib.dar_op_gemm(wq, ctypes.c_void_p(4096), None, 4, 256, ctypes.c_void_p(4096), 1,
+                                 ctypes.c_void_p(4096), None) == N.DAR_E_INVAL
+    assert N.lib.dar_op_gemv(4, ctypes.c_void_p(4096), ctypes.c_void_p(4096), 4, 256, ctypes.c_void_p(4096), 1,
                              ctypes.c_void_p(4096), None) == N.DAR_E_INVAL
     assert N.lib.dar_op_attention(None, None, None, 4, 2, 64, 16, 0, 1, 0, None, None) == N.DAR_E_INVAL
     assert N.lib.dar_quantize_fp8_rows(ctypes.c_void_p(4096), 4, 24, ctypes.c_void_p(4096),
                                        ctypes.c_void_p(4096), None) == N.DAR_E_INVAL
     assert N.lib.dar_quantize_int8_rows(ctypes.c_void_p(4096), 4, 24, ctypes.c_void_p(4096),
                                         ctypes.c_void_p(4096), None) == N.DAR_E_INVAL
+    for cols in (64, 200):  # int4 groups are 128 columns
+        assert N.lib.dar_quantize_int4_groups(ctypes.c_void_p(4096), 4, cols, ctypes.c_void_p(4096),
+                                              ctypes.c_void_p(4096), None) == N.DAR_E_INVAL
 
 
 def test_status_strings(N):

@@ -3,8 +3,9 @@
 Tiny Dual-AR (2 slow layers, 1 fast layer, d 256): each sequence of the batch
 is teacher-forced with its own oracle greedy frames and compared with its own
 oracle run (logits rel-L2, argmax agreement, exact codes above the margin),
-bf16, fp8 and int8 at B = 4, at the largest batch (64, whose first fast pass is
-a 128-row GEMM) and with prompts long enough for several attention splits. At full shape (36 + 4 layers, d 2560): a batch of two equals
+bf16, fp8, int8 and int4 at B = 4, at the largest batch (64, whose first fast
+pass is a 128-row GEMM; bf16 and int4) and with prompts long enough for several
+attention splits. At full shape (36 + 4 layers, d 2560): a batch of two equals
 two batch-1 contexts decoding the same prompts (same codes where the margin
 exceeds 1e-2, logits within the bf16 tolerance).
 """
@@ -36,7 +37,7 @@ def _oracle_frames(model, prompt, frames, max_len):
 # sequence crossing a split boundary while the frames are decoded
 @pytest.mark.parametrize("wtype,B,frames,max_len,lmax",
                          [("bf16", 4, 20, 48, 24), ("fp8", 4, 20, 48, 24), ("int8", 4, 20, 48, 24),
-                          ("bf16", 64, 2, 48, 24),
+                          ("int4", 4, 20, 48, 24), ("bf16", 64, 2, 48, 24), ("int4", 64, 2, 48, 24),
                           ("bf16", 3, 24, 200, 130)])
 def test_tiny_batched_parity(tiny_host, wtype, B, frames, max_len, lmax):
     from dar_decode_frame_amd.session import DarSession, DeviceWeights

@@ -54,7 +54,7 @@ def _random_frames(dims, n, seed):
             for _ in range(n)]
 
 
-@pytest.mark.parametrize("wtype", ["bf16", "fp8", "int8"])
+@pytest.mark.parametrize("wtype", ["bf16", "fp8", "int8", "int4"])
 @pytest.mark.parametrize("forcing", ["oracle", "random"])
 def test_tiny_teacher_forced_parity(tiny_host, wtype, forcing):
     # 60 frames instead of the workload's 16: the agreement rate is a
@@ -84,7 +84,8 @@ def test_tiny_teacher_forced_parity(tiny_host, wtype, forcing):
     sess.close()
 
 
-@pytest.mark.parametrize("wtype,n_prompt", [("bf16", 1), ("bf16", 128), ("bf16", 200), ("fp8", 200), ("int8", 200)])
+@pytest.mark.parametrize("wtype,n_prompt", [("bf16", 1), ("bf16", 128), ("bf16", 200), ("fp8", 200), ("int8", 200),
+                                                   ("int4", 200)])
 def test_tiny_prefill_blocks_parity(tiny_host, wtype, n_prompt):
     """Prompts of one position, exactly one prefill block, and two blocks (the
     second ragged), teacher-forced with the oracle's own frames."""
@@ -148,16 +149,19 @@ def test_reset_and_second_prefill_reproduce(tiny_host):
     sess.close()
 
 
-@pytest.mark.parametrize("wtype", ["fp8", "int8"])
+@pytest.mark.parametrize("wtype", ["fp8", "int8", "int4"])
 def test_device_quantiser_matches_oracle(tiny_host, wtype):
     dims, host = tiny_host
     from dar_decode_frame_amd.session import DeviceWeights
+    from oracle.int4 import pack_int4
     dw = DeviceWeights(dims, host, wtype)
     m = OracleModel(dims, host, wtype=wtype)
     names = synth.linear_names(dims)
     assert len(m.quant) == len(names)
     for name in names:
         codes, scale = m.quant[name]
+        if wtype == "int4":
+            codes = pack_int4(codes)
         assert np.array_equal(dw.t[name].cpu().numpy(), codes), name
         assert np.array_equal(dw.scale[name].cpu().numpy(), scale), name
 

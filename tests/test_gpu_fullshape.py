@@ -1,5 +1,5 @@
 """Parity at the benchmark's full shapes (36 + 4 layers, d 2560, 32/8 heads of
-128, SwiGLU 9728, 4096-entry codebooks; slow AR alone, bf16, fp8 and int8 frames)
+128, SwiGLU 9728, 4096-entry codebooks; slow AR alone, bf16, fp8, int8 and int4 frames)
 against CPU oracle references written by tests/golden/make_fullshape.py, in
 the launch configuration bench.py times (two streams, eager launches).
 
@@ -25,7 +25,7 @@ from parity import TOL
 pytestmark = pytest.mark.gpu
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-WORKLOADS = ["s2pro_slow_bf16", "s2pro_dual_bf16", "s2pro_dual_fp8", "s2pro_dual_int8"]
+WORKLOADS = ["s2pro_slow_bf16", "s2pro_dual_bf16", "s2pro_dual_fp8", "s2pro_dual_int8", "s2pro_dual_int4"]
 
 
 def _golden(name):

@@ -1,6 +1,6 @@
 """Per-kernel parity of the HIP library against the oracle, through the C ABI.
 
-Bars: fp8 decode and the fp8 and int8 quantisers are integer/byte work, so bit-exact;
+Bars: fp8 decode and the fp8, int8 and int4 quantisers are integer/byte work, so bit-exact;
 GEMV and attention are fp32 accumulations checked against the oracle in fp64
 on the same bf16 / fp8 inputs, within a bound derived from fp32 summation
 (|error| <= 1e-5 * sum_j |w_j x_j|, and 2e-5 relative for attention).
@@ -12,19 +12,25 @@ import pytest
 
 import synth
 from oracle import e4m3_decode, e4m3_decode_table, gqa_attention, quantize_rows
+from oracle.int4 import dequantize_int4, pack_int4, quantize_int4_groups
 from oracle.int8 import quantize_int8_rows
 from oracle.model import bf16_to_f32
 
-WT_CODES = {"bf16": 0, "fp8": 1, "int8": 2}
+WT_CODES = {"bf16": 0, "fp8": 1, "int8": 2, "int4": 3}
+QTYPES = ["bf16", "fp8", "int8", "int4"]
 
 
 def _quantised(wtype, w32):
-    """(device codes array, fp32 row scales, the codes' fp64 values) of the oracle's quantiser."""
+    """(device codes array, fp32 scales, fp64 weights before the row scale, fp64
+    row scale) of the oracle's quantiser; int4's group scales are inside the weights."""
     if wtype == "fp8":
         codes, scale = quantize_rows(w32)
-        return codes, scale, e4m3_decode(codes).astype(np.float64)
+        return codes, scale, e4m3_decode(codes).astype(np.float64), scale.astype(np.float64)
+    if wtype == "int4":
+        codes, scale = quantize_int4_groups(w32)
+        return pack_int4(codes), scale, dequantize_int4(codes, scale), np.ones(w32.shape[0])
     codes, scale = quantize_int8_rows(w32)
-    return codes, scale, codes.astype(np.float64)
+    return codes, scale, codes.astype(np.float64), scale.astype(np.float64)
 
 pytestmark = pytest.mark.gpu
 
@@ -97,11 +103,29 @@ def test_int8_quantizer_bit_exact(env, rows, cols):
     assert np.array_equal(q.cpu().numpy(), codes)
 
 
+@pytest.mark.parametrize("rows,cols", [(7, 256), (96, 2560), (33, 9728)])
+def test_int4_quantizer_bit_exact(env, rows, cols):
+    torch, N, dev = env
+    bits = _bf16_matrix(rows, cols, 300 + rows)
+    bits[1] = 0                                   # zero row
+    bits[2, 128:256] = 0                          # one zero group
+    bits[2, 5] = 0x8000                           # negative zero
+    bits[3, 9] = synth.f32_to_bf16_bits(np.float32([0.9]))[0]   # outlier
+    w = torch.from_numpy(bits.view(np.int16)).to(dev)
+    q = torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev)
+    s = torch.empty((rows, cols // 128), dtype=torch.float32, device=dev)
+    N.dar_quantize_int4_groups(_p(w), rows, cols, _p(q), _p(s), _sp(torch))
+    torch.cuda.synchronize()
+    codes, scale = quantize_int4_groups(bf16_to_f32(bits))
+    assert np.array_equal(s.cpu().numpy(), scale)
+    assert np.array_equal(q.cpu().numpy(), pack_int4(codes))
+
+
 GEMV_SHAPES = [(512, 256), (300, 768), (6144, 2560), (2560, 4096), (9728, 2560), (2560, 9728), (4096, 2560),
                (33, 3072), (17, 13312)]  # last two: ragged rows over chunk counts split unevenly across waves
 
 
-@pytest.mark.parametrize("wtype", ["bf16", "fp8", "int8"])
+@pytest.mark.parametrize("wtype", QTYPES)
 @pytest.mark.parametrize("M", [1, 2])
 @pytest.mark.parametrize("rows,cols", GEMV_SHAPES)
 def test_gemv_against_fp64(env, wtype, M, rows, cols):
@@ -118,11 +142,10 @@ def test_gemv_against_fp64(env, wtype, M, rows, cols):
         w_ref = w32.astype(np.float64)
         sc = np.ones(rows)
     else:
-        codes, scale, w_ref = _quantised(wtype, w32)
+        codes, scale, w_ref, sc = _quantised(wtype, w32)
         w_dev = torch.from_numpy(codes).to(dev)
         s_dev = torch.from_numpy(scale).to(dev)
         N.dar_op_gemv(WT_CODES[wtype], _p(w_dev), _p(s_dev), rows, cols, _p(xt), M, _p(y), _sp(torch))
-        sc = scale.astype(np.float64)
     torch.cuda.synchronize()
     got = y.cpu().numpy().astype(np.float64)
     want = (x.astype(np.float64) @ w_ref.T) * sc
@@ -136,7 +159,7 @@ GEMM_SHAPES = [(6144, 2560, 128), (2560, 4096, 128), (9728, 2560, 100), (2560, 9
                (17, 256, 1), (129, 512, 64)]
 
 
-@pytest.mark.parametrize("wtype", ["bf16", "fp8", "int8"])
+@pytest.mark.parametrize("wtype", QTYPES)
 @pytest.mark.parametrize("n_out,k_in,M", GEMM_SHAPES)
 def test_gemm_against_fp64(env, wtype, n_out, k_in, M):
     torch, N, dev = env
@@ -152,11 +175,10 @@ def test_gemm_against_fp64(env, wtype, n_out, k_in, M):
         w_ref = w32.astype(np.float64)
         sc = np.ones(n_out)
     else:
-        codes, scale, w_ref = _quantised(wtype, w32)
+        codes, scale, w_ref, sc = _quantised(wtype, w32)
         w_dev = torch.from_numpy(codes).to(dev)
         s_dev = torch.from_numpy(scale).to(dev)
         N.dar_op_gemm(WT_CODES[wtype], _p(w_dev), _p(s_dev), n_out, k_in, _p(xt), M, _p(y), _sp(torch))
-        sc = scale.astype(np.float64)
     got = y.cpu().numpy().astype(np.float64)
     want = (x.astype(np.float64) @ w_ref.T) * sc
     # inputs carried as bf16 hi + lo (relative error <= 2^-16), fp32 accumulation
