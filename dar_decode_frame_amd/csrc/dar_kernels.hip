@@ -105,9 +105,13 @@ __device__ __forceinline__ const float* group_scales(const float* scale, int r, 
 template <typename WT>
 struct Dot;
 
+// Dot<WT>: V, the per-lane load (E weights, 16 bytes unless stated) and load()
+// to fetch it, streaming (nontemporal); run(w, x) = sum_e w_e x[e].
 template <>
 struct Dot<BF16> {
   static constexpr int E = 8;  // elements per 16-byte load
+  using V = u32x4;
+  __device__ static __forceinline__ V load(const char* p) { return ld16_nt(p); }
   __device__ static __forceinline__ float run(u32x4 w, const float* x) {
     const float4 a = *reinterpret_cast<const float4*>(x);
     const float4 b = *reinterpret_cast<const float4*>(x + 4);
@@ -130,6 +134,8 @@ __device__ __forceinline__ f32x2 fp8x2_hi(uint32_t u) { return __builtin_amdgcn_
 template <>
 struct Dot<FP8> {
   static constexpr int E = 16;
+  using V = u32x4;
+  __device__ static __forceinline__ V load(const char* p) { return ld16_nt(p); }
   __device__ static __forceinline__ float word(uint32_t u, const float4 x, float s) {
     const f32x2 lo = fp8x2_lo(u);
     const f32x2 hi = fp8x2_hi(u);
@@ -153,6 +159,8 @@ struct Dot<FP8> {
 template <>
 struct Dot<INT8> {
   static constexpr int E = 16;
+  using V = u32x4;
+  __device__ static __forceinline__ V load(const char* p) { return ld16_nt(p); }
   __device__ static __forceinline__ float word(uint32_t u, const float4 x, float s) {
     const int v = (int)u;
     s = fmaf((float)((v << 24) >> 24), x.x, s);
@@ -171,49 +179,77 @@ struct Dot<INT8> {
   }
 };
 
-// Two's complement int4 codes, eight per word (even column in the low nibble).
+// Two's complement int4 codes, eight per 4-byte load (column 2i in the low
+// nibble of byte i): 64 lanes cover 512 columns, so every width here (a
+// multiple of 512 but for the tiny 256 and 768) fills whole chunks, and a
+// lane's eight columns sit inside one 128-column scale group.
 template <>
 struct Dot<INT4> {
-  static constexpr int E = 32;
-  __device__ static __forceinline__ float word(uint32_t u, const float* x, float s) {
-    const int v = (int)u;
-#pragma unroll
-    for (int n = 0; n < 8; ++n) s = fmaf((float)((v << (28 - 4 * n)) >> 28), x[n], s);
-    return s;
+  static constexpr int E = 8;
+  using V = uint32_t;
+  __device__ static __forceinline__ V load(const char* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
   }
-  __device__ static __forceinline__ float run(u32x4 w, const float* x) {
-    float s0 = word(w.x, x, 0.f);
-    float s1 = word(w.y, x + 8, 0.f);
-    s0 = word(w.z, x + 16, s0);
-    s1 = word(w.w, x + 24, s1);
+  __device__ static __forceinline__ float run(uint32_t w, const float* x) {
+    const float4 a = *reinterpret_cast<const float4*>(x);
+    const float4 b = *reinterpret_cast<const float4*>(x + 4);
+    const int v = (int)w;
+    float s0 = (float)((v << 28) >> 28) * a.x;
+    float s1 = (float)((v << 24) >> 28) * a.y;
+    s0 = fmaf((float)((v << 20) >> 28), a.z, s0);
+    s1 = fmaf((float)((v << 16) >> 28), a.w, s1);
+    s0 = fmaf((float)((v << 12) >> 28), b.x, s0);
+    s1 = fmaf((float)((v << 8) >> 28), b.y, s1);
+    s0 = fmaf((float)((v << 4) >> 28), b.z, s0);
+    s1 = fmaf((float)(v >> 28), b.w, s1);
+    return s0 + s1;
+  }
+  // sum_e (q_e + 8) x[e]: flipping each nibble's top bit turns q into q + 8 in
+  // [0, 15], which converts straight from a byte once the even and odd
+  // columns sit in separate bytes; the caller subtracts 8 sum_e x[e]
+  __device__ static __forceinline__ float run_biased(uint32_t w, const float* x) {
+    const float4 a = *reinterpret_cast<const float4*>(x);
+    const float4 b = *reinterpret_cast<const float4*>(x + 4);
+    const uint32_t u = w ^ 0x88888888u;
+    const uint32_t ev = u & 0x0f0f0f0fu;         // columns 0, 2, 4, 6
+    const uint32_t od = (u >> 4) & 0x0f0f0f0fu;  // columns 1, 3, 5, 7
+    float s0 = (float)(ev & 0xffu) * a.x;
+    float s1 = (float)(od & 0xffu) * a.y;
+    s0 = fmaf((float)((ev >> 8) & 0xffu), a.z, s0);
+    s1 = fmaf((float)((od >> 8) & 0xffu), a.w, s1);
+    s0 = fmaf((float)((ev >> 16) & 0xffu), b.x, s0);
+    s1 = fmaf((float)((od >> 16) & 0xffu), b.y, s1);
+    s0 = fmaf((float)(ev >> 24), b.z, s0);
+    s1 = fmaf((float)(od >> 24), b.w, s1);
     return s0 + s1;
   }
 };
 
 // Streams RPW weight rows (K elements each, starting at base[i]) against M
-// input vectors staged in LDS (xs[m*K + j]). Lane l covers 16 bytes of every
-// 1024-byte chunk of a row. Chunks are fetched in batches of U per row, one
-// batch ahead of the arithmetic; the first batch is issued by start(), which
+// input vectors staged in LDS (xs[m*K + j]). Lane l covers one load (E
+// elements) of every 64-load chunk of a row. Chunks are fetched in batches of
+// U per row (as many bytes for every type), one batch ahead of the arithmetic; the first batch is issued by start(), which
 // kernels call before their prologue so the HBM stream overlaps it. Lanes past
 // the row end load a clamped (valid) address and skip the arithmetic.
 template <typename WT, int M, int RPW>
 struct RowStream {
   static constexpr int E = Dot<WT>::E;
   static constexpr int CW = kWave * E;
-  static constexpr int U = (RPW >= 4) ? 2 : (8 / RPW);
+  using V = typename Dot<WT>::V;
+  static constexpr int U = ((RPW >= 4) ? 2 : (8 / RPW)) * 16 / (int)sizeof(V);
   const char* base[RPW];
   const float* sb[RPW];  // group scales of each row (group-scaled types)
   int K, nchunks, lane;
-  u32x4 buf[U][RPW];
+  V buf[U][RPW];
   float gbuf[U][RPW];
 
-  __device__ __forceinline__ void fetch(int c0, u32x4 (&w)[U][RPW], float (&g)[U][RPW]) const {
+  __device__ __forceinline__ void fetch(int c0, V (&w)[U][RPW], float (&g)[U][RPW]) const {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int col = min((c0 + u) * CW + lane * E, K - E);
 #pragma unroll
       for (int i = 0; i < RPW; ++i) {
-        w[u][i] = ld16_nt(base[i] + wbytes<WT>(col));
+        w[u][i] = Dot<WT>::load(base[i] + wbytes<WT>(col));
         if constexpr (WT::kGrouped) g[u][i] = sb[i][col / kGroup];
       }
     }
@@ -238,7 +274,7 @@ struct RowStream {
 #pragma unroll
       for (int m = 0; m < M; ++m) acc[i][m] = 0.f;
     for (int c0 = 0; c0 < nchunks; c0 += U) {
-      u32x4 nxt[U][RPW];
+      V nxt[U][RPW];
       float gnxt[U][RPW];
       const bool more = c0 + U < nchunks;
       if (more) fetch(c0 + U, nxt, gnxt);
@@ -869,7 +905,8 @@ __device__ __forceinline__ void combine_body(const AttnArgs& a, int bid, char* l
 // -------------------------------------------- register-input weight streaming --
 
 // Wave-independent GEMV machinery for inputs of at most NCH chunks (NCH*64*E
-// columns, E = 8 bf16 or 16 fp8 per 16-byte load). Each lane keeps its own
+// columns, E = 8 bf16 or 16 fp8 / int8 per 16-byte load, 8 int4 per 4-byte
+// load). Each lane keeps its own
 // slice of the input row in registers (the same columns for every weight row
 // it touches), so no LDS staging and no workgroup barrier are needed: a wave
 // issues its input loads, then every weight load of all its rows at once (one
@@ -882,10 +919,12 @@ struct RegStream {
   static constexpr int CW = kWave * E;
   static constexpr int NX = E / 4;   // float4 of input per chunk
   static constexpr int NG = E / 8;   // 16-byte loads of bf16 gain per chunk
+  static constexpr bool kBiased = WT::kGrouped;  // int4: offset-binary products, see Dot<INT4>
   float4 x[NCH][NX];
   u32x4 g[NCH][NG];
-  u32x4 w[RPW][NCH];
+  typename Dot<WT>::V w[RPW][NCH];
   float gs[RPW][NCH];  // group scale of each row's chunk slice (group-scaled types)
+  float xb[NCH];       // 8 * the sum of this lane's slice of chunk c (kBiased)
   int lane, K;
   int c0 = 0, cs = 1;  // this wave's chunk c is input chunk c0 + c * cs
 
@@ -912,7 +951,7 @@ struct RegStream {
       const int col = min(col_of(c), K - E);
 #pragma unroll
       for (int i = 0; i < RPW; ++i) {
-        w[i][c] = ld16_nt(base[i] + wbytes<WT>(col));
+        w[i][c] = Dot<WT>::load(base[i] + wbytes<WT>(col));
         if constexpr (WT::kGrouped) gs[i][c] = scales[i][col / kGroup];
       }
     }
@@ -930,7 +969,10 @@ struct RegStream {
         ss += (x[c][j].x * x[c][j].x + x[c][j].y * x[c][j].y) + (x[c][j].z * x[c][j].z + x[c][j].w * x[c][j].w);
       }
     }
-    if (!has_gain) return;
+    if (!has_gain) {
+      slice_bias();
+      return;
+    }
     ss = wave_sum(ss);
     const float inv = 1.0f / sqrtf(ss / (float)K + eps);
 #pragma unroll
@@ -950,15 +992,33 @@ struct RegStream {
         b.w = (b.w * inv) * bf_hi(gg.w);
       }
     }
+    slice_bias();
+  }
+
+  __device__ __forceinline__ void slice_bias() {
+    if constexpr (kBiased) {
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        float t = 0.f;
+#pragma unroll
+        for (int j = 0; j < NX; ++j) t += (x[c][j].x + x[c][j].y) + (x[c][j].z + x[c][j].w);
+        xb[c] = 8.f * t;
+      }
+    }
   }
 
   __device__ __forceinline__ float dot_row(int i) const {
     float acc = 0.f;
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
-      const float d = Dot<WT>::run(w[i][c], reinterpret_cast<const float*>(&x[c][0]));
-      if constexpr (WT::kGrouped) acc = fmaf(gs[i][c], d, acc);
-      else acc += d;
+      const float* xc = reinterpret_cast<const float*>(&x[c][0]);
+      if constexpr (kBiased) {
+        acc = fmaf(gs[i][c], Dot<WT>::run_biased(w[i][c], xc) - xb[c], acc);
+      } else if constexpr (WT::kGrouped) {
+        acc = fmaf(gs[i][c], Dot<WT>::run(w[i][c], xc), acc);
+      } else {
+        acc += Dot<WT>::run(w[i][c], xc);
+      }
     }
     return acc;
   }
