@@ -211,8 +211,13 @@ struct Dot<INT4> {
     const float4 a = *reinterpret_cast<const float4*>(x);
     const float4 b = *reinterpret_cast<const float4*>(x + 4);
     const uint32_t u = w ^ 0x88888888u;
-    const uint32_t ev = u & 0x0f0f0f0fu;         // columns 0, 2, 4, 6
-    const uint32_t od = (u >> 4) & 0x0f0f0f0fu;  // columns 1, 3, 5, 7
+    uint32_t ev = u & 0x0f0f0f0fu;         // columns 0, 2, 4, 6
+    uint32_t od = (u >> 4) & 0x0f0f0f0fu;  // columns 1, 3, 5, 7
+    // hide the known-zero high nibbles from the optimiser, which would
+    // otherwise narrow the byte masks below and lose the one-instruction
+    // byte-to-float conversions (v_cvt_f32_ubyte1..3)
+    asm("" : "+v"(ev));
+    asm("" : "+v"(od));
     float s0 = (float)(ev & 0xffu) * a.x;
     float s1 = (float)(od & 0xffu) * a.y;
     s0 = fmaf((float)((ev >> 8) & 0xffu), a.z, s0);
@@ -1053,7 +1058,7 @@ struct PerWave<INT8> {
 };
 template <>
 struct PerWave<INT4> {
-  static constexpr int v = 4;  // a quarter of a bf16 row's bytes per row
+  static constexpr int v = 2;  // more waves rather than more rows each: the int4 dot is ALU-heavy
 };
 
 // y[r] (+)= scale[r] * W[r] . x, P rows per wave
