@@ -128,11 +128,12 @@ def main():
     codes = sess.ring(wl.prefill_len - 1, args.steps + 1)
 
     # dominant kernel: the kind with the largest share of serialised frames
-    # (both chains on one stream, every launch bracketed by HIP events on that
-    # stream: the kernels' own durations, as rocprofv3, which also serialises
-    # the streams, reports them). Its launches are then also timed live on
-    # their own streams over a second pass of the two-stream frames, where a
-    # launch shares HBM with the other chain's kernels.
+    # (both chains on one stream, every launch timed by a pair of HIP events
+    # that the launch itself stamps at the kernel's start and end: the
+    # kernels' own durations, as rocprofv3, which also serialises the streams,
+    # reports them). Its launches are then also timed live on their own
+    # streams over a second pass of the two-stream frames, where a launch
+    # shares HBM with the other chain's kernels.
     roof = None
     if args.profile_frames > 0:
         sess.reset()

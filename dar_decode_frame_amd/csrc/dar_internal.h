@@ -263,7 +263,9 @@ struct Task {
 
 int head_grid(int rows);
 // Launch the kernel specialised for this task (kind, rows M, input width).
-hipError_t launch_task(int wtype, const Task& t, hipStream_t s);
+// Timing events, when given, are stamped by the launch at the kernel's start
+// and end (a many-row stage: recorded before and after its launches).
+hipError_t launch_task(int wtype, const Task& t, hipStream_t s, hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 // What launch_task needs set up on the host (kernel LDS limits) without
 // launching; call before capturing the launch into a graph.
 hipError_t prepare_task(int wtype, const Task& t);

@@ -18,6 +18,7 @@
 // applied once to the finished dot product. Activations on the residual path
 // stay fp32; the slow and fast KV caches are bf16.
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -1749,21 +1750,29 @@ static hipError_t allow_lds(KernelT kern, size_t lds, bool& done) {
   return e;
 }
 
-// prep: only raise the LDS limit (before graph capture), no launch
+// prep: only raise the LDS limit (before graph capture), no launch. With
+// events, the launch itself stamps them at the kernel's start and end.
 template <class A>
-static hipError_t go1(const typename A::Args& a, const Geo& g, hipStream_t s, bool prep) {
+static hipError_t go1(const typename A::Args& a, const Geo& g, hipStream_t s, bool prep, hipEvent_t ev0,
+                      hipEvent_t ev1) {
   static bool big = false;
   hipError_t e = allow_lds(k_one<A>, g.lds, big);
   if (e != hipSuccess || prep) return e;
-  hipLaunchKernelGGL(k_one<A>, dim3(g.grid), dim3(kBlock), g.lds, s, a);
+  if (ev0 || ev1)
+    hipExtLaunchKernelGGL(k_one<A>, dim3(g.grid), dim3(kBlock), g.lds, s, ev0, ev1, 0, a);
+  else
+    hipLaunchKernelGGL(k_one<A>, dim3(g.grid), dim3(kBlock), g.lds, s, a);
   return hipGetLastError();
 }
 
 template <typename WT>
-static hipError_t single_launch(const Task& t, hipStream_t s, bool prep) {
+static hipError_t single_launch(const Task& t, hipStream_t s, bool prep, hipEvent_t ev0 = nullptr,
+                                hipEvent_t ev1 = nullptr) {
   if (t.kind == T_NONE) return hipSuccess;
   hipError_t err = hipErrorInvalidValue;
-  with_body<WT>(t, [&](auto body, const auto& args, const Geo& g) { err = go1<decltype(body)>(args, g, s, prep); });
+  with_body<WT>(t, [&](auto body, const auto& args, const Geo& g) {
+    err = go1<decltype(body)>(args, g, s, prep, ev0, ev1);
+  });
   return err;
 }
 
@@ -1791,13 +1800,19 @@ static bool row_stage(const Task& t, hipStream_t s, hipError_t& e) {
   }
 }
 
-hipError_t launch_task(int wtype, const Task& t, hipStream_t s) {
+hipError_t launch_task(int wtype, const Task& t, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
   hipError_t e = hipSuccess;
-  if (row_stage(t, s, e)) return e;
-  if (wtype == W_FP8) return single_launch<FP8>(t, s, false);
-  if (wtype == W_INT8) return single_launch<INT8>(t, s, false);
-  if (wtype == W_INT4) return single_launch<INT4>(t, s, false);
-  return single_launch<BF16>(t, s, false);
+  if (t.kind >= T_NORM_SPLIT) {
+    // a many-row stage may take several launches: events around all of them
+    if (ev0 && (e = hipEventRecord(ev0, s)) != hipSuccess) return e;
+    if (!row_stage(t, s, e)) return hipErrorInvalidValue;
+    if (e == hipSuccess && ev1) e = hipEventRecord(ev1, s);
+    return e;
+  }
+  if (wtype == W_FP8) return single_launch<FP8>(t, s, false, ev0, ev1);
+  if (wtype == W_INT8) return single_launch<INT8>(t, s, false, ev0, ev1);
+  if (wtype == W_INT4) return single_launch<INT4>(t, s, false, ev0, ev1);
+  return single_launch<BF16>(t, s, false, ev0, ev1);
 }
 
 hipError_t prepare_task(int wtype, const Task& t) {

@@ -838,7 +838,7 @@ hipError_t enqueue_plan(dar_ctx* c, const Plan& p, hipStream_t s, size_t ev_base
     if (ev_base != SIZE_MAX) {
       before = c->events[2 * (ev_base + i)];
       after = c->events[2 * (ev_base + i) + 1];
-    } else if (timed(c, p, i)) {
+    } else if (live && timed(c, p, i)) {  // (eager launches only, not under capture)
       while (c->tpool.size() < c->tused + 2) {
         hipEvent_t ev;
         hipError_t e = hipEventCreate(&ev);
@@ -848,10 +848,6 @@ hipError_t enqueue_plan(dar_ctx* c, const Plan& p, hipStream_t s, size_t ev_base
       before = c->tpool[c->tused];
       after = c->tpool[c->tused + 1];
       c->tused += 2;
-    }
-    if (before) {
-      hipError_t e = hipEventRecord(before, s);
-      if (e != hipSuccess) return e;
     }
     const Task& t = p.tasks[i];
     hipError_t e;
@@ -865,15 +861,11 @@ hipError_t enqueue_plan(dar_ctx* c, const Plan& p, hipStream_t s, size_t ev_base
       Task trimmed = t;
       trimmed.attn.chunk = c->attn_chunk_live;
       trimmed.attn.nsplit_max = std::max(2, c->attn_splits_live);
-      e = launch_task(wt, trimmed, s);
+      e = launch_task(wt, trimmed, s, before, after);
     } else {
-      e = launch_task(wt, t, s);
+      e = launch_task(wt, t, s, before, after);
     }
     if (e != hipSuccess) return e;
-    if (after) {
-      e = hipEventRecord(after, s);
-      if (e != hipSuccess) return e;
-    }
   }
   return hipSuccess;
 }

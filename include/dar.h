@@ -278,15 +278,17 @@ int dar_op_attention(const float* q, const void* K, const void* V, int32_t n_hea
 int dar_op_fp8_decode(const void* codes, int32_t n, float* out, void* stream);
 
 /* Time one kind of launch live: from the next decode call on, every one-row
- * launch of `kind` (the kinds of dar_profile_frame; -1 = off) is bracketed by
- * a HIP event pair on the stream it runs on (eager launches only, not graph
- * replay). dar_kind_time synchronises, returns the summed milliseconds and the
+ * launch of `kind` (the kinds of dar_profile_frame; -1 = off) is timed by a
+ * HIP event pair on the stream it runs on, which a single-kernel launch
+ * stamps at the kernel's own start and end (hipExtLaunchKernel; a many-row
+ * stage of a batched context: recorded around its launches). Eager launches
+ * only, not graph replay. dar_kind_time synchronises, returns the summed milliseconds and the
  * number of timed launches since dar_time_kind or the last read, and resets. */
 int dar_time_kind(dar_ctx* ctx, int32_t kind);
 int dar_kind_time(dar_ctx* ctx, double* ms_total, int32_t* launches);
 
-/* Run one frame eagerly on one stream with a HIP event pair around every
- * launch and report per-launch milliseconds, kind and layer tag (host arrays
+/* Run one frame eagerly on one stream with a HIP event pair timing every
+ * launch (stamped as for dar_time_kind) and report per-launch milliseconds, kind and layer tag (host arrays
  * of capacity cap; *n_out is the number of launches). Kinds: 0 qkv,
  * 1 attention, 2 wo, 3 w13, 4 w2, 5 codebook head, 6 other. Layer tags: slow
  * layer l is l; fast layer l of pass k is 1000k + l. The frame advances the
