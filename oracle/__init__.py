@@ -14,6 +14,11 @@ Pinned against what the pages and the mathematics fix (see tests/test_oracle_*):
             cache-free full recompute (tuna-fish README, intro and "Inference
             estimation"; groxaxo fork README, architecture paragraph; pyshine
             fish-speech tour, "Why You Need This")
+  int8.py, int4.py  weight-only quantisers (tuna-fish README's int8wo and
+            int4wo modes; readings in their headers)
+  sampling.py  temperature / top-k / top-p / repetition-window sampling of
+            one code (pyshine fish-speech tour, "Why You Need This"; reading
+            in its header)
 End-to-end logits have no printed values on the pages: parity unpinned at that
 level; the pins are the parts and the invariants that tie them together.
 """

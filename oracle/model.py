@@ -242,9 +242,15 @@ class OracleModel:
 
 
 class OracleDecoder:
-    """Greedy batch-1 decode state: slow KV cache, position, committed frames."""
+    """Batch-1 decode state: slow KV cache, position, committed frames.
 
-    def __init__(self, model: OracleModel, max_len: int):
+    Greedy by default. With `sampling` (oracle/sampling.SamplingParams) and
+    `uniforms` ([max_len][1 + n_res] values in [0, 1)), the code of codebook k
+    of the frame at slow position p is drawn by sample_code with uniforms[p][k],
+    its repetition window reading the committed codes of the frames since the
+    prompt (the first frame sits at the last prompt position)."""
+
+    def __init__(self, model: OracleModel, max_len: int, sampling=None, uniforms=None):
         d = model.dims
         self.m = model
         self.max_len = max_len
@@ -253,6 +259,23 @@ class OracleDecoder:
         self.v = np.zeros(shape, dtype=model.dt)
         self.pos = 0
         self.last_c0 = None
+        self.sampling = sampling
+        self.uniforms = uniforms
+        self.ring = np.full((max_len, d.n_res + 1), -1, dtype=np.int64)
+        self.first = 0          # slow position of frame 0
+        self.frame_pos = 0      # slow position of the frame being produced
+        self.margins = []       # (logit_gap, mass_gap) per sampled code
+
+    def _choose(self, logits, k):
+        """The model's code for codebook k of the current frame."""
+        if self.sampling is None:
+            return greedy_argmax(logits)
+        from .sampling import sample_code, window_history
+        p = self.frame_pos
+        hist = window_history(self.ring, p, k, self.first, self.sampling.window)
+        code, info = sample_code(logits, hist, self.sampling, float(self.uniforms[p][k]))
+        self.margins.append((info["logit_gap"], info["mass_gap"]))
+        return code
 
     def _slow(self, x: np.ndarray, p0: int):
         for i, layer in enumerate(self.m.slow):
@@ -278,17 +301,19 @@ class OracleDecoder:
         for k in range(1, R + 1):
             y = run(m.fast_emb[k - 1][prev], k)
             lk = m.fast_logits(y)
-            ck = greedy_argmax(lk)
+            ck = self._choose(lk, k)
             codes.append(ck)
             logits.append(lk)
             prev = ck if forced is None else int(forced[k])
+            self.ring[self.frame_pos][k] = prev
         return codes, logits
 
     def _frame_from_slow(self, x_last, forced):
         l0, h_t = self.m.head0(x_last)
-        c0 = greedy_argmax(l0)
+        c0 = self._choose(l0, 0)
         codes, logits = [c0], [l0]
         committed_c0 = c0 if forced is None else int(forced[0])
+        self.ring[self.frame_pos][0] = committed_c0
         if self.m.dims.has_fast:
             cs, ls = self.fast_frame(h_t, c0, forced)
             codes += cs
@@ -311,6 +336,7 @@ class OracleDecoder:
             for p in range(n):
                 x_last = self._slow(x[p:p + 1], p)[0]
         self.pos = n
+        self.first = self.frame_pos = n - 1
         return self._frame_from_slow(x_last, forced)
 
     def decode_frame(self, forced=None):
@@ -321,6 +347,7 @@ class OracleDecoder:
             raise RuntimeError("capacity")
         x = self.m.w0[self.last_c0][None, :]
         x = self._slow(x, self.pos)[0]
+        self.frame_pos = self.pos
         self.pos += 1
         return self._frame_from_slow(x, forced)
 
