@@ -82,6 +82,29 @@ struct HeadArgs {
 };
 
 // Reduce a head's slots to its code and do the frame bookkeeping.
+// Sampling of a frame's codes instead of the argmax (u == nullptr: argmax).
+// Per codebook: the codes of the previous `window` frames (committed codes,
+// from the sequence's first frame on) have their logits divided by `penalty`
+// when positive and multiplied otherwise; all logits are divided by
+// `temperature`; the top_k largest (ties: lower code) are the candidates;
+// softmax over them; cut after the first candidate whose running probability
+// sum reaches top_p times the total; the code is the first kept candidate
+// whose running sum exceeds u times the kept total.
+constexpr int kMaxTopK = 256;          // candidates sorted within one workgroup
+constexpr int kMaxSampleVocab = 8192;  // logits held in LDS
+constexpr int kMaxWindow = 64;
+struct SampleArgs {
+  const float* u;     // [max_len][B][frame_codes] draws in [0, 1), by frame position
+  float temperature, top_p, penalty;
+  int top_k, window;
+  const int* win_lo;  // [B] slow position of each sequence's first frame
+};
+// dynamic LDS of one sampling workgroup over V logits
+inline size_t sample_lds_bytes(int V) {
+  return (((size_t)V * 4 + 15) & ~(size_t)15) + ((((size_t)V + 31) / 32 * 4 + 15) & ~(size_t)15) + 256 * 4 +
+         (size_t)kMaxTopK * 8 + 256 * 4 + 128;
+}
+
 struct CommitArgs {
   const unsigned long long* slots;
   int nslots;
@@ -104,6 +127,9 @@ struct CommitArgs {
   const float* copy_src[2];   // optional plain copies done by the same workgroup
   float* copy_dst[2];
   int copy_n[2];
+  const float* logits;        // the head's logits [V] (read when sampling)
+  int V;
+  SampleArgs smp;
 };
 
 struct AttnArgs {
@@ -178,6 +204,7 @@ struct RowsCommitArgs {
   float* copy_dst[2];        // for i < copy_n[j]
   int copy_src_stride[2], copy_dst_stride[2], copy_n[2];
   int* anomalies;
+  SampleArgs smp;
 };
 
 enum TaskKind : int {
@@ -321,6 +348,10 @@ hipError_t launch_quantize_int8(const uint16_t* w, int rows, int cols, int8_t* q
 // int4 in groups of 128 columns: scale [rows][cols/128] = max|w| / 7, codes
 // rint(w / scale) in [-7, 7], packed two per byte (even column low)
 hipError_t launch_quantize_int4(const uint16_t* w, int rows, int cols, uint8_t* q, float* scale, hipStream_t s);
+// codes[r] = the sampled code of logits row r (sample.u[r] the draw,
+// history[r][0..n_hist) its window's codes, entries outside [0, V) ignored)
+hipError_t launch_sample_rows(const float* logits, int rows, int V, const SampleArgs& sample, const int* history,
+                              int n_hist, int* codes, hipStream_t s);
 hipError_t launch_copy_i32(const int* src, int* dst, int n, hipStream_t s);
 
 size_t attn_partial_floats(int M, int n_kv, int nsplit_max, int group, int head_dim);

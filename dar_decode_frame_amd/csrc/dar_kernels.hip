@@ -23,6 +23,7 @@
 #include <stdint.h>
 
 #include "dar_internal.h"
+#include "dar_sample.h"
 
 namespace dar {
 
@@ -651,15 +652,24 @@ __device__ __forceinline__ void head_body(const HeadArgs& a, int bid, char* lds)
   }
 }
 
-// One workgroup after each head: reduce the per-block maxima to the code,
-// record it (argmax and committed/forced), gather the next step's inputs and,
-// after the frame's last head, advance the position.
+// One workgroup after each head: reduce the per-block maxima to the code (or
+// sample it from the head's logits), record it (the model's code and the
+// committed/forced one), gather the next step's inputs and, after the frame's
+// last head, advance the position.
 __device__ __forceinline__ void commit_body(const CommitArgs& a, char* lds) {
   unsigned long long* red = reinterpret_cast<unsigned long long*>(lds);
   int* code_sh = reinterpret_cast<int*>(lds + kWaves * sizeof(unsigned long long));
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   // independent loads first: they overlap the slot reduction
   const int force = *a.force_flag, forced = a.forced[a.code_index], pos = *a.pos;
+  int sampled = 0;
+  if (a.smp.u) {
+    // window: this codebook's committed codes at positions [lo, pos)
+    const int lo = max(*a.smp.win_lo, pos - a.smp.window);
+    sampled = sample_row(a.logits, a.V, a.smp, a.smp.u[(size_t)pos * a.frame_codes + a.code_index],
+                         a.ring + (size_t)lo * a.frame_codes + a.code_index, a.frame_codes, max(pos - lo, 0), lds);
+    __syncthreads();  // the LDS is reused below
+  }
   unsigned long long b = 0ull;
   for (int i = tid; i < a.nslots; i += kBlock) b = a.slots[i] > b ? a.slots[i] : b;
 #pragma unroll
@@ -673,7 +683,7 @@ __device__ __forceinline__ void commit_body(const CommitArgs& a, char* lds) {
     unsigned long long m = red[0];
 #pragma unroll
     for (int w = 1; w < kWaves; ++w) m = red[w] > m ? red[w] : m;
-    const int pred = (int)(0xffffffffu - (uint32_t)(m & 0xffffffffull));
+    const int pred = a.smp.u ? sampled : (int)(0xffffffffu - (uint32_t)(m & 0xffffffffull));
     const int code = force ? forced : pred;
     a.pred[a.code_index] = pred;
     a.committed[a.code_index] = code;
@@ -1591,6 +1601,15 @@ __global__ __launch_bounds__(kBlock) void k_quantize_int4(const uint16_t* w, int
   }
 }
 
+// codes[r] = the code sampled from logits row r (one workgroup per row)
+__global__ __launch_bounds__(kBlock) void k_sample_rows(const float* logits, int V, SampleArgs sp, const int* history,
+                                                       int n_hist, int* codes) {
+  extern __shared__ __align__(16) char lds[];
+  const int r = blockIdx.x;
+  const int c = sample_row(logits + (size_t)r * V, V, sp, sp.u[r], history + (size_t)r * n_hist, 1, n_hist, lds);
+  if (threadIdx.x == 0) codes[r] = c;
+}
+
 __global__ void k_fp8_decode(const uint8_t* codes, int n, float* out) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) {
@@ -1714,7 +1733,9 @@ static bool with_body(const Task& t, F&& f) {
     }
     case T_HEAD: return head_body_for<WT, WT>(t.head, f);
     case T_HEAD_BF16: return head_body_for<WT, BF16>(t.head, f);
-    case T_COMMIT: f(Commit{}, t.commit, Geo{1, 64}); return true;
+    case T_COMMIT:
+      f(Commit{}, t.commit, Geo{1, t.commit.smp.u ? sample_lds_bytes(t.commit.V) : (size_t)64});
+      return true;
     case T_ATTN:
     case T_COMBINE: {
       const int g = t.attn.n_heads_q / t.attn.n_heads_kv;
@@ -1872,6 +1893,15 @@ hipError_t launch_quantize_int8(const uint16_t* w, int rows, int cols, int8_t* q
 hipError_t launch_quantize_int4(const uint16_t* w, int rows, int cols, uint8_t* q, float* scale, hipStream_t s) {
   if (cols % kGroup) return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_quantize_int4, dim3(rows), dim3(kBlock), 0, s, w, rows, cols, q, scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_sample_rows(const float* logits, int rows, int V, const SampleArgs& sample, const int* history,
+                              int n_hist, int* codes, hipStream_t s) {
+  if (rows < 1 || V < 1 || V > kMaxSampleVocab || sample.top_k < 1 || sample.top_k > kMaxTopK || n_hist < 0)
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_sample_rows, dim3(rows), dim3(kBlock), sample_lds_bytes(V), s, logits, V, sample, history,
+                     n_hist, codes);
   return hipGetLastError();
 }
 

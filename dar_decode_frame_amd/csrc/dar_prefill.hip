@@ -18,6 +18,7 @@
 #include <algorithm>
 
 #include "dar_internal.h"
+#include "dar_sample.h"
 
 namespace dar {
 
@@ -597,8 +598,17 @@ __global__ __launch_bounds__(kBlock) void k_silu_split(const float* a, const flo
 __global__ __launch_bounds__(kBlock) void k_commit_rows(RowsCommitArgs a) {
   __shared__ unsigned long long red[kWaves];
   __shared__ int code_sh;
+  extern __shared__ __align__(16) char sample_lds[];  // sample_lds_bytes(V) when sampling
   const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const float* lg = a.logits + (size_t)b * a.ld;
+  int sampled = 0;
+  if (a.smp.u) {
+    // window: sequence b's committed codes of this codebook at positions [lo, pos)
+    const int pos = a.pos[b], lo = max(a.smp.win_lo[b], pos - a.smp.window);
+    sampled = sample_row(lg, a.V, a.smp, a.smp.u[((size_t)pos * a.B + b) * a.frame_codes + a.code_index],
+                         a.ring + ((size_t)lo * a.B + b) * a.frame_codes + a.code_index,
+                         (long long)a.B * a.frame_codes, max(pos - lo, 0), sample_lds);
+  }
   unsigned long long best = 0ull;
   int bad = 0;
   for (int i = tid; i < a.V; i += kBlock) {
@@ -625,7 +635,7 @@ __global__ __launch_bounds__(kBlock) void k_commit_rows(RowsCommitArgs a) {
     unsigned long long m = red[0];
 #pragma unroll
     for (int w = 1; w < kWaves; ++w) m = red[w] > m ? red[w] : m;
-    const int pred = (int)(0xffffffffu - (uint32_t)(m & 0xffffffffull));
+    const int pred = a.smp.u ? sampled : (int)(0xffffffffu - (uint32_t)(m & 0xffffffffull));
     const int slot = b * a.frame_codes + a.code_index;
     const int code = *a.force_flag ? a.forced[slot] : pred;
     a.pred[slot] = pred;
@@ -786,7 +796,7 @@ hipError_t launch_inc_rows(int* v, int n, hipStream_t s) {
 }
 
 hipError_t launch_commit_rows(const RowsCommitArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(k_commit_rows, dim3(a.B), dim3(kBlock), 0, s, a);
+  hipLaunchKernelGGL(k_commit_rows, dim3(a.B), dim3(kBlock), a.smp.u ? sample_lds_bytes(a.V) : 0, s, a);
   return hipGetLastError();
 }
 

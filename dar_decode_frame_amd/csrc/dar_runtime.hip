@@ -126,7 +126,7 @@ Layout make_layout(const dar_config* c) {
   L.committed = take(sizeof(int) * B * fc);
   L.forced = take(sizeof(int) * B * fc);
   L.flags = take(sizeof(int) * 4);
-  L.pos = take(sizeof(int) * (2 * B + 4));  // slow positions [B], frame positions [B]
+  L.pos = take(sizeof(int) * (3 * B + 4));  // slow positions [B], frame positions [B], first frames [B]
   L.seqpos = take(sizeof(int) * L.seq_len);
   L.ring = take(sizeof(int) * (size_t)c->max_len * B * fc);
   L.rope = take(sizeof(float) * 2 * (size_t)L.rope_len * (c->head_dim / 2));
@@ -288,6 +288,8 @@ struct dar_ctx {
   float *ht, *logits0, *flogits;
   unsigned long long *slots0, *slotsf;
   int *pred, *committed, *forced, *flags, *pos_s, *pos_f, *seqpos, *ring;
+  int* win_lo;                 // [B] slow position of each sequence's first frame (sampling windows)
+  SampleArgs smp{};            // sampling of the codes (u == nullptr: greedy argmax)
   int B = 1;                   // sequences decoded in lockstep
   float* bgp[2];
   uint16_t *bxh[2], *bxl[2];
@@ -481,13 +483,16 @@ std::vector<TaskRec> slow_chain(dar_ctx* c, bool with_head) {
   return out;
 }
 
-Task commit_task(dar_ctx* c, int k, const unsigned long long* slots, int rows) {
+Task commit_task(dar_ctx* c, int k, const unsigned long long* slots, int rows, const float* logits) {
   Task t = none_task();
   t.kind = T_COMMIT;
   t.M = 1;
   CommitArgs& a = t.commit;
   a.slots = slots;
   a.nslots = head_grid(rows);
+  a.logits = logits;
+  a.V = rows;
+  a.smp = c->smp;
   a.code_index = k;
   a.frame_codes = frame_codes(&c->cfg);
   a.pred = c->pred;
@@ -510,7 +515,7 @@ std::vector<TaskRec> commit0_chain(dar_ctx* c) {
   const int d = g.d_model;
   const bool fast = has_fast(&g);
   std::vector<TaskRec> out;
-  Task t0 = commit_task(c, 0, c->slots0, g.vocab_c0);
+  Task t0 = commit_task(c, 0, c->slots0, g.vocab_c0, c->logits0);
   CommitArgs& a = t0.commit;
   a.pos_inc = fast ? nullptr : c->pos_f;
   a.next_table = fast ? c->fast_emb[0] : nullptr;
@@ -558,7 +563,7 @@ std::vector<TaskRec> fast_chain(dar_ctx* c) {
     hk.slots = c->slotsf;
     hk.anomalies = c->flags + 1;
     out.push_back(rec(t, K_HEAD, k));
-    Task ck = commit_task(c, k, c->slotsf, g.vocab_res);
+    Task ck = commit_task(c, k, c->slotsf, g.vocab_res, c->flogits + (size_t)k * c->L.vmax);
     ck.commit.pos_inc = (k == g.n_res) ? c->pos_f : nullptr;
     ck.commit.next_table = (k < g.n_res) ? c->fast_emb[k] : nullptr;
     ck.commit.next_rows = g.vocab_res;
@@ -721,6 +726,7 @@ RowsCommitArgs rows_commit(dar_ctx* c, int k, const float* logits, int ld, int V
   r.pos = c->pos_f;
   r.K = g.d_model;
   r.anomalies = c->flags + 1;
+  r.smp = c->smp;
   return r;
 }
 
@@ -1182,6 +1188,7 @@ int dar_create(const dar_config* cfg, const dar_weights* w, void* workspace, siz
   c->pos_hb.assign(c->B, 0);
   c->pos_s = reinterpret_cast<int*>(b + L.pos);
   c->pos_f = c->pos_s + c->B;
+  c->win_lo = c->pos_s + 2 * c->B;
   if (c->B > 1) {
     for (int ch = 0; ch < 2; ++ch) {
       c->bgp[ch] = reinterpret_cast<float*>(b + L.bgp[ch]);
@@ -1313,9 +1320,10 @@ int dar_prefill(dar_ctx* c, int32_t batch, const int32_t* tokens, const int32_t*
   }
   // codebook-0 head on each sequence's last position (moves pos_s to the
   // prompt length); frame 0 sits at the last prompt position
-  c->pos_init.assign(2 * c->B, 0);
-  for (int b = 0; b < batch; ++b) c->pos_init[b] = c->pos_init[c->B + b] = lens_host[b] - 1;
-  DAR_HIP(c, hipMemcpyAsync(c->pos_s, c->pos_init.data(), sizeof(int) * 2 * c->B, hipMemcpyHostToDevice, s),
+  c->pos_init.assign(3 * c->B, 0);
+  for (int b = 0; b < batch; ++b)
+    c->pos_init[b] = c->pos_init[c->B + b] = c->pos_init[2 * c->B + b] = lens_host[b] - 1;
+  DAR_HIP(c, hipMemcpyAsync(c->pos_s, c->pos_init.data(), sizeof(int) * 3 * c->B, hipMemcpyHostToDevice, s),
           "prefill positions");
   if (c->B == 1) {
     DAR_HIP(c, launch_task(wt, c->p_slow.tasks.back(), s), "prefill head");
@@ -1615,6 +1623,85 @@ int dar_op_fp8_decode(const void* codes, int32_t n, float* out, void* stream) {
   if (!codes || !out || n < 1) return DAR_E_INVAL;
   hipError_t e = launch_fp8_decode(static_cast<const uint8_t*>(codes), n, out, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(nullptr, e, "fp8 decode");
+  return DAR_OK;
+}
+
+// checks a dar_sampling against a vocabulary of up to vmax codes; fills sp
+static int sampling_args(const dar_sampling* s, int vmax, SampleArgs& sp, std::string& why) {
+  if (!s->uniforms || (reinterpret_cast<uintptr_t>(s->uniforms) & 3u)) {
+    why = "uniforms NULL or misaligned";
+    return DAR_E_INVAL;
+  }
+  if (!(s->temperature > 0.f) || !std::isfinite(s->temperature)) {
+    why = "temperature must be positive and finite";
+    return DAR_E_INVAL;
+  }
+  if (!(s->top_p > 0.f) || !(s->top_p <= 1.f)) {
+    why = "top_p must be in (0, 1]";
+    return DAR_E_INVAL;
+  }
+  if (!(s->repetition_penalty >= 1.f) || !std::isfinite(s->repetition_penalty)) {
+    why = "repetition_penalty must be >= 1 and finite";
+    return DAR_E_INVAL;
+  }
+  if (s->top_k < 1 || s->repetition_window < 0) {
+    why = "top_k must be >= 1 and repetition_window >= 0";
+    return DAR_E_INVAL;
+  }
+  if (s->top_k > kMaxTopK || s->repetition_window > kMaxWindow || vmax > kMaxSampleVocab) {
+    why = "top_k above 256, repetition_window above 64 or a vocabulary above 8192";
+    return DAR_E_UNSUPPORTED;
+  }
+  sp.u = s->uniforms;
+  sp.temperature = s->temperature;
+  sp.top_p = s->top_p;
+  sp.penalty = s->repetition_penalty;
+  sp.top_k = s->top_k;
+  sp.window = s->repetition_window;
+  return DAR_OK;
+}
+
+int dar_set_sampling(dar_ctx* c, const dar_sampling* s) {
+  if (!c) return DAR_E_INVAL;
+  SampleArgs sp{};
+  if (s) {
+    const int vmax = std::max(c->cfg.vocab_c0, has_fast(&c->cfg) ? c->cfg.vocab_res : 0);
+    const int st = sampling_args(s, vmax, sp, c->err);
+    if (st != DAR_OK) return st;
+    sp.win_lo = c->win_lo;
+  }
+  // no frame of this context may still read the plans' arguments or graphs
+  DAR_HIP(c, hipStreamSynchronize(c->cs.s), "synchronize");
+  DAR_HIP(c, hipStreamSynchronize(c->cf.s), "synchronize");
+  c->smp = sp;
+  for (Plan* p : {&c->p_c0, &c->p_fast, &c->p_slow}) {
+    bool changed = false;
+    for (Task& t : p->tasks) {
+      if (t.kind == T_COMMIT) {
+        t.commit.smp = sp;
+        changed = true;
+      } else if (t.kind == T_COMMIT_ROWS) {
+        t.rows.smp = sp;
+        changed = true;
+      }
+    }
+    if (changed) free_plan(*p);  // a captured graph is captured again with the new arguments
+  }
+  return DAR_OK;
+}
+
+int dar_op_sample(const float* logits, int32_t rows, int32_t V, const dar_sampling* s, const int32_t* history,
+                  int32_t n_hist, int32_t* codes_out, void* stream) {
+  if (!logits || !s || !codes_out || rows < 1 || V < 1 || n_hist < 0 || (n_hist > 0 && !history))
+    return DAR_E_INVAL;
+  SampleArgs sp{};
+  std::string why;
+  const int st = sampling_args(s, V, sp, why);
+  if (st != DAR_OK) return st;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  hipError_t e = launch_sample_rows(logits, rows, V, sp, history, n_hist, codes_out, hs);
+  if (e == hipSuccess) e = hipStreamSynchronize(hs);
+  if (e != hipSuccess) return hip_fail(nullptr, e, "sample");
   return DAR_OK;
 }
 

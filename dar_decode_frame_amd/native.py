@@ -72,6 +72,17 @@ class dar_layer_weights(ctypes.Structure):
     ]
 
 
+class dar_sampling(ctypes.Structure):
+    _fields_ = [
+        ("temperature", ctypes.c_float),
+        ("top_k", ctypes.c_int32),
+        ("top_p", ctypes.c_float),
+        ("repetition_penalty", ctypes.c_float),
+        ("repetition_window", ctypes.c_int32),
+        ("uniforms", ctypes.c_void_p),
+    ]
+
+
 class dar_weights(ctypes.Structure):
     _fields_ = [
         ("w0", ctypes.c_void_p),
@@ -109,6 +120,8 @@ _SIGS = {
     "dar_op_gemm": ([_I32, _VP, _VP, _I32, _I32, _VP, _I32, _VP, _VP], ctypes.c_int),
     "dar_op_attention": ([_VP, _VP, _VP, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _VP, _VP], ctypes.c_int),
     "dar_op_fp8_decode": ([_VP, _I32, _VP, _VP], ctypes.c_int),
+    "dar_set_sampling": ([_VP, ctypes.POINTER(dar_sampling)], ctypes.c_int),
+    "dar_op_sample": ([_VP, _I32, _I32, ctypes.POINTER(dar_sampling), _VP, _I32, _VP, _VP], ctypes.c_int),
     "dar_time_kind": ([_VP, _I32], ctypes.c_int),
     "dar_kind_time": ([_VP, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_I32)], ctypes.c_int),
     "dar_profile_frame": ([_VP, _I32, _VP, _VP, _VP, ctypes.POINTER(_I32)], ctypes.c_int),
@@ -262,6 +275,21 @@ def dar_op_gemm(wtype, w_ptr, scale_ptr, N, K, x_ptr, M, y_ptr, stream_ptr):
 
 def dar_op_fp8_decode(codes_ptr, n, out_ptr, stream_ptr):
     return _check(lib.dar_op_fp8_decode(codes_ptr, n, out_ptr, stream_ptr), "dar_op_fp8_decode")
+
+
+def make_sampling(temperature, top_k, top_p, repetition_penalty, repetition_window, uniforms_ptr):
+    return dar_sampling(temperature, top_k, top_p, repetition_penalty, repetition_window, uniforms_ptr)
+
+
+def dar_set_sampling(ctx, sampling):
+    """sampling: a dar_sampling, or None for greedy argmax."""
+    return _check(lib.dar_set_sampling(ctx, ctypes.byref(sampling) if sampling is not None else None),
+                  "dar_set_sampling", ctx)
+
+
+def dar_op_sample(logits_ptr, rows, V, sampling, history_ptr, n_hist, codes_ptr, stream_ptr):
+    return _check(lib.dar_op_sample(logits_ptr, rows, V, ctypes.byref(sampling), history_ptr, n_hist, codes_ptr,
+                                    stream_ptr), "dar_op_sample")
 
 
 def dar_time_kind(ctx, kind):

@@ -191,6 +191,20 @@ class DarSession:
     def nonfinite(self):
         return N.dar_nonfinite(self.ctx)
 
+    def set_sampling(self, temperature=None, top_k=None, top_p=1.0, penalty=1.0, window=0, uniforms=None):
+        """Sample the codes (uniforms: [max_len][batch][1 + n_res] values in
+        [0, 1), kept on the device while the session samples); no arguments:
+        greedy argmax again."""
+        if temperature is None:
+            N.dar_set_sampling(self.ctx, None)
+            self._uniforms = None
+            return
+        u = torch.as_tensor(np.asarray(uniforms, dtype=np.float32).reshape(self.max_len, self.batch, self.fc))
+        self._uniforms = u.to(self.device).contiguous()
+        torch.cuda.current_stream(self.device).synchronize()
+        N.dar_set_sampling(self.ctx, N.make_sampling(temperature, top_k, top_p, penalty, window,
+                                                     self._uniforms.data_ptr()))
+
     def time_kind(self, kind):
         N.dar_time_kind(self.ctx, kind)
 

@@ -277,6 +277,51 @@ int dar_op_attention(const float* q, const void* K, const void* V, int32_t n_hea
  * out[i] = value of codes[i] (fp32). codes device uint8 [n], out device fp32 [n]. */
 int dar_op_fp8_decode(const void* codes, int32_t n, float* out, void* stream);
 
+/* Sampling of the frame's codes instead of the greedy argmax. The pages name
+ * top-p and top-k sampling with repetition windows in the generation loop
+ * (pyshine fish-speech tour, "Why You Need This") and give no formula; the
+ * reading taken, per codebook k of the frame at slow position p of sequence b:
+ *   1. every distinct code among codebook k's committed codes of the previous
+ *      repetition_window frames (from the sequence's first frame, the one at
+ *      its last prompt position) has its logit divided by repetition_penalty
+ *      when positive and multiplied by it otherwise;
+ *   2. every logit is divided by temperature (fp32);
+ *   3. the top_k largest are the candidates (equal values: the lower code);
+ *   4. softmax over the candidates, largest first;
+ *   5. the candidates are cut after the first one at which the running sum of
+ *      probabilities reaches top_p times their total;
+ *   6. the code is the first kept candidate whose running sum exceeds
+ *      u * (kept total), u = uniforms[(p * max_batch + b) * (1 + n_res) + k].
+ * The draws are inputs: uniforms is a caller-owned device fp32 array
+ * [max_len][max_batch][1 + n_res] of values in [0, 1), read while the
+ * context samples. NaN logits count as -infinity. Limits: 1 <= top_k <= 256,
+ * 0 <= repetition_window <= 64, vocabularies up to 8192 (DAR_E_UNSUPPORTED
+ * beyond); temperature > 0, top_p in (0, 1], repetition_penalty >= 1
+ * (DAR_E_INVAL otherwise). */
+typedef struct {
+  float temperature;
+  int32_t top_k;
+  float top_p;
+  float repetition_penalty;
+  int32_t repetition_window;
+  const float* uniforms;
+} dar_sampling;
+
+/* Switch the context to sampling with these parameters (copied), or back to
+ * greedy argmax with NULL. The codes returned and committed from then on are
+ * the sampled ones (forced codes still replace the committed ones). Waits for
+ * the context's frames in flight; a captured graph is captured again. */
+int dar_set_sampling(dar_ctx* ctx, const dar_sampling* sampling);
+
+/* The frame's sampling step alone: codes_out[r] = the code drawn from logits
+ * row r with u = sampling->uniforms[r] and window codes history[r][0..n_hist)
+ * (entries outside [0, V) ignored; the window length field is not used).
+ * logits device fp32 [rows][V], uniforms device fp32 [rows], history device
+ * int32 [rows][n_hist] (may be NULL when n_hist == 0), codes_out device int32
+ * [rows]. Synchronises the stream. */
+int dar_op_sample(const float* logits, int32_t rows, int32_t V, const dar_sampling* sampling,
+                  const int32_t* history, int32_t n_hist, int32_t* codes_out, void* stream);
+
 /* Time one kind of launch live: from the next decode call on, every one-row
  * launch of `kind` (the kinds of dar_profile_frame; -1 = off) is timed by a
  * HIP event pair on the stream it runs on, which a single-kernel launch

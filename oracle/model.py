@@ -264,7 +264,7 @@ class OracleDecoder:
         self.ring = np.full((max_len, d.n_res + 1), -1, dtype=np.int64)
         self.first = 0          # slow position of frame 0
         self.frame_pos = 0      # slow position of the frame being produced
-        self.margins = []       # (logit_gap, mass_gap) per sampled code
+        self.margins = []       # sample_code's info per sampled code, in order
 
     def _choose(self, logits, k):
         """The model's code for codebook k of the current frame."""
@@ -274,7 +274,7 @@ class OracleDecoder:
         p = self.frame_pos
         hist = window_history(self.ring, p, k, self.first, self.sampling.window)
         code, info = sample_code(logits, hist, self.sampling, float(self.uniforms[p][k]))
-        self.margins.append((info["logit_gap"], info["mass_gap"]))
+        self.margins.append(info)
         return code
 
     def _slow(self, x: np.ndarray, p0: int):

@@ -56,7 +56,8 @@ def sample_code(logits, history, params: SamplingParams, u: float):
     the kept candidates in order, their fp32 probabilities and running sums,
     and the margins: `logit_gap` between the last candidate and the first
     value left out (inf when all are kept), `mass_gap` the smallest relative
-    distance of the top-p and draw thresholds from a running sum."""
+    distance of the top-p and draw thresholds from a running sum, `order_gap`
+    between the picked candidate's value and its neighbours' in the order."""
     v = penalise(logits, history, params.penalty)
     v = v / np.float32(params.temperature)
     v = np.where(np.isnan(v), np.float32(-np.inf), v).astype(np.float32)
@@ -76,15 +77,23 @@ def sample_code(logits, history, params: SamplingParams, u: float):
     target = np.float32(u) * S
     pick = int(np.sum(cum[:m] <= target))
     pick = min(pick, m - 1)
-    gaps = [abs(float(cum[m - 1]) - float(thr))]
+    # the cut moves if the running sum at it drops below the threshold (only
+    # possible before the last candidate: at the last one the threshold is
+    # at most the total) or the one before it reaches the threshold
+    gaps = [abs(float(cum[m - 1]) - float(thr))] if m < k else []
     if m >= 2:
         gaps.append(abs(float(cum[m - 2]) - float(thr)))
     gaps.append(abs(float(cum[pick]) - float(target)))
     if pick >= 1:
         gaps.append(abs(float(cum[pick - 1]) - float(target)))
     mass_gap = min(gaps) / float(total)
+    # candidates whose values nearly tie with the pick's may come in the
+    # other order from logits that differ by rounding: the draw then lands on
+    # the same rank but another code
+    nb = [abs(float(vals[pick]) - float(vals[j])) for j in (pick - 1, pick + 1) if 0 <= j < k]
+    order_gap = min(nb) if nb else np.inf
     info = {"candidates": cand, "probs": w, "cum": cum, "kept": m, "pick": pick,
-            "logit_gap": logit_gap, "mass_gap": mass_gap}
+            "logit_gap": logit_gap, "mass_gap": mass_gap, "order_gap": order_gap}
     return int(cand[pick]), info
 
 

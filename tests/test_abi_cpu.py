@@ -120,3 +120,25 @@ def test_status_strings(N):
     for s in range(-6, 1):
         assert N.dar_status_string(s) not in ("", "unknown status")
     assert N.dar_status_string(-99) == "unknown status"
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("temperature", 0.0, -1), ("temperature", float("inf"), -1), ("top_k", 0, -1), ("top_k", 257, -6),
+    ("top_p", 0.0, -1), ("top_p", 1.5, -1), ("repetition_penalty", 0.5, -1), ("repetition_window", -1, -1),
+    ("repetition_window", 65, -6), ("uniforms", None, -1),
+])
+def test_sampling_argument_checks(N, field, value, status):
+    """Checked on the host before any launch (no GPU needed)."""
+    s = N.make_sampling(0.8, 50, 0.9, 1.2, 16, 4096)
+    setattr(s, field, value)
+    p = ctypes.c_void_p(4096)
+    assert N.lib.dar_op_sample(p, 4, 1024, ctypes.byref(s), p, 4, p, None) == status
+    assert N.lib.dar_set_sampling(None, ctypes.byref(s)) == N.DAR_E_INVAL
+
+
+def test_sampling_vocabulary_limit(N):
+    s = N.make_sampling(0.8, 50, 0.9, 1.2, 16, 4096)
+    p = ctypes.c_void_p(4096)
+    assert N.lib.dar_op_sample(p, 4, 8193, ctypes.byref(s), p, 4, p, None) == N.DAR_E_UNSUPPORTED
+    assert N.lib.dar_op_sample(p, 0, 1024, ctypes.byref(s), p, 4, p, None) == N.DAR_E_INVAL
+    assert N.lib.dar_op_sample(p, 4, 1024, ctypes.byref(s), None, 4, p, None) == N.DAR_E_INVAL
