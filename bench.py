@@ -42,6 +42,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-frames", type=int, default=3)
     ap.add_argument("--graph", action="store_true", help="replay captured graphs instead of eager launches")
+    ap.add_argument("--sample", action="store_true",
+                    help="sample the codes instead of the argmax (stand-in settings, the pages give none: "
+                         "temperature 0.8, top-k 50, top-p 0.9, repetition penalty 1.2 over 16 frames)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="first copy MIB MiB device to device once (a known-size reference for HBM byte counters)")
     args = ap.parse_args()
@@ -88,6 +91,7 @@ def main():
     log(f"uploaded{' and quantised' if wl.wtype != 'bf16' else ''} in {time.time() - t0:.1f}s")
     prompt = synth.gen_prompt(wl.prefill_len, dims.vocab_c0, wl.prompt_seed)
     sess = DarSession(dims, weights, wl.max_len, dev, graph=args.graph)
+    set_sampling(sess, dims, wl, args)
     stream = sess.stream
 
     # warmup: prefill, W frames (captures the graph), then start over
@@ -189,7 +193,7 @@ def main():
         "config": {"workload": wl.name, "batch": 1, "prefill": wl.prefill_len, "first_decode_position": wl.prefill_len,
                    "decode_frames": args.steps, "max_len": wl.max_len, "layers_slow": dims.n_layers_slow,
                    "layers_fast": dims.n_layers_fast, "residual_codebooks": dims.n_res,
-                   "graph": args.graph},
+                   "graph": args.graph, "sampling": SAMPLING if args.sample else None},
         "achieved_gb_s": round(gbs / 1e9, 1),
         "hbm_frac": round(gbs / HBM_PEAK, 4),
         "alg_bytes_per_frame_avg": int(alg_bytes // args.steps),
@@ -230,6 +234,7 @@ def bench_batched(args, wl):
         del host
     log(f"weights ready in {time.time() - t0:.1f}s; {B} prompts of {int(lens.min())}..{int(lens.max())} ids")
     sess = DarSession(dims, weights, wl.max_len, dev, graph=args.graph, batch=B)
+    set_sampling(sess, dims, wl, args)
     stream = sess.stream
     sess.prefill(prompts, want=False)
     for _ in range(args.warmup):
@@ -303,7 +308,8 @@ def bench_batched(args, wl):
         "data": "synthetic (seeded random-init weights, ragged random prompts)",
         "config": {"workload": wl.name, "batch": B, "prompt_lengths": [int(n) for n in lens], "max_len": wl.max_len,
                    "layers_slow": dims.n_layers_slow, "layers_fast": dims.n_layers_fast,
-                   "residual_codebooks": dims.n_res, "graph": args.graph},
+                   "residual_codebooks": dims.n_res, "graph": args.graph,
+                   "sampling": SAMPLING if args.sample else None},
         "achieved_gb_s": round(gbs / 1e9, 1), "hbm_frac": round(gbs / HBM_PEAK, 4),
         "alg_bytes_per_step_avg": int(alg_bytes // steps), "prefill_ms": round(prefill_ms, 2),
         "nonfinite_logits": n_bad, "roofline": roof, "cpu_baseline": cpu,
@@ -329,6 +335,19 @@ def measured_traffic(kind, workload):
     if hashlib.sha256(open(src, "rb").read()).hexdigest() != m_h.group(1):
         return None
     return int(m_t.group(1))
+
+
+SAMPLING = {"temperature": 0.8, "top_k": 50, "top_p": 0.9, "repetition_penalty": 1.2, "repetition_window": 16}
+
+
+def set_sampling(sess, dims, wl, args):
+    """With --sample: sampled codes, draws from a seeded table of uniforms."""
+    if not args.sample:
+        return
+    import synth
+    u = synth.gen_uniforms(wl.max_len, wl.batch, dims.n_res + 1, seed=3)
+    sess.set_sampling(SAMPLING["temperature"], SAMPLING["top_k"], SAMPLING["top_p"],
+                      SAMPLING["repetition_penalty"], SAMPLING["repetition_window"], u)
 
 
 def per_launch_bytes(dims, wtype, kind):
