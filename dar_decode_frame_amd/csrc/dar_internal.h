@@ -101,8 +101,8 @@ struct SampleArgs {
 };
 // dynamic LDS of one sampling workgroup over V logits
 inline size_t sample_lds_bytes(int V) {
-  return (((size_t)V * 4 + 15) & ~(size_t)15) + ((((size_t)V + 31) / 32 * 4 + 15) & ~(size_t)15) + 256 * 4 +
-         (size_t)kMaxTopK * 8 + 256 * 4 + 128;
+  return ((((size_t)V + 31) / 32 * 4 + 15) & ~(size_t)15) + (size_t)kWaves * 256 * 4 + (size_t)kMaxTopK * 8 +
+         256 * 4 + 128;
 }
 
 struct CommitArgs {

@@ -3,12 +3,15 @@
 // loop's top-p / top-k sampling with repetition windows (pyshine fish-speech
 // tour, "Why You Need This"; the reading is stated with SampleArgs):
 //   1. window codes marked in an LDS bitmap; each logit penalised if marked,
-//      then divided by the temperature, and stored as an order-preserving key;
+//      then divided by the temperature, and kept as an order-preserving key in
+//      registers (thread t owns the contiguous codes [t per, (t + 1) per));
 //   2. top-k: radix select of the k-th largest key, MSB first, 8 bits a pass
-//      (integer histograms, so the result does not depend on thread timing);
+//      (integer histograms, one per wave so that keys sharing their top byte
+//      spread their LDS atomics; the result does not depend on thread timing);
 //   3. the k candidates (larger keys, then equal keys by lower code) compacted
 //      with block scans and sorted by (value desc, code asc) with a bitonic
-//      network in LDS;
+//      network, one element per thread: lane shuffles within a wave, LDS and
+//      a barrier only for the strides of 64 and 128;
 //   4. exp(v - vmax) per candidate, a block scan for the running sums, then
 //      the top-p cut and the draw as counts over the running sums.
 #pragma once
@@ -73,15 +76,14 @@ __device__ __forceinline__ float sample_scan_incl(float v, float* red) {
 __device__ __forceinline__ int sample_row(const float* lg, int V, const SampleArgs& sp, float u, const int* hist,
                                           long long hist_stride, int nh, char* lds) {
   static_assert(kBlock == 256 && kMaxTopK == kBlock, "one candidate per thread, one histogram bin per thread");
+  constexpr int kPer = kMaxSampleVocab / kBlock;  // codes per thread at most
   const int tid = threadIdx.x;
   char* p = lds;
-  uint32_t* keys = reinterpret_cast<uint32_t*>(p);
-  p += ((size_t)V * 4 + 15) & ~(size_t)15;
   const int nwords = (V + 31) / 32;
   uint32_t* bits = reinterpret_cast<uint32_t*>(p);
   p += ((size_t)nwords * 4 + 15) & ~(size_t)15;
-  int* hcount = reinterpret_cast<int*>(p);
-  p += 256 * 4;
+  int* hcount = reinterpret_cast<int*>(p);  // [kWaves][256]
+  p += kWaves * 256 * 4;
   unsigned long long* cand = reinterpret_cast<unsigned long long*>(p);
   p += (size_t)kMaxTopK * 8;
   float* cum = reinterpret_cast<float*>(p);
@@ -98,29 +100,39 @@ __device__ __forceinline__ int sample_row(const float* lg, int V, const SampleAr
     if (c >= 0 && c < V) atomicOr(&bits[c >> 5], 1u << (c & 31));
   }
   __syncthreads();
-  for (int i = tid; i < V; i += kBlock) {
-    float v = lg[i];
-    if (v != v) v = -INFINITY;
-    if ((bits[i >> 5] >> (i & 31)) & 1u) v = v > 0.f ? v / sp.penalty : v * sp.penalty;
-    keys[i] = sample_key(v / sp.temperature);
+  const int per = (V + kBlock - 1) / kBlock;
+  const int i0 = min(tid * per, V), n_own = min(per, V - i0);
+  uint32_t kr[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    kr[j] = 0u;
+    if (j < n_own) {
+      const int i = i0 + j;
+      float v = lg[i];
+      if (v != v) v = -INFINITY;
+      if ((bits[i >> 5] >> (i & 31)) & 1u) v = v > 0.f ? v / sp.penalty : v * sp.penalty;
+      kr[j] = sample_key(v / sp.temperature);
+    }
   }
-  __syncthreads();
 
   // 2. the k-th largest key: digit by digit from the top, `want` = how many of
   // the keys matching the digits so far are still to be taken
   const int k = min(sp.top_k, V);
   uint32_t prefix = 0u, mask = 0u;
   int want = k;
+  int* hwave = hcount + (tid / kWave) * 256;
   for (int shift = 24; shift >= 0; shift -= 8) {
-    hcount[tid] = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) hcount[w * 256 + tid] = 0;
     __syncthreads();
-    for (int i = tid; i < V; i += kBlock) {
-      const uint32_t key = keys[i];
-      if ((key & mask) == prefix) atomicAdd(&hcount[(key >> shift) & 255u], 1);
-    }
+#pragma unroll
+    for (int j = 0; j < kPer; ++j)
+      if (j < n_own && (kr[j] & mask) == prefix) atomicAdd(&hwave[(kr[j] >> shift) & 255u], 1);
     __syncthreads();
     // thread t looks at digit 255 - t: the keys above it are the scan's prefix
-    const int c = hcount[255 - tid];
+    int c = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) c += hcount[w * 256 + 255 - tid];
     int tot;
     const int above = sample_scan_excl(c, red, &tot);
     if (above < want && above + c >= want) {
@@ -136,21 +148,23 @@ __device__ __forceinline__ int sample_row(const float* lg, int V, const SampleAr
   }
 
   // 3. candidates: the keys above the threshold, then `want` keys equal to it
-  // (lowest codes first); thread t scans codes [t per, (t + 1) per)
+  // (lowest codes first)
   const uint32_t T = prefix;
-  const int per = (V + kBlock - 1) / kBlock;
-  const int i0 = min(tid * per, V), i1 = min(i0 + per, V);
   int ngt = 0, neq = 0;
-  for (int i = i0; i < i1; ++i) {
-    const uint32_t key = keys[i];
-    ngt += key > T;
-    neq += key == T;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    if (j < n_own) {
+      ngt += kr[j] > T;
+      neq += kr[j] == T;
+    }
   }
   int tot_gt, tot_eq;
   int off_gt = sample_scan_excl(ngt, red, &tot_gt);
   int off_eq = sample_scan_excl(neq, red, &tot_eq);
-  for (int i = i0; i < i1; ++i) {
-    const uint32_t key = keys[i];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    if (j >= n_own) continue;
+    const uint32_t key = kr[j];
     int slot = -1;
     if (key > T) {
       slot = off_gt++;
@@ -159,23 +173,31 @@ __device__ __forceinline__ int sample_row(const float* lg, int V, const SampleAr
       ++off_eq;
     }
     // ascending order of (~key, code) = descending value, ascending code
-    if (slot >= 0) cand[slot] = ((unsigned long long)(~key) << 32) | (unsigned long long)(uint32_t)i;
+    if (slot >= 0) cand[slot] = ((unsigned long long)(~key) << 32) | (unsigned long long)(uint32_t)(i0 + j);
   }
   if (tid >= k) cand[tid] = ~0ull;
   __syncthreads();
+  // ascending sort, element tid in a register: at each compare-exchange the
+  // lower element of a pair keeps the minimum when its block of `size` runs up
+  unsigned long long x = cand[tid];
   for (int size = 2; size <= kMaxTopK; size <<= 1) {
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      const int j = tid ^ stride;
-      if (j > tid) {
-        const unsigned long long a = cand[tid], b = cand[j];
-        if ((a > b) == ((tid & size) == 0)) {
-          cand[tid] = b;
-          cand[j] = a;
-        }
+      unsigned long long y;
+      if (stride >= kWave) {
+        __syncthreads();  // every lane's previous value read
+        cand[tid] = x;
+        __syncthreads();
+        y = cand[tid ^ stride];
+      } else {
+        y = __shfl_xor(x, stride);
       }
-      __syncthreads();
+      const bool keep_min = ((tid & stride) == 0) == ((tid & size) == 0);
+      x = keep_min ? (x < y ? x : y) : (x < y ? y : x);
     }
   }
+  __syncthreads();
+  cand[tid] = x;
+  __syncthreads();
 
   // 4. probabilities, running sums, top-p cut, draw
   const bool valid = tid < k;
