@@ -168,10 +168,11 @@ def main():
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK, 4),
                 "traffic": measured_traffic(name, wl.name),
                 "bytes_per_launch": per, "avg_launch_us": round(avg_ms * 1000, 2), "launches_timed": len(one_row),
-                "overlapped_avg_launch_us": round(live_ms / live_n * 1000, 2), "overlapped_launches": live_n,
+                "overlapped_avg_launch_us": round(live_ms / live_n * 1000, 2) if live_n else None, "overlapped_launches": live_n,
                 "launches_per_frame": len(recs) // args.profile_frames, "frame_time_share": share}
         log(f"dominant kernel {name}: {avg_ms * 1000:.1f} us/launch serialised ({achieved / 1e9:.0f} GB/s), "
-            f"{live_ms / live_n * 1000:.1f} us beside the other chain; serialised-frame shares {share}")
+            + (f"{live_ms / live_n * 1000:.1f} us beside the other chain" if live_n else "no live timing (graph replay)")
+            + f"; serialised-frame shares {share}")
 
     cpu = None
     if not args.no_cpu_baseline:

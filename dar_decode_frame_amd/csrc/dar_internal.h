@@ -148,7 +148,19 @@ struct AttnArgs {
   int out_stride;
   const int* row_pos;       // non-null: position of query row m is row_pos[m] (else *pos + m)
   const int* row_seq;       // non-null: row m reads the cache of sequence row_seq[m]
-  long long seq_stride;     // elements between two sequences' caches
+  long long seq_stride;     // elements between two sequences' caches (paged: between two pages)
+  // Paged cache (page_table non-null): position p of sequence s lives in page
+  // page_table[s * pages_per_seq + (p >> page_shift)] at offset p & (2^page_shift - 1);
+  // cache_len is then the page length. A split never crosses a page (chunk <= page length).
+  const int* page_table;
+  int page_shift, pages_per_seq;
+  int seq0;                 // sequence of every row when row_seq is null (paged prefill)
+};
+
+// The same page map for the KV append of many-row stages.
+struct PageMap {
+  const int* table;         // nullptr: contiguous per-sequence caches
+  int shift, per_seq, seq0;
 };
 
 // y[m][n] (+)= scale[n] * sum_k x[m][k] W[n][k] for m < M, n < N (prefill
@@ -204,6 +216,7 @@ struct RowsCommitArgs {
   float* copy_dst[2];        // for i < copy_n[j]
   int copy_src_stride[2], copy_dst_stride[2], copy_n[2];
   int* anomalies;
+  const int* active;         // non-null: rows b with active[b] == 0 keep their position (free slots)
   SampleArgs smp;
 };
 
@@ -255,6 +268,7 @@ struct RopeRowsArgs {
   uint16_t* kc;
   uint16_t* vc;
   int cache_len;
+  PageMap pages;
 };
 struct SiluSplitArgs {
   const float* a;
@@ -267,6 +281,7 @@ struct SiluSplitArgs {
 struct IncRowsArgs {
   int* v;
   int n;
+  const int* active;     // non-null: only entries with active[i] != 0 advance
 };
 
 struct Task {
@@ -323,11 +338,24 @@ hipError_t launch_embed_rows(const uint16_t* table, int rows, int K, const int* 
 hipError_t launch_rope_rows(const float* qkv, int M, int p0, int n_heads_q, int n_heads_kv, int head_dim,
                             const float2* rope, float* q_out, uint16_t* kc, uint16_t* vc, int cache_len,
                             hipStream_t s, const int* row_pos = nullptr, const int* row_seq = nullptr,
-                            long long seq_stride = 0, PartSum src = PartSum{nullptr, 0, 0});
+                            long long seq_stride = 0, PartSum src = PartSum{nullptr, 0, 0},
+                            PageMap pages = PageMap{nullptr, 0, 0, 0});
 // argmax + commit of one codebook for B sequences (k_commit_rows)
 hipError_t launch_commit_rows(const RowsCommitArgs& a, hipStream_t s);
-// v[i] += 1 for i < n
-hipError_t launch_inc_rows(int* v, int n, hipStream_t s);
+// v[i] += 1 for i < n (only where active[i] != 0 when active is set)
+hipError_t launch_inc_rows(int* v, int n, hipStream_t s, const int* active = nullptr);
+// One slot of a paged context: its block-table row (row[0..per_seq) = pages,
+// unused entries the parking page 0), its positions (slow pos_s[b], frame
+// pos_f[b], first frame win_lo[b]) and its active flag, in one launch.
+constexpr int kMaxPagesPerSeq = 64;
+struct SlotState {
+  int b, per_seq;
+  int pages[kMaxPagesPerSeq];
+  int set_state;  // 0: the block-table row only
+  int pos_slow, pos_frame, win_lo, active;
+};
+hipError_t launch_slot_state(int* table, int* pos_s, int* pos_f, int* win_lo, int* active, const SlotState& st,
+                             hipStream_t s);
 // SiLU(a) * b as hi/lo bf16 rows (a, b: the sums pa, pb when those are set)
 hipError_t launch_silu_split(const float* a, const float* b, int M, int F, uint16_t* hh, uint16_t* hl,
                              hipStream_t s, PartSum pa = PartSum{nullptr, 0, 0}, PartSum pb = PartSum{nullptr, 0, 0});

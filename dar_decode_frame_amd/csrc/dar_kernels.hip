@@ -718,8 +718,19 @@ __device__ __forceinline__ void commit_body(const CommitArgs& a, char* lds) {
 __device__ __forceinline__ int attn_len(const AttnArgs& a, int m) {
   return (a.row_pos ? a.row_pos[m] : *a.pos + m) + 1;
 }
-__device__ __forceinline__ size_t attn_seq_offset(const AttnArgs& a, int m) {
-  return a.row_seq ? (size_t)a.row_seq[m] * a.seq_stride : 0;
+// Offset of the cache block holding position j0 of row m's sequence and, in
+// jb0, the first position that block holds: a sequence's whole cache
+// (jb0 = 0), or with a page table the page of j0 (positions j0 .. the page's
+// end are then at j - jb0 within it).
+__device__ __forceinline__ size_t attn_kv_base(const AttnArgs& a, int m, int j0, int& jb0) {
+  const int sq = a.row_seq ? a.row_seq[m] : a.seq0;
+  if (a.page_table) {
+    const int pi = j0 >> a.page_shift;
+    jb0 = pi << a.page_shift;
+    return (size_t)a.page_table[(size_t)sq * a.pages_per_seq + pi] * a.seq_stride;
+  }
+  jb0 = 0;
+  return (size_t)sq * a.seq_stride;
 }
 
 // ------------------------------------------------ split-K decode attention --
@@ -766,7 +777,9 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, int bid, char* lds)
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
   }
-  const size_t kv0 = attn_seq_offset(a, m) + (size_t)kvh * a.cache_len * HD + sub * 8;
+  // the split's positions lie in one cache block (a page never ends inside a split)
+  int jb0;
+  const size_t kv0 = attn_kv_base(a, m, j0, jb0) + (size_t)kvh * a.cache_len * HD + sub * 8;
   const uint16_t* Kb = a.K + kv0;
   const uint16_t* Vb = a.V + kv0;
   constexpr int STEP = kWaves * PPW;
@@ -777,8 +790,8 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, int bid, char* lds)
     for (int u = 0; u < U; ++u) {
       const int j = jb + u * STEP + grp;
       ok[u] = j < j1;
-      kk[u] = ok[u] ? ld16(Kb + (size_t)j * HD) : u32x4{0u, 0u, 0u, 0u};
-      vv[u] = ok[u] ? ld16(Vb + (size_t)j * HD) : u32x4{0u, 0u, 0u, 0u};
+      kk[u] = ok[u] ? ld16(Kb + (size_t)(j - jb0) * HD) : u32x4{0u, 0u, 0u, 0u};
+      vv[u] = ok[u] ? ld16(Vb + (size_t)(j - jb0) * HD) : u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -1309,7 +1322,10 @@ __device__ __forceinline__ void attn_wide_body(const AttnArgs& a, int bid, char*
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
   }
-  const size_t kv0 = attn_seq_offset(a, m) + (size_t)kvh * a.cache_len * HD + sub * 8;
+  // every position of a one-split launch lies in the first cache block (with
+  // a page table: T <= one split <= the page length)
+  int jb0;
+  const size_t kv0 = attn_kv_base(a, m, 0, jb0) + (size_t)kvh * a.cache_len * HD + sub * 8;
   const uint16_t* Kb = a.K + kv0;
   const uint16_t* Vb = a.V + kv0;
   for (int jb = wave * PPW; jb < T; jb += STEP * U) {
@@ -1809,14 +1825,14 @@ static bool row_stage(const Task& t, hipStream_t s, hipError_t& e) {
     case T_ROPE_ROWS: {
       const RopeRowsArgs& a = t.rope;
       e = launch_rope_rows(a.qkv, a.M, 0, a.n_heads_q, a.n_heads_kv, a.head_dim, a.rope, a.q_out, a.kc, a.vc,
-                           a.cache_len, s, a.row_pos, a.row_seq, a.seq_stride, a.src);
+                           a.cache_len, s, a.row_pos, a.row_seq, a.seq_stride, a.src, a.pages);
       return true;
     }
     case T_SILU_SPLIT:
       e = launch_silu_split(t.silu.a, t.silu.b, t.silu.M, t.silu.F, t.silu.hh, t.silu.hl, s, t.silu.pa, t.silu.pb);
       return true;
     case T_COMMIT_ROWS: e = launch_commit_rows(t.rows, s); return true;
-    case T_INC_ROWS: e = launch_inc_rows(t.inc.v, t.inc.n, s); return true;
+    case T_INC_ROWS: e = launch_inc_rows(t.inc.v, t.inc.n, s, t.inc.active); return true;
     default: return false;
   }
 }

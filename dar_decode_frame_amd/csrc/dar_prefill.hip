@@ -525,17 +525,27 @@ __global__ __launch_bounds__(kBlock) void k_embed_rows(const uint16_t* table, in
 // RoPE at positions p0 + m (or row_pos[m]) on q and k of the rows' QKV output
 // (or of the pending split-K sums src), q to q_out, k and v appended to the
 // bf16 caches (rotate-half pairs (i, i + hd/2)); with row_seq, row m appends
-// to sequence row_seq[m]'s cache. One wave per (row, head), lane i: pair i.
+// to sequence row_seq[m]'s cache; with a page map, position p of sequence s
+// goes to page table[s][p >> shift] (seq_stride elements per page) at offset
+// p within the page. One wave per (row, head), lane i: pair i.
 __global__ __launch_bounds__(kWave) void k_rope_rows(const float* qkv, PartSum src, int M, int p0,
                                                       const int* row_pos, const int* row_seq, long long seq_stride,
                                                       int n_heads_q, int n_heads_kv, int head_dim, const float2* rope,
-                                                      float* q_out, uint16_t* kc, uint16_t* vc, int cache_len) {
+                                                      float* q_out, uint16_t* kc, uint16_t* vc, int cache_len,
+                                                      PageMap pm) {
   const int m = blockIdx.x, head = blockIdx.y, i = threadIdx.x;
   const int half = head_dim / 2;
   if (i >= half) return;
   const int width = (n_heads_q + 2 * n_heads_kv) * head_dim;
-  const int pos = row_pos ? row_pos[m] : p0 + m;
-  if (row_seq) {
+  const int pos_abs = row_pos ? row_pos[m] : p0 + m;
+  int pos = pos_abs;  // position within the cache block written
+  if (pm.table) {
+    const int sq = row_seq ? row_seq[m] : pm.seq0;
+    const size_t page = (size_t)pm.table[(size_t)sq * pm.per_seq + (pos_abs >> pm.shift)];
+    kc += page * seq_stride;
+    vc += page * seq_stride;
+    pos = pos_abs & ((1 << pm.shift) - 1);
+  } else if (row_seq) {
     kc += (size_t)row_seq[m] * seq_stride;
     vc += (size_t)row_seq[m] * seq_stride;
   }
@@ -554,7 +564,7 @@ __global__ __launch_bounds__(kWave) void k_rope_rows(const float* qkv, PartSum s
     v = qkv[(size_t)m * width + r2];
   }
   if (head < n_heads_q + n_heads_kv) {
-    const float2 cs = rope[(size_t)pos * half + i];
+    const float2 cs = rope[(size_t)pos_abs * half + i];
     const float o1 = u * cs.x - v * cs.y;
     const float o2 = u * cs.y + v * cs.x;
     if (head < n_heads_q) {
@@ -661,12 +671,24 @@ __global__ __launch_bounds__(kBlock) void k_commit_rows(RowsCommitArgs a) {
     }
   }
   __syncthreads();
-  if (a.pos_inc && tid == 0) a.pos_inc[b] = a.pos_inc[b] + 1;
+  if (a.pos_inc && tid == 0 && (!a.active || a.active[b])) a.pos_inc[b] = a.pos_inc[b] + 1;
 }
 
-__global__ void k_inc_rows(int* v, int n) {
+__global__ void k_inc_rows(int* v, int n, const int* active) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) v[i] = v[i] + 1;
+  if (i < n && (!active || active[i])) v[i] = v[i] + 1;
+}
+
+// one slot of a paged context: block-table row, positions, active flag
+__global__ void k_slot_state(int* table, int* pos_s, int* pos_f, int* win_lo, int* active, SlotState st) {
+  const int i = threadIdx.x;
+  if (i < st.per_seq) table[(size_t)st.b * st.per_seq + i] = st.pages[i];
+  if (i == 0 && st.set_state) {
+    pos_s[st.b] = st.pos_slow;
+    pos_f[st.b] = st.pos_frame;
+    win_lo[st.b] = st.win_lo;
+    active[st.b] = st.active;
+  }
 }
 
 hipError_t gemm_dispatch(int wtype, const GemmArgs& a, int mt, dim3 grid, hipStream_t s) {
@@ -783,15 +805,22 @@ hipError_t launch_embed_rows(const uint16_t* table, int rows, int K, const int* 
 hipError_t launch_rope_rows(const float* qkv, int M, int p0, int n_heads_q, int n_heads_kv, int head_dim,
                             const float2* rope, float* q_out, uint16_t* kc, uint16_t* vc, int cache_len,
                             hipStream_t s, const int* row_pos, const int* row_seq, long long seq_stride,
-                            PartSum src) {
+                            PartSum src, PageMap pages) {
   if (head_dim / 2 > kWave) return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_rope_rows, dim3(M, n_heads_q + 2 * n_heads_kv), dim3(kWave), 0, s, qkv, src, M, p0, row_pos,
-                     row_seq, seq_stride, n_heads_q, n_heads_kv, head_dim, rope, q_out, kc, vc, cache_len);
+                     row_seq, seq_stride, n_heads_q, n_heads_kv, head_dim, rope, q_out, kc, vc, cache_len, pages);
   return hipGetLastError();
 }
 
-hipError_t launch_inc_rows(int* v, int n, hipStream_t s) {
-  hipLaunchKernelGGL(k_inc_rows, dim3((n + kBlock - 1) / kBlock), dim3(kBlock), 0, s, v, n);
+hipError_t launch_inc_rows(int* v, int n, hipStream_t s, const int* active) {
+  hipLaunchKernelGGL(k_inc_rows, dim3((n + kBlock - 1) / kBlock), dim3(kBlock), 0, s, v, n, active);
+  return hipGetLastError();
+}
+
+hipError_t launch_slot_state(int* table, int* pos_s, int* pos_f, int* win_lo, int* active, const SlotState& st,
+                             hipStream_t s) {
+  if (st.per_seq < 1 || st.per_seq > kMaxPagesPerSeq || st.b < 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_slot_state, dim3(1), dim3(kMaxPagesPerSeq), 0, s, table, pos_s, pos_f, win_lo, active, st);
   return hipGetLastError();
 }
 

@@ -69,6 +69,15 @@ struct Layout {
   size_t bgp_floats[2];
   int nsplit_slow, chunk, rope_len, seq_len, vmax, fast_len, nslots;
   int chunk_rows, nsplit_rows;  // batched slow attention: positions per split, most splits
+  // paged slow KV (page_len > 0): K/V pools [L_s][n_pages][n_kv][page_len][hd],
+  // block table [max_batch][pages_per_seq], active flags [max_batch]
+  int page_len, page_shift, n_pages, pages_per_seq;
+  size_t ptable, active;
+};
+
+// Paging of a context (page_len 0: one contiguous cache per sequence).
+struct Paging {
+  int page_len, n_pages;
 };
 
 // the kernels' weight type of a dar_wtype (callers have validated it)
@@ -85,8 +94,14 @@ bool has_scales(int32_t wtype) {
   return wtype == DAR_WTYPE_FP8_E4M3_ROW || wtype == DAR_WTYPE_INT8_ROW || wtype == DAR_WTYPE_INT4_G128;
 }
 
-Layout make_layout(const dar_config* c) {
+Layout make_layout(const dar_config* c, Paging pg = Paging{0, 0}) {
   Layout L{};
+  L.page_len = pg.page_len;
+  L.n_pages = pg.n_pages;
+  if (pg.page_len > 0) {
+    while ((1 << L.page_shift) < pg.page_len) ++L.page_shift;
+    L.pages_per_seq = (c->max_len + pg.page_len - 1) / pg.page_len;
+  }
   const int d = c->d_model, qw = c->n_heads_q * c->head_dim, F = c->ffn_dim;
   const int g = c->n_heads_q / c->n_heads_kv;
   const int fc = frame_codes(c);
@@ -130,7 +145,9 @@ Layout make_layout(const dar_config* c) {
   L.seqpos = take(sizeof(int) * L.seq_len);
   L.ring = take(sizeof(int) * (size_t)c->max_len * B * fc);
   L.rope = take(sizeof(float) * 2 * (size_t)L.rope_len * (c->head_dim / 2));
-  const size_t kv_slow = (size_t)c->n_layers_slow * B * c->n_heads_kv * c->max_len * c->head_dim * 2;
+  const size_t kv_slow = pg.page_len > 0
+                             ? (size_t)c->n_layers_slow * pg.n_pages * c->n_heads_kv * pg.page_len * c->head_dim * 2
+                             : (size_t)c->n_layers_slow * B * c->n_heads_kv * c->max_len * c->head_dim * 2;
   L.ks = take(kv_slow);
   L.vs = take(kv_slow);
   const size_t kv_fast =
@@ -171,6 +188,10 @@ Layout make_layout(const dar_config* c) {
     }
     // sequence ids [B], first-pass positions and sequences [2B], pass positions [R+1][B]
     L.rows = take(sizeof(int) * (size_t)(B + 4 * B + (c->n_res + 1) * B));
+  }
+  if (pg.page_len > 0) {
+    L.ptable = take(sizeof(int) * (size_t)B * L.pages_per_seq);
+    L.active = take(sizeof(int) * (size_t)B);
   }
   L.total = off;
   return L;
@@ -298,6 +319,14 @@ struct dar_ctx {
   std::vector<int> pos_init;   // host staging of the positions set by a prefill
   float2* rope;
   uint16_t *ks, *vs, *kf, *vf;
+
+  // paged slow KV and continuous batching (dar_create_paged)
+  bool paged = false;
+  int* ptable = nullptr;        // device block table [B][pages_per_seq]
+  int* active = nullptr;        // device flags [B]: slot holds a sequence
+  std::vector<int> free_pages;  // host allocator: pages not held by a slot (page 0 never: parking)
+  std::vector<std::vector<int>> slot_pages;  // pages of each slot, in position order
+  std::vector<char> slot_on;    // host mirror of active
 
   int pos_host = 0;       // slow position of the next frame to decode
   int attn_splits_live = 0;  // batched slow attention splits for the coming frame (0: all)
@@ -616,7 +645,8 @@ Task t_gemm(int wtype, const void* W, const float* scale, int N, int K, int M, c
 // seq_stride elements apart).
 void add_layer_rows(dar_ctx* c, std::vector<TaskRec>& out, int ch, const dar_layer_weights& w, int tag, int M,
                     const int* row_pos, const int* row_seq, uint16_t* kc, uint16_t* vc, int cache_len,
-                    long long seq_stride, int nsplit_max, int chunk, PartSum& pend, bool defer_w2) {
+                    long long seq_stride, int nsplit_max, int chunk, PartSum& pend, bool defer_w2,
+                    PageMap pm = PageMap{nullptr, 0, 0, 0}) {
   const dar_config& g = c->cfg;
   const int d = g.d_model, qw = g.n_heads_q * g.head_dim, F = g.ffn_dim;
   const int qkv_rows = (g.n_heads_q + 2 * g.n_heads_kv) * g.head_dim;
@@ -636,7 +666,7 @@ void add_layer_rows(dar_ctx* c, std::vector<TaskRec>& out, int ch, const dar_lay
   t.kind = T_ROPE_ROWS;
   t.M = M;
   t.rope = RopeRowsArgs{nullptr, sums(gp, qkv_rows, d), M, row_pos, row_seq, seq_stride, g.n_heads_q, g.n_heads_kv,
-                        g.head_dim, c->rope, cn.q, kc, vc, cache_len};
+                        g.head_dim, c->rope, cn.q, kc, vc, cache_len, pm};
   out.push_back(rec(t, K_OTHER, tag));
   t = none_task();
   t.kind = T_ATTN;
@@ -660,6 +690,9 @@ void add_layer_rows(dar_ctx* c, std::vector<TaskRec>& out, int ch, const dar_lay
   aa.row_pos = row_pos;
   aa.row_seq = row_seq;
   aa.seq_stride = seq_stride;
+  aa.page_table = pm.table;
+  aa.page_shift = pm.shift;
+  aa.pages_per_seq = pm.per_seq;
   out.push_back(rec(t, K_ATTN, tag));
   if (nsplit_max > 1) {
     t.kind = T_COMBINE;
@@ -691,12 +724,24 @@ std::vector<TaskRec> slow_chain_rows(dar_ctx* c) {
   const dar_config& g = c->cfg;
   const int B = c->B, d = g.d_model;
   std::vector<TaskRec> out;
-  const long long seq_stride = (long long)g.n_heads_kv * g.max_len * g.head_dim;
   PartSum pend = kNoSums;  // the layer's residual sums, added by the next norm
-  for (int l = 0; l < g.n_layers_slow; ++l)
-    add_layer_rows(c, out, 0, c->slow[l], l, B, c->pos_s, c->seq_ident, c->ks + (size_t)l * B * seq_stride,
-                   c->vs + (size_t)l * B * seq_stride, g.max_len, seq_stride, c->L.nsplit_rows, c->L.chunk_rows, pend,
-                   true);
+  if (c->paged) {
+    // a page holds page_len positions of every KV head; row b's positions go
+    // through its block-table row
+    const Layout& L = c->L;
+    const long long page_stride = (long long)g.n_heads_kv * L.page_len * g.head_dim;
+    const PageMap pm{c->ptable, L.page_shift, L.pages_per_seq, 0};
+    for (int l = 0; l < g.n_layers_slow; ++l)
+      add_layer_rows(c, out, 0, c->slow[l], l, B, c->pos_s, c->seq_ident,
+                     c->ks + (size_t)l * L.n_pages * page_stride, c->vs + (size_t)l * L.n_pages * page_stride,
+                     L.page_len, page_stride, L.nsplit_rows, L.chunk_rows, pend, true, pm);
+  } else {
+    const long long seq_stride = (long long)g.n_heads_kv * g.max_len * g.head_dim;
+    for (int l = 0; l < g.n_layers_slow; ++l)
+      add_layer_rows(c, out, 0, c->slow[l], l, B, c->pos_s, c->seq_ident, c->ks + (size_t)l * B * seq_stride,
+                     c->vs + (size_t)l * B * seq_stride, g.max_len, seq_stride, c->L.nsplit_rows, c->L.chunk_rows,
+                     pend, true);
+  }
   out.push_back(
       rec(t_norm(c->cs.x, d, B, d, c->slow_fn, g.rms_eps, c->bxh[0], c->bxl[0], c->ht, pend), K_OTHER, 0));
   out.push_back(rec(t_gemm(W_BF16, c->w0, nullptr, g.vocab_c0, d, B, c->bxh[0], c->bxl[0], c->logits0, g.vocab_c0, 0,
@@ -704,7 +749,7 @@ std::vector<TaskRec> slow_chain_rows(dar_ctx* c) {
                     K_HEAD, 0));
   Task t = none_task();
   t.kind = T_INC_ROWS;
-  t.inc = IncRowsArgs{c->pos_s, B};
+  t.inc = IncRowsArgs{c->pos_s, B, c->active};
   out.push_back(rec(t, K_OTHER, 0));
   return out;
 }
@@ -726,6 +771,7 @@ RowsCommitArgs rows_commit(dar_ctx* c, int k, const float* logits, int ld, int V
   r.pos = c->pos_f;
   r.K = g.d_model;
   r.anomalies = c->flags + 1;
+  r.active = c->active;
   r.smp = c->smp;
   return r;
 }
@@ -831,6 +877,7 @@ void set_live_attention(dar_ctx* c, int tmax) {
       break;
     }
   }
+  if (c->paged) chunk = std::min(chunk, c->L.page_len);  // a split stays within one page
   c->attn_chunk_live = chunk;
   c->attn_splits_live = (tmax + chunk - 1) / chunk;
 }
@@ -979,6 +1026,9 @@ int prefill_blocks(dar_ctx* c, const int32_t* tokens, int n, hipStream_t s, int 
   float* pgp = reinterpret_cast<float*>(b + L.pgp);
   int* ppos = reinterpret_cast<int*>(b + L.ppos);
   const size_t per_layer = (size_t)g.n_heads_kv * g.max_len * g.head_dim;
+  // paged: the layer's page pool, positions through sequence seq's block-table row
+  const long long page_stride = (long long)g.n_heads_kv * L.page_len * g.head_dim;
+  const PageMap pm = c->paged ? PageMap{c->ptable, L.page_shift, L.pages_per_seq, seq} : PageMap{nullptr, 0, 0, 0};
   float* pgp2 = pgp + L.pgp_floats;  // second region: W3's sums beside W1's
   auto gemm = [&](const void* W, const float* scale, int N, int K, int M, float* y, int acc, float* part,
                   int defer) {
@@ -1009,16 +1059,19 @@ int prefill_blocks(dar_ctx* c, const int32_t* tokens, int n, hipStream_t s, int 
     PartSum pend{nullptr, 0, 0};  // the previous layer's residual sums
     for (int l = 0; l < g.n_layers_slow; ++l) {
       const dar_layer_weights& w = c->slow[l];
-      uint16_t* kc = c->ks + ((size_t)l * c->B + seq) * per_layer;  // layer l of sequence seq
-      uint16_t* vc = c->vs + ((size_t)l * c->B + seq) * per_layer;
+      uint16_t* kc = c->paged ? c->ks + (size_t)l * L.n_pages * page_stride
+                              : c->ks + ((size_t)l * c->B + seq) * per_layer;  // layer l of sequence seq
+      uint16_t* vc = c->paged ? c->vs + (size_t)l * L.n_pages * page_stride
+                              : c->vs + ((size_t)l * c->B + seq) * per_layer;
+      const int cache_len = c->paged ? L.page_len : g.max_len;
       DAR_HIP(c,
               launch_norm_split(px, d, M, d, static_cast<const uint16_t*>(w.attn_norm), g.rms_eps, xh, xl, s, nullptr,
                                 pend),
               "prefill attn norm");
       DAR_HIP(c, gemm(w.wqkv, w.wqkv_scale, qkv_rows, d, M, nullptr, 0, pgp, 1), "prefill qkv");
       DAR_HIP(c,
-              launch_rope_rows(nullptr, M, p0, g.n_heads_q, g.n_heads_kv, g.head_dim, c->rope, pq, kc, vc, g.max_len,
-                               s, nullptr, nullptr, 0, sums(pgp, qkv_rows, d, M)),
+              launch_rope_rows(nullptr, M, p0, g.n_heads_q, g.n_heads_kv, g.head_dim, c->rope, pq, kc, vc, cache_len,
+                               s, nullptr, nullptr, c->paged ? page_stride : 0, sums(pgp, qkv_rows, d, M), pm),
               "prefill rope");
       Task t{};
       t.kind = T_ATTN;
@@ -1028,7 +1081,14 @@ int prefill_blocks(dar_ctx* c, const int32_t* tokens, int n, hipStream_t s, int 
       aa.q_stride = qw;
       aa.K = kc;
       aa.V = vc;
-      aa.cache_len = g.max_len;
+      aa.cache_len = cache_len;
+      if (c->paged) {
+        aa.seq_stride = page_stride;
+        aa.page_table = pm.table;
+        aa.page_shift = pm.shift;
+        aa.pages_per_seq = pm.per_seq;
+        aa.seq0 = seq;
+      }
       aa.pos = ppos;
       aa.n_heads_q = g.n_heads_q;
       aa.n_heads_kv = g.n_heads_kv;
@@ -1090,8 +1150,72 @@ int dar_workspace_bytes(const dar_config* cfg, size_t* bytes_out) {
   return DAR_OK;
 }
 
+namespace {
+
+// Paging parameters: page_len a power of two in [64, 2^20], at most
+// kMaxPagesPerSeq pages per sequence, page 0 reserved, the many-row path.
+int validate_paging(const dar_config* cfg, const dar_paging* pg, std::string& why) {
+  if (!pg) {
+    why = "paging is NULL";
+    return DAR_E_INVAL;
+  }
+  const int P = pg->page_len;
+  if (P < kAttnChunkDefault || P > (1 << 20) || (P & (P - 1))) {
+    why = "page_len must be a power of two in [64, 2^20]";
+    return DAR_E_INVAL;
+  }
+  if (pg->n_pages < 2) {
+    why = "n_pages must be >= 2 (page 0 parks free slots)";
+    return DAR_E_INVAL;
+  }
+  if ((cfg->max_len + P - 1) / P > kMaxPagesPerSeq) {
+    why = "max_len / page_len above 64 pages per sequence";
+    return DAR_E_UNSUPPORTED;
+  }
+  if (cfg->max_batch < 2) {
+    why = "a paged context needs max_batch >= 2";
+    return DAR_E_UNSUPPORTED;
+  }
+  return DAR_OK;
+}
+
+int create_impl(const dar_config* cfg, const dar_weights* w, void* workspace, size_t ws_bytes, void* stream,
+                const dar_paging* paging, dar_ctx** ctx_out);
+
+}  // namespace
+
 int dar_create(const dar_config* cfg, const dar_weights* w, void* workspace, size_t ws_bytes, void* stream,
                dar_ctx** ctx_out) {
+  return create_impl(cfg, w, workspace, ws_bytes, stream, nullptr, ctx_out);
+}
+
+int dar_workspace_bytes_paged(const dar_config* cfg, const dar_paging* paging, size_t* bytes_out) {
+  std::string why;
+  int st = validate_config(cfg, why);
+  if (st == DAR_OK) st = validate_paging(cfg, paging, why);
+  if (st != DAR_OK) {
+    g_create_error = why;
+    return st;
+  }
+  if (!bytes_out) return DAR_E_INVAL;
+  *bytes_out = make_layout(cfg, Paging{paging->page_len, paging->n_pages}).total;
+  return DAR_OK;
+}
+
+int dar_create_paged(const dar_config* cfg, const dar_paging* paging, const dar_weights* w, void* workspace,
+                     size_t ws_bytes, void* stream, dar_ctx** ctx_out) {
+  if (!paging) {
+    g_create_error = "paging is NULL";
+    if (ctx_out) *ctx_out = nullptr;
+    return DAR_E_INVAL;
+  }
+  return create_impl(cfg, w, workspace, ws_bytes, stream, paging, ctx_out);
+}
+
+namespace {
+
+int create_impl(const dar_config* cfg, const dar_weights* w, void* workspace, size_t ws_bytes, void* stream,
+                const dar_paging* paging, dar_ctx** ctx_out) {
   std::string why;
   if (!ctx_out) {
     g_create_error = "ctx_out is NULL";
@@ -1099,6 +1223,7 @@ int dar_create(const dar_config* cfg, const dar_weights* w, void* workspace, siz
   }
   *ctx_out = nullptr;
   int st = validate_config(cfg, why);
+  if (st == DAR_OK && paging) st = validate_paging(cfg, paging, why);
   if (st != DAR_OK) {
     g_create_error = why;
     return st;
@@ -1111,7 +1236,7 @@ int dar_create(const dar_config* cfg, const dar_weights* w, void* workspace, siz
     g_create_error = "workspace is NULL or not 256-byte aligned";
     return DAR_E_INVAL;
   }
-  const Layout L = make_layout(cfg);
+  const Layout L = make_layout(cfg, paging ? Paging{paging->page_len, paging->n_pages} : Paging{0, 0});
   if (ws_bytes < L.total) {
     g_create_error = "workspace smaller than dar_workspace_bytes()";
     return DAR_E_WORKSPACE;
@@ -1200,6 +1325,14 @@ int dar_create(const dar_config* cfg, const dar_weights* w, void* workspace, siz
     c->p1_seq = c->p1_pos + 2 * c->B;
     c->pk_pos = c->p1_seq + 2 * c->B;
   }
+  if (paging) {
+    c->paged = true;
+    c->ptable = reinterpret_cast<int*>(b + L.ptable);
+    c->active = reinterpret_cast<int*>(b + L.active);
+    for (int p = L.n_pages - 1; p >= 1; --p) c->free_pages.push_back(p);  // handed out from page 1 up
+    c->slot_pages.assign(c->B, {});
+    c->slot_on.assign(c->B, 0);
+  }
   c->seqpos = reinterpret_cast<int*>(b + L.seqpos);
   c->ring = reinterpret_cast<int*>(b + L.ring);
   c->rope = reinterpret_cast<float2*>(b + L.rope);
@@ -1270,6 +1403,10 @@ int dar_create(const dar_config* cfg, const dar_weights* w, void* workspace, siz
   if (!rows.empty() && (e = hipMemcpyAsync(c->seq_ident, rows.data(), rows.size() * sizeof(int),
                                            hipMemcpyHostToDevice, c->stream)) != hipSuccess)
     return fail(e, "upload rows");
+  // paged: every slot free, its block-table row on the parking page
+  if (c->paged && ((e = launch_fill_i32(c->ptable, c->B * L.pages_per_seq, 0, c->stream)) != hipSuccess ||
+                   (e = launch_fill_i32(c->active, c->B, 0, c->stream)) != hipSuccess))
+    return fail(e, "clear block table");
   if ((e = hipStreamSynchronize(c->stream)) != hipSuccess) return fail(e, "synchronize create");
   if ((e = hipEventRecord(c->ev_s_done, c->cs.s)) != hipSuccess) return fail(e, "record event");
   if ((e = hipEventRecord(c->ev_f_done, c->cf.s)) != hipSuccess) return fail(e, "record event");
@@ -1277,9 +1414,179 @@ int dar_create(const dar_config* cfg, const dar_weights* w, void* workspace, siz
   return DAR_OK;
 }
 
+// ---- paged contexts: continuous batching over a shared pool of KV pages
+
+// One launch on the slow stream: slot b's block-table row (its pages, the
+// parking page 0 beyond them) and, with set_state, its positions and flag.
+hipError_t slot_update(dar_ctx* c, int b, bool set_state, int pos_slow, int pos_frame, int win_lo, int active) {
+  SlotState st{};
+  st.b = b;
+  st.per_seq = c->L.pages_per_seq;
+  for (int i = 0; i < st.per_seq; ++i)
+    st.pages[i] = i < (int)c->slot_pages[b].size() ? c->slot_pages[b][i] : 0;
+  st.set_state = set_state ? 1 : 0;
+  st.pos_slow = pos_slow;
+  st.pos_frame = pos_frame;
+  st.win_lo = win_lo;
+  st.active = active;
+  return launch_slot_state(c->ptable, c->pos_s, c->pos_f, c->win_lo, c->active, st, c->cs.s);
+}
+
+// the slow stream starts after the caller's queued work and the last fast chain
+int slow_stream_begin(dar_ctx* c) {
+  DAR_HIP(c, hipEventRecord(c->ev_start, c->stream), "record start");
+  DAR_HIP(c, hipStreamWaitEvent(c->cs.s, c->ev_start, 0), "wait start");
+  DAR_HIP(c, hipStreamWaitEvent(c->cs.s, c->ev_f_done, 0), "wait fast chain");
+  return DAR_OK;
+}
+
+// ... and the caller's stream waits for it
+int slow_stream_end(dar_ctx* c) {
+  DAR_HIP(c, hipEventRecord(c->ev_s_done, c->cs.s), "record slow done");
+  DAR_HIP(c, hipStreamWaitEvent(c->stream, c->ev_s_done, 0), "join slow");
+  return DAR_OK;
+}
+
+// A frame of every active slot: slot b returns its frame at position
+// pos_hb[b] and its slow step runs at pos_hb[b] + 1, whose page is taken from
+// the pool first when the sequence enters a new page.
+int paged_frame(dar_ctx* c, const int32_t* forced, int32_t* codes_out, float* logits_out) {
+  const int P = c->L.page_len;
+  int n_active = 0, need = 0, tmax = 1;
+  for (int b = 0; b < c->B; ++b) {
+    if (!c->slot_on[b]) continue;
+    ++n_active;
+    const int next = c->pos_hb[b] + 1;
+    if (next >= c->cfg.max_len) {
+      c->err = "slot " + std::to_string(b) + " reached max_len - 1 (remove it with dar_seq_remove)";
+      return DAR_E_CAPACITY;
+    }
+    if (next / P >= (int)c->slot_pages[b].size()) ++need;
+    tmax = std::max(tmax, next + 1);
+  }
+  if (n_active == 0) {
+    c->err = "no sequence in the context (dar_seq_add)";
+    return DAR_E_STATE;
+  }
+  if (need > (int)c->free_pages.size()) {
+    c->err = "KV page pool exhausted: " + std::to_string(need) + " pages needed, " +
+             std::to_string(c->free_pages.size()) + " free";
+    return DAR_E_CAPACITY;
+  }
+  // new pages go into the block table on the slow stream, after the previous
+  // slow step and before this frame's
+  for (int b = 0; b < c->B; ++b) {
+    if (!c->slot_on[b] || (c->pos_hb[b] + 1) / P < (int)c->slot_pages[b].size()) continue;
+    c->slot_pages[b].push_back(c->free_pages.back());
+    c->free_pages.pop_back();
+    DAR_HIP(c, slot_update(c, b, false, 0, 0, 0, 0), "block table");
+  }
+  set_live_attention(c, tmax);
+  const int st = pipeline_step(c, forced, codes_out, logits_out, true);
+  if (st != DAR_OK) return st;
+  for (int b = 0; b < c->B; ++b)
+    if (c->slot_on[b]) c->pos_hb[b] += 1;
+  return DAR_OK;
+}
+
+}  // namespace
+
+int dar_seq_add(dar_ctx* c, int32_t slot, const int32_t* tokens, int32_t len) {
+  if (!c) return DAR_E_INVAL;
+  if (!c->paged) {
+    c->err = "dar_seq_add needs a paged context (dar_create_paged)";
+    return DAR_E_STATE;
+  }
+  if (slot < 0 || slot >= c->B || !tokens || len < 1) {
+    c->err = "slot out of range, tokens NULL or len < 1";
+    return DAR_E_INVAL;
+  }
+  if (c->slot_on[slot]) {
+    c->err = "slot already holds a sequence";
+    return DAR_E_STATE;
+  }
+  if (len >= c->cfg.max_len) {
+    c->err = "prompt length must be below max_len";
+    return DAR_E_CAPACITY;
+  }
+  const int P = c->L.page_len;
+  const int need = (len + P - 1) / P;
+  if (need > (int)c->free_pages.size()) {
+    c->err = "KV page pool exhausted: " + std::to_string(need) + " pages needed, " +
+             std::to_string(c->free_pages.size()) + " free";
+    return DAR_E_CAPACITY;
+  }
+  const dar_config& g = c->cfg;
+  const int d = g.d_model;
+  for (int i = 0; i < need; ++i) {
+    c->slot_pages[slot].push_back(c->free_pages.back());
+    c->free_pages.pop_back();
+  }
+  c->slot_on[slot] = 1;
+  int st = slow_stream_begin(c);
+  if (st != DAR_OK) return st;
+  hipStream_t s = c->cs.s;
+  // frame 0 sits at the last prompt position len - 1; the next slow step at len
+  DAR_HIP(c, slot_update(c, slot, true, len, len - 1, len - 1, 1), "slot state");
+  st = prefill_blocks(c, tokens, len, s, slot);
+  if (st != DAR_OK) return st;
+  // the codebook-0 head on the slot's last prompt position (h_t kept for the fast AR)
+  DAR_HIP(c,
+          launch_task(c->wq, t_norm(c->cs.x + (size_t)slot * d, d, 1, d, c->slow_fn, g.rms_eps, c->bxh[0], c->bxl[0],
+                                    c->ht + (size_t)slot * d),
+                      s),
+          "slot head norm");
+  DAR_HIP(c,
+          launch_task(c->wq, t_gemm(W_BF16, c->w0, nullptr, g.vocab_c0, d, 1, c->bxh[0], c->bxl[0],
+                                    c->logits0 + (size_t)slot * g.vocab_c0, g.vocab_c0, 0, c->bgp[0],
+                                    c->L.bgp_floats[0]),
+                      s),
+          "slot head");
+  st = slow_stream_end(c);
+  if (st != DAR_OK) return st;
+  c->pos_hb[slot] = len - 1;
+  c->prefilled = true;
+  return DAR_OK;
+}
+
+int dar_seq_remove(dar_ctx* c, int32_t slot) {
+  if (!c) return DAR_E_INVAL;
+  if (!c->paged) {
+    c->err = "dar_seq_remove needs a paged context (dar_create_paged)";
+    return DAR_E_STATE;
+  }
+  if (slot < 0 || slot >= c->B) {
+    c->err = "slot out of range";
+    return DAR_E_INVAL;
+  }
+  if (!c->slot_on[slot]) {
+    c->err = "slot holds no sequence";
+    return DAR_E_STATE;
+  }
+  int st = slow_stream_begin(c);
+  if (st != DAR_OK) return st;
+  // the pages return to the pool; the slot parks at position 0 of page 0
+  for (int p : c->slot_pages[slot]) c->free_pages.push_back(p);
+  c->slot_pages[slot].clear();
+  c->slot_on[slot] = 0;
+  c->pos_hb[slot] = 0;
+  DAR_HIP(c, slot_update(c, slot, true, 0, 0, 0, 0), "slot state");
+  return slow_stream_end(c);
+}
+
+int dar_pages_free(const dar_ctx* c, int32_t* n_free) {
+  if (!c || !n_free) return DAR_E_INVAL;
+  *n_free = c->paged ? (int32_t)c->free_pages.size() : 0;
+  return DAR_OK;
+}
+
 int dar_prefill(dar_ctx* c, int32_t batch, const int32_t* tokens, const int32_t* lens_host, const int32_t* forced,
                 int32_t* codes_out, float* logits_out) {
   if (!c) return DAR_E_INVAL;
+  if (c->paged) {
+    c->err = "a paged context takes its sequences one at a time (dar_seq_add)";
+    return DAR_E_STATE;
+  }
   if (!tokens || !lens_host) {
     c->err = "tokens and lens_host are required";
     return DAR_E_INVAL;
@@ -1350,6 +1657,7 @@ int dar_prefill(dar_ctx* c, int32_t batch, const int32_t* tokens, const int32_t*
 
 int dar_decode_frame(dar_ctx* c, const int32_t* forced, int32_t* codes_out, float* logits_out) {
   if (!c) return DAR_E_INVAL;
+  if (c->paged) return paged_frame(c, forced, codes_out, logits_out);
   if (!c->prefilled) {
     c->err = "decode before prefill";
     return DAR_E_STATE;
@@ -1385,6 +1693,13 @@ int dar_destroy(dar_ctx* c) {
 
 int dar_reset(dar_ctx* c) {
   if (!c) return DAR_E_INVAL;
+  if (c->paged) {
+    for (int b = 0; b < c->B; ++b) {
+      if (!c->slot_on[b]) continue;
+      const int st = dar_seq_remove(c, b);
+      if (st != DAR_OK) return st;
+    }
+  }
   DAR_HIP(c, launch_fill_i32(c->flags + 1, 1, 0, c->stream), "reset counters");
   c->pos_host = 0;
   std::fill(c->pos_hb.begin(), c->pos_hb.end(), 0);
@@ -1394,7 +1709,7 @@ int dar_reset(dar_ctx* c) {
 
 int dar_position(const dar_ctx* c, int32_t* pos_out) {
   if (!c || !pos_out) return DAR_E_INVAL;
-  for (int b = 0; b < c->B; ++b) pos_out[b] = c->pos_hb[b];
+  for (int b = 0; b < c->B; ++b) pos_out[b] = c->paged && !c->slot_on[b] ? -1 : c->pos_hb[b];
   return DAR_OK;
 }
 

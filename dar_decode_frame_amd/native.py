@@ -83,6 +83,13 @@ class dar_sampling(ctypes.Structure):
     ]
 
 
+class dar_paging(ctypes.Structure):
+    _fields_ = [
+        ("page_len", ctypes.c_int32),
+        ("n_pages", ctypes.c_int32),
+    ]
+
+
 class dar_weights(ctypes.Structure):
     _fields_ = [
         ("w0", ctypes.c_void_p),
@@ -103,6 +110,13 @@ _SIGS = {
     "dar_create": ([ctypes.POINTER(dar_config), ctypes.POINTER(dar_weights), _VP, ctypes.c_size_t, _VP,
                     ctypes.POINTER(_VP)], ctypes.c_int),
     "dar_prefill": ([_VP, _I32, _VP, ctypes.POINTER(_I32), _VP, _VP, _VP], ctypes.c_int),
+    "dar_workspace_bytes_paged": ([ctypes.POINTER(dar_config), ctypes.POINTER(dar_paging),
+                                   ctypes.POINTER(ctypes.c_size_t)], ctypes.c_int),
+    "dar_create_paged": ([ctypes.POINTER(dar_config), ctypes.POINTER(dar_paging), ctypes.POINTER(dar_weights), _VP,
+                          ctypes.c_size_t, _VP, ctypes.POINTER(_VP)], ctypes.c_int),
+    "dar_seq_add": ([_VP, _I32, _VP, _I32], ctypes.c_int),
+    "dar_seq_remove": ([_VP, _I32], ctypes.c_int),
+    "dar_pages_free": ([_VP, ctypes.POINTER(_I32)], ctypes.c_int),
     "dar_decode_frame": ([_VP, _VP, _VP, _VP], ctypes.c_int),
     "dar_destroy": ([_VP], ctypes.c_int),
     "dar_reset": ([_VP], ctypes.c_int),
@@ -192,6 +206,34 @@ def dar_create(cfg, weights, workspace_ptr, workspace_bytes, stream_ptr):
     _check(lib.dar_create(ctypes.byref(cfg), ctypes.byref(weights), workspace_ptr, workspace_bytes, stream_ptr,
                           ctypes.byref(ctx)), "dar_create")
     return ctx
+
+
+def dar_workspace_bytes_paged(cfg, paging):
+    out = ctypes.c_size_t(0)
+    _check(lib.dar_workspace_bytes_paged(ctypes.byref(cfg), ctypes.byref(paging), ctypes.byref(out)),
+           "dar_workspace_bytes_paged")
+    return out.value
+
+
+def dar_create_paged(cfg, paging, weights, workspace_ptr, workspace_bytes, stream_ptr):
+    ctx = ctypes.c_void_p(0)
+    _check(lib.dar_create_paged(ctypes.byref(cfg), ctypes.byref(paging), ctypes.byref(weights), workspace_ptr,
+                                workspace_bytes, stream_ptr, ctypes.byref(ctx)), "dar_create_paged")
+    return ctx
+
+
+def dar_seq_add(ctx, slot, tokens_ptr, length):
+    return _check(lib.dar_seq_add(ctx, slot, tokens_ptr, length), "dar_seq_add", ctx)
+
+
+def dar_seq_remove(ctx, slot):
+    return _check(lib.dar_seq_remove(ctx, slot), "dar_seq_remove", ctx)
+
+
+def dar_pages_free(ctx):
+    out = ctypes.c_int32(0)
+    _check(lib.dar_pages_free(ctx, ctypes.byref(out)), "dar_pages_free", ctx)
+    return out.value
 
 
 def dar_prefill(ctx, batch, tokens_ptr, lens, forced_ptr=None, codes_out_ptr=None, logits_out_ptr=None):

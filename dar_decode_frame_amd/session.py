@@ -109,19 +109,25 @@ class DarSession:
     [batch][1 + n_res][vmax]. With batch 1 the leading axis is dropped."""
 
     def __init__(self, dims, weights: DeviceWeights, max_len: int, device="cuda", stream=None, graph=False,
-                 batch=1):
+                 batch=1, paging=None):
         self.dims = dims
         self.max_len = max_len
         self.device = device
         self.batch = batch
         self.stream = stream if stream is not None else torch.cuda.Stream(device)
         self.cfg = N.make_config(dims, max_len, weights.wtype, max_batch=batch)
-        nbytes = N.dar_workspace_bytes(self.cfg)
+        self.paging = N.dar_paging(*paging) if paging is not None else None
+        nbytes = (N.dar_workspace_bytes_paged(self.cfg, self.paging) if self.paging is not None
+                  else N.dar_workspace_bytes(self.cfg))
         self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
         self.weights = weights
         wstruct, self._keep = weights.struct()
-        self.ctx = N.dar_create(self.cfg, wstruct, ctypes.c_void_p(self.workspace.data_ptr()), nbytes,
-                                ctypes.c_void_p(self.stream.cuda_stream))
+        ws, st = ctypes.c_void_p(self.workspace.data_ptr()), ctypes.c_void_p(self.stream.cuda_stream)
+        if self.paging is not None:
+            self.ctx = N.dar_create_paged(self.cfg, self.paging, wstruct, ws, nbytes, st)
+        else:
+            self.ctx = N.dar_create(self.cfg, wstruct, ws, nbytes, st)
+        self._seq_toks = {}
         N.dar_set_graph(self.ctx, graph)
         self.fc = dims.n_res + 1
         self.vmax = max(dims.vocab_c0, dims.vocab_res if dims.n_res > 0 else 0)
@@ -158,6 +164,20 @@ class DarSession:
                       _dev(self.logits) if want else None)
         self._toks = toks
         return self._out(want)
+
+    def seq_add(self, slot, tokens):
+        """Paged context: prefill one prompt into a free slot; its frame 0
+        comes out of the next decode_frame."""
+        toks = torch.as_tensor(np.asarray(tokens, dtype=np.int32)).to(self.device)
+        torch.cuda.current_stream(self.device).synchronize()
+        N.dar_seq_add(self.ctx, slot, _dev(toks), len(tokens))
+        self._seq_toks[slot] = toks  # read on the stream: kept until the slot is reused
+
+    def seq_remove(self, slot):
+        N.dar_seq_remove(self.ctx, slot)
+
+    def pages_free(self):
+        return N.dar_pages_free(self.ctx)
 
     def decode_frame(self, forced=None, want=True):
         fp = self._forced_ptr(forced)

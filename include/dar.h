@@ -241,6 +241,67 @@ int dar_quantize_int4_groups(const void* w, int32_t rows, int32_t cols, void* q,
 const char* dar_status_string(int status);
 const char* dar_last_error(const dar_ctx* ctx);   /* ctx may be NULL: last create error */
 
+/* ---- paged KV cache and continuous batching ----------------------------
+ *
+ * The fish-speech fork README's serving notes say the Dual-AR model takes the
+ * batching of ordinary LLM serving (requests joining and leaving a running
+ * batch, a paged KV cache). A paged context holds max_batch slots. The slow
+ * KV cache of every slot comes from one pool of n_pages pages. A page holds
+ * page_len consecutive positions of every slow layer and KV head. A slot's
+ * block table maps its position p to page (p / page_len), offset
+ * (p % page_len). Pages are taken from the pool when a sequence reaches them
+ * and returned when it leaves. Workspace:
+ *   K, V [n_layers_slow][n_pages][n_heads_kv][page_len][head_dim] bf16
+ *   block table int32 [max_batch][ceil(max_len / page_len)]
+ * instead of one [max_len] cache per sequence. Page 0 is reserved: a free
+ * slot is parked at position 0 of page 0. Its rows still run every frame
+ * but change nothing any sequence reads.
+ *
+ * Frames: dar_seq_add prefills one prompt into a free slot. That slot's
+ * frame 0 (at position len - 1) comes out of the next dar_decode_frame.
+ * Each dar_decode_frame then returns the next frame of every occupied slot.
+ * codes_out / logits_out / forced are [max_batch][...] as for a lockstep
+ * batch; rows of free slots are undefined on output and ignored on input.
+ * A slot's frames run up to position max_len - 2, because the next frame's
+ * slow step is computed ahead. dar_decode_frame returns DAR_E_CAPACITY,
+ * and changes nothing, when an occupied slot's frame position has reached
+ * max_len - 1 (remove that slot first) or when the pool lacks a page a
+ * sequence enters. dar_prefill is refused (DAR_E_STATE). dar_position gives
+ * each slot's next frame position, or -1 for a free slot. dar_reset removes
+ * every sequence. */
+typedef struct {
+  int32_t page_len;  /* positions per page: a power of two in [64, 2^20]; at most 64
+                        pages per sequence (ceil(max_len / page_len) <= 64) */
+  int32_t n_pages;   /* pages in the pool, >= 2 (page 0 is the parking page) */
+} dar_paging;
+
+/* Bytes of device workspace of a paged context (host only). Requires
+ * max_batch >= 2 (DAR_E_UNSUPPORTED otherwise). */
+int dar_workspace_bytes_paged(const dar_config* cfg, const dar_paging* paging, size_t* bytes_out);
+
+/* dar_create for a paged context (arguments and ownership as there). Every
+ * slot starts free and all n_pages - 1 usable pages start in the pool. */
+int dar_create_paged(const dar_config* cfg, const dar_paging* paging, const dar_weights* weights,
+                     void* workspace, size_t workspace_bytes, void* stream, dar_ctx** ctx_out);
+
+/* Prefill a prompt into free slot `slot` (the slow AR over the prompt, on
+ * MFMA, and the codebook-0 head on its last position). tokens: device int32
+ * [len] with ids in [0, vocab_c0) (clamped otherwise), read on the context's
+ * stream. 1 <= len < max_len. Takes ceil(len / page_len) pages from the pool.
+ * Errors, all before any change: DAR_E_INVAL (slot out of range, NULL
+ * tokens, len < 1), DAR_E_STATE (slot occupied, context not paged),
+ * DAR_E_CAPACITY (len >= max_len, too few free pages). Stream-ordered; other
+ * slots keep their state and continue with the next dar_decode_frame. */
+int dar_seq_add(dar_ctx* ctx, int32_t slot, const int32_t* tokens, int32_t len);
+
+/* Remove the sequence in `slot`. Its pages return to the pool, and the slot
+ * is free for dar_seq_add. Work already queued for the slot finishes first
+ * (stream order). DAR_E_STATE if the slot is free or the context not paged. */
+int dar_seq_remove(dar_ctx* ctx, int32_t slot);
+
+/* Pages left in the pool (host state; 0 for a context that is not paged). */
+int dar_pages_free(const dar_ctx* ctx, int32_t* n_free);
+
 /* ---- diagnostics: single operations of the frame, for tests and timing --- */
 
 /* y[m][r] = sum_j W[r][j] * x[m][j] (times scale[r] with fp8 / int8 weights,

@@ -142,3 +142,44 @@ def test_sampling_vocabulary_limit(N):
     assert N.lib.dar_op_sample(p, 4, 8193, ctypes.byref(s), p, 4, p, None) == N.DAR_E_UNSUPPORTED
     assert N.lib.dar_op_sample(p, 0, 1024, ctypes.byref(s), p, 4, p, None) == N.DAR_E_INVAL
     assert N.lib.dar_op_sample(p, 4, 1024, ctypes.byref(s), None, 4, p, None) == N.DAR_E_INVAL
+
+
+@pytest.mark.parametrize("page_len,n_pages,max_batch,max_len,status", [
+    (64, 2, 2, 32, 0), (256, 40, 16, 4096, 0),
+    (96, 8, 2, 256, -1), (32, 8, 2, 256, -1), (64, 1, 2, 256, -1),   # not a power of two, below 64, no usable page
+    (64, 8, 1, 256, -6),                                              # paged contexts use the many-row path
+    (64, 80, 2, 64 * 65, -6),                                         # 65 pages per sequence
+])
+def test_paging_validation(N, page_len, n_pages, max_batch, max_len, status):
+    c = _cfg(N, max_batch=max_batch, max_len=max_len)
+    pg = N.dar_paging(page_len, n_pages)
+    out = ctypes.c_size_t(0)
+    assert N.lib.dar_workspace_bytes_paged(ctypes.byref(c), ctypes.byref(pg), ctypes.byref(out)) == status
+    ctx = ctypes.c_void_p(0)
+    if status != 0:
+        assert N.dar_last_error(None)
+        # create rejects the same arguments before any HIP call
+        w = N.dar_weights()
+        assert N.lib.dar_create_paged(ctypes.byref(c), ctypes.byref(pg), ctypes.byref(w), ctypes.c_void_p(256),
+                                      out.value or 1 << 30, None, ctypes.byref(ctx)) == status
+        assert not ctx.value
+
+
+def test_paged_workspace_holds_the_pool(N):
+    # the slow KV is the page pool instead of max_batch full-length caches
+    d = DIMS["s2pro_dual"]
+    c = N.make_config(d, 4096, max_batch=16)
+    full = N.dar_workspace_bytes(c)
+    page_bytes = 2 * d.n_layers_slow * d.n_heads_kv * 256 * d.head_dim * 2
+    for n_pages in (17, 65):
+        paged = N.dar_workspace_bytes_paged(c, N.dar_paging(256, n_pages))
+        kv_full = 2 * d.n_layers_slow * 16 * d.n_heads_kv * 4096 * d.head_dim * 2
+        assert paged - (full - kv_full) >= n_pages * page_bytes
+        assert paged - (full - kv_full) < n_pages * page_bytes + 2 ** 20
+
+
+def test_paged_calls_reject_without_context(N):
+    n = ctypes.c_int32(0)
+    assert N.lib.dar_seq_add(None, 0, ctypes.c_void_p(256), 4) == N.DAR_E_INVAL
+    assert N.lib.dar_seq_remove(None, 0) == N.DAR_E_INVAL
+    assert N.lib.dar_pages_free(None, ctypes.byref(n)) == N.DAR_E_INVAL

@@ -1,0 +1,179 @@
+"""Continuous batching over a paged slow KV cache (dar_create_paged).
+
+Tiny Dual-AR (2 slow layers, 1 fast layer, d 256), four slots, pages of 64
+positions. Sequences join and leave while the others keep decoding. A
+sequence that joins takes pages another one just returned (stale KV in them).
+One slot stays free throughout (its parked rows run every frame). Prompts
+span several pages, and sequences cross page boundaries while decoding.
+Every sequence is teacher-forced with its own oracle greedy frames and held to
+the bar of a single sequence: logits rel-L2, argmax agreement, exact codes
+above the margin. Pool exhaustion and the position limit return
+DAR_E_CAPACITY and change nothing: the run continues after a removal and
+still matches the oracle.
+"""
+import numpy as np
+import pytest
+
+import synth
+from oracle import OracleDecoder, OracleModel
+from parity import TOL, assert_parity, compare_frames
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def tiny_host():
+    d = synth.DIMS["tiny"]
+    return d, synth.gen_weights(d, 0)
+
+
+def _oracle_frames(model, prompt, frames, max_len):
+    dec = OracleDecoder(model, max_len)
+    out = [dec.prefill(prompt)]
+    for _ in range(frames):
+        out.append(dec.decode_frame())
+    return out
+
+
+class Driver:
+    """Runs a schedule of adds, removes and frames on a paged session, forcing
+    each slot's sequence with its oracle frames and collecting its outputs."""
+
+    def __init__(self, sess, dims, refs):
+        self.sess, self.dims, self.refs = sess, dims, refs
+        self.fc = dims.n_res + 1
+        self.slot_seq = {}                     # slot -> sequence id
+        self.done = {k: 0 for k in refs}       # frames returned per sequence
+        self.got = {k: [] for k in refs}
+
+    def add(self, slot, seq, prompt):
+        self.sess.seq_add(slot, prompt)
+        self.slot_seq[slot] = seq
+
+    def remove(self, slot):
+        self.sess.seq_remove(slot)
+        del self.slot_seq[slot]
+
+    def frame(self):
+        forced = np.zeros((self.sess.batch, self.fc), dtype=np.int32)
+        for slot, seq in self.slot_seq.items():
+            forced[slot] = self.refs[seq][self.done[seq]][0]
+        codes, logits = self.sess.decode_frame(forced=forced)
+        for slot, seq in self.slot_seq.items():
+            self.got[seq].append((codes[slot].copy(), logits[slot].copy()))
+            self.done[seq] += 1
+
+    def check(self, wtype):
+        allst = {"max_rel": 0.0, "agree": 0.0, "n": 0, "exact_fail": [], "tol": TOL[wtype]}
+        for seq, frames in self.got.items():
+            st = compare_frames(frames, self.refs[seq][:len(frames)], self.dims, wtype)
+            allst["max_rel"] = max(allst["max_rel"], st["max_rel"])
+            allst["agree"] += st["agree"] * st["n"]
+            allst["n"] += st["n"]
+            allst["exact_fail"] += [(seq,) + e for e in st["exact_fail"]]
+        allst["agree"] /= allst["n"]
+        return allst
+
+
+@pytest.mark.parametrize("wtype", ["bf16", "fp8", "int4"])
+def test_paged_continuous_parity(tiny_host, wtype):
+    from dar_decode_frame_amd.session import DarSession, DeviceWeights
+    dims, host = tiny_host
+    max_len, page, n_pages = 200, 64, 12
+    lens = {"A": 60, "B": 20, "C": 130, "D": 5, "E": 100}
+    frames = {"A": 16, "B": 6, "C": 20, "D": 14, "E": 8}
+    prompts = {k: synth.gen_prompt(n, dims.vocab_c0, 300 + i) for i, (k, n) in enumerate(lens.items())}
+    model = OracleModel(dims, host, wtype=wtype)
+    refs = {k: _oracle_frames(model, prompts[k], frames[k], max_len) for k in lens}
+    sess = DarSession(dims, DeviceWeights(dims, host, wtype), max_len, batch=4, paging=(page, n_pages))
+    assert sess.pages_free() == n_pages - 1
+    drv = Driver(sess, dims, refs)
+    drv.add(0, "A", prompts["A"])      # 1 page; crosses into its second page at its 5th frame
+    drv.add(2, "B", prompts["B"])      # 1 page
+    assert sess.pages_free() == n_pages - 3
+    for _ in range(3):
+        drv.frame()
+    drv.add(1, "C", prompts["C"])      # 3 pages, attention over three splits
+    for _ in range(4):
+        drv.frame()
+    assert sess.position() == [lens["A"] - 1 + 7, lens["C"] - 1 + 4, lens["B"] - 1 + 7, -1]
+    drv.remove(2)                      # B leaves after 7 frames; D reuses its page (stale KV)
+    drv.add(2, "D", prompts["D"])
+    for _ in range(6):
+        drv.frame()
+    drv.remove(0)                      # A leaves after 13 frames
+    drv.add(0, "E", prompts["E"])
+    for _ in range(9):
+        drv.frame()                    # E: frames 0..8
+    st = drv.check(wtype)
+    print(f"\n{wtype} paged: {st}")
+    assert_parity(st)
+    assert {k: len(v) for k, v in drv.got.items()} == {"A": 13, "B": 7, "C": 19, "D": 15, "E": 9}
+    for slot in list(drv.slot_seq):
+        drv.remove(slot)
+    assert sess.pages_free() == n_pages - 1
+    assert sess.position() == [-1, -1, -1, -1]
+    assert sess.nonfinite() == 0
+    sess.close()
+
+
+def test_paged_capacity_changes_nothing(tiny_host):
+    from dar_decode_frame_amd import native as N
+    from dar_decode_frame_amd.session import DarSession, DeviceWeights
+    dims, host = tiny_host
+    max_len, page, n_pages = 256, 64, 4        # 3 usable pages
+    lens = {"A": 62, "B": 64, "C": 10}
+    frames = {"A": 8, "B": 4, "C": 4}
+    prompts = {k: synth.gen_prompt(n, dims.vocab_c0, 400 + i) for i, (k, n) in enumerate(lens.items())}
+    model = OracleModel(dims, host, wtype="bf16")
+    refs = {k: _oracle_frames(model, prompts[k], frames[k], max_len) for k in lens}
+    sess = DarSession(dims, DeviceWeights(dims, host, "bf16"), max_len, batch=2, paging=(page, n_pages))
+    drv = Driver(sess, dims, refs)
+    # a prompt longer than the pool, and an occupied slot, are refused
+    long_prompt = synth.gen_prompt(200, dims.vocab_c0, 9)
+    with pytest.raises(N.DarError) as e:
+        sess.seq_add(0, long_prompt)
+    assert e.value.status == N.DAR_E_CAPACITY
+    assert sess.pages_free() == 3
+    drv.add(0, "A", prompts["A"])      # positions 0..61: page 1
+    drv.add(1, "B", prompts["B"])      # positions 0..63: one page; its first slow step needs a second
+    with pytest.raises(N.DarError) as e:
+        sess.seq_add(1, prompts["C"])
+    assert e.value.status == N.DAR_E_STATE
+    assert sess.pages_free() == 1
+    drv.frame()                        # B's slow step at 64 takes the last page
+    assert sess.pages_free() == 0
+    drv.frame()                        # A's slow step at 62..63: still its first page
+    with pytest.raises(N.DarError) as e:
+        drv.frame()                    # A's slow step at 64 needs a page: refused, nothing changes
+    assert e.value.status == N.DAR_E_CAPACITY
+    assert sess.position() == [lens["A"] - 1 + 2, lens["B"] - 1 + 2]
+    drv.remove(1)                      # B leaves: two pages back
+    drv.add(1, "C", prompts["C"])
+    for _ in range(4):
+        drv.frame()
+    st = drv.check("bf16")
+    print(f"\npaged capacity run: {st}")
+    assert_parity(st)
+    assert {k: len(v) for k, v in drv.got.items()} == {"A": 6, "B": 2, "C": 4}
+    sess.close()
+
+
+def test_paged_position_limit(tiny_host):
+    from dar_decode_frame_amd import native as N
+    from dar_decode_frame_amd.session import DarSession, DeviceWeights
+    dims, host = tiny_host
+    sess = DarSession(dims, DeviceWeights(dims, host, "bf16"), 64, batch=2, paging=(64, 3))
+    sess.seq_add(1, synth.gen_prompt(60, dims.vocab_c0, 5))   # frame 0 at 59
+    for _ in range(3):
+        sess.decode_frame(want=False)                        # frames at 59, 60, 61; next at 62 = max_len - 2
+    sess.decode_frame(want=False)
+    assert sess.position() == [-1, 63]
+    with pytest.raises(N.DarError) as e:
+        sess.decode_frame(want=False)                        # its slow step would be at 64 = max_len
+    assert e.value.status == N.DAR_E_CAPACITY
+    sess.seq_remove(1)
+    with pytest.raises(N.DarError) as e:
+        sess.decode_frame(want=False)                        # no sequence left
+    assert e.value.status == N.DAR_E_STATE
+    sess.close()
