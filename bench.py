@@ -64,6 +64,8 @@ def main():
 
     wl = synth.WORKLOADS[args.workload]
     dims = wl.dims
+    if wl.requests > 0:
+        return bench_continuous(args, wl)
     if wl.batch != 1:
         return bench_batched(args, wl)
     max_steps = wl.max_len - wl.prefill_len
@@ -313,6 +315,140 @@ def bench_batched(args, wl):
                    "sampling": SAMPLING if args.sample else None},
         "achieved_gb_s": round(gbs / 1e9, 1), "hbm_frac": round(gbs / HBM_PEAK, 4),
         "alg_bytes_per_step_avg": int(alg_bytes // steps), "prefill_ms": round(prefill_ms, 2),
+        "nonfinite_logits": n_bad, "roofline": roof, "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def bench_continuous(args, wl):
+    """Continuous batching over the paged slow KV cache: wl.batch slots serve
+    wl.requests requests in arrival order; a request joins (its prompt is
+    prefilled) as soon as a slot is free, its frames come out of the following
+    frame calls, and it leaves after its frame count. The timed region runs
+    from the first admission to the last frame and includes the admissions'
+    prefills. value = frames delivered / elapsed; algorithmic bytes count each
+    frame call's weights once and every active request's slow KV reads."""
+    import ctypes
+
+    import numpy as np
+    import torch
+
+    import synth
+    from dar_decode_frame_amd import bytes_model as bm
+    from dar_decode_frame_amd import native as N
+    from dar_decode_frame_amd.session import DarSession, DeviceWeights
+
+    dims, S = wl.dims, wl.batch
+    dev = torch.device("cuda:0")
+    lens, nframes, prompts = synth.gen_requests(wl.requests, wl.prefill_len, wl.prefill_len_max, wl.frames_min,
+                                                wl.decode_frames, dims.vocab_c0, wl.prompt_seed, wl.length_seed)
+    t0 = time.time()
+    host = synth.gen_weights(dims, wl.weight_seed)
+    weights = DeviceWeights(dims, host, wl.wtype, dev)
+    if args.no_cpu_baseline:
+        del host
+    log(f"weights ready in {time.time() - t0:.1f}s; {wl.requests} requests, prompts {int(lens.min())}..."
+        f"{int(lens.max())} ids, {int(nframes.min())}..{int(nframes.max())} frames, {S} slots")
+    sess = DarSession(dims, weights, wl.max_len, dev, batch=S, paging=(wl.page_len, wl.n_pages))
+    stream, ctx = sess.stream, sess.ctx
+    # every prompt resident on the device before timing
+    offs = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    toks = torch.as_tensor(np.concatenate(prompts).astype(np.int32)).to(dev)
+    torch.cuda.synchronize()
+    base = toks.data_ptr()
+
+    def add(slot, r):
+        N.dar_seq_add(ctx, slot, ctypes.c_void_p(base + 4 * int(offs[r])), int(lens[r]))
+
+    # warmup: fill the slots, a few frames, empty them again
+    for b in range(S):
+        add(b, b)
+    for _ in range(args.warmup):
+        N.dar_decode_frame(ctx, None, None, None)
+    for b in range(S):
+        N.dar_seq_remove(ctx, b)
+    stream.synchronize()
+
+    kvp = bm.kv_bytes_per_position(dims)
+    weights_b = bm.slow_weight_bytes(dims, wl.wtype) + dims.n_res * bm.fast_pass_bytes(dims, wl.wtype)
+    queue = list(range(wl.requests))
+    slot_req, left, pos = [None] * S, [0] * S, [0] * S
+    calls = frames = active_sum = 0
+    alg_bytes = 0
+    min_free = sess.pages_free()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    while queue or any(r is not None for r in slot_req):
+        for b in range(S):
+            if slot_req[b] is None and queue:
+                r = queue.pop(0)
+                add(b, r)
+                slot_req[b], left[b], pos[b] = r, int(nframes[r]), int(lens[r]) - 1
+        min_free = min(min_free, N.dar_pages_free(ctx))
+        N.dar_decode_frame(ctx, None, None, None)
+        calls += 1
+        alg_bytes += weights_b
+        for b in range(S):
+            if slot_req[b] is None:
+                continue
+            alg_bytes += kvp * (pos[b] + 2) + bm.fast_kv_bytes(dims)  # its slow step attends pos + 2 positions
+            pos[b] += 1
+            left[b] -= 1
+            frames += 1
+            active_sum += 1
+            if left[b] == 0:
+                N.dar_seq_remove(ctx, b)
+                slot_req[b] = None
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1)
+    fps = frames * 1000.0 / ms
+    gbs = alg_bytes / (ms / 1000.0)
+    assert frames == int(nframes.sum())
+    page_bytes = 2 * dims.n_layers_slow * dims.n_heads_kv * wl.page_len * dims.head_dim * 2
+    log(f"timed {wl.requests} requests, {frames} frames in {calls} frame calls: {ms:.1f} ms, {fps:.1f} frames/s, "
+        f"{gbs / 1e9:.0f} GB/s, mean {active_sum / calls:.1f} active slots, peak "
+        f"{wl.n_pages - 1 - min_free} of {wl.n_pages - 1} pages")
+
+    # dominant GEMM (W1 or W3, one matrix per launch) timed live over frames with every slot busy
+    for b in range(S):
+        add(b, b)
+    sess.time_kind(3)
+    for _ in range(32):
+        N.dar_decode_frame(ctx, None, None, None)
+    live_ms, live_n = sess.kind_time()
+    sess.time_kind(-1)
+    per = per_launch_bytes(dims, wl.wtype, "w13") // 2
+    avg_ms = live_ms / live_n
+    achieved = per / (avg_ms / 1000.0)
+    roof = {"kernel": "w13", "bound": "hbm", "achieved": round(achieved / 1e9, 1), "peak": HBM_PEAK / 1e9,
+            "unit": "GB/s", "frac": round(achieved / HBM_PEAK, 4), "traffic": None, "bytes_per_launch": per,
+            "avg_launch_us": round(avg_ms * 1000, 2), "launches_timed": live_n,
+            "note": "W1 and W3 GEMMs over the 16 slots' rows, timed live on their stream beside the other chain"}
+    n_bad = sess.nonfinite()
+    sess.close()
+    cpu = None
+    if not args.no_cpu_baseline:
+        del sess, weights
+        torch.cuda.empty_cache()
+        cpu = cpu_baseline_batched(dims, wl, host, lens, prompts)
+        del host
+    out = {
+        "metric": METRIC, "value": round(fps, 2), "unit": "frames/s", "n_gpus": 1, "steps": calls,
+        "warmup": args.warmup, "ms_per_step": round(ms / calls, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": DTYPE_NAMES[wl.wtype],
+        "data": "synthetic (seeded random-init weights, random prompts, seeded request lengths)",
+        "config": {"workload": wl.name, "slots": S, "requests": wl.requests,
+                   "prompt_lengths": [int(lens.min()), int(lens.max())],
+                   "frames_per_request": [int(nframes.min()), int(nframes.max())], "frames_total": frames,
+                   "page_len": wl.page_len, "n_pages": wl.n_pages, "max_len": wl.max_len,
+                   "layers_slow": dims.n_layers_slow, "layers_fast": dims.n_layers_fast,
+                   "residual_codebooks": dims.n_res},
+        "achieved_gb_s": round(gbs / 1e9, 1), "hbm_frac": round(gbs / HBM_PEAK, 4),
+        "mean_active_slots": round(active_sum / calls, 2), "pages_peak": wl.n_pages - 1 - min_free,
+        "kv_pool_bytes": wl.n_pages * page_bytes,
+        "kv_bytes_lockstep_same_max_len": S * (wl.max_len // wl.page_len) * page_bytes,
         "nonfinite_logits": n_bad, "roofline": roof, "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -2046,6 +2046,10 @@ int dar_kind_time(dar_ctx* c, double* ms_total, int32_t* launches) {
 int dar_profile_frame(dar_ctx* c, int32_t cap, float* ms_out, int32_t* kind_out, int32_t* layer_out,
                       int32_t* n_out) {
   if (!c || !ms_out || !kind_out || !layer_out || !n_out || cap < 1) return DAR_E_INVAL;
+  if (c->paged) {
+    c->err = "a paged context takes new pages in dar_decode_frame: time it with dar_time_kind";
+    return DAR_E_STATE;
+  }
   if (!c->prefilled) {
     c->err = "decode before prefill";
     return DAR_E_STATE;

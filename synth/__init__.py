@@ -15,4 +15,4 @@ from .configs import (  # noqa: F401
     linear_names,
 )
 from .weights import gen_weights, gen_tensor, f32_to_bf16_bits  # noqa: F401
-from .prompts import gen_prompt, gen_ragged_prompts, gen_sample_logits, gen_uniforms  # noqa: F401
+from .prompts import gen_prompt, gen_ragged_prompts, gen_requests, gen_sample_logits, gen_uniforms  # noqa: F401

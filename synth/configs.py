@@ -79,6 +79,13 @@ class Workload:
     weight_seed: int = 0
     prompt_seed: int = 1
     length_seed: int = 2
+    # continuous batching (requests > 0): `batch` slots serve `requests`
+    # requests, prompts prefill_len..prefill_len_max ids, each decoding
+    # frames_min..decode_frames frames; slow KV in pages of page_len positions
+    requests: int = 0
+    frames_min: int = 0
+    page_len: int = 0
+    n_pages: int = 0
 
 
 TINY = DarDims(
@@ -111,6 +118,11 @@ WORKLOADS = {
     # batched Dual-AR decode, ragged prompts 128..512, max length 4096
     "s2pro_dual_b16": Workload("s2pro_dual_b16", S2_DUAL, "bf16", 16, 128, 512, 3584, 4096),
     "s2pro_dual_b64": Workload("s2pro_dual_b64", S2_DUAL, "bf16", 64, 128, 512, 3584, 4096),
+    # continuous batching: 16 slots serve 64 requests (prompts 128..512, 64..1024
+    # frames each), slow KV from a pool of 256-position pages sized for 16 of
+    # the longest requests (6 pages each) plus the parking page
+    "s2pro_dual_cb16": Workload("s2pro_dual_cb16", S2_DUAL, "bf16", 16, 128, 512, 1024, 4096,
+                                requests=64, frames_min=64, page_len=256, n_pages=97),
 }
 
 

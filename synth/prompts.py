@@ -25,6 +25,16 @@ def gen_ragged_prompts(batch: int, lo: int, hi: int, vocab: int, seed: int = 1, 
     return lens, prompts
 
 
+def gen_requests(n: int, lo: int, hi: int, frames_lo: int, frames_hi: int, vocab: int, seed: int = 1,
+                 length_seed: int = 2):
+    """A stream of n requests: prompt lengths uniform on [lo, hi], frame
+    counts uniform on [frames_lo, frames_hi] (inclusive), random prompt ids."""
+    lens, prompts = gen_ragged_prompts(n, lo, hi, vocab, seed, length_seed)
+    frng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([length_seed, 1])))
+    frames = frng.integers(frames_lo, frames_hi + 1, size=n, dtype=np.int64).astype(np.int32)
+    return lens, frames, prompts
+
+
 def gen_uniforms(max_len: int, batch: int, codes: int, seed: int = 3) -> np.ndarray:
     """Draws for sampling: fp32 [max_len][batch][codes], uniform on [0, 1)."""
     rng = np.random.default_rng(seed)
