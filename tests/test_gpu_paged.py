@@ -177,3 +177,65 @@ def test_paged_position_limit(tiny_host):
         sess.decode_frame(want=False)                        # no sequence left
     assert e.value.status == N.DAR_E_STATE
     sess.close()
+
+
+def test_fullshape_paged_matches_oracle():
+    """Full shape (36 + 4 layers, d 2560, bf16) in the continuous-batching
+    bench's configuration (16 slots, 256-position pages, 97 pages, max length
+    4096): one slot decodes the oracle reference runs while three other slots
+    hold other sequences; its frames must meet the full-shape bar against the
+    stored oracle references (prefill 128 + 9 greedy-forced frames, and the
+    frame at position 1007 after 880 randomly forced frames)."""
+    import torch
+
+    from dar_decode_frame_amd.session import DarSession, DeviceWeights
+    from test_gpu_fullshape import _compare, _golden, _random_frames
+    wl = synth.WORKLOADS["s2pro_dual_bf16"]
+    cb = synth.WORKLOADS["s2pro_dual_cb16"]
+    dims = wl.dims
+    ref = _golden("s2pro_dual_bf16")
+    host = synth.gen_weights(dims, wl.weight_seed)
+    dw = DeviceWeights(dims, host, "bf16")
+    del host
+    sess = DarSession(dims, dw, cb.max_len, batch=cb.batch, paging=(cb.page_len, cb.n_pages))
+    prompt = synth.gen_prompt(wl.prefill_len, dims.vocab_c0, wl.prompt_seed)
+    others = {b: synth.gen_prompt(300, dims.vocab_c0, 600 + b) for b in (0, 1, 2)}
+    slot = 5
+    fc = dims.n_res + 1
+    stats = {"rel": [], "n": 0, "agree": 0, "exact_fail": []}
+
+    def run(forced_frames, keep):
+        for b, p in others.items():
+            sess.seq_add(b, p)
+        sess.seq_add(slot, prompt)
+        outs = []
+        for i, f in enumerate(forced_frames):
+            forced = np.zeros((cb.batch, fc), dtype=np.int32)
+            forced[slot] = f
+            out = sess.decode_frame(forced=forced, want=keep(i))
+            if keep(i):
+                outs.append((out[0][slot].copy(), out[1][slot].copy()))
+        return outs
+
+    early = [np.asarray(f, dtype=np.int32) for f in ref["early"]["forced"]]
+    got = run(early, lambda i: True)
+    for (codes, logits), rv in zip(got, ref["early"]["frames"]):
+        _compare(rv, codes, logits, dims, stats)
+    sess.reset()
+    assert sess.pages_free() == cb.n_pages - 1
+    late = ref["late"]
+    forced = [np.asarray(f, dtype=np.int32) for f in _random_frames()(dims, late["frames_forced"], late["force_seed"])]
+    got = run(forced, lambda i: i == len(forced) - 1)
+    assert sess.position()[slot] == late["position"] + 1
+    codes, logits = got[-1]
+    _compare(late["frame"], codes, logits, dims, stats)
+    agree = stats["agree"] / stats["n"]
+    print(f"\npaged full shape: max rel {max(stats['rel']):.3e}, agreement {agree:.4f} over {stats['n']} vectors, "
+          f"exact failures {stats['exact_fail']}")
+    assert max(stats["rel"]) <= TOL["bf16"], stats
+    assert not stats["exact_fail"], stats
+    assert agree >= 0.99, stats
+    assert sess.nonfinite() == 0
+    sess.close()
+    del dw
+    torch.cuda.empty_cache()
