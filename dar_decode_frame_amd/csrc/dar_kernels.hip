@@ -1072,23 +1072,51 @@ template <typename WT>
 struct PerWave {
   static constexpr int v = 1;
 };
+// One-byte weights: three outputs per wave (fewer, wider workgroups share the
+// chip better with the other chain's launches: fp8 frame 396 -> 410 frames/s,
+// although a W13 launch alone takes 14.9 instead of 13.9 us), two QKV
+// rotation pairs per wave.
 template <>
 struct PerWave<FP8> {
-  static constexpr int v = 2;
+  static constexpr int v = 3;
 };
 template <>
 struct PerWave<INT8> {
-  static constexpr int v = 2;
+  static constexpr int v = 3;
 };
 template <>
 struct PerWave<INT4> {
   static constexpr int v = 2;  // more waves rather than more rows each: the int4 dot is ALU-heavy
 };
+// Rows per wave of the plain GEMV (Wo, fast first pass) and of the fused QKV
+// (rotation pairs per wave) where they differ from the SwiGLU's PerWave.
+template <typename WT>
+struct PerWaveGemv {
+  static constexpr int v = PerWave<WT>::v;
+};
+template <typename WT>
+struct PerWaveQkv {
+  static constexpr int v = PerWave<WT>::v;
+};
+// Inputs of at least this many chunks go to the split-K GEMV (four waves share
+// a row's chunks) when there is no RMSNorm prologue.
+template <typename WT>
+struct SplitFrom {
+  static constexpr int v = 9;
+};
+template <>
+struct PerWaveQkv<FP8> {
+  static constexpr int v = 2;
+};
+template <>
+struct PerWaveQkv<INT8> {
+  static constexpr int v = 2;
+};
 
 // y[r] (+)= scale[r] * W[r] . x, P rows per wave
 template <typename WT, int NCH>
 __device__ __forceinline__ void gemv_reg_body(const GemvArgs& a, int bid) {
-  constexpr int P = PerWave<WT>::v;
+  constexpr int P = PerWaveGemv<WT>::v;
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
   const int r0 = (bid * kWaves + wave) * P;
   RegStream<WT, NCH, P> rs;
@@ -1119,7 +1147,7 @@ __device__ __forceinline__ void gemv_reg_body(const GemvArgs& a, int bid) {
 // (head, i), (head, i + hd/2)
 template <typename WT, int NCH>
 __device__ __forceinline__ void qkv_reg_body(const QkvArgs& a, int bid) {
-  constexpr int P = PerWave<WT>::v;
+  constexpr int P = PerWaveQkv<WT>::v;
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
   const int half = a.head_dim / 2;
   const int n_heads = a.n_heads_q + 2 * a.n_heads_kv;
@@ -1693,9 +1721,11 @@ static bool with_body(const Task& t, F&& f) {
     case T_GEMV: {
       const GemvArgs& a = t.gemv;
       if (t.M == 1) {
-        const Geo g{(a.rows + kWaves * PerWave<WT>::v - 1) / (kWaves * PerWave<WT>::v), 0};
+        const Geo g{(a.rows + kWaves * PerWaveGemv<WT>::v - 1) / (kWaves * PerWaveGemv<WT>::v), 0};
 #define CALL(N) f(GemvR<WT, N>{}, a, g)
-        switch (nch_of<WT>(a.K)) { DAR_NCH_CASES(CALL) }
+        if (a.gain || nch_of<WT>(a.K) < SplitFrom<WT>::v) {
+          switch (nch_of<WT>(a.K)) { DAR_NCH_CASES(CALL) }
+        }
 #undef CALL
         if (!a.gain) {
           // wider inputs: four waves split the chunks, two rows per block
@@ -1721,7 +1751,7 @@ static bool with_body(const Task& t, F&& f) {
       const int pairs = (a.n_heads_q + 2 * a.n_heads_kv) * a.head_dim / 2;
       const int grid = (pairs + kWaves - 1) / kWaves;
       if (t.M == 1) {
-        const int rgrid = (pairs + kWaves * PerWave<WT>::v - 1) / (kWaves * PerWave<WT>::v);
+        const int rgrid = (pairs + kWaves * PerWaveQkv<WT>::v - 1) / (kWaves * PerWaveQkv<WT>::v);
 #define CALL(N) f(QkvR<WT, N>{}, a, Geo{rgrid, 0})
         switch (nch_of<WT>(a.K)) { DAR_NCH_CASES(CALL) }
 #undef CALL
