@@ -75,8 +75,8 @@ class Driver:
         return allst
 
 
-@pytest.mark.parametrize("wtype", ["bf16", "fp8", "int4"])
-def test_paged_continuous_parity(tiny_host, wtype):
+@pytest.mark.parametrize("wtype,graph", [("bf16", False), ("fp8", False), ("int4", False), ("bf16", True)])
+def test_paged_continuous_parity(tiny_host, wtype, graph):
     from dar_decode_frame_amd.session import DarSession, DeviceWeights
     dims, host = tiny_host
     max_len, page, n_pages = 200, 64, 12
@@ -85,7 +85,7 @@ def test_paged_continuous_parity(tiny_host, wtype):
     prompts = {k: synth.gen_prompt(n, dims.vocab_c0, 300 + i) for i, (k, n) in enumerate(lens.items())}
     model = OracleModel(dims, host, wtype=wtype)
     refs = {k: _oracle_frames(model, prompts[k], frames[k], max_len) for k in lens}
-    sess = DarSession(dims, DeviceWeights(dims, host, wtype), max_len, batch=4, paging=(page, n_pages))
+    sess = DarSession(dims, DeviceWeights(dims, host, wtype), max_len, batch=4, paging=(page, n_pages), graph=graph)
     assert sess.pages_free() == n_pages - 1
     drv = Driver(sess, dims, refs)
     drv.add(0, "A", prompts["A"])      # 1 page; crosses into its second page at its 5th frame
@@ -114,6 +114,46 @@ def test_paged_continuous_parity(tiny_host, wtype):
     assert sess.pages_free() == n_pages - 1
     assert sess.position() == [-1, -1, -1, -1]
     assert sess.nonfinite() == 0
+    sess.close()
+
+
+def test_paged_sampling_matches_oracle(tiny_host):
+    """Sampling in a paged context: each sequence draws from the uniforms of
+    its slot at its own frame positions and its repetition window starts at
+    its own first frame, also in a slot whose previous sequence left codes in
+    the committed-code ring at the positions it reaches."""
+    from dar_decode_frame_amd.session import DarSession, DeviceWeights
+    from test_gpu_sampling import PARAMS, _check_codes
+    dims, host = tiny_host
+    fc = dims.n_res + 1
+    max_len, S = 64, 4
+    u = synth.gen_uniforms(max_len, S, fc, 13)
+    spec = {"P": (0, 12, 18), "X": (1, 30, 6), "Q": (2, 5, 15), "Y": (1, 10, 12)}  # slot, prompt, frames
+    prompts = {k: synth.gen_prompt(n, dims.vocab_c0, 500 + i) for i, (k, (_, n, _)) in enumerate(spec.items())}
+    model = OracleModel(dims, host, "bf16")
+    refs, margins = {}, {}
+    for k, (slot, n, f) in spec.items():
+        dec = OracleDecoder(model, max_len, PARAMS, u[:, slot, :])
+        refs[k] = [dec.prefill(prompts[k])] + [dec.decode_frame() for _ in range(f - 1)]
+        margins[k] = dec.margins
+    sess = DarSession(dims, DeviceWeights(dims, host, "bf16"), max_len, batch=S, paging=(64, 8))
+    sess.set_sampling(PARAMS.temperature, PARAMS.top_k, PARAMS.top_p, PARAMS.penalty, PARAMS.window, u)
+    drv = Driver(sess, dims, refs)
+    drv.add(0, "P", prompts["P"])
+    drv.add(1, "X", prompts["X"])
+    for _ in range(3):
+        drv.frame()
+    drv.add(2, "Q", prompts["Q"])
+    for _ in range(3):
+        drv.frame()
+    drv.remove(1)                      # X leaves after 6 frames; Y reuses its slot and ring column
+    drv.add(1, "Y", prompts["Y"])
+    for _ in range(12):
+        drv.frame()
+    assert {k: len(v) for k, v in drv.got.items()} == {k: f for k, (_, _, f) in spec.items()}
+    for k in spec:
+        agree, total, unsafe = _check_codes(drv.got[k], refs[k], margins[k], dims)
+        print(f"\n{k}: sampled codes agree {agree}/{total} ({unsafe} within rounding of a boundary)")
     sess.close()
 
 
