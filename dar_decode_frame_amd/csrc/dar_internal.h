@@ -146,6 +146,10 @@ struct AttnArgs {
   float* part;              // [M][n_kv][nsplit_max][group][head_dim + 2]
   float* out;
   int out_stride;
+  // non-null: the output also as the GEMM input pair hi = bf16(o), lo =
+  // bf16(o - hi), same indexing as out (the next projection's input split)
+  uint16_t* out_hi;
+  uint16_t* out_lo;
   const int* row_pos;       // non-null: position of query row m is row_pos[m] (else *pos + m)
   const int* row_seq;       // non-null: row m reads the cache of sequence row_seq[m]
   long long seq_stride;     // elements between two sequences' caches (paged: between two pages)

@@ -733,6 +733,16 @@ __device__ __forceinline__ size_t attn_kv_base(const AttnArgs& a, int m, int j0,
   return (size_t)sq * a.seq_stride;
 }
 
+// One output value of the attention, and its hi/lo bf16 pair when asked for.
+__device__ __forceinline__ void attn_store(const AttnArgs& a, size_t idx, float v) {
+  a.out[idx] = v;
+  if (a.out_hi) {
+    const uint16_t h = f2bf(v);
+    a.out_hi[idx] = h;
+    a.out_lo[idx] = f2bf(v - bf2f(h));
+  }
+}
+
 // ------------------------------------------------ split-K decode attention --
 
 // One block = one KV head x one split of `chunk` positions for one query row
@@ -867,7 +877,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, int bid, char* lds)
     }
     if (direct) {
       // a single split covers every position: normalise and write the output
-      a.out[(size_t)m * a.out_stride + (kvh * G + h) * HD + e] = num / den;
+      attn_store(a, (size_t)m * a.out_stride + (kvh * G + h) * HD + e, num / den);
     } else {
       float* ps = part + (size_t)s * stride_s + h * (HD + 2);
       ps[e] = num;
@@ -927,7 +937,7 @@ __device__ __forceinline__ void combine_body(const AttnArgs& a, int bid, char* l
     float sum = red[e];
 #pragma unroll
     for (int q = 1; q < R; ++q) sum += red[q * HD + e];
-    a.out[(size_t)m * a.out_stride + (kvh * G + h) * HD + e] = sum / wsh[a.nsplit_max];
+    attn_store(a, (size_t)m * a.out_stride + (kvh * G + h) * HD + e, sum / wsh[a.nsplit_max]);
   }
 }
 
@@ -1432,7 +1442,7 @@ __device__ __forceinline__ void attn_wide_body(const AttnArgs& a, int bid, char*
       num += sm_acc[(w * G + h) * HD + e] * c;
       den += sm_ml[(w * G + h) * 2 + 1] * c;
     }
-    a.out[(size_t)m * a.out_stride + (kvh * G + h) * HD + e] = num / den;
+    attn_store(a, (size_t)m * a.out_stride + (kvh * G + h) * HD + e, num / den);
   }
 }
 

@@ -693,12 +693,13 @@ void add_layer_rows(dar_ctx* c, std::vector<TaskRec>& out, int ch, const dar_lay
   aa.page_table = pm.table;
   aa.page_shift = pm.shift;
   aa.pages_per_seq = pm.per_seq;
+  aa.out_hi = xh;  // the O projection's input split, written by the attention itself
+  aa.out_lo = xl;
   out.push_back(rec(t, K_ATTN, tag));
   if (nsplit_max > 1) {
     t.kind = T_COMBINE;
     out.push_back(rec(t, K_ATTN, tag));
   }
-  out.push_back(rec(t_norm(cn.o, qw, M, qw, nullptr, 0.f, xh, xl), K_OTHER, tag));
   out.push_back(rec(t_gemm(wt, w.wo, w.wo_scale, d, qw, M, xh, xl, nullptr, 0, 0, gp, cap, 1), K_WO, tag));
   out.push_back(rec(t_norm(cn.x, d, M, d, w.ffn_norm, g.rms_eps, xh, xl, nullptr, sums(gp, d, qw)), K_OTHER, tag));
   out.push_back(rec(t_gemm(wt, w.w1, w.w1_scale, F, d, M, xh, xl, nullptr, 0, 0, gp, cap, 1), K_W13, tag));
@@ -1099,12 +1100,13 @@ int prefill_blocks(dar_ctx* c, const int32_t* tokens, int n, hipStream_t s, int 
       aa.part = reinterpret_cast<float*>(b + L.patt);
       aa.out = po;
       aa.out_stride = qw;
+      aa.out_hi = xh;  // the O projection's input split
+      aa.out_lo = xl;
       DAR_HIP(c, launch_task(wt, t, s), "prefill attention");
       if (aa.nsplit_max > 1) {
         t.kind = T_COMBINE;
         DAR_HIP(c, launch_task(wt, t, s), "prefill attention combine");
       }
-      DAR_HIP(c, launch_norm_split(po, qw, M, qw, nullptr, 0.f, xh, xl, s), "prefill split o");
       DAR_HIP(c, gemm(w.wo, w.wo_scale, d, qw, M, nullptr, 0, pgp, 1), "prefill wo");
       DAR_HIP(c,
               launch_norm_split(px, d, M, d, static_cast<const uint16_t*>(w.ffn_norm), g.rms_eps, xh, xl, s, nullptr,
