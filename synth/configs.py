@@ -123,6 +123,9 @@ WORKLOADS = {
     # the longest requests (6 pages each) plus the parking page
     "s2pro_dual_cb16": Workload("s2pro_dual_cb16", S2_DUAL, "bf16", 16, 128, 512, 1024, 4096,
                                 requests=64, frames_min=64, page_len=256, n_pages=97),
+    # and 64 slots serving 256 requests from a pool sized the same way (6 pages per slot)
+    "s2pro_dual_cb64": Workload("s2pro_dual_cb64", S2_DUAL, "bf16", 64, 128, 512, 1024, 4096,
+                                requests=256, frames_min=64, page_len=256, n_pages=385),
 }
 
 
