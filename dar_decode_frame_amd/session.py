@@ -134,6 +134,8 @@ class DarSession:
         self.codes = torch.zeros(batch, self.fc, dtype=torch.int32, device=device)
         self.logits = torch.zeros(batch, self.fc, self.vmax, dtype=torch.float32, device=device)
         self.forced = torch.zeros(batch, self.fc, dtype=torch.int32, device=device)
+        # these fills run on torch's stream; the context writes the buffers on its own
+        torch.cuda.current_stream(device).synchronize()
 
     def close(self):
         if self.ctx:
@@ -192,7 +194,9 @@ class DarSession:
         return (codes[0], logits[0]) if self.batch == 1 else (codes, logits)
 
     def ring(self, first, count):
-        dst = torch.zeros(count, self.batch, self.fc, dtype=torch.int32, device=self.device)
+        dst = torch.empty(count, self.batch, self.fc, dtype=torch.int32, device=self.device)
+        # the copy runs on the context's stream: nothing queued on torch's may touch dst after it
+        torch.cuda.current_stream(self.device).synchronize()
         N.dar_codes(self.ctx, first, count, _dev(dst))
         self.stream.synchronize()
         out = dst.cpu().numpy()
