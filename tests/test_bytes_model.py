@@ -72,3 +72,19 @@ def test_frame_bytes_full_shape():
     assert bm.fast_kv_bytes(dual) == 884_736
     # run sums match frame-by-frame sums
     assert bm.run_bytes(dual, "bf16", 129, 896) == sum(bm.frame_bytes(dual, "bf16", t) for t in range(129, 1025))
+
+
+@pytest.mark.parametrize("name", ["s2pro_dual_cb16", "s2pro_dual_cb64"])
+def test_continuous_workload_pool_covers_its_requests(name):
+    """A continuous-batching workload's page pool holds every slot's longest
+    request (prompt + frames + the slow step computed ahead), and no request
+    passes the position limit of a paged slot (frames up to max_len - 2)."""
+    import synth
+    wl = synth.WORKLOADS[name]
+    lens, frames, _ = synth.gen_requests(wl.requests, wl.prefill_len, wl.prefill_len_max, wl.frames_min,
+                                         wl.decode_frames, wl.dims.vocab_c0, wl.prompt_seed, wl.length_seed)
+    longest = int((lens + frames).max()) + 1
+    assert longest <= wl.max_len - 1
+    per_slot = -(-longest // wl.page_len)
+    assert wl.batch * per_slot <= wl.n_pages - 1
+    assert wl.max_len % wl.page_len == 0 and wl.max_len // wl.page_len <= 64
