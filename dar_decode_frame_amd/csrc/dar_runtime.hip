@@ -1491,6 +1491,33 @@ int paged_frame(dar_ctx* c, const int32_t* forced, int32_t* codes_out, float* lo
   return DAR_OK;
 }
 
+// dar_seq_add's device work on the slow stream: the slot's table row and
+// state, the prompt's prefill through its pages, the codebook-0 head on the
+// last prompt position (h_t kept for the fast AR)
+int seq_add_launch(dar_ctx* c, int slot, const int32_t* tokens, int len) {
+  const dar_config& g = c->cfg;
+  const int d = g.d_model;
+  int st = slow_stream_begin(c);
+  if (st != DAR_OK) return st;
+  hipStream_t s = c->cs.s;
+  // frame 0 sits at the last prompt position len - 1; the next slow step at len
+  DAR_HIP(c, slot_update(c, slot, true, len, len - 1, len - 1, 1), "slot state");
+  st = prefill_blocks(c, tokens, len, s, slot);
+  if (st != DAR_OK) return st;
+  DAR_HIP(c,
+          launch_task(c->wq, t_norm(c->cs.x + (size_t)slot * d, d, 1, d, c->slow_fn, g.rms_eps, c->bxh[0], c->bxl[0],
+                                    c->ht + (size_t)slot * d),
+                      s),
+          "slot head norm");
+  DAR_HIP(c,
+          launch_task(c->wq, t_gemm(W_BF16, c->w0, nullptr, g.vocab_c0, d, 1, c->bxh[0], c->bxl[0],
+                                    c->logits0 + (size_t)slot * g.vocab_c0, g.vocab_c0, 0, c->bgp[0],
+                                    c->L.bgp_floats[0]),
+                      s),
+          "slot head");
+  return slow_stream_end(c);
+}
+
 }  // namespace
 
 int dar_seq_add(dar_ctx* c, int32_t slot, const int32_t* tokens, int32_t len) {
@@ -1518,34 +1545,20 @@ int dar_seq_add(dar_ctx* c, int32_t slot, const int32_t* tokens, int32_t len) {
              std::to_string(c->free_pages.size()) + " free";
     return DAR_E_CAPACITY;
   }
-  const dar_config& g = c->cfg;
-  const int d = g.d_model;
   for (int i = 0; i < need; ++i) {
     c->slot_pages[slot].push_back(c->free_pages.back());
     c->free_pages.pop_back();
   }
   c->slot_on[slot] = 1;
-  int st = slow_stream_begin(c);
-  if (st != DAR_OK) return st;
-  hipStream_t s = c->cs.s;
-  // frame 0 sits at the last prompt position len - 1; the next slow step at len
-  DAR_HIP(c, slot_update(c, slot, true, len, len - 1, len - 1, 1), "slot state");
-  st = prefill_blocks(c, tokens, len, s, slot);
-  if (st != DAR_OK) return st;
-  // the codebook-0 head on the slot's last prompt position (h_t kept for the fast AR)
-  DAR_HIP(c,
-          launch_task(c->wq, t_norm(c->cs.x + (size_t)slot * d, d, 1, d, c->slow_fn, g.rms_eps, c->bxh[0], c->bxl[0],
-                                    c->ht + (size_t)slot * d),
-                      s),
-          "slot head norm");
-  DAR_HIP(c,
-          launch_task(c->wq, t_gemm(W_BF16, c->w0, nullptr, g.vocab_c0, d, 1, c->bxh[0], c->bxl[0],
-                                    c->logits0 + (size_t)slot * g.vocab_c0, g.vocab_c0, 0, c->bgp[0],
-                                    c->L.bgp_floats[0]),
-                      s),
-          "slot head");
-  st = slow_stream_end(c);
-  if (st != DAR_OK) return st;
+  const int st = seq_add_launch(c, slot, tokens, len);
+  if (st != DAR_OK) {
+    // a HIP failure: the host state goes back to the slot being free (the
+    // device may hold part of the work; the context should not be used further)
+    for (int p : c->slot_pages[slot]) c->free_pages.push_back(p);
+    c->slot_pages[slot].clear();
+    c->slot_on[slot] = 0;
+    return st;
+  }
   c->pos_hb[slot] = len - 1;
   c->prefilled = true;
   return DAR_OK;
