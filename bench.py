@@ -118,13 +118,28 @@ def main():
     # timed region: K frames back to back, HIP events on the session stream
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
+    # 64-frame windows at the start and the end of the run (shortest and longest KV)
+    W64 = 64 if args.steps >= 128 else 0
+    ev_w = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     torch.cuda.synchronize()
     ev0.record(stream)
-    for _ in range(args.steps):
+    for i in range(args.steps):
+        if W64 and i == W64:
+            ev_w[0].record(stream)
+        if W64 and i == args.steps - W64:
+            ev_w[1].record(stream)
         sess.decode_frame(want=False)
     ev1.record(stream)
     torch.cuda.synchronize()
     ms = ev0.elapsed_time(ev1)
+    windows = None
+    if W64:
+        windows = {}
+        for name, t0_ev, t1_ev, first in (("first64", ev0, ev_w[0], 0), ("last64", ev_w[1], ev1, args.steps - W64)):
+            wms = t0_ev.elapsed_time(t1_ev)
+            wbytes = bm.run_bytes(dims, wl.wtype, wl.prefill_len + 1 + first, W64)
+            windows[name] = {"kv_positions": [wl.prefill_len + 1 + first, wl.prefill_len + first + W64],
+                             "frames_s": round(W64 * 1000.0 / wms, 2), "gb_s": round(wbytes / (wms / 1000.0) / 1e9, 1)}
     fps = args.steps * 1000.0 / ms
     t_first = wl.prefill_len + 1
     alg_bytes = bm.run_bytes(dims, wl.wtype, t_first, args.steps)
@@ -198,7 +213,7 @@ def main():
                    "layers_fast": dims.n_layers_fast, "residual_codebooks": dims.n_res,
                    "graph": args.graph, "sampling": SAMPLING if args.sample else None},
         "achieved_gb_s": round(gbs / 1e9, 1),
-        "hbm_frac": round(gbs / HBM_PEAK, 4),
+        "hbm_frac": round(gbs / HBM_PEAK, 4), "windows": windows,
         "alg_bytes_per_frame_avg": int(alg_bytes // args.steps),
         "prefill_ms": round(prefill_ms, 2),
         "nonfinite_logits": n_bad,
