@@ -213,7 +213,8 @@ def main():
                    "layers_fast": dims.n_layers_fast, "residual_codebooks": dims.n_res,
                    "graph": args.graph, "sampling": SAMPLING if args.sample else None},
         "achieved_gb_s": round(gbs / 1e9, 1),
-        "hbm_frac": round(gbs / HBM_PEAK, 4), "windows": windows,
+        "hbm_frac": round(gbs / HBM_PEAK, 4), "achieved_gib_s": round(gbs / bm.GIB, 1),
+        "pages_formula": pages_formula(dims, wl, fps), "windows": windows,
         "alg_bytes_per_frame_avg": int(alg_bytes // args.steps),
         "prefill_ms": round(prefill_ms, 2),
         "nonfinite_logits": n_bad,
@@ -467,6 +468,24 @@ def bench_continuous(args, wl):
         "nonfinite_logits": n_bad, "roofline": roof, "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def pages_formula(dims, wl, fps):
+    """The tuna-fish README's own decode-step bytes ("Inference estimation":
+    parameters without embeddings, the fast AR once per pass, plus the static
+    KV of max_length slow and R+1 fast positions, one byte count per element of
+    the weight type) applied to this model, and the frame rate in its unit
+    (GiB/s), the unit of the README's speed table."""
+    from dar_decode_frame_amd import bytes_model as bm
+    c = bm.param_counts(dims)
+    p_slow = c["slow_layers"] + c["slow_final_norm"] + c["slow_head"]
+    p_fast = bm.fast_params_wo_emb(dims) if dims.has_fast else 0
+    passes = dims.n_res if dims.has_fast else 0
+    elems = bm.pages_decode_elements(p_slow, p_fast, dims.n_layers_slow, dims.n_layers_fast,
+                                     dims.n_heads_kv * dims.head_dim, wl.max_len, dims.n_res + 1, passes)
+    per_elem = {"bf16": 2.0, "fp8": 1.0, "int8": 1.0, "int4": 0.5}[wl.wtype]
+    step = elems * per_elem
+    return {"bytes_per_step": int(step), "gib_s": round(fps * step / bm.GIB, 1)}
 
 
 def measured_traffic(kind, workload):
