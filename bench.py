@@ -566,8 +566,22 @@ def cpu_baseline(dims, wl, host, prompt):
         frames += 1
     t_dec = time.time() - t0
     log(f"oracle: build {t_build:.1f}s, prefill {t_prefill:.1f}s, {frames} frames {t_dec:.1f}s on {threads} threads")
+    # the same decode on one BLAS thread, a shorter sample (about 6 s)
+    one = None
+    try:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            f1, t1 = 0, time.time()
+            while dec.pos < wl.max_len and (f1 < 1 or time.time() - t1 < 6.0):
+                dec.decode_frame()
+                f1 += 1
+            one = round(f1 / (time.time() - t1), 4) if f1 else None
+        log(f"oracle on one thread: {f1} frames, {one} frames/s")
+    except ImportError:
+        pass
     del model, dec
     return {"value": round(frames / t_dec, 4), "unit": "frames/s", "cores": threads, "kind": "oracle",
+            "value_one_thread": one,
             "sample": f"{wl.name}: oracle (NumPy fp32) prefill {wl.prefill_len} as one causal block, then "
                       f"{frames} decode frames at positions {wl.prefill_len}..{wl.prefill_len + frames - 1} timed "
                       f"({t_dec:.1f} s, budget about 12 s); weight conversion {t_build:.1f} s and "
