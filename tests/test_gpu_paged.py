@@ -75,7 +75,8 @@ class Driver:
         return allst
 
 
-@pytest.mark.parametrize("wtype,graph", [("bf16", False), ("fp8", False), ("int4", False), ("bf16", True)])
+@pytest.mark.parametrize("wtype,graph", [("bf16", False), ("fp8", False), ("int8", False), ("int4", False),
+                                         ("bf16", True)])
 def test_paged_continuous_parity(tiny_host, wtype, graph):
     from dar_decode_frame_amd.session import DarSession, DeviceWeights
     dims, host = tiny_host
@@ -215,6 +216,24 @@ def test_paged_position_limit(tiny_host):
     sess.seq_remove(1)
     with pytest.raises(N.DarError) as e:
         sess.decode_frame(want=False)                        # no sequence left
+    assert e.value.status == N.DAR_E_STATE
+    with pytest.raises(N.DarError) as e:
+        sess.seq_remove(1)                                   # already free
+    assert e.value.status == N.DAR_E_STATE
+    for slot in (-1, 2):
+        with pytest.raises(N.DarError) as e:
+            sess.seq_add(slot, synth.gen_prompt(4, dims.vocab_c0, 6))
+        assert e.value.status == N.DAR_E_INVAL
+        with pytest.raises(N.DarError) as e:
+            sess.seq_remove(slot)
+        assert e.value.status == N.DAR_E_INVAL
+    with pytest.raises(N.DarError) as e:
+        sess.seq_add(0, synth.gen_prompt(64, dims.vocab_c0, 7))   # len == max_len
+    assert e.value.status == N.DAR_E_CAPACITY
+    assert sess.pages_free() == 2
+    # a paged context takes no lockstep prefill
+    with pytest.raises(N.DarError) as e:
+        sess.prefill([synth.gen_prompt(4, dims.vocab_c0, 8)] * 2, want=False)
     assert e.value.status == N.DAR_E_STATE
     sess.close()
 
