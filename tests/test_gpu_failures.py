@@ -1,0 +1,82 @@
+"""Failure detection and repeatability on the GPU.
+
+A NaN planted in one row of the fast head's weights makes that codebook
+entry's logit non-finite in every fast pass: the context's non-finite counter
+must see it after the frames (read by dar_nonfinite), the argmax must never
+pick the entry (NaN counts as -infinity), and dar_reset must clear the
+counter. Batch 1 (register kernels, one-workgroup commit) and a lockstep batch
+of two (GEMM head, per-row commit).
+
+A paged context running the same schedule of joins and frames twice, in two
+fresh contexts, returns bit-identical codes and logits (every split-K sum is
+reduced in a fixed order; no float atomics).
+"""
+import numpy as np
+import pytest
+
+import synth
+
+pytestmark = pytest.mark.gpu
+
+BF16_QNAN = 0x7FC0
+
+
+@pytest.fixture(scope="module")
+def tiny_host():
+    d = synth.DIMS["tiny"]
+    return d, synth.gen_weights(d, 0)
+
+
+@pytest.mark.parametrize("batch", [1, 2])
+def test_nan_weight_sets_the_nonfinite_counter(tiny_host, batch):
+    from dar_decode_frame_amd.session import DarSession, DeviceWeights
+    dims, host = tiny_host
+    row = 17
+    bad = dict(host)
+    head = np.array(host["fast.head"], copy=True)
+    head.view(np.uint16)[row, 0] = BF16_QNAN
+    bad["fast.head"] = head
+    sess = DarSession(dims, DeviceWeights(dims, bad, "bf16"), 32, batch=batch)
+    prompts = [synth.gen_prompt(8 + 3 * b, dims.vocab_c0, 40 + b) for b in range(batch)]
+    frames = [sess.prefill(prompts[0] if batch == 1 else prompts)]
+    frames += [sess.decode_frame() for _ in range(2)]
+    assert sess.nonfinite() > 0
+    for codes, logits in frames:
+        codes = np.asarray(codes).reshape(batch, -1)
+        logits = np.asarray(logits).reshape(batch, dims.n_res + 1, -1)
+        assert np.all(codes[:, 1:] != row)
+        assert np.all(np.isnan(logits[:, 1:, row]))
+        assert np.all(np.isfinite(logits[:, 1:, :dims.vocab_res][:, :, np.arange(dims.vocab_res) != row]))
+    sess.reset()
+    assert sess.nonfinite() == 0
+    sess.close()
+
+
+def test_paged_runs_repeat_bit_for_bit(tiny_host):
+    from dar_decode_frame_amd.session import DarSession, DeviceWeights
+    dims, host = tiny_host
+    weights = DeviceWeights(dims, host, "bf16")
+    prompts = [synth.gen_prompt(n, dims.vocab_c0, 60 + n) for n in (70, 9, 33)]
+
+    def run():
+        sess = DarSession(dims, weights, 160, batch=3, paging=(64, 8))
+        out = []
+        sess.seq_add(0, prompts[0])
+        sess.seq_add(2, prompts[1])
+        for _ in range(4):
+            out.append(sess.decode_frame())
+        sess.seq_add(1, prompts[2])
+        for _ in range(6):
+            out.append(sess.decode_frame())
+        sess.seq_remove(2)
+        for _ in range(3):
+            out.append(sess.decode_frame())
+        sess.close()
+        return out
+
+    a, b = run(), run()
+    busy = [[0, 2]] * 4 + [[0, 1, 2]] * 6 + [[0, 1]] * 3  # rows of free slots are undefined
+    assert len(a) == len(b) == len(busy)
+    for (ca, la), (cb, lb), rows in zip(a, b, busy):
+        assert np.array_equal(ca[rows], cb[rows])
+        assert np.array_equal(la[rows].view(np.uint32), lb[rows].view(np.uint32))
