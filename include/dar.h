@@ -160,7 +160,8 @@ int dar_create(const dar_config* cfg, const dar_weights* weights, void* workspac
  * [batch][1+n_res] argmax codes of frame 0. logits_out: NULL or device fp32
  * [batch][1+n_res][max(vocab_c0, vocab_res)] (entries past a codebook's size
  * are left untouched). Token ids are not range-checked on the host (they are
- * in device memory); an out-of-range id is clamped to the table. */
+ * in device memory); an out-of-range id is clamped to the table and counted
+ * with the anomalies dar_nonfinite reports. */
 int dar_prefill(dar_ctx* ctx, int32_t batch, const int32_t* tokens, const int32_t* lens_host,
                 const int32_t* forced, int32_t* codes_out, float* logits_out);
 
@@ -199,7 +200,8 @@ int dar_set_graph(dar_ctx* ctx, int32_t enable);
  * [count][max_batch][1+n_res], stream-ordered. */
 int dar_codes(dar_ctx* ctx, int32_t first, int32_t count, int32_t* dst);
 
-/* Non-finite logit counter since create/reset (synchronises the stream). */
+/* Anomaly counter since create/reset: non-finite logits and out-of-range
+ * prompt ids (synchronises the stream). */
 int dar_nonfinite(dar_ctx* ctx, int32_t* count_out);
 
 /* Algorithmic bytes of one decode frame that attends over T slow positions:

@@ -80,3 +80,27 @@ def test_paged_runs_repeat_bit_for_bit(tiny_host):
     for (ca, la), (cb, lb), rows in zip(a, b, busy):
         assert np.array_equal(ca[rows], cb[rows])
         assert np.array_equal(la[rows].view(np.uint32), lb[rows].view(np.uint32))
+
+
+def test_out_of_range_prompt_id_is_clamped_and_counted(tiny_host):
+    """Prompt ids are not range-checked on the host: an id past the table is
+    clamped to its last row (the run equals the one with that id replaced) and
+    counted with the anomalies dar_nonfinite reports."""
+    from dar_decode_frame_amd.session import DarSession, DeviceWeights
+    dims, host = tiny_host
+    weights = DeviceWeights(dims, host, "bf16")
+    prompt = synth.gen_prompt(10, dims.vocab_c0, 77)
+    bad, clamped = prompt.copy(), prompt.copy()
+    bad[4] = dims.vocab_c0 + 5
+    clamped[4] = dims.vocab_c0 - 1
+    out = []
+    for p in (bad, clamped):
+        sess = DarSession(dims, weights, 32)
+        frames = [sess.prefill(p)] + [sess.decode_frame() for _ in range(2)]
+        out.append((frames, sess.nonfinite()))
+        sess.close()
+    (fa, na), (fb, nb) = out
+    assert na == 1 and nb == 0
+    for (ca, la), (cb, lb) in zip(fa, fb):
+        assert np.array_equal(ca, cb)
+        assert np.array_equal(la.view(np.uint32), lb.view(np.uint32))
