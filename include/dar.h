@@ -400,7 +400,9 @@ int dar_kind_time(dar_ctx* ctx, double* ms_total, int32_t* launches);
  * of capacity cap; *n_out is the number of launches). Kinds: 0 qkv,
  * 1 attention, 2 wo, 3 w13, 4 w2, 5 codebook head, 6 other. Layer tags: slow
  * layer l is l; fast layer l of pass k is 1000k + l. The frame advances the
- * state like dar_decode_frame(ctx, NULL, NULL, NULL). Synchronises. */
+ * state like dar_decode_frame(ctx, NULL, NULL, NULL). Synchronises. A paged
+ * context is refused (DAR_E_STATE): its frames take pages in
+ * dar_decode_frame, so time them with dar_time_kind. */
 int dar_profile_frame(dar_ctx* ctx, int32_t cap, float* ms_out, int32_t* kind_out,
                       int32_t* layer_out, int32_t* n_out);
 
