@@ -238,8 +238,9 @@ def test_paged_position_limit(tiny_host):
     sess.close()
 
 
-def test_fullshape_paged_matches_oracle():
-    """Full shape (36 + 4 layers, d 2560, bf16) in the continuous-batching
+@pytest.mark.parametrize("name", ["s2pro_dual_bf16", "s2pro_dual_fp8", "s2pro_dual_int8", "s2pro_dual_int4"])
+def test_fullshape_paged_matches_oracle(name):
+    """Full shape (36 + 4 layers, d 2560; bf16, fp8, int8, int4) in the continuous-batching
     bench's configuration (16 slots, 256-position pages, 97 pages, max length
     4096): one slot decodes the oracle reference runs while three other slots
     hold other sequences; its frames must meet the full-shape bar against the
@@ -249,12 +250,12 @@ def test_fullshape_paged_matches_oracle():
 
     from dar_decode_frame_amd.session import DarSession, DeviceWeights
     from test_gpu_fullshape import _compare, _golden, _random_frames
-    wl = synth.WORKLOADS["s2pro_dual_bf16"]
+    wl = synth.WORKLOADS[name]
     cb = synth.WORKLOADS["s2pro_dual_cb16"]
     dims = wl.dims
-    ref = _golden("s2pro_dual_bf16")
+    ref = _golden(name)
     host = synth.gen_weights(dims, wl.weight_seed)
-    dw = DeviceWeights(dims, host, "bf16")
+    dw = DeviceWeights(dims, host, wl.wtype)
     del host
     sess = DarSession(dims, dw, cb.max_len, batch=cb.batch, paging=(cb.page_len, cb.n_pages))
     prompt = synth.gen_prompt(wl.prefill_len, dims.vocab_c0, wl.prompt_seed)
@@ -289,9 +290,9 @@ def test_fullshape_paged_matches_oracle():
     codes, logits = got[-1]
     _compare(late["frame"], codes, logits, dims, stats)
     agree = stats["agree"] / stats["n"]
-    print(f"\npaged full shape: max rel {max(stats['rel']):.3e}, agreement {agree:.4f} over {stats['n']} vectors, "
-          f"exact failures {stats['exact_fail']}")
-    assert max(stats["rel"]) <= TOL["bf16"], stats
+    print(f"\npaged full shape {name}: max rel {max(stats['rel']):.3e}, agreement {agree:.4f} over {stats['n']} "
+          f"vectors, exact failures {stats['exact_fail']}")
+    assert max(stats["rel"]) <= TOL[wl.wtype], stats
     assert not stats["exact_fail"], stats
     assert agree >= 0.99, stats
     assert sess.nonfinite() == 0
