@@ -7,6 +7,10 @@ pick the entry (NaN counts as -infinity), and dar_reset must clear the
 counter. Batch 1 (register kernels, one-workgroup commit) and a lockstep batch
 of two (GEMM head, per-row commit).
 
+Argmax ties: two identical rows of the fast head whose logit dominates give
+bit-equal logits, and the commit picks the lower index (the oracle's np.argmax
+rule), in the one-workgroup commit and in the per-row batched commit.
+
 A paged context running the same schedule of joins and frames twice, in two
 fresh contexts, returns bit-identical codes and logits (every split-K sum is
 reduced in a fixed order; no float atomics).
@@ -104,3 +108,30 @@ def test_out_of_range_prompt_id_is_clamped_and_counted(tiny_host):
     for (ca, la), (cb, lb) in zip(fa, fb):
         assert np.array_equal(ca, cb)
         assert np.array_equal(la.view(np.uint32), lb.view(np.uint32))
+
+
+@pytest.mark.parametrize("batch", [1, 3])
+def test_argmax_ties_pick_the_lower_index(tiny_host, batch):
+    from dar_decode_frame_amd.session import DarSession, DeviceWeights
+    dims, host = tiny_host
+    lo, hi, neg = 5, 9, 12
+    tied = dict(host)
+    head = np.array(host["fast.head"], copy=True)
+    bits = head.view(np.uint16)
+    bits[lo, :] = 0x3F80   # +1.0: logit = sum of the normalised input, far above the other rows
+    bits[hi, :] = 0x3F80
+    bits[neg, :] = 0xBF80  # -1.0: wins when that sum is negative
+    tied["fast.head"] = head
+    sess = DarSession(dims, DeviceWeights(dims, tied, "bf16"), 32, batch=batch)
+    prompts = [synth.gen_prompt(6 + 2 * b, dims.vocab_c0, 90 + b) for b in range(batch)]
+    frames = [sess.prefill(prompts[0] if batch == 1 else prompts)]
+    frames += [sess.decode_frame() for _ in range(3)]
+    seen = set()
+    for codes, logits in frames:
+        codes = np.asarray(codes).reshape(batch, -1)[:, 1:]
+        logits = np.asarray(logits).reshape(batch, dims.n_res + 1, -1)[:, 1:, :]
+        assert np.array_equal(logits[..., lo].view(np.uint32), logits[..., hi].view(np.uint32))
+        assert np.all((codes == lo) | (codes == neg)), codes
+        seen.update(np.unique(codes).tolist())
+    assert lo in seen
+    sess.close()
