@@ -7,9 +7,13 @@ One slot stays free throughout (its parked rows run every frame). Prompts
 span several pages, and sequences cross page boundaries while decoding.
 Every sequence is teacher-forced with its own oracle greedy frames and held to
 the bar of a single sequence: logits rel-L2, argmax agreement, exact codes
-above the margin. Pool exhaustion and the position limit return
-DAR_E_CAPACITY and change nothing: the run continues after a removal and
-still matches the oracle.
+above the margin (bf16, fp8, int8, int4, and bf16 with graph replay). Sampling
+draws from each slot's uniforms with its own repetition window. Pool
+exhaustion and the position limit return DAR_E_CAPACITY and change nothing:
+the run continues after a removal and still matches the oracle. At full shape,
+in the continuous-batching bench's configuration, one slot beside three other
+sequences meets the full-shape bar against the stored oracle references for
+every weight type.
 """
 import numpy as np
 import pytest
