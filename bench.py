@@ -546,11 +546,7 @@ def cpu_baseline(dims, wl, host, prompt):
     """The oracle on this host's cores: prefill 128 then two decode frames; decode timed."""
     import numpy as np
     from oracle import OracleDecoder, OracleModel
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max((i.get("num_threads", 0) for i in threadpool_info()), default=os.cpu_count())
-    except Exception:
-        threads = os.cpu_count()
+    threads = _blas_threads()
     t0 = time.time()
     model = OracleModel(dims, host, wtype=wl.wtype)
     t_build = time.time() - t0
@@ -586,7 +582,7 @@ def cpu_baseline(dims, wl, host, prompt):
                       f"{frames} decode frames at positions {wl.prefill_len}..{wl.prefill_len + frames - 1} timed "
                       f"({t_dec:.1f} s, budget about 12 s); weight conversion {t_build:.1f} s and "
                       f"prefill {t_prefill:.1f} s not timed",
-            "cpu_model": _cpu_model()}
+            **_host_cpus()}
 
 
 def cpu_baseline_batched(dims, wl, host, lens, prompts):
@@ -595,11 +591,7 @@ def cpu_baseline_batched(dims, wl, host, lens, prompts):
     sequences (prefill, then frames alternating between them until about 12 s
     of decode) gives its aggregate frames/s."""
     from oracle import OracleDecoder, OracleModel
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max((i.get("num_threads", 0) for i in threadpool_info()), default=os.cpu_count())
-    except Exception:
-        threads = os.cpu_count()
+    threads = _blas_threads()
     t0 = time.time()
     model = OracleModel(dims, host, wtype=wl.wtype)
     t_build = time.time() - t0
@@ -625,7 +617,25 @@ def cpu_baseline_batched(dims, wl, host, lens, prompts):
                       f"between them timed ({t_dec:.1f} s, budget about 12 s; the oracle decodes one sequence at a "
                       f"time, so this is its aggregate rate); weight conversion {t_build:.1f} s and prefill "
                       f"{t_prefill:.1f} s not timed",
-            "cpu_model": _cpu_model()}
+            **_host_cpus()}
+
+
+def _blas_threads():
+    """Threads the oracle's BLAS calls actually run on (the `cores` it used)."""
+    try:
+        from threadpoolctl import threadpool_info
+        return max((i.get("num_threads", 0) for i in threadpool_info()), default=os.cpu_count())
+    except Exception:
+        return os.cpu_count()
+
+
+def _host_cpus():
+    """The host's CPU model, its logical CPU count and the CPUs this process may run on."""
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = None
+    return {"cpu_model": _cpu_model(), "host_cpu_count": os.cpu_count(), "usable_cpus": usable}
 
 
 def _cpu_model():

@@ -21,6 +21,7 @@
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <atomic>
 
 #include "dar_internal.h"
 #include "dar_sample.h"
@@ -1817,13 +1818,15 @@ static bool with_body(const Task& t, F&& f) {
 }
 #undef DAR_NCH_CASES
 
-// kernels whose dynamic LDS may exceed the default 64 KB get the 160 KB limit once
+// kernels whose dynamic LDS may exceed the default 64 KB get the 160 KB limit
+// once per kernel; the flag is atomic because contexts on other host threads
+// launch the same kernels (setting the attribute twice is harmless)
 template <typename KernelT>
-static hipError_t allow_lds(KernelT kern, size_t lds, bool& done) {
-  if (lds <= 65536 || done) return hipSuccess;
+static hipError_t allow_lds(KernelT kern, size_t lds, std::atomic<bool>& done) {
+  if (lds <= 65536 || done.load(std::memory_order_acquire)) return hipSuccess;
   const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-  if (e == hipSuccess) done = true;
+  if (e == hipSuccess) done.store(true, std::memory_order_release);
   return e;
 }
 
@@ -1832,7 +1835,7 @@ static hipError_t allow_lds(KernelT kern, size_t lds, bool& done) {
 template <class A>
 static hipError_t go1(const typename A::Args& a, const Geo& g, hipStream_t s, bool prep, hipEvent_t ev0,
                       hipEvent_t ev1) {
-  static bool big = false;
+  static std::atomic<bool> big{false};  // one flag per kernel instantiation
   hipError_t e = allow_lds(k_one<A>, g.lds, big);
   if (e != hipSuccess || prep) return e;
   if (ev0 || ev1)

@@ -1736,7 +1736,7 @@ int dar_set_graph(dar_ctx* c, int32_t enable) {
 
 int dar_codes(dar_ctx* c, int32_t first, int32_t count, int32_t* dst) {
   if (!c || !dst) return DAR_E_INVAL;
-  if (first < 0 || count < 0 || first + count > c->cfg.max_len) {
+  if (first < 0 || count < 0 || (int64_t)first + count > c->cfg.max_len) {
     c->err = "ring range out of bounds";
     return DAR_E_INVAL;
   }
@@ -2117,6 +2117,7 @@ int dar_profile_frame(dar_ctx* c, int32_t cap, float* ms_out, int32_t* kind_out,
   }
   *n_out = (int32_t)i;
   c->pos_host += 1;
+  for (int& p : c->pos_hb) p += 1;
   return DAR_OK;
 }
 

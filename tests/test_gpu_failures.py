@@ -135,3 +135,30 @@ def test_argmax_ties_pick_the_lower_index(tiny_host, batch):
         seen.update(np.unique(codes).tolist())
     assert lo in seen
     sess.close()
+
+
+def test_ring_bounds_checked_in_64_bits_and_profile_frame_advances_position(tiny_host):
+    """dar_codes rejects a range whose end overflows int32 (first near
+    INT32_MAX) before any HIP call, and dar_profile_frame advances the
+    position dar_position reports exactly as dar_decode_frame does."""
+    from dar_decode_frame_amd import native as N
+    from dar_decode_frame_amd.session import DarSession, DeviceWeights
+    dims, host = tiny_host
+    sess = DarSession(dims, DeviceWeights(dims, host, "bf16"), 32)
+    prompt = synth.gen_prompt(8, dims.vocab_c0, 7)
+    sess.prefill(prompt)
+    assert sess.position() == 8
+    sess.decode_frame()
+    assert sess.position() == 9
+    sess.profile_frame()
+    assert sess.position() == 10
+    sess.decode_frame()
+    assert sess.position() == 11
+    import torch
+    dst = torch.zeros(33 * (dims.n_res + 1), dtype=torch.int32, device="cuda")
+    for first, count in [(2 ** 31 - 1, 1), (2 ** 31 - 16, 32), (1, 2 ** 31 - 1), (-1, 1), (0, -1), (0, 33)]:
+        with pytest.raises(N.DarError) as e:
+            N.dar_codes(sess.ctx, first, count, dst.data_ptr())
+        assert e.value.status == N.DAR_E_INVAL
+    assert sess.ring(8, 3).shape == (3, dims.n_res + 1)
+    sess.close()

@@ -187,3 +187,31 @@ def test_round_bf16_nearest_even():
     v = np.random.default_rng(0).standard_normal(100000).astype(np.float32) * 10
     ref = torch.from_numpy(v).to(torch.bfloat16).to(torch.float32).numpy()
     assert np.array_equal(round_bf16(v), ref)
+
+
+def test_bf16_to_f32_every_bit_pattern():
+    """The widening every bf16 weight goes through, over all 65,536 patterns.
+
+    bf16 is the upper half of an IEEE binary32 word (same sign, exponent and
+    top seven fraction bits), so the widening is exact. Checked against torch's
+    own uint16 -> bfloat16 view -> float32 cast (a library routine): finite
+    values, infinities and zeros bit for bit, NaNs by class (NaN in, NaN out,
+    sign kept), plus hand-decoded patterns from the format definition.
+    """
+    import torch
+    from oracle import bf16_to_f32
+    bits = np.arange(1 << 16, dtype=np.uint16)
+    got = bf16_to_f32(bits)
+    assert got.dtype == np.float32 and got.shape == bits.shape
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float32).numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan].view(np.uint32), ref[~nan].view(np.uint32))
+    assert np.array_equal(np.signbit(got[nan]), np.signbit(ref[nan]))
+    # exponent 0x7F, fraction 0 -> 1; 0x4049 -> 3.140625; 0xC000 -> -2;
+    # smallest subnormal 0x0001 -> 2^-133; 0x7F80 -> +inf; 0x8000 -> -0
+    assert got[0x3F80] == 1.0 and got[0x4049] == 3.140625 and got[0xC000] == -2.0
+    assert got[0x0001] == np.float32(2.0 ** -133)
+    assert got[0x7F80] == np.inf and got[0xFF80] == -np.inf
+    assert got[0x8000] == 0.0 and np.signbit(got[0x8000])
+    assert np.isnan(got[0x7FC0]) and np.isnan(got[0xFFFF])
