@@ -19,6 +19,9 @@ Pinned against what the pages and the mathematics fix (see tests/test_oracle_*):
   sampling.py  temperature / top-k / top-p / repetition-window sampling of
             one code (pyshine fish-speech tour, "Why You Need This"; reading
             in its header)
+  codec.py  RVQ decode and the DAC-style convolutional decoder, codes to
+            waveform (tuna-fish README, intro and "Audio tokenizer speedtest";
+            pyshine fish-speech tour, "Why You Need This"; readings in its header)
 End-to-end logits have no printed values on the pages: parity unpinned at that
 level; the pins are the parts and the invariants that tie them together.
 """
@@ -43,4 +46,13 @@ from .model import (  # noqa: F401
     greedy_argmax,
     full_recompute_slow,
     full_recompute_fast,
+)
+from .codec import (  # noqa: F401
+    rvq_decode,
+    snake,
+    conv1d,
+    conv_transpose1d,
+    CodecParams,
+    codec_decode,
+    receptive_halo,
 )

@@ -16,3 +16,12 @@ from .configs import (  # noqa: F401
 )
 from .weights import gen_weights, gen_tensor, f32_to_bf16_bits  # noqa: F401
 from .prompts import gen_prompt, gen_ragged_prompts, gen_requests, gen_sample_logits, gen_uniforms  # noqa: F401
+from .codec import (  # noqa: F401
+    CodecDims,
+    CodecWorkload,
+    CODEC_DIMS,
+    CODEC_WORKLOADS,
+    codec_tensor_specs,
+    gen_codec_weights,
+    gen_codes,
+)
