@@ -63,6 +63,8 @@ def main():
     from dar_decode_frame_amd import native as N
     from dar_decode_frame_amd.session import DarSession, DeviceWeights
 
+    if args.workload in synth.CODEC_WORKLOADS:
+        return bench_codec(args, synth.CODEC_WORKLOADS[args.workload])
     wl = synth.WORKLOADS[args.workload]
     dims = wl.dims
     if wl.requests > 0:
@@ -473,6 +475,149 @@ def bench_continuous(args, wl):
     print(json.dumps(out), flush=True)
 
 
+CODEC_TAGS = {0: "rvq", 1: "in_conv", 2: "up", 3: "res_conv7", 4: "res_conv1", 5: "out_conv"}
+MFMA_BF16_PEAK = 2.5e15
+
+
+def codec_launch_cost(d, frames, tag):
+    """(FLOPs, bytes) one launch of a codec kind moves: the convolution's
+    multiply-adds (2 per weight per output row per tap) and the activations it
+    must read and write (fp32 residual stream, bf16 residual-unit hidden rows,
+    bf16 latent frames; weights counted once)."""
+    kind, blk = tag % 16, tag // 16
+    w = d.widths
+    if kind == 0:
+        return 0, frames * d.n_codebooks * d.latent_dim * 2 + frames * d.latent_dim * 2
+    if kind == 1:
+        return (2 * frames * w[0] * d.latent_dim * d.kernel,
+                frames * d.latent_dim * 2 + frames * w[0] * 4 + w[0] * d.latent_dim * d.kernel * 2)
+    rows_in = frames
+    for s in d.rates[:blk]:
+        rows_in *= s
+    cin, cout, s = w[blk], w[blk + 1], d.rates[blk]
+    rows = rows_in * s
+    if kind == 2:
+        return 2 * rows * cout * cin * 2, rows_in * cin * 4 + rows * cout * 4 + cin * cout * 2 * s * 2
+    if kind == 3:
+        return 2 * rows * cout * cout * d.kernel, rows * cout * 4 + rows * cout * 2 + cout * cout * d.kernel * 2
+    if kind == 4:
+        return 2 * rows * cout * cout, rows * cout * 2 + 2 * rows * cout * 4 + cout * cout * 2
+    rows_out = frames * d.hop
+    return 2 * rows_out * w[-1] * d.kernel, rows_out * w[-1] * 4 + rows_out * 4
+
+
+def bench_codec(args, wl):
+    """RVQ codec decode of one clip per step (codes resident in HBM, audio
+    written to HBM): audio seconds decoded per second (x realtime) and the
+    real-time factor; the dominant launch kind against bf16 MFMA peak."""
+    import numpy as np
+    import torch
+
+    import synth
+    from dar_decode_frame_amd.session import CodecSession
+
+    d = wl.dims
+    steps = args.steps if args.steps is not None else 20
+    dev = torch.device("cuda:0")
+    t0 = time.time()
+    host = synth.gen_codec_weights(d, wl.weight_seed)
+    codes = synth.gen_codes(wl.frames, d, wl.code_seed)
+    sess = CodecSession(d, host, wl.frames, dev)
+    sess.load_codes(codes)
+    log(f"codec weights ready in {time.time() - t0:.1f}s; {wl.frames} frames -> {wl.frames * d.hop} samples")
+    for _ in range(args.warmup):
+        sess.decode(frames=wl.frames, want=False)
+    sess.stream.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(sess.stream)
+    for _ in range(steps):
+        sess.decode(frames=wl.frames, want=False)
+    ev1.record(sess.stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / steps
+    audio_s = wl.frames * d.hop / d.sample_rate
+    xrt = audio_s / (ms / 1000.0)
+    log(f"timed {steps} decodes: {ms:.3f} ms each, {xrt:.0f}x realtime, RTF {ms / 1000.0 / audio_s:.2e}")
+    audio = sess.decode(frames=wl.frames)
+    flops = sum(codec_launch_cost(d, wl.frames, t)[0] for _, t in sess.profile(wl.frames))
+    roof = None
+    if args.profile_frames > 0:
+        recs = []
+        for _ in range(max(1, args.profile_frames)):
+            recs += sess.profile(wl.frames)
+        totals = {}
+        for m, t in recs:
+            totals[t] = totals.get(t, 0.0) + m
+        dom = max((t for t in totals if t % 16 != 0), key=totals.get)
+        times = [m for m, t in recs if t == dom]
+        avg = sum(times) / len(times)
+        f, b = codec_launch_cost(d, wl.frames, dom)
+        achieved = f / (avg / 1000.0)
+        share = {f"{CODEC_TAGS[t % 16]}{'' if t % 16 in (0, 1, 5) else t // 16}": round(v / sum(totals.values()), 4)
+                 for t, v in sorted(totals.items(), key=lambda kv: -kv[1])}
+        name = f"{CODEC_TAGS[dom % 16]}{'' if dom % 16 in (0, 1, 5) else dom // 16}"
+        roof = {"kernel": name, "bound": "mfma", "achieved": round(achieved / 1e12, 1),
+                "peak": MFMA_BF16_PEAK / 1e12, "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK, 4),
+                "traffic": measured_traffic(name, wl.name, "dar_codec.hip"), "flops_per_launch": f,
+                "bytes_per_launch": b, "avg_launch_us": round(avg * 1000, 2), "launches_timed": len(times),
+                "hbm_gb_s": round(b / (avg / 1000.0) / 1e9, 1), "launches_per_step": len(recs) // max(1, args.profile_frames),
+                "step_time_share": share}
+        log(f"dominant kind {name}: {avg * 1000:.1f} us/launch, {achieved / 1e12:.0f} TFLOP/s; shares {share}")
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline_codec(wl, host, codes)
+    out = {
+        "metric": "RVQ codec decode x realtime (audio seconds per second) @batch1",
+        "value": round(xrt, 1),
+        "unit": "x realtime",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded random-init codec weights and codes)",
+        "config": {"workload": wl.name, "batch": 1, "frames": wl.frames, "samples": wl.frames * d.hop,
+                   "sample_rate": d.sample_rate, "codebooks": d.n_codebooks, "latent_dim": d.latent_dim,
+                   "channels": d.channels, "rates": list(d.rates)},
+        "rtf": round(ms / 1000.0 / audio_s, 8),
+        "tflop_s": round(flops / (ms / 1000.0) / 1e12, 1),
+        "flops_per_step": flops,
+        "audio_checksum": round(float(np.abs(audio).sum()), 3),
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    sess.close()
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline_codec(wl, host, codes):
+    """The codec oracle (NumPy fp64, bf16 activations) on this host's cores, on
+    a window of the clip's frames sized to about 12 s of CPU work."""
+    import numpy as np
+    from oracle import CodecParams, codec_decode
+    d = wl.dims
+    threads = _blas_threads()
+    P = CodecParams(d, host)
+    n, t_dec = 4, 0.0
+    while True:
+        t0 = time.time()
+        codec_decode(codes[:n], P, act="bf16")
+        t_dec = time.time() - t0
+        if t_dec > 6.0 or n >= wl.frames:
+            break
+        n = min(wl.frames, max(n + 1, int(n * 12.0 / max(t_dec, 1e-3))))
+    audio_s = n * d.hop / d.sample_rate
+    log(f"oracle: {n} frames ({audio_s:.3f} s of audio) in {t_dec:.1f}s on {threads} threads")
+    return {"value": round(audio_s / t_dec, 4), "unit": "x realtime", "cores": threads, "kind": "oracle",
+            "sample": f"{wl.name}: oracle (NumPy fp64, bf16 activations) decode of the first {n} frames "
+                      f"({audio_s:.3f} s of audio) in {t_dec:.1f} s; weight conversion not timed",
+            **_host_cpus()}
+
+
 def pages_formula(dims, wl, fps):
     """The tuna-fish README's own decode-step bytes ("Inference estimation":
     parameters without embeddings, the fast AR once per pass, plus the static
@@ -491,7 +636,7 @@ def pages_formula(dims, wl, fps):
     return {"bytes_per_step": int(step), "gib_s": round(fps * step / bm.GIB, 1)}
 
 
-def measured_traffic(kind, workload):
+def measured_traffic(kind, workload, source="dar_kernels.hip"):
     """HBM bytes per launch of `kind` from the committed counter summary
     (profiles/hbm_traffic_<kind>_<workload>.md), or None when there is none or
     the kernel source has changed since the counters were taken."""
@@ -505,7 +650,7 @@ def measured_traffic(kind, workload):
     m_h = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)
     if not m_t or not m_h:
         return None
-    src = os.path.join(ROOT, "dar_decode_frame_amd", "csrc", "dar_kernels.hip")
+    src = os.path.join(ROOT, "dar_decode_frame_amd", "csrc", source)
     if hashlib.sha256(open(src, "rb").read()).hexdigest() != m_h.group(1):
         return None
     return int(m_t.group(1))

@@ -17,7 +17,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libdar.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
-SOURCES = ["dar_kernels.hip", "dar_prefill.hip", "dar_runtime.hip"]
+SOURCES = ["dar_kernels.hip", "dar_prefill.hip", "dar_runtime.hip", "dar_codec.hip"]
 ARCH = "gfx950"
 
 

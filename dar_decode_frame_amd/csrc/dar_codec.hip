@@ -1,0 +1,890 @@
+// RVQ codec decode on gfx950: codes -> 44.1 kHz audio (include/dar_codec.h).
+//
+// What is computed (tuna-fish README, intro and "Audio tokenizer speedtest";
+// pyshine fish-speech tour, "Why You Need This"): the ten selected codebook
+// vectors of a frame are summed into the latent frame, then a DAC-style
+// convolutional decoder upsamples it 2048-fold: an input convolution, blocks of
+// Snake + transposed convolution + residual units, and Snake + an output
+// convolution + tanh.
+//
+// Every convolution with more than one output channel is one implicit GEMM on
+// MFMA (v_mfma_f32_32x32x16_bf16): output rows (time) x output channels, the
+// sum over input channels and taps. A transposed convolution with kernel
+// 2 stride and padding stride / 2 splits into `stride` phases: output row
+// t stride + r is a two-tap convolution of input rows {t, t - 1} or
+// {t + 1, t} with the kernel taps that land on phase r, so each phase is the
+// same GEMM with its own two taps (blockIdx.z). A workgroup stages, per chunk of
+// 32 input channels, the input window its output rows need under every tap
+// (rows t0 + min offset .. t0 + BM + max offset, Snake applied and rounded to
+// bf16 on the way in, zeros outside [0, T)) and the chunk of every tap's
+// weights into LDS, then each wave runs its 32-row x 32 NT-column MFMA tiles
+// over the taps. Activations are time-major [T][C], so a window row is one
+// contiguous run of channels. The epilogue adds the bias and either the
+// residual (fp32 out) or applies the next Snake and rounds to bf16 (the input
+// of the residual unit's 1-tap convolution).
+
+#include <hip/hip_ext.h>
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <algorithm>
+#include <atomic>
+#include <cmath>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/dar.h"
+#include "../../include/dar_codec.h"
+
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kThreads = 256;
+constexpr int kChunk = 32;      // input channels per staged chunk (two MFMA k-steps)
+constexpr int kMaxTaps = 7;
+constexpr int kMaxOff = 64;     // largest |tap offset| of a convolution
+constexpr int kMaxOffs = 32;    // taps x phases of one launch
+constexpr int kOutRows = 256;   // output samples per workgroup of the output convolution
+
+__device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float(((uint32_t)h) << 16); }
+
+// fp32 -> bf16, nearest even (finite values)
+__device__ __forceinline__ uint32_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ float snake(float x, float a) {
+  const float s = sinf(a * x);
+  return x + s * s / a;
+}
+
+struct ConvArgs {
+  const float* xf;          // fp32 input [T][Cin] (or null)
+  const uint16_t* xb;       // bf16 input [T][Cin] (or null)
+  const uint16_t* alpha_in; // Snake of the fp32 input on load (null: none)
+  int T, Cin, Cout;
+  const uint16_t* W;        // [nphase][ntap][Cout][Cin] bf16
+  int nphase, ntap;
+  int off[kMaxOffs];        // input row offset of tap j of phase z: off[z * ntap + j]
+  const uint16_t* bias;     // bf16 [Cout]
+  float* yf;                // fp32 output [T * nphase][Cout], row t * nphase + z
+  const float* res;         // added to the fp32 output (may alias yf)
+  int tanh_out;
+  uint16_t* yb;             // bf16 output: Snake(acc + bias, alpha_out), rounded
+  const uint16_t* alpha_out;
+};
+
+// LDS row r of 32 bf16 (64 B, four 16-byte units): unit u sits at slot
+// u ^ ((r >> 1) & 3), so any eight consecutive rows read at one unit hit
+// eight distinct 16-byte bank groups.
+__device__ __forceinline__ int lds_at(int r, int u) { return r * 64 + ((u ^ ((r >> 1) & 3)) << 4); }
+
+template <int WM, int WN, int NT, bool XB16, bool YB16>
+__global__ __launch_bounds__(kThreads) void k_conv(ConvArgs a) {
+  constexpr int BM = 32 * WM, BN = 32 * NT * WN;
+  static_assert(WM * WN == 4, "four waves");
+  extern __shared__ __align__(16) char smem[];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave % WM, wn = wave / WM;
+  const int z = blockIdx.z;
+  const int t0 = blockIdx.x * BM, n0 = blockIdx.y * BN;
+  const int* off = a.off + z * a.ntap;
+  int omin = off[0], omax = off[0];
+  for (int j = 1; j < a.ntap; ++j) {
+    omin = min(omin, off[j]);
+    omax = max(omax, off[j]);
+  }
+  const int wrows = BM + omax - omin;
+  char* xs = smem;
+  char* ws = smem + wrows * 64;
+  const uint16_t* Wz = a.W + (size_t)z * a.ntap * a.Cout * a.Cin;
+  f32x16 acc[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[nt][v] = 0.f;
+  const int half = lane >> 5, l32 = lane & 31;
+  for (int c0 = 0; c0 < a.Cin; c0 += kChunk) {
+    // the input window of this chunk: row w is input row t0 + omin + w
+    for (int i = tid; i < wrows * 4; i += kThreads) {
+      const int w = i >> 2, u = i & 3;
+      const int row = t0 + omin + w;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (row >= 0 && row < a.T) {
+        if constexpr (XB16) {
+          v = *reinterpret_cast<const u32x4*>(a.xb + (size_t)row * a.Cin + c0 + 8 * u);
+        } else {
+          const f32x4* src = reinterpret_cast<const f32x4*>(a.xf + (size_t)row * a.Cin + c0 + 8 * u);
+          const f32x4 p = src[0], q = src[1];
+          float f[8] = {p.x, p.y, p.z, p.w, q.x, q.y, q.z, q.w};
+          if (a.alpha_in) {
+            const u32x4 al = *reinterpret_cast<const u32x4*>(a.alpha_in + c0 + 8 * u);
+            const uint32_t aw[4] = {al.x, al.y, al.z, al.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) f[e] = snake(f[e], bf2f((uint16_t)(aw[e >> 1] >> (16 * (e & 1)))));
+          }
+          v.x = f2bf(f[0]) | (f2bf(f[1]) << 16);
+          v.y = f2bf(f[2]) | (f2bf(f[3]) << 16);
+          v.z = f2bf(f[4]) | (f2bf(f[5]) << 16);
+          v.w = f2bf(f[6]) | (f2bf(f[7]) << 16);
+        }
+      }
+      *reinterpret_cast<u32x4*>(xs + lds_at(w, u)) = v;
+    }
+    // every tap's weights of this chunk: row j * BN + n holds output channel n0 + n
+    for (int i = tid; i < a.ntap * BN * 4; i += kThreads) {
+      const int r = i >> 2, u = i & 3;
+      const int j = r / BN, n = n0 + r % BN;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (n < a.Cout) v = *reinterpret_cast<const u32x4*>(Wz + ((size_t)j * a.Cout + n) * a.Cin + c0 + 8 * u);
+      *reinterpret_cast<u32x4*>(ws + lds_at(r, u)) = v;
+    }
+    __syncthreads();
+    for (int j = 0; j < a.ntap; ++j) {
+      const int xr = wm * 32 + l32 + off[j] - omin;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const int u = 2 * ks + half;
+        const bf16x8 A = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(xs + lds_at(xr, u)));
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          const int wr = j * BN + (wn * NT + nt) * 32 + l32;
+          const bf16x8 B = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(ws + lds_at(wr, u)));
+          acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B, acc[nt], 0, 0, 0);
+        }
+      }
+    }
+    __syncthreads();
+  }
+  // lane holds output channel n of its tiles; accumulator v holds output row
+  // t0 + 32 wm + (v % 4) + 4 half + 8 (v / 4)
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int n = n0 + (wn * NT + nt) * 32 + l32;
+    if (n >= a.Cout) continue;
+    const float b = bf2f(a.bias[n]);
+    const float ao = YB16 ? bf2f(a.alpha_out[n]) : 0.f;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int t = t0 + wm * 32 + (v & 3) + 4 * half + 8 * (v >> 2);
+      if (t >= a.T) continue;
+      const size_t at = ((size_t)t * a.nphase + z) * a.Cout + n;
+      float val = acc[nt][v] + b;
+      if constexpr (YB16) {
+        a.yb[at] = (uint16_t)f2bf(snake(val, ao));
+      } else {
+        if (a.res) val += a.res[at];
+        if (a.tanh_out) val = tanhf(val);
+        a.yf[at] = val;
+      }
+    }
+  }
+}
+
+// The output convolution (one channel): Snake, K taps, bias, tanh. A
+// workgroup makes kOutRows samples from its window of input rows, staged
+// channel-major in LDS (after Snake, rounded to bf16) so that consecutive
+// lanes read consecutive samples.
+__global__ __launch_bounds__(kThreads) void k_conv_out(const float* x, const uint16_t* alpha, int T, int C,
+                                                     const uint16_t* w, const uint16_t* b, int K, float* y) {
+  extern __shared__ __align__(16) char smem[];
+  const int halfk = (K - 1) / 2, W = kOutRows + K - 1;
+  uint16_t* xs = reinterpret_cast<uint16_t*>(smem);  // [C][W]
+  float* wsm = reinterpret_cast<float*>(smem + (((size_t)C * W * 2 + 15) & ~(size_t)15));  // [C][K]
+  const int t0 = blockIdx.x * kOutRows, tid = threadIdx.x;
+  for (int i = tid; i < C * K; i += kThreads) wsm[i] = bf2f(w[i]);
+  for (int i = tid; i < W * C; i += kThreads) {
+    const int r = i / C, c = i % C;
+    const int row = t0 - halfk + r;
+    uint16_t v = 0;
+    if (row >= 0 && row < T) v = (uint16_t)f2bf(snake(x[(size_t)row * C + c], bf2f(alpha[c])));
+    xs[c * W + r] = v;
+  }
+  __syncthreads();
+  const int t = t0 + tid;
+  if (t >= T) return;
+  float acc = 0.f;
+  for (int c = 0; c < C; ++c)
+    for (int j = 0; j < K; ++j) acc = fmaf(wsm[c * K + j], bf2f(xs[c * W + tid + j]), acc);
+  y[t] = tanhf(acc + bf2f(b[0]));
+}
+
+// z[t] = sum_k table_k[code[t][k]] over the codebooks in order, fp32 sums
+// rounded to bf16 (the input convolution's operand). A thread makes eight
+// channels of one frame.
+struct RvqArgs {
+  const uint16_t* tab[32];
+  const int* codes;  // [T][nq]
+  int T, nq, V, D;
+  uint16_t* z;       // [T][D]
+  int* anomalies;
+};
+
+__global__ __launch_bounds__(kThreads) void k_rvq(RvqArgs a) {
+  const int per = a.D / 8;
+  const long long idx = (long long)blockIdx.x * kThreads + threadIdx.x;
+  if (idx >= (long long)a.T * per) return;
+  const int t = (int)(idx / per), u = (int)(idx % per);
+  float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int k = 0; k < 32; ++k) {
+    if (k >= a.nq) break;
+    int c = a.codes[(size_t)t * a.nq + k];
+    if (c < 0 || c >= a.V) {
+      if (u == 0) atomicAdd(a.anomalies, 1);
+      c = c < 0 ? 0 : a.V - 1;
+    }
+    const u32x4 v = *reinterpret_cast<const u32x4*>(a.tab[k] + (size_t)c * a.D + 8 * u);
+    const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s[e] += bf2f((uint16_t)(wv[e >> 1] >> (16 * (e & 1))));
+  }
+  u32x4 o;
+  o.x = f2bf(s[0]) | (f2bf(s[1]) << 16);
+  o.y = f2bf(s[2]) | (f2bf(s[3]) << 16);
+  o.z = f2bf(s[4]) | (f2bf(s[5]) << 16);
+  o.w = f2bf(s[6]) | (f2bf(s[7]) << 16);
+  *reinterpret_cast<u32x4*>(a.z + (size_t)t * a.D + 8 * u) = o;
+}
+
+// [Cout][Cin][K] -> [K][Cout][Cin]
+__global__ void k_relayout_conv(const uint16_t* src, int Cout, int Cin, int K, uint16_t* dst) {
+  const long long n = (long long)Cout * Cin * K;
+  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (long long)gridDim.x * blockDim.x) {
+    const int c = (int)(i % Cin);
+    const long long r = i / Cin;
+    const int o = (int)(r % Cout), j = (int)(r / Cout);
+    dst[i] = src[((size_t)o * Cin + c) * K + j];
+  }
+}
+
+// transposed convolution [Cin][Cout][2s] -> [phase r][tap j][Cout][Cin], tap j
+// of phase r being kernel index kidx[2 r + j]
+struct PhaseTaps {
+  int k[kMaxOffs];
+};
+__global__ void k_relayout_convT(const uint16_t* src, int Cin, int Cout, int s, PhaseTaps taps, uint16_t* dst) {
+  const long long n = (long long)2 * s * Cout * Cin;
+  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (long long)gridDim.x * blockDim.x) {
+    const int c = (int)(i % Cin);
+    const long long r = i / Cin;
+    const int o = (int)(r % Cout), pj = (int)(r / Cout);
+    dst[i] = src[((size_t)c * Cout + o) * (2 * s) + taps.k[pj]];
+  }
+}
+
+// ---- host side -----------------------------------------------------------
+
+struct TileCfg {
+  int wm, wn, nt;
+  int bm() const { return 32 * wm; }
+  int bn() const { return 32 * nt * wn; }
+};
+// largest tiles first
+constexpr TileCfg kCfgs[] = {{4, 1, 4}, {4, 1, 3}, {2, 2, 2}, {2, 2, 1}, {1, 4, 1}, {4, 1, 1}};
+constexpr int kNumCfgs = sizeof(kCfgs) / sizeof(kCfgs[0]);
+
+long long cfg_grid(const TileCfg& c, int rows, int Cout, int nphase) {
+  return (long long)((rows + c.bm() - 1) / c.bm()) * ((Cout + c.bn() - 1) / c.bn()) * nphase;
+}
+
+// The tile shape of a convolution: among the shapes whose column width
+// divides Cout (else all), the largest that still gives every CU two
+// workgroups, else the one with the most workgroups.
+int pick_cfg(int rows, int Cout, int nphase) {
+  bool any_exact = false;
+  for (int i = 0; i < kNumCfgs; ++i) any_exact |= Cout % kCfgs[i].bn() == 0;
+  int best = -1;
+  long long best_grid = -1;
+  for (int i = 0; i < kNumCfgs; ++i) {
+    if (any_exact && Cout % kCfgs[i].bn() != 0) continue;
+    const long long g = cfg_grid(kCfgs[i], rows, Cout, nphase);
+    if (g >= 512) return i;
+    if (g > best_grid) {
+      best_grid = g;
+      best = i;
+    }
+  }
+  return best;
+}
+
+size_t conv_lds(const TileCfg& c, int span, int ntap) {
+  return (size_t)(c.bm() + span) * 64 + (size_t)ntap * c.bn() * 64;
+}
+
+template <typename KernelT>
+hipError_t allow_lds(KernelT kern, size_t lds, std::atomic<bool>& done) {
+  if (lds <= 65536 || done.load(std::memory_order_acquire)) return hipSuccess;
+  const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+  if (e == hipSuccess) done.store(true, std::memory_order_release);
+  return e;
+}
+
+template <int WM, int WN, int NT, bool XB16, bool YB16>
+hipError_t go_conv(const ConvArgs& a, dim3 grid, size_t lds, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  static std::atomic<bool> big{false};  // one flag per kernel instantiation
+  hipError_t e = allow_lds(k_conv<WM, WN, NT, XB16, YB16>, lds, big);
+  if (e != hipSuccess) return e;
+  if (e0 || e1)
+    hipExtLaunchKernelGGL((k_conv<WM, WN, NT, XB16, YB16>), grid, dim3(kThreads), lds, s, e0, e1, 0, a);
+  else
+    hipLaunchKernelGGL((k_conv<WM, WN, NT, XB16, YB16>), grid, dim3(kThreads), lds, s, a);
+  return hipGetLastError();
+}
+
+template <bool XB16, bool YB16>
+hipError_t go_conv_cfg(int ci, const ConvArgs& a, dim3 grid, size_t lds, hipStream_t s, hipEvent_t e0,
+                       hipEvent_t e1) {
+  switch (ci) {
+    case 0: return go_conv<4, 1, 4, XB16, YB16>(a, grid, lds, s, e0, e1);
+    case 1: return go_conv<4, 1, 3, XB16, YB16>(a, grid, lds, s, e0, e1);
+    case 2: return go_conv<2, 2, 2, XB16, YB16>(a, grid, lds, s, e0, e1);
+    case 3: return go_conv<2, 2, 1, XB16, YB16>(a, grid, lds, s, e0, e1);
+    case 4: return go_conv<1, 4, 1, XB16, YB16>(a, grid, lds, s, e0, e1);
+    default: return go_conv<4, 1, 1, XB16, YB16>(a, grid, lds, s, e0, e1);
+  }
+}
+
+// Launch one convolution (rows = input rows per phase).
+hipError_t launch_conv(const ConvArgs& a, hipStream_t s, hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr) {
+  const int ci = pick_cfg(a.T, a.Cout, a.nphase);
+  const TileCfg& c = kCfgs[ci];
+  int span = 0;
+  for (int z = 0; z < a.nphase; ++z) {
+    int lo = a.off[z * a.ntap], hi = lo;
+    for (int j = 1; j < a.ntap; ++j) {
+      lo = std::min(lo, a.off[z * a.ntap + j]);
+      hi = std::max(hi, a.off[z * a.ntap + j]);
+    }
+    span = std::max(span, hi - lo);
+  }
+  const size_t lds = conv_lds(c, span, a.ntap);
+  const dim3 grid((a.T + c.bm() - 1) / c.bm(), (a.Cout + c.bn() - 1) / c.bn(), a.nphase);
+  const bool xb = a.xb != nullptr, yb = a.yb != nullptr;
+  if (xb && !yb) return go_conv_cfg<true, false>(ci, a, grid, lds, s, e0, e1);
+  if (!xb && yb) return go_conv_cfg<false, true>(ci, a, grid, lds, s, e0, e1);
+  if (!xb && !yb) return go_conv_cfg<false, false>(ci, a, grid, lds, s, e0, e1);
+  return hipErrorInvalidValue;  // bf16 in and bf16 out: not a layer of the decoder
+}
+
+size_t out_lds(int C, int K) { return (((size_t)C * (kOutRows + K - 1) * 2 + 15) & ~(size_t)15) + (size_t)C * K * 4; }
+
+hipError_t launch_conv_out(const float* x, const uint16_t* alpha, int T, int C, const uint16_t* w, const uint16_t* b,
+                           int K, float* y, hipStream_t s, hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr) {
+  static std::atomic<bool> big{false};
+  const size_t lds = out_lds(C, K);
+  hipError_t e = allow_lds(k_conv_out, lds, big);
+  if (e != hipSuccess) return e;
+  const dim3 grid((T + kOutRows - 1) / kOutRows);
+  if (e0 || e1)
+    hipExtLaunchKernelGGL(k_conv_out, grid, dim3(kThreads), lds, s, e0, e1, 0, x, alpha, T, C, w, b, K, y);
+  else
+    hipLaunchKernelGGL(k_conv_out, grid, dim3(kThreads), lds, s, x, alpha, T, C, w, b, K, y);
+  return hipGetLastError();
+}
+
+// kernel taps of a transposed convolution (kernel 2s, padding s/2) that land on
+// output phase r: input rows t and t - 1 (first half of the phases) or t + 1
+// and t (second half)
+void convT_taps(int s, int* kidx, int* offs) {
+  for (int r = 0; r < s; ++r) {
+    const int q = r + s / 2;
+    if (q < s) {
+      kidx[2 * r] = q;
+      offs[2 * r] = 0;
+      kidx[2 * r + 1] = q + s;
+      offs[2 * r + 1] = -1;
+    } else {
+      kidx[2 * r] = q - s;
+      offs[2 * r] = 1;
+      kidx[2 * r + 1] = q;
+      offs[2 * r + 1] = 0;
+    }
+  }
+}
+
+void conv_taps(int K, int dil, int* offs) {
+  for (int j = 0; j < K; ++j) offs[j] = dil * (j - (K - 1) / 2);
+}
+
+hipError_t relayout_conv(const uint16_t* src, int Cout, int Cin, int K, uint16_t* dst, hipStream_t s) {
+  hipLaunchKernelGGL(k_relayout_conv, dim3(1024), dim3(kThreads), 0, s, src, Cout, Cin, K, dst);
+  return hipGetLastError();
+}
+
+hipError_t relayout_convT(const uint16_t* src, int Cin, int Cout, int st, uint16_t* dst, hipStream_t s) {
+  PhaseTaps t{};
+  int offs[kMaxOffs];
+  convT_taps(st, t.k, offs);
+  hipLaunchKernelGGL(k_relayout_convT, dim3(1024), dim3(kThreads), 0, s, src, Cin, Cout, st, t, dst);
+  return hipGetLastError();
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+thread_local std::string g_codec_error;
+
+struct CodecLayout {
+  size_t in_w;
+  size_t up_w[DAR_CODEC_MAX_BLOCKS];
+  size_t w1[DAR_CODEC_MAX_BLOCKS][DAR_CODEC_MAX_UNITS], w2[DAR_CODEC_MAX_BLOCKS][DAR_CODEC_MAX_UNITS];
+  size_t z, xa, xb, h, anom, total;
+  size_t act_elems;  // largest rows x channels of any activation
+};
+
+int width(const dar_codec_config* c, int i) { return c->channels >> i; }
+
+CodecLayout codec_layout(const dar_codec_config* c) {
+  CodecLayout L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align_up(off + bytes);
+    return at;
+  };
+  const int K = c->kernel_size;
+  L.in_w = take((size_t)2 * K * c->channels * c->latent_dim);
+  size_t rows = (size_t)c->max_frames;
+  L.act_elems = rows * c->channels;
+  for (int i = 0; i < c->n_blocks; ++i) {
+    const int cin = width(c, i), cout = width(c, i + 1), s = c->rates[i];
+    L.up_w[i] = take((size_t)2 * 2 * s * cout * cin);
+    for (int u = 0; u < c->n_units; ++u) {
+      L.w1[i][u] = take((size_t)2 * K * cout * cout);
+      L.w2[i][u] = take((size_t)2 * cout * cout);
+    }
+    rows *= s;
+    L.act_elems = std::max(L.act_elems, rows * cout);
+  }
+  L.z = take((size_t)2 * c->max_frames * c->latent_dim);
+  L.xa = take(4 * L.act_elems);
+  L.xb = take(4 * L.act_elems);
+  L.h = take(2 * L.act_elems);
+  L.anom = take(sizeof(int) * 4);
+  L.total = off;
+  return L;
+}
+
+int validate_codec(const dar_codec_config* c, std::string& why) {
+  if (!c) {
+    why = "config is NULL";
+    return DAR_E_INVAL;
+  }
+  auto bad = [&](const char* m) {
+    why = m;
+    return DAR_E_INVAL;
+  };
+  if (c->n_codebooks < 1 || c->n_codebooks > 32) return bad("n_codebooks must be in [1, 32]");
+  if (c->codebook_size < 1) return bad("codebook_size must be >= 1");
+  if (c->latent_dim < 32 || c->latent_dim % 32 || c->latent_dim > 8192) return bad("latent_dim: multiple of 32 in [32, 8192]");
+  if (c->channels < 32 || c->channels % 32 || c->channels > 8192) return bad("channels: multiple of 32 in [32, 8192]");
+  if (c->n_blocks < 1 || c->n_blocks > DAR_CODEC_MAX_BLOCKS) return bad("n_blocks must be in [1, 8]");
+  const int last = c->channels >> c->n_blocks;
+  if (last < 32 || last % 32 || (last << c->n_blocks) != c->channels)
+    return bad("every block width (channels >> i) must be a multiple of 32");
+  if (c->n_units < 1 || c->n_units > DAR_CODEC_MAX_UNITS) return bad("n_units must be in [1, 4]");
+  const int K = c->kernel_size;
+  if (K < 1 || K > kMaxTaps || K % 2 == 0) return bad("kernel_size must be odd, in [1, 7]");
+  for (int u = 0; u < c->n_units; ++u)
+    if (c->dilations[u] < 1 || (long long)(K - 1) / 2 * c->dilations[u] > kMaxOff)
+      return bad("dilations must be >= 1 with (kernel_size - 1) / 2 * dilation <= 64");
+  long long hop = 1;
+  for (int i = 0; i < c->n_blocks; ++i) {
+    if (c->rates[i] < 2 || c->rates[i] > 16 || c->rates[i] % 2) return bad("rates must be even, in [2, 16]");
+    hop *= c->rates[i];
+  }
+  if (out_lds(last, K) > 160 * 1024) return bad("last block width too large for the output convolution's LDS window");
+  if (c->max_frames < 1) return bad("max_frames must be >= 1");
+  if ((long long)c->max_frames * hop * c->channels >= (1LL << 31)) return bad("max_frames * hop * channels must be < 2^31");
+  return DAR_OK;
+}
+
+bool al16(const void* p) { return p && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace
+
+struct dar_codec {
+  dar_codec_config cfg{};
+  CodecLayout L{};
+  hipStream_t stream = nullptr;
+  char* ws = nullptr;
+  std::vector<const uint16_t*> tables;
+  const uint16_t* in_b = nullptr;
+  dar_codec_block blocks[DAR_CODEC_MAX_BLOCKS];
+  const uint16_t *out_alpha = nullptr, *out_w = nullptr, *out_b = nullptr;
+  std::string err;
+  std::vector<hipEvent_t> events;
+};
+
+namespace {
+
+int codec_hip_fail(dar_codec* c, hipError_t e, const char* what) {
+  const std::string msg = std::string(what) + ": " + hipGetErrorString(e);
+  if (c)
+    c->err = msg;
+  else
+    g_codec_error = msg;
+  return DAR_E_HIP;
+}
+
+#define CODEC_HIP(ctx, call, what)                              \
+  do {                                                          \
+    hipError_t e_ = (call);                                     \
+    if (e_ != hipSuccess) return codec_hip_fail(ctx, e_, what); \
+  } while (0)
+
+const uint16_t* U16(const void* p) { return static_cast<const uint16_t*>(p); }
+
+// One decode: every launch in order, each optionally timed (events[2i], [2i+1]).
+int run_decode(dar_codec* c, const int32_t* codes, int frames, float* audio, bool timed, std::vector<int>* tags) {
+  const dar_codec_config& g = c->cfg;
+  const CodecLayout& L = c->L;
+  hipStream_t s = c->stream;
+  const int K = g.kernel_size;
+  size_t ev = 0;
+  auto evs = [&](hipEvent_t*& e0, hipEvent_t*& e1) {
+    if (!timed) return;
+    while (c->events.size() < 2 * (ev + 1)) {
+      hipEvent_t e;
+      if (hipEventCreate(&e) != hipSuccess) return;
+      c->events.push_back(e);
+    }
+    e0 = &c->events[2 * ev];
+    e1 = &c->events[2 * ev + 1];
+    ++ev;
+  };
+  auto tag = [&](int t) {
+    if (tags) tags->push_back(t);
+  };
+  uint16_t* z = reinterpret_cast<uint16_t*>(c->ws + L.z);
+  float* bufs[2] = {reinterpret_cast<float*>(c->ws + L.xa), reinterpret_cast<float*>(c->ws + L.xb)};
+  uint16_t* h = reinterpret_cast<uint16_t*>(c->ws + L.h);
+  int* anom = reinterpret_cast<int*>(c->ws + L.anom);
+
+  RvqArgs ra{};
+  for (int k = 0; k < g.n_codebooks; ++k) ra.tab[k] = c->tables[k];
+  ra.codes = codes;
+  ra.T = frames;
+  ra.nq = g.n_codebooks;
+  ra.V = g.codebook_size;
+  ra.D = g.latent_dim;
+  ra.z = z;
+  ra.anomalies = anom;
+  {
+    hipEvent_t *e0 = nullptr, *e1 = nullptr;
+    evs(e0, e1);
+    const long long n = (long long)frames * (g.latent_dim / 8);
+    const dim3 grid((unsigned)((n + kThreads - 1) / kThreads));
+    if (timed && e0)
+      hipExtLaunchKernelGGL(k_rvq, grid, dim3(kThreads), 0, s, *e0, *e1, 0, ra);
+    else
+      hipLaunchKernelGGL(k_rvq, grid, dim3(kThreads), 0, s, ra);
+    CODEC_HIP(c, hipGetLastError(), "rvq sum");
+    tag(0);
+  }
+  auto conv = [&](ConvArgs& a, int t) -> int {
+    hipEvent_t *e0 = nullptr, *e1 = nullptr;
+    evs(e0, e1);
+    CODEC_HIP(c, launch_conv(a, s, e0 ? *e0 : nullptr, e1 ? *e1 : nullptr), "codec convolution");
+    tag(t);
+    return DAR_OK;
+  };
+  int st;
+  {
+    ConvArgs a{};
+    a.xb = z;
+    a.T = frames;
+    a.Cin = g.latent_dim;
+    a.Cout = g.channels;
+    a.W = reinterpret_cast<const uint16_t*>(c->ws + L.in_w);
+    a.nphase = 1;
+    a.ntap = K;
+    conv_taps(K, 1, a.off);
+    a.bias = c->in_b;
+    a.yf = bufs[0];
+    if ((st = conv(a, 1)) != DAR_OK) return st;
+  }
+  int cur = 0, rows = frames;
+  for (int i = 0; i < g.n_blocks; ++i) {
+    const dar_codec_block& B = c->blocks[i];
+    const int cin = width(&g, i), cout = width(&g, i + 1), sr = g.rates[i];
+    ConvArgs a{};
+    a.xf = bufs[cur];
+    a.alpha_in = U16(B.alpha);
+    a.T = rows;
+    a.Cin = cin;
+    a.Cout = cout;
+    a.W = reinterpret_cast<const uint16_t*>(c->ws + L.up_w[i]);
+    a.nphase = sr;
+    a.ntap = 2;
+    int kidx[kMaxOffs];
+    convT_taps(sr, kidx, a.off);
+    a.bias = U16(B.up_b);
+    a.yf = bufs[cur ^ 1];
+    if ((st = conv(a, 2 + 16 * i)) != DAR_OK) return st;
+    cur ^= 1;
+    rows *= sr;
+    for (int u = 0; u < g.n_units; ++u) {
+      const dar_codec_unit& U = B.units[u];
+      ConvArgs a1{};
+      a1.xf = bufs[cur];
+      a1.alpha_in = U16(U.alpha1);
+      a1.T = rows;
+      a1.Cin = cout;
+      a1.Cout = cout;
+      a1.W = reinterpret_cast<const uint16_t*>(c->ws + L.w1[i][u]);
+      a1.nphase = 1;
+      a1.ntap = K;
+      conv_taps(K, g.dilations[u], a1.off);
+      a1.bias = U16(U.b1);
+      a1.yb = h;
+      a1.alpha_out = U16(U.alpha2);
+      if ((st = conv(a1, 3 + 16 * i)) != DAR_OK) return st;
+      ConvArgs a2{};
+      a2.xb = h;
+      a2.T = rows;
+      a2.Cin = cout;
+      a2.Cout = cout;
+      a2.W = reinterpret_cast<const uint16_t*>(c->ws + L.w2[i][u]);
+      a2.nphase = 1;
+      a2.ntap = 1;
+      a2.off[0] = 0;
+      a2.bias = U16(U.b2);
+      a2.yf = bufs[cur];
+      a2.res = bufs[cur];
+      if ((st = conv(a2, 4 + 16 * i)) != DAR_OK) return st;
+    }
+  }
+  {
+    hipEvent_t *e0 = nullptr, *e1 = nullptr;
+    evs(e0, e1);
+    CODEC_HIP(c,
+              launch_conv_out(bufs[cur], c->out_alpha, rows, width(&g, g.n_blocks), c->out_w, c->out_b, K, audio, s,
+                              e0 ? *e0 : nullptr, e1 ? *e1 : nullptr),
+              "codec output convolution");
+    tag(5);
+  }
+  return DAR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dar_codec_workspace_bytes(const dar_codec_config* cfg, size_t* bytes_out) {
+  std::string why;
+  const int st = validate_codec(cfg, why);
+  if (st != DAR_OK) {
+    g_codec_error = why;
+    return st;
+  }
+  if (!bytes_out) return DAR_E_INVAL;
+  *bytes_out = codec_layout(cfg).total;
+  return DAR_OK;
+}
+
+int dar_codec_create(const dar_codec_config* cfg, const dar_codec_weights* w, void* workspace, size_t workspace_bytes,
+                     void* stream, dar_codec** out) {
+  std::string why;
+  int st = validate_codec(cfg, why);
+  if (st != DAR_OK) {
+    g_codec_error = why;
+    return st;
+  }
+  if (!w || !out || !workspace || (reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1))) {
+    g_codec_error = "weights, out and a 256-byte aligned workspace are required";
+    return DAR_E_INVAL;
+  }
+  const CodecLayout L = codec_layout(cfg);
+  if (workspace_bytes < L.total) {
+    g_codec_error = "workspace smaller than dar_codec_workspace_bytes";
+    return DAR_E_WORKSPACE;
+  }
+  if (!w->tables || !w->blocks || !al16(w->in_w) || !al16(w->in_b) || !al16(w->out_alpha) || !al16(w->out_w) ||
+      !al16(w->out_b)) {
+    g_codec_error = "a weight pointer is NULL or not 16-byte aligned";
+    return DAR_E_INVAL;
+  }
+  for (int k = 0; k < cfg->n_codebooks; ++k)
+    if (!al16(w->tables[k])) {
+      g_codec_error = "a codebook table pointer is NULL or not 16-byte aligned";
+      return DAR_E_INVAL;
+    }
+  for (int i = 0; i < cfg->n_blocks; ++i) {
+    const dar_codec_block& B = w->blocks[i];
+    bool ok = al16(B.alpha) && al16(B.up_w) && al16(B.up_b);
+    for (int u = 0; u < cfg->n_units; ++u) {
+      const dar_codec_unit& U = B.units[u];
+      ok = ok && al16(U.alpha1) && al16(U.w1) && al16(U.b1) && al16(U.alpha2) && al16(U.w2) && al16(U.b2);
+    }
+    if (!ok) {
+      g_codec_error = "a block weight pointer is NULL or not 16-byte aligned";
+      return DAR_E_INVAL;
+    }
+  }
+  dar_codec* c = new dar_codec();
+  c->cfg = *cfg;
+  c->L = L;
+  c->stream = static_cast<hipStream_t>(stream);
+  c->ws = static_cast<char*>(workspace);
+  c->tables.assign(reinterpret_cast<const uint16_t* const*>(w->tables),
+                   reinterpret_cast<const uint16_t* const*>(w->tables) + cfg->n_codebooks);
+  c->in_b = U16(w->in_b);
+  for (int i = 0; i < cfg->n_blocks; ++i) c->blocks[i] = w->blocks[i];
+  c->out_alpha = U16(w->out_alpha);
+  c->out_w = U16(w->out_w);
+  c->out_b = U16(w->out_b);
+  hipStream_t s = c->stream;
+  const int K = cfg->kernel_size;
+  auto fail = [&](hipError_t e, const char* what) {
+    codec_hip_fail(nullptr, e, what);
+    delete c;
+    return DAR_E_HIP;
+  };
+  hipError_t e;
+  if ((e = relayout_conv(U16(w->in_w), cfg->channels, cfg->latent_dim, K,
+                         reinterpret_cast<uint16_t*>(c->ws + L.in_w), s)) != hipSuccess)
+    return fail(e, "relayout input conv");
+  for (int i = 0; i < cfg->n_blocks; ++i) {
+    const int cin = width(cfg, i), cout = width(cfg, i + 1);
+    if ((e = relayout_convT(U16(w->blocks[i].up_w), cin, cout, cfg->rates[i],
+                            reinterpret_cast<uint16_t*>(c->ws + L.up_w[i]), s)) != hipSuccess)
+      return fail(e, "relayout transposed conv");
+    for (int u = 0; u < cfg->n_units; ++u) {
+      if ((e = relayout_conv(U16(w->blocks[i].units[u].w1), cout, cout, K,
+                             reinterpret_cast<uint16_t*>(c->ws + L.w1[i][u]), s)) != hipSuccess ||
+          (e = relayout_conv(U16(w->blocks[i].units[u].w2), cout, cout, 1,
+                             reinterpret_cast<uint16_t*>(c->ws + L.w2[i][u]), s)) != hipSuccess)
+        return fail(e, "relayout residual conv");
+    }
+  }
+  if ((e = hipMemsetAsync(c->ws + L.anom, 0, sizeof(int) * 4, s)) != hipSuccess) return fail(e, "clear counter");
+  if ((e = hipStreamSynchronize(s)) != hipSuccess) return fail(e, "create synchronize");
+  *out = c;
+  return DAR_OK;
+}
+
+int dar_codec_decode(dar_codec* c, const int32_t* codes, int32_t frames, float* audio) {
+  if (!c || !codes || !audio) return DAR_E_INVAL;
+  if (frames < 1) {
+    c->err = "frames must be >= 1";
+    return DAR_E_INVAL;
+  }
+  if (frames > c->cfg.max_frames) {
+    c->err = "frames above max_frames";
+    return DAR_E_CAPACITY;
+  }
+  return run_decode(c, codes, frames, audio, false, nullptr);
+}
+
+int dar_codec_anomalies(dar_codec* c, int32_t* count_out) {
+  if (!c || !count_out) return DAR_E_INVAL;
+  int v = 0;
+  CODEC_HIP(c, hipMemcpyAsync(&v, c->ws + c->L.anom, sizeof(int), hipMemcpyDeviceToHost, c->stream), "read counter");
+  CODEC_HIP(c, hipStreamSynchronize(c->stream), "synchronize");
+  *count_out = v;
+  return DAR_OK;
+}
+
+int dar_codec_profile(dar_codec* c, const int32_t* codes, int32_t frames, float* audio, int32_t cap, float* ms_out,
+                      int32_t* tag_out, int32_t* n_out) {
+  if (!c || !codes || !audio || !ms_out || !tag_out || !n_out || cap < 1) return DAR_E_INVAL;
+  if (frames < 1 || frames > c->cfg.max_frames) return frames < 1 ? DAR_E_INVAL : DAR_E_CAPACITY;
+  const int launches = 3 + c->cfg.n_blocks * (1 + 2 * c->cfg.n_units);
+  if (cap < launches) {
+    c->err = "cap below the launches of one decode";
+    return DAR_E_INVAL;
+  }
+  std::vector<int> tags;
+  const int st = run_decode(c, codes, frames, audio, true, &tags);
+  if (st != DAR_OK) return st;
+  CODEC_HIP(c, hipStreamSynchronize(c->stream), "profile synchronize");
+  if (c->events.size() < 2 * tags.size()) {
+    c->err = "event creation failed";
+    return DAR_E_HIP;
+  }
+  for (size_t i = 0; i < tags.size(); ++i) {
+    float ms = 0.f;
+    CODEC_HIP(c, hipEventElapsedTime(&ms, c->events[2 * i], c->events[2 * i + 1]), "event time");
+    ms_out[i] = ms;
+    tag_out[i] = tags[i];
+  }
+  *n_out = (int32_t)tags.size();
+  return DAR_OK;
+}
+
+const char* dar_codec_last_error(const dar_codec* c) { return c ? c->err.c_str() : g_codec_error.c_str(); }
+
+int dar_codec_destroy(dar_codec* c) {
+  if (!c) return DAR_OK;
+  (void)hipStreamSynchronize(c->stream);
+  for (hipEvent_t e : c->events) (void)hipEventDestroy(e);
+  delete c;
+  return DAR_OK;
+}
+
+int dar_codec_op_conv(const void* x, int32_t x_bf16, const void* alpha, int32_t T, int32_t Cin, int32_t Cout,
+                      const void* w, const void* b, int32_t taps, int32_t dilation, int32_t stride, const float* res,
+                      int32_t tanh_out, float* y, void* stream) {
+  if (!x || !w || !b || !y || T < 1 || Cin < 1) return DAR_E_INVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (Cout == 1) {
+    if (x_bf16 || !alpha || stride != 0 || dilation != 1 || taps < 1 || taps > kMaxTaps || taps % 2 == 0 ||
+        !tanh_out || res || out_lds(Cin, taps) > 160 * 1024)
+      return DAR_E_INVAL;
+    hipError_t e = launch_conv_out(static_cast<const float*>(x), U16(alpha), T, Cin, U16(w), U16(b), taps, y, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    return e == hipSuccess ? DAR_OK : codec_hip_fail(nullptr, e, "op conv out");
+  }
+  if (Cin % 32 || Cout % 32 || (x_bf16 && alpha)) return DAR_E_INVAL;
+  ConvArgs a{};
+  if (x_bf16)
+    a.xb = U16(x);
+  else
+    a.xf = static_cast<const float*>(x);
+  a.alpha_in = U16(alpha);
+  a.T = T;
+  a.Cin = Cin;
+  a.Cout = Cout;
+  a.bias = U16(b);
+  a.yf = y;
+  a.res = res;
+  a.tanh_out = tanh_out;
+  size_t wbytes;
+  if (stride == 0) {
+    if (taps < 1 || taps > kMaxTaps || taps % 2 == 0 || dilation < 1 || (taps - 1) / 2 * dilation > kMaxOff)
+      return DAR_E_INVAL;
+    a.nphase = 1;
+    a.ntap = taps;
+    conv_taps(taps, dilation, a.off);
+    wbytes = (size_t)2 * taps * Cout * Cin;
+  } else {
+    if (stride < 2 || stride > 16 || stride % 2) return DAR_E_INVAL;
+    a.nphase = stride;
+    a.ntap = 2;
+    int kidx[kMaxOffs];
+    convT_taps(stride, kidx, a.off);
+    wbytes = (size_t)2 * 2 * stride * Cout * Cin;
+  }
+  void* wr = nullptr;
+  hipError_t e = hipMalloc(&wr, wbytes);
+  if (e != hipSuccess) return codec_hip_fail(nullptr, e, "op conv alloc");
+  e = stride == 0 ? relayout_conv(U16(w), Cout, Cin, taps, static_cast<uint16_t*>(wr), s)
+                  : relayout_convT(U16(w), Cin, Cout, stride, static_cast<uint16_t*>(wr), s);
+  a.W = static_cast<const uint16_t*>(wr);
+  if (e == hipSuccess) e = launch_conv(a, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  (void)hipFree(wr);
+  return e == hipSuccess ? DAR_OK : codec_hip_fail(nullptr, e, "op conv");
+}
+
+}  // extern "C"

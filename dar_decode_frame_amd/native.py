@@ -13,6 +13,7 @@ import re
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libdar.so")
 HEADER = os.path.join(os.path.dirname(HERE), "include", "dar.h")
+HEADERS = [HEADER, os.path.join(os.path.dirname(HERE), "include", "dar_codec.h")]
 
 DAR_OK = 0
 DAR_E_INVAL = -1
@@ -103,6 +104,46 @@ class dar_weights(ctypes.Structure):
     ]
 
 
+CODEC_MAX_BLOCKS = 8
+CODEC_MAX_UNITS = 4
+
+
+class dar_codec_config(ctypes.Structure):
+    _fields_ = [
+        ("n_codebooks", ctypes.c_int32),
+        ("codebook_size", ctypes.c_int32),
+        ("latent_dim", ctypes.c_int32),
+        ("channels", ctypes.c_int32),
+        ("n_blocks", ctypes.c_int32),
+        ("rates", ctypes.c_int32 * CODEC_MAX_BLOCKS),
+        ("n_units", ctypes.c_int32),
+        ("dilations", ctypes.c_int32 * CODEC_MAX_UNITS),
+        ("kernel_size", ctypes.c_int32),
+        ("max_frames", ctypes.c_int32),
+    ]
+
+
+class dar_codec_unit(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("alpha1", "w1", "b1", "alpha2", "w2", "b2")]
+
+
+class dar_codec_block(ctypes.Structure):
+    _fields_ = [("alpha", ctypes.c_void_p), ("up_w", ctypes.c_void_p), ("up_b", ctypes.c_void_p),
+                ("units", dar_codec_unit * CODEC_MAX_UNITS)]
+
+
+class dar_codec_weights(ctypes.Structure):
+    _fields_ = [
+        ("tables", ctypes.POINTER(ctypes.c_void_p)),
+        ("in_w", ctypes.c_void_p),
+        ("in_b", ctypes.c_void_p),
+        ("blocks", ctypes.POINTER(dar_codec_block)),
+        ("out_alpha", ctypes.c_void_p),
+        ("out_w", ctypes.c_void_p),
+        ("out_b", ctypes.c_void_p),
+    ]
+
+
 _VP = ctypes.c_void_p
 _I32 = ctypes.c_int32
 _SIGS = {
@@ -139,6 +180,16 @@ _SIGS = {
     "dar_time_kind": ([_VP, _I32], ctypes.c_int),
     "dar_kind_time": ([_VP, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_I32)], ctypes.c_int),
     "dar_profile_frame": ([_VP, _I32, _VP, _VP, _VP, ctypes.POINTER(_I32)], ctypes.c_int),
+    "dar_codec_workspace_bytes": ([ctypes.POINTER(dar_codec_config), ctypes.POINTER(ctypes.c_size_t)], ctypes.c_int),
+    "dar_codec_create": ([ctypes.POINTER(dar_codec_config), ctypes.POINTER(dar_codec_weights), _VP, ctypes.c_size_t,
+                          _VP, ctypes.POINTER(_VP)], ctypes.c_int),
+    "dar_codec_decode": ([_VP, _VP, _I32, _VP], ctypes.c_int),
+    "dar_codec_anomalies": ([_VP, ctypes.POINTER(_I32)], ctypes.c_int),
+    "dar_codec_profile": ([_VP, _VP, _I32, _VP, _I32, _VP, _VP, ctypes.POINTER(_I32)], ctypes.c_int),
+    "dar_codec_destroy": ([_VP], ctypes.c_int),
+    "dar_codec_last_error": ([_VP], ctypes.c_char_p),
+    "dar_codec_op_conv": ([_VP, _I32, _VP, _I32, _I32, _I32, _VP, _VP, _I32, _I32, _I32, _VP, _I32, _VP, _VP],
+                          ctypes.c_int),
 }
 
 
@@ -171,8 +222,8 @@ def _status_text(status):
 
 
 def header_functions():
-    """Names of every function declared in include/dar.h."""
-    text = open(HEADER).read()
+    """Names of every function declared in include/dar.h and include/dar_codec.h."""
+    text = "\n".join(open(h).read() for h in HEADERS)
     return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(dar_\w+)\s*\(", text, flags=re.M)))
 
 
@@ -354,3 +405,73 @@ def dar_profile_frame(ctx, cap=4096):
     n = ctypes.c_int32(0)
     _check(lib.dar_profile_frame(ctx, cap, ms, kind, layer, ctypes.byref(n)), "dar_profile_frame", ctx)
     return [(float(ms[i]), int(kind[i]), int(layer[i])) for i in range(n.value)]
+
+
+# ---- codec (include/dar_codec.h)
+
+def _check_codec(status, where, ctx=None):
+    if status != DAR_OK:
+        msg = lib.dar_codec_last_error(ctx)
+        raise DarError(status, where, msg.decode() if msg else "")
+    return status
+
+
+def make_codec_config(dims, max_frames):
+    """dar_codec_config from any object with the CodecDims attribute names."""
+    c = dar_codec_config()
+    c.n_codebooks = dims.n_codebooks
+    c.codebook_size = dims.codebook_size
+    c.latent_dim = dims.latent_dim
+    c.channels = dims.channels
+    c.n_blocks = len(dims.rates)
+    for i, r in enumerate(dims.rates):
+        c.rates[i] = r
+    c.n_units = len(dims.dilations)
+    for i, d in enumerate(dims.dilations):
+        c.dilations[i] = d
+    c.kernel_size = dims.kernel
+    c.max_frames = max_frames
+    return c
+
+
+def dar_codec_workspace_bytes(cfg):
+    out = ctypes.c_size_t(0)
+    _check_codec(lib.dar_codec_workspace_bytes(ctypes.byref(cfg), ctypes.byref(out)), "dar_codec_workspace_bytes")
+    return out.value
+
+
+def dar_codec_create(cfg, weights, ws_ptr, ws_bytes, stream_ptr):
+    ctx = ctypes.c_void_p(0)
+    _check_codec(lib.dar_codec_create(ctypes.byref(cfg), ctypes.byref(weights), ws_ptr, ws_bytes, stream_ptr,
+                                      ctypes.byref(ctx)), "dar_codec_create")
+    return ctx
+
+
+def dar_codec_decode(ctx, codes_ptr, frames, audio_ptr):
+    return _check_codec(lib.dar_codec_decode(ctx, codes_ptr, frames, audio_ptr), "dar_codec_decode", ctx)
+
+
+def dar_codec_anomalies(ctx):
+    out = ctypes.c_int32(0)
+    _check_codec(lib.dar_codec_anomalies(ctx, ctypes.byref(out)), "dar_codec_anomalies", ctx)
+    return out.value
+
+
+def dar_codec_profile(ctx, codes_ptr, frames, audio_ptr, cap=256):
+    """Per launch of one decode: (ms, tag)."""
+    ms = (ctypes.c_float * cap)()
+    tag = (ctypes.c_int32 * cap)()
+    n = ctypes.c_int32(0)
+    _check_codec(lib.dar_codec_profile(ctx, codes_ptr, frames, audio_ptr, cap, ms, tag, ctypes.byref(n)),
+                 "dar_codec_profile", ctx)
+    return [(float(ms[i]), int(tag[i])) for i in range(n.value)]
+
+
+def dar_codec_destroy(ctx):
+    return _check_codec(lib.dar_codec_destroy(ctx), "dar_codec_destroy")
+
+
+def dar_codec_op_conv(x_ptr, x_bf16, alpha_ptr, T, Cin, Cout, w_ptr, b_ptr, taps, dilation, stride, res_ptr,
+                      tanh_out, y_ptr, stream_ptr):
+    return _check_codec(lib.dar_codec_op_conv(x_ptr, x_bf16, alpha_ptr, T, Cin, Cout, w_ptr, b_ptr, taps, dilation,
+                                              stride, res_ptr, tanh_out, y_ptr, stream_ptr), "dar_codec_op_conv")

@@ -237,3 +237,78 @@ class DarSession:
 
     def profile_frame(self):
         return N.dar_profile_frame(self.ctx)
+
+
+class CodecSession:
+    """One dar_codec context: device copies of the canonical codec tensors
+    (uint16 bf16 bit arrays by name), its workspace and stream, and
+    decode(codes) -> audio with torch tensors. Marshalling only."""
+
+    def __init__(self, dims, host: dict, max_frames: int, device="cuda", stream=None):
+        self.dims = dims
+        self.device = device
+        self.max_frames = max_frames
+        self.stream = stream if stream is not None else torch.cuda.Stream(device)
+        self.t = {name: torch.from_numpy(np.ascontiguousarray(v).view(np.int16)).to(device)
+                  for name, v in host.items()}
+        ptr = lambda name: ctypes.c_void_p(self.t[name].data_ptr())  # noqa: E731
+        self.cfg = N.make_codec_config(dims, max_frames)
+        nbytes = N.dar_codec_workspace_bytes(self.cfg)
+        self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        tables = (ctypes.c_void_p * dims.n_codebooks)(*[ptr(f"codec.rvq.{k}").value for k in range(dims.n_codebooks)])
+        blocks = (N.dar_codec_block * len(dims.rates))()
+        for i in range(len(dims.rates)):
+            p = f"codec.b{i}"
+            blocks[i].alpha, blocks[i].up_w, blocks[i].up_b = ptr(f"{p}.alpha"), ptr(f"{p}.up.w"), ptr(f"{p}.up.b")
+            for j in range(len(dims.dilations)):
+                r = f"{p}.ru{j}"
+                u = blocks[i].units[j]
+                u.alpha1, u.w1, u.b1 = ptr(f"{r}.alpha1"), ptr(f"{r}.w1"), ptr(f"{r}.b1")
+                u.alpha2, u.w2, u.b2 = ptr(f"{r}.alpha2"), ptr(f"{r}.w2"), ptr(f"{r}.b2")
+        w = N.dar_codec_weights(ctypes.cast(tables, ctypes.POINTER(ctypes.c_void_p)), ptr("codec.in.w"),
+                                ptr("codec.in.b"), ctypes.cast(blocks, ctypes.POINTER(N.dar_codec_block)),
+                                ptr("codec.out.alpha"), ptr("codec.out.w"), ptr("codec.out.b"))
+        self._keep = (tables, blocks)
+        # the uploads ran on torch's stream; the context reads them on its own
+        torch.cuda.current_stream(device).synchronize()
+        self.ctx = N.dar_codec_create(self.cfg, w, ctypes.c_void_p(self.workspace.data_ptr()), nbytes,
+                                      ctypes.c_void_p(self.stream.cuda_stream))
+        self.codes = torch.zeros(max_frames, dims.n_codebooks, dtype=torch.int32, device=device)
+        self.audio = torch.zeros(max_frames * dims.hop, dtype=torch.float32, device=device)
+        torch.cuda.current_stream(device).synchronize()
+
+    def load_codes(self, codes):
+        """Copy host codes [frames][n_codebooks] to the device buffer; returns frames."""
+        c = torch.as_tensor(np.ascontiguousarray(codes, dtype=np.int32))
+        n = c.shape[0]
+        with torch.cuda.stream(self.stream):
+            self.codes[:n].copy_(c.to(self.device))
+        return n
+
+    def decode(self, codes=None, frames=None, want=True):
+        """Decode `codes` (host) or, with codes None, the first `frames` frames
+        already in the device buffer; returns the audio as a host array."""
+        n = self.load_codes(codes) if codes is not None else frames
+        N.dar_codec_decode(self.ctx, ctypes.c_void_p(self.codes.data_ptr()), n, ctypes.c_void_p(self.audio.data_ptr()))
+        if not want:
+            return None
+        self.stream.synchronize()
+        return self.audio[:n * self.dims.hop].cpu().numpy().copy()
+
+    def profile(self, frames):
+        return N.dar_codec_profile(self.ctx, ctypes.c_void_p(self.codes.data_ptr()), frames,
+                                   ctypes.c_void_p(self.audio.data_ptr()))
+
+    def anomalies(self):
+        return N.dar_codec_anomalies(self.ctx)
+
+    def close(self):
+        if getattr(self, "ctx", None):
+            N.dar_codec_destroy(self.ctx)
+            self.ctx = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -5,9 +5,12 @@ dar_bytes_per_frame must agree with the host bytes model, which is itself
 pinned to the pages' numbers (tests/test_bytes_model.py)."""
 import ctypes
 
+import numpy as np
+
 import pytest
 
 from dar_decode_frame_amd import bytes_model as bm
+import synth
 from synth import DIMS
 
 
@@ -183,3 +186,53 @@ def test_paged_calls_reject_without_context(N):
     assert N.lib.dar_seq_add(None, 0, ctypes.c_void_p(256), 4) == N.DAR_E_INVAL
     assert N.lib.dar_seq_remove(None, 0) == N.DAR_E_INVAL
     assert N.lib.dar_pages_free(None, ctypes.byref(n)) == N.DAR_E_INVAL
+
+
+def _codec_cfg(N, **kw):
+    c = N.make_codec_config(synth.CODEC_DIMS["tiny_codec"], 64)
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+def test_codec_workspace_holds_weights_and_activations(N):
+    d = synth.CODEC_DIMS["s2pro_codec"]
+    n = N.dar_codec_workspace_bytes(N.make_codec_config(d, 167))
+    params = sum(int(np.prod(shape)) for name, shape, _, _ in synth.codec_tensor_specs(d)
+                 if name.endswith((".w", ".w1", ".w2")))
+    act = 167 * d.hop * d.widths[-1]  # the widest activation: 2048 samples x 96 channels per frame
+    assert n >= 2 * params + 2 * 4 * act + 2 * act
+    assert n < 2 * params + 2 * 4 * act + 2 * act + 64 * 2 ** 20
+
+
+@pytest.mark.parametrize("field,value", [
+    ("n_codebooks", 0), ("n_codebooks", 33), ("latent_dim", 48), ("channels", 100), ("n_blocks", 0),
+    ("n_blocks", 9), ("kernel_size", 4), ("kernel_size", 9), ("n_units", 0), ("max_frames", 0),
+])
+def test_codec_config_validation(N, field, value):
+    c = _codec_cfg(N, **{field: value})
+    out = ctypes.c_size_t(0)
+    assert N.lib.dar_codec_workspace_bytes(ctypes.byref(c), ctypes.byref(out)) == N.DAR_E_INVAL
+    assert N.lib.dar_codec_last_error(None)
+
+
+def test_codec_rates_and_dilations_checked(N):
+    c = _codec_cfg(N)
+    c.rates[1] = 3                        # odd stride
+    out = ctypes.c_size_t(0)
+    assert N.lib.dar_codec_workspace_bytes(ctypes.byref(c), ctypes.byref(out)) == N.DAR_E_INVAL
+    c = _codec_cfg(N)
+    c.dilations[2] = 30                   # 3 * 30 > 64 positions of reach
+    assert N.lib.dar_codec_workspace_bytes(ctypes.byref(c), ctypes.byref(out)) == N.DAR_E_INVAL
+
+
+def test_codec_create_rejects_before_hip(N):
+    c = _codec_cfg(N)
+    need = N.dar_codec_workspace_bytes(c)
+    w = N.dar_codec_weights()
+    ctx = ctypes.c_void_p(0)
+    assert N.lib.dar_codec_create(ctypes.byref(c), ctypes.byref(w), ctypes.c_void_p(1 << 20), need, None,
+                                  ctypes.byref(ctx)) == N.DAR_E_INVAL
+    assert N.lib.dar_codec_create(ctypes.byref(c), ctypes.byref(w), ctypes.c_void_p(1 << 20), need - 1, None,
+                                  ctypes.byref(ctx)) == N.DAR_E_WORKSPACE
+    assert N.lib.dar_codec_decode(None, None, 1, None) == N.DAR_E_INVAL
