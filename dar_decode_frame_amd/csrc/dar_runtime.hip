@@ -32,11 +32,19 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
 #include "../../include/dar.h"
 #include "dar_internal.h"
+
+// Device scratch of dar_op_gemm_noalloc: the GEMM's hi/lo input halves and
+// its split-K partial sums, for callers that cannot allocate. Each GPU the
+// library runs on holds its own copy until the process ends. In host code this
+// name is only a stand-in for the device symbol: kernels get the address that
+// hipGetSymbolAddress returns for the current device (noalloc_scratch()).
+static __device__ __align__(256) unsigned char scratch[DAR_NOALLOC_SCRATCH_BYTES];
 
 using namespace dar;
 
@@ -1861,6 +1869,70 @@ int dar_op_gemv(int32_t wtype, const void* W, const float* scale, int32_t rows, 
   a.accumulate = 0;
   return run_single_task(t, wtype_of(wtype), static_cast<hipStream_t>(stream),
                          "gemv");
+}
+
+// Address of the current device's copy of `scratch`, looked up once per device
+// with that device current (hipGetSymbolAddress) and kept for later calls.
+static std::mutex g_noalloc_mu;
+static void* g_noalloc_ptr[64] = {};
+
+static hipError_t noalloc_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_noalloc_mu);
+  if (!g_noalloc_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_noalloc_ptr[dev] = p;
+  }
+  *out = g_noalloc_ptr[dev];
+  return hipSuccess;
+}
+
+int dar_op_gemm_noalloc(int32_t wtype, const void* W, const float* scale, int32_t N, int32_t K, const float* x,
+                        int32_t M, float* y, void* stream) {
+  if (!W || !x || !y || N < 1 || K < 256 || K % 256 || K > 16384 || M < 1 || M > kPrefillRows) return DAR_E_INVAL;
+  if (wtype != DAR_WTYPE_BF16 && !has_scales(wtype)) return DAR_E_INVAL;
+  if (has_scales(wtype) && !scale) return DAR_E_INVAL;
+  if (!aligned16(W) || !aligned16(x)) return DAR_E_INVAL;
+  const size_t half_bytes = align_up((size_t)gemm_mpad(M) * K * sizeof(uint16_t));
+  // the input halves must fit; the partial sums adapt to what is left (one
+  // K split needs none). Within the shape limits above the halves take at
+  // most 2 x 128 x 16384 x 2 bytes = 8 MiB.
+  if (2 * half_bytes > DAR_NOALLOC_SCRATCH_BYTES) {
+    g_create_error = "dar_op_gemm_noalloc: the input halves exceed the static scratch";
+    return DAR_E_CAPACITY;
+  }
+  void* base = nullptr;
+  hipError_t e = noalloc_scratch(&base);
+  if (e != hipSuccess) return hip_fail(nullptr, e, "gemm scratch address");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* sc = static_cast<char*>(base);
+  uint16_t* xh = reinterpret_cast<uint16_t*>(sc);
+  uint16_t* xl = reinterpret_cast<uint16_t*>(sc + half_bytes);
+  GemmArgs a{};
+  a.W = W;
+  a.scale = has_scales(wtype) ? scale : nullptr;
+  a.N = N;
+  a.K = K;
+  a.M = M;
+  a.xh = xh;
+  a.xl = xl;
+  a.y = y;
+  a.y_stride = N;
+  a.accumulate = 0;
+  a.part = reinterpret_cast<float*>(sc + 2 * half_bytes);
+  // fewer K splits when the rest of the scratch holds fewer partial sums (one
+  // split needs none: it writes y directly)
+  const size_t part_cap = (DAR_NOALLOC_SCRATCH_BYTES - 2 * half_bytes) / sizeof(float);
+  // x is only read: no sums are pending
+  if ((e = launch_norm_split(const_cast<float*>(x), K, M, K, nullptr, 0.f, xh, xl, s)) == hipSuccess)
+    e = launch_gemm(wtype_of(wtype), a, part_cap, s);
+  if (e != hipSuccess) return hip_fail(nullptr, e, "gemm (no allocation)");
+  return DAR_OK;
 }
 
 int dar_op_gemm(int32_t wtype, const void* W, const float* scale, int32_t N, int32_t K, const float* x,

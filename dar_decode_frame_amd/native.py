@@ -173,6 +173,7 @@ _SIGS = {
     "dar_last_error": ([_VP], ctypes.c_char_p),
     "dar_op_gemv": ([_I32, _VP, _VP, _I32, _I32, _VP, _I32, _VP, _VP], ctypes.c_int),
     "dar_op_gemm": ([_I32, _VP, _VP, _I32, _I32, _VP, _I32, _VP, _VP], ctypes.c_int),
+    "dar_op_gemm_noalloc": ([_I32, _VP, _VP, _I32, _I32, _VP, _I32, _VP, _VP], ctypes.c_int),
     "dar_op_attention": ([_VP, _VP, _VP, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _VP, _VP], ctypes.c_int),
     "dar_op_fp8_decode": ([_VP, _I32, _VP, _VP], ctypes.c_int),
     "dar_set_sampling": ([_VP, ctypes.POINTER(dar_sampling)], ctypes.c_int),
@@ -364,6 +365,11 @@ def dar_op_attention(q_ptr, k_ptr, v_ptr, n_heads_q, n_heads_kv, head_dim, max_l
 
 def dar_op_gemm(wtype, w_ptr, scale_ptr, N, K, x_ptr, M, y_ptr, stream_ptr):
     return _check(lib.dar_op_gemm(wtype, w_ptr, scale_ptr, N, K, x_ptr, M, y_ptr, stream_ptr), "dar_op_gemm")
+
+
+def dar_op_gemm_noalloc(wtype, w_ptr, scale_ptr, N, K, x_ptr, M, y_ptr, stream_ptr):
+    return _check(lib.dar_op_gemm_noalloc(wtype, w_ptr, scale_ptr, N, K, x_ptr, M, y_ptr, stream_ptr),
+                  "dar_op_gemm_noalloc")
 
 
 def dar_op_fp8_decode(codes_ptr, n, out_ptr, stream_ptr):

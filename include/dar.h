@@ -325,6 +325,25 @@ int dar_op_gemv(int32_t wtype, const void* W, const float* scale, int32_t rows, 
 int dar_op_gemm(int32_t wtype, const void* W, const float* scale, int32_t N, int32_t K, const float* x,
                 int32_t M, float* y, void* stream);
 
+/* Bytes of the static device scratch array of dar_op_gemm_noalloc (per GPU). */
+#define DAR_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+
+/* dar_op_gemm without any allocation, for callers that cannot allocate (code
+ * under HIP graph capture, serving loops, harnesses that forbid hipMalloc).
+ * Same arguments, shape limits and kernels as dar_op_gemm; the fp32 inputs'
+ * hi/lo bf16 halves and the K-split partial sums live in a static device
+ * array of DAR_NOALLOC_SCRATCH_BYTES held by each GPU the library runs on
+ * until the process ends (the halves take at most 8 MiB; where the rest holds
+ * fewer partial sums than dar_op_gemm would use, the product runs with fewer
+ * K splits, so sums may round differently). Uses the array of the current
+ * device (stream must belong to it). Stream-ordered: no synchronisation and no
+ * hipMalloc/hipFree. Every call on one GPU shares that GPU's array, which
+ * keeps the last call's contents: calls that overlap on one GPU (other
+ * streams, other threads) race and must be serialised by the caller. Errors:
+ * as dar_op_gemm, DAR_E_CAPACITY if the halves exceed the array. */
+int dar_op_gemm_noalloc(int32_t wtype, const void* W, const float* scale, int32_t N, int32_t K, const float* x,
+                        int32_t M, float* y, void* stream);
+
 /* Decode attention of one layer (the frame's split-K kernel): for query row m
  * at position pos+m, head h, out[m][h] = softmax(q[m][h] . K[kv][0..pos+m] /
  * sqrt(head_dim)) V[kv][0..pos+m] with kv = h / (n_heads_q/n_heads_kv).
