@@ -47,7 +47,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 constexpr int kThreads = 256;
 constexpr int kChunk = 32;      // input channels per staged chunk (two MFMA k-steps)
 constexpr int kMaxTaps = 7;
-constexpr int kMaxOff = 64;     // largest |tap offset| of a convolution
+constexpr int kMaxOff = 32;     // largest |tap offset| of a convolution
 constexpr int kMaxOffs = 32;    // taps x phases of one launch
 constexpr int kOutRows = 256;   // output samples per workgroup of the output convolution
 
@@ -82,14 +82,19 @@ struct ConvArgs {
 };
 
 // LDS row r of 32 bf16 (64 B, four 16-byte units): unit u sits at slot
-// u ^ ((r >> 1) & 3), so any eight consecutive rows read at one unit hit
-// eight distinct 16-byte bank groups.
-__device__ __forceinline__ int lds_at(int r, int u) { return r * 64 + ((u ^ ((r >> 1) & 3)) << 4); }
+// u ^ ((r >> 2) & 3). The LDS serves 16-byte reads sixteen lanes at a time
+// from 64 four-byte banks (256 B): sixteen consecutive rows read at one unit
+// then hit sixteen distinct 16-byte bank groups (row r % 4 picks the 64-byte
+// quarter, the swizzle the unit within it).
+__device__ __forceinline__ int lds_at(int r, int u) { return r * 64 + ((u ^ ((r >> 2) & 3)) << 4); }
 
 template <int WM, int WN, int NT, bool XB16, bool YB16>
 __global__ __launch_bounds__(kThreads) void k_conv(ConvArgs a) {
   constexpr int BM = 32 * WM, BN = 32 * NT * WN;
   static_assert(WM * WN == 4, "four waves");
+  // 16-byte units a thread stages per chunk: window rows x 4, tap rows x 4
+  constexpr int XN = ((BM + 2 * kMaxOff) * 4 + kThreads - 1) / kThreads;
+  constexpr int WNU = (kMaxTaps * BN * 4 + kThreads - 1) / kThreads;
   extern __shared__ __align__(16) char smem[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave % WM, wn = wave / WM;
@@ -102,6 +107,7 @@ __global__ __launch_bounds__(kThreads) void k_conv(ConvArgs a) {
     omax = max(omax, off[j]);
   }
   const int wrows = BM + omax - omin;
+  const int xunits = wrows * 4, wunits = a.ntap * BN * 4;
   char* xs = smem;
   char* ws = smem + wrows * 64;
   const uint16_t* Wz = a.W + (size_t)z * a.ntap * a.Cout * a.Cin;
@@ -111,42 +117,77 @@ __global__ __launch_bounds__(kThreads) void k_conv(ConvArgs a) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc[nt][v] = 0.f;
   const int half = lane >> 5, l32 = lane & 31;
-  for (int c0 = 0; c0 < a.Cin; c0 += kChunk) {
-    // the input window of this chunk: row w is input row t0 + omin + w
-    for (int i = tid; i < wrows * 4; i += kThreads) {
+  // A chunk of 32 input channels is staged in two steps, so that its global
+  // loads are all in flight together and overlap the previous chunk's MFMAs:
+  // load() issues every load of the chunk into registers, store() converts
+  // (Snake, bf16) and writes them to LDS once they have landed.
+  // window unit i: row w = i / 4 (input row t0 + omin + w), channels c0 + 8 (i % 4) ..
+  f32x4 xv[XN][2];
+  u32x4 xa[XN];
+  u32x4 wv[WNU];
+  auto load = [&](int c0) {
+#pragma unroll
+    for (int k = 0; k < XN; ++k) {
+      const int i = tid + k * kThreads;
       const int w = i >> 2, u = i & 3;
       const int row = t0 + omin + w;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (row >= 0 && row < a.T) {
-        if constexpr (XB16) {
-          v = *reinterpret_cast<const u32x4*>(a.xb + (size_t)row * a.Cin + c0 + 8 * u);
-        } else {
-          const f32x4* src = reinterpret_cast<const f32x4*>(a.xf + (size_t)row * a.Cin + c0 + 8 * u);
-          const f32x4 p = src[0], q = src[1];
-          float f[8] = {p.x, p.y, p.z, p.w, q.x, q.y, q.z, q.w};
-          if (a.alpha_in) {
-            const u32x4 al = *reinterpret_cast<const u32x4*>(a.alpha_in + c0 + 8 * u);
-            const uint32_t aw[4] = {al.x, al.y, al.z, al.w};
+      const bool in = i < xunits && row >= 0 && row < a.T;
+      if constexpr (XB16) {
+        xa[k] = in ? *reinterpret_cast<const u32x4*>(a.xb + (size_t)row * a.Cin + c0 + 8 * u) : u32x4{0u, 0u, 0u, 0u};
+      } else {
+        const f32x4 zf = {0.f, 0.f, 0.f, 0.f};
+        const f32x4* src = reinterpret_cast<const f32x4*>(a.xf + (size_t)(in ? row : 0) * a.Cin + c0 + 8 * u);
+        xv[k][0] = in ? src[0] : zf;
+        xv[k][1] = in ? src[1] : zf;
+        if (a.alpha_in && i < xunits) xa[k] = *reinterpret_cast<const u32x4*>(a.alpha_in + c0 + 8 * u);
+      }
+    }
+    // tap unit i: LDS row r = i / 4 = j BN + n holds output channel n0 + n of tap j
 #pragma unroll
-            for (int e = 0; e < 8; ++e) f[e] = snake(f[e], bf2f((uint16_t)(aw[e >> 1] >> (16 * (e & 1)))));
-          }
-          v.x = f2bf(f[0]) | (f2bf(f[1]) << 16);
-          v.y = f2bf(f[2]) | (f2bf(f[3]) << 16);
-          v.z = f2bf(f[4]) | (f2bf(f[5]) << 16);
-          v.w = f2bf(f[6]) | (f2bf(f[7]) << 16);
+    for (int k = 0; k < WNU; ++k) {
+      const int i = tid + k * kThreads;
+      const int r = i >> 2, u = i & 3;
+      const int j = r / BN, n = n0 + r % BN;
+      wv[k] = (i < wunits && n < a.Cout)
+                  ? *reinterpret_cast<const u32x4*>(Wz + ((size_t)j * a.Cout + n) * a.Cin + c0 + 8 * u)
+                  : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  auto store = [&]() {
+#pragma unroll
+    for (int k = 0; k < XN; ++k) {
+      const int i = tid + k * kThreads;
+      if (i >= xunits) continue;
+      const int w = i >> 2, u = i & 3;
+      u32x4 v;
+      if constexpr (XB16) {
+        v = xa[k];
+      } else {
+        const int row = t0 + omin + w;
+        float f[8] = {xv[k][0].x, xv[k][0].y, xv[k][0].z, xv[k][0].w, xv[k][1].x, xv[k][1].y, xv[k][1].z, xv[k][1].w};
+        if (a.alpha_in && row >= 0 && row < a.T) {
+          const uint32_t aw[4] = {xa[k].x, xa[k].y, xa[k].z, xa[k].w};
+#pragma unroll
+          for (int e = 0; e < 8; ++e) f[e] = snake(f[e], bf2f((uint16_t)(aw[e >> 1] >> (16 * (e & 1)))));
         }
+        v.x = f2bf(f[0]) | (f2bf(f[1]) << 16);
+        v.y = f2bf(f[2]) | (f2bf(f[3]) << 16);
+        v.z = f2bf(f[4]) | (f2bf(f[5]) << 16);
+        v.w = f2bf(f[6]) | (f2bf(f[7]) << 16);
       }
       *reinterpret_cast<u32x4*>(xs + lds_at(w, u)) = v;
     }
-    // every tap's weights of this chunk: row j * BN + n holds output channel n0 + n
-    for (int i = tid; i < a.ntap * BN * 4; i += kThreads) {
-      const int r = i >> 2, u = i & 3;
-      const int j = r / BN, n = n0 + r % BN;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (n < a.Cout) v = *reinterpret_cast<const u32x4*>(Wz + ((size_t)j * a.Cout + n) * a.Cin + c0 + 8 * u);
-      *reinterpret_cast<u32x4*>(ws + lds_at(r, u)) = v;
+#pragma unroll
+    for (int k = 0; k < WNU; ++k) {
+      const int i = tid + k * kThreads;
+      if (i < wunits) *reinterpret_cast<u32x4*>(ws + lds_at(i >> 2, i & 3)) = wv[k];
     }
+  };
+  load(0);
+  for (int c0 = 0; c0 < a.Cin; c0 += kChunk) {
+    store();
     __syncthreads();
+    if (c0 + kChunk < a.Cin) load(c0 + kChunk);
     for (int j = 0; j < a.ntap; ++j) {
       const int xr = wm * 32 + l32 + off[j] - omin;
 #pragma unroll
@@ -189,31 +230,62 @@ __global__ __launch_bounds__(kThreads) void k_conv(ConvArgs a) {
 }
 
 // The output convolution (one channel): Snake, K taps, bias, tanh. A
-// workgroup makes kOutRows samples from its window of input rows, staged
-// channel-major in LDS (after Snake, rounded to bf16) so that consecutive
-// lanes read consecutive samples.
+// workgroup makes kOutRows samples from its window of input rows, 32 channels
+// at a time: every load of a channel block is issued before any is used (so
+// their latencies overlap), then the block is staged channel-major in LDS
+// (after Snake, rounded to bf16) so that consecutive lanes read consecutive
+// samples, and each thread adds the block's taps to its sample's sum.
+constexpr int kOutCB = 32;  // channels per staged block
 __global__ __launch_bounds__(kThreads) void k_conv_out(const float* x, const uint16_t* alpha, int T, int C,
                                                      const uint16_t* w, const uint16_t* b, int K, float* y) {
   extern __shared__ __align__(16) char smem[];
   const int halfk = (K - 1) / 2, W = kOutRows + K - 1;
-  uint16_t* xs = reinterpret_cast<uint16_t*>(smem);  // [C][W]
-  float* wsm = reinterpret_cast<float*>(smem + (((size_t)C * W * 2 + 15) & ~(size_t)15));  // [C][K]
+  uint16_t* xs = reinterpret_cast<uint16_t*>(smem);  // [kOutCB][W]
+  float* wsm = reinterpret_cast<float*>(smem + (((size_t)kOutCB * W * 2 + 15) & ~(size_t)15));  // [C][K]
   const int t0 = blockIdx.x * kOutRows, tid = threadIdx.x;
   for (int i = tid; i < C * K; i += kThreads) wsm[i] = bf2f(w[i]);
-  for (int i = tid; i < W * C; i += kThreads) {
-    const int r = i / C, c = i % C;
-    const int row = t0 - halfk + r;
-    uint16_t v = 0;
-    if (row >= 0 && row < T) v = (uint16_t)f2bf(snake(x[(size_t)row * C + c], bf2f(alpha[c])));
-    xs[c * W + r] = v;
-  }
-  __syncthreads();
-  const int t = t0 + tid;
-  if (t >= T) return;
+  constexpr int Q = kOutCB / 4;                                        // float4s per window row
+  constexpr int NL = ((kOutRows + 14) * Q + kThreads - 1) / kThreads;  // per thread (K <= 15)
   float acc = 0.f;
-  for (int c = 0; c < C; ++c)
-    for (int j = 0; j < K; ++j) acc = fmaf(wsm[c * K + j], bf2f(xs[c * W + tid + j]), acc);
-  y[t] = tanhf(acc + bf2f(b[0]));
+  for (int cb = 0; cb < C; cb += kOutCB) {
+    f32x4 v[NL];
+    uint32_t al[NL][2];
+#pragma unroll
+    for (int k = 0; k < NL; ++k) {
+      const int i = tid + k * kThreads;
+      const int r = i / Q, c4 = i % Q;
+      const int row = t0 - halfk + r;
+      const bool in = i < W * Q && row >= 0 && row < T;
+      v[k] = in ? *reinterpret_cast<const f32x4*>(x + (size_t)row * C + cb + 4 * c4) : f32x4{0.f, 0.f, 0.f, 0.f};
+      if (i < W * Q) {
+        const uint2 a2 = *reinterpret_cast<const uint2*>(alpha + cb + 4 * c4);
+        al[k][0] = a2.x;
+        al[k][1] = a2.y;
+      }
+    }
+    __syncthreads();  // the previous block's reads of xs are done
+#pragma unroll
+    for (int k = 0; k < NL; ++k) {
+      const int i = tid + k * kThreads;
+      if (i >= W * Q) continue;
+      const int r = i / Q, c4 = i % Q;
+      const int row = t0 - halfk + r;
+      const bool in = row >= 0 && row < T;
+      const float f[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float a = bf2f((uint16_t)(al[k][e >> 1] >> (16 * (e & 1))));
+        xs[(4 * c4 + e) * W + r] = in ? (uint16_t)f2bf(snake(f[e], a)) : (uint16_t)0;
+      }
+    }
+    __syncthreads();
+    if (t0 + tid < T) {
+      for (int c = 0; c < kOutCB; ++c)
+        for (int j = 0; j < K; ++j) acc = fmaf(wsm[(cb + c) * K + j], bf2f(xs[c * W + tid + j]), acc);
+    }
+  }
+  const int t = t0 + tid;
+  if (t < T) y[t] = tanhf(acc + bf2f(b[0]));
 }
 
 // z[t] = sum_k table_k[code[t][k]] over the codebooks in order, fp32 sums
@@ -287,8 +359,9 @@ struct TileCfg {
   int bm() const { return 32 * wm; }
   int bn() const { return 32 * nt * wn; }
 };
-// largest tiles first
-constexpr TileCfg kCfgs[] = {{4, 1, 4}, {4, 1, 3}, {2, 2, 2}, {2, 2, 1}, {1, 4, 1}, {4, 1, 1}};
+// largest tiles first (a 128 x 128 tile needs more registers than a wave has
+// room for with the staged chunk in flight)
+constexpr TileCfg kCfgs[] = {{4, 1, 3}, {2, 2, 2}, {2, 2, 1}, {1, 4, 1}, {4, 1, 1}};
 constexpr int kNumCfgs = sizeof(kCfgs) / sizeof(kCfgs[0]);
 
 long long cfg_grid(const TileCfg& c, int rows, int Cout, int nphase) {
@@ -344,11 +417,10 @@ template <bool XB16, bool YB16>
 hipError_t go_conv_cfg(int ci, const ConvArgs& a, dim3 grid, size_t lds, hipStream_t s, hipEvent_t e0,
                        hipEvent_t e1) {
   switch (ci) {
-    case 0: return go_conv<4, 1, 4, XB16, YB16>(a, grid, lds, s, e0, e1);
-    case 1: return go_conv<4, 1, 3, XB16, YB16>(a, grid, lds, s, e0, e1);
-    case 2: return go_conv<2, 2, 2, XB16, YB16>(a, grid, lds, s, e0, e1);
-    case 3: return go_conv<2, 2, 1, XB16, YB16>(a, grid, lds, s, e0, e1);
-    case 4: return go_conv<1, 4, 1, XB16, YB16>(a, grid, lds, s, e0, e1);
+    case 0: return go_conv<4, 1, 3, XB16, YB16>(a, grid, lds, s, e0, e1);
+    case 1: return go_conv<2, 2, 2, XB16, YB16>(a, grid, lds, s, e0, e1);
+    case 2: return go_conv<2, 2, 1, XB16, YB16>(a, grid, lds, s, e0, e1);
+    case 3: return go_conv<1, 4, 1, XB16, YB16>(a, grid, lds, s, e0, e1);
     default: return go_conv<4, 1, 1, XB16, YB16>(a, grid, lds, s, e0, e1);
   }
 }
@@ -375,7 +447,9 @@ hipError_t launch_conv(const ConvArgs& a, hipStream_t s, hipEvent_t e0 = nullptr
   return hipErrorInvalidValue;  // bf16 in and bf16 out: not a layer of the decoder
 }
 
-size_t out_lds(int C, int K) { return (((size_t)C * (kOutRows + K - 1) * 2 + 15) & ~(size_t)15) + (size_t)C * K * 4; }
+size_t out_lds(int C, int K) {
+  return (((size_t)kOutCB * (kOutRows + K - 1) * 2 + 15) & ~(size_t)15) + (size_t)C * K * 4;
+}
 
 hipError_t launch_conv_out(const float* x, const uint16_t* alpha, int T, int C, const uint16_t* w, const uint16_t* b,
                            int K, float* y, hipStream_t s, hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr) {
@@ -496,7 +570,7 @@ int validate_codec(const dar_codec_config* c, std::string& why) {
   if (K < 1 || K > kMaxTaps || K % 2 == 0) return bad("kernel_size must be odd, in [1, 7]");
   for (int u = 0; u < c->n_units; ++u)
     if (c->dilations[u] < 1 || (long long)(K - 1) / 2 * c->dilations[u] > kMaxOff)
-      return bad("dilations must be >= 1 with (kernel_size - 1) / 2 * dilation <= 64");
+      return bad("dilations must be >= 1 with (kernel_size - 1) / 2 * dilation <= 32");
   long long hop = 1;
   for (int i = 0; i < c->n_blocks; ++i) {
     if (c->rates[i] < 2 || c->rates[i] > 16 || c->rates[i] % 2) return bad("rates must be even, in [2, 16]");
@@ -839,7 +913,7 @@ int dar_codec_op_conv(const void* x, int32_t x_bf16, const void* alpha, int32_t 
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (Cout == 1) {
     if (x_bf16 || !alpha || stride != 0 || dilation != 1 || taps < 1 || taps > kMaxTaps || taps % 2 == 0 ||
-        !tanh_out || res || out_lds(Cin, taps) > 160 * 1024)
+        !tanh_out || res || Cin % kOutCB || out_lds(Cin, taps) > 160 * 1024)
       return DAR_E_INVAL;
     hipError_t e = launch_conv_out(static_cast<const float*>(x), U16(alpha), T, Cin, U16(w), U16(b), taps, y, s);
     if (e == hipSuccess) e = hipStreamSynchronize(s);

@@ -62,14 +62,24 @@ __device__ __forceinline__ void wait_loads() {
 }
 
 // A staged chunk holds 128 B of each of 128 weight rows; the 16-byte units of
-// row r sit XOR-swizzled, unit u at slot u ^ (r % 8), so the 32 lanes that
-// read one unit of 32 consecutive rows hit distinct bank groups.
+// row r sit XOR-swizzled, unit u at slot u ^ swz8(r). The LDS serves 16-byte
+// reads sixteen lanes at a time from 64 four-byte banks (256 B), and sixteen
+// consecutive 128-byte rows read at one unit then land in sixteen distinct
+// 16-byte bank groups (r % 2 picks the half of the 256 B, swz8 the unit).
+__device__ __forceinline__ int swz8(int r) { return (r >> 1) & 7; }
+// the same for the staged input rows of XU units: 128-byte rows (XU = 8) as
+// above; rows of 256 or 512 bytes (XU = 16, 32) start on the same bank, so
+// the unit is swizzled by r % 16
+template <int XU>
+__device__ __forceinline__ int swzx(int r) {
+  return XU >= 16 ? (r & 15) : ((r >> 1) & 7);
+}
 struct BF16T {
   static constexpr int kBits = 16;
   static constexpr bool kGrouped = false;
   // eight consecutive weights of row r at k = 16 s + 8 half, as the MFMA B operand
   __device__ static __forceinline__ bf16x8 frag(const char* st, int r, int s, int half) {
-    const int u = (2 * s + half) ^ (r & 7);
+    const int u = (2 * s + half) ^ swz8(r);
     return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(st + (r * 8 + u) * 16));
   }
 };
@@ -82,7 +92,7 @@ struct FP8T {
     return (__float_as_uint(v.x) >> 16) | (__float_as_uint(v.y) & 0xffff0000u);
   }
   __device__ static __forceinline__ bf16x8 frag(const char* st, int r, int s, int half) {
-    const int u = s ^ (r & 7);
+    const int u = s ^ swz8(r);
     const u32x2 w = *reinterpret_cast<const u32x2*>(st + (r * 8 + u) * 16 + 8 * half);
     u32x4 o;
     o.x = pack2(__builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, false));
@@ -101,7 +111,7 @@ struct INT8T {
     return (__float_as_uint((float)a) >> 16) | (__float_as_uint((float)b) & 0xffff0000u);
   }
   __device__ static __forceinline__ bf16x8 frag(const char* st, int r, int s, int half) {
-    const int u = s ^ (r & 7);
+    const int u = s ^ swz8(r);
     const u32x2 w = *reinterpret_cast<const u32x2*>(st + (r * 8 + u) * 16 + 8 * half);
     const int x = (int)w.x, y = (int)w.y;
     u32x4 o;
@@ -123,7 +133,7 @@ struct INT4T {
     return (__float_as_uint((float)a) >> 16) | (__float_as_uint((float)b) & 0xffff0000u);
   }
   __device__ static __forceinline__ bf16x8 frag(const char* st, int r, int s, int half) {
-    const int u = (s >> 1) ^ (r & 7);
+    const int u = (s >> 1) ^ swz8(r);
     const int w = *reinterpret_cast<const int*>(st + (r * 8 + u) * 16 + (s & 1) * 8 + 4 * half);
     u32x4 o;
     o.x = pack2((w << 28) >> 28, (w << 24) >> 28);
@@ -197,7 +207,7 @@ __global__ __launch_bounds__(kBlock) void k_gemm(GemmArgs a) {
   for (int i = 0; i < 4; ++i) {
     const int r = wave * 32 + 8 * i + (lane >> 3);
     wsrc[i] = reinterpret_cast<const char*>(a.W) + (size_t)min(nb + r, a.N - 1) * a.K * WT::kBits / 8 +
-              (size_t)c_begin * kRowChunk + 16 * ((lane & 7) ^ (lane >> 3));
+              (size_t)c_begin * kRowChunk + 16 * ((lane & 7) ^ swz8(r));
   }
   // group scales of this lane's weight row, two per chunk
   const f32x2* gsrc = nullptr;
@@ -212,7 +222,7 @@ __global__ __launch_bounds__(kBlock) void k_gemm(GemmArgs a) {
     const int q0 = (wave * XL + j) * 64;
     const int part = q0 / (32 * MT * XU);
     const int q = q0 % (32 * MT * XU) + lane;
-    const int row = q / XU, u = (q % XU) ^ (row & 7);
+    const int row = q / XU, u = (q % XU) ^ swzx<XU>(row);
     xsrc[j] = reinterpret_cast<const char*>(part ? a.xl : a.xh) +
               ((size_t)(m0 + row) * a.K + (size_t)c_begin * KC) * 2 + 16 * u;
   }
@@ -258,7 +268,7 @@ __global__ __launch_bounds__(kBlock) void k_gemm(GemmArgs a) {
 #pragma unroll
             for (int s = 8 * g; s < 8 * g + 8; ++s) {
               const bf16x8 b = WT::frag(ws, wave * 32 + row, s, half);
-              const int u = (2 * s + half) ^ (row & 7);
+              const int u = (2 * s + half) ^ swzx<XU>(row);
               const bf16x8 ah = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(xs + (row * XU + u) * 16));
               const bf16x8 al =
                   __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(xs + ((32 + row) * XU + u) * 16));
@@ -276,7 +286,7 @@ __global__ __launch_bounds__(kBlock) void k_gemm(GemmArgs a) {
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
               const int row = mt * 32 + (lane & 31);
-              const int u = (2 * s + half) ^ (row & 7);
+              const int u = (2 * s + half) ^ swzx<XU>(row);
               const bf16x8 ah = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(xs + (row * XU + u) * 16));
               const bf16x8 al =
                   __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(xs + ((32 * MT + row) * XU + u) * 16));
@@ -294,6 +304,113 @@ __global__ __launch_bounds__(kBlock) void k_gemm(GemmArgs a) {
     gemm_store<MT>(b, acc, nb + wave * 32 + (lane & 31), m0, lane);
   } else {
     gemm_store<MT>(a, acc, nb + wave * 32 + (lane & 31), m0, lane);
+  }
+}
+
+// The same product with eight waves per workgroup (two per SIMD, so one
+// wave's MFMAs cover the other's LDS reads and waits) over 64 or 128 input
+// rows: the staged chunk and its layout are k_gemm's; each wave multiplies
+// 32 input rows by 32 NT weight rows (NT = 2 at 128 input rows: a k-step
+// reads two weight fragments and one hi/lo pair for four MFMAs), with the hi
+// and lo products in separate accumulators.
+constexpr int kWaves8 = 8;
+template <typename WT, int MT>
+__global__ __launch_bounds__(kWaves8 * kWave) void k_gemm8(GemmArgs a) {
+  static_assert(!WT::kGrouped && (MT == 2 || MT == 4), "row-scaled or unscaled weights, 64 or 128 rows");
+  constexpr int KC = kChunkK<WT>;
+  constexpr int ST = KC / 16;
+  constexpr int XU = KC / 8;
+  constexpr int WB = kTileN * kRowChunk;
+  constexpr int XB = 2 * 32 * MT * XU * 16;
+  constexpr int SB = WB + XB;
+  constexpr int WL = WB / (16 * 64 * kWaves8);         // weight loads per wave per stage
+  constexpr int XL = XB / (16 * 64 * kWaves8);         // input loads per wave per stage
+  constexpr int LPS = WL + XL;
+  constexpr int WMW = MT;                              // waves along the input rows (32 rows each)
+  constexpr int WNW = kWaves8 / WMW;                   // waves along the weight rows
+  constexpr int NT = kTileN / 32 / WNW;                // 32-row weight tiles per wave
+  static_assert(WL * 16 * 64 * kWaves8 == WB && XL * 16 * 64 * kWaves8 == XB, "staging split");
+  static_assert(kStages * SB <= 160 * 1024, "LDS");
+  __shared__ __align__(16) char sm[kStages * SB];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wn = wave % WNW, wm = wave / WNW;
+  const int nb = blockIdx.x * kTileN;
+  const int m0 = blockIdx.y * 32 * MT;
+  const int c_begin = blockIdx.z * a.cps;
+  const int nc = min(a.K / KC, c_begin + a.cps) - c_begin;
+  // weight load i of this wave fills rows 16 wave + 8 i + lane / 8, slot lane % 8
+  const char* wsrc[WL];
+#pragma unroll
+  for (int i = 0; i < WL; ++i) {
+    const int r = wave * 8 * WL + 8 * i + (lane >> 3);
+    wsrc[i] = reinterpret_cast<const char*>(a.W) + (size_t)min(nb + r, a.N - 1) * a.K * WT::kBits / 8 +
+              (size_t)c_begin * kRowChunk + 16 * ((lane & 7) ^ swz8(r));
+  }
+  const char* xsrc[XL];
+#pragma unroll
+  for (int j = 0; j < XL; ++j) {
+    const int q0 = (wave * XL + j) * 64;
+    const int part = q0 / (32 * MT * XU);
+    const int q = q0 % (32 * MT * XU) + lane;
+    const int row = q / XU, u = (q % XU) ^ swzx<XU>(row);
+    xsrc[j] = reinterpret_cast<const char*>(part ? a.xl : a.xh) +
+              ((size_t)(m0 + row) * a.K + (size_t)c_begin * KC) * 2 + 16 * u;
+  }
+  auto issue = [&](int t, int stage) {
+    char* base = sm + stage * SB;
+#pragma unroll
+    for (int i = 0; i < WL; ++i)
+      load_lds16(wsrc[i] + (size_t)t * kRowChunk, base + (wave * WL + i) * 1024);
+#pragma unroll
+    for (int j = 0; j < XL; ++j) load_lds16(xsrc[j] + (size_t)t * KC * 2, base + WB + (wave * XL + j) * 1024);
+  };
+  f32x16 acc_h[NT], acc_l[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc_h[nt][v] = acc_l[nt][v] = 0.f;
+#pragma unroll
+  for (int j = 0; j < kStages - 1; ++j)
+    if (j < nc) issue(j, j);
+  const int half = lane >> 5;
+  const int row = wm * 32 + (lane & 31);
+  for (int t0 = 0; t0 < nc; t0 += kStages) {
+#pragma unroll
+    for (int j = 0; j < kStages; ++j) {
+      const int t = t0 + j;
+      if (t < nc) {
+        static_assert(kStages == 3, "wait counts below assume three stages");
+        if (t + 1 < nc) wait_loads<LPS>();
+        else wait_loads<0>();
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        if (t + kStages - 1 < nc) issue(t + kStages - 1, (j + kStages - 1) % kStages);
+        const char* ws = sm + j * SB;
+        const char* xs = ws + WB;
+#pragma unroll
+        for (int s = 0; s < ST; ++s) {
+          bf16x8 b[NT];
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) b[nt] = WT::frag(ws, (wn * NT + nt) * 32 + (lane & 31), s, half);
+          const int u = (2 * s + half) ^ swzx<XU>(row);
+          const bf16x8 ah = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(xs + (row * XU + u) * 16));
+          const bf16x8 al =
+              __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(xs + ((32 * MT + row) * XU + u) * 16));
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) {
+            acc_h[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, b[nt], acc_h[nt], 0, 0, 0);
+            acc_l[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, b[nt], acc_l[nt], 0, 0, 0);
+          }
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    f32x16 acc[1];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[0][v] = acc_h[nt][v] + acc_l[nt][v];
+    gemm_store<1>(a, acc, nb + (wn * NT + nt) * 32 + (lane & 31), m0 + wm * 32, lane);
   }
 }
 
@@ -345,7 +462,7 @@ __global__ __launch_bounds__(kBlock) void k_gemm_x(GemmArgs a) {
   for (int i = 0; i < 4; ++i) {
     const int r = wave * 32 + 8 * i + (lane >> 3);
     wsrc[i] = reinterpret_cast<const char*>(a.W) + (size_t)min(nb + r, a.N - 1) * a.K * WT::kBits / 8 +
-              (size_t)c_begin * kRowChunk + 16 * ((lane & 7) ^ (lane >> 3));
+              (size_t)c_begin * kRowChunk + 16 * ((lane & 7) ^ swz8(r));
   }
   auto issue_w = [&](int t) {
 #pragma unroll
@@ -358,7 +475,7 @@ __global__ __launch_bounds__(kBlock) void k_gemm_x(GemmArgs a) {
       const int q0 = (wave * XL + j) * 64;
       const int part = q0 / (XROWS * XU);
       const int q = q0 % (XROWS * XU) + lane;
-      const int row = q / XU, u = (q % XU) ^ (row & 7);
+      const int row = q / XU, u = (q % XU) ^ swzx<XU>(row);
       load_lds16(reinterpret_cast<const char*>(part ? a.xl : a.xh) +
                      ((size_t)row * a.K + (size_t)(c_begin + t) * KC) * 2 + 16 * u,
                  sm + t * XB + (wave * XL + j) * 1024);
@@ -385,7 +502,7 @@ __global__ __launch_bounds__(kBlock) void k_gemm_x(GemmArgs a) {
 #pragma unroll
     for (int s = 0; s < ST; ++s) {
       const bf16x8 b = WT::frag(ws, lane & 31, s, half);
-      const int u = (2 * s + half) ^ (xrow & 7);
+      const int u = (2 * s + half) ^ swzx<XU>(xrow);
       const bf16x8 ah = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(xs + (xrow * XU + u) * 16));
       const bf16x8 al =
           __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(xs + ((XROWS + xrow) * XU + u) * 16));
@@ -700,14 +817,14 @@ hipError_t gemm_dispatch(int wtype, const GemmArgs& a, int mt, dim3 grid, hipStr
     else if (mt == 1)
       hipLaunchKernelGGL((k_gemm<INT8T, 1>), grid, dim3(kBlock), 0, s, a);
     else
-      hipLaunchKernelGGL((k_gemm<INT8T, 2>), grid, dim3(kBlock), 0, s, a);
+      hipLaunchKernelGGL((k_gemm8<INT8T, 2>), grid, dim3(kWaves8 * kWave), 0, s, a);
   } else if (wtype == W_FP8) {
     if (mt == 1 && a.cps <= kResidentChunks<FP8T>)
       hipLaunchKernelGGL((k_gemm_x<FP8T>), grid, dim3(kBlock), 0, s, a);
     else if (mt == 1)
       hipLaunchKernelGGL((k_gemm<FP8T, 1>), grid, dim3(kBlock), 0, s, a);
     else
-      hipLaunchKernelGGL((k_gemm<FP8T, 2>), grid, dim3(kBlock), 0, s, a);
+      hipLaunchKernelGGL((k_gemm8<FP8T, 2>), grid, dim3(kWaves8 * kWave), 0, s, a);
   } else {
     switch (mt) {
       case 1:
@@ -716,8 +833,8 @@ hipError_t gemm_dispatch(int wtype, const GemmArgs& a, int mt, dim3 grid, hipStr
         else
           hipLaunchKernelGGL((k_gemm<BF16T, 1>), grid, dim3(kBlock), 0, s, a);
         break;
-      case 2: hipLaunchKernelGGL((k_gemm<BF16T, 2>), grid, dim3(kBlock), 0, s, a); break;
-      default: hipLaunchKernelGGL((k_gemm<BF16T, 4>), grid, dim3(kBlock), 0, s, a); break;
+      case 2: hipLaunchKernelGGL((k_gemm8<BF16T, 2>), grid, dim3(kWaves8 * kWave), 0, s, a); break;
+      default: hipLaunchKernelGGL((k_gemm8<BF16T, 4>), grid, dim3(kWaves8 * kWave), 0, s, a); break;
     }
   }
   return hipGetLastError();

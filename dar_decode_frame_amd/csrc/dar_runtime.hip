@@ -1082,7 +1082,7 @@ int prefill_blocks(dar_ctx* c, const int32_t* tokens, int n, hipStream_t s, int 
               launch_rope_rows(nullptr, M, p0, g.n_heads_q, g.n_heads_kv, g.head_dim, c->rope, pq, kc, vc, cache_len,
                                s, nullptr, nullptr, c->paged ? page_stride : 0, sums(pgp, qkv_rows, d, M), pm),
               "prefill rope");
-      Task t{};
+      Task t = none_task();  // every byte zero: the union's members past the first are not covered by {}
       t.kind = T_ATTN;
       t.M = M;
       AttnArgs& aa = t.attn;

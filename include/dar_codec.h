@@ -50,7 +50,7 @@ extern "C" {
  * codebook_size >= 1; latent_dim and channels multiples of 32, at most 8192;
  * n_blocks in [1, 8] with channels >> n_blocks >= 32 and a multiple of 32;
  * every rate even, in [2, 16]; n_units in [1, 4], dilations >= 1; kernel_size
- * odd, in [1, 7], with (kernel_size - 1) / 2 * dilation <= 64;
+ * odd, in [1, 7], with (kernel_size - 1) / 2 * dilation <= 32;
  * max_frames >= 1 with max_frames * prod(rates) * channels < 2^31. */
 typedef struct {
   int32_t n_codebooks;

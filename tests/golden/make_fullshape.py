@@ -11,11 +11,12 @@ For each workload it records two runs on the seeded weights and prompt:
   oracle runs the prompt and the forced codebook-0 ids as one causal block and
   records the last frame only.
 
-Per (frame, codebook) logit vector it stores the oracle's argmax, its top-1 -
-top-2 margin, and the logits at 64 seeded sample indices plus the top two,
-to 7 significant digits (the full vectors would be 160 K floats per run). Slow to run (the fp8
-oracle quantises 4 billion weights in NumPy: minutes); run from the
-repository root:  python3 tests/golden/make_fullshape.py [workload ...]
+Per (frame, codebook) logit vector it stores the oracle's argmax and its
+top-1 - top-2 margin (fullshape_<workload>.json) and the whole fp32 logit
+vector (fullshape_<workload>.npz: "early" [frames][1 + n_res][4096], "late"
+[1 + n_res][4096]). Slow to run (the fp8 oracle quantises 4 billion weights in
+NumPy: minutes); run from the repository root:
+  python3 tests/golden/make_fullshape.py [workload ...]
 """
 import json
 import os
@@ -33,7 +34,6 @@ from oracle import OracleDecoder, OracleModel  # noqa: E402
 WORKLOADS = ["s2pro_slow_bf16", "s2pro_dual_bf16", "s2pro_dual_fp8", "s2pro_dual_int8", "s2pro_dual_int4"]
 EARLY_FRAMES = 9
 LATE_LAST_POS = 1007          # slow position of the late frame
-SAMPLES = 64
 FORCE_SEED = 4242
 
 
@@ -47,19 +47,19 @@ def random_frames(dims, n, seed):
     return out
 
 
-def record(frame, dims, seed):
+def record(frame, dims):
+    """Per codebook: the oracle's code and top-1 - top-2 margin; and the logit
+    vectors [1 + n_res][vmax] in fp32 (entries past a codebook's size zero)."""
     codes, logits = frame
-    rng = np.random.default_rng(seed)
-    vecs = []
+    vmax = max(dims.vocab_c0, dims.vocab_res if dims.n_res else 0)
+    vecs, full = [], np.zeros((dims.n_res + 1, vmax), dtype=np.float32)
     for k in range(dims.n_res + 1):
         V = dims.vocab_c0 if k == 0 else dims.vocab_res
         lg = np.asarray(logits[k][:V], dtype=np.float64)
         order = np.argsort(lg)
-        top = [int(order[-1]), int(order[-2])]
-        idx = sorted(set(rng.choice(V, SAMPLES, replace=False).tolist()) | set(top))
-        vecs.append({"code": int(codes[k]), "margin": float(lg[top[0]] - lg[top[1]]), "idx": idx,
-                     "logits": [float("%.7g" % lg[i]) for i in idx]})
-    return vecs
+        vecs.append({"code": int(codes[k]), "margin": float(lg[order[-1]] - lg[order[-2]])})
+        full[k, :V] = lg
+    return vecs, full
 
 
 def main(names):
@@ -79,8 +79,8 @@ def main(names):
         frames = [dec.prefill(prompt)]
         for _ in range(EARLY_FRAMES):
             frames.append(dec.decode_frame())
-        early = {"forced": [[int(c) for c in f[0]] for f in frames],
-                 "frames": [record(f, dims, 100 + i) for i, f in enumerate(frames)]}
+        recs = [record(f, dims) for f in frames]
+        early = {"forced": [[int(c) for c in f[0]] for f in frames], "frames": [r[0] for r in recs]}
 
         # late frame: forced random frames 0..K, frame K sits at position n - 1 + K
         K = LATE_LAST_POS - (wl.prefill_len - 1)
@@ -88,13 +88,15 @@ def main(names):
         dec = OracleDecoder(model, wl.max_len)
         tokens = np.concatenate([prompt, np.array([f[0] for f in forced[:K]], dtype=prompt.dtype)])
         last = dec.prefill(tokens, forced=np.array(forced[K], dtype=np.int32))
-        late = {"force_seed": FORCE_SEED, "frames_forced": K + 1, "position": LATE_LAST_POS,
-                "frame": record(last, dims, 999)}
+        late_vecs, late_full = record(last, dims)
+        late = {"force_seed": FORCE_SEED, "frames_forced": K + 1, "position": LATE_LAST_POS, "frame": late_vecs}
         doc = {"workload": name, "source": "tests/golden/make_fullshape.py (CPU oracle, oracle/model.py)",
                "weight_seed": wl.weight_seed, "prompt_seed": wl.prompt_seed, "prefill": wl.prefill_len,
                "max_len": wl.max_len, "early": early, "late": late}
         with open(os.path.join(out_dir, f"fullshape_{name}.json"), "w") as f:
             json.dump(doc, f, separators=(",", ":"))
+        np.savez_compressed(os.path.join(out_dir, f"fullshape_{name}.npz"),
+                            early=np.stack([r[1] for r in recs]), late=late_full)
         print(f"{name}: done in {time.time() - t0:.0f} s", flush=True)
         del model, dec
 

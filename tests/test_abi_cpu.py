@@ -222,7 +222,7 @@ def test_codec_rates_and_dilations_checked(N):
     out = ctypes.c_size_t(0)
     assert N.lib.dar_codec_workspace_bytes(ctypes.byref(c), ctypes.byref(out)) == N.DAR_E_INVAL
     c = _codec_cfg(N)
-    c.dilations[2] = 30                   # 3 * 30 > 64 positions of reach
+    c.dilations[2] = 11                   # 3 * 11 > 32 positions of reach
     assert N.lib.dar_codec_workspace_bytes(ctypes.byref(c), ctypes.byref(out)) == N.DAR_E_INVAL
 
 

@@ -129,3 +129,67 @@ def test_fullshape_batch_equals_single():
         assert not st["exact_fail"], st
     del dw
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("name", ["s2pro_dual_b16", "s2pro_dual_b64"])
+def test_fullshape_lockstep_batch_matches_oracle(name):
+    """Full shape in the batched benchmark's configuration (16 or 64 sequences
+    decoded in lockstep, max length 4096, ragged prompts of 128..512 ids): row
+    0 holds the stored oracle reference runs (prefill 128 + 9 greedy-forced
+    frames, and the frame at position 1007 after 880 randomly forced frames)
+    beside the workload's own prompts in the other rows; row 0's frames must
+    meet the full-shape bar (whole logit vectors within the bf16 relative-L2
+    tolerance, codes exact above the 1e-2 margin, >= 99% agreement)."""
+    import torch
+
+    from dar_decode_frame_amd.session import DarSession, DeviceWeights
+    from test_gpu_fullshape import _compare, _golden, _random_frames
+    wl = synth.WORKLOADS[name]
+    ref_wl = synth.WORKLOADS["s2pro_dual_bf16"]
+    dims = wl.dims
+    B = wl.batch
+    ref = _golden(ref_wl.name)
+    host = synth.gen_weights(dims, wl.weight_seed)
+    dw = DeviceWeights(dims, host, "bf16")
+    del host
+    lens, prompts = synth.gen_ragged_prompts(B, wl.prefill_len, wl.prefill_len_max, dims.vocab_c0,
+                                             wl.prompt_seed, wl.length_seed)
+    prompts = [synth.gen_prompt(ref_wl.prefill_len, dims.vocab_c0, ref_wl.prompt_seed)] + list(prompts[1:])
+    sess = DarSession(dims, dw, wl.max_len, batch=B)
+    fc = dims.n_res + 1
+    rng = np.random.default_rng(31)
+    stats = {"rel": [], "n": 0, "agree": 0, "exact_fail": []}
+
+    def run(row0_frames, keep):
+        outs = []
+        for i, f in enumerate(row0_frames):
+            forced = rng.integers(0, min(dims.vocab_c0, dims.vocab_res), (B, fc)).astype(np.int32)
+            forced[0] = f
+            if i == 0:
+                out = sess.prefill(prompts, forced=forced, want=keep(i))
+            else:
+                out = sess.decode_frame(forced=forced, want=keep(i))
+            if keep(i):
+                outs.append((out[0][0].copy(), out[1][0].copy()))
+        return outs
+
+    early = [np.asarray(f, dtype=np.int32) for f in ref["early"]["forced"]]
+    got = run(early, lambda i: True)
+    for (codes, logits), rv, rf in zip(got, ref["early"]["frames"], ref["early"]["full"]):
+        _compare(rv, rf, codes, logits, dims, stats)
+    late = ref["late"]
+    forced = [np.asarray(f, dtype=np.int32) for f in _random_frames()(dims, late["frames_forced"], late["force_seed"])]
+    got = run(forced, lambda i: i == len(forced) - 1)
+    assert sess.position()[0] == late["position"] + 1
+    codes, logits = got[-1]
+    _compare(late["frame"], late["full"], codes, logits, dims, stats)
+    agree = stats["agree"] / stats["n"]
+    print(f"\nlockstep full shape B={B}: max rel {max(stats['rel']):.3e}, median rel {np.median(stats['rel']):.3e}, "
+          f"agreement {agree:.4f} over {stats['n']} vectors, exact failures {stats['exact_fail']}")
+    assert max(stats["rel"]) <= TOL["bf16"], stats
+    assert not stats["exact_fail"], stats
+    assert agree >= 0.99, stats
+    assert sess.nonfinite() == 0
+    sess.close()
+    del dw
+    torch.cuda.empty_cache()

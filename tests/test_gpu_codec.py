@@ -18,11 +18,12 @@ chains about thirty such roundings, and a rounding decision flips wherever
 fp32 and fp64 sums straddle a bf16 boundary; the flips then propagate. The
 oracle itself shows the size of that: perturbing each of its convolution sums
 by a relative 1e-7 (fp32 noise) moves its bf16-activation output by 0.6e-3 to
-2.8e-3 relative L2 at the tiny shape. So a whole decode is held to <= 1e-2
-against the oracle in the same activation precision and <= 2e-2 against the
-fp64 oracle (bf16 activation rounding alone moves the oracle's output by 0.4%
-at the tiny shape and 0.8% at full shape), and each convolution to the tight
-per-output bound above.
+2.8e-3 relative L2 at the tiny shape and by 7.3e-3 to 7.7e-3 at full shape (a
+24-frame window). So a whole decode is held to <= 1.5e-2 (about twice that
+spread) against the oracle in the same activation precision and <= 2e-2
+against the fp64 oracle (bf16 activation rounding alone moves the oracle's
+output by 0.4% at the tiny shape and 0.8% at full shape), and each
+convolution to the tight per-output bound above.
 """
 import ctypes
 
@@ -161,7 +162,7 @@ def test_tiny_decode_against_oracle(tiny_codec, frames):
     ref_f = codec_decode(codes, P)
     assert got.shape == ref_b.shape == (frames * d.hop,)
     assert np.all(np.abs(got) < 1)
-    assert _rel(got, ref_b) <= 1e-2, _rel(got, ref_b)
+    assert _rel(got, ref_b) <= 1.5e-2, _rel(got, ref_b)
     assert _rel(got, ref_f) <= 2e-2, _rel(got, ref_f)
     print(f"tiny codec {frames} frames: rel L2 {_rel(got, ref_b):.2e} (bf16 activations), {_rel(got, ref_f):.2e} (fp64)")
 
@@ -222,4 +223,4 @@ def test_fullshape_decode_windows_against_oracle():
         ref_f = codec_decode(codes[lo:hi], P)[win]
         rb, rf = _rel(got[seg], ref_b), _rel(got[seg], ref_f)
         print(f"full-shape codec frames {a}..{b}: rel L2 {rb:.2e} (bf16 activations), {rf:.2e} (fp64)")
-        assert rb <= 1e-2 and rf <= 2e-2
+        assert rb <= 1.5e-2 and rf <= 2e-2

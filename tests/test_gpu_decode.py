@@ -84,6 +84,31 @@ def test_tiny_teacher_forced_parity(tiny_host, wtype, forcing):
     sess.close()
 
 
+@pytest.mark.parametrize("wtype", ["bf16", "fp8"])
+def test_tiny_workload_own_frames(tiny_host, wtype):
+    """The tiny workload exactly as specified: prefill 16, 16 decoded frames,
+    max length 32 (17 frames x 4 codebooks = 68 comparisons), teacher-forced
+    with the oracle's greedy frames. Reports the agreement and the oracle
+    margin of every code that differs; the bar is the same as above (99% of 68
+    comparisons: every code must agree)."""
+    dims, host = tiny_host
+    wl = W[f"tiny_{wtype}"]
+    prompt = synth.gen_prompt(wl.prefill_len, dims.vocab_c0, wl.prompt_seed)
+    free, _ = _oracle_run(dims, host, wtype, prompt, wl.decode_frames, wl.max_len)
+    forced = [c for c, _ in free]
+    sess, _ = _session(dims, host, wtype, wl.max_len)
+    got = _gpu_run(sess, prompt, wl.decode_frames, forced)
+    stats = compare_frames(got, free, dims, wtype)
+    flips = [(f, k, int(g[0][k]), int(o[0][k]), round(float(np.sort(o[1][k][:dims.vocab_c0 if k == 0 else dims.vocab_res])[-1]
+                                                       - np.sort(o[1][k][:dims.vocab_c0 if k == 0 else dims.vocab_res])[-2]), 6))
+             for f, (g, o) in enumerate(zip(got, free)) for k in range(dims.n_res + 1) if g[0][k] != o[0][k]]
+    print(f"\n{wl.name}: agreement {stats['agree']:.4f} over {stats['n']} comparisons, max rel {stats['max_rel']:.2e}, "
+          f"median rel {stats['median_rel']:.2e}, codes that differ (frame, codebook, gpu, oracle, oracle margin): {flips}")
+    assert stats["n"] == (wl.decode_frames + 1) * (dims.n_res + 1)
+    assert_parity(stats)
+    sess.close()
+
+
 @pytest.mark.parametrize("wtype,n_prompt", [("bf16", 1), ("bf16", 128), ("bf16", 200), ("fp8", 200), ("int8", 200),
                                                    ("int4", 200)])
 def test_tiny_prefill_blocks_parity(tiny_host, wtype, n_prompt):

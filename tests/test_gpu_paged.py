@@ -283,8 +283,8 @@ def test_fullshape_paged_matches_oracle(name):
 
     early = [np.asarray(f, dtype=np.int32) for f in ref["early"]["forced"]]
     got = run(early, lambda i: True)
-    for (codes, logits), rv in zip(got, ref["early"]["frames"]):
-        _compare(rv, codes, logits, dims, stats)
+    for (codes, logits), rv, rf in zip(got, ref["early"]["frames"], ref["early"]["full"]):
+        _compare(rv, rf, codes, logits, dims, stats)
     sess.reset()
     assert sess.pages_free() == cb.n_pages - 1
     late = ref["late"]
@@ -292,7 +292,7 @@ def test_fullshape_paged_matches_oracle(name):
     got = run(forced, lambda i: i == len(forced) - 1)
     assert sess.position()[slot] == late["position"] + 1
     codes, logits = got[-1]
-    _compare(late["frame"], codes, logits, dims, stats)
+    _compare(late["frame"], late["full"], codes, logits, dims, stats)
     agree = stats["agree"] / stats["n"]
     print(f"\npaged full shape {name}: max rel {max(stats['rel']):.3e}, agreement {agree:.4f} over {stats['n']} "
           f"vectors, exact failures {stats['exact_fail']}")
