@@ -192,6 +192,9 @@ def main():
                 "bytes_per_launch": per, "avg_launch_us": round(avg_ms * 1000, 2), "launches_timed": len(one_row),
                 "overlapped_avg_launch_us": round(live_ms / live_n * 1000, 2) if live_n else None, "overlapped_launches": live_n,
                 "launches_per_frame": len(recs) // args.profile_frames, "frame_time_share": share}
+        rp = rocprof_launch_us(name, wl.name)
+        roof["rocprof_avg_launch_us"] = rp
+        roof["rocprof_frac"] = round(per / (rp * 1e-6) / HBM_PEAK, 4) if rp else None
         log(f"dominant kernel {name}: {avg_ms * 1000:.1f} us/launch serialised ({achieved / 1e9:.0f} GB/s), "
             + (f"{live_ms / live_n * 1000:.1f} us beside the other chain" if live_n else "no live timing (graph replay)")
             + f"; serialised-frame shares {share}")
@@ -563,6 +566,9 @@ def bench_codec(args, wl):
                 "bytes_per_launch": b, "avg_launch_us": round(avg * 1000, 2), "launches_timed": len(times),
                 "hbm_gb_s": round(b / (avg / 1000.0) / 1e9, 1), "launches_per_step": len(recs) // max(1, args.profile_frames),
                 "step_time_share": share}
+        rp = rocprof_launch_us(name, wl.name, "dar_codec.hip")
+        roof["rocprof_avg_launch_us"] = rp
+        roof["rocprof_frac"] = round(f / (rp * 1e-6) / MFMA_BF16_PEAK, 4) if rp else None
         log(f"dominant kind {name}: {avg * 1000:.1f} us/launch, {achieved / 1e12:.0f} TFLOP/s; shares {share}")
     cpu = None
     if not args.no_cpu_baseline:
@@ -654,6 +660,29 @@ def measured_traffic(kind, workload, source="dar_kernels.hip"):
     if hashlib.sha256(open(src, "rb").read()).hexdigest() != m_h.group(1):
         return None
     return int(m_t.group(1))
+
+
+def rocprof_launch_us(kind, workload, source="dar_kernels.hip"):
+    """The dominant kind's average launch duration in the committed rocprofv3
+    kernel-trace summary of this workload's bench run (profiles/
+    frame_kernels_<workload>.md: the kind's launches in the serialised frames,
+    as the tracer timed them), or None when there is none or the kernel source
+    has changed since the trace was taken."""
+    import hashlib
+    import re
+    path = os.path.join(ROOT, "profiles", f"frame_kernels_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_k = re.search(r"roofline_kind:\s*(\w+)", text)
+    m_t = re.search(r"rocprof_avg_launch_us:\s*([0-9.]+)", text)
+    m_h = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)
+    if not (m_k and m_t and m_h) or m_k.group(1) != kind:
+        return None
+    src = os.path.join(ROOT, "dar_decode_frame_amd", "csrc", source)
+    if hashlib.sha256(open(src, "rb").read()).hexdigest() != m_h.group(1):
+        return None
+    return float(m_t.group(1))
 
 
 SAMPLING = {"temperature": 0.8, "top_k": 50, "top_p": 0.9, "repetition_penalty": 1.2, "repetition_window": 16}
