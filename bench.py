@@ -478,7 +478,7 @@ def bench_continuous(args, wl):
     print(json.dumps(out), flush=True)
 
 
-CODEC_TAGS = {0: "rvq", 1: "in_conv", 2: "up", 3: "res_conv7", 4: "res_conv1", 5: "out_conv"}
+CODEC_TAGS = {0: "rvq", 1: "in_conv", 2: "up", 3: "res_conv7", 4: "res_conv1", 5: "out_conv", 6: "res_unit"}
 MFMA_BF16_PEAK = 2.5e15
 
 
@@ -486,7 +486,9 @@ def codec_launch_cost(d, frames, tag):
     """(FLOPs, bytes) one launch of a codec kind moves: the convolution's
     multiply-adds (2 per weight per output row per tap) and the activations it
     must read and write (fp32 residual stream, bf16 residual-unit hidden rows,
-    bf16 latent frames; weights counted once)."""
+    bf16 latent frames; weights counted once). A one-launch residual unit
+    reads its fp32 input rows and writes its output rows once, its hidden rows
+    staying on chip."""
     kind, blk = tag % 16, tag // 16
     w = d.widths
     if kind == 0:
@@ -505,6 +507,8 @@ def codec_launch_cost(d, frames, tag):
         return 2 * rows * cout * cout * d.kernel, rows * cout * 4 + rows * cout * 2 + cout * cout * d.kernel * 2
     if kind == 4:
         return 2 * rows * cout * cout, rows * cout * 2 + 2 * rows * cout * 4 + cout * cout * 2
+    if kind == 6:
+        return 2 * rows * cout * cout * (d.kernel + 1), 2 * rows * cout * 4 + cout * cout * (d.kernel + 1) * 2
     rows_out = frames * d.hop
     return 2 * rows_out * w[-1] * d.kernel, rows_out * w[-1] * 4 + rows_out * 4
 

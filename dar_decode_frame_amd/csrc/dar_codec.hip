@@ -88,18 +88,23 @@ struct ConvArgs {
 // quarter, the swizzle the unit within it).
 __device__ __forceinline__ int lds_at(int r, int u) { return r * 64 + ((u ^ ((r >> 2) & 3)) << 4); }
 
-template <int WM, int WN, int NT, bool XB16, bool YB16>
-__global__ __launch_bounds__(kThreads) void k_conv(ConvArgs a) {
+// The MFMA tiles of one workgroup: rows t0 .. t0 + 32 WM of phase z times
+// columns n0 .. n0 + 32 NT WN, summed over every input channel and tap, then
+// handed to epi(acc) (wave (wm, wn) holds rows t0 + 32 wm .., columns
+// n0 + 32 (wn NT + nt) ..). Uses the LDS at smem (window rows, then every
+// tap's weights); epi runs after a barrier, so it may reuse that LDS. (The
+// accumulators stay local to this function: passed in by reference instead,
+// they cost the compiler about fifty more registers and a wave per SIMD.)
+template <int WM, int WN, int NT, bool XB16, typename Epi>
+__device__ __forceinline__ void conv_accumulate(const ConvArgs& a, int z, int t0, int n0, char* smem, Epi&& epi) {
+  f32x16 acc[NT];
   constexpr int BM = 32 * WM, BN = 32 * NT * WN;
   static_assert(WM * WN == 4, "four waves");
   // 16-byte units a thread stages per chunk: window rows x 4, tap rows x 4
   constexpr int XN = ((BM + 2 * kMaxOff) * 4 + kThreads - 1) / kThreads;
   constexpr int WNU = (kMaxTaps * BN * 4 + kThreads - 1) / kThreads;
-  extern __shared__ __align__(16) char smem[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave % WM, wn = wave / WM;
-  const int z = blockIdx.z;
-  const int t0 = blockIdx.x * BM, n0 = blockIdx.y * BN;
   const int* off = a.off + z * a.ntap;
   int omin = off[0], omax = off[0];
   for (int j = 1; j < a.ntap; ++j) {
@@ -111,7 +116,6 @@ __global__ __launch_bounds__(kThreads) void k_conv(ConvArgs a) {
   char* xs = smem;
   char* ws = smem + wrows * 64;
   const uint16_t* Wz = a.W + (size_t)z * a.ntap * a.Cout * a.Cin;
-  f32x16 acc[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
@@ -204,29 +208,43 @@ __global__ __launch_bounds__(kThreads) void k_conv(ConvArgs a) {
     }
     __syncthreads();
   }
-  // lane holds output channel n of its tiles; accumulator v holds output row
-  // t0 + 32 wm + (v % 4) + 4 half + 8 (v / 4)
+  epi(acc);
+}
+
+template <int WM, int WN, int NT, bool XB16, bool YB16>
+__global__ __launch_bounds__(kThreads) void k_conv(ConvArgs a) {
+  constexpr int BM = 32 * WM, BN = 32 * NT * WN;
+  extern __shared__ __align__(16) char smem[];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave % WM, wn = wave / WM;
+  const int z = blockIdx.z;
+  const int t0 = blockIdx.x * BM, n0 = blockIdx.y * BN;
+  const int half = lane >> 5, l32 = lane & 31;
+  conv_accumulate<WM, WN, NT, XB16>(a, z, t0, n0, smem, [&](f32x16 (&acc)[NT]) {
+    // lane holds output channel n of its tiles; accumulator v holds output row
+    // t0 + 32 wm + (v % 4) + 4 half + 8 (v / 4)
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const int n = n0 + (wn * NT + nt) * 32 + l32;
-    if (n >= a.Cout) continue;
-    const float b = bf2f(a.bias[n]);
-    const float ao = YB16 ? bf2f(a.alpha_out[n]) : 0.f;
+    for (int nt = 0; nt < NT; ++nt) {
+      const int n = n0 + (wn * NT + nt) * 32 + l32;
+      if (n >= a.Cout) continue;
+      const float b = bf2f(a.bias[n]);
+      const float ao = YB16 ? bf2f(a.alpha_out[n]) : 0.f;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int t = t0 + wm * 32 + (v & 3) + 4 * half + 8 * (v >> 2);
-      if (t >= a.T) continue;
-      const size_t at = ((size_t)t * a.nphase + z) * a.Cout + n;
-      float val = acc[nt][v] + b;
-      if constexpr (YB16) {
-        a.yb[at] = (uint16_t)f2bf(snake(val, ao));
-      } else {
-        if (a.res) val += a.res[at];
-        if (a.tanh_out) val = tanhf(val);
-        a.yf[at] = val;
+      for (int v = 0; v < 16; ++v) {
+        const int t = t0 + wm * 32 + (v & 3) + 4 * half + 8 * (v >> 2);
+        if (t >= a.T) continue;
+        const size_t at = ((size_t)t * a.nphase + z) * a.Cout + n;
+        float val = acc[nt][v] + b;
+        if constexpr (YB16) {
+          a.yb[at] = (uint16_t)f2bf(snake(val, ao));
+        } else {
+          if (a.res) val += a.res[at];
+          if (a.tanh_out) val = tanhf(val);
+          a.yf[at] = val;
+        }
       }
     }
-  }
+  });
 }
 
 // The output convolution (one channel): Snake, K taps, bias, tanh. A
@@ -401,6 +419,98 @@ hipError_t allow_lds(KernelT kern, size_t lds, std::atomic<bool>& done) {
   return e;
 }
 
+// One residual unit in one launch, for widths a workgroup's tile spans
+// (C = 32 NT WN): h = Snake(conv_K,dil(Snake(x, alpha1)) + b1, alpha2) is
+// rounded to bf16 and kept in LDS, then y = x + conv_1(h) + b2. The 1-tap
+// convolution needs only the workgroup's own rows of h, so h never goes to
+// HBM. y and x are different buffers: the neighbouring workgroups still read
+// the rows of x around their tiles.
+struct ResArgs {
+  ConvArgs c1;              // the 7-tap convolution (fp32 x with Snake alpha1, [K][C][C] weights, b1)
+  const uint16_t* alpha2;   // Snake of the hidden rows
+  const uint16_t* W2;       // [C][C] bf16 (the 1-tap convolution)
+  const uint16_t* b2;
+  float* y;                 // [T][C] = x + conv_1(h) + b2
+  int h_at;                 // LDS byte offset of h (past the 7-tap convolution's staging)
+};
+
+template <int WM, int WN, int NT>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void k_resunit(ResArgs r) {
+  constexpr int BM = 32 * WM, C = 32 * NT * WN;
+  constexpr int CH = C / 32;                       // 32-channel chunks of h
+  constexpr int WU = (C * 4 + kThreads - 1) / kThreads;  // 16-byte units of a W2 chunk per thread
+  extern __shared__ __align__(16) char smem[];
+  const ConvArgs& a = r.c1;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave % WM, wn = wave / WM;
+  const int t0 = blockIdx.x * BM;
+  const int half = lane >> 5, l32 = lane & 31;
+  // h: chunk c's rows at hs + c BM 64, laid out as a staged window (lds_at)
+  char* hs = smem + r.h_at;
+  conv_accumulate<WM, WN, NT, false>(a, 0, t0, 0, smem, [&](f32x16 (&acc)[NT]) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const int n = (wn * NT + nt) * 32 + l32;  // chunk wn NT + nt, channel l32 of it
+      const float b = bf2f(a.bias[n]), ao = bf2f(r.alpha2[n]);
+      char* hc = hs + (size_t)(wn * NT + nt) * BM * 64;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int row = wm * 32 + (v & 3) + 4 * half + 8 * (v >> 2);
+        const uint16_t hv = t0 + row < a.T ? (uint16_t)f2bf(snake(acc[nt][v] + b, ao)) : (uint16_t)0;
+        *reinterpret_cast<uint16_t*>(hc + lds_at(row, l32 >> 3) + 2 * (l32 & 7)) = hv;
+      }
+    }
+  });
+  // the 1-tap convolution over h, chunk by chunk; its weight chunk reuses the
+  // LDS of the 7-tap convolution's staging
+  char* ws = smem;
+  f32x16 acc[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[nt][v] = 0.f;
+  for (int c = 0; c < CH; ++c) {
+    u32x4 wv[WU];
+#pragma unroll
+    for (int k = 0; k < WU; ++k) {
+      const int i = tid + k * kThreads;
+      wv[k] = i < C * 4 ? *reinterpret_cast<const u32x4*>(r.W2 + (size_t)(i >> 2) * C + 32 * c + 8 * (i & 3))
+                        : u32x4{0u, 0u, 0u, 0u};
+    }
+    __syncthreads();  // h is complete (c = 0) / the previous chunk's reads of ws are done
+#pragma unroll
+    for (int k = 0; k < WU; ++k) {
+      const int i = tid + k * kThreads;
+      if (i < C * 4) *reinterpret_cast<u32x4*>(ws + lds_at(i >> 2, i & 3)) = wv[k];
+    }
+    __syncthreads();
+    const char* hc = hs + (size_t)c * BM * 64;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int u = 2 * ks + half;
+      const bf16x8 A = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(hc + lds_at(wm * 32 + l32, u)));
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const bf16x8 B =
+            __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(ws + lds_at((wn * NT + nt) * 32 + l32, u)));
+        acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B, acc[nt], 0, 0, 0);
+      }
+    }
+  }
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int n = (wn * NT + nt) * 32 + l32;
+    const float b = bf2f(r.b2[n]);
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int t = t0 + wm * 32 + (v & 3) + 4 * half + 8 * (v >> 2);
+      if (t >= a.T) continue;
+      const size_t at = (size_t)t * C + n;
+      r.y[at] = (acc[nt][v] + b) + a.xf[at];  // the two-launch path's order of the sums
+    }
+  }
+}
+
 template <int WM, int WN, int NT, bool XB16, bool YB16>
 hipError_t go_conv(const ConvArgs& a, dim3 grid, size_t lds, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   static std::atomic<bool> big{false};  // one flag per kernel instantiation
@@ -445,6 +555,50 @@ hipError_t launch_conv(const ConvArgs& a, hipStream_t s, hipEvent_t e0 = nullptr
   if (!xb && yb) return go_conv_cfg<false, true>(ci, a, grid, lds, s, e0, e1);
   if (!xb && !yb) return go_conv_cfg<false, false>(ci, a, grid, lds, s, e0, e1);
   return hipErrorInvalidValue;  // bf16 in and bf16 out: not a layer of the decoder
+}
+
+// Tile of the one-launch residual unit at width C: the workgroup spans all C
+// output channels (index into kCfgs, or -1: C is run as two launches).
+int resunit_cfg(int C) {
+  switch (C) {
+    case 32: return 4;   // 128 x 32
+    case 64: return 2;   // 64 x 64
+    case 96: return 0;   // 128 x 96
+    case 128: return 1;  // 64 x 128
+    default: return -1;  // (a 64 x 192 tile runs at one wave per SIMD: slower than two launches)
+  }
+}
+
+template <int WM, int WN, int NT>
+hipError_t go_resunit(const ResArgs& r, dim3 grid, size_t lds, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  static std::atomic<bool> big{false};
+  hipError_t e = allow_lds(k_resunit<WM, WN, NT>, lds, big);
+  if (e != hipSuccess) return e;
+  if (e0 || e1)
+    hipExtLaunchKernelGGL((k_resunit<WM, WN, NT>), grid, dim3(kThreads), lds, s, e0, e1, 0, r);
+  else
+    hipLaunchKernelGGL((k_resunit<WM, WN, NT>), grid, dim3(kThreads), lds, s, r);
+  return hipGetLastError();
+}
+
+// One residual unit in one launch (r.c1 describes the 7-tap convolution:
+// fp32 input with alpha1, C in and out, one phase; y != x).
+hipError_t launch_resunit(ResArgs r, hipStream_t s, hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr) {
+  const ConvArgs& a = r.c1;
+  const int ci = resunit_cfg(a.Cout);
+  if (ci < 0 || a.Cin != a.Cout || a.nphase != 1 || a.xb || !a.xf || r.y == a.xf) return hipErrorInvalidValue;
+  const TileCfg& c = kCfgs[ci];
+  const int span = a.off[a.ntap - 1] - a.off[0];
+  const size_t conv = conv_lds(c, span, a.ntap);
+  r.h_at = (int)conv;
+  const size_t lds = conv + (size_t)c.bm() * a.Cout * 2;
+  const dim3 grid((a.T + c.bm() - 1) / c.bm());
+  switch (ci) {
+    case 0: return go_resunit<4, 1, 3>(r, grid, lds, s, e0, e1);
+    case 1: return go_resunit<2, 2, 2>(r, grid, lds, s, e0, e1);
+    case 2: return go_resunit<2, 2, 1>(r, grid, lds, s, e0, e1);
+    default: return go_resunit<4, 1, 1>(r, grid, lds, s, e0, e1);
+  }
 }
 
 size_t out_lds(int C, int K) {
@@ -707,6 +861,7 @@ int run_decode(dar_codec* c, const int32_t* codes, int frames, float* audio, boo
     if ((st = conv(a, 2 + 16 * i)) != DAR_OK) return st;
     cur ^= 1;
     rows *= sr;
+    const bool fuse = resunit_cfg(cout) >= 0;
     for (int u = 0; u < g.n_units; ++u) {
       const dar_codec_unit& U = B.units[u];
       ConvArgs a1{};
@@ -720,6 +875,20 @@ int run_decode(dar_codec* c, const int32_t* codes, int frames, float* audio, boo
       a1.ntap = K;
       conv_taps(K, g.dilations[u], a1.off);
       a1.bias = U16(U.b1);
+      if (fuse) {
+        ResArgs r{};
+        r.c1 = a1;
+        r.alpha2 = U16(U.alpha2);
+        r.W2 = reinterpret_cast<const uint16_t*>(c->ws + L.w2[i][u]);
+        r.b2 = U16(U.b2);
+        r.y = bufs[cur ^ 1];
+        hipEvent_t *e0 = nullptr, *e1 = nullptr;
+        evs(e0, e1);
+        CODEC_HIP(c, launch_resunit(r, s, e0 ? *e0 : nullptr, e1 ? *e1 : nullptr), "codec residual unit");
+        tag(6 + 16 * i);
+        cur ^= 1;
+        continue;
+      }
       a1.yb = h;
       a1.alpha_out = U16(U.alpha2);
       if ((st = conv(a1, 3 + 16 * i)) != DAR_OK) return st;
@@ -959,6 +1128,69 @@ int dar_codec_op_conv(const void* x, int32_t x_bf16, const void* alpha, int32_t 
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   (void)hipFree(wr);
   return e == hipSuccess ? DAR_OK : codec_hip_fail(nullptr, e, "op conv");
+}
+
+int dar_codec_op_resunit(const float* x, int32_t T, int32_t C, const void* alpha1, const void* w1, const void* b1,
+                         int32_t taps, int32_t dilation, const void* alpha2, const void* w2, const void* b2,
+                         int32_t fused, float* y, void* stream) {
+  if (!x || !alpha1 || !w1 || !b1 || !alpha2 || !w2 || !b2 || !y || T < 1 || C < 32 || C % 32 || C > 8192 ||
+      taps < 1 || taps > kMaxTaps || taps % 2 == 0 || dilation < 1 || (taps - 1) / 2 * dilation > kMaxOff) {
+    g_codec_error = "op resunit: bad pointer, width or taps";
+    return DAR_E_INVAL;
+  }
+  if (fused && (resunit_cfg(C) < 0 || y == x)) {
+    g_codec_error = "op resunit: the one-launch unit needs C in {32, 64, 96, 128} and y != x";
+    return DAR_E_INVAL;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const size_t w1b = (size_t)2 * taps * C * C, w2b = (size_t)2 * C * C, hb = fused ? 0 : (size_t)2 * T * C;
+  char* buf = nullptr;
+  hipError_t e = hipMalloc(reinterpret_cast<void**>(&buf), w1b + w2b + hb);
+  if (e != hipSuccess) return codec_hip_fail(nullptr, e, "op resunit alloc");
+  uint16_t* W1 = reinterpret_cast<uint16_t*>(buf);
+  uint16_t* W2 = reinterpret_cast<uint16_t*>(buf + w1b);
+  uint16_t* h = reinterpret_cast<uint16_t*>(buf + w1b + w2b);
+  e = relayout_conv(U16(w1), C, C, taps, W1, s);
+  if (e == hipSuccess) e = relayout_conv(U16(w2), C, C, 1, W2, s);
+  ConvArgs a1{};
+  a1.xf = x;
+  a1.alpha_in = U16(alpha1);
+  a1.T = T;
+  a1.Cin = C;
+  a1.Cout = C;
+  a1.W = W1;
+  a1.nphase = 1;
+  a1.ntap = taps;
+  conv_taps(taps, dilation, a1.off);
+  a1.bias = U16(b1);
+  if (e == hipSuccess && fused) {
+    ResArgs r{};
+    r.c1 = a1;
+    r.alpha2 = U16(alpha2);
+    r.W2 = W2;
+    r.b2 = U16(b2);
+    r.y = y;
+    e = launch_resunit(r, s);
+  } else if (e == hipSuccess) {
+    a1.yb = h;
+    a1.alpha_out = U16(alpha2);
+    e = launch_conv(a1, s);
+    ConvArgs a2{};
+    a2.xb = h;
+    a2.T = T;
+    a2.Cin = C;
+    a2.Cout = C;
+    a2.W = W2;
+    a2.nphase = 1;
+    a2.ntap = 1;
+    a2.bias = U16(b2);
+    a2.yf = y;
+    a2.res = x;
+    if (e == hipSuccess) e = launch_conv(a2, s);
+  }
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  (void)hipFree(buf);
+  return e == hipSuccess ? DAR_OK : codec_hip_fail(nullptr, e, "op resunit");
 }
 
 }  // extern "C"

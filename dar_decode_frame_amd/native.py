@@ -191,6 +191,8 @@ _SIGS = {
     "dar_codec_last_error": ([_VP], ctypes.c_char_p),
     "dar_codec_op_conv": ([_VP, _I32, _VP, _I32, _I32, _I32, _VP, _VP, _I32, _I32, _I32, _VP, _I32, _VP, _VP],
                           ctypes.c_int),
+    "dar_codec_op_resunit": ([_VP, _I32, _I32, _VP, _VP, _VP, _I32, _I32, _VP, _VP, _VP, _I32, _VP, _VP],
+                             ctypes.c_int),
 }
 
 
@@ -481,3 +483,9 @@ def dar_codec_op_conv(x_ptr, x_bf16, alpha_ptr, T, Cin, Cout, w_ptr, b_ptr, taps
                       tanh_out, y_ptr, stream_ptr):
     return _check_codec(lib.dar_codec_op_conv(x_ptr, x_bf16, alpha_ptr, T, Cin, Cout, w_ptr, b_ptr, taps, dilation,
                                               stride, res_ptr, tanh_out, y_ptr, stream_ptr), "dar_codec_op_conv")
+
+
+def dar_codec_op_resunit(x_ptr, T, C, alpha1_ptr, w1_ptr, b1_ptr, taps, dilation, alpha2_ptr, w2_ptr, b2_ptr, fused,
+                         y_ptr, stream_ptr):
+    return _check_codec(lib.dar_codec_op_resunit(x_ptr, T, C, alpha1_ptr, w1_ptr, b1_ptr, taps, dilation, alpha2_ptr,
+                                                 w2_ptr, b2_ptr, fused, y_ptr, stream_ptr), "dar_codec_op_resunit")

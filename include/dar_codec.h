@@ -132,7 +132,9 @@ int dar_codec_anomalies(dar_codec* ctx, int32_t* count_out);
  * launch itself (its kernel's start and end); one stream, synchronises.
  * ms_out, tag_out: host arrays of capacity cap; *n_out launches. Tags: 0 RVQ
  * sum, 1 input conv, 2 transposed conv, 3 residual 7-tap conv, 4 residual
- * 1-tap conv, 5 output conv; block i adds 16 i to tags 2..4. */
+ * 1-tap conv, 5 output conv, 6 residual unit in one launch (blocks of width
+ * 32, 64, 96 or 128 run each unit so, the others as tags 3 and 4);
+ * block i adds 16 i to tags 2, 3, 4 and 6. */
 int dar_codec_profile(dar_codec* ctx, const int32_t* codes, int32_t frames, float* audio, int32_t cap,
                       float* ms_out, int32_t* tag_out, int32_t* n_out);
 
@@ -157,6 +159,19 @@ const char* dar_codec_last_error(const dar_codec* ctx);
 int dar_codec_op_conv(const void* x, int32_t x_bf16, const void* alpha, int32_t T, int32_t Cin, int32_t Cout,
                       const void* w, const void* b, int32_t taps, int32_t dilation, int32_t stride,
                       const float* res, int32_t tanh_out, float* y, void* stream);
+
+/* Diagnostic: one residual unit on its own, y = x + conv1(Snake(conv_taps,dil(
+ * Snake(x, alpha1)) + b1, alpha2)) + b2, with the hidden activation rounded
+ * to bf16 (as in a decode). x, y: device fp32 [T][C]; alpha1, b1, alpha2, b2:
+ * device bf16 [C]; w1: bf16 [C][C][taps]; w2: bf16 [C][C][1] (PyTorch
+ * layouts). fused == 1 runs the one-launch kernel a decode uses at this width
+ * (C in {32, 64, 96, 128}, y != x; DAR_E_INVAL otherwise); fused == 0
+ * runs the two convolutions as two launches through a bf16 hidden buffer
+ * (any C multiple of 32, up to 8192; y may alias x). Both give the same
+ * values bit for bit. Allocates per call and synchronises the stream. */
+int dar_codec_op_resunit(const float* x, int32_t T, int32_t C, const void* alpha1, const void* w1, const void* b1,
+                         int32_t taps, int32_t dilation, const void* alpha2, const void* w2, const void* b2,
+                         int32_t fused, float* y, void* stream);
 
 #ifdef __cplusplus
 }

@@ -138,6 +138,53 @@ def test_residual_add_in_place_and_output_conv():
     assert np.max(np.abs(got2 - ref2)) < 1e-5 + 2.0 ** -7 * np.abs(w2).max() * np.abs(xin).max()
 
 
+@pytest.mark.parametrize("T,C,dil", [(150, 32, 9), (70, 64, 3), (333, 96, 1), (45, 128, 3), (700, 96, 9),
+                                     (1, 96, 1), (129, 128, 1)])
+def test_fused_residual_unit(T, C, dil):
+    """dar_codec_op_resunit: the one-launch unit (hidden rows kept in LDS)
+    gives the two-launch path's values bit for bit, and both are within the
+    oracle's bound: the 7-tap convolution's per-output bound e1, carried
+    through Snake (slope at most 2) and the hidden bf16 rounding (a value may
+    land one bf16 step, at most 2^-7 of its size, away), then summed by the
+    1-tap convolution, plus fp32 summation error."""
+    import torch
+    from dar_decode_frame_amd import native as N
+    r = np.random.default_rng(C * 1000 + T)
+    x = r.standard_normal((T, C)).astype(np.float32)
+    a1, a2 = _wide(0.5 + r.random(C)), _wide(0.5 + r.random(C))
+    w1 = _wide(r.standard_normal((C, C, 7)) / np.sqrt(7 * C))
+    b1 = _wide(r.standard_normal(C) * 0.1)
+    w2 = _wide(r.standard_normal((C, C, 1)) / np.sqrt(C))
+    b2 = _wide(r.standard_normal(C) * 0.1)
+    xd = _dev(x, np.float32)
+    dev = {k: _dev(_bf16_bits(v), np.int16) for k, v in dict(a1=a1, a2=a2, w1=w1, b1=b1, w2=w2, b2=b2).items()}
+    out = {}
+    p = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    for fused in (1, 0):
+        y = torch.full((T, C), float("nan"), dtype=torch.float32, device="cuda")
+        torch.cuda.synchronize()
+        N.dar_codec_op_resunit(p(xd), T, C, p(dev["a1"]), p(dev["w1"]), p(dev["b1"]), 7, dil, p(dev["a2"]),
+                               p(dev["w2"]), p(dev["b2"]), fused, p(y), None)
+        out[fused] = y.cpu().numpy()
+    assert np.array_equal(out[1].view(np.uint32), out[0].view(np.uint32))
+    xin = round_bf16(snake(x.astype(np.float64), a1)).astype(np.float64)
+    pre = conv1d(xin, w1, b1, dil)
+    e1 = 2e-5 * conv1d(np.abs(xin), np.abs(w1), np.zeros(C), dil) + 2.0 ** -7 * np.abs(w1).max() * np.abs(xin).max()
+    h = round_bf16(snake(pre, a2)).astype(np.float64)
+    ref = x + conv1d(h, w2, b2)
+    dh = 2.0 ** -7 * np.abs(h) + 2 * e1
+    bound = conv1d(dh, np.abs(w2), np.zeros(C)) + 2e-5 * (conv1d(np.abs(h), np.abs(w2), np.zeros(C)) + np.abs(x))
+    err = np.abs(out[1] - ref)
+    assert np.all(err <= bound), float((err / bound).max())
+    # in place is refused for the one-launch kernel, allowed for two launches
+    with pytest.raises(RuntimeError):
+        N.dar_codec_op_resunit(p(xd), T, C, p(dev["a1"]), p(dev["w1"]), p(dev["b1"]), 7, dil, p(dev["a2"]),
+                               p(dev["w2"]), p(dev["b2"]), 1, p(xd), None)
+    N.dar_codec_op_resunit(p(xd), T, C, p(dev["a1"]), p(dev["w1"]), p(dev["b1"]), 7, dil, p(dev["a2"]),
+                           p(dev["w2"]), p(dev["b2"]), 0, p(xd), None)
+    assert np.array_equal(xd.cpu().numpy().view(np.uint32), out[0].view(np.uint32))
+
+
 def _rel(a, b):
     return float(np.linalg.norm(a - b) / np.linalg.norm(b))
 
