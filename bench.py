@@ -63,6 +63,16 @@ def main():
     from dar_decode_frame_amd import native as N
     from dar_decode_frame_amd.session import DarSession, DeviceWeights
 
+    if args.calibrate_copy > 0:
+        # a device copy of known size, for scaling the profiler's HBM byte counters
+        n = args.calibrate_copy * 2 ** 20 // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"calibration copy of {args.calibrate_copy} MiB done")
+        del src, dst
     if args.workload in synth.CODEC_WORKLOADS:
         return bench_codec(args, synth.CODEC_WORKLOADS[args.workload])
     wl = synth.WORKLOADS[args.workload]
@@ -77,16 +87,6 @@ def main():
     if args.steps > max_steps or args.steps < 1:
         raise SystemExit(f"--steps must be in [1, {max_steps}] for {wl.name}")
     dev = torch.device("cuda:0")
-
-    if args.calibrate_copy > 0:
-        n = args.calibrate_copy * 2 ** 20 // 4
-        src = torch.ones(n, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        log(f"calibration copy of {args.calibrate_copy} MiB done")
-        del src, dst
 
     t0 = time.time()
     host = synth.gen_weights(dims, wl.weight_seed)
@@ -560,20 +560,27 @@ def bench_codec(args, wl):
         times = [m for m, t in recs if t == dom]
         avg = sum(times) / len(times)
         f, b = codec_launch_cost(d, wl.frames, dom)
-        achieved = f / (avg / 1000.0)
+        # the kind's roofline: MFMA if its FLOPs per algorithmic byte exceed
+        # the part's balance point (2.5 PFLOP/s / 8 TB/s = 312), else HBM
+        mfma = f / b >= MFMA_BF16_PEAK / HBM_PEAK
+        achieved = (f if mfma else b) / (avg / 1000.0)
+        peak = MFMA_BF16_PEAK if mfma else HBM_PEAK
         share = {f"{CODEC_TAGS[t % 16]}{'' if t % 16 in (0, 1, 5) else t // 16}": round(v / sum(totals.values()), 4)
                  for t, v in sorted(totals.items(), key=lambda kv: -kv[1])}
         name = f"{CODEC_TAGS[dom % 16]}{'' if dom % 16 in (0, 1, 5) else dom // 16}"
-        roof = {"kernel": name, "bound": "mfma", "achieved": round(achieved / 1e12, 1),
-                "peak": MFMA_BF16_PEAK / 1e12, "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK, 4),
+        roof = {"kernel": name, "bound": "mfma" if mfma else "hbm",
+                "achieved": round(achieved / (1e12 if mfma else 1e9), 1), "peak": peak / (1e12 if mfma else 1e9),
+                "unit": "TFLOP/s" if mfma else "GB/s", "frac": round(achieved / peak, 4),
                 "traffic": measured_traffic(name, wl.name, "dar_codec.hip"), "flops_per_launch": f,
                 "bytes_per_launch": b, "avg_launch_us": round(avg * 1000, 2), "launches_timed": len(times),
-                "hbm_gb_s": round(b / (avg / 1000.0) / 1e9, 1), "launches_per_step": len(recs) // max(1, args.profile_frames),
-                "step_time_share": share}
+                "tflop_s": round(f / (avg / 1000.0) / 1e12, 1), "hbm_gb_s": round(b / (avg / 1000.0) / 1e9, 1),
+                "mfma_frac": round(f / (avg / 1000.0) / MFMA_BF16_PEAK, 4),
+                "launches_per_step": len(recs) // max(1, args.profile_frames), "step_time_share": share}
         rp = rocprof_launch_us(name, wl.name, "dar_codec.hip")
         roof["rocprof_avg_launch_us"] = rp
-        roof["rocprof_frac"] = round(f / (rp * 1e-6) / MFMA_BF16_PEAK, 4) if rp else None
-        log(f"dominant kind {name}: {avg * 1000:.1f} us/launch, {achieved / 1e12:.0f} TFLOP/s; shares {share}")
+        roof["rocprof_frac"] = round((f if mfma else b) / (rp * 1e-6) / peak, 4) if rp else None
+        log(f"dominant kind {name}: {avg * 1000:.1f} us/launch, {f / (avg / 1000.0) / 1e12:.0f} TFLOP/s, "
+            f"{b / (avg / 1000.0) / 1e9:.0f} GB/s; shares {share}")
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline_codec(wl, host, codes)
