@@ -224,7 +224,10 @@ def main():
         "hbm_frac": round(gbs / HBM_PEAK, 4), "achieved_gib_s": round(gbs / bm.GIB, 1),
         "pages_formula": pages_formula(dims, wl, fps), "windows": windows,
         "alg_bytes_per_frame_avg": int(alg_bytes // args.steps),
-        "prefill_ms": round(prefill_ms, 2),
+        # dar_prefill runs the prompt blocks, the codebook-0 head and frame 0
+        # (its codes are the call's output), so the blocks alone take about
+        # one frame less
+        "prefill_ms": round(prefill_ms, 2), "prefill_blocks_ms_est": round(prefill_ms - ms / args.steps, 2),
         "nonfinite_logits": n_bad,
         "codes_checksum": int(np.asarray(codes, dtype=np.int64).sum()),
         "roofline": roof,
@@ -339,6 +342,7 @@ def bench_batched(args, wl):
                    "sampling": SAMPLING if args.sample else None},
         "achieved_gb_s": round(gbs / 1e9, 1), "hbm_frac": round(gbs / HBM_PEAK, 4),
         "alg_bytes_per_step_avg": int(alg_bytes // steps), "prefill_ms": round(prefill_ms, 2),
+        "prefill_blocks_ms_est": round(prefill_ms - ms / steps, 2),
         "nonfinite_logits": n_bad, "roofline": roof, "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
