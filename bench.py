@@ -228,6 +228,7 @@ def main():
         # (its codes are the call's output), so the blocks alone take about
         # one frame less
         "prefill_ms": round(prefill_ms, 2), "prefill_blocks_ms_est": round(prefill_ms - ms / args.steps, 2),
+        "prefill_tok_s_est": round(wl.prefill_len * 1000.0 / max(prefill_ms - ms / args.steps, 1e-6), 1),
         "nonfinite_logits": n_bad,
         "codes_checksum": int(np.asarray(codes, dtype=np.int64).sum()),
         "roofline": roof,

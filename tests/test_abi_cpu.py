@@ -236,3 +236,28 @@ def test_codec_create_rejects_before_hip(N):
     assert N.lib.dar_codec_create(ctypes.byref(c), ctypes.byref(w), ctypes.c_void_p(1 << 20), need - 1, None,
                                   ctypes.byref(ctx)) == N.DAR_E_WORKSPACE
     assert N.lib.dar_codec_decode(None, None, 1, None) == N.DAR_E_INVAL
+
+
+def test_codec_ops_reject_bad_arguments_before_hip(N):
+    fake = ctypes.c_void_p(1 << 20)  # never dereferenced: every call below fails its host checks
+    # one residual unit: the one-launch kernel needs a width a tile spans and y != x
+    args = dict(T=100, C=96, taps=7, dilation=3, fused=1)
+
+    def unit(**kw):
+        a = dict(args, **kw)
+        return N.lib.dar_codec_op_resunit(fake, a["T"], a["C"], fake, fake, fake, a["taps"], a["dilation"], fake,
+                                          fake, fake, a["fused"], ctypes.c_void_p(2 << 20), None)
+
+    assert unit(C=192) == N.DAR_E_INVAL            # no one-launch tile at 192 channels
+    assert b"one-launch" in N.lib.dar_codec_last_error(None)
+    assert unit(C=100, fused=0) == N.DAR_E_INVAL   # not a multiple of 32
+    assert unit(taps=4) == N.DAR_E_INVAL           # even kernel
+    assert unit(dilation=11) == N.DAR_E_INVAL      # 3 * 11 > 32 rows of reach
+    assert unit(T=0) == N.DAR_E_INVAL
+    assert N.lib.dar_codec_op_resunit(fake, 100, 96, fake, fake, fake, 7, 1, fake, fake, fake, 1, fake,
+                                      None) == N.DAR_E_INVAL  # in place
+    # one convolution: widths, taps and strides
+    assert N.lib.dar_codec_op_conv(fake, 0, fake, 10, 48, 64, fake, fake, 7, 1, 0, None, 0, fake, None) == N.DAR_E_INVAL
+    assert N.lib.dar_codec_op_conv(fake, 0, fake, 10, 64, 64, fake, fake, 7, 1, 3, None, 0, fake, None) == N.DAR_E_INVAL
+    assert N.lib.dar_codec_op_conv(fake, 1, fake, 10, 64, 64, fake, fake, 7, 1, 0, None, 0, fake, None) == N.DAR_E_INVAL
+    assert N.lib.dar_codec_op_conv(fake, 0, None, 10, 64, 1, fake, fake, 7, 1, 0, None, 1, fake, None) == N.DAR_E_INVAL
