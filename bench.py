@@ -199,6 +199,8 @@ def main():
             + (f"{live_ms / live_n * 1000:.1f} us beside the other chain" if live_n else "no live timing (graph replay)")
             + f"; serialised-frame shares {share}")
 
+    ref_read = reference_read(gbs)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(dims, wl, host, prompt)
@@ -227,6 +229,7 @@ def main():
         # dar_prefill runs the prompt blocks, the codebook-0 head and frame 0
         # (its codes are the call's output), so the blocks alone take about
         # one frame less
+        "reference_read": ref_read,
         "prefill_ms": round(prefill_ms, 2), "prefill_blocks_ms_est": round(prefill_ms - ms / args.steps, 2),
         "prefill_tok_s_est": round(wl.prefill_len * 1000.0 / max(prefill_ms - ms / args.steps, 1e-6), 1),
         "nonfinite_logits": n_bad,
@@ -656,6 +659,30 @@ def pages_formula(dims, wl, fps):
     per_elem = {"bf16": 2.0, "fp8": 1.0, "int8": 1.0, "int4": 0.5}[wl.wtype]
     step = elems * per_elem
     return {"bytes_per_step": int(step), "gib_s": round(fps * step / bm.GIB, 1)}
+
+
+def reference_read(frame_bytes_per_s):
+    """The box's own plain-read rate (dar_op_stream_read over 1 GiB, five reads,
+    16-byte non-temporal loads as the GEMVs use) and the frame's algorithmic
+    byte rate as a fraction of it: context for hbm_frac, which is against the
+    8 TB/s datasheet figure."""
+    import ctypes
+
+    import torch
+
+    from dar_decode_frame_amd import native as N
+    buf = torch.ones(2 ** 30, dtype=torch.uint8, device="cuda:0")
+    sink = torch.zeros(2048, dtype=torch.int32, device="cuda:0")
+    torch.cuda.synchronize()
+    N.dar_op_stream_read(ctypes.c_void_p(buf.data_ptr()), buf.numel(), 1, ctypes.c_void_p(sink.data_ptr()), None)
+    ms = N.dar_op_stream_read(ctypes.c_void_p(buf.data_ptr()), buf.numel(), 5, ctypes.c_void_p(sink.data_ptr()),
+                              None)
+    rate = buf.numel() / (ms * 1e-3)
+    del buf, sink
+    torch.cuda.empty_cache()
+    log(f"reference read: {rate / 1e9:.0f} GB/s; the frame moves {frame_bytes_per_s / rate:.3f} of that")
+    return {"kernel": "dar_op_stream_read", "bytes": 2 ** 30, "gb_s": round(rate / 1e9, 1),
+            "frame_frac": round(frame_bytes_per_s / rate, 4)}
 
 
 def measured_traffic(kind, workload, source="dar_kernels.hip"):

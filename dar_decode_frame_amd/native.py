@@ -174,6 +174,7 @@ _SIGS = {
     "dar_op_gemv": ([_I32, _VP, _VP, _I32, _I32, _VP, _I32, _VP, _VP], ctypes.c_int),
     "dar_op_gemm": ([_I32, _VP, _VP, _I32, _I32, _VP, _I32, _VP, _VP], ctypes.c_int),
     "dar_op_gemm_noalloc": ([_I32, _VP, _VP, _I32, _I32, _VP, _I32, _VP, _VP], ctypes.c_int),
+    "dar_op_stream_read": ([_VP, ctypes.c_size_t, _I32, _VP, ctypes.POINTER(ctypes.c_float), _VP], ctypes.c_int),
     "dar_op_attention": ([_VP, _VP, _VP, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _VP, _VP], ctypes.c_int),
     "dar_op_fp8_decode": ([_VP, _I32, _VP, _VP], ctypes.c_int),
     "dar_set_sampling": ([_VP, ctypes.POINTER(dar_sampling)], ctypes.c_int),
@@ -372,6 +373,14 @@ def dar_op_gemm(wtype, w_ptr, scale_ptr, N, K, x_ptr, M, y_ptr, stream_ptr):
 def dar_op_gemm_noalloc(wtype, w_ptr, scale_ptr, N, K, x_ptr, M, y_ptr, stream_ptr):
     return _check(lib.dar_op_gemm_noalloc(wtype, w_ptr, scale_ptr, N, K, x_ptr, M, y_ptr, stream_ptr),
                   "dar_op_gemm_noalloc")
+
+
+def dar_op_stream_read(src_ptr, nbytes, iters, sink_ptr, stream_ptr):
+    """Mean milliseconds per plain read of nbytes at src (see dar.h)."""
+    ms = ctypes.c_float(0.0)
+    _check(lib.dar_op_stream_read(src_ptr, nbytes, iters, sink_ptr, ctypes.byref(ms), stream_ptr),
+           "dar_op_stream_read")
+    return ms.value
 
 
 def dar_op_fp8_decode(codes_ptr, n, out_ptr, stream_ptr):

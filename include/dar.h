@@ -355,6 +355,16 @@ int dar_op_attention(const float* q, const void* K, const void* V, int32_t n_hea
                      int32_t n_heads_kv, int32_t head_dim, int32_t max_len, int32_t pos,
                      int32_t M, int32_t chunk, float* out, void* stream);
 
+/* Reference read rate of the GPU: reads `bytes` of device memory at src
+ * (16-byte aligned, bytes a multiple of 16) `iters` times back to back with
+ * 16-byte non-temporal loads over a grid-stride loop of 2048 workgroups, the
+ * way the frame's GEMVs stream their weights but with no arithmetic, and
+ * returns the mean milliseconds per read in *ms_out (HIP events around the
+ * launches; synchronises the stream). sink: device, at least 8 KiB, written
+ * only with a value no read produces in practice (it keeps the loads). A
+ * measurement aid: the frame's weight rate means most next to it. */
+int dar_op_stream_read(const void* src, size_t bytes, int32_t iters, uint32_t* sink, float* ms_out, void* stream);
+
 /* Decode e4m3fn codes with the same conversion the fp8 GEMV uses:
  * out[i] = value of codes[i] (fp32). codes device uint8 [n], out device fp32 [n]. */
 int dar_op_fp8_decode(const void* codes, int32_t n, float* out, void* stream);

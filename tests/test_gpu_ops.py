@@ -56,6 +56,24 @@ def _bf16_matrix(rows, cols, seed, scale=0.02):
     return synth.f32_to_bf16_bits((rng.standard_normal((rows, cols)) * scale).astype(np.float32))
 
 
+def test_stream_read_reference(env):
+    """dar_op_stream_read: a plain read of 64 MiB reports a rate a read can
+    have (between 0.2 and 10 TB/s on this part), leaves the sink alone (its
+    marker value needs a read that sums to it), and rejects bad arguments."""
+    torch, N, dev = env
+    buf = torch.zeros(64 << 20, dtype=torch.uint8, device=dev)
+    sink = torch.full((2048,), 7, dtype=torch.int32, device=dev)
+    torch.cuda.synchronize()
+    N.dar_op_stream_read(_p(buf), buf.numel(), 1, _p(sink), _sp(torch))  # the first launch loads the kernel
+    ms = N.dar_op_stream_read(_p(buf), buf.numel(), 3, _p(sink), _sp(torch))
+    rate = buf.numel() / (ms * 1e-3)
+    assert 0.2e12 < rate < 10e12, rate
+    assert bool((sink == 7).all())
+    out = ctypes.c_float(0)
+    assert N.lib.dar_op_stream_read(_p(buf), 100, 1, _p(sink), ctypes.byref(out), None) == N.DAR_E_INVAL
+    assert N.lib.dar_op_stream_read(_p(buf), 1024, 0, _p(sink), ctypes.byref(out), None) == N.DAR_E_INVAL
+
+
 def test_fp8_decode_all_codes(env):
     torch, N, dev = env
     codes = torch.arange(256, dtype=torch.int32).to(torch.uint8).to(dev)
