@@ -271,25 +271,30 @@ int check_layer(const dar_layer_weights& w, bool scaled, std::string& why, const
 }
 
 typedef uint32_t ru32x4 __attribute__((ext_vector_type(4)));
-constexpr int kReadGrid = 2048;
+// Launch shape of the reference read: of the forms timed on this part (1024 to
+// 8192 workgroups, four or eight 16-byte loads in flight per thread, ordinary,
+// non-temporal or buffer loads), 8192 workgroups with eight non-temporal loads
+// in flight per thread read fastest.
+constexpr int kReadGrid = 8192;
+constexpr int kReadUnroll = 8;
 
-// n 16-byte units from p, four loads in flight per thread and iteration
+// n 16-byte units from p
 __global__ __launch_bounds__(kBlock) void k_stream_read(const ru32x4* __restrict__ p, size_t n, uint32_t* sink) {
   const size_t stride = (size_t)gridDim.x * kBlock;
   size_t i = blockIdx.x * (size_t)kBlock + threadIdx.x;
   uint32_t acc = 0;
-  for (; i + 3 * stride < n; i += 4 * stride) {
-    const ru32x4 a = __builtin_nontemporal_load(p + i);
-    const ru32x4 b = __builtin_nontemporal_load(p + i + stride);
-    const ru32x4 c = __builtin_nontemporal_load(p + i + 2 * stride);
-    const ru32x4 d = __builtin_nontemporal_load(p + i + 3 * stride);
-    acc ^= (a.x ^ b.y ^ c.z ^ d.w) + (a.w ^ b.x ^ c.y ^ d.z);
+  for (; i + (kReadUnroll - 1) * stride < n; i += kReadUnroll * stride) {
+    ru32x4 v[kReadUnroll];
+#pragma unroll
+    for (int u = 0; u < kReadUnroll; ++u) v[u] = __builtin_nontemporal_load(p + i + u * stride);
+#pragma unroll
+    for (int u = 0; u < kReadUnroll; ++u) acc ^= v[u].x + v[u].y * 3u + v[u].z * 5u + v[u].w * 7u;
   }
   for (; i < n; i += stride) {
     const ru32x4 a = __builtin_nontemporal_load(p + i);
     acc ^= a.x ^ a.y ^ a.z ^ a.w;
   }
-  if (acc == 0x9e3779b9u) sink[blockIdx.x] = acc;
+  if (acc == 0x9e3779b9u) sink[blockIdx.x & 2047] = acc;
 }
 
 

@@ -357,8 +357,9 @@ int dar_op_attention(const float* q, const void* K, const void* V, int32_t n_hea
 
 /* Reference read rate of the GPU: reads `bytes` of device memory at src
  * (16-byte aligned, bytes a multiple of 16) `iters` times back to back with
- * 16-byte non-temporal loads over a grid-stride loop of 2048 workgroups, the
- * way the frame's GEMVs stream their weights but with no arithmetic, and
+ * 16-byte non-temporal loads (as the frame's GEMVs stream their weights, but
+ * with no arithmetic) over a grid-stride loop of 8192 workgroups, eight loads
+ * in flight per thread (the fastest plain read among the forms tried), and
  * returns the mean milliseconds per read in *ms_out (HIP events around the
  * launches; synchronises the stream). sink: device, at least 8 KiB, written
  * only with a value no read produces in practice (it keeps the loads). A
