@@ -491,34 +491,38 @@ MFMA_BF16_PEAK = 2.5e15
 
 
 def codec_launch_cost(d, frames, tag):
-    """(FLOPs, bytes) one launch of a codec kind moves: the convolution's
-    multiply-adds (2 per weight per output row per tap) and the activations it
-    must read and write (fp32 residual stream, bf16 residual-unit hidden rows,
-    bf16 latent frames; weights counted once). A one-launch residual unit
-    reads its fp32 input rows and writes its output rows once, its hidden rows
-    staying on chip."""
+    """(FLOPs, bytes) one launch of a codec kind moves, averaged over the
+    launches of the kind: the convolution's multiply-adds (2 per weight per
+    output row per tap) and the activations it must read and write (fp32
+    residual stream, bf16 latent frames and residual-unit hidden rows, and the
+    bf16 operand that the input convolution and each block's last residual
+    unit hand to the next convolution; weights counted once). A one-launch
+    residual unit reads its fp32 input rows and writes its output rows once,
+    its hidden rows staying on chip."""
     kind, blk = tag % 16, tag // 16
     w = d.widths
+    U = d.n_units
+    out_b = (4 * (U - 1) + 2) / U  # bytes per output element of a block's units: fp32, the last bf16
     if kind == 0:
         return 0, frames * d.n_codebooks * d.latent_dim * 2 + frames * d.latent_dim * 2
     if kind == 1:
         return (2 * frames * w[0] * d.latent_dim * d.kernel,
-                frames * d.latent_dim * 2 + frames * w[0] * 4 + w[0] * d.latent_dim * d.kernel * 2)
+                frames * d.latent_dim * 2 + frames * w[0] * 2 + w[0] * d.latent_dim * d.kernel * 2)
     rows_in = frames
     for s in d.rates[:blk]:
         rows_in *= s
     cin, cout, s = w[blk], w[blk + 1], d.rates[blk]
     rows = rows_in * s
     if kind == 2:
-        return 2 * rows * cout * cin * 2, rows_in * cin * 4 + rows * cout * 4 + cin * cout * 2 * s * 2
+        return 2 * rows * cout * cin * 2, rows_in * cin * 2 + rows * cout * 4 + cin * cout * 2 * s * 2
     if kind == 3:
         return 2 * rows * cout * cout * d.kernel, rows * cout * 4 + rows * cout * 2 + cout * cout * d.kernel * 2
     if kind == 4:
-        return 2 * rows * cout * cout, rows * cout * 2 + 2 * rows * cout * 4 + cout * cout * 2
+        return 2 * rows * cout * cout, int(rows * cout * (2 + 4 + out_b)) + cout * cout * 2
     if kind == 6:
-        return 2 * rows * cout * cout * (d.kernel + 1), 2 * rows * cout * 4 + cout * cout * (d.kernel + 1) * 2
+        return 2 * rows * cout * cout * (d.kernel + 1), int(rows * cout * (4 + out_b)) + cout * cout * (d.kernel + 1) * 2
     rows_out = frames * d.hop
-    return 2 * rows_out * w[-1] * d.kernel, rows_out * w[-1] * 4 + rows_out * 4
+    return 2 * rows_out * w[-1] * d.kernel, rows_out * w[-1] * 2 + rows_out * 4
 
 
 def bench_codec(args, wl):

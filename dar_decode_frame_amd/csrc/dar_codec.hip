@@ -79,6 +79,8 @@ struct ConvArgs {
   int tanh_out;
   uint16_t* yb;             // bf16 output: Snake(acc + bias, alpha_out), rounded
   const uint16_t* alpha_out;
+  uint16_t* ys;             // beside the fp32 output (bf16 input only): bf16(Snake(y, alpha_s)), the
+  const uint16_t* alpha_s;  // next residual unit's operand
 };
 
 // LDS row r of 32 bf16 (64 B, four 16-byte units): unit u sits at slot
@@ -236,11 +238,19 @@ __global__ __launch_bounds__(kThreads) void k_conv(ConvArgs a) {
         const size_t at = ((size_t)t * a.nphase + z) * a.Cout + n;
         float val = acc[nt][v] + b;
         if constexpr (YB16) {
+          if constexpr (XB16) {  // a block's last 1-tap conv: residual, then the next layer's Snake
+            if (a.res) val += a.res[at];
+          }
           a.yb[at] = (uint16_t)f2bf(snake(val, ao));
         } else {
           if (a.res) val += a.res[at];
-          if (a.tanh_out) val = tanhf(val);
-          a.yf[at] = val;
+          if constexpr (XB16) {  // (tanh is the fp32-input path's only: it keeps this epilogue's code small)
+            a.yf[at] = val;
+            if (a.ys) a.ys[at] = (uint16_t)f2bf(snake(val, bf2f(a.alpha_s[n])));
+          } else {
+            if (a.tanh_out) val = tanhf(val);
+            a.yf[at] = val;
+          }
         }
       }
     }
@@ -254,8 +264,9 @@ __global__ __launch_bounds__(kThreads) void k_conv(ConvArgs a) {
 // (after Snake, rounded to bf16) so that consecutive lanes read consecutive
 // samples, and each thread adds the block's taps to its sample's sum.
 constexpr int kOutCB = 32;  // channels per staged block
-__global__ __launch_bounds__(kThreads) void k_conv_out(const float* x, const uint16_t* alpha, int T, int C,
-                                                     const uint16_t* w, const uint16_t* b, int K, float* y) {
+__global__ __launch_bounds__(kThreads) void k_conv_out(const float* x, const uint16_t* xb16, const uint16_t* alpha,
+                                                     int T, int C, const uint16_t* w, const uint16_t* b, int K,
+                                                     float* y) {
   extern __shared__ __align__(16) char smem[];
   const int halfk = (K - 1) / 2, W = kOutRows + K - 1;
   uint16_t* xs = reinterpret_cast<uint16_t*>(smem);  // [kOutCB][W]
@@ -274,6 +285,11 @@ __global__ __launch_bounds__(kThreads) void k_conv_out(const float* x, const uin
       const int r = i / Q, c4 = i % Q;
       const int row = t0 - halfk + r;
       const bool in = i < W * Q && row >= 0 && row < T;
+      if (xb16) {  // the operand already Snake'd and rounded: four bf16 in the first two lanes' words
+        const uint2 h = in ? *reinterpret_cast<const uint2*>(xb16 + (size_t)row * C + cb + 4 * c4) : uint2{0u, 0u};
+        v[k] = f32x4{__uint_as_float(h.x), __uint_as_float(h.y), 0.f, 0.f};
+        continue;
+      }
       v[k] = in ? *reinterpret_cast<const f32x4*>(x + (size_t)row * C + cb + 4 * c4) : f32x4{0.f, 0.f, 0.f, 0.f};
       if (i < W * Q) {
         const uint2 a2 = *reinterpret_cast<const uint2*>(alpha + cb + 4 * c4);
@@ -289,6 +305,12 @@ __global__ __launch_bounds__(kThreads) void k_conv_out(const float* x, const uin
       const int r = i / Q, c4 = i % Q;
       const int row = t0 - halfk + r;
       const bool in = row >= 0 && row < T;
+      if (xb16) {
+        const uint32_t h[2] = {__float_as_uint(v[k].x), __float_as_uint(v[k].y)};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) xs[(4 * c4 + e) * W + r] = in ? (uint16_t)(h[e >> 1] >> (16 * (e & 1))) : (uint16_t)0;
+        continue;
+      }
       const float f[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -431,10 +453,19 @@ struct ResArgs {
   const uint16_t* W2;       // [C][C] bf16 (the 1-tap convolution)
   const uint16_t* b2;
   float* y;                 // [T][C] = x + conv_1(h) + b2
+  uint16_t* ys;             // with y (optional): bf16(Snake(y, alpha_s)), the next unit's operand
+  const uint16_t* alpha_s;
+  uint16_t* yb;             // or, in y's place, bf16(Snake(y, alpha_out)): the next layer's operand
+  const uint16_t* alpha_out;
   int h_at;                 // LDS byte offset of h (past the 7-tap convolution's staging)
 };
 
-template <int WM, int WN, int NT>
+// XB16: the 7-tap convolution stages c1.xb (its operand, bf16(Snake(x,
+// alpha1)), written by the layer before) instead of Snake'ing c1.xf itself;
+// the residual add reads c1.xf either way. OUT: 0 writes y, 1 y and ys, 2 yb
+// (one output form per instantiation keeps the epilogue's Snake code small
+// enough to stay inline).
+template <int WM, int WN, int NT, bool XB16, int OUT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void k_resunit(ResArgs r) {
   constexpr int BM = 32 * WM, C = 32 * NT * WN;
   constexpr int CH = C / 32;                       // 32-channel chunks of h
@@ -447,7 +478,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   const int half = lane >> 5, l32 = lane & 31;
   // h: chunk c's rows at hs + c BM 64, laid out as a staged window (lds_at)
   char* hs = smem + r.h_at;
-  conv_accumulate<WM, WN, NT, false>(a, 0, t0, 0, smem, [&](f32x16 (&acc)[NT]) {
+  conv_accumulate<WM, WN, NT, XB16>(a, 0, t0, 0, smem, [&](f32x16 (&acc)[NT]) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       const int n = (wn * NT + nt) * 32 + l32;  // chunk wn NT + nt, channel l32 of it
@@ -506,7 +537,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       const int t = t0 + wm * 32 + (v & 3) + 4 * half + 8 * (v >> 2);
       if (t >= a.T) continue;
       const size_t at = (size_t)t * C + n;
-      r.y[at] = (acc[nt][v] + b) + a.xf[at];  // the two-launch path's order of the sums
+      const float val = (acc[nt][v] + b) + a.xf[at];  // the two-launch path's order of the sums
+      if constexpr (OUT == 2) {
+        r.yb[at] = (uint16_t)f2bf(snake(val, bf2f(r.alpha_out[n])));
+      } else {
+        r.y[at] = val;
+        if constexpr (OUT == 1) r.ys[at] = (uint16_t)f2bf(snake(val, bf2f(r.alpha_s[n])));
+      }
     }
   }
 }
@@ -554,7 +591,7 @@ hipError_t launch_conv(const ConvArgs& a, hipStream_t s, hipEvent_t e0 = nullptr
   if (xb && !yb) return go_conv_cfg<true, false>(ci, a, grid, lds, s, e0, e1);
   if (!xb && yb) return go_conv_cfg<false, true>(ci, a, grid, lds, s, e0, e1);
   if (!xb && !yb) return go_conv_cfg<false, false>(ci, a, grid, lds, s, e0, e1);
-  return hipErrorInvalidValue;  // bf16 in and bf16 out: not a layer of the decoder
+  return go_conv_cfg<true, true>(ci, a, grid, lds, s, e0, e1);  // a block's last 1-tap conv to the next operand
 }
 
 // Tile of the one-launch residual unit at width C: the workgroup spans all C
@@ -569,53 +606,72 @@ int resunit_cfg(int C) {
   }
 }
 
-template <int WM, int WN, int NT>
+template <int WM, int WN, int NT, bool XB16, int OUT>
 hipError_t go_resunit(const ResArgs& r, dim3 grid, size_t lds, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   static std::atomic<bool> big{false};
-  hipError_t e = allow_lds(k_resunit<WM, WN, NT>, lds, big);
+  hipError_t e = allow_lds(k_resunit<WM, WN, NT, XB16, OUT>, lds, big);
   if (e != hipSuccess) return e;
   if (e0 || e1)
-    hipExtLaunchKernelGGL((k_resunit<WM, WN, NT>), grid, dim3(kThreads), lds, s, e0, e1, 0, r);
+    hipExtLaunchKernelGGL((k_resunit<WM, WN, NT, XB16, OUT>), grid, dim3(kThreads), lds, s, e0, e1, 0, r);
   else
-    hipLaunchKernelGGL((k_resunit<WM, WN, NT>), grid, dim3(kThreads), lds, s, r);
+    hipLaunchKernelGGL((k_resunit<WM, WN, NT, XB16, OUT>), grid, dim3(kThreads), lds, s, r);
   return hipGetLastError();
 }
 
+template <bool XB16, int OUT>
+hipError_t go_resunit_cfg(int ci, const ResArgs& r, dim3 grid, size_t lds, hipStream_t s, hipEvent_t e0,
+                          hipEvent_t e1) {
+  switch (ci) {
+    case 0: return go_resunit<4, 1, 3, XB16, OUT>(r, grid, lds, s, e0, e1);
+    case 1: return go_resunit<2, 2, 2, XB16, OUT>(r, grid, lds, s, e0, e1);
+    case 2: return go_resunit<2, 2, 1, XB16, OUT>(r, grid, lds, s, e0, e1);
+    default: return go_resunit<4, 1, 1, XB16, OUT>(r, grid, lds, s, e0, e1);
+  }
+}
+
 // One residual unit in one launch (r.c1 describes the 7-tap convolution:
-// fp32 input with alpha1, C in and out, one phase; y != x).
+// fp32 input xf, which the residual add reads, staged either from its
+// operand xb or from xf with Snake(alpha1); C in and out, one phase; the
+// output y (fp32, optionally with ys) or yb in a buffer other than xf).
 hipError_t launch_resunit(ResArgs r, hipStream_t s, hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr) {
   const ConvArgs& a = r.c1;
   const int ci = resunit_cfg(a.Cout);
-  if (ci < 0 || a.Cin != a.Cout || a.nphase != 1 || a.xb || !a.xf || r.y == a.xf) return hipErrorInvalidValue;
+  if (ci < 0 || a.Cin != a.Cout || a.nphase != 1 || !a.xf || (!a.xb && !a.alpha_in) || !r.y == !r.yb ||
+      (r.yb && !r.alpha_out) || (r.ys && (!r.y || !r.alpha_s)) ||
+      static_cast<const void*>(r.y ? static_cast<const void*>(r.y) : r.yb) == a.xf)
+    return hipErrorInvalidValue;
   const TileCfg& c = kCfgs[ci];
   const int span = a.off[a.ntap - 1] - a.off[0];
   const size_t conv = conv_lds(c, span, a.ntap);
   r.h_at = (int)conv;
   const size_t lds = conv + (size_t)c.bm() * a.Cout * 2;
   const dim3 grid((a.T + c.bm() - 1) / c.bm());
-  switch (ci) {
-    case 0: return go_resunit<4, 1, 3>(r, grid, lds, s, e0, e1);
-    case 1: return go_resunit<2, 2, 2>(r, grid, lds, s, e0, e1);
-    case 2: return go_resunit<2, 2, 1>(r, grid, lds, s, e0, e1);
-    default: return go_resunit<4, 1, 1>(r, grid, lds, s, e0, e1);
-  }
+  // the decode's forms (operand staged, output with its operand or as the
+  // next layer's operand) and the diagnostic's (fp32 staged, fp32 out)
+  if (a.xb && r.ys) return go_resunit_cfg<true, 1>(ci, r, grid, lds, s, e0, e1);
+  if (a.xb && r.yb) return go_resunit_cfg<true, 2>(ci, r, grid, lds, s, e0, e1);
+  if (!a.xb && !r.ys && !r.yb) return go_resunit_cfg<false, 0>(ci, r, grid, lds, s, e0, e1);
+  return hipErrorInvalidValue;
 }
 
 size_t out_lds(int C, int K) {
   return (((size_t)kOutCB * (kOutRows + K - 1) * 2 + 15) & ~(size_t)15) + (size_t)C * K * 4;
 }
 
-hipError_t launch_conv_out(const float* x, const uint16_t* alpha, int T, int C, const uint16_t* w, const uint16_t* b,
-                           int K, float* y, hipStream_t s, hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr) {
+// x: fp32 rows with Snake(alpha) applied on load, or xb16: bf16 rows already
+// Snake'd and rounded (alpha unused)
+hipError_t launch_conv_out(const float* x, const uint16_t* xb16, const uint16_t* alpha, int T, int C,
+                           const uint16_t* w, const uint16_t* b, int K, float* y, hipStream_t s,
+                           hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr) {
   static std::atomic<bool> big{false};
   const size_t lds = out_lds(C, K);
   hipError_t e = allow_lds(k_conv_out, lds, big);
   if (e != hipSuccess) return e;
   const dim3 grid((T + kOutRows - 1) / kOutRows);
   if (e0 || e1)
-    hipExtLaunchKernelGGL(k_conv_out, grid, dim3(kThreads), lds, s, e0, e1, 0, x, alpha, T, C, w, b, K, y);
+    hipExtLaunchKernelGGL(k_conv_out, grid, dim3(kThreads), lds, s, e0, e1, 0, x, xb16, alpha, T, C, w, b, K, y);
   else
-    hipLaunchKernelGGL(k_conv_out, grid, dim3(kThreads), lds, s, x, alpha, T, C, w, b, K, y);
+    hipLaunchKernelGGL(k_conv_out, grid, dim3(kThreads), lds, s, x, xb16, alpha, T, C, w, b, K, y);
   return hipGetLastError();
 }
 
@@ -665,7 +721,7 @@ struct CodecLayout {
   size_t in_w;
   size_t up_w[DAR_CODEC_MAX_BLOCKS];
   size_t w1[DAR_CODEC_MAX_BLOCKS][DAR_CODEC_MAX_UNITS], w2[DAR_CODEC_MAX_BLOCKS][DAR_CODEC_MAX_UNITS];
-  size_t z, xa, xb, h, anom, total;
+  size_t z, xa, xb, h, sa, sb, anom, total;
   size_t act_elems;  // largest rows x channels of any activation
 };
 
@@ -697,6 +753,8 @@ CodecLayout codec_layout(const dar_codec_config* c) {
   L.xa = take(4 * L.act_elems);
   L.xb = take(4 * L.act_elems);
   L.h = take(2 * L.act_elems);
+  L.sa = take(2 * L.act_elems);  // residual units' operands, bf16(Snake(x, alpha1)), alternating
+  L.sb = take(2 * L.act_elems);
   L.anom = take(sizeof(int) * 4);
   L.total = off;
   return L;
@@ -796,6 +854,7 @@ int run_decode(dar_codec* c, const int32_t* codes, int frames, float* audio, boo
   uint16_t* z = reinterpret_cast<uint16_t*>(c->ws + L.z);
   float* bufs[2] = {reinterpret_cast<float*>(c->ws + L.xa), reinterpret_cast<float*>(c->ws + L.xb)};
   uint16_t* h = reinterpret_cast<uint16_t*>(c->ws + L.h);
+  uint16_t* ops[2] = {reinterpret_cast<uint16_t*>(c->ws + L.sa), reinterpret_cast<uint16_t*>(c->ws + L.sb)};
   int* anom = reinterpret_cast<int*>(c->ws + L.anom);
 
   RvqArgs ra{};
@@ -838,16 +897,27 @@ int run_decode(dar_codec* c, const int32_t* codes, int frames, float* audio, boo
     a.ntap = K;
     conv_taps(K, 1, a.off);
     a.bias = c->in_b;
-    a.yf = bufs[0];
+    // the first transposed convolution's operand, bf16(Snake(x, its alpha)), as below
+    a.yb = reinterpret_cast<uint16_t*>(bufs[0]);
+    a.alpha_out = U16(c->blocks[0].alpha);
     if ((st = conv(a, 1)) != DAR_OK) return st;
   }
-  int cur = 0, rows = frames;
+  // Every convolution's operand is bf16(Snake(x, its alpha)) of the fp32
+  // rows before it. The layer that makes those rows writes that operand too
+  // (the same values the convolution would compute when staging the rows,
+  // once per element instead of once per workgroup that stages it): the
+  // input convolution and each block's last residual unit write only the
+  // operand (nothing else reads their rows), the transposed convolutions and
+  // the other residual units write it beside their fp32 rows, which the next
+  // residual add reads.
+  const uint16_t* xb_next = reinterpret_cast<const uint16_t*>(bufs[0]);
+  int cur = 0, rows = frames, so = 0;
   for (int i = 0; i < g.n_blocks; ++i) {
     const dar_codec_block& B = c->blocks[i];
     const int cin = width(&g, i), cout = width(&g, i + 1), sr = g.rates[i];
+    const uint16_t* alpha_next = U16(i + 1 < g.n_blocks ? c->blocks[i + 1].alpha : c->out_alpha);
     ConvArgs a{};
-    a.xf = bufs[cur];
-    a.alpha_in = U16(B.alpha);
+    a.xb = xb_next;
     a.T = rows;
     a.Cin = cin;
     a.Cout = cout;
@@ -858,15 +928,20 @@ int run_decode(dar_codec* c, const int32_t* codes, int frames, float* audio, boo
     convT_taps(sr, kidx, a.off);
     a.bias = U16(B.up_b);
     a.yf = bufs[cur ^ 1];
+    a.ys = ops[so];
+    a.alpha_s = U16(B.units[0].alpha1);
     if ((st = conv(a, 2 + 16 * i)) != DAR_OK) return st;
     cur ^= 1;
     rows *= sr;
     const bool fuse = resunit_cfg(cout) >= 0;
     for (int u = 0; u < g.n_units; ++u) {
       const dar_codec_unit& U = B.units[u];
+      const bool last = u + 1 == g.n_units;
+      uint16_t* hand = reinterpret_cast<uint16_t*>(bufs[cur ^ 1]);  // the last unit's operand for the next layer
+      const uint16_t* alpha_s = last ? nullptr : U16(B.units[u + 1].alpha1);
       ConvArgs a1{};
-      a1.xf = bufs[cur];
-      a1.alpha_in = U16(U.alpha1);
+      a1.xf = bufs[cur];  // the residual add's rows
+      a1.xb = ops[so];    // the 7-tap convolution's operand
       a1.T = rows;
       a1.Cin = cout;
       a1.Cout = cout;
@@ -881,14 +956,24 @@ int run_decode(dar_codec* c, const int32_t* codes, int frames, float* audio, boo
         r.alpha2 = U16(U.alpha2);
         r.W2 = reinterpret_cast<const uint16_t*>(c->ws + L.w2[i][u]);
         r.b2 = U16(U.b2);
-        r.y = bufs[cur ^ 1];
+        if (last) {
+          r.yb = hand;
+          r.alpha_out = alpha_next;
+        } else {
+          r.y = bufs[cur ^ 1];
+          r.ys = ops[so ^ 1];
+          r.alpha_s = alpha_s;
+        }
         hipEvent_t *e0 = nullptr, *e1 = nullptr;
         evs(e0, e1);
         CODEC_HIP(c, launch_resunit(r, s, e0 ? *e0 : nullptr, e1 ? *e1 : nullptr), "codec residual unit");
         tag(6 + 16 * i);
         cur ^= 1;
+        so ^= 1;
+        if (last) xb_next = hand;
         continue;
       }
+      a1.xf = nullptr;
       a1.yb = h;
       a1.alpha_out = U16(U.alpha2);
       if ((st = conv(a1, 3 + 16 * i)) != DAR_OK) return st;
@@ -902,17 +987,29 @@ int run_decode(dar_codec* c, const int32_t* codes, int frames, float* audio, boo
       a2.ntap = 1;
       a2.off[0] = 0;
       a2.bias = U16(U.b2);
-      a2.yf = bufs[cur];
       a2.res = bufs[cur];
+      if (last) {
+        a2.yb = hand;
+        a2.alpha_out = alpha_next;
+      } else {
+        a2.yf = bufs[cur];
+        a2.ys = ops[so ^ 1];
+        a2.alpha_s = alpha_s;
+      }
       if ((st = conv(a2, 4 + 16 * i)) != DAR_OK) return st;
+      so ^= 1;
+      if (last) {
+        cur ^= 1;
+        xb_next = hand;
+      }
     }
   }
   {
     hipEvent_t *e0 = nullptr, *e1 = nullptr;
     evs(e0, e1);
     CODEC_HIP(c,
-              launch_conv_out(bufs[cur], c->out_alpha, rows, width(&g, g.n_blocks), c->out_w, c->out_b, K, audio, s,
-                              e0 ? *e0 : nullptr, e1 ? *e1 : nullptr),
+              launch_conv_out(xb_next ? nullptr : bufs[cur], xb_next, c->out_alpha, rows, width(&g, g.n_blocks),
+                              c->out_w, c->out_b, K, audio, s, e0 ? *e0 : nullptr, e1 ? *e1 : nullptr),
               "codec output convolution");
     tag(5);
   }
@@ -1084,11 +1181,11 @@ int dar_codec_op_conv(const void* x, int32_t x_bf16, const void* alpha, int32_t 
     if (x_bf16 || !alpha || stride != 0 || dilation != 1 || taps < 1 || taps > kMaxTaps || taps % 2 == 0 ||
         !tanh_out || res || Cin % kOutCB || out_lds(Cin, taps) > 160 * 1024)
       return DAR_E_INVAL;
-    hipError_t e = launch_conv_out(static_cast<const float*>(x), U16(alpha), T, Cin, U16(w), U16(b), taps, y, s);
+    hipError_t e = launch_conv_out(static_cast<const float*>(x), nullptr, U16(alpha), T, Cin, U16(w), U16(b), taps, y, s);
     if (e == hipSuccess) e = hipStreamSynchronize(s);
     return e == hipSuccess ? DAR_OK : codec_hip_fail(nullptr, e, "op conv out");
   }
-  if (Cin % 32 || Cout % 32 || (x_bf16 && alpha)) return DAR_E_INVAL;
+  if (Cin % 32 || Cout % 32 || (x_bf16 && (alpha || tanh_out))) return DAR_E_INVAL;
   ConvArgs a{};
   if (x_bf16)
     a.xb = U16(x);
