@@ -60,8 +60,18 @@ __device__ __forceinline__ uint32_t f2bf(float f) {
   return u >> 16;
 }
 
+// Snake(x) = x + sin(a x)^2 / a. The sine: a x reduced by whole turns with a
+// two-part 2 pi (the high part 6.28125 is exact in 8 bits, so k times it is
+// exact for |k| < 2^16), then the hardware sine of the remaining fraction of a
+// turn. Measured on this part within 4e-7 of sin for |a x| <= 1000 (the
+// library sinf: 7e-8), several times cheaper, and far below the bf16 step
+// that every Snake output is rounded to next.
 __device__ __forceinline__ float snake(float x, float a) {
-  const float s = sinf(a * x);
+  const float t = a * x;
+  const float k = rintf(t * 0.15915494309189535f);
+  float f = fmaf(-k, 6.28125f, t);
+  f = fmaf(-k, 1.9353071795864769e-3f, f);
+  const float s = __builtin_amdgcn_sinf(f * 0.15915494309189535f);  // sin(2 pi turns)
   return x + s * s / a;
 }
 
