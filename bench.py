@@ -493,16 +493,17 @@ MFMA_BF16_PEAK = 2.5e15
 def codec_launch_cost(d, frames, tag):
     """(FLOPs, bytes) one launch of a codec kind moves, averaged over the
     launches of the kind: the convolution's multiply-adds (2 per weight per
-    output row per tap) and the activations it must read and write (fp32
-    residual stream, bf16 latent frames and residual-unit hidden rows, and the
-    bf16 operand that the input convolution and each block's last residual
-    unit hand to the next convolution; weights counted once). A one-launch
-    residual unit reads its fp32 input rows and writes its output rows once,
-    its hidden rows staying on chip."""
+    output row per tap) and the activations it must read and write; weights
+    counted once. Every convolution reads its operand, bf16(Snake(x)), which
+    the layer before wrote: the input convolution and a block's last residual
+    unit write only that, the transposed convolutions and the other units
+    write it beside their fp32 rows (the residual stream, which the next
+    residual add reads); an unfused unit also writes and reads its bf16 hidden
+    rows, a one-launch unit keeps them on chip."""
     kind, blk = tag % 16, tag // 16
     w = d.widths
-    U = d.n_units
-    out_b = (4 * (U - 1) + 2) / U  # bytes per output element of a block's units: fp32, the last bf16
+    U = len(d.dilations)  # residual units per block
+    out_b = (6 * (U - 1) + 2) / U  # bytes per output element of a block's units: fp32 + operand, the last operand
     if kind == 0:
         return 0, frames * d.n_codebooks * d.latent_dim * 2 + frames * d.latent_dim * 2
     if kind == 1:
@@ -514,13 +515,13 @@ def codec_launch_cost(d, frames, tag):
     cin, cout, s = w[blk], w[blk + 1], d.rates[blk]
     rows = rows_in * s
     if kind == 2:
-        return 2 * rows * cout * cin * 2, rows_in * cin * 2 + rows * cout * 4 + cin * cout * 2 * s * 2
+        return 2 * rows * cout * cin * 2, rows_in * cin * 2 + rows * cout * 6 + cin * cout * 2 * s * 2
     if kind == 3:
-        return 2 * rows * cout * cout * d.kernel, rows * cout * 4 + rows * cout * 2 + cout * cout * d.kernel * 2
+        return 2 * rows * cout * cout * d.kernel, rows * cout * 2 + rows * cout * 2 + cout * cout * d.kernel * 2
     if kind == 4:
         return 2 * rows * cout * cout, int(rows * cout * (2 + 4 + out_b)) + cout * cout * 2
     if kind == 6:
-        return 2 * rows * cout * cout * (d.kernel + 1), int(rows * cout * (4 + out_b)) + cout * cout * (d.kernel + 1) * 2
+        return 2 * rows * cout * cout * (d.kernel + 1), int(rows * cout * (2 + 4 + out_b)) + cout * cout * (d.kernel + 1) * 2
     rows_out = frames * d.hop
     return 2 * rows_out * w[-1] * d.kernel, rows_out * w[-1] * 2 + rows_out * 4
 
