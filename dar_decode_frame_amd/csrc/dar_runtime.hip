@@ -60,6 +60,8 @@ int frame_codes(const dar_config* c) { return 1 + c->n_res; }
 bool has_fast(const dar_config* c) { return c->n_res > 0; }
 
 // the slow chain splits its attention over 64-position chunks once the cache is longer than one chunk
+constexpr int kPrefillChunk = 128;  // positions per attention split in the prompt prefill
+
 int nsplit_slow_of(const dar_config* c) { return (c->max_len + kAttnChunkDefault - 1) / kAttnChunkDefault; }
 
 struct Layout {
@@ -1130,8 +1132,11 @@ int prefill_blocks(dar_ctx* c, const int32_t* tokens, int n, hipStream_t s, int 
       aa.n_heads_q = g.n_heads_q;
       aa.n_heads_kv = g.n_heads_kv;
       aa.head_dim = g.head_dim;
-      aa.chunk = L.chunk;
-      aa.nsplit_max = (p0 + M + L.chunk - 1) / L.chunk;  // splits of the block's longest row
+      // 128-position splits (within a page when paged): a first block of 128
+      // prompt positions is one split with no merge launch (a prompt block
+      // 6.4 -> 5.9 ms, 16 prompts of 143..510 ids 301 -> 284 ms against 64)
+      aa.chunk = c->paged ? std::min(kPrefillChunk, L.page_len) : kPrefillChunk;
+      aa.nsplit_max = (p0 + M + aa.chunk - 1) / aa.chunk;  // splits of the block's longest row
       aa.M = M;
       aa.part = reinterpret_cast<float*>(b + L.patt);
       aa.out = po;
