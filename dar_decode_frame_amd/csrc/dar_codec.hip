@@ -53,12 +53,8 @@ constexpr int kOutRows = 256;   // output samples per workgroup of the output co
 
 __device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float(((uint32_t)h) << 16); }
 
-// fp32 -> bf16, nearest even (finite values)
-__device__ __forceinline__ uint32_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
-}
+// fp32 -> bf16, nearest even (gfx950 converts in one instruction)
+__device__ __forceinline__ uint32_t f2bf(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
 
 // Snake(x) = x + sin(a x)^2 / a. The sine: a x reduced by whole turns with a
 // two-part 2 pi (the high part 6.28125 is exact in 8 bits, so k times it is
@@ -66,14 +62,17 @@ __device__ __forceinline__ uint32_t f2bf(float f) {
 // turn. Measured on this part within 4e-7 of sin for |a x| <= 1000 (the
 // library sinf: 7e-8), several times cheaper, and far below the bf16 step
 // that every Snake output is rounded to next.
-__device__ __forceinline__ float snake(float x, float a) {
+// ra = 1 / a, which the epilogues compute once per channel (a multiply per
+// value instead of a division).
+__device__ __forceinline__ float snake(float x, float a, float ra) {
   const float t = a * x;
   const float k = rintf(t * 0.15915494309189535f);
   float f = fmaf(-k, 6.28125f, t);
   f = fmaf(-k, 1.9353071795864769e-3f, f);
   const float s = __builtin_amdgcn_sinf(f * 0.15915494309189535f);  // sin(2 pi turns)
-  return x + s * s / a;
+  return x + (s * s) * ra;
 }
+__device__ __forceinline__ float snake(float x, float a) { return snake(x, a, 1.0f / a); }
 
 struct ConvArgs {
   const float* xf;          // fp32 input [T][Cin] (or null)
@@ -240,7 +239,8 @@ __global__ __launch_bounds__(kThreads) void k_conv(ConvArgs a) {
       const int n = n0 + (wn * NT + nt) * 32 + l32;
       if (n >= a.Cout) continue;
       const float b = bf2f(a.bias[n]);
-      const float ao = YB16 ? bf2f(a.alpha_out[n]) : 0.f;
+      const float ao = YB16 ? bf2f(a.alpha_out[n]) : (XB16 && a.ys ? bf2f(a.alpha_s[n]) : 1.f);
+      const float rao = 1.0f / ao;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int t = t0 + wm * 32 + (v & 3) + 4 * half + 8 * (v >> 2);
@@ -251,12 +251,12 @@ __global__ __launch_bounds__(kThreads) void k_conv(ConvArgs a) {
           if constexpr (XB16) {  // a block's last 1-tap conv: residual, then the next layer's Snake
             if (a.res) val += a.res[at];
           }
-          a.yb[at] = (uint16_t)f2bf(snake(val, ao));
+          a.yb[at] = (uint16_t)f2bf(snake(val, ao, rao));
         } else {
           if (a.res) val += a.res[at];
           if constexpr (XB16) {  // (tanh is the fp32-input path's only: it keeps this epilogue's code small)
             a.yf[at] = val;
-            if (a.ys) a.ys[at] = (uint16_t)f2bf(snake(val, bf2f(a.alpha_s[n])));
+            if (a.ys) a.ys[at] = (uint16_t)f2bf(snake(val, ao, rao));
           } else {
             if (a.tanh_out) val = tanhf(val);
             a.yf[at] = val;
@@ -492,12 +492,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       const int n = (wn * NT + nt) * 32 + l32;  // chunk wn NT + nt, channel l32 of it
-      const float b = bf2f(a.bias[n]), ao = bf2f(r.alpha2[n]);
+      const float b = bf2f(a.bias[n]), ao = bf2f(r.alpha2[n]), rao = 1.0f / ao;
       char* hc = hs + (size_t)(wn * NT + nt) * BM * 64;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int row = wm * 32 + (v & 3) + 4 * half + 8 * (v >> 2);
-        const uint16_t hv = t0 + row < a.T ? (uint16_t)f2bf(snake(acc[nt][v] + b, ao)) : (uint16_t)0;
+        const uint16_t hv = t0 + row < a.T ? (uint16_t)f2bf(snake(acc[nt][v] + b, ao, rao)) : (uint16_t)0;
         *reinterpret_cast<uint16_t*>(hc + lds_at(row, l32 >> 3) + 2 * (l32 & 7)) = hv;
       }
     }
@@ -542,6 +542,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   for (int nt = 0; nt < NT; ++nt) {
     const int n = (wn * NT + nt) * 32 + l32;
     const float b = bf2f(r.b2[n]);
+    const float ao = OUT == 2 ? bf2f(r.alpha_out[n]) : (OUT == 1 ? bf2f(r.alpha_s[n]) : 1.f), rao = 1.0f / ao;
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int t = t0 + wm * 32 + (v & 3) + 4 * half + 8 * (v >> 2);
@@ -549,10 +550,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       const size_t at = (size_t)t * C + n;
       const float val = (acc[nt][v] + b) + a.xf[at];  // the two-launch path's order of the sums
       if constexpr (OUT == 2) {
-        r.yb[at] = (uint16_t)f2bf(snake(val, bf2f(r.alpha_out[n])));
+        r.yb[at] = (uint16_t)f2bf(snake(val, ao, rao));
       } else {
         r.y[at] = val;
-        if constexpr (OUT == 1) r.ys[at] = (uint16_t)f2bf(snake(val, bf2f(r.alpha_s[n])));
+        if constexpr (OUT == 1) r.ys[at] = (uint16_t)f2bf(snake(val, ao, rao));
       }
     }
   }
