@@ -32,6 +32,7 @@
 #include <cmath>
 #include <cstring>
 #include <string>
+#include <type_traits>
 #include <vector>
 
 #include "../../include/dar.h"
@@ -489,6 +490,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   // h: chunk c's rows at hs + c BM 64, laid out as a staged window (lds_at)
   char* hs = smem + r.h_at;
   conv_accumulate<WM, WN, NT, XB16>(a, 0, t0, 0, smem, [&](f32x16 (&acc)[NT]) {
+    const bool whole = t0 + BM <= a.T;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       const int n = (wn * NT + nt) * 32 + l32;  // chunk wn NT + nt, channel l32 of it
@@ -497,7 +499,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int row = wm * 32 + (v & 3) + 4 * half + 8 * (v >> 2);
-        const uint16_t hv = t0 + row < a.T ? (uint16_t)f2bf(snake(acc[nt][v] + b, ao, rao)) : (uint16_t)0;
+        // rows past the end hold zero (a select, not a branch)
+        const float h = snake(acc[nt][v] + b, ao, rao);
+        const uint16_t hv = (whole || t0 + row < a.T) ? (uint16_t)f2bf(h) : (uint16_t)0;
         *reinterpret_cast<uint16_t*>(hc + lds_at(row, l32 >> 3) + 2 * (l32 & 7)) = hv;
       }
     }
@@ -538,25 +542,32 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       }
     }
   }
+  // whole tiles (all but the last) are stored without per-row bound checks
+  auto epilogue = [&](auto whole) {
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const int n = (wn * NT + nt) * 32 + l32;
-    const float b = bf2f(r.b2[n]);
-    const float ao = OUT == 2 ? bf2f(r.alpha_out[n]) : (OUT == 1 ? bf2f(r.alpha_s[n]) : 1.f), rao = 1.0f / ao;
+    for (int nt = 0; nt < NT; ++nt) {
+      const int n = (wn * NT + nt) * 32 + l32;
+      const float b = bf2f(r.b2[n]);
+      const float ao = OUT == 2 ? bf2f(r.alpha_out[n]) : (OUT == 1 ? bf2f(r.alpha_s[n]) : 1.f), rao = 1.0f / ao;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int t = t0 + wm * 32 + (v & 3) + 4 * half + 8 * (v >> 2);
-      if (t >= a.T) continue;
-      const size_t at = (size_t)t * C + n;
-      const float val = (acc[nt][v] + b) + a.xf[at];  // the two-launch path's order of the sums
-      if constexpr (OUT == 2) {
-        r.yb[at] = (uint16_t)f2bf(snake(val, ao, rao));
-      } else {
-        r.y[at] = val;
-        if constexpr (OUT == 1) r.ys[at] = (uint16_t)f2bf(snake(val, ao, rao));
+      for (int v = 0; v < 16; ++v) {
+        const int t = t0 + wm * 32 + (v & 3) + 4 * half + 8 * (v >> 2);
+        if (!decltype(whole)::value && t >= a.T) continue;
+        const size_t at = (size_t)t * C + n;
+        const float val = (acc[nt][v] + b) + a.xf[at];  // the two-launch path's order of the sums
+        if constexpr (OUT == 2) {
+          r.yb[at] = (uint16_t)f2bf(snake(val, ao, rao));
+        } else {
+          r.y[at] = val;
+          if constexpr (OUT == 1) r.ys[at] = (uint16_t)f2bf(snake(val, ao, rao));
+        }
       }
     }
-  }
+  };
+  if (t0 + BM <= a.T)
+    epilogue(std::true_type{});
+  else
+    epilogue(std::false_type{});
 }
 
 template <int WM, int WN, int NT, bool XB16, bool YB16>
