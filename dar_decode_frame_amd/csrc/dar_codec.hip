@@ -542,7 +542,54 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       }
     }
   }
-  // whole tiles (all but the last) are stored without per-row bound checks
+  if (OUT != 2 && t0 + BM <= a.T) {
+    // A whole tile's sums go through LDS (the 7-tap staging area, free again)
+    // so that the residual rows are read and the outputs written 16 bytes per
+    // lane along the rows instead of one value per lane and instruction; the
+    // channels' 1/alpha sit in the hidden rows' area, free after the 1-tap
+    // convolution. The values are the per-element path's.
+    constexpr int YP = C + 8;  // floats per staged row: the two half-waves' rows 32 banks apart
+    float* yl = reinterpret_cast<float*>(smem);
+    float* al = reinterpret_cast<float*>(hs);  // [C] alpha, [C] 1/alpha
+    __syncthreads();  // every wave is done with the 1-tap convolution's LDS
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const int col = (wn * NT + nt) * 32 + l32;
+      const float b = bf2f(r.b2[col]);
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+        yl[(wm * 32 + (v & 3) + 4 * half + 8 * (v >> 2)) * YP + col] = acc[nt][v] + b;
+    }
+    if constexpr (OUT != 0) {
+      for (int n = tid; n < C; n += kThreads) {
+        const float ao = bf2f(OUT == 2 ? r.alpha_out[n] : r.alpha_s[n]);
+        al[n] = ao;
+        al[C + n] = 1.0f / ao;
+      }
+    }
+    __syncthreads();
+    constexpr int Q = C / 4;  // 16-byte units of a row
+    for (int i = tid; i < BM * Q; i += kThreads) {
+      const int row = i / Q, q = i % Q;
+      const size_t at = (size_t)(t0 + row) * C + 4 * q;
+      const f32x4 xv = *reinterpret_cast<const f32x4*>(a.xf + at);
+      const f32x4 sv = *reinterpret_cast<const f32x4*>(yl + row * YP + 4 * q);
+      const f32x4 val = {sv.x + xv.x, sv.y + xv.y, sv.z + xv.z, sv.w + xv.w};  // (sum + b2) + x
+      if constexpr (OUT != 2) *reinterpret_cast<f32x4*>(r.y + at) = val;
+      if constexpr (OUT != 0) {
+        const f32x4 av = *reinterpret_cast<const f32x4*>(al + 4 * q);
+        const f32x4 rv = *reinterpret_cast<const f32x4*>(al + C + 4 * q);
+        uint2 o;
+        o.x = f2bf(snake(val.x, av.x, rv.x)) | (f2bf(snake(val.y, av.y, rv.y)) << 16);
+        o.y = f2bf(snake(val.z, av.z, rv.z)) | (f2bf(snake(val.w, av.w, rv.w)) << 16);
+        *reinterpret_cast<uint2*>((OUT == 2 ? r.yb : r.ys) + at) = o;
+      }
+    }
+    return;
+  }
+  // one value per lane (a block's last unit, whose bf16 output is a quarter
+  // of the rows' bytes, measured faster this way; and the partial last
+  // tile, whose rows past the end are skipped)
   auto epilogue = [&](auto whole) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
@@ -664,7 +711,8 @@ hipError_t launch_resunit(ResArgs r, hipStream_t s, hipEvent_t e0 = nullptr, hip
     return hipErrorInvalidValue;
   const TileCfg& c = kCfgs[ci];
   const int span = a.off[a.ntap - 1] - a.off[0];
-  const size_t conv = conv_lds(c, span, a.ntap);
+  // the 7-tap staging area also holds a whole tile's fp32 sums at the end
+  const size_t conv = std::max(conv_lds(c, span, a.ntap), (size_t)c.bm() * (a.Cout + 8) * 4);
   r.h_at = (int)conv;
   const size_t lds = conv + (size_t)c.bm() * a.Cout * 2;
   const dim3 grid((a.T + c.bm() - 1) / c.bm());
