@@ -233,16 +233,19 @@ __global__ __launch_bounds__(kThreads) void k_conv(ConvArgs a) {
   const int t0 = blockIdx.x * BM, n0 = blockIdx.y * BN;
   const int half = lane >> 5, l32 = lane & 31;
   conv_accumulate<WM, WN, NT, XB16>(a, z, t0, n0, smem, [&](f32x16 (&acc)[NT]) {
-    if constexpr (XB16 && !YB16) {
+    if constexpr (XB16) {
       if (t0 + BM <= a.T && n0 + BN <= a.Cout) {
-        // A whole tile with fp32 output rows (a transposed convolution, an
-        // unfused unit's 1-tap convolution): the sums go through LDS (the
-        // staging area, free again; the launch sizes it for this) so that the
-        // residual is read and the rows and the next operand are written 16
-        // bytes per lane along the rows. The values are the per-element path's.
+        // A whole tile: the sums go through LDS (the staging area, free
+        // again; the launch sizes it for this) so that the residual is read
+        // and the outputs written 16 or 8 bytes per lane along the rows: the
+        // fp32 rows and the next operand (a transposed convolution, an
+        // unfused unit's 1-tap convolution), or one bf16 operand (the input
+        // convolution, a 7-tap convolution's hidden rows, a block's last
+        // 1-tap convolution). The values are the per-element path's.
         constexpr int YP = BN + 8;  // floats per staged row: the two half-waves' rows 32 banks apart
         float* yl = reinterpret_cast<float*>(smem);
-        float* al = yl + BM * YP;   // [BN] alpha_s, [BN] 1/alpha_s of the tile's channels
+        float* al = yl + BM * YP;   // [BN] alpha, [BN] 1/alpha of the tile's channels
+        const uint16_t* alpha = YB16 ? a.alpha_out : a.ys ? a.alpha_s : nullptr;
         const int tid = threadIdx.x;
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
@@ -252,15 +255,15 @@ __global__ __launch_bounds__(kThreads) void k_conv(ConvArgs a) {
           for (int v = 0; v < 16; ++v)
             yl[(wm * 32 + (v & 3) + 4 * half + 8 * (v >> 2)) * YP + col] = acc[nt][v] + b;
         }
-        if (a.ys) {
+        if (alpha) {
           for (int c = tid; c < BN; c += kThreads) {
-            const float ao = bf2f(a.alpha_s[n0 + c]);
+            const float ao = bf2f(alpha[n0 + c]);
             al[c] = ao;
             al[BN + c] = 1.0f / ao;
           }
         }
         __syncthreads();
-        constexpr int Q = BN / 4;  // 16-byte units of a tile row
+        constexpr int Q = BN / 4;  // 16-byte units of a staged row
         for (int i = tid; i < BM * Q; i += kThreads) {
           const int row = i / Q, q = i % Q;
           const size_t at = ((size_t)(t0 + row) * a.nphase + z) * a.Cout + n0 + 4 * q;
@@ -269,14 +272,14 @@ __global__ __launch_bounds__(kThreads) void k_conv(ConvArgs a) {
             const f32x4 rv = *reinterpret_cast<const f32x4*>(a.res + at);
             val = f32x4{val.x + rv.x, val.y + rv.y, val.z + rv.z, val.w + rv.w};
           }
-          *reinterpret_cast<f32x4*>(a.yf + at) = val;
-          if (a.ys) {
+          if constexpr (!YB16) *reinterpret_cast<f32x4*>(a.yf + at) = val;
+          if (alpha) {
             const f32x4 av = *reinterpret_cast<const f32x4*>(al + 4 * q);
             const f32x4 rv = *reinterpret_cast<const f32x4*>(al + BN + 4 * q);
             uint2 o;
             o.x = f2bf(snake(val.x, av.x, rv.x)) | (f2bf(snake(val.y, av.y, rv.y)) << 16);
             o.y = f2bf(snake(val.z, av.z, rv.z)) | (f2bf(snake(val.w, av.w, rv.w)) << 16);
-            *reinterpret_cast<uint2*>(a.ys + at) = o;
+            *reinterpret_cast<uint2*>((YB16 ? a.yb : a.ys) + at) = o;
           }
         }
         return;
@@ -704,7 +707,7 @@ hipError_t launch_conv(const ConvArgs& a, hipStream_t s, hipEvent_t e0 = nullptr
     span = std::max(span, hi - lo);
   }
   size_t lds = conv_lds(c, span, a.ntap);
-  if (a.xb && !a.yb)  // whole tiles stage their fp32 sums and the channels' alphas at the end
+  if (a.xb)  // whole tiles stage their fp32 sums and the channels' alphas at the end
     lds = std::max(lds, (size_t)c.bm() * (c.bn() + 8) * 4 + (size_t)c.bn() * 8);
   const dim3 grid((a.T + c.bm() - 1) / c.bm(), (a.Cout + c.bn() - 1) / c.bn(), a.nphase);
   const bool xb = a.xb != nullptr, yb = a.yb != nullptr;
