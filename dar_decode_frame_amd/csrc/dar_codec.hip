@@ -50,7 +50,6 @@ constexpr int kChunk = 32;      // input channels per staged chunk (two MFMA k-s
 constexpr int kMaxTaps = 7;
 constexpr int kMaxOff = 32;     // largest |tap offset| of a convolution
 constexpr int kMaxOffs = 32;    // taps x phases of one launch
-constexpr int kOutRows = 256;   // output samples per workgroup of the output convolution
 
 __device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float(((uint32_t)h) << 16); }
 
@@ -320,75 +319,101 @@ __global__ __launch_bounds__(kThreads) void k_conv(ConvArgs a) {
   });
 }
 
-// The output convolution (one channel): Snake, K taps, bias, tanh. A
-// workgroup makes kOutRows samples from its window of input rows, 32 channels
-// at a time: every load of a channel block is issued before any is used (so
-// their latencies overlap), then the block is staged channel-major in LDS
-// (after Snake, rounded to bf16) so that consecutive lanes read consecutive
-// samples, and each thread adds the block's taps to its sample's sum.
-constexpr int kOutCB = 32;  // channels per staged block
+// The output convolution (one channel): y[t] = tanh(b + sum_j sum_c w[c][j]
+// u[t + j - h][c]), u the operand rows (Snake, rounded to bf16; zeros outside
+// [0, T)), h = (K - 1) / 2. The double sum splits into per-row tap projections
+// p_j[r] = sum_c w[c][j] u[r][c] -- a [rows x C] by [C x K] product, run on
+// MFMA with the taps as the tile's columns -- and then y[t] needs only
+// p_j[t + j - h] over the K taps. A workgroup projects kOutP consecutive rows
+// (each wave two 32-row tiles; every operand load of a pass over the channels
+// is issued at once, straight into the A registers, so each row is read from
+// memory once and no staging sits between the loads and the MFMAs), parks the
+// projections in LDS and sums them into kOutP - (K - 1) output samples.
+constexpr int kOutP = 256;     // projected rows per workgroup (4 waves x 2 tiles of 32)
+constexpr int kOutPitch = 9;   // LDS floats per projected row: odd, so a wave's reads of one tap hit 64 banks
+constexpr int kOutSteps = 6;   // MFMA k-steps (16 channels each) per pass over the channels
+static_assert(kMaxTaps < kOutPitch, "every tap's projection needs its own LDS slot");
+
+// XB16: the operand rows are given (bf16, Snake applied); otherwise fp32 rows
+// take Snake(alpha) and the bf16 rounding on load
+template <bool XB16>
 __global__ __launch_bounds__(kThreads) void k_conv_out(const float* x, const uint16_t* xb16, const uint16_t* alpha,
                                                      int T, int C, const uint16_t* w, const uint16_t* b, int K,
                                                      float* y) {
-  extern __shared__ __align__(16) char smem[];
-  const int halfk = (K - 1) / 2, W = kOutRows + K - 1;
-  uint16_t* xs = reinterpret_cast<uint16_t*>(smem);  // [kOutCB][W]
-  float* wsm = reinterpret_cast<float*>(smem + (((size_t)kOutCB * W * 2 + 15) & ~(size_t)15));  // [C][K]
-  const int t0 = blockIdx.x * kOutRows, tid = threadIdx.x;
-  for (int i = tid; i < C * K; i += kThreads) wsm[i] = bf2f(w[i]);
-  constexpr int Q = kOutCB / 4;                                        // float4s per window row
-  constexpr int NL = ((kOutRows + 14) * Q + kThreads - 1) / kThreads;  // per thread (K <= 15)
-  float acc = 0.f;
-  for (int cb = 0; cb < C; cb += kOutCB) {
-    f32x4 v[NL];
-    uint32_t al[NL][2];
+  __shared__ float ps[kOutP * kOutPitch];  // ps[r * kOutPitch + j] = p_j[p0 + r]
+  __shared__ bf16x8 bs[kOutSteps * 64];    // the B operand of each k-step, per lane
+  const int halfk = (K - 1) / 2, TM = kOutP - (K - 1);
+  const int t0 = blockIdx.x * TM, p0 = t0 - halfk;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int n = lane & 31, hk = lane >> 5;  // this lane's MFMA row / column (tap) and k half
+  const bool whole = p0 >= 0 && p0 + kOutP <= T;
+  f32x16 acc[2];
 #pragma unroll
-    for (int k = 0; k < NL; ++k) {
-      const int i = tid + k * kThreads;
-      const int r = i / Q, c4 = i % Q;
-      const int row = t0 - halfk + r;
-      const bool in = i < W * Q && row >= 0 && row < T;
-      if (xb16) {  // the operand already Snake'd and rounded: four bf16 in the first two lanes' words
-        const uint2 h = in ? *reinterpret_cast<const uint2*>(xb16 + (size_t)row * C + cb + 4 * c4) : uint2{0u, 0u};
-        v[k] = f32x4{__uint_as_float(h.x), __uint_as_float(h.y), 0.f, 0.f};
-        continue;
-      }
-      v[k] = in ? *reinterpret_cast<const f32x4*>(x + (size_t)row * C + cb + 4 * c4) : f32x4{0.f, 0.f, 0.f, 0.f};
-      if (i < W * Q) {
-        const uint2 a2 = *reinterpret_cast<const uint2*>(alpha + cb + 4 * c4);
-        al[k][0] = a2.x;
-        al[k][1] = a2.y;
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[m][v] = 0.f;
+  const bf16x8 zero = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+  for (int c0 = 0; c0 < C; c0 += 16 * kOutSteps) {
+    const int S = min(kOutSteps, (C - c0) / 16);
+    // A: row (tile base + n), channels c0 + 16 s + 8 hk .. + 8
+    bf16x8 A[2][kOutSteps];
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const int row = p0 + 32 * (2 * wv + m) + n;
+      const bool in = whole || (row >= 0 && row < T);
+#pragma unroll
+      for (int st = 0; st < kOutSteps; ++st) {
+        A[m][st] = zero;
+        if (st >= S || !in) continue;
+        const int c = c0 + 16 * st + 8 * hk;
+        if constexpr (XB16) {
+          A[m][st] = *reinterpret_cast<const bf16x8*>(xb16 + (size_t)row * C + c);
+        } else {
+          const f32x4 lo = *reinterpret_cast<const f32x4*>(x + (size_t)row * C + c);
+          const f32x4 hi = *reinterpret_cast<const f32x4*>(x + (size_t)row * C + c + 4);
+          const float f[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+#pragma unroll
+          for (int e = 0; e < 8; ++e) A[m][st][e] = (__bf16)snake(f[e], bf2f(alpha[c + e]));
+        }
       }
     }
-    __syncthreads();  // the previous block's reads of xs are done
+    // B: column j of k-step s holds w[c][j] for the step's 16 channels (zero past the taps)
+    for (int i = tid; i < S * 64; i += kThreads) {
+      const int st = i >> 6, nn = i & 31, hh = (i >> 5) & 1;
+      bf16x8 v = zero;
+      if (nn < K) {
 #pragma unroll
-    for (int k = 0; k < NL; ++k) {
-      const int i = tid + k * kThreads;
-      if (i >= W * Q) continue;
-      const int r = i / Q, c4 = i % Q;
-      const int row = t0 - halfk + r;
-      const bool in = row >= 0 && row < T;
-      if (xb16) {
-        const uint32_t h[2] = {__float_as_uint(v[k].x), __float_as_uint(v[k].y)};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) xs[(4 * c4 + e) * W + r] = in ? (uint16_t)(h[e >> 1] >> (16 * (e & 1))) : (uint16_t)0;
-        continue;
+        for (int e = 0; e < 8; ++e)
+          v[e] = __builtin_bit_cast(__bf16, w[(size_t)(c0 + 16 * st + 8 * hh + e) * K + nn]);
       }
-      const float f[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float a = bf2f((uint16_t)(al[k][e >> 1] >> (16 * (e & 1))));
-        xs[(4 * c4 + e) * W + r] = in ? (uint16_t)f2bf(snake(f[e], a)) : (uint16_t)0;
-      }
+      bs[i] = v;
     }
     __syncthreads();
-    if (t0 + tid < T) {
-      for (int c = 0; c < kOutCB; ++c)
-        for (int j = 0; j < K; ++j) acc = fmaf(wsm[(cb + c) * K + j], bf2f(xs[c * W + tid + j]), acc);
+#pragma unroll
+    for (int st = 0; st < kOutSteps; ++st) {
+      if (st >= S) break;
+      const bf16x8 B = bs[st * 64 + lane];
+#pragma unroll
+      for (int m = 0; m < 2; ++m) acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[m][st], B, acc[m], 0, 0, 0);
     }
+    __syncthreads();  // bs is rewritten by the next pass
   }
+  if (n < K) {
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int r = 32 * (2 * wv + m) + (v & 3) + 4 * hk + 8 * (v >> 2);
+        ps[r * kOutPitch + n] = acc[m][v];
+      }
+  }
+  __syncthreads();
   const int t = t0 + tid;
-  if (t < T) y[t] = tanhf(acc + bf2f(b[0]));
+  if (tid < TM && t < T) {
+    float sum = 0.f;
+    for (int j = 0; j < K; ++j) sum += ps[(tid + j) * kOutPitch + j];
+    y[t] = tanhf(sum + bf2f(b[0]));
+  }
 }
 
 // z[t] = sum_k table_k[code[t][k]] over the codebooks in order, fp32 sums
@@ -778,24 +803,22 @@ hipError_t launch_resunit(ResArgs r, hipStream_t s, hipEvent_t e0 = nullptr, hip
   return hipErrorInvalidValue;
 }
 
-size_t out_lds(int C, int K) {
-  return (((size_t)kOutCB * (kOutRows + K - 1) * 2 + 15) & ~(size_t)15) + (size_t)C * K * 4;
-}
-
 // x: fp32 rows with Snake(alpha) applied on load, or xb16: bf16 rows already
 // Snake'd and rounded (alpha unused)
 hipError_t launch_conv_out(const float* x, const uint16_t* xb16, const uint16_t* alpha, int T, int C,
                            const uint16_t* w, const uint16_t* b, int K, float* y, hipStream_t s,
                            hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr) {
-  static std::atomic<bool> big{false};
-  const size_t lds = out_lds(C, K);
-  hipError_t e = allow_lds(k_conv_out, lds, big);
-  if (e != hipSuccess) return e;
-  const dim3 grid((T + kOutRows - 1) / kOutRows);
-  if (e0 || e1)
-    hipExtLaunchKernelGGL(k_conv_out, grid, dim3(kThreads), lds, s, e0, e1, 0, x, xb16, alpha, T, C, w, b, K, y);
+  const dim3 grid((T + kOutP - K) / (kOutP - (K - 1)));
+  auto go = [&](auto kern) {
+    if (e0 || e1)
+      hipExtLaunchKernelGGL(kern, grid, dim3(kThreads), 0, s, e0, e1, 0, x, xb16, alpha, T, C, w, b, K, y);
+    else
+      hipLaunchKernelGGL(kern, grid, dim3(kThreads), 0, s, x, xb16, alpha, T, C, w, b, K, y);
+  };
+  if (xb16)
+    go(k_conv_out<true>);
   else
-    hipLaunchKernelGGL(k_conv_out, grid, dim3(kThreads), lds, s, x, xb16, alpha, T, C, w, b, K, y);
+    go(k_conv_out<false>);
   return hipGetLastError();
 }
 
@@ -912,7 +935,6 @@ int validate_codec(const dar_codec_config* c, std::string& why) {
     if (c->rates[i] < 2 || c->rates[i] > 16 || c->rates[i] % 2) return bad("rates must be even, in [2, 16]");
     hop *= c->rates[i];
   }
-  if (out_lds(last, K) > 160 * 1024) return bad("last block width too large for the output convolution's LDS window");
   if (c->max_frames < 1) return bad("max_frames must be >= 1");
   if ((long long)c->max_frames * hop * c->channels >= (1LL << 31)) return bad("max_frames * hop * channels must be < 2^31");
   return DAR_OK;
@@ -1302,10 +1324,12 @@ int dar_codec_op_conv(const void* x, int32_t x_bf16, const void* alpha, int32_t 
   if (!x || !w || !b || !y || T < 1 || Cin < 1) return DAR_E_INVAL;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (Cout == 1) {
-    if (x_bf16 || !alpha || stride != 0 || dilation != 1 || taps < 1 || taps > kMaxTaps || taps % 2 == 0 ||
-        !tanh_out || res || Cin % kOutCB || out_lds(Cin, taps) > 160 * 1024)
+    if ((x_bf16 != 0) == (alpha != nullptr) || stride != 0 || dilation != 1 || taps < 1 || taps > kMaxTaps ||
+        taps % 2 == 0 || !tanh_out || res || Cin % 32)
       return DAR_E_INVAL;
-    hipError_t e = launch_conv_out(static_cast<const float*>(x), nullptr, U16(alpha), T, Cin, U16(w), U16(b), taps, y, s);
+    hipError_t e = x_bf16 ? launch_conv_out(nullptr, U16(x), nullptr, T, Cin, U16(w), U16(b), taps, y, s)
+                          : launch_conv_out(static_cast<const float*>(x), nullptr, U16(alpha), T, Cin, U16(w), U16(b),
+                                            taps, y, s);
     if (e == hipSuccess) e = hipStreamSynchronize(s);
     return e == hipSuccess ? DAR_OK : codec_hip_fail(nullptr, e, "op conv out");
   }

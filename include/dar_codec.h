@@ -154,9 +154,10 @@ const char* dar_codec_last_error(const dar_codec* ctx);
  * for a transposed convolution (stride even, padding stride / 2, output
  * T * stride rows); b: device bf16 [Cout]; y: device fp32 [rows][Cout], plus
  * res (device fp32, same shape, may alias y) when non-NULL; tanh_out applies
- * tanh last (fp32 input only). Cin, Cout multiples of 32 (Cout == 1 is the output kernel: 7
- * taps, dilation 1, fp32 input with alpha). Allocates its re-laid weights per
- * call and synchronises the stream. */
+ * tanh last (fp32 input only). Cin, Cout multiples of 32. Cout == 1 is the
+ * output kernel: odd taps <= 7, dilation 1, tanh_out set, no res, and either
+ * fp32 input with alpha or bf16 input (the Snake'd operand) without it.
+ * Allocates its re-laid weights per call and synchronises the stream. */
 int dar_codec_op_conv(const void* x, int32_t x_bf16, const void* alpha, int32_t T, int32_t Cin, int32_t Cout,
                       const void* w, const void* b, int32_t taps, int32_t dilation, int32_t stride,
                       const float* res, int32_t tanh_out, float* y, void* stream);

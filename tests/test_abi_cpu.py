@@ -262,3 +262,10 @@ def test_codec_ops_reject_bad_arguments_before_hip(N):
     assert N.lib.dar_codec_op_conv(fake, 0, fake, 10, 64, 64, fake, fake, 7, 1, 3, None, 0, fake, None) == N.DAR_E_INVAL
     assert N.lib.dar_codec_op_conv(fake, 1, fake, 10, 64, 64, fake, fake, 7, 1, 0, None, 0, fake, None) == N.DAR_E_INVAL
     assert N.lib.dar_codec_op_conv(fake, 0, None, 10, 64, 1, fake, fake, 7, 1, 0, None, 1, fake, None) == N.DAR_E_INVAL
+    # the output convolution: bf16 operand without alpha or fp32 rows with it; odd taps <= 7; tanh; no residual
+    assert N.lib.dar_codec_op_conv(fake, 1, fake, 10, 64, 1, fake, fake, 7, 1, 0, None, 1, fake, None) == N.DAR_E_INVAL
+    assert N.lib.dar_codec_op_conv(fake, 1, None, 10, 64, 1, fake, fake, 9, 1, 0, None, 1, fake, None) == N.DAR_E_INVAL
+    assert N.lib.dar_codec_op_conv(fake, 1, None, 10, 64, 1, fake, fake, 6, 1, 0, None, 1, fake, None) == N.DAR_E_INVAL
+    assert N.lib.dar_codec_op_conv(fake, 1, None, 10, 48, 1, fake, fake, 7, 1, 0, None, 1, fake, None) == N.DAR_E_INVAL
+    assert N.lib.dar_codec_op_conv(fake, 1, None, 10, 64, 1, fake, fake, 7, 1, 0, None, 0, fake, None) == N.DAR_E_INVAL
+    assert N.lib.dar_codec_op_conv(fake, 1, None, 10, 64, 1, fake, fake, 7, 1, 0, fake, 1, fake, None) == N.DAR_E_INVAL

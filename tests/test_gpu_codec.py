@@ -138,6 +138,31 @@ def test_residual_add_in_place_and_output_conv():
     assert np.max(np.abs(got2 - ref2)) < 1e-5 + 2.0 ** -7 * np.abs(w2).max() * np.abs(xin).max()
 
 
+@pytest.mark.parametrize("T,C,K,x_bf16", [
+    (1, 96, 7, True), (250, 96, 7, True), (251, 96, 7, False), (1000, 32, 7, True), (777, 64, 5, False),
+    (513, 96, 3, True), (300, 96, 1, True), (4001, 96, 7, True), (2500, 192, 7, False), (256, 128, 7, True),
+])
+def test_output_conv_against_oracle(T, C, K, x_bf16):
+    """The one-channel output convolution (per-row tap projections on MFMA,
+    then the shifted sum over taps): both operand forms, row counts around a
+    workgroup's 256 - (K - 1) outputs and ragged tails, every odd kernel size,
+    widths of one to two passes over the channels. Against the oracle's conv1d
+    on the same bf16 operand: fp32 summation error, plus one bf16 step of a
+    Snake'd input where fp32 and fp64 Snake round differently (fp32 input)."""
+    r = np.random.default_rng(T * 3 + C + K)
+    x = r.standard_normal((T, C)).astype(np.float32)
+    alpha = None if x_bf16 else _wide(0.5 + r.random(C))
+    w = _wide(r.standard_normal((1, C, K)) * 0.05)
+    b = _wide(r.standard_normal(1) * 0.1)
+    got = _op(_wide(x) if x_bf16 else x, x_bf16, alpha, w, b, K, 1, 0, 1, tanh=True)[:, 0]
+    xin = _wide(x) if x_bf16 else round_bf16(snake(x.astype(np.float64), alpha)).astype(np.float64)
+    pre = conv1d(xin, w, b)[:, 0]
+    S = conv1d(np.abs(xin), np.abs(w), np.zeros(1))[:, 0]
+    bound = 2e-5 * S + 1e-7 + (0 if x_bf16 else 2.0 ** -7 * np.abs(w).max() * np.abs(xin).max())
+    assert got.shape == (T,)
+    assert np.all(np.abs(got - np.tanh(pre)) <= bound), np.abs(got - np.tanh(pre)).max()
+
+
 @pytest.mark.parametrize("T,C,dil", [(150, 32, 9), (70, 64, 3), (333, 96, 1), (45, 128, 3), (700, 96, 9),
                                      (1, 96, 1), (129, 128, 1)])
 def test_fused_residual_unit(T, C, dil):
