@@ -583,7 +583,10 @@ __device__ __forceinline__ void split_store4(float4 v, uint16_t* oh, uint16_t* o
 // Row m of the GEMM input: v = x[m] (RMSNorm(x[m]) * gain when gain is set),
 // written as hi = bf16(v), lo = bf16(v - hi); rows M..Mpad-1 are zero. With
 // residual sums pending, x[m] += their sum first (written back). With out_f32
-// set, v is also written there in fp32 (row stride K). Columns in fours.
+// set, v is also written there in fp32 (row stride K). Columns in fours, at
+// most kNormCols4 per thread, kept in registers from the load to the split
+// (no second read of the row after the norm's block sum).
+constexpr int kNormCols4 = 4;  // K <= 4 * kNormCols4 * kNormBlock
 __global__ __launch_bounds__(kNormBlock) void k_norm_split(float* x, int x_stride, int M, int K,
                                                             const uint16_t* gain, float eps, uint16_t* xh,
                                                             uint16_t* xl, float* out_f32, PartSum add) {
@@ -598,26 +601,33 @@ __global__ __launch_bounds__(kNormBlock) void k_norm_split(float* x, int x_strid
   }
   float* xr = x + (size_t)m * x_stride;
   float ss = 0.f;
-  if (add.n > 0 || gain) {
-    for (int k = 4 * tid; k < K; k += 4 * kNormBlock) {
-      float4 v = ld4(xr + k);
-      if (add.n > 0) {
-        v = add4(v, part_sum4(add, (size_t)m * K + k));
-        *reinterpret_cast<float4*>(xr + k) = v;
-      }
-      ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+  float4 xv[kNormCols4];
+  u32x2 gv[kNormCols4];
+#pragma unroll
+  for (int j = 0; j < kNormCols4; ++j) {
+    const int k = 4 * tid + j * 4 * kNormBlock;
+    if (k >= K) break;
+    if (gain) gv[j] = *reinterpret_cast<const u32x2*>(gain + k);  // in flight with the row's loads
+    float4 v = ld4(xr + k);
+    if (add.n > 0) {
+      v = add4(v, part_sum4(add, (size_t)m * K + k));
+      *reinterpret_cast<float4*>(xr + k) = v;
     }
+    ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+    xv[j] = v;
   }
   float inv = 1.f;
   if (gain) {
     ss = block_sum<NW>(ss, red);
     inv = 1.0f / sqrtf(ss / (float)K + eps);
   }
-  // each thread rereads only the columns it wrote above
-  for (int k = 4 * tid; k < K; k += 4 * kNormBlock) {
-    float4 v = ld4(xr + k);
+#pragma unroll
+  for (int j = 0; j < kNormCols4; ++j) {
+    const int k = 4 * tid + j * 4 * kNormBlock;
+    if (k >= K) break;
+    float4 v = xv[j];
     if (gain) {
-      const u32x2 g = *reinterpret_cast<const u32x2*>(gain + k);
+      const u32x2 g = gv[j];
       v.x = (v.x * inv) * bf2f((uint16_t)(g.x & 0xffffu));
       v.y = (v.y * inv) * bf2f((uint16_t)(g.x >> 16));
       v.z = (v.z * inv) * bf2f((uint16_t)(g.y & 0xffffu));
@@ -907,7 +917,8 @@ hipError_t launch_gemm(int wtype, GemmArgs a, size_t part_cap, hipStream_t s) {
 
 hipError_t launch_norm_split(float* x, int x_stride, int M, int K, const uint16_t* gain, float eps, uint16_t* xh,
                              uint16_t* xl, hipStream_t s, float* out_f32, PartSum add) {
-  if (K % 4 || x_stride % 4 || (add.n > 0 && x_stride != K)) return hipErrorInvalidValue;
+  if (K % 4 || K > 4 * kNormCols4 * kNormBlock || x_stride % 4 || (add.n > 0 && x_stride != K))
+    return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_norm_split, dim3(gemm_mpad(M)), dim3(kNormBlock), 0, s, x, x_stride, M, K, gain, eps, xh, xl,
                      out_f32, add);
   return hipGetLastError();
