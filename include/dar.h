@@ -356,11 +356,13 @@ int dar_op_attention(const float* q, const void* K, const void* V, int32_t n_hea
                      int32_t M, int32_t chunk, float* out, void* stream);
 
 /* Reference read rate of the GPU: reads `bytes` of device memory at src
- * (16-byte aligned, bytes a multiple of 16) `iters` times back to back with
- * 16-byte non-temporal loads (as the frame's GEMVs stream their weights, but
- * with no arithmetic) over a grid-stride loop of 8192 workgroups, eight loads
- * in flight per thread (the fastest plain read among the forms tried), and
- * returns the mean milliseconds per read in *ms_out (HIP events around the
+ * (16-byte aligned, bytes a multiple of 16) with 16-byte non-temporal loads
+ * (as the frame's GEMVs stream their weights, but with no arithmetic) over a
+ * grid-stride loop, in each of five launch shapes (384 workgroups x 4 loads
+ * in flight per thread, 768 x 2, 256 x 8, 512 x 4, 8192 x 8: HBM on this
+ * part streams fastest with about 6-8 MB in flight), each shape one untimed
+ * read and then `iters` timed reads back to back, and returns in *ms_out the
+ * mean milliseconds per read of the fastest shape (HIP events around the
  * launches; synchronises the stream). sink: device, at least 8 KiB, written
  * only with a value no read produces in practice (it keeps the loads). A
  * measurement aid: the frame's weight rate means most next to it. */

@@ -57,9 +57,11 @@ def _bf16_matrix(rows, cols, seed, scale=0.02):
 
 
 def test_stream_read_reference(env):
-    """dar_op_stream_read: a plain read of 64 MiB reports a rate a read can
-    have (between 0.2 and 10 TB/s on this part), leaves the sink alone (its
-    marker value needs a read that sums to it), and rejects bad arguments."""
+    """dar_op_stream_read: a plain read of 64 MiB (the fastest of its launch
+    shapes) reports a rate a read can have (between 0.2 and 10 TB/s on this
+    part), leaves the sink alone (its marker value needs a read that sums to
+    it), handles a buffer smaller than a grid stride, and rejects bad
+    arguments."""
     torch, N, dev = env
     buf = torch.zeros(64 << 20, dtype=torch.uint8, device=dev)
     sink = torch.full((2048,), 7, dtype=torch.int32, device=dev)
@@ -69,6 +71,9 @@ def test_stream_read_reference(env):
     rate = buf.numel() / (ms * 1e-3)
     assert 0.2e12 < rate < 10e12, rate
     assert bool((sink == 7).all())
+    # smaller than one grid stride of every shape: only the loops' tails read
+    ms_small = N.dar_op_stream_read(_p(buf), 4096, 2, _p(sink), _sp(torch))
+    assert ms_small > 0 and bool((sink == 7).all())
     out = ctypes.c_float(0)
     assert N.lib.dar_op_stream_read(_p(buf), 100, 1, _p(sink), ctypes.byref(out), None) == N.DAR_E_INVAL
     assert N.lib.dar_op_stream_read(_p(buf), 1024, 0, _p(sink), ctypes.byref(out), None) == N.DAR_E_INVAL
