@@ -57,7 +57,14 @@ S2_CODEC = CodecDims("s2pro_codec", n_codebooks=10, codebook_size=4096, latent_d
 # tiny shape: the oracle finishes in well under a second; widths 128 -> 64 -> 32
 TINY_CODEC = CodecDims("tiny_codec", n_codebooks=10, codebook_size=64, latent_dim=64, channels=128, rates=(2, 4))
 
-CODEC_DIMS = {"s2pro_codec": S2_CODEC, "tiny_codec": TINY_CODEC}
+# a second small shape for the layer forms the first does not reach: 5-tap
+# convolutions, two residual units per block (dilations 1, 2), three blocks,
+# and a 256-channel block whose units take the two-launch path; widths
+# 256 -> 128 -> 64 -> 32
+SMALL_CODEC_K5 = CodecDims("small_codec_k5", n_codebooks=4, codebook_size=32, latent_dim=96, channels=256,
+                           rates=(2, 2, 4), dilations=(1, 2), kernel=5)
+
+CODEC_DIMS = {"s2pro_codec": S2_CODEC, "tiny_codec": TINY_CODEC, "small_codec_k5": SMALL_CODEC_K5}
 
 
 @dataclass(frozen=True)

@@ -71,6 +71,7 @@ def _wide(a):
 @pytest.mark.parametrize("T,Cin,Cout,K,dil,snk", [
     (45, 64, 64, 7, 1, True), (150, 32, 96, 7, 9, True), (333, 96, 96, 7, 3, True), (37, 64, 128, 7, 1, False),
     (70, 64, 32, 1, 1, False), (1, 32, 64, 7, 1, True), (2000, 96, 96, 7, 9, True), (167, 1024, 1536, 7, 1, False),
+    (150, 64, 96, 3, 9, True), (77, 96, 64, 5, 3, True), (300, 256, 256, 5, 2, False),
 ])
 def test_conv_against_oracle(T, Cin, Cout, K, dil, snk):
     r = np.random.default_rng(T * 7 + Cin)
@@ -163,12 +164,13 @@ def test_output_conv_against_oracle(T, C, K, x_bf16):
     assert np.all(np.abs(got - np.tanh(pre)) <= bound), np.abs(got - np.tanh(pre)).max()
 
 
-@pytest.mark.parametrize("T,C,dil", [(150, 32, 9), (70, 64, 3), (333, 96, 1), (45, 128, 3), (700, 96, 9),
-                                     (1, 96, 1), (129, 128, 1)])
-def test_fused_residual_unit(T, C, dil):
+@pytest.mark.parametrize("T,C,dil,taps", [(150, 32, 9, 7), (70, 64, 3, 7), (333, 96, 1, 7), (45, 128, 3, 7),
+                                          (700, 96, 9, 7), (1, 96, 1, 7), (129, 128, 1, 7), (200, 96, 3, 3),
+                                          (97, 64, 9, 5), (130, 128, 2, 5), (50, 32, 1, 1)])
+def test_fused_residual_unit(T, C, dil, taps):
     """dar_codec_op_resunit: the one-launch unit (hidden rows kept in LDS)
     gives the two-launch path's values bit for bit, and both are within the
-    oracle's bound: the 7-tap convolution's per-output bound e1, carried
+    oracle's bound: the dilated convolution's per-output bound e1, carried
     through Snake (slope at most 2) and the hidden bf16 rounding (a value may
     land one bf16 step, at most 2^-7 of its size, away), then summed by the
     1-tap convolution, plus fp32 summation error."""
@@ -177,7 +179,7 @@ def test_fused_residual_unit(T, C, dil):
     r = np.random.default_rng(C * 1000 + T)
     x = r.standard_normal((T, C)).astype(np.float32)
     a1, a2 = _wide(0.5 + r.random(C)), _wide(0.5 + r.random(C))
-    w1 = _wide(r.standard_normal((C, C, 7)) / np.sqrt(7 * C))
+    w1 = _wide(r.standard_normal((C, C, taps)) / np.sqrt(taps * C))
     b1 = _wide(r.standard_normal(C) * 0.1)
     w2 = _wide(r.standard_normal((C, C, 1)) / np.sqrt(C))
     b2 = _wide(r.standard_normal(C) * 0.1)
@@ -188,7 +190,7 @@ def test_fused_residual_unit(T, C, dil):
     for fused in (1, 0):
         y = torch.full((T, C), float("nan"), dtype=torch.float32, device="cuda")
         torch.cuda.synchronize()
-        N.dar_codec_op_resunit(p(xd), T, C, p(dev["a1"]), p(dev["w1"]), p(dev["b1"]), 7, dil, p(dev["a2"]),
+        N.dar_codec_op_resunit(p(xd), T, C, p(dev["a1"]), p(dev["w1"]), p(dev["b1"]), taps, dil, p(dev["a2"]),
                                p(dev["w2"]), p(dev["b2"]), fused, p(y), None)
         out[fused] = y.cpu().numpy()
     assert np.array_equal(out[1].view(np.uint32), out[0].view(np.uint32))
@@ -203,9 +205,9 @@ def test_fused_residual_unit(T, C, dil):
     assert np.all(err <= bound), float((err / bound).max())
     # in place is refused for the one-launch kernel, allowed for two launches
     with pytest.raises(RuntimeError):
-        N.dar_codec_op_resunit(p(xd), T, C, p(dev["a1"]), p(dev["w1"]), p(dev["b1"]), 7, dil, p(dev["a2"]),
+        N.dar_codec_op_resunit(p(xd), T, C, p(dev["a1"]), p(dev["w1"]), p(dev["b1"]), taps, dil, p(dev["a2"]),
                                p(dev["w2"]), p(dev["b2"]), 1, p(xd), None)
-    N.dar_codec_op_resunit(p(xd), T, C, p(dev["a1"]), p(dev["w1"]), p(dev["b1"]), 7, dil, p(dev["a2"]),
+    N.dar_codec_op_resunit(p(xd), T, C, p(dev["a1"]), p(dev["w1"]), p(dev["b1"]), taps, dil, p(dev["a2"]),
                            p(dev["w2"]), p(dev["b2"]), 0, p(xd), None)
     assert np.array_equal(xd.cpu().numpy().view(np.uint32), out[0].view(np.uint32))
 
@@ -237,6 +239,30 @@ def test_tiny_decode_against_oracle(tiny_codec, frames):
     assert _rel(got, ref_b) <= 1.5e-2, _rel(got, ref_b)
     assert _rel(got, ref_f) <= 2e-2, _rel(got, ref_f)
     print(f"tiny codec {frames} frames: rel L2 {_rel(got, ref_b):.2e} (bf16 activations), {_rel(got, ref_f):.2e} (fp64)")
+
+
+@pytest.mark.parametrize("frames", [23, 1])
+def test_small_k5_decode_against_oracle(frames):
+    """A second shape (5-tap convolutions, two residual units per block, three
+    blocks, a 256-channel block on the two-launch path) against the oracle, to
+    the tiny codec's bar."""
+    from dar_decode_frame_amd.session import CodecSession
+    d = synth.CODEC_DIMS["small_codec_k5"]
+    host = synth.gen_codec_weights(d, 5)
+    P = CodecParams(d, host)
+    sess = CodecSession(d, host, 32)
+    try:
+        codes = synth.gen_codes(frames, d, 11 + frames)
+        got = sess.decode(codes).astype(np.float64)
+    finally:
+        sess.close()
+    ref_b = codec_decode(codes, P, act="bf16")
+    ref_f = codec_decode(codes, P)
+    assert got.shape == ref_b.shape == (frames * d.hop,)
+    assert np.all(np.abs(got) < 1)
+    assert _rel(got, ref_b) <= 1.5e-2, _rel(got, ref_b)
+    assert _rel(got, ref_f) <= 2e-2, _rel(got, ref_f)
+    print(f"small k5 codec {frames} frames: rel L2 {_rel(got, ref_b):.2e} (bf16 activations), {_rel(got, ref_f):.2e} (fp64)")
 
 
 def test_tiny_decode_repeats_and_clamps_out_of_range_codes(tiny_codec):
