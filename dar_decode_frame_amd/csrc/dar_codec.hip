@@ -566,7 +566,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   const int half = lane >> 5, l32 = lane & 31;
   // h: chunk c's rows at hs + c BM 64, laid out as a staged window (lds_at)
   char* hs = smem + r.h_at;
+  // the 1-tap convolution's weights, every chunk at once: chunk c's rows at
+  // ws + c C 64 (the 7-tap staging area, free once its loop has ended; the
+  // launch sizes it for at least a whole tile's fp32 sums, BM (C + 8) 4 bytes)
+  char* ws = smem;
+  static_assert(CH * C * 64 <= BM * (C + 8) * 4, "the 1-tap weights fit in the staging area");
   conv_accumulate<WM, WN, NT, XB16>(a, 0, t0, 0, smem, [&](f32x16 (&acc)[NT]) {
+    // issued before the hidden rows' Snake, so that their latency hides behind it
+    u32x4 wv[CH][WU];
+#pragma unroll
+    for (int c = 0; c < CH; ++c)
+#pragma unroll
+      for (int k = 0; k < WU; ++k) {
+        const int i = tid + k * kThreads;
+        wv[c][k] = i < C * 4 ? *reinterpret_cast<const u32x4*>(r.W2 + (size_t)(i >> 2) * C + 32 * c + 8 * (i & 3))
+                             : u32x4{0u, 0u, 0u, 0u};
+      }
     const bool whole = t0 + BM <= a.T;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
@@ -582,30 +597,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         *reinterpret_cast<uint16_t*>(hc + lds_at(row, l32 >> 3) + 2 * (l32 & 7)) = hv;
       }
     }
+#pragma unroll
+    for (int c = 0; c < CH; ++c)
+#pragma unroll
+      for (int k = 0; k < WU; ++k) {
+        const int i = tid + k * kThreads;
+        if (i < C * 4) *reinterpret_cast<u32x4*>(ws + (size_t)c * C * 64 + lds_at(i >> 2, i & 3)) = wv[c][k];
+      }
   });
-  // the 1-tap convolution over h, chunk by chunk; its weight chunk reuses the
-  // LDS of the 7-tap convolution's staging
-  char* ws = smem;
+  __syncthreads();  // h and the 1-tap weights are complete
+  // the 1-tap convolution over h, chunk by chunk
   f32x16 acc[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc[nt][v] = 0.f;
   for (int c = 0; c < CH; ++c) {
-    u32x4 wv[WU];
-#pragma unroll
-    for (int k = 0; k < WU; ++k) {
-      const int i = tid + k * kThreads;
-      wv[k] = i < C * 4 ? *reinterpret_cast<const u32x4*>(r.W2 + (size_t)(i >> 2) * C + 32 * c + 8 * (i & 3))
-                        : u32x4{0u, 0u, 0u, 0u};
-    }
-    __syncthreads();  // h is complete (c = 0) / the previous chunk's reads of ws are done
-#pragma unroll
-    for (int k = 0; k < WU; ++k) {
-      const int i = tid + k * kThreads;
-      if (i < C * 4) *reinterpret_cast<u32x4*>(ws + lds_at(i >> 2, i & 3)) = wv[k];
-    }
-    __syncthreads();
+    const char* wc = ws + (size_t)c * C * 64;
     const char* hc = hs + (size_t)c * BM * 64;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
@@ -614,7 +622,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         const bf16x8 B =
-            __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(ws + lds_at((wn * NT + nt) * 32 + l32, u)));
+            __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(wc + lds_at((wn * NT + nt) * 32 + l32, u)));
         acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B, acc[nt], 0, 0, 0);
       }
     }
