@@ -667,7 +667,7 @@ def pages_formula(dims, wl, fps):
 
 
 def reference_read(frame_bytes_per_s):
-    """The box's own plain-read rate (dar_op_stream_read over 1 GiB: the
+    """The GPU's own plain-read rate (dar_op_stream_read over 1 GiB: the
     fastest of its five launch shapes, five reads each, 16-byte non-temporal
     loads as the GEMVs use) and the frame's algorithmic byte rate as a
     fraction of it: context for hbm_frac, which is against the 8 TB/s

@@ -301,7 +301,7 @@ __global__ __launch_bounds__(kBlock) void k_stream_read(const ru32x4* __restrict
 // The read's launch shapes (workgroups, loads in flight per thread). HBM on
 // this part streams fastest with about 6-8 MB of loads in flight (384 x 4,
 // 768 x 2, 256 x 8 reached 7.2-7.4 TB/s over 1 GiB; 16 MB or more in flight
-// fell to 5.2-6.0); the reference takes the fastest shape on the box at hand.
+// fell to 5.2-6.0); the reference takes the fastest shape on the GPU at hand.
 struct ReadShape {
   int grid, loads;
 };
