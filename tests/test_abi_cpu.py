@@ -110,6 +110,16 @@ def test_null_context_and_ops_reject(N):
     assert N.lib.dar_op_gemv(4, ctypes.c_void_p(4096), ctypes.c_void_p(4096), 4, 256, ctypes.c_void_p(4096), 1,
                              ctypes.c_void_p(4096), None) == N.DAR_E_INVAL
     assert N.lib.dar_op_attention(None, None, None, 4, 2, 64, 16, 0, 1, 0, None, None) == N.DAR_E_INVAL
+    # the reference read: 16-byte aligned source, a multiple of 16 bytes, at least one read, all pointers
+    ms = ctypes.c_float(0)
+    src, sink = ctypes.c_void_p(4096), ctypes.c_void_p(8192)
+    assert N.lib.dar_op_stream_read(src, 100, 1, sink, ctypes.byref(ms), None) == N.DAR_E_INVAL
+    assert N.lib.dar_op_stream_read(src, 0, 1, sink, ctypes.byref(ms), None) == N.DAR_E_INVAL
+    assert N.lib.dar_op_stream_read(src, 1024, 0, sink, ctypes.byref(ms), None) == N.DAR_E_INVAL
+    assert N.lib.dar_op_stream_read(ctypes.c_void_p(4100), 1024, 1, sink, ctypes.byref(ms), None) == N.DAR_E_INVAL
+    assert N.lib.dar_op_stream_read(None, 1024, 1, sink, ctypes.byref(ms), None) == N.DAR_E_INVAL
+    assert N.lib.dar_op_stream_read(src, 1024, 1, None, ctypes.byref(ms), None) == N.DAR_E_INVAL
+    assert N.lib.dar_op_stream_read(src, 1024, 1, sink, None, None) == N.DAR_E_INVAL
     assert N.lib.dar_quantize_fp8_rows(ctypes.c_void_p(4096), 4, 24, ctypes.c_void_p(4096),
                                        ctypes.c_void_p(4096), None) == N.DAR_E_INVAL
     assert N.lib.dar_quantize_int8_rows(ctypes.c_void_p(4096), 4, 24, ctypes.c_void_p(4096),
