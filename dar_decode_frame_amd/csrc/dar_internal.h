@@ -144,6 +144,12 @@ struct AttnArgs {
   int nsplit_max;           // grid.x
   int M;
   float* part;              // [M][n_kv][nsplit_max][group][head_dim + 2]
+  // non-null: the splits merge inside the split launch. The split workgroups
+  // of (row m, KV head kvh) count themselves on cnt[m * n_kv + kvh] (zero
+  // before the launch, zero again after it) and the last to arrive merges
+  // every split's partials into the output; null: a second launch
+  // (T_COMBINE) merges them
+  unsigned* cnt;
   float* out;
   int out_stride;
   // non-null: the output also as the GEMM input pair hi = bf16(o), lo =

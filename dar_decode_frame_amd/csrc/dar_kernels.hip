@@ -744,6 +744,17 @@ __device__ __forceinline__ void attn_store(const AttnArgs& a, size_t idx, float 
   }
 }
 
+// Stores and loads of data that another workgroup, possibly on another XCD,
+// reads or wrote inside the same launch: system scope (sc0 sc1), so the store
+// writes through to memory and the load does not take a line one XCD's L2
+// held from before.
+__device__ __forceinline__ void st_coherent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+__device__ __forceinline__ float ld_coherent(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
 // ------------------------------------------------ split-K decode attention --
 
 // One block = one KV head x one split of `chunk` positions for one query row
@@ -751,8 +762,13 @@ __device__ __forceinline__ void attn_store(const AttnArgs& a, size_t idx, float 
 // bytes each); a wave covers 64/(hd/8) positions per step and keeps an online
 // softmax per lane group; groups and waves are merged at the end. With one
 // split the block writes the output; otherwise it writes the split's (max,
-// sum, acc) and combine_body merges the splits in the following launch (no
-// cross-workgroup signalling inside a launch).
+// sum, acc), and either combine_body merges the splits in the following
+// launch (a.cnt null) or the last split of the (row, KV head) to finish
+// merges them in this one (a.cnt set). The merging split reads partials that
+// workgroups on other XCDs wrote; those are exchanged with system-coherent
+// stores and loads (written through to memory, not held in one XCD's L2), the
+// writers wait for their stores to complete before they count themselves, and
+// the count is an agent-scope atomic, so no cache-wide fence is needed.
 template <int HD, int G>
 __device__ __forceinline__ void attn_body(const AttnArgs& a, int bid, char* lds) {
   constexpr int LPP = HD / 8;
@@ -860,7 +876,8 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, int bid, char* lds)
     }
   }
   __syncthreads();
-  const bool direct = a.nsplit_max == 1;
+  const bool merge_here = a.cnt != nullptr;
+  const bool direct = a.nsplit_max == 1 || (merge_here && nsplit == 1);
   const int stride_s = G * (HD + 2);
   float* part = a.part + (((size_t)m * a.n_heads_kv + kvh) * a.nsplit_max) * stride_s;
   for (int idx = tid; idx < G * HD; idx += kBlock) {
@@ -879,6 +896,13 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, int bid, char* lds)
     if (direct) {
       // a single split covers every position: normalise and write the output
       attn_store(a, (size_t)m * a.out_stride + (kvh * G + h) * HD + e, num / den);
+    } else if (merge_here) {
+      float* ps = part + (size_t)s * stride_s + h * (HD + 2);
+      st_coherent(ps + e, num);
+      if (e == 0) {
+        st_coherent(ps + HD, M);
+        st_coherent(ps + HD + 1, den);
+      }
     } else {
       float* ps = part + (size_t)s * stride_s + h * (HD + 2);
       ps[e] = num;
@@ -887,6 +911,53 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, int bid, char* lds)
         ps[HD + 1] = den;
       }
     }
+  }
+  if (direct || !merge_here) return;
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's partials have reached memory
+  __syncthreads();                // ... and every wave's (the LDS above is free again)
+  int* last = reinterpret_cast<int*>(lds);
+  if (tid == 0) {
+    unsigned* c = a.cnt + (size_t)m * a.n_heads_kv + kvh;
+    const unsigned before = __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const bool is_last = before + 1u == (unsigned)nsplit;
+    if (is_last) __hip_atomic_store(c, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // for the next launch
+    *last = is_last;
+  }
+  __syncthreads();
+  if (!*last) return;
+  // every split has written its partials: merge them in split order (the
+  // same sums whichever split arrives last), MU splits' loads in flight per
+  // step, with the running maximum rescaling the sums as in the splits
+  constexpr int MU = 4;
+#pragma unroll
+  for (int i = 0; i < (G * HD + kBlock - 1) / kBlock; ++i) {
+    const int idx = tid + i * kBlock;
+    if (idx >= G * HD) break;
+    const int h = idx / HD, e = idx % HD;
+    const float* ph = part + h * (HD + 2);
+    float M = -INFINITY, num = 0.f, den = 0.f;
+    for (int t0 = 0; t0 < nsplit; t0 += MU) {
+      float mv[MU], lv[MU], av[MU];
+#pragma unroll
+      for (int u = 0; u < MU; ++u) {
+        const float* pt = ph + (size_t)min(t0 + u, nsplit - 1) * stride_s;
+        mv[u] = ld_coherent(pt + HD);
+        lv[u] = ld_coherent(pt + HD + 1);
+        av[u] = ld_coherent(pt + e);
+      }
+#pragma unroll
+      for (int u = 0; u < MU; ++u) {
+        if (t0 + u < nsplit) {
+          const float mn = fmaxf(M, mv[u]);
+          const float ca = exp2f(M - mn);  // 0 for the first split (M = -inf)
+          const float cb = exp2f(mv[u] - mn);
+          num = num * ca + av[u] * cb;
+          den = den * ca + lv[u] * cb;
+          M = mn;
+        }
+      }
+    }
+    attn_store(a, (size_t)m * a.out_stride + (kvh * G + h) * HD + e, num / den);
   }
 }
 

@@ -66,7 +66,7 @@ int nsplit_slow_of(const dar_config* c) { return (c->max_len + kAttnChunkDefault
 
 struct Layout {
   size_t x[2], q[2], o[2], h[2], part[2];  // chain scratch: [0] slow (one row), [1] fast (two rows)
-  size_t ht, logits0, flogits, slots0, slotsf, pred, committed, forced, flags, pos, seqpos, ring, rope;
+  size_t ht, logits0, flogits, slots0, slotsf, pred, committed, forced, flags, acnt, pos, seqpos, ring, rope;
   size_t ks, vs, kf, vf;
   // prefill block scratch (kPrefillRows rows): residual, GEMM input halves,
   // QKV output, q, attention output, W1/W3 outputs, GEMM and attention partials
@@ -151,6 +151,7 @@ Layout make_layout(const dar_config* c, Paging pg = Paging{0, 0}) {
   L.committed = take(sizeof(int) * B * fc);
   L.forced = take(sizeof(int) * B * fc);
   L.flags = take(sizeof(int) * 4);
+  L.acnt = take(sizeof(unsigned) * B * c->n_heads_kv);  // the slow attention's split counters (zero between launches)
   L.pos = take(sizeof(int) * (3 * B + 4));  // slow positions [B], frame positions [B], first frames [B]
   L.seqpos = take(sizeof(int) * L.seq_len);
   L.ring = take(sizeof(int) * (size_t)c->max_len * B * fc);
@@ -329,6 +330,7 @@ struct Plan {
 // Scratch and stream of one chain of launches.
 struct Chain {
   float *x = nullptr, *q = nullptr, *o = nullptr, *h = nullptr, *part = nullptr;
+  unsigned* cnt = nullptr;  // non-null: split attention merges its splits in its own launch
   hipStream_t s = nullptr;
 };
 
@@ -467,10 +469,11 @@ void add_layer(dar_ctx* c, std::vector<TaskRec>& out, const Chain& ch, const dar
   aa.nsplit_max = nsplit_max;
   aa.M = M;
   aa.part = ch.part;
+  aa.cnt = nsplit_max > 1 ? ch.cnt : nullptr;
   aa.out = ch.o;
   aa.out_stride = qw;
   out.push_back(rec(t, K_ATTN, tag));
-  if (nsplit_max > 1) {
+  if (nsplit_max > 1 && !aa.cnt) {
     t.kind = T_COMBINE;
     out.push_back(rec(t, K_ATTN, tag));
   }
@@ -1351,6 +1354,7 @@ int create_impl(const dar_config* cfg, const dar_weights* w, void* workspace, si
     chains[i]->h = reinterpret_cast<float*>(b + L.h[i]);
     chains[i]->part = reinterpret_cast<float*>(b + L.part[i]);
   }
+  c->cs.cnt = reinterpret_cast<unsigned*>(b + L.acnt);
   c->ht = reinterpret_cast<float*>(b + L.ht);
   c->logits0 = reinterpret_cast<float*>(b + L.logits0);
   c->flogits = reinterpret_cast<float*>(b + L.flogits);
@@ -2063,9 +2067,11 @@ int dar_op_attention(const float* q, const void* K, const void* V, int32_t n_hea
   const size_t pf = attn_partial_floats(M, n_heads_kv, nsplit_max, g, head_dim);
   char* scratch = nullptr;
   const size_t off_pos = align_up(pf * sizeof(float));
-  hipError_t e = hipMalloc(&scratch, off_pos + 256);
+  const size_t off_cnt = off_pos + 256;
+  hipError_t e = hipMalloc(&scratch, off_cnt + align_up(sizeof(unsigned) * M * n_heads_kv));
   if (e != hipSuccess) return hip_fail(nullptr, e, "attention scratch");
   int* dpos = reinterpret_cast<int*>(scratch + off_pos);
+  unsigned* cnt = reinterpret_cast<unsigned*>(scratch + off_cnt);
   Task t = none_task();
   t.kind = T_ATTN;
   t.M = M;
@@ -2083,15 +2089,14 @@ int dar_op_attention(const float* q, const void* K, const void* V, int32_t n_hea
   a.nsplit_max = nsplit_max;
   a.M = M;
   a.part = reinterpret_cast<float*>(scratch);
+  a.cnt = nsplit_max > 1 ? cnt : nullptr;  // the splits merge in the same launch, as in the decode frame
   a.out = out;
   a.out_stride = n_heads_q * head_dim;
   int st = DAR_OK;
-  if ((e = launch_fill_i32(dpos, 1, pos, s)) != hipSuccess) st = hip_fail(nullptr, e, "attention");
+  if ((e = launch_fill_i32(dpos, 1, pos, s)) != hipSuccess ||
+      (e = launch_fill_i32(reinterpret_cast<int*>(cnt), M * n_heads_kv, 0, s)) != hipSuccess)
+    st = hip_fail(nullptr, e, "attention");
   if (st == DAR_OK) st = run_single_task(t, W_BF16, s, "attention");
-  if (st == DAR_OK && nsplit_max > 1) {
-    t.kind = T_COMBINE;
-    st = run_single_task(t, W_BF16, s, "attention combine");
-  }
   (void)hipStreamSynchronize(s);
   (void)hipFree(scratch);
   return st;
