@@ -3,9 +3,9 @@
 //
 // Frame (tuna-fish README, intro: "slowAR decode + fastAR loop"; "Inference
 // estimation": slow AR once, fast AR nine times with a 10-long fast KV):
-//   slow layers 0..Ls-1 : QKV(+norm, RoPE, KV append) -> attention (-> split
-//                         combine) -> Wo(+res) -> W1/W3(+norm, SiLU*mul)
-//                         -> W2(+res)
+//   slow layers 0..Ls-1 : QKV(+norm, RoPE, KV append) -> attention (splits
+//                         merged in the same launch) -> Wo(+res)
+//                         -> W1/W3(+norm, SiLU*mul) -> W2(+res)
 //   codebook-0 head     : norm -> W0 -> per-block argmax
 //   commit c0           : argmax (or the forced code) -> ring, fast inputs
 //                         [h_t, E0[c0]], next frame's slow input W0[c0]
@@ -66,7 +66,7 @@ int nsplit_slow_of(const dar_config* c) { return (c->max_len + kAttnChunkDefault
 
 struct Layout {
   size_t x[2], q[2], o[2], h[2], part[2];  // chain scratch: [0] slow (one row), [1] fast (two rows)
-  size_t ht, logits0, flogits, slots0, slotsf, pred, committed, forced, flags, acnt, pos, seqpos, ring, rope;
+  size_t ht, logits0, flogits, slots0, slotsf, pred, committed, forced, flags, acnt, pcnt, pos, seqpos, ring, rope;
   size_t ks, vs, kf, vf;
   // prefill block scratch (kPrefillRows rows): residual, GEMM input halves,
   // QKV output, q, attention output, W1/W3 outputs, GEMM and attention partials
@@ -151,7 +151,9 @@ Layout make_layout(const dar_config* c, Paging pg = Paging{0, 0}) {
   L.committed = take(sizeof(int) * B * fc);
   L.forced = take(sizeof(int) * B * fc);
   L.flags = take(sizeof(int) * 4);
-  L.acnt = take(sizeof(unsigned) * B * c->n_heads_kv);  // the slow attention's split counters (zero between launches)
+  // split counters of the slow decode attention and of the prefill's (zero between launches)
+  L.acnt = take(sizeof(unsigned) * B * c->n_heads_kv);
+  L.pcnt = take(sizeof(unsigned) * kPrefillRows * c->n_heads_kv);
   L.pos = take(sizeof(int) * (3 * B + 4));  // slow positions [B], frame positions [B], first frames [B]
   L.seqpos = take(sizeof(int) * L.seq_len);
   L.ring = take(sizeof(int) * (size_t)c->max_len * B * fc);
@@ -473,10 +475,6 @@ void add_layer(dar_ctx* c, std::vector<TaskRec>& out, const Chain& ch, const dar
   aa.out = ch.o;
   aa.out_stride = qw;
   out.push_back(rec(t, K_ATTN, tag));
-  if (nsplit_max > 1 && !aa.cnt) {
-    t.kind = T_COMBINE;
-    out.push_back(rec(t, K_ATTN, tag));
-  }
 
   t = none_task();
   t.kind = T_GEMV;
@@ -745,6 +743,11 @@ void add_layer_rows(dar_ctx* c, std::vector<TaskRec>& out, int ch, const dar_lay
   aa.out_hi = xh;  // the O projection's input split, written by the attention itself
   aa.out_lo = xl;
   out.push_back(rec(t, K_ATTN, tag));
+  // a merge launch rather than merging in the split launch: with 64 sequences
+  // the in-launch merge made the step slower (5,862 against 6,089 frames/s)
+  // although the split and merge kernels alone took longer (31.2 + 7.6 against
+  // 36.3 us): its tail of dependent memory round trips overlaps worse with the
+  // other chain's kernels
   if (nsplit_max > 1) {
     t.kind = T_COMBINE;
     out.push_back(rec(t, K_ATTN, tag));
@@ -1150,15 +1153,12 @@ int prefill_blocks(dar_ctx* c, const int32_t* tokens, int n, hipStream_t s, int 
       aa.nsplit_max = (p0 + M + aa.chunk - 1) / aa.chunk;  // splits of the block's longest row
       aa.M = M;
       aa.part = reinterpret_cast<float*>(b + L.patt);
+      aa.cnt = aa.nsplit_max > 1 ? reinterpret_cast<unsigned*>(b + L.pcnt) : nullptr;
       aa.out = po;
       aa.out_stride = qw;
       aa.out_hi = xh;  // the O projection's input split
       aa.out_lo = xl;
       DAR_HIP(c, launch_task(wt, t, s), "prefill attention");
-      if (aa.nsplit_max > 1) {
-        t.kind = T_COMBINE;
-        DAR_HIP(c, launch_task(wt, t, s), "prefill attention combine");
-      }
       DAR_HIP(c, gemm(w.wo, w.wo_scale, d, qw, M, nullptr, 0, pgp, 1), "prefill wo");
       DAR_HIP(c,
               launch_norm_split(px, d, M, d, static_cast<const uint16_t*>(w.ffn_norm), g.rms_eps, xh, xl, s, nullptr,
