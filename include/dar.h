@@ -350,7 +350,9 @@ int dar_op_gemm_noalloc(int32_t wtype, const void* W, const float* scale, int32_
  * q device fp32 [M][n_heads_q*head_dim]; K, V device bf16
  * [n_heads_kv][max_len][head_dim]; out device fp32 [M][n_heads_q*head_dim];
  * 0 <= pos, pos + M <= max_len; M in {1, 2}; chunk = positions per split
- * (multiple of 16, 0 = default). Uses its own scratch (allocated per call). */
+ * (multiple of 16, 0 = default). One launch: the last split of a (row, KV
+ * head) to finish merges the splits. Uses its own scratch (allocated per
+ * call). */
 int dar_op_attention(const float* q, const void* K, const void* V, int32_t n_heads_q,
                      int32_t n_heads_kv, int32_t head_dim, int32_t max_len, int32_t pos,
                      int32_t M, int32_t chunk, float* out, void* stream);
