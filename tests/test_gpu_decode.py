@@ -110,12 +110,15 @@ def test_tiny_workload_own_frames(tiny_host, wtype):
 
 
 @pytest.mark.parametrize("wtype,n_prompt", [("bf16", 1), ("bf16", 128), ("bf16", 200), ("fp8", 200), ("int8", 200),
-                                                   ("int4", 200)])
+                                                   ("int4", 200), ("bf16", 300)])
 def test_tiny_prefill_blocks_parity(tiny_host, wtype, n_prompt):
-    """Prompts of one position, exactly one prefill block, and two blocks (the
-    second ragged), teacher-forced with the oracle's own frames."""
+    """Prompts of one position, exactly one prefill block, two blocks (the
+    second ragged) and three (its attention merging three 128-position splits
+    in its launch; the frames after it merge five 64-position splits),
+    teacher-forced with the oracle's own frames."""
     dims, host = tiny_host
-    max_len, n = 256, 3
+    n = 3
+    max_len = 256 if n_prompt + n < 256 else 512
     prompt = synth.gen_prompt(n_prompt, dims.vocab_c0, 5)
     free, _ = _oracle_run(dims, host, wtype, prompt, n, max_len)
     forced = [c for c, _ in free]
